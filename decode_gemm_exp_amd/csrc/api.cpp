@@ -1,0 +1,806 @@
+// api.cpp -- the extern "C" entry points of libunweight (include/unweight.h):
+// argument checks, section allocation, table construction, UWF1
+// serialisation, pipeline dispatch and the CU-split sequence runner.
+//
+// [EVC] = "Cloudflare推出Unweight無損壓縮系統，將LLM模型大小壓縮15-22%"
+// (easyvibecoding.app/curated/736), cited by section heading.
+#include <hip/hip_ext.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "uw_internal.h"
+
+using namespace uw;
+
+namespace {
+
+#define UW_HIP(call)                                   \
+  do {                                                 \
+    hipError_t e_ = (call);                            \
+    if (e_ != hipSuccess) {                            \
+      if (std::getenv("UW_LOG"))                       \
+        std::fprintf(stderr, "unweight: %s failed: %s (%s:%d)\n", #call, hipGetErrorString(e_), \
+                     __FILE__, __LINE__);              \
+      return e_ == hipErrorOutOfMemory ? UW_ERR_NOMEM : UW_ERR_DEVICE; \
+    }                                                  \
+  } while (0)
+
+#define UW_CHECK(st)             \
+  do {                           \
+    uw_status s_ = (st);         \
+    if (s_ != UW_OK) return s_;  \
+  } while (0)
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline uint64_t pad256(uint64_t n) { return (n + 255) / 256 * 256; }
+
+template <typename T>
+uw_status dev_alloc(T** p, uint64_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) return UW_OK;
+  void* q = nullptr;
+  hipError_t e = hipMalloc(&q, bytes);
+  if (e != hipSuccess) return e == hipErrorOutOfMemory ? UW_ERR_NOMEM : UW_ERR_DEVICE;
+  *p = static_cast<T*>(q);
+  return UW_OK;
+}
+
+template <typename T>
+void dev_free(T*& p) {
+  if (p) (void)hipFree((void*)p);
+  p = nullptr;
+}
+
+void free_sections(uw_matrix* m) {
+  dev_free(m->sm);
+  dev_free(m->vflags);
+  dev_free(m->vrank);
+  dev_free(m->vexp);
+  dev_free(m->seg_off);
+  dev_free(m->stream);
+  dev_free(m->lut);
+  dev_free(m->pidx);
+  dev_free(m->corrupt);
+}
+
+// Stream allocation: W + 2 words, rounded up so that the decoder's aligned
+// 16-byte chunk loads (up to 8 words past a segment) stay inside it.
+uint64_t stream_alloc_words(uint64_t W) { return (W + 2 + 3) / 4 * 4 + 8; }
+
+bool valid_seg_groups(uint32_t sg) { return sg >= 1 && sg <= 64 && (sg & (sg - 1)) == 0; }
+
+void shape_from(uw_matrix* m, uint64_t rows, uint64_t cols, uint32_t layout, uint32_t sg) {
+  m->rows = rows;
+  m->cols = cols;
+  m->layout = layout;
+  m->seg_groups = sg;
+  m->numel = rows * cols;
+  m->groups = m->numel / kGroup;
+  m->segments = (m->groups + sg - 1) / sg;
+  m->flag_words = (m->groups + 31) / 32;
+}
+
+uint64_t logical_n(const uw_matrix* m) { return m->layout == 0 ? m->rows : m->cols; }
+uint64_t logical_k(const uw_matrix* m) { return m->layout == 0 ? m->cols : m->rows; }
+
+// derive code lengths and codes from the coded histogram
+void finish_code(Tables& t) {
+  std::memset(t.code_len, 0, sizeof(t.code_len));
+  int idx[kPal], n = 0;
+  uint64_t wts[kPal];
+  for (int s = 0; s < kPal; ++s)
+    if (t.coded_count[s] > 0) {
+      idx[n] = s;
+      wts[n] = t.coded_count[s];
+      ++n;
+    }
+  t.n_coded = (uint32_t)n;
+  if (n == 1) {
+    t.code_len[idx[0]] = 1;
+  } else if (n >= 2) {
+    uint8_t lens[kPal];
+    limited_lengths(wts, n, kMaxLen, lens);
+    for (int i = 0; i < n; ++i) t.code_len[idx[i]] = lens[i];
+  }
+  assign_codes(t);
+}
+
+uint64_t len_pack(const Tables& t) {
+  uint64_t p = 0;
+  for (int s = 0; s < kPal; ++s) p |= (uint64_t)(t.code_len[s] & 15u) << (4 * s);
+  return p;
+}
+
+void pal_words(const Tables& t, uint32_t out[4]) {
+  for (int i = 0; i < 4; ++i)
+    out[i] = (uint32_t)t.palette[4 * i] | ((uint32_t)t.palette[4 * i + 1] << 8) |
+             ((uint32_t)t.palette[4 * i + 2] << 16) | ((uint32_t)t.palette[4 * i + 3] << 24);
+}
+
+uw_status upload_lut(uw_matrix* m, hipStream_t s) {
+  std::vector<uint32_t> lut(1u << kLutBits);
+  build_decode_lut(m->t, lut.data());
+  if (!m->lut) UW_CHECK(dev_alloc(&m->lut, lut.size() * 4));
+  UW_HIP(hipMemcpyAsync(m->lut, lut.data(), lut.size() * 4, hipMemcpyHostToDevice, s));
+  UW_HIP(hipStreamSynchronize(s));
+  return UW_OK;
+}
+
+uint64_t compressed_bytes(const uw_matrix* m) {
+  return kHeaderBytes + m->numel + 8 * m->flag_words + 64 * m->V + 4 * (m->segments + 1) + 4 * (m->W + 2);
+}
+
+uint64_t export_bytes(const uw_matrix* m) {
+  return kHeaderBytes + pad256(m->numel) + 2 * pad256(4 * m->flag_words) + pad256(64 * m->V) +
+         pad256(4 * (m->segments + 1)) + pad256(4 * (m->W + 2));
+}
+
+void wr32(uint8_t* p, uint32_t v) { std::memcpy(p, &v, 4); }
+void wr64(uint8_t* p, uint64_t v) { std::memcpy(p, &v, 8); }
+uint32_t rd32(const uint8_t* p) { uint32_t v; std::memcpy(&v, p, 4); return v; }
+uint64_t rd64(const uint8_t* p) { uint64_t v; std::memcpy(&v, p, 8); return v; }
+
+// UWF1 header offsets
+enum : uint32_t {
+  kOffMagic = 0, kOffVersion = 4, kOffLayout = 8, kOffSegGroups = 12, kOffRows = 16, kOffCols = 24,
+  kOffPalSize = 32, kOffNCoded = 36, kOffPalette = 40, kOffLen = 56, kOffV = 72, kOffW = 80,
+  kOffHist = 88, kOffCoded = 2136
+};
+
+// ---- CU-masked streams for the sequence runner -------------------------------------
+struct SplitStreams {
+  hipStream_t dec = nullptr, gemm = nullptr;
+};
+std::mutex g_split_mu;
+std::map<std::pair<int, int>, SplitStreams> g_split;   // (device, decode CUs)
+
+// Mask of `count` CUs starting at `first`, in the runtime's CU numbering.
+std::vector<uint32_t> cu_mask(int total, int first, int count) {
+  std::vector<uint32_t> m((size_t)(total + 31) / 32, 0u);
+  for (int i = first; i < first + count && i < total; ++i) m[(size_t)i / 32] |= 1u << (i % 32);
+  return m;
+}
+
+uw_status split_streams(int decode_cus, SplitStreams* out) {
+  int dev = 0;
+  UW_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_split_mu);
+  auto it = g_split.find({dev, decode_cus});
+  if (it != g_split.end()) {
+    *out = it->second;
+    return UW_OK;
+  }
+  hipDeviceProp_t prop;
+  UW_HIP(hipGetDeviceProperties(&prop, dev));
+  const int total = prop.multiProcessorCount;
+  if (decode_cus <= 0 || decode_cus >= total) return UW_ERR_INVALID;
+  SplitStreams ss;
+  std::vector<uint32_t> md = cu_mask(total, 0, decode_cus);
+  std::vector<uint32_t> mg = cu_mask(total, decode_cus, total - decode_cus);
+  UW_HIP(hipExtStreamCreateWithCUMask(&ss.dec, (uint32_t)md.size(), md.data()));
+  UW_HIP(hipExtStreamCreateWithCUMask(&ss.gemm, (uint32_t)mg.size(), mg.data()));
+  g_split[{dev, decode_cus}] = ss;
+  *out = ss;
+  return UW_OK;
+}
+
+// ---- preprocessing + GEMM of one matrix -------------------------------------------------
+size_t prep_bytes(const uw_matrix* m, int p) {
+  switch (p) {
+    case UW_PIPE_FULL: return pad256(2 * m->numel);
+    case UW_PIPE_EXPONENT: return pad256(m->numel);
+    case UW_PIPE_PALETTE_TRANSCODE: return pad256(m->numel / 2);
+    default: return 0;
+  }
+}
+
+WeightView base_view(const uw_matrix* m) {
+  WeightView v;
+  std::memset(&v, 0, sizeof(v));
+  v.layout = (int)m->layout;
+  v.n = logical_n(m);
+  v.k = logical_k(m);
+  v.sm = m->sm;
+  v.vflags = m->vflags;
+  v.vrank = m->vrank;
+  v.vexp = m->vexp;
+  pal_words(m->t, v.pal);
+  return v;
+}
+
+DecodeArgs decode_args(const uw_matrix* m, void* out) {
+  DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.stream = m->stream;
+  a.stream_words = stream_alloc_words(m->W);
+  a.seg_off = m->seg_off;
+  a.vflags = m->vflags;
+  a.vrank = m->vrank;
+  a.vexp = m->vexp;
+  a.sm = m->sm;
+  a.lut = m->lut;
+  pal_words(m->t, a.pal);
+  a.len_pack = len_pack(m->t);
+  a.groups = m->groups;
+  a.segments = m->segments;
+  a.seg_groups = m->seg_groups;
+  a.out = out;
+  a.corrupt = m->corrupt;
+  return a;
+}
+
+uw_status preprocess(const uw_matrix* m, int p, void* buf, hipStream_t s) {
+  if (p == UW_PIPE_PALETTE_DIRECT) return m->pidx ? UW_OK : UW_ERR_STATE;
+  if (!m->stream) return UW_ERR_STATE;
+  const int mode = p == UW_PIPE_FULL ? kDecodeFull : p == UW_PIPE_EXPONENT ? kDecodeExponent : kDecodeNibble;
+  UW_HIP(launch_decode(decode_args(m, buf), mode, s));
+  return UW_OK;
+}
+
+WeightView pipeline_view(const uw_matrix* m, int p, const void* buf) {
+  WeightView v = base_view(m);
+  switch (p) {
+    case UW_PIPE_FULL: v.fmt = kFmtBf16; v.bf16 = static_cast<const uint16_t*>(buf); break;
+    case UW_PIPE_EXPONENT: v.fmt = kFmtExp; v.ex = static_cast<const uint8_t*>(buf); break;
+    case UW_PIPE_PALETTE_TRANSCODE: v.fmt = kFmtPal; v.pidx = static_cast<const uint8_t*>(buf); break;
+    default: v.fmt = kFmtPal; v.pidx = m->pidx; break;
+  }
+  return v;
+}
+
+size_t partial_bytes(const uw_matrix* m, int p, int64_t batch, const uw_kernel_cfg* cfg) {
+  WeightView v = pipeline_view(m, p, nullptr);
+  return pad256(gemm_partial_elems(v, batch, cfg) * sizeof(float));
+}
+
+uw_status check_matmul_args(const uw_matrix* m, int p, const uint16_t* x, int64_t batch, const float* y) {
+  if (!m || !x || !y || batch <= 0) return UW_ERR_INVALID;
+  if (p < UW_PIPE_FULL || p > UW_PIPE_PALETTE_DIRECT) return UW_ERR_INVALID;
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(y) & 3u)) return UW_ERR_INVALID;
+  if (logical_k(m) % 8 != 0) return UW_ERR_UNSUPPORTED;
+  if (p == UW_PIPE_PALETTE_DIRECT && !m->pidx) return UW_ERR_STATE;
+  if (p != UW_PIPE_PALETTE_DIRECT && !m->stream) return UW_ERR_STATE;
+  return UW_OK;
+}
+
+}  // namespace
+
+// =====================================================================================
+extern "C" {
+
+const char* uw_status_str(uw_status st) {
+  switch (st) {
+    case UW_OK: return "ok";
+    case UW_ERR_INVALID: return "invalid argument";
+    case UW_ERR_UNSUPPORTED: return "unsupported shape";
+    case UW_ERR_NOMEM: return "out of memory";
+    case UW_ERR_DEVICE: return "HIP runtime error";
+    case UW_ERR_CORRUPT: return "corrupt compressed data";
+    case UW_ERR_STATE: return "handle lacks the required section";
+    case UW_ERR_WORKSPACE: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+uint32_t uw_version(void) { return (1u << 16) | 0u; }
+
+uw_status uw_compress(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout layout,
+                      const uw_compress_opts* opts, void* stream, uw_matrix** out) try {
+  if (!out) return UW_ERR_INVALID;
+  *out = nullptr;
+  if (!w_dev || n <= 0 || k <= 0 || (layout != UW_LAYOUT_NK && layout != UW_LAYOUT_KN)) return UW_ERR_INVALID;
+  if (!aligned16(w_dev)) return UW_ERR_INVALID;
+  const uint32_t sg = (opts && opts->seg_groups) ? opts->seg_groups : 8u;
+  if (!valid_seg_groups(sg) || (opts && opts->flags)) return UW_ERR_INVALID;
+  const uint64_t rows = layout == UW_LAYOUT_NK ? (uint64_t)n : (uint64_t)k;
+  const uint64_t cols = layout == UW_LAYOUT_NK ? (uint64_t)k : (uint64_t)n;
+  if (cols % kGroup != 0) return UW_ERR_UNSUPPORTED;
+  if (rows * cols >= (1ull << 32)) return UW_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  uw_matrix* m = new (std::nothrow) uw_matrix();
+  if (!m) return UW_ERR_NOMEM;
+  struct Guard {
+    uw_matrix* m;
+    void* scratch = nullptr;
+    ~Guard() {
+      if (scratch) (void)hipFree(scratch);
+      if (m) { free_sections(m); delete m; }
+    }
+  } guard{m};
+  UW_HIP(hipGetDevice(&m->device));
+  shape_from(m, rows, cols, (uint32_t)layout, sg);
+
+  UW_CHECK(dev_alloc(&m->sm, m->numel));
+  UW_CHECK(dev_alloc(&m->vflags, 4 * m->flag_words));
+  UW_CHECK(dev_alloc(&m->vrank, 4 * m->flag_words));
+  UW_CHECK(dev_alloc(&m->seg_off, 4 * (m->segments + 1)));
+  UW_CHECK(dev_alloc(&m->corrupt, sizeof(int)));
+  UW_HIP(hipMemsetAsync(m->corrupt, 0, sizeof(int), s));
+
+  // scratch: hist u32[256] | coded u32[16] | total u64 | slot/len tables | codebook u32[256] | seg words
+  const uint64_t off_coded = 1024, off_total = 1088, off_slot = 1152, off_len = 1408, off_book = 1664,
+                 off_seg = 2688;
+  void* scratch = nullptr;
+  UW_CHECK(dev_alloc(&scratch, off_seg + 4 * m->segments + 256));
+  guard.scratch = scratch;
+  uint8_t* sc = static_cast<uint8_t*>(scratch);
+  uint32_t* d_hist = reinterpret_cast<uint32_t*>(sc);
+  uint32_t* d_coded = reinterpret_cast<uint32_t*>(sc + off_coded);
+  uint64_t* d_total = reinterpret_cast<uint64_t*>(sc + off_total);
+  uint8_t* d_slot = sc + off_slot;
+  uint8_t* d_len = sc + off_len;
+  uint32_t* d_book = reinterpret_cast<uint32_t*>(sc + off_book);
+  uint32_t* d_seg = reinterpret_cast<uint32_t*>(sc + off_seg);
+
+  // 1. exponent histogram
+  UW_HIP(hipMemsetAsync(sc, 0, off_slot, s));
+  UW_HIP(launch_histogram(w_dev, m->numel, d_hist, s));
+  uint32_t hist32[256];
+  UW_HIP(hipMemcpyAsync(hist32, d_hist, sizeof(hist32), hipMemcpyDeviceToHost, s));
+  UW_HIP(hipStreamSynchronize(s));
+  for (int v = 0; v < 256; ++v) m->t.hist[v] = hist32[v];
+
+  // 2. palette, verbatim flags, sign/mantissa, coded histogram, ranks
+  choose_palette(m->t);
+  uint8_t slot_tab[256];
+  for (int v = 0; v < 256; ++v) slot_tab[v] = m->t.slot_of[v] < 0 ? 0xFFu : (uint8_t)m->t.slot_of[v];
+  UW_HIP(hipMemcpyAsync(d_slot, slot_tab, 256, hipMemcpyHostToDevice, s));
+  UW_HIP(launch_flags(w_dev, m->numel, m->groups, d_slot, m->sm, m->vflags, d_coded, s));
+  UW_HIP(launch_rank_scan(m->vflags, m->flag_words, m->vrank, d_total, s));
+  uint32_t coded32[16];
+  uint64_t vtotal = 0;
+  UW_HIP(hipMemcpyAsync(coded32, d_coded, sizeof(coded32), hipMemcpyDeviceToHost, s));
+  UW_HIP(hipMemcpyAsync(&vtotal, d_total, sizeof(vtotal), hipMemcpyDeviceToHost, s));
+  UW_HIP(hipStreamSynchronize(s));
+  m->V = vtotal;
+  for (int i = 0; i < kPal; ++i) m->t.coded_count[i] = coded32[i];
+  finish_code(m->t);
+  UW_CHECK(dev_alloc(&m->vexp, 64 * m->V));
+
+  // 3. segment lengths and offsets
+  uint8_t len_tab[256];
+  uint32_t book[256];
+  for (int v = 0; v < 256; ++v) {
+    const int sl = m->t.slot_of[v];
+    len_tab[v] = sl < 0 ? 0 : m->t.code_len[sl];
+    book[v] = sl < 0 ? 0u : ((uint32_t)m->t.code[sl] << 8) | m->t.code_len[sl];
+  }
+  UW_HIP(hipMemcpyAsync(d_len, len_tab, 256, hipMemcpyHostToDevice, s));
+  UW_HIP(hipMemcpyAsync(d_book, book, sizeof(book), hipMemcpyHostToDevice, s));
+  UW_HIP(hipMemsetAsync(d_seg, 0, 4 * m->segments, s));
+  UW_HIP(launch_segment_bits(w_dev, m->groups, sg, m->segments, d_len, m->vflags, d_seg, s));
+  UW_HIP(launch_offsets_scan(d_seg, m->segments, m->seg_off, s));
+  uint32_t W32 = 0;
+  UW_HIP(hipMemcpyAsync(&W32, m->seg_off + m->segments, 4, hipMemcpyDeviceToHost, s));
+  UW_HIP(hipStreamSynchronize(s));
+  m->W = W32;
+
+  // 4. encode
+  const uint64_t sw = stream_alloc_words(m->W);
+  UW_CHECK(dev_alloc(&m->stream, 4 * sw));
+  UW_HIP(hipMemsetAsync(m->stream, 0, 4 * sw, s));
+  UW_HIP(launch_encode(w_dev, m->groups, sg, m->segments, d_book, m->vflags, m->vrank, m->seg_off, m->stream,
+                       m->vexp, s));
+  m->code_bits = 0;
+  for (int i = 0; i < kPal; ++i) m->code_bits += m->t.coded_count[i] * m->t.code_len[i];
+  UW_CHECK(upload_lut(m, s));   // synchronises: host tables above stay alive until here
+  guard.m = nullptr;
+  *out = m;
+  return UW_OK;
+} catch (...) {
+  return UW_ERR_NOMEM;
+}
+
+uw_status uw_get_info(const uw_matrix* m, uw_info* o) {
+  if (!m || !o) return UW_ERR_INVALID;
+  std::memset(o, 0, sizeof(*o));
+  o->layout = m->layout;
+  o->seg_groups = m->seg_groups;
+  o->rows = m->rows;
+  o->cols = m->cols;
+  o->n = logical_n(m);
+  o->k = logical_k(m);
+  o->numel = m->numel;
+  o->groups = m->groups;
+  o->segments = m->segments;
+  o->palette_size = m->t.palette_size;
+  o->n_coded = m->t.n_coded;
+  std::memcpy(o->palette, m->t.palette, 16);
+  std::memcpy(o->code_len, m->t.code_len, 16);
+  std::memcpy(o->code, m->t.code, sizeof(o->code));
+  std::memcpy(o->hist, m->t.hist, sizeof(o->hist));
+  std::memcpy(o->coded_count, m->t.coded_count, sizeof(o->coded_count));
+  o->verbatim_groups = m->V;
+  o->stream_words = m->W;
+  o->code_bits = m->code_bits;
+  o->compressed_bytes = compressed_bytes(m);
+  o->export_bytes = export_bytes(m);
+  o->bits_per_weight = 8.0 * (double)o->compressed_bytes / (double)m->numel;
+  o->has_stream = m->stream != nullptr;
+  o->has_palette_idx = m->pidx != nullptr;
+  return UW_OK;
+}
+
+uw_status uw_export(const uw_matrix* m, void* host_buf, size_t cap, size_t* bytes) try {
+  if (!m || !bytes) return UW_ERR_INVALID;
+  const uint64_t total = export_bytes(m);
+  *bytes = total;
+  if (cap == 0) return UW_OK;
+  if (!host_buf || cap < total) return UW_ERR_INVALID;
+  if (!m->stream) return UW_ERR_STATE;
+  UW_HIP(hipDeviceSynchronize());
+  uint8_t* b = static_cast<uint8_t*>(host_buf);
+  std::memset(b, 0, total);
+  std::memcpy(b + kOffMagic, "UWF1", 4);
+  wr32(b + kOffVersion, 1);
+  wr32(b + kOffLayout, m->layout);
+  wr32(b + kOffSegGroups, m->seg_groups);
+  wr64(b + kOffRows, m->rows);
+  wr64(b + kOffCols, m->cols);
+  wr32(b + kOffPalSize, m->t.palette_size);
+  wr32(b + kOffNCoded, m->t.n_coded);
+  std::memcpy(b + kOffPalette, m->t.palette, 16);
+  std::memcpy(b + kOffLen, m->t.code_len, 16);
+  wr64(b + kOffV, m->V);
+  wr64(b + kOffW, m->W);
+  for (int v = 0; v < 256; ++v) wr64(b + kOffHist + 8 * v, m->t.hist[v]);
+  for (int s = 0; s < kPal; ++s) wr64(b + kOffCoded + 8 * s, m->t.coded_count[s]);
+  uint64_t at = kHeaderBytes;
+  const void* src[6] = {m->sm, m->vflags, m->vrank, m->vexp, m->seg_off, m->stream};
+  const uint64_t sz[6] = {m->numel, 4 * m->flag_words, 4 * m->flag_words, 64 * m->V, 4 * (m->segments + 1),
+                          4 * (m->W + 2)};
+  for (int i = 0; i < 6; ++i) {
+    if (sz[i]) UW_HIP(hipMemcpy(b + at, src[i], sz[i], hipMemcpyDeviceToHost));
+    at += pad256(sz[i]);
+  }
+  return UW_OK;
+} catch (...) {
+  return UW_ERR_NOMEM;
+}
+
+uw_status uw_import(const void* host_blob, size_t nbytes, void* stream, uw_matrix** out) try {
+  if (!out) return UW_ERR_INVALID;
+  *out = nullptr;
+  if (!host_blob) return UW_ERR_INVALID;
+  const uint8_t* b = static_cast<const uint8_t*>(host_blob);
+  if (nbytes < kHeaderBytes || std::memcmp(b, "UWF1", 4) != 0) return UW_ERR_CORRUPT;
+  if (rd32(b + kOffVersion) != 1) return UW_ERR_CORRUPT;
+  const uint32_t layout = rd32(b + kOffLayout), sg = rd32(b + kOffSegGroups);
+  const uint64_t rows = rd64(b + kOffRows), cols = rd64(b + kOffCols);
+  if (layout > 1 || !valid_seg_groups(sg) || rows == 0 || cols == 0 || cols % kGroup != 0) return UW_ERR_CORRUPT;
+  if (rows > (1ull << 32) || rows * cols >= (1ull << 32)) return UW_ERR_CORRUPT;
+
+  uw_matrix tmp;
+  shape_from(&tmp, rows, cols, layout, sg);
+  tmp.V = rd64(b + kOffV);
+  tmp.W = rd64(b + kOffW);
+  if (tmp.V > tmp.groups || tmp.W >= (1ull << 32)) return UW_ERR_CORRUPT;
+  for (int v = 0; v < 256; ++v) tmp.t.hist[v] = rd64(b + kOffHist + 8 * v);
+  uint64_t hsum = 0;
+  for (int v = 0; v < 256; ++v) hsum += tmp.t.hist[v];
+  if (hsum != tmp.numel) return UW_ERR_CORRUPT;
+  // the palette must be the one the histogram implies
+  choose_palette(tmp.t);
+  if (rd32(b + kOffPalSize) != tmp.t.palette_size || std::memcmp(b + kOffPalette, tmp.t.palette, 16) != 0)
+    return UW_ERR_CORRUPT;
+  uint64_t coded_sum = 0;
+  for (int s = 0; s < kPal; ++s) {
+    tmp.t.coded_count[s] = rd64(b + kOffCoded + 8 * s);
+    if (tmp.t.coded_count[s] && (uint32_t)s >= tmp.t.palette_size) return UW_ERR_CORRUPT;
+    coded_sum += tmp.t.coded_count[s];
+  }
+  if (coded_sum != (tmp.groups - tmp.V) * kGroup) return UW_ERR_CORRUPT;
+  // the code must be the one the coded histogram implies
+  finish_code(tmp.t);
+  if (rd32(b + kOffNCoded) != tmp.t.n_coded || std::memcmp(b + kOffLen, tmp.t.code_len, 16) != 0)
+    return UW_ERR_CORRUPT;
+  if (export_bytes(&tmp) != nbytes) return UW_ERR_CORRUPT;
+
+  // small sections: flags, ranks, offsets
+  const uint64_t o_sm = kHeaderBytes, o_vf = o_sm + pad256(tmp.numel), o_vr = o_vf + pad256(4 * tmp.flag_words),
+                 o_vx = o_vr + pad256(4 * tmp.flag_words), o_so = o_vx + pad256(64 * tmp.V),
+                 o_st = o_so + pad256(4 * (tmp.segments + 1));
+  std::vector<uint32_t> vf(tmp.flag_words), vr(tmp.flag_words), so(tmp.segments + 1);
+  std::memcpy(vf.data(), b + o_vf, 4 * tmp.flag_words);
+  std::memcpy(vr.data(), b + o_vr, 4 * tmp.flag_words);
+  std::memcpy(so.data(), b + o_so, 4 * (tmp.segments + 1));
+  uint64_t run = 0;
+  for (uint64_t w = 0; w < tmp.flag_words; ++w) {
+    if (vr[w] != run) return UW_ERR_CORRUPT;
+    uint32_t f = vf[w];
+    if (w == tmp.flag_words - 1 && (tmp.groups & 31)) f &= (1u << (tmp.groups & 31)) - 1u;
+    if (f != vf[w]) return UW_ERR_CORRUPT;   // bits past the last group
+    run += (uint64_t)__builtin_popcount(f);
+  }
+  if (run != tmp.V) return UW_ERR_CORRUPT;
+  if (so[0] != 0 || so[tmp.segments] != tmp.W) return UW_ERR_CORRUPT;
+  uint32_t maxlen = 0;
+  for (int s = 0; s < kPal; ++s) maxlen = std::max<uint32_t>(maxlen, tmp.t.code_len[s]);
+  for (uint64_t sgi = 0; sgi < tmp.segments; ++sgi) {
+    if (so[sgi + 1] < so[sgi]) return UW_ERR_CORRUPT;
+    uint64_t coded_groups = 0;
+    const uint64_t g1 = std::min<uint64_t>((sgi + 1) * sg, tmp.groups);
+    for (uint64_t g = sgi * sg; g < g1; ++g) coded_groups += ((vf[g >> 5] >> (g & 31)) & 1u) ? 0 : 1;
+    const uint64_t words = so[sgi + 1] - so[sgi];
+    if ((coded_groups == 0) != (words == 0)) return UW_ERR_CORRUPT;
+    if (words > (coded_groups * kGroup * maxlen + 31) / 32) return UW_ERR_CORRUPT;
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uw_matrix* m = new (std::nothrow) uw_matrix();
+  if (!m) return UW_ERR_NOMEM;
+  struct Guard {
+    uw_matrix* m;
+    ~Guard() { if (m) { free_sections(m); delete m; } }
+  } guard{m};
+  UW_HIP(hipGetDevice(&m->device));
+  shape_from(m, rows, cols, layout, sg);
+  m->V = tmp.V;
+  m->W = tmp.W;
+  m->t = tmp.t;
+  m->code_bits = 0;
+  for (int i = 0; i < kPal; ++i) m->code_bits += m->t.coded_count[i] * m->t.code_len[i];
+  const uint64_t sw = stream_alloc_words(m->W);
+  UW_CHECK(dev_alloc(&m->sm, m->numel));
+  UW_CHECK(dev_alloc(&m->vflags, 4 * m->flag_words));
+  UW_CHECK(dev_alloc(&m->vrank, 4 * m->flag_words));
+  UW_CHECK(dev_alloc(&m->vexp, 64 * m->V));
+  UW_CHECK(dev_alloc(&m->seg_off, 4 * (m->segments + 1)));
+  UW_CHECK(dev_alloc(&m->stream, 4 * sw));
+  UW_CHECK(dev_alloc(&m->corrupt, sizeof(int)));
+  UW_HIP(hipMemsetAsync(m->corrupt, 0, sizeof(int), s));
+  UW_HIP(hipMemsetAsync(m->stream, 0, 4 * sw, s));
+  UW_HIP(hipMemcpyAsync(m->sm, b + o_sm, m->numel, hipMemcpyHostToDevice, s));
+  UW_HIP(hipMemcpyAsync(m->vflags, vf.data(), 4 * m->flag_words, hipMemcpyHostToDevice, s));
+  UW_HIP(hipMemcpyAsync(m->vrank, vr.data(), 4 * m->flag_words, hipMemcpyHostToDevice, s));
+  if (m->V) UW_HIP(hipMemcpyAsync(m->vexp, b + o_vx, 64 * m->V, hipMemcpyHostToDevice, s));
+  UW_HIP(hipMemcpyAsync(m->seg_off, so.data(), 4 * (m->segments + 1), hipMemcpyHostToDevice, s));
+  UW_HIP(hipMemcpyAsync(m->stream, b + o_st, 4 * (m->W + 2), hipMemcpyHostToDevice, s));
+  UW_CHECK(upload_lut(m, s));   // synchronises
+  guard.m = nullptr;
+  *out = m;
+  return UW_OK;
+} catch (...) {
+  return UW_ERR_NOMEM;
+}
+
+void uw_free(uw_matrix* m) {
+  if (!m) return;
+  free_sections(m);
+  delete m;
+}
+
+static uw_status decode_to(const uw_matrix* m, void* out, int mode, hipStream_t s) {
+  if (!m || !out || !aligned16(out)) return UW_ERR_INVALID;
+  if (!m->stream) return UW_ERR_STATE;
+  UW_HIP(launch_decode(decode_args(m, out), mode, s));
+  return UW_OK;
+}
+
+uw_status uw_decode_full(const uw_matrix* m, uint16_t* w_out_dev, void* stream) {
+  return decode_to(m, w_out_dev, kDecodeFull, static_cast<hipStream_t>(stream));
+}
+
+uw_status uw_decode_exponent(const uw_matrix* m, uint8_t* e_out_dev, void* stream) {
+  return decode_to(m, e_out_dev, kDecodeExponent, static_cast<hipStream_t>(stream));
+}
+
+uw_status uw_transcode_palette(uw_matrix* m, uint8_t* idx_out_dev, void* stream) {
+  if (!m) return UW_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (idx_out_dev) return decode_to(m, idx_out_dev, kDecodeNibble, s);
+  if (!m->stream) return m->pidx ? UW_OK : UW_ERR_STATE;
+  if (!m->pidx) UW_CHECK(dev_alloc(&m->pidx, m->numel / 2));
+  return decode_to(m, m->pidx, kDecodeNibble, s);
+}
+
+uw_status uw_drop_stream(uw_matrix* m, void* stream) {
+  if (!m) return UW_ERR_INVALID;
+  if (!m->pidx) return UW_ERR_STATE;
+  UW_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  dev_free(m->stream);
+  dev_free(m->seg_off);
+  dev_free(m->lut);
+  return UW_OK;
+}
+
+uw_status uw_workspace_size(const uw_matrix* m, uw_pipeline p, int64_t batch, size_t* bytes) {
+  if (!m || !bytes || batch <= 0 || p < UW_PIPE_FULL || p > UW_PIPE_PALETTE_DIRECT) return UW_ERR_INVALID;
+  *bytes = prep_bytes(m, p) + partial_bytes(m, p, batch, nullptr);
+  return UW_OK;
+}
+
+static uw_status workspace_for(const uw_matrix* m, int p, int64_t batch, const uw_kernel_cfg* cfg, size_t* b) {
+  *b = prep_bytes(m, p) + partial_bytes(m, p, batch, cfg);
+  return UW_OK;
+}
+
+uw_status uw_matmul_reconstruct(const uw_matrix* m, uw_pipeline p, const uint16_t* x_dev, int64_t batch,
+                                float* y_dev, void* ws_dev, size_t ws_bytes, const uw_kernel_cfg* cfg,
+                                void* stream) {
+  UW_CHECK(check_matmul_args(m, p, x_dev, batch, y_dev));
+  size_t need = 0;
+  workspace_for(m, p, batch, cfg, &need);
+  if (need > ws_bytes || (need && !ws_dev) || !aligned16(ws_dev)) return UW_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(ws_dev);
+  UW_CHECK(preprocess(m, p, ws, s));
+  WeightView v = pipeline_view(m, p, ws);
+  const size_t pb = prep_bytes(m, p);
+  float* part = reinterpret_cast<float*>(ws + pb);
+  UW_HIP(launch_gemm(v, x_dev, batch, y_dev, (int64_t)v.n, 0, cfg, part, (need - pb) / sizeof(float), s));
+  return UW_OK;
+}
+
+uw_status uw_matmul_reconstruct_grouped(const uw_matrix* const* ms, int count, uw_pipeline p,
+                                        const uint16_t* x_dev, int64_t batch, float* y_dev, void* ws_dev,
+                                        size_t ws_bytes, const uw_kernel_cfg* cfg, void* stream) {
+  if (!ms || count <= 0) return UW_ERR_INVALID;
+  uint64_t total_n = 0;
+  size_t need = 0;
+  for (int i = 0; i < count; ++i) {
+    UW_CHECK(check_matmul_args(ms[i], p, x_dev, batch, y_dev));
+    if (logical_k(ms[i]) != logical_k(ms[0])) return UW_ERR_INVALID;
+    total_n += logical_n(ms[i]);
+    size_t b = 0;
+    workspace_for(ms[i], p, batch, cfg, &b);
+    need += b;
+  }
+  if (need > ws_bytes || (need && !ws_dev) || !aligned16(ws_dev)) return UW_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(ws_dev);
+  size_t off = 0;
+  std::vector<size_t> offs((size_t)count);
+  for (int i = 0; i < count; ++i) {
+    offs[(size_t)i] = off;
+    UW_CHECK(preprocess(ms[i], p, ws + off, s));
+    size_t b = 0;
+    workspace_for(ms[i], p, batch, cfg, &b);
+    off += b;
+  }
+  uint64_t col0 = 0;
+  for (int i = 0; i < count; ++i) {
+    WeightView v = pipeline_view(ms[i], p, ws + offs[(size_t)i]);
+    const size_t pb = prep_bytes(ms[i], p);
+    size_t b = 0;
+    workspace_for(ms[i], p, batch, cfg, &b);
+    float* part = reinterpret_cast<float*>(ws + offs[(size_t)i] + pb);
+    UW_HIP(launch_gemm(v, x_dev, batch, y_dev, (int64_t)total_n, (int64_t)col0, cfg, part,
+                       (b - pb) / sizeof(float), s));
+    col0 += v.n;
+  }
+  return UW_OK;
+}
+
+uw_status uw_gemm_bf16(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout layout, const uint16_t* x_dev,
+                       int64_t batch, float* y_dev, const uw_kernel_cfg* cfg, void* stream) {
+  if (!w_dev || !x_dev || !y_dev || n <= 0 || k <= 0 || batch <= 0) return UW_ERR_INVALID;
+  if (layout != UW_LAYOUT_NK && layout != UW_LAYOUT_KN) return UW_ERR_INVALID;
+  if (!aligned16(w_dev) || !aligned16(x_dev)) return UW_ERR_INVALID;
+  const uint64_t cols = layout == UW_LAYOUT_NK ? (uint64_t)k : (uint64_t)n;
+  if (cols % 64 != 0 || k % 8 != 0) return UW_ERR_UNSUPPORTED;
+  WeightView v;
+  std::memset(&v, 0, sizeof(v));
+  v.fmt = kFmtBf16;
+  v.layout = (int)layout;
+  v.n = (uint64_t)n;
+  v.k = (uint64_t)k;
+  v.bf16 = w_dev;
+  const size_t pe = gemm_partial_elems(v, batch, cfg);
+  float* part = nullptr;
+  if (pe) UW_CHECK(dev_alloc(&part, pe * sizeof(float)));   // yardstick path only
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_gemm(v, x_dev, batch, y_dev, n, 0, cfg, part, pe, s);
+  if (part) {
+    (void)hipStreamSynchronize(s);
+    dev_free(part);
+  }
+  return e == hipSuccess ? UW_OK : UW_ERR_DEVICE;
+}
+
+int32_t uw_variant_count(void) { return gemm_variant_count(); }
+
+uw_status uw_sequence_workspace_size(const uw_job* jobs, int count, size_t* bytes) {
+  if (!jobs || count <= 0 || !bytes) return UW_ERR_INVALID;
+  size_t prep = 0, part = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!jobs[i].m) return UW_ERR_INVALID;
+    prep = std::max(prep, prep_bytes(jobs[i].m, jobs[i].pipeline));
+    part = std::max(part, partial_bytes(jobs[i].m, jobs[i].pipeline, jobs[i].batch, &jobs[i].cfg));
+  }
+  *bytes = 2 * prep + part;
+  return UW_OK;
+}
+
+uw_status uw_run_sequence(const uw_job* jobs, int count, int32_t decode_cus, void* ws_dev, size_t ws_bytes,
+                          void* stream) {
+  if (!jobs || count <= 0) return UW_ERR_INVALID;
+  for (int i = 0; i < count; ++i)
+    UW_CHECK(check_matmul_args(jobs[i].m, jobs[i].pipeline, jobs[i].x_dev, jobs[i].batch, jobs[i].y_dev));
+  size_t need = 0;
+  UW_CHECK(uw_sequence_workspace_size(jobs, count, &need));
+  if (need > ws_bytes || (need && !ws_dev) || !aligned16(ws_dev)) return UW_ERR_WORKSPACE;
+  size_t prep = 0;
+  for (int i = 0; i < count; ++i) prep = std::max(prep, prep_bytes(jobs[i].m, jobs[i].pipeline));
+  uint8_t* ws = static_cast<uint8_t*>(ws_dev);
+  uint8_t* bufs[2] = {ws, ws + prep};
+  float* part = reinterpret_cast<float*>(ws + 2 * prep);
+  const size_t part_elems = (need - 2 * prep) / sizeof(float);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (decode_cus <= 0) {   // everything in order on the caller's stream
+    for (int i = 0; i < count; ++i) {
+      const uw_job& j = jobs[i];
+      UW_CHECK(preprocess(j.m, j.pipeline, bufs[0], s));
+      WeightView v = pipeline_view(j.m, j.pipeline, bufs[0]);
+      UW_HIP(launch_gemm(v, j.x_dev, j.batch, j.y_dev, (int64_t)v.n, 0, &j.cfg, part, part_elems, s));
+    }
+    return UW_OK;
+  }
+
+  SplitStreams ss;
+  UW_CHECK(split_streams(decode_cus, &ss));
+  // events: fork, per-buffer "prep done" and "gemm done", join
+  hipEvent_t fork, prep_done[2], gemm_done[2], join_dec, join_gemm;
+  UW_HIP(hipEventCreateWithFlags(&fork, hipEventDisableTiming));
+  for (int b = 0; b < 2; ++b) {
+    UW_HIP(hipEventCreateWithFlags(&prep_done[b], hipEventDisableTiming));
+    UW_HIP(hipEventCreateWithFlags(&gemm_done[b], hipEventDisableTiming));
+  }
+  UW_HIP(hipEventCreateWithFlags(&join_dec, hipEventDisableTiming));
+  UW_HIP(hipEventCreateWithFlags(&join_gemm, hipEventDisableTiming));
+  UW_HIP(hipEventRecord(fork, s));
+  UW_HIP(hipStreamWaitEvent(ss.dec, fork, 0));
+  UW_HIP(hipStreamWaitEvent(ss.gemm, fork, 0));
+  bool used[2] = {false, false};
+  for (int i = 0; i < count; ++i) {
+    const uw_job& j = jobs[i];
+    const int b = i & 1;
+    hipStream_t pre_s = ss.dec;
+    if (j.pipeline != UW_PIPE_PALETTE_DIRECT) {
+      if (used[b]) UW_HIP(hipStreamWaitEvent(ss.dec, gemm_done[b], 0));   // buffer free again
+      UW_CHECK(preprocess(j.m, j.pipeline, bufs[b], pre_s));
+      UW_HIP(hipEventRecord(prep_done[b], pre_s));
+      UW_HIP(hipStreamWaitEvent(ss.gemm, prep_done[b], 0));
+    }
+    WeightView v = pipeline_view(j.m, j.pipeline, bufs[b]);
+    UW_HIP(launch_gemm(v, j.x_dev, j.batch, j.y_dev, (int64_t)v.n, 0, &j.cfg, part, part_elems, ss.gemm));
+    UW_HIP(hipEventRecord(gemm_done[b], ss.gemm));
+    used[b] = true;
+  }
+  UW_HIP(hipEventRecord(join_dec, ss.dec));
+  UW_HIP(hipEventRecord(join_gemm, ss.gemm));
+  UW_HIP(hipStreamWaitEvent(s, join_dec, 0));
+  UW_HIP(hipStreamWaitEvent(s, join_gemm, 0));
+  (void)hipEventDestroy(fork);
+  for (int b = 0; b < 2; ++b) {
+    (void)hipEventDestroy(prep_done[b]);
+    (void)hipEventDestroy(gemm_done[b]);
+  }
+  (void)hipEventDestroy(join_dec);
+  (void)hipEventDestroy(join_gemm);
+  return UW_OK;
+}
+
+uw_status uw_sync_status(const uw_matrix* m, void* stream) {
+  if (!m) return UW_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  UW_HIP(hipStreamSynchronize(s));
+  int flag = 0;
+  UW_HIP(hipMemcpy(&flag, m->corrupt, sizeof(int), hipMemcpyDeviceToHost));
+  if (flag) {
+    UW_HIP(hipMemset(m->corrupt, 0, sizeof(int)));
+    return UW_ERR_CORRUPT;
+  }
+  return UW_OK;
+}
+
+}  // extern "C"

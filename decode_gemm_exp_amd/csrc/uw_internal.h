@@ -1,0 +1,109 @@
+// uw_internal.h -- shared declarations of libunweight's host code and kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/unweight.h"
+
+namespace uw {
+
+constexpr int kGroup = 64;        // weights per verbatim decision
+constexpr int kPal = 16;          // palette entries
+constexpr int kMaxLen = 12;       // longest codeword
+constexpr int kLutBits = 12;      // decode table index width (4096 entries, 16 KB)
+constexpr uint64_t kHeaderBytes = 2304;
+
+// Host-side tables of one matrix (all tiny).
+struct Tables {
+  uint64_t hist[256];
+  uint32_t palette_size;
+  uint8_t palette[kPal];
+  int16_t slot_of[256];           // -1 = not in palette
+  uint64_t coded_count[kPal];
+  uint32_t n_coded;
+  uint8_t code_len[kPal];
+  uint16_t code[kPal];
+};
+
+}  // namespace uw
+
+struct uw_matrix {
+  int device = 0;
+  uint32_t layout = 0, seg_groups = 8;
+  uint64_t rows = 0, cols = 0, numel = 0, groups = 0, segments = 0, flag_words = 0;
+  uint64_t V = 0, W = 0, code_bits = 0;
+  uw::Tables t{};
+  // device sections
+  uint8_t* sm = nullptr;          // numel
+  uint32_t* vflags = nullptr;     // flag_words
+  uint32_t* vrank = nullptr;      // flag_words
+  uint8_t* vexp = nullptr;        // 64 * V (may be null when V == 0)
+  uint32_t* seg_off = nullptr;    // segments + 1
+  uint32_t* stream = nullptr;     // W + 2
+  uint32_t* lut = nullptr;        // 4096 decode entries
+  uint8_t* pidx = nullptr;        // resident palette indices (numel / 2) or null
+  int* corrupt = nullptr;         // device flag set by decoders
+};
+
+namespace uw {
+
+// ---- tables.cpp --------------------------------------------------------------
+void choose_palette(Tables& t);                        // from t.hist
+bool limited_lengths(const uint64_t* w, int n, int lmax, uint8_t* len);
+void assign_codes(Tables& t);                          // from code_len
+void build_decode_lut(const Tables& t, uint32_t* lut4096);
+
+// ---- kernel launchers (compress.hip, decode.hip, gemm*.hip) ------------------
+hipError_t launch_histogram(const uint16_t* w, uint64_t numel, uint32_t* hist, hipStream_t s);
+hipError_t launch_flags(const uint16_t* w, uint64_t numel, uint64_t groups, const uint8_t* slot_tab,
+                        uint8_t* sm, uint32_t* vflags, uint32_t* coded, hipStream_t s);
+hipError_t launch_rank_scan(const uint32_t* vflags, uint64_t words, uint32_t* vrank,
+                            uint64_t* total, hipStream_t s);
+hipError_t launch_segment_bits(const uint16_t* w, uint64_t groups, uint32_t seg_groups,
+                               uint64_t segments, const uint8_t* len_tab, const uint32_t* vflags,
+                               uint32_t* seg_words, hipStream_t s);
+hipError_t launch_offsets_scan(const uint32_t* seg_words, uint64_t segments, uint32_t* seg_off,
+                               hipStream_t s);
+hipError_t launch_encode(const uint16_t* w, uint64_t groups, uint32_t seg_groups, uint64_t segments,
+                         const uint32_t* codebook, const uint32_t* vflags, const uint32_t* vrank,
+                         const uint32_t* seg_off, uint32_t* stream, uint8_t* vexp, hipStream_t s);
+
+enum DecodeMode { kDecodeNibble = 0, kDecodeExponent = 1, kDecodeFull = 2 };
+struct DecodeArgs {
+  const uint32_t* stream; uint64_t stream_words;   // including slack
+  const uint32_t* seg_off;
+  const uint32_t* vflags; const uint32_t* vrank; const uint8_t* vexp;
+  const uint8_t* sm;
+  const uint32_t* lut;
+  uint32_t pal[4];                                  // palette bytes
+  uint64_t len_pack;                                // 4-bit code length per slot
+  uint64_t groups, segments; uint32_t seg_groups;
+  void* out;
+  int* corrupt;
+};
+hipError_t launch_decode(const DecodeArgs& a, int mode, hipStream_t s);
+
+// weight formats seen by the GEMM kernels
+enum WFmt { kFmtBf16 = 0, kFmtExp = 1, kFmtPal = 2 };
+struct WeightView {
+  int fmt;
+  int layout;                       // 0 = stored [N][K], 1 = stored [K][N]
+  uint64_t n, k;                    // logical
+  const uint16_t* bf16;             // kFmtBf16
+  const uint8_t* sm;                // kFmtExp / kFmtPal
+  const uint8_t* ex;                // kFmtExp: exponent bytes
+  const uint8_t* pidx;              // kFmtPal
+  const uint32_t* vflags; const uint32_t* vrank; const uint8_t* vexp;   // kFmtPal
+  uint32_t pal[4];
+};
+// y[:, col0 : col0+n] of a row-major [batch][ldy] output
+hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, float* y,
+                       int64_t ldy, int64_t col0, const uw_kernel_cfg* cfg, float* partial,
+                       size_t partial_elems, hipStream_t s);
+size_t gemm_partial_elems(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg);
+int gemm_variant_count();
+
+}  // namespace uw

@@ -1,0 +1,282 @@
+"""Thin ctypes binding of libunweight.so (include/unweight.h).
+
+Argument marshalling only: every step of the codec and the GEMMs runs in the
+library's HIP kernels.  torch tensors are accepted for device buffers and
+their ``data_ptr()`` is passed through; streams default to torch's current
+stream.  Importing this module fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libunweight.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: run __graft_entry__.build() (hipcc for gfx950) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+UW_OK = 0
+STATUS = {0: "ok", -1: "invalid", -2: "unsupported", -3: "nomem", -4: "device", -5: "corrupt",
+          -6: "state", -7: "workspace"}
+PIPE_FULL, PIPE_EXPONENT, PIPE_PALETTE_TRANSCODE, PIPE_PALETTE_DIRECT = 0, 1, 2, 3
+PIPELINES = {"full": 0, "exponent": 1, "transcode": 2, "direct": 3}
+LAYOUT_NK, LAYOUT_KN = 0, 1
+
+
+class UwError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({status})")
+        self.status = status
+
+
+class uw_compress_opts(ctypes.Structure):
+    _fields_ = [("seg_groups", ctypes.c_uint32), ("flags", ctypes.c_uint32)]
+
+
+class uw_kernel_cfg(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("split_k", ctypes.c_int32), ("decode_cus", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class uw_info(ctypes.Structure):
+    _fields_ = [("layout", ctypes.c_uint32), ("seg_groups", ctypes.c_uint32),
+                ("rows", ctypes.c_uint64), ("cols", ctypes.c_uint64), ("n", ctypes.c_uint64),
+                ("k", ctypes.c_uint64), ("numel", ctypes.c_uint64), ("groups", ctypes.c_uint64),
+                ("segments", ctypes.c_uint64), ("palette_size", ctypes.c_uint32), ("n_coded", ctypes.c_uint32),
+                ("palette", ctypes.c_uint8 * 16), ("code_len", ctypes.c_uint8 * 16),
+                ("code", ctypes.c_uint16 * 16), ("hist", ctypes.c_uint64 * 256),
+                ("coded_count", ctypes.c_uint64 * 16), ("verbatim_groups", ctypes.c_uint64),
+                ("stream_words", ctypes.c_uint64), ("code_bits", ctypes.c_uint64),
+                ("compressed_bytes", ctypes.c_uint64), ("export_bytes", ctypes.c_uint64),
+                ("bits_per_weight", ctypes.c_double), ("has_stream", ctypes.c_int32),
+                ("has_palette_idx", ctypes.c_int32)]
+
+
+class uw_job(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_void_p), ("pipeline", ctypes.c_int32), ("cfg", uw_kernel_cfg),
+                ("x_dev", ctypes.c_void_p), ("y_dev", ctypes.c_void_p), ("batch", ctypes.c_int64)]
+
+
+_vp, _i64, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+_SIGS = {
+    "uw_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "uw_version": (ctypes.c_uint32, []),
+    "uw_compress": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, ctypes.POINTER(uw_compress_opts), _vp,
+                                   ctypes.POINTER(_vp)]),
+    "uw_get_info": (ctypes.c_int, [_vp, ctypes.POINTER(uw_info)]),
+    "uw_export": (ctypes.c_int, [_vp, _vp, _sz, ctypes.POINTER(_sz)]),
+    "uw_import": (ctypes.c_int, [_vp, _sz, _vp, ctypes.POINTER(_vp)]),
+    "uw_free": (None, [_vp]),
+    "uw_decode_full": (ctypes.c_int, [_vp, _vp, _vp]),
+    "uw_decode_exponent": (ctypes.c_int, [_vp, _vp, _vp]),
+    "uw_transcode_palette": (ctypes.c_int, [_vp, _vp, _vp]),
+    "uw_drop_stream": (ctypes.c_int, [_vp, _vp]),
+    "uw_workspace_size": (ctypes.c_int, [_vp, ctypes.c_int, _i64, ctypes.POINTER(_sz)]),
+    "uw_matmul_reconstruct": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _vp, _vp, _sz,
+                                             ctypes.POINTER(uw_kernel_cfg), _vp]),
+    "uw_matmul_reconstruct_grouped": (ctypes.c_int, [ctypes.POINTER(_vp), ctypes.c_int, ctypes.c_int, _vp, _i64,
+                                                     _vp, _vp, _sz, ctypes.POINTER(uw_kernel_cfg), _vp]),
+    "uw_gemm_bf16": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, _vp, _i64, _vp,
+                                    ctypes.POINTER(uw_kernel_cfg), _vp]),
+    "uw_variant_count": (ctypes.c_int32, []),
+    "uw_sequence_workspace_size": (ctypes.c_int, [ctypes.POINTER(uw_job), ctypes.c_int, ctypes.POINTER(_sz)]),
+    "uw_run_sequence": (ctypes.c_int, [ctypes.POINTER(uw_job), ctypes.c_int, ctypes.c_int32, _vp, _sz, _vp]),
+    "uw_sync_status": (ctypes.c_int, [_vp, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+def _check(st: int, what: str) -> None:
+    if st != UW_OK:
+        raise UwError(st, what)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        return t.data_ptr()
+    return int(t)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _cfg(cfg) -> ctypes.POINTER(uw_kernel_cfg) | None:
+    if cfg is None:
+        return None
+    if isinstance(cfg, dict):
+        c = uw_kernel_cfg(cfg.get("variant", 0), cfg.get("split_k", 0), cfg.get("decode_cus", 0), 0)
+    else:
+        c = cfg
+    return ctypes.pointer(c)
+
+
+def version() -> int:
+    return _lib.uw_version()
+
+
+def variant_count() -> int:
+    return _lib.uw_variant_count()
+
+
+class Matrix:
+    """Owns one uw_matrix handle."""
+
+    def __init__(self, handle: int):
+        self.handle = ctypes.c_void_p(handle)
+
+    def info(self) -> uw_info:
+        inf = uw_info()
+        _check(_lib.uw_get_info(self.handle, ctypes.byref(inf)), "uw_get_info")
+        return inf
+
+    def free(self) -> None:
+        if self.handle and self.handle.value:
+            _lib.uw_free(self.handle)
+            self.handle = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def uw_compress(w_dev: torch.Tensor, n: int, k: int, layout: int = LAYOUT_NK, seg_groups: int = 8,
+                stream=None) -> Matrix:
+    opts = uw_compress_opts(seg_groups, 0)
+    h = ctypes.c_void_p()
+    _check(_lib.uw_compress(_ptr(w_dev), n, k, layout, ctypes.byref(opts), _stream(stream), ctypes.byref(h)),
+           "uw_compress")
+    return Matrix(h.value)
+
+
+def uw_get_info(m: Matrix) -> uw_info:
+    return m.info()
+
+
+def uw_export(m: Matrix) -> bytes:
+    n = ctypes.c_size_t()
+    _check(_lib.uw_export(m.handle, None, 0, ctypes.byref(n)), "uw_export(size)")
+    buf = np.zeros(n.value, dtype=np.uint8)
+    _check(_lib.uw_export(m.handle, buf.ctypes.data, n.value, ctypes.byref(n)), "uw_export")
+    return buf.tobytes()
+
+
+def uw_import(blob: bytes, stream=None) -> Matrix:
+    arr = np.frombuffer(blob, dtype=np.uint8)
+    h = ctypes.c_void_p()
+    _check(_lib.uw_import(arr.ctypes.data, len(blob), _stream(stream), ctypes.byref(h)), "uw_import")
+    return Matrix(h.value)
+
+
+def uw_import_status(blob: bytes) -> int:
+    """Status of uw_import without keeping the handle (validation tests)."""
+    arr = np.frombuffer(blob, dtype=np.uint8)
+    h = ctypes.c_void_p()
+    st = _lib.uw_import(arr.ctypes.data if len(blob) else None, len(blob), None, ctypes.byref(h))
+    if h.value:
+        _lib.uw_free(h)
+    return st
+
+
+def uw_free(m: Matrix) -> None:
+    m.free()
+
+
+def uw_decode_full(m: Matrix, out: torch.Tensor, stream=None) -> None:
+    _check(_lib.uw_decode_full(m.handle, _ptr(out), _stream(stream)), "uw_decode_full")
+
+
+def uw_decode_exponent(m: Matrix, out: torch.Tensor, stream=None) -> None:
+    _check(_lib.uw_decode_exponent(m.handle, _ptr(out), _stream(stream)), "uw_decode_exponent")
+
+
+def uw_transcode_palette(m: Matrix, out: torch.Tensor | None, stream=None) -> None:
+    _check(_lib.uw_transcode_palette(m.handle, _ptr(out), _stream(stream)), "uw_transcode_palette")
+
+
+def uw_drop_stream(m: Matrix, stream=None) -> None:
+    _check(_lib.uw_drop_stream(m.handle, _stream(stream)), "uw_drop_stream")
+
+
+def uw_workspace_size(m: Matrix, pipeline: int, batch: int) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.uw_workspace_size(m.handle, pipeline, batch, ctypes.byref(n)), "uw_workspace_size")
+    return n.value
+
+
+def uw_matmul_reconstruct(m: Matrix, pipeline: int, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor | None,
+                          cfg=None, stream=None) -> None:
+    batch = x.shape[0]
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(_lib.uw_matmul_reconstruct(m.handle, pipeline, _ptr(x), batch, _ptr(y), _ptr(ws), nbytes, _cfg(cfg),
+                                      _stream(stream)), "uw_matmul_reconstruct")
+
+
+def uw_matmul_reconstruct_grouped(ms, pipeline: int, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor | None,
+                                  cfg=None, stream=None) -> None:
+    arr = (ctypes.c_void_p * len(ms))(*[m.handle.value for m in ms])
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(_lib.uw_matmul_reconstruct_grouped(arr, len(ms), pipeline, _ptr(x), x.shape[0], _ptr(y), _ptr(ws),
+                                              nbytes, _cfg(cfg), _stream(stream)), "uw_matmul_reconstruct_grouped")
+
+
+def uw_gemm_bf16(w: torch.Tensor, n: int, k: int, layout: int, x: torch.Tensor, y: torch.Tensor, cfg=None,
+                 stream=None) -> None:
+    _check(_lib.uw_gemm_bf16(_ptr(w), n, k, layout, _ptr(x), x.shape[0], _ptr(y), _cfg(cfg), _stream(stream)),
+           "uw_gemm_bf16")
+
+
+@dataclass
+class Job:
+    m: Matrix
+    pipeline: int
+    x: torch.Tensor
+    y: torch.Tensor
+    cfg: dict | None = None
+
+
+def _jobs(jobs) -> ctypes.Array:
+    arr = (uw_job * len(jobs))()
+    for i, j in enumerate(jobs):
+        c = j.cfg or {}
+        arr[i] = uw_job(j.m.handle.value, j.pipeline,
+                        uw_kernel_cfg(c.get("variant", 0), c.get("split_k", 0), c.get("decode_cus", 0), 0),
+                        _ptr(j.x), _ptr(j.y), j.x.shape[0])
+    return arr
+
+
+def uw_sequence_workspace_size(jobs) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.uw_sequence_workspace_size(_jobs(jobs), len(jobs), ctypes.byref(n)), "uw_sequence_workspace_size")
+    return n.value
+
+
+def uw_run_sequence(jobs, decode_cus: int, ws: torch.Tensor | None, stream=None, _arr=None) -> None:
+    arr = _arr if _arr is not None else _jobs(jobs)
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(_lib.uw_run_sequence(arr, len(jobs), decode_cus, _ptr(ws), nbytes, _stream(stream)),
+           "uw_run_sequence")
+
+
+def uw_sync_status(m: Matrix, stream=None) -> int:
+    return _lib.uw_sync_status(m.handle, _stream(stream))
