@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Benchmark of the lossless BF16 MLP-weight hot path on one MI355X.
+
+One step = the four pipelines of the method on the Llama-3.1-8B gate
+projection (14336 x 4096 bf16, N(0, 0.02), 0.05 % outliers x 2^10) at batch 1:
+  full       : Huffman decode to BF16 in HBM   + dense GEMV
+  exponent   : exponent-only decode            + reconstructive GEMV
+  transcode  : palette transcode               + reconstructive GEMV
+  direct     : reconstructive GEMV from resident palette indices
+The compressed matrices are resident in HBM before timing starts; several
+compressed copies are rotated so that the 256 MB Infinity Cache cannot hold
+the inputs of consecutive steps.  ``value`` is decoded-weight throughput:
+bf16 bytes of weights delivered to the GEMVs per second (4 x 2 x numel per
+step).  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decoded weight GB/s + fused MLP GEMM TFLOP/s (batch 1..1024), % roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+PIPE_NAMES = ("full", "exponent", "transcode", "direct")
+# kernel symbol (as rocprofv3 prints it, prefix) for each timed stage
+STAGE_KERNELS = {
+    "decode_full": "k_decode<2>", "gemv_full": "k_gemv_nk<0, 1>",
+    "decode_exponent": "k_decode<1>", "gemv_exponent": "k_gemv_nk<1, 1>",
+    "transcode": "k_decode<0>", "gemv_transcode": "k_gemv_nk<2, 1>",
+    "gemv_direct": "k_gemv_nk<2, 1>",
+}
+STAGE_SOURCES = {"decode": ["decode.hip", "uw_internal.h"], "gemv": ["gemm.hip", "rebuild.h", "uw_internal.h"]}
+
+
+def source_sha(stage: str) -> str:
+    h = hashlib.sha256()
+    for f in STAGE_SOURCES["decode" if stage.startswith(("decode", "transcode")) else "gemv"]:
+        with open(os.path.join(ROOT, "decode_gemm_exp_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(info, stage: str, batch: int = 1) -> float:
+    """Compulsory HBM bytes of one launch of a stage (compressed inputs +
+    outputs; not the dense work avoided)."""
+    M = info.numel
+    Z = 4 * (info.stream_words + 2)
+    O = 4 * (info.segments + 1)
+    Aux = 8 * ((info.groups + 31) // 32)
+    Vb = 64 * info.verbatim_groups
+    X = 2 * batch * info.k
+    Y = 4 * batch * info.n
+    return {
+        "decode_full": Z + O + Aux + Vb + M + 2 * M,
+        "decode_exponent": Z + O + Aux + Vb + M,
+        "transcode": Z + O + Aux + M / 2,
+        "gemv_full": 2 * M + X + Y,
+        "gemv_exponent": 2 * M + X + Y,
+        "gemv_transcode": 1.5 * M + Aux + Vb + X + Y,
+        "gemv_direct": 1.5 * M + Aux + Vb + X + Y,
+    }[stage]
+
+
+def load_traffic(stage: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic_gate8b.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    k = rec.get("kernels", {}).get(stage)
+    if not k or k.get("source_sha") != source_sha(stage):
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w_np, x_np, min_seconds: float = 10.0):
+    """The oracle, as it stands, on the same matrix: 3 decodes + 4 fp64 GEMVs
+    per step, repeated whole steps until min_seconds have passed."""
+    import threadpoolctl
+
+    from oracle import oracle
+    om = oracle.compress(w_np, seg_groups=4)
+    steps = 0
+    t0 = time.perf_counter()
+    with threadpoolctl.threadpool_limits(1):
+        while True:
+            st1, full = om.decode_full()
+            st2, e = om.decode_exponent()
+            st3, idx = om.transcode()
+            assert st1 == st2 == st3 == 0
+            for _ in range(4):
+                oracle.gemm_ref(x_np, full.reshape(w_np.shape), 0)
+            steps += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": round(4 * 2 * w_np.size * steps / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"full {w_np.shape[0]}x{w_np.shape[1]} matrix, {steps} whole steps "
+                      f"(decode_full + decode_exponent + transcode + 4 fp64 GEMVs, single thread), "
+                      f"{dt:.1f} s"}
+
+
+def extras(uw, synth, torch, dev, iters: int = 10):
+    """Short measurements of the larger-batch rows: fused gate+up (2 x
+    14336x4096) and the transposed down projection (stored [14336][4096])."""
+    out = {}
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    wl = synth.WORKLOADS["gateup8b"]
+    ms = []
+    for i in range(2):
+        _, n, k, layout = wl.mats[i]
+        w = synth.workload_weights(wl, i, device=dev)
+        m = uw.uw_compress(w, n, k, layout)
+        uw.uw_transcode_palette(m, None)
+        ms.append(m)
+        del w
+    N = sum(m.info().n for m in ms)
+    for b in wl.batches:
+        x = synth.activations(b, 4096, seed=wl.seed, device=dev)
+        y = torch.empty((b, N), dtype=torch.float32, device=dev)
+        for p in (2, 3):
+            ws = torch.empty(max(16, sum(uw.uw_workspace_size(m, p, b) for m in ms)), dtype=torch.uint8,
+                             device=dev)
+            for _ in range(3):
+                uw.uw_matmul_reconstruct_grouped(ms, p, x, y, ws)
+            s, e = ev(), ev()
+            s.record()
+            for _ in range(iters):
+                uw.uw_matmul_reconstruct_grouped(ms, p, x, y, ws)
+            e.record()
+            torch.cuda.synchronize()
+            t = s.elapsed_time(e) / iters / 1e3
+            flops = 2.0 * b * N * 4096
+            out[f"gateup8b_b{b}_{PIPE_NAMES[p]}"] = {"us": round(t * 1e6, 2),
+                                                   "tflops": round(flops / t / 1e12, 3),
+                                                   "decoded_gbs": round(2 * 2 * 14336 * 4096 / t / 1e9, 1)}
+    del ms
+    wl = synth.WORKLOADS["down8b"]
+    _, n, k, layout = wl.mats[0]
+    w = synth.workload_weights(wl, 0, device=dev)
+    m = uw.uw_compress(w, n, k, layout)
+    uw.uw_transcode_palette(m, None)
+    del w
+    for b in wl.batches:
+        x = synth.activations(b, k, seed=wl.seed, device=dev)
+        y = torch.empty((b, n), dtype=torch.float32, device=dev)
+        for p in (1, 2, 3):
+            ws = torch.empty(max(16, uw.uw_workspace_size(m, p, b)), dtype=torch.uint8, device=dev)
+            for _ in range(2):
+                uw.uw_matmul_reconstruct(m, p, x, y, ws)
+            s, e = ev(), ev()
+            s.record()
+            for _ in range(iters):
+                uw.uw_matmul_reconstruct(m, p, x, y, ws)
+            e.record()
+            torch.cuda.synchronize()
+            t = s.elapsed_time(e) / iters / 1e3
+            flops = 2.0 * b * n * k
+            out[f"down8b_b{b}_{PIPE_NAMES[p]}"] = {"us": round(t * 1e6, 2), "tflops": round(flops / t / 1e12, 2),
+                                                 "mfma_frac": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    return out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rotate", type=int, default=10, help="compressed copies cycled through")
+    ap.add_argument("--seg-groups", type=int, default=4, help="groups per bitstream segment")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-extras", action="store_true", help="skip the larger-batch rows")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="run a plain device copy of this size first (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; the path shards per matrix "
+                                   "(see the design notes) but no multi-GPU run is made", "n_gpus": args.gpus}))
+        return 2
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    from decode_gemm_exp_amd import synth, uw
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    print("bench: building inputs", file=sys.stderr, flush=True)
+
+    if args.copy_calibration_mb:
+        nb = args.copy_calibration_mb << 20
+        a = torch.empty(nb, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    wl = synth.WORKLOADS["gate8b"]
+    _, n, k, layout = wl.mats[0]
+    w = synth.workload_weights(wl, 0, device=dev)
+    x = synth.activations(1, k, seed=wl.seed, device=dev)
+    mats = []
+    for _ in range(args.rotate):
+        m = uw.uw_compress(w, n, k, layout, seg_groups=args.seg_groups)
+        uw.uw_transcode_palette(m, None)
+        mats.append(m)
+    torch.cuda.synchronize()
+    info = mats[0].info()
+    w_np = synth.bits_numpy(w) if not args.no_cpu else None
+    x_np = synth.bits_numpy(x) if not args.no_cpu else None
+    del w
+
+    numel = info.numel
+    ws_bf16 = torch.empty(numel, dtype=torch.int16, device=dev)
+    ws_e = torch.empty(numel, dtype=torch.uint8, device=dev)
+    ws_p = torch.empty(numel // 2, dtype=torch.uint8, device=dev)
+    ys = [torch.empty((1, n), dtype=torch.float32, device=dev) for _ in range(4)]
+    part = torch.empty(16, dtype=torch.uint8, device=dev)   # NK GEMV needs no partials
+    stages = ["decode_full", "gemv_full", "decode_exponent", "gemv_exponent", "transcode", "gemv_transcode",
+              "gemv_direct"]
+    stream = torch.cuda.current_stream()
+
+    def run_stage(st, m):
+        if st == "decode_full":
+            uw.uw_decode_full(m, ws_bf16, stream)
+        elif st == "gemv_full":
+            uw.uw_matmul_stage(m, 0, ws_bf16, x, ys[0], part, stream=stream)
+        elif st == "decode_exponent":
+            uw.uw_decode_exponent(m, ws_e, stream)
+        elif st == "gemv_exponent":
+            uw.uw_matmul_stage(m, 1, ws_e, x, ys[1], part, stream=stream)
+        elif st == "transcode":
+            uw.uw_transcode_palette(m, ws_p, stream)
+        elif st == "gemv_transcode":
+            uw.uw_matmul_stage(m, 2, ws_p, x, ys[2], part, stream=stream)
+        else:
+            uw.uw_matmul_stage(m, 3, None, x, ys[3], part, stream=stream)
+
+    def step(i, events=None):
+        m = mats[i % len(mats)]
+        for j, st in enumerate(stages):
+            if events is not None:
+                events[j][0].record(stream)
+            run_stage(st, m)
+            if events is not None:
+                events[j][1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print("bench: timing", file=sys.stderr, flush=True)
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in stages]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for m in mats:
+        assert uw.uw_sync_status(m) == 0, "decoder reported corrupt data"
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_us = {st: 1e3 * sum(evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(args.steps)) / args.steps
+                for j, st in enumerate(stages)}
+    gpu_step_us = sum(stage_us.values())
+    kernels = {}
+    for st in stages:
+        t = stage_us[st] * 1e-6
+        ab = algorithmic_bytes(info, st)
+        kernels[st] = {"kernel": STAGE_KERNELS[st], "us": round(stage_us[st], 2), "alg_bytes": int(ab),
+                       "gbs": round(ab / t / 1e9, 1), "hbm_frac": round(ab / t / 1e9 / HBM_PEAK_GBS, 4)}
+    pipes = {}
+    for p, (pre, gem) in zip(PIPE_NAMES, [("decode_full", "gemv_full"), ("decode_exponent", "gemv_exponent"),
+                                          ("transcode", "gemv_transcode"), (None, "gemv_direct")]):
+        t = (stage_us[pre] if pre else 0.0) + stage_us[gem]
+        pb = (algorithmic_bytes(info, pre) if pre else 0.0) + algorithmic_bytes(info, gem)
+        pipes[p] = {"us": round(t, 2), "decoded_gbs": round(2 * numel / (t * 1e-6) / 1e9, 1),
+                    "hbm_frac": round(pb / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    dom = max(stages, key=lambda s: stage_us[s])
+    dom_t = stage_us[dom] * 1e-6
+    dom_b = algorithmic_bytes(info, dom)
+    roofline = {"bound": "hbm", "achieved": round(dom_b / dom_t / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom_b / dom_t / 1e9 / HBM_PEAK_GBS, 4), "traffic": load_traffic(dom),
+                "kernel": STAGE_KERNELS[dom], "stage": dom, "alg_bytes_per_launch": int(dom_b),
+                "avg_launch_us": round(stage_us[dom], 2)}
+    value = 4 * 2 * numel / (ms_per_step * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "gate8b: Llama-3.1-8B gate projection 14336x4096 bf16 N(0,0.02), 0.05% "
+                               "outliers x2^10, batch 1, pipelines full/exponent/transcode/direct",
+                   "batch": 1, "rotated_copies": args.rotate, "seg_groups": args.seg_groups, "bits_per_weight": round(info.bits_per_weight, 3),
+                   "verbatim_groups": int(info.verbatim_groups), "parallelism": "single GPU"},
+        "gpu_step_us": round(gpu_step_us, 2),
+        "pipelines": pipes, "kernels": kernels, "roofline": roofline,
+    }
+    if not args.no_extras:
+        print("bench: larger-batch rows", file=sys.stderr, flush=True)
+        del mats
+        torch.cuda.empty_cache()
+        res["extras"] = extras(uw, synth, torch, dev)
+    if not args.no_cpu:
+        print("bench: oracle cpu baseline", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w_np, x_np)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

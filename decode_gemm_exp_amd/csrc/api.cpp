@@ -231,6 +231,7 @@ DecodeArgs decode_args(const uw_matrix* m, void* out) {
   a.groups = m->groups;
   a.segments = m->segments;
   a.seg_groups = m->seg_groups;
+  a.wave_span = m->wave_span;
   a.out = out;
   a.corrupt = m->corrupt;
   return a;
@@ -297,7 +298,7 @@ uw_status uw_compress(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout lay
   *out = nullptr;
   if (!w_dev || n <= 0 || k <= 0 || (layout != UW_LAYOUT_NK && layout != UW_LAYOUT_KN)) return UW_ERR_INVALID;
   if (!aligned16(w_dev)) return UW_ERR_INVALID;
-  const uint32_t sg = (opts && opts->seg_groups) ? opts->seg_groups : 8u;
+  const uint32_t sg = (opts && opts->seg_groups) ? opts->seg_groups : 4u;
   if (!valid_seg_groups(sg) || (opts && opts->flags)) return UW_ERR_INVALID;
   const uint64_t rows = layout == UW_LAYOUT_NK ? (uint64_t)n : (uint64_t)k;
   const uint64_t cols = layout == UW_LAYOUT_NK ? (uint64_t)k : (uint64_t)n;
@@ -378,10 +379,14 @@ uw_status uw_compress(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout lay
   UW_HIP(hipMemsetAsync(d_seg, 0, 4 * m->segments, s));
   UW_HIP(launch_segment_bits(w_dev, m->groups, sg, m->segments, d_len, m->vflags, d_seg, s));
   UW_HIP(launch_offsets_scan(d_seg, m->segments, m->seg_off, s));
-  uint32_t W32 = 0;
+  UW_HIP(hipMemsetAsync(d_coded, 0, 4, s));
+  UW_HIP(launch_wave_span(m->seg_off, m->segments, d_coded, s));
+  uint32_t W32 = 0, span32 = 0;
   UW_HIP(hipMemcpyAsync(&W32, m->seg_off + m->segments, 4, hipMemcpyDeviceToHost, s));
+  UW_HIP(hipMemcpyAsync(&span32, d_coded, 4, hipMemcpyDeviceToHost, s));
   UW_HIP(hipStreamSynchronize(s));
   m->W = W32;
+  m->wave_span = span32;
 
   // 4. encode
   const uint64_t sw = stream_alloc_words(m->W);
@@ -546,6 +551,10 @@ uw_status uw_import(const void* host_blob, size_t nbytes, void* stream, uw_matri
   m->V = tmp.V;
   m->W = tmp.W;
   m->t = tmp.t;
+  for (uint64_t w = 0; w * 64 < m->segments; ++w) {
+    const uint64_t e = std::min<uint64_t>((w + 1) * 64, m->segments);
+    m->wave_span = std::max<uint32_t>(m->wave_span, so[e] - (so[w * 64] & ~3u));
+  }
   m->code_bits = 0;
   for (int i = 0; i < kPal; ++i) m->code_bits += m->t.coded_count[i] * m->t.code_len[i];
   const uint64_t sw = stream_alloc_words(m->W);
@@ -637,6 +646,25 @@ uw_status uw_matmul_reconstruct(const uw_matrix* m, uw_pipeline p, const uint16_
   const size_t pb = prep_bytes(m, p);
   float* part = reinterpret_cast<float*>(ws + pb);
   UW_HIP(launch_gemm(v, x_dev, batch, y_dev, (int64_t)v.n, 0, cfg, part, (need - pb) / sizeof(float), s));
+  return UW_OK;
+}
+
+uw_status uw_matmul_stage(const uw_matrix* m, uw_pipeline p, const void* prep_dev, const uint16_t* x_dev,
+                          int64_t batch, float* y_dev, void* ws_dev, size_t ws_bytes, const uw_kernel_cfg* cfg,
+                          void* stream) {
+  if (!m || !x_dev || !y_dev || batch <= 0 || p < UW_PIPE_FULL || p > UW_PIPE_PALETTE_DIRECT) return UW_ERR_INVALID;
+  if (!aligned16(x_dev) || (reinterpret_cast<uintptr_t>(y_dev) & 3u)) return UW_ERR_INVALID;
+  if (logical_k(m) % 8 != 0) return UW_ERR_UNSUPPORTED;
+  if (p == UW_PIPE_PALETTE_DIRECT) {
+    if (!m->pidx) return UW_ERR_STATE;
+  } else if (!prep_dev || !aligned16(prep_dev)) {
+    return UW_ERR_INVALID;
+  }
+  const size_t need = partial_bytes(m, p, batch, cfg);
+  if (need > ws_bytes || (need && !ws_dev) || !aligned16(ws_dev)) return UW_ERR_WORKSPACE;
+  WeightView v = pipeline_view(m, p, prep_dev);
+  UW_HIP(launch_gemm(v, x_dev, batch, y_dev, (int64_t)v.n, 0, cfg, static_cast<float*>(ws_dev),
+                     need / sizeof(float), static_cast<hipStream_t>(stream)));
   return UW_OK;
 }
 

@@ -263,6 +263,18 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ w, 
   }
 }
 
+// Largest stream span of any decoder wave (64 consecutive segments), counted
+// from the 4-word boundary below its first word: sizes the decoder's LDS copy.
+__global__ __launch_bounds__(256) void k_wave_span(const uint32_t* __restrict__ seg_off, uint64_t segments,
+                                                   uint32_t* __restrict__ out) {
+  const uint64_t waves = (segments + 63) / 64;
+  for (uint64_t w = blockIdx.x * 256ull + threadIdx.x; w < waves; w += (uint64_t)gridDim.x * 256ull) {
+    const uint64_t e = min((w + 1) * 64, segments);
+    const uint32_t span = seg_off[e] - (seg_off[w * 64] & ~3u);
+    atomicMax(out, span);
+  }
+}
+
 unsigned grid_for(uint64_t items, unsigned per_block, unsigned cap = 65535u * 4u) {
   uint64_t b = (items + per_block - 1) / per_block;
   if (b == 0) b = 1;
@@ -309,6 +321,12 @@ hipError_t launch_segment_bits(const uint16_t* w, uint64_t groups, uint32_t seg_
 hipError_t launch_offsets_scan(const uint32_t* seg_words, uint64_t segments, uint32_t* seg_off,
                                hipStream_t s) {
   hipLaunchKernelGGL(k_offsets_scan, dim3(1), dim3(1024), 0, s, seg_words, segments, seg_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_wave_span(const uint32_t* seg_off, uint64_t segments, uint32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_wave_span, dim3(grid_for((segments + 63) / 64, 256, 1024)), dim3(256), 0, s, seg_off,
+                     segments, out);
   return hipGetLastError();
 }
 

@@ -10,16 +10,27 @@
 //
 // Work split.  One lane owns one segment (seg_groups consecutive groups whose
 // codes start on a word boundary), so every lane knows where its output goes
-// without any search.  A lane keeps a 64-bit MSB-aligned bit buffer fed from a
-// prefetched 16-byte chunk of the stream (raw buffer loads: reads past the
-// stream return zero instead of faulting), looks up 12-bit windows in the
-// LDS table (each entry yields up to six whole codewords), and appends the
-// decoded slot nibbles to a 16-nibble accumulator.  Every 8 nibbles go to a
-// per-wave LDS stage.  After each group step the wave rewrites the stage
-// cooperatively: 64 groups x 64 weights become coalesced 16-byte stores, the
-// palette lookup (v_perm on the 16 palette bytes) and the BF16 rebuild
-// happen there with every lane active, and verbatim groups are filled from
-// the side section in the same pass.
+// without any search.
+//
+// Decode loop (per lane).  A 64-bit MSB-aligned bit buffer is fed from a
+// queue of three prefetched 16-byte stream chunks (raw buffer loads: reads
+// past the stream return zero instead of faulting), so a chunk is requested
+// about 8 words before it is needed.  Each step refills 32 bits if fewer than
+// 24 remain and then looks up two 12-bit windows in the LDS table; an entry
+// gives up to six whole codewords (their palette slots as nibbles) and their
+// total length.  Slots accumulate in a 16-nibble register and leave 8 at a
+// time into the wave's LDS stage.  A lane decodes all coded groups of a round
+// (up to 8 groups) in one loop, so lanes only meet at the end of a round.
+//
+// Copy-out (per wave, every lane active).  The 64 segments of a wave write a
+// contiguous output range, swept 16 weights per lane per step: 16-byte
+// coalesced stores, verbatim groups taken from the side section, the palette
+// lookup (v_perm over the 16 palette bytes) and the BF16 rebuild done here.
+// The owner lane's verbatim flags and rank reach the copying lane through a
+// cross-lane shuffle.  Stage word f of lane L sits at f * 64 + (L ^ f), which
+// keeps both the per-lane writes and the per-owner reads on distinct banks.
+#include <cstdlib>
+
 #include "uw_internal.h"
 
 namespace uw {
@@ -27,9 +38,12 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int kRound = 8;                      // groups per decode round
+constexpr int kStageWords = kRound * 8;        // 8 slot nibbles per word, 64 per group
+
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 __device__ __forceinline__ uint4 load_chunk(__amdgpu_buffer_rsrc_t r, uint32_t word) {
-  typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
   u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(word * 4u), 0, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
@@ -52,150 +66,181 @@ __device__ __forceinline__ uint32_t slots_to_exp(uint32_t sel, uint32_t p0, uint
   return (hi & m) | (lo & ~m);
 }
 
-// 2 (sign+mantissa, exponent) byte pairs interleaved as bytes [s0 e0 s1 e1]
-// -> two packed bf16: sign to bit 15, exponent to bits 14..7, mantissa 6..0
+// interleaved bytes [s0 e0 s1 e1] -> two packed bf16: sign to bit 15,
+// exponent to bits 14..7, mantissa to 6..0
 __device__ __forceinline__ uint32_t rebuild2(uint32_t x) {
   uint32_t r = (x & 0x007F007Fu) | ((x >> 1) & 0x7F807F80u);
   return r | ((x << 8) & 0x80008000u);
 }
 
 __device__ __forceinline__ void rebuild8(uint32_t s, uint32_t e, uint32_t& o0, uint32_t& o1) {
-  // s = 4 sign+mantissa bytes, e = 4 exponent bytes -> 4 bf16
   o0 = rebuild2(__builtin_amdgcn_perm(e, s, 0x05010400u));
   o1 = rebuild2(__builtin_amdgcn_perm(e, s, 0x07030602u));
 }
 
-__device__ __forceinline__ bool is_verbatim(const uint32_t* vflags, uint64_t g) {
-  return (vflags[g >> 5] >> (g & 31)) & 1u;
-}
-__device__ __forceinline__ uint32_t verbatim_rank(const uint32_t* vflags, const uint32_t* vrank, uint64_t g) {
-  const uint32_t fw = vflags[g >> 5];
-  return vrank[g >> 5] + (uint32_t)__popc(fw & ((1u << (g & 31)) - 1u));
-}
+__device__ __forceinline__ uint32_t stage_at(uint32_t f, uint32_t L) { return f * 64u + (L ^ (f & 63u)); }
 
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void k_decode_direct(DecodeArgs a) {
   __shared__ uint32_t lut[1 << kLutBits];
-  __shared__ __attribute__((aligned(16))) uint32_t stage[kWaves][64 * 8];
+  __shared__ uint32_t stage_all[kWaves][64 * kStageWords];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < (1 << kLutBits); i += kThreads) lut[i] = a.lut[i];
-  __syncthreads();
-
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)a.stream, (short)0, (int)(a.stream_words * 4u), 0x00020000);
+  uint32_t* stage = stage_all[wave];
 
   const uint64_t sbase = (uint64_t)blockIdx.x * kThreads + (uint64_t)wave * 64;
   const uint64_t s = sbase + (uint64_t)lane;
   const bool sval = s < a.segments;
+  const uint32_t SG = a.seg_groups;
+  const uint32_t CH = SG < (uint32_t)kRound ? SG : (uint32_t)kRound;   // groups per round
+  const uint32_t rounds = SG / CH;
+  // segment bounds first, so their latency overlaps the table load
   const uint32_t w0 = sval ? a.seg_off[s] : 0u;
   const uint32_t w1 = sval ? a.seg_off[s + 1] : 0u;
-  const uint32_t SG = a.seg_groups;
 
-  // bit reader
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.stream, (short)0, (int)(a.stream_words * 4u), 0x00020000);
   uint32_t cw = w0 & ~3u, qi = w0 & 3u;
-  uint4 cur = load_chunk(rs, cw);
-  uint4 nxt = load_chunk(rs, cw + 4);
+  uint4 q0 = load_chunk(rs, cw);
+  uint4 q1 = load_chunk(rs, cw + 4);
+  uint4 q2 = load_chunk(rs, cw + 8);
+
+  for (int i = threadIdx.x; i < (1 << kLutBits); i += kThreads) lut[i] = a.lut[i];
+  __syncthreads();
+
   uint64_t buf = 0;
   int avail = 0;
   uint32_t consumed = 0;
   bool bad = false;
   auto refill = [&]() {
-    const uint32_t word = qi == 0 ? cur.x : qi == 1 ? cur.y : qi == 2 ? cur.z : cur.w;
+    const uint32_t word = qi == 0 ? q0.x : qi == 1 ? q0.y : qi == 2 ? q0.z : q0.w;
     buf |= (uint64_t)word << (32 - avail);
     avail += 32;
     if (++qi == 4) {
-      cur = nxt;
+      q0 = q1;
+      q1 = q2;
       qi = 0;
       cw += 4;
-      nxt = load_chunk(rs, cw + 4);
+      q2 = load_chunk(rs, cw + 8);
     }
   };
   refill();
   refill();
 
-  uint64_t acc = 0;      // pending slot nibbles, first decoded in the low nibble
+  uint64_t acc = 0;     // pending slot nibbles, first decoded in the low nibble
   int n = 0;
   uint32_t coded_groups = 0;
-  uint32_t* st = &stage[wave][lane * 8];
   const uint32_t p0 = a.pal[0], p1 = a.pal[1], p2 = a.pal[2], p3 = a.pal[3];
+  const uint8_t* __restrict__ vexp = a.vexp;
+  const uint8_t* __restrict__ smp = a.sm;
 
-  for (uint32_t j = 0; j < SG; ++j) {
-    const uint64_t g = s * SG + j;
-    const bool gval = sval && g < a.groups;
-    const bool dec = gval && !is_verbatim(a.vflags, g);
-    if (dec) {
-      ++coded_groups;
-      int f = 0;
-      while (f < 8) {
-        if (avail <= 32) refill();
+  for (uint32_t r = 0; r < rounds; ++r) {
+    // verbatim flags and rank of this lane's groups in the round (<= 8 groups,
+    // always inside one 32-group flag word)
+    const uint64_t g0 = s * SG + (uint64_t)r * CH;
+    uint32_t vbits = 0, rank0 = 0, ngroups = 0;
+    if (sval && g0 < a.groups) {
+      const uint32_t fw = a.vflags[g0 >> 5];
+      const uint32_t sh = (uint32_t)(g0 & 31);
+      const uint64_t left = a.groups - g0;
+      ngroups = left < CH ? (uint32_t)left : CH;
+      vbits = (fw >> sh) & ((1u << ngroups) - 1u);
+      rank0 = a.vrank[g0 >> 5] + (uint32_t)__popc(fw & ((1u << sh) - 1u));
+    }
+    const uint32_t ncoded = ngroups - (uint32_t)__popc(vbits);
+    coded_groups += ncoded;
+    const uint32_t ftarget = ncoded * 8;
+
+    // ---- decode every coded group of the round ----
+    uint32_t f = 0;
+    if (n >= 8 && f < ftarget) {   // words left over from the previous round
+      stage[stage_at(f, lane)] = (uint32_t)acc;
+      acc >>= 32;
+      n -= 8;
+      ++f;
+    }
+    while (f < ftarget) {
+      if (avail < 24) refill();
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
         const uint32_t e = lut[(uint32_t)(buf >> (64 - kLutBits))];
-        uint32_t cnt = e & 15u, nb = (e >> 4) & 15u;
-        if (cnt == 0) {   // no codeword starts here: corrupt stream; make progress anyway
+        uint32_t cnt = e & 7u, nb = (e >> 4) & 15u, syms = e >> 8;
+        if (f >= ftarget) {   // second lookup after the round is complete: discard it
+          cnt = 0;
+          nb = 0;
+          syms = 0;
+        } else if (e & 8u) {   // no codeword starts here: corrupt stream (entry still advances)
           bad = true;
-          cnt = 1;
-          nb = 1;
         }
         buf <<= nb;
         avail -= (int)nb;
         consumed += nb;
-        acc |= (uint64_t)(e >> 8) << (4 * n);
+        acc |= (uint64_t)syms << (4 * n);
         n += (int)cnt;
         if (n >= 8) {
-          st[f++] = (uint32_t)acc;
+          stage[stage_at(f, lane)] = (uint32_t)acc;
           acc >>= 32;
           n -= 8;
+          ++f;
         }
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
 
-    // ---- cooperative copy-out of the 64 groups of this step ----
-    if (MODE == kDecodeNibble) {
-      uint8_t* out = (uint8_t*)a.out;
+    // ---- cooperative copy-out of the wave's round ----
+    // the wave covers 64 owners x CH groups x 64 weights; 16 weights per lane-step
+    const uint32_t per_owner = CH * 64u;
+    const uint32_t steps = 4u * CH;     // 64 owners * per_owner weights / 1024 weights per step
+    constexpr int U = 4;
+    for (uint32_t it = 0; it < steps; it += U) {
+      uint4 ev[U], sv[U] = {};
+      uint64_t el[U];
+      bool ok[U];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int L = p * 32 + (lane >> 1), h = lane & 1;
-        const uint64_t sL = sbase + (uint64_t)L;
-        const uint64_t gL = sL * SG + j;
-        if (sL < a.segments && gL < a.groups) {
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (!is_verbatim(a.vflags, gL)) v = *reinterpret_cast<const uint4*>(&stage[wave][L * 8 + h * 4]);
-          *reinterpret_cast<uint4*>(out + gL * 32 + (uint64_t)h * 16) = v;
+      for (int u = 0; u < U; ++u) {
+        const uint32_t e = (it + (uint32_t)u) * 1024u + (uint32_t)lane * 16u;
+        const uint32_t L = e / per_owner, o = e % per_owner, j = o >> 6, w16 = o & 63u;
+        const uint32_t fl = (uint32_t)__shfl((int)vbits, (int)L, 64);
+        const uint32_t rk = (uint32_t)__shfl((int)rank0, (int)L, 64);
+        const uint32_t ng = (uint32_t)__shfl((int)ngroups, (int)L, 64);
+        const uint64_t sL = sbase + L;
+        ok[u] = sL < a.segments && j < ng;
+        el[u] = (sL * SG + (uint64_t)r * CH + j) * 64u + w16;
+        const uint32_t below = fl & ((1u << j) - 1u);
+        if (ok[u] && ((fl >> j) & 1u)) {
+          const uint32_t rank = rk + (uint32_t)__popc(below);
+          ev[u] = *reinterpret_cast<const uint4*>(vexp + (uint64_t)rank * 64u + w16);
+          if (MODE == kDecodeNibble) ev[u] = make_uint4(0, 0, 0, 0);
+        } else {
+          const uint32_t slot = 8u * (j - (uint32_t)__popc(below)) + (w16 >> 3);
+          const uint32_t n0 = stage[stage_at(slot, L)], n1 = stage[stage_at(slot + 1, L)];
+          if (MODE == kDecodeNibble) {
+            ev[u] = make_uint4(n0, n1, 0, 0);
+          } else {
+            ev[u].x = slots_to_exp(spread_nibbles(n0), p0, p1, p2, p3);
+            ev[u].y = slots_to_exp(spread_nibbles(n0 >> 16), p0, p1, p2, p3);
+            ev[u].z = slots_to_exp(spread_nibbles(n1), p0, p1, p2, p3);
+            ev[u].w = slots_to_exp(spread_nibbles(n1 >> 16), p0, p1, p2, p3);
+          }
         }
+        if (MODE == kDecodeFull && ok[u]) sv[u] = *reinterpret_cast<const uint4*>(smp + el[u]);
       }
-    } else {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int L = p * 16 + (lane >> 2), q = lane & 3;
-        const uint64_t sL = sbase + (uint64_t)L;
-        const uint64_t gL = sL * SG + j;
-        if (sL < a.segments && gL < a.groups) {
-          uint4 ev;
-          if (is_verbatim(a.vflags, gL)) {
-            const uint32_t r = verbatim_rank(a.vflags, a.vrank, gL);
-            ev = *reinterpret_cast<const uint4*>(a.vexp + (uint64_t)r * 64 + (uint64_t)q * 16);
-          } else {
-            const uint2 nib = *reinterpret_cast<const uint2*>(&stage[wave][L * 8 + q * 2]);
-            ev.x = slots_to_exp(spread_nibbles(nib.x), p0, p1, p2, p3);
-            ev.y = slots_to_exp(spread_nibbles(nib.x >> 16), p0, p1, p2, p3);
-            ev.z = slots_to_exp(spread_nibbles(nib.y), p0, p1, p2, p3);
-            ev.w = slots_to_exp(spread_nibbles(nib.y >> 16), p0, p1, p2, p3);
-          }
-          const uint64_t e0 = gL * 64 + (uint64_t)q * 16;
-          if (MODE == kDecodeExponent) {
-            *reinterpret_cast<uint4*>((uint8_t*)a.out + e0) = ev;
-          } else {
-            const uint4 sv = *reinterpret_cast<const uint4*>(a.sm + e0);
-            uint4 o0, o1;
-            rebuild8(sv.x, ev.x, o0.x, o0.y);
-            rebuild8(sv.y, ev.y, o0.z, o0.w);
-            rebuild8(sv.z, ev.z, o1.x, o1.y);
-            rebuild8(sv.w, ev.w, o1.z, o1.w);
-            uint4* dst = reinterpret_cast<uint4*>((uint16_t*)a.out + e0);
-            dst[0] = o0;
-            dst[1] = o1;
-          }
+      for (int u = 0; u < U; ++u) {
+        if (!ok[u]) continue;
+        if (MODE == kDecodeNibble) {
+          *reinterpret_cast<uint2*>((uint8_t*)a.out + el[u] / 2) = make_uint2(ev[u].x, ev[u].y);
+        } else if (MODE == kDecodeExponent) {
+          *reinterpret_cast<uint4*>((uint8_t*)a.out + el[u]) = ev[u];
+        } else {
+          uint4 o0, o1;
+          rebuild8(sv[u].x, ev[u].x, o0.x, o0.y);
+          rebuild8(sv[u].y, ev[u].y, o0.z, o0.w);
+          rebuild8(sv[u].z, ev[u].z, o1.x, o1.y);
+          rebuild8(sv[u].w, ev[u].w, o1.z, o1.w);
+          uint4* dst = reinterpret_cast<uint4*>((uint16_t*)a.out + el[u]);
+          dst[0] = o0;
+          dst[1] = o1;
         }
       }
     }
@@ -219,6 +264,278 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
   if (bad) atomicOr(a.corrupt, 1);
 }
 
+
+// ---------------------------------------------------------------------------------
+// Staged decoder.  Same output as k_decode_direct, but every wave first copies
+// the contiguous stream range of its 64 segments into LDS with coalesced
+// 16-byte loads, so the per-lane bit reader never waits on HBM; the next word
+// is read from LDS one refill ahead.  Rounds are CH groups (1 or 2) and the
+// global loads that the copy-out needs (sign+mantissa bytes for the BF16
+// rebuild, exponents of verbatim groups) are issued before the round's decode
+// loop so that the loop hides their latency.  LDS per block: the 16 KB table
+// (static), then per wave a 64 x (8 CH + 1)-word stage and a wave_span-word
+// stream copy (dynamic).  The host picks CH and the waves per block that keep
+// the most waves resident under the 160 KB LDS of a CU.
+// stage words per lane: 8 per group of the round, plus one so that the odd
+// stride spreads lanes over the LDS banks
+template <int CH>
+constexpr uint32_t staged_stride() { return 8u * CH + 1u; }
+constexpr uint32_t kStagedMaxThreads = 512;
+
+template <int MODE, int CH>
+__global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs a) {
+  constexpr uint32_t kStagedStride = staged_stride<CH>();
+  constexpr uint32_t kStagedStage = 64 * kStagedStride;
+  __shared__ __attribute__((aligned(16))) uint32_t lut[1 << kLutBits];
+  extern __shared__ uint32_t dyn[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t span = (a.wave_span + 8u + 3u) & ~3u;   // + read slack, 16-byte multiple
+  uint32_t* stage = dyn + (uint32_t)wave * (kStagedStage + span);
+  uint32_t* sbuf = stage + kStagedStage;
+
+  const uint64_t sbase = (uint64_t)blockIdx.x * blockDim.x + (uint64_t)wave * 64;
+  const uint64_t s = sbase + (uint64_t)lane;
+  const bool sval = s < a.segments;
+  const bool wval = sbase < a.segments;
+  const uint32_t SG = a.seg_groups;
+  const uint32_t rounds = SG / CH;
+  const uint32_t w0 = sval ? a.seg_off[s] : 0u;
+  const uint32_t w1 = sval ? a.seg_off[s + 1] : 0u;
+  const uint32_t ws0 = wval ? (a.seg_off[sbase] & ~3u) : 0u;
+  const uint32_t we1 = wval ? a.seg_off[sbase + 64 < a.segments ? sbase + 64 : a.segments] : 0u;
+
+  // verbatim flags of the whole segment (<= 64 groups, SG-aligned) and the
+  // rank of its first group
+  uint64_t segbits = 0;
+  uint32_t rank_seg = 0;
+  uint32_t seg_ng = 0;
+  if (sval) {
+    const uint64_t g0 = s * SG;
+    const uint64_t left = a.groups - g0;
+    seg_ng = left < SG ? (uint32_t)left : SG;
+    const uint32_t sh = (uint32_t)(g0 & 31);
+    const uint32_t fw = a.vflags[g0 >> 5];
+    uint64_t bits = fw >> sh;
+    if (SG == 64 && seg_ng > 32) bits |= (uint64_t)a.vflags[(g0 >> 5) + 1] << 32;
+    segbits = seg_ng == 64 ? bits : (bits & ((1ull << seg_ng) - 1ull));
+    rank_seg = a.vrank[g0 >> 5] + (uint32_t)__popc(fw & ((1u << sh) - 1u));
+  }
+
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.stream, (short)0, (int)(a.stream_words * 4u), 0x00020000);
+  // stream range of this wave -> LDS (16 bytes per lane per step)
+  const uint32_t nwords = we1 - ws0;
+  for (uint32_t i = (uint32_t)lane * 4u; i < nwords; i += 256u) {
+    const uint4 v = load_chunk(rs, ws0 + i);
+    *reinterpret_cast<uint4*>(&sbuf[i]) = v;
+  }
+  for (int i = threadIdx.x; i < (1 << kLutBits) / 4; i += (int)blockDim.x)
+    reinterpret_cast<uint4*>(lut)[i] = reinterpret_cast<const uint4*>(a.lut)[i];
+  __syncthreads();
+  if (!wval) return;
+
+  uint32_t p = sval ? w0 - ws0 : 0u;   // next LDS word to shift into the buffer
+  uint64_t buf = ((uint64_t)sbuf[p] << 32) | (uint64_t)sbuf[p + 1];
+  p += 2;
+  uint32_t nw = sbuf[p];
+  int avail = 64;
+  uint32_t words_in = 2;
+  uint32_t flags = 0;     // OR of all table entries used: bit 3 = invalid codeword
+  uint64_t acc = 0;
+  uint32_t sh4 = 0;       // 4 x pending nibbles in acc
+  auto refill = [&]() {
+    buf |= (uint64_t)nw << (32 - avail);
+    avail += 32;
+    ++words_in;
+    ++p;
+    nw = sbuf[p < span ? p : span - 1u];   // a corrupt stream cannot read past the copy
+  };
+  uint32_t coded_groups = 0;
+  const uint32_t p0 = a.pal[0], p1 = a.pal[1], p2 = a.pal[2], p3 = a.pal[3];
+  const uint8_t* __restrict__ vexp = a.vexp;
+  const uint8_t* __restrict__ smp = a.sm;
+  constexpr uint32_t per_owner = CH * 64u;
+  constexpr int STEPS = 4 * CH;   // 64 owners * per_owner weights / 1024 per step
+
+  for (uint32_t r = 0; r < rounds; ++r) {
+    const uint32_t ng = seg_ng > r * CH ? (seg_ng - r * CH < CH ? seg_ng - r * CH : CH) : 0u;
+    const uint32_t vbits = (uint32_t)(segbits >> (r * CH)) & ((1u << CH) - 1u) & ((1u << ng) - 1u);
+    const uint32_t rank0 = rank_seg + (uint32_t)__popcll(segbits & ((1ull << (r * CH)) - 1ull));
+    const uint32_t ncoded = ng - (uint32_t)__popc(vbits);
+    coded_groups += ncoded;
+    const uint32_t ftarget = ncoded * 8;
+
+    // ---- issue the copy-out loads of this round ----
+    uint4 ev[STEPS], sv[STEPS];
+    uint64_t el[STEPS];
+    uint32_t info[STEPS];   // bit 31: ok, bit 30: verbatim, low bits: stage slot | owner << 8
+#pragma unroll
+    for (int u = 0; u < STEPS; ++u) {
+      const uint32_t e = (uint32_t)u * 1024u + (uint32_t)lane * 16u;
+      const uint32_t L = e / per_owner, o = e % per_owner, j = o >> 6, w16 = o & 63u;
+      const uint32_t fl = (uint32_t)__shfl((int)vbits, (int)L, 64);
+      const uint32_t rk = (uint32_t)__shfl((int)rank0, (int)L, 64);
+      const uint32_t gn = (uint32_t)__shfl((int)ng, (int)L, 64);
+      const uint64_t sL = sbase + L;
+      const bool ok = sL < a.segments && j < gn;
+      const bool verb = ok && ((fl >> j) & 1u);
+      const uint32_t below = fl & ((1u << j) - 1u);
+      el[u] = (sL * SG + (uint64_t)r * CH + j) * 64u + w16;
+      info[u] = (ok ? 0x80000000u : 0u) | (verb ? 0x40000000u : 0u) | (L << 8) |
+                (8u * (j - (uint32_t)__popc(below)) + (w16 >> 3));
+      ev[u] = make_uint4(0, 0, 0, 0);
+      sv[u] = make_uint4(0, 0, 0, 0);
+      if (MODE != kDecodeNibble && verb)
+        ev[u] = *reinterpret_cast<const uint4*>(vexp + (uint64_t)(rk + (uint32_t)__popc(below)) * 64u + w16);
+      if (MODE == kDecodeFull && ok) sv[u] = *reinterpret_cast<const uint4*>(smp + el[u]);
+    }
+
+    // ---- decode every coded group of the round (LDS only) ----
+    // one lookup: the entry's codewords join the nibble accumulator, whose
+    // low 8 nibbles go to the stage once complete
+    uint32_t f = 0;
+    uint32_t* my = stage + (uint32_t)lane * kStagedStride;
+    auto lookup = [&]() {
+      const uint32_t e = lut[(uint32_t)(buf >> (64 - kLutBits))];
+      const uint32_t nb = (e >> 4) & 15u;
+      flags |= e;
+      buf <<= nb;
+      avail -= (int)nb;
+      acc |= (uint64_t)(e >> 8) << sh4;
+      sh4 += 4u * (e & 7u);
+      if (sh4 >= 32u) {
+        my[f++] = (uint32_t)acc;
+        acc >>= 32;
+        sh4 -= 32u;
+      }
+    };
+    // two lookups per refill while at least two stage words remain (each
+    // lookup completes at most one word), then single lookups
+    while (f + 1 < ftarget) {
+      if (avail < 24) refill();
+      lookup();
+      lookup();
+    }
+    while (f < ftarget) {
+      if (avail < 24) refill();
+      lookup();
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- copy-out ----
+#pragma unroll
+    for (int u = 0; u < STEPS; ++u) {
+      if (!(info[u] & 0x80000000u)) continue;
+      uint4 ex = ev[u];
+      if (!(info[u] & 0x40000000u)) {
+        const uint32_t L = (info[u] >> 8) & 63u, slot = info[u] & 0xFFu;
+        const uint32_t n0 = stage[L * kStagedStride + slot], n1 = stage[L * kStagedStride + slot + 1];
+        if (MODE == kDecodeNibble) {
+          ex = make_uint4(n0, n1, 0, 0);
+        } else {
+          ex.x = slots_to_exp(spread_nibbles(n0), p0, p1, p2, p3);
+          ex.y = slots_to_exp(spread_nibbles(n0 >> 16), p0, p1, p2, p3);
+          ex.z = slots_to_exp(spread_nibbles(n1), p0, p1, p2, p3);
+          ex.w = slots_to_exp(spread_nibbles(n1 >> 16), p0, p1, p2, p3);
+        }
+      }
+      if (MODE == kDecodeNibble) {
+        *reinterpret_cast<uint2*>((uint8_t*)a.out + el[u] / 2) = make_uint2(ex.x, ex.y);
+      } else if (MODE == kDecodeExponent) {
+        *reinterpret_cast<uint4*>((uint8_t*)a.out + el[u]) = ex;
+      } else {
+        uint4 o0, o1;
+        rebuild8(sv[u].x, ex.x, o0.x, o0.y);
+        rebuild8(sv[u].y, ex.y, o0.z, o0.w);
+        rebuild8(sv[u].z, ex.z, o1.x, o1.y);
+        rebuild8(sv[u].w, ex.w, o1.z, o1.w);
+        uint4* dst = reinterpret_cast<uint4*>((uint16_t*)a.out + el[u]);
+        dst[0] = o0;
+        dst[1] = o1;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  bool bad = (flags & 8u) != 0;
+  if (sval) {
+    uint32_t left_bits = 0;
+    for (uint32_t i = 0; i < sh4 / 4u; ++i)
+      left_bits += (uint32_t)((a.len_pack >> (4 * ((acc >> (4 * i)) & 15u))) & 15u);
+    const uint32_t used = 32u * words_in - (uint32_t)avail - left_bits;
+    const uint32_t words = w1 - w0;
+    if (coded_groups == 0) {
+      if (words != 0) bad = true;
+    } else if (used > 32u * words || used <= 32u * (words - 1u)) {
+      bad = true;
+    }
+  }
+  if (bad) atomicOr(a.corrupt, 1);
+}
+
+constexpr uint32_t kMaxLds = 160u * 1024u;                      // per workgroup on gfx950
+constexpr uint32_t kMaxDynLds = kMaxLds - 4u * (1u << kLutBits);  // the table is static
+
+// dynamic LDS of the staged kernel per wave (the table is static)
+template <int CH>
+uint32_t staged_wave_bytes(const DecodeArgs& a) {
+  return 4u * (64u * staged_stride<CH>() + ((a.wave_span + 8u + 3u) & ~3u));
+}
+
+// waves per block that keep the most waves resident per CU (LDS-limited,
+// at most 16 per CU), and that count; 0 waves if one wave does not fit
+template <int CH>
+void staged_shape(const DecodeArgs& a, uint32_t* wpb_out, uint32_t* resident_out) {
+  const uint32_t per_wave = staged_wave_bytes<CH>(a);
+  uint32_t best_w = 0, best_res = 0;
+  for (uint32_t wpb = 1; wpb <= kStagedMaxThreads / 64; ++wpb) {
+    const uint32_t dyn = wpb * per_wave;
+    if (dyn > kMaxDynLds) break;
+    const uint32_t blocks = kMaxLds / (dyn + 4u * (1u << kLutBits));
+    uint32_t res = blocks * wpb;
+    if (res > 16) res = 16;
+    if (res > best_res) {   // ties keep the smaller block: more blocks balance better over CUs
+      best_res = res;
+      best_w = wpb;
+    }
+  }
+  *wpb_out = best_w;
+  *resident_out = best_res;
+}
+
+template <int MODE, int CH>
+hipError_t launch_staged(const DecodeArgs& a, uint32_t wpb, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_decode_staged<MODE, CH>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const uint64_t threads = 64ull * wpb;
+  const uint64_t blocks = (a.segments + threads - 1) / threads;
+  hipLaunchKernelGGL((k_decode_staged<MODE, CH>), dim3((uint32_t)blocks), dim3((uint32_t)threads),
+                     wpb * staged_wave_bytes<CH>(a), s, a);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(const DecodeArgs& a, uint32_t blocks, hipStream_t s) {
+  const char* force = std::getenv("UW_DECODE_DIRECT");   // selects the fallback kernel (tests)
+  if (a.wave_span > 0 && !(force && force[0] == '1')) {
+    // rounds of two groups where that keeps as many waves resident as rounds of one
+    uint32_t w1 = 0, r1 = 0, w2 = 0, r2 = 0;
+    staged_shape<1>(a, &w1, &r1);
+    if (a.seg_groups >= 2) staged_shape<2>(a, &w2, &r2);
+    if (r2 > 0 && r2 >= r1) return launch_staged<MODE, 2>(a, w2, s);
+    if (r1 > 0) return launch_staged<MODE, 1>(a, w1, s);
+  }
+  hipLaunchKernelGGL(k_decode_direct<MODE>, dim3(blocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int mode, hipStream_t s) {
@@ -226,11 +543,10 @@ hipError_t launch_decode(const DecodeArgs& a, int mode, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
   switch (mode) {
-    case kDecodeNibble: hipLaunchKernelGGL(k_decode<kDecodeNibble>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a); break;
-    case kDecodeExponent: hipLaunchKernelGGL(k_decode<kDecodeExponent>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL(k_decode<kDecodeFull>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a); break;
+    case kDecodeNibble: return launch_mode<kDecodeNibble>(a, (uint32_t)blocks, s);
+    case kDecodeExponent: return launch_mode<kDecodeExponent>(a, (uint32_t)blocks, s);
+    default: return launch_mode<kDecodeFull>(a, (uint32_t)blocks, s);
   }
-  return hipGetLastError();
 }
 
 }  // namespace uw

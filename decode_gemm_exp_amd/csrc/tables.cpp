@@ -108,9 +108,11 @@ void assign_codes(Tables& t) {
 }
 
 // Decoder table: entry v describes the 12-bit window v (first stream bit =
-// bit 11): how many whole codewords it starts with (up to 6), how many bits
-// they take, and their slots as nibbles.  A window that starts with no valid
-// codeword has count 0.
+// bit 11): bits 0-2 how many whole codewords it starts with (up to 6), bits
+// 4-7 how many bits they take, bits 8-31 their slots as nibbles.  A window
+// that starts with no valid codeword (possible only with a one-symbol code)
+// gets count 1, length 1, no slots and bit 3 set, so decoders always make
+// progress and can OR the entries to detect corruption.
 void build_decode_lut(const Tables& t, uint32_t* lut) {
   for (uint32_t v = 0; v < (1u << kLutBits); ++v) {
     int pos = 0, cnt = 0;
@@ -131,7 +133,7 @@ void build_decode_lut(const Tables& t, uint32_t* lut) {
       pos += flen;
       ++cnt;
     }
-    lut[v] = (uint32_t)cnt | ((uint32_t)pos << 4) | (syms << 8);
+    lut[v] = cnt == 0 ? (1u | 8u | (1u << 4)) : ((uint32_t)cnt | ((uint32_t)pos << 4) | (syms << 8));
   }
 }
 

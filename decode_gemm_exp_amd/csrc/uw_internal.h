@@ -32,7 +32,7 @@ struct Tables {
 
 struct uw_matrix {
   int device = 0;
-  uint32_t layout = 0, seg_groups = 8;
+  uint32_t layout = 0, seg_groups = 4;
   uint64_t rows = 0, cols = 0, numel = 0, groups = 0, segments = 0, flag_words = 0;
   uint64_t V = 0, W = 0, code_bits = 0;
   uw::Tables t{};
@@ -46,6 +46,7 @@ struct uw_matrix {
   uint32_t* lut = nullptr;        // 4096 decode entries
   uint8_t* pidx = nullptr;        // resident palette indices (numel / 2) or null
   int* corrupt = nullptr;         // device flag set by decoders
+  uint32_t wave_span = 0;         // most stream words any 64-segment wave covers (from a 4-word boundary)
 };
 
 namespace uw {
@@ -67,6 +68,7 @@ hipError_t launch_segment_bits(const uint16_t* w, uint64_t groups, uint32_t seg_
                                uint32_t* seg_words, hipStream_t s);
 hipError_t launch_offsets_scan(const uint32_t* seg_words, uint64_t segments, uint32_t* seg_off,
                                hipStream_t s);
+hipError_t launch_wave_span(const uint32_t* seg_off, uint64_t segments, uint32_t* out, hipStream_t s);
 hipError_t launch_encode(const uint16_t* w, uint64_t groups, uint32_t seg_groups, uint64_t segments,
                          const uint32_t* codebook, const uint32_t* vflags, const uint32_t* vrank,
                          const uint32_t* seg_off, uint32_t* stream, uint8_t* vexp, hipStream_t s);
@@ -81,6 +83,7 @@ struct DecodeArgs {
   uint32_t pal[4];                                  // palette bytes
   uint64_t len_pack;                                // 4-bit code length per slot
   uint64_t groups, segments; uint32_t seg_groups;
+  uint32_t wave_span;                               // see uw_matrix::wave_span
   void* out;
   int* corrupt;
 };

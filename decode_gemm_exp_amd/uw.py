@@ -81,6 +81,8 @@ _SIGS = {
     "uw_workspace_size": (ctypes.c_int, [_vp, ctypes.c_int, _i64, ctypes.POINTER(_sz)]),
     "uw_matmul_reconstruct": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _vp, _vp, _sz,
                                              ctypes.POINTER(uw_kernel_cfg), _vp]),
+    "uw_matmul_stage": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _i64, _vp, _vp, _sz,
+                                       ctypes.POINTER(uw_kernel_cfg), _vp]),
     "uw_matmul_reconstruct_grouped": (ctypes.c_int, [ctypes.POINTER(_vp), ctypes.c_int, ctypes.c_int, _vp, _i64,
                                                      _vp, _vp, _sz, ctypes.POINTER(uw_kernel_cfg), _vp]),
     "uw_gemm_bf16": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, _vp, _i64, _vp,
@@ -160,7 +162,7 @@ class Matrix:
             pass
 
 
-def uw_compress(w_dev: torch.Tensor, n: int, k: int, layout: int = LAYOUT_NK, seg_groups: int = 8,
+def uw_compress(w_dev: torch.Tensor, n: int, k: int, layout: int = LAYOUT_NK, seg_groups: int = 4,
                 stream=None) -> Matrix:
     opts = uw_compress_opts(seg_groups, 0)
     h = ctypes.c_void_p()
@@ -230,6 +232,13 @@ def uw_matmul_reconstruct(m: Matrix, pipeline: int, x: torch.Tensor, y: torch.Te
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(_lib.uw_matmul_reconstruct(m.handle, pipeline, _ptr(x), batch, _ptr(y), _ptr(ws), nbytes, _cfg(cfg),
                                       _stream(stream)), "uw_matmul_reconstruct")
+
+
+def uw_matmul_stage(m: Matrix, pipeline: int, prep: torch.Tensor | None, x: torch.Tensor, y: torch.Tensor,
+                    ws: torch.Tensor | None, cfg=None, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(_lib.uw_matmul_stage(m.handle, pipeline, _ptr(prep), _ptr(x), x.shape[0], _ptr(y), _ptr(ws), nbytes,
+                                _cfg(cfg), _stream(stream)), "uw_matmul_stage")
 
 
 def uw_matmul_reconstruct_grouped(ms, pipeline: int, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor | None,

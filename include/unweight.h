@@ -86,7 +86,7 @@ typedef enum {
 } uw_pipeline;
 
 typedef struct {
-  uint32_t seg_groups;  /* groups per segment: power of two in [1, 64]; 0 = 8 */
+  uint32_t seg_groups;  /* groups per segment: power of two in [1, 64]; 0 = 4 */
   uint32_t flags;       /* reserved, must be 0                               */
 } uw_compress_opts;
 
@@ -180,6 +180,17 @@ uw_status uw_workspace_size(const uw_matrix* m, uw_pipeline p, int64_t batch, si
 uw_status uw_matmul_reconstruct(const uw_matrix* m, uw_pipeline p, const uint16_t* x_dev,
                                 int64_t batch, float* y_dev, void* ws_dev, size_t ws_bytes,
                                 const uw_kernel_cfg* cfg, void* stream);
+
+/* The GEMM stage alone, from a buffer already holding what uw_decode_full
+ * (pipeline 0), uw_decode_exponent (1) or uw_transcode_palette (2) wrote for
+ * this matrix; prep_dev is ignored for pipeline 3 (resident indices).  The
+ * workspace holds only the small-batch KN kernel's partial sums; a workspace
+ * of uw_workspace_size bytes is always enough.  Lets a caller run the
+ * preprocessing and the GEMM on different streams or at different times.
+ * ([EVC] "解壓與運算資源共享": decoder and matmul are separate kernels) */
+uw_status uw_matmul_stage(const uw_matrix* m, uw_pipeline p, const void* prep_dev, const uint16_t* x_dev,
+                          int64_t batch, float* y_dev, void* ws_dev, size_t ws_bytes,
+                          const uw_kernel_cfg* cfg, void* stream);
 
 /* Several matrices with the same K sharing one x (e.g. gate and up), one
  * launch per stage: y_dev is [batch][sum of N] with matrix i's columns at

@@ -138,7 +138,7 @@ class Compressed:
             pass
 
 
-def compress(w_stored: np.ndarray, seg_groups: int = 8, layout: int = 0) -> Compressed:
+def compress(w_stored: np.ndarray, seg_groups: int = 4, layout: int = 0) -> Compressed:
     """Compress the stored 2-D uint16 array (bf16 bit patterns)."""
     w = np.ascontiguousarray(w_stored, dtype=np.uint16)
     assert w.ndim == 2

@@ -42,13 +42,13 @@ def to_dev_bits(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(a.astype(np.uint16).view(np.int16)).to(DEV).view(torch.bfloat16)
 
 
-def gpu_compress(uw, w_dev, n, k, layout, sg=8):
+def gpu_compress(uw, w_dev, n, k, layout, sg=4):
     m = uw.uw_compress(w_dev, n, k, layout, seg_groups=sg)
     torch.cuda.synchronize()
     return m
 
 
-def check_codec(uw, oracle, w_dev, n, k, layout, sg=8, check_transcode=True):
+def check_codec(uw, oracle, w_dev, n, k, layout, sg=4, check_transcode=True):
     """Compress on the GPU, compare the UWF1 blob with the oracle's, decode."""
     w_np = bits(w_dev)
     m = gpu_compress(uw, w_dev, n, k, layout, sg)
@@ -249,3 +249,13 @@ def test_sequence_runner_matches_single_calls(uw, synth, oracle):
         torch.cuda.synchronize()
         for j, (w_np, x_np, layout) in zip(jobs, ref):
             check_gemm(oracle, j.y.cpu().numpy(), x_np, w_np, layout, what=f"seq cus={dcus}")
+
+
+@pytest.mark.parametrize("sg", [1, 8, 64])
+def test_fallback_decoder_matches(uw, synth, oracle, monkeypatch, sg):
+    """The direct-from-HBM decoder (used when a wave's stream does not fit in
+    LDS) gives the same bytes as the oracle."""
+    say(f"fallback decoder sg={sg}")
+    monkeypatch.setenv("UW_DECODE_DIRECT", "1")
+    w = synth.weights(1024, 1024, 0.02, 0.002, 11, seed=40 + sg).to(DEV)
+    check_codec(uw, oracle, w, 1024, 1024, 0, sg)
