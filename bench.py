@@ -171,6 +171,101 @@ def extras(uw, synth, torch, dev, iters: int = 10):
     return out
 
 
+def job_bytes(info, pipeline: int, batch: int) -> float:
+    """Compulsory HBM bytes of one projection under a pipeline (preprocessing
+    writes and re-reads included)."""
+    M = info.numel
+    Z = 4 * (info.stream_words + 2)
+    O = 4 * (info.segments + 1)
+    Aux = 8 * ((info.groups + 31) // 32)
+    Vb = 64 * info.verbatim_groups
+    X, Y = 2 * batch * info.k, 4 * batch * info.n
+    return {0: (Z + O + Aux + Vb + M + 2 * M) + (2 * M + X + Y),
+            1: (Z + O + Aux + Vb + M) + (2 * M + X + Y),
+            2: (Z + O + Aux + M / 2) + (1.5 * M + Aux + Vb + X + Y),
+            3: 1.5 * M + Aux + Vb + X + Y}[pipeline]
+
+
+def run_mlp70b(args) -> int:
+    """80 Llama-70B MLP layers (gate/up 28672x8192, down 8192x28672 stored
+    transposed) compressed-resident in HBM; the autotuner picks pipeline,
+    GEMM variant and CU split per projection and batch on the first
+    ``--tune-layers`` layers; then one full pass over all layers is timed
+    per batch."""
+    import torch
+
+    from decode_gemm_exp_amd import synth, uw
+    dev = "cuda:0"
+    wl = synth.WORKLOADS["mlp70b"]
+    L = args.layers
+    batches = [int(b) for b in args.batches.split(",")] if args.batches else list(wl.batches)
+    mats, proj = [], []
+    t0 = time.perf_counter()
+    for layer in range(L):
+        for i, (label, n, k, layout) in enumerate(wl.mats):
+            w = synth.workload_weights(wl, i, layer=layer, device=dev)
+            m = uw.uw_compress(w, n, k, layout, seg_groups=args.seg_groups)
+            uw.uw_transcode_palette(m, None)
+            mats.append(m)
+            proj.append(i)
+            del w
+        if layer % 10 == 9:
+            print(f"bench: {layer + 1}/{L} layers resident ({time.perf_counter() - t0:.0f} s)", file=sys.stderr,
+                  flush=True)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    infos = [m.info() for m in mats]
+    resident = sum(i.compressed_bytes + (i.numel // 2) for i in infos)
+    nt = min(args.tune_layers, L) * 3
+    print(f"bench: autotune on {nt // 3} layers, batches {batches}", file=sys.stderr, flush=True)
+    t_tune = time.perf_counter()
+    tuned = uw.uw_autotune(mats[:nt], proj[:nt], batches, max_passes=2,
+                           json_path=os.path.join(ROOT, "gpurun_out", "mlp70b_tuned.json")
+                           if os.path.isdir(os.path.join(ROOT, "gpurun_out")) else None)
+    t_tune = time.perf_counter() - t_tune
+    rows = []
+    for b in batches:
+        choice = {e["projection"]: e for e in tuned if e["batch"] == b}
+        K_max = max(i.k for i in infos)
+        N_max = max(i.n for i in infos)
+        x = synth.activations(b, K_max, seed=wl.seed, device=dev)
+        y = torch.empty((b, N_max), dtype=torch.float32, device=dev)
+        jobs = []
+        for m, pj in zip(mats, proj):
+            c = choice[pj]
+            jobs.append(uw.Job(m, c["pipeline"], x, y, {"variant": c["variant"], "split_k": c["split_k"],
+                                                       "decode_cus": c["decode_cus"]}))
+        arr = uw._jobs(jobs)
+        ws = torch.empty(max(16, uw.uw_sequence_workspace_size(jobs)), dtype=torch.uint8, device=dev)
+        times = []
+        for r in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            uw.uw_run_sequence(jobs, 0, ws, _arr=arr)
+            e1.record()
+            torch.cuda.synchronize()
+            if r:
+                times.append(e0.elapsed_time(e1) * 1e3)
+        t = sorted(times)[len(times) // 2]
+        flops = sum(2.0 * b * i.n * i.k for i in infos)
+        nbytes = sum(job_bytes(i, choice[pj]["pipeline"], b) for i, pj in zip(infos, proj))
+        rows.append({"batch": b, "us_per_pass": round(t, 1), "tflops": round(flops / t / 1e6, 2),
+                     "decoded_gbs": round(2 * sum(i.numel for i in infos) / t / 1e3, 1),
+                     "hbm_frac": round(nbytes / t / 1e3 / HBM_PEAK_GBS, 4),
+                     "mfma_frac": round(flops / t / 1e6 / BF16_PEAK_TFLOPS, 4),
+                     "roofline_frac": round(max(nbytes / 8e12, flops / 2.5e15) / (t * 1e-6), 4),
+                     "choice": {wl.mats[p][0]: {k2: choice[p][k2] for k2 in ("pipeline", "variant", "decode_cus")}
+                                for p in range(3)}})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        del x, y, ws
+    res = {"metric": METRIC, "workload": f"mlp70b: {L} layers of Llama-70B MLP (gate/up 28672x8192, down "
+                                        f"8192x28672 stored transposed) bf16 N(0,0.02), compressed-resident",
+           "resident_gb": round(resident / 1e9, 2), "dense_bf16_gb": round(sum(2 * i.numel for i in infos) / 1e9, 2),
+           "tune_layers": nt // 3, "tune_seconds": round(t_tune, 1), "rows": rows}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,12 +277,18 @@ def main() -> int:
     ap.add_argument("--no-extras", action="store_true", help="skip the larger-batch rows")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run a plain device copy of this size first (HBM counter calibration)")
+    ap.add_argument("--workload", default="gate8b", choices=["gate8b", "mlp70b"])
+    ap.add_argument("--layers", type=int, default=80, help="mlp70b: resident layers")
+    ap.add_argument("--tune-layers", type=int, default=4, help="mlp70b: layers the autotuner times")
+    ap.add_argument("--batches", default="", help="mlp70b: comma-separated batch sizes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; the path shards per matrix "
                                    "(see the design notes) but no multi-GPU run is made", "n_gpus": args.gpus}))
         return 2
 
+    if args.workload == "mlp70b":
+        return run_mlp70b(args)
     import numpy as np  # noqa: F401
     import torch
 

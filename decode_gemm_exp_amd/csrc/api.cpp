@@ -621,6 +621,14 @@ uw_status uw_drop_stream(uw_matrix* m, void* stream) {
   return UW_OK;
 }
 
+uw_status uw_drop_palette(uw_matrix* m, void* stream) {
+  if (!m) return UW_ERR_INVALID;
+  if (!m->stream) return UW_ERR_STATE;   // would leave no form to decode from
+  UW_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  dev_free(m->pidx);
+  return UW_OK;
+}
+
 uw_status uw_workspace_size(const uw_matrix* m, uw_pipeline p, int64_t batch, size_t* bytes) {
   if (!m || !bytes || batch <= 0 || p < UW_PIPE_FULL || p > UW_PIPE_PALETTE_DIRECT) return UW_ERR_INVALID;
   *bytes = prep_bytes(m, p) + partial_bytes(m, p, batch, nullptr);
@@ -764,7 +772,12 @@ uw_status uw_run_sequence(const uw_job* jobs, int count, int32_t decode_cus, voi
   const size_t part_elems = (need - 2 * prep) / sizeof(float);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  if (decode_cus <= 0) {   // everything in order on the caller's stream
+  bool any_split = false;
+  for (int i = 0; i < count; ++i) {
+    const int d = jobs[i].cfg.decode_cus > 0 ? jobs[i].cfg.decode_cus : decode_cus;
+    if (d > 0 && jobs[i].pipeline != UW_PIPE_PALETTE_DIRECT) any_split = true;
+  }
+  if (!any_split) {   // everything in order on the caller's stream
     for (int i = 0; i < count; ++i) {
       const uw_job& j = jobs[i];
       UW_CHECK(preprocess(j.m, j.pipeline, bufs[0], s));
@@ -774,47 +787,62 @@ uw_status uw_run_sequence(const uw_job* jobs, int count, int32_t decode_cus, voi
     return UW_OK;
   }
 
-  SplitStreams ss;
-  UW_CHECK(split_streams(decode_cus, &ss));
-  // events: fork, per-buffer "prep done" and "gemm done", join
-  hipEvent_t fork, prep_done[2], gemm_done[2], join_dec, join_gemm;
-  UW_HIP(hipEventCreateWithFlags(&fork, hipEventDisableTiming));
-  for (int b = 0; b < 2; ++b) {
-    UW_HIP(hipEventCreateWithFlags(&prep_done[b], hipEventDisableTiming));
-    UW_HIP(hipEventCreateWithFlags(&gemm_done[b], hipEventDisableTiming));
+  // Per job: its preprocessing runs on a stream masked to D CUs and its GEMM on
+  // a stream masked to the other CUs (D = the job's decode_cus, else the
+  // sequence default; D = 0 puts both on the caller's stream).  GEMMs stay in
+  // job order; preprocessing of job i waits for the GEMM of job i-2, which
+  // used the same buffer.
+  thread_local std::vector<hipEvent_t> pool;
+  const size_t need_ev = 2 * (size_t)count + 1;
+  while (pool.size() < need_ev) {
+    hipEvent_t e;
+    UW_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    pool.push_back(e);
   }
-  UW_HIP(hipEventCreateWithFlags(&join_dec, hipEventDisableTiming));
-  UW_HIP(hipEventCreateWithFlags(&join_gemm, hipEventDisableTiming));
+  hipEvent_t fork = pool[0];
+  hipEvent_t* prep_done = pool.data() + 1;
+  hipEvent_t* gemm_done = pool.data() + 1 + count;
   UW_HIP(hipEventRecord(fork, s));
-  UW_HIP(hipStreamWaitEvent(ss.dec, fork, 0));
-  UW_HIP(hipStreamWaitEvent(ss.gemm, fork, 0));
-  bool used[2] = {false, false};
+  std::vector<hipStream_t> used;
+  auto enter = [&](hipStream_t st) -> uw_status {
+    if (st == s) return UW_OK;
+    for (hipStream_t u : used)
+      if (u == st) return UW_OK;
+    UW_HIP(hipStreamWaitEvent(st, fork, 0));
+    used.push_back(st);
+    return UW_OK;
+  };
   for (int i = 0; i < count; ++i) {
     const uw_job& j = jobs[i];
-    const int b = i & 1;
-    hipStream_t pre_s = ss.dec;
-    if (j.pipeline != UW_PIPE_PALETTE_DIRECT) {
-      if (used[b]) UW_HIP(hipStreamWaitEvent(ss.dec, gemm_done[b], 0));   // buffer free again
-      UW_CHECK(preprocess(j.m, j.pipeline, bufs[b], pre_s));
-      UW_HIP(hipEventRecord(prep_done[b], pre_s));
-      UW_HIP(hipStreamWaitEvent(ss.gemm, prep_done[b], 0));
+    const int d = j.cfg.decode_cus > 0 ? j.cfg.decode_cus : decode_cus;
+    hipStream_t ds = s, gs = s;
+    if (d > 0 && j.pipeline != UW_PIPE_PALETTE_DIRECT) {
+      SplitStreams ss;
+      UW_CHECK(split_streams(d, &ss));
+      ds = ss.dec;
+      gs = ss.gemm;
     }
-    WeightView v = pipeline_view(j.m, j.pipeline, bufs[b]);
-    UW_HIP(launch_gemm(v, j.x_dev, j.batch, j.y_dev, (int64_t)v.n, 0, &j.cfg, part, part_elems, ss.gemm));
-    UW_HIP(hipEventRecord(gemm_done[b], ss.gemm));
-    used[b] = true;
+    UW_CHECK(enter(ds));
+    UW_CHECK(enter(gs));
+    uint8_t* buf = bufs[i & 1];
+    if (j.pipeline != UW_PIPE_PALETTE_DIRECT) {
+      if (i >= 2) UW_HIP(hipStreamWaitEvent(ds, gemm_done[i - 2], 0));
+      UW_CHECK(preprocess(j.m, j.pipeline, buf, ds));
+      UW_HIP(hipEventRecord(prep_done[i], ds));
+      UW_HIP(hipStreamWaitEvent(gs, prep_done[i], 0));
+    }
+    if (i >= 1) UW_HIP(hipStreamWaitEvent(gs, gemm_done[i - 1], 0));
+    WeightView v = pipeline_view(j.m, j.pipeline, buf);
+    UW_HIP(launch_gemm(v, j.x_dev, j.batch, j.y_dev, (int64_t)v.n, 0, &j.cfg, part, part_elems, gs));
+    UW_HIP(hipEventRecord(gemm_done[i], gs));
   }
-  UW_HIP(hipEventRecord(join_dec, ss.dec));
-  UW_HIP(hipEventRecord(join_gemm, ss.gemm));
-  UW_HIP(hipStreamWaitEvent(s, join_dec, 0));
-  UW_HIP(hipStreamWaitEvent(s, join_gemm, 0));
-  (void)hipEventDestroy(fork);
-  for (int b = 0; b < 2; ++b) {
-    (void)hipEventDestroy(prep_done[b]);
-    (void)hipEventDestroy(gemm_done[b]);
+  // join: the last GEMM follows every earlier GEMM and preprocessing it needed;
+  // make the caller's stream wait for it and for any preprocessing stream
+  UW_HIP(hipStreamWaitEvent(s, gemm_done[count - 1], 0));
+  for (hipStream_t u : used) {
+    UW_HIP(hipEventRecord(prep_done[0], u));
+    UW_HIP(hipStreamWaitEvent(s, prep_done[0], 0));
   }
-  (void)hipEventDestroy(join_dec);
-  (void)hipEventDestroy(join_gemm);
   return UW_OK;
 }
 

@@ -15,10 +15,7 @@
 //     KN: lanes own 8 consecutive outputs, waves stride K, partial sums per
 //     K slice go to the workspace and a second kernel adds them in a fixed
 //     order (deterministic).
-//   * MFMA (batch > 8): 256-thread tiles; every K step of 64 (one weight
-//     group along K for NK) the block loads the x tile and the compressed
-//     weight tile, rebuilds BF16 into LDS, then each wave issues
-//     v_mfma_f32_32x32x16_bf16 from LDS.
+//   * MFMA (batch > 8): gemm_mfma.hip.
 #include "rebuild.h"
 
 namespace uw {
@@ -141,128 +138,6 @@ __global__ __launch_bounds__(256) void k_reduce_slices(const float* __restrict__
   }
 }
 
-// ---- MFMA GEMM -------------------------------------------------------------------------
-// Operand layout of v_mfma_f32_32x32x16_bf16 (64 lanes): A[i][k] with
-// i = lane % 32 and k = 8 * (lane / 32) + 0..7 held as 8 bf16; B[k][j] with
-// j = lane % 32, same k; D[i][j] in 16 floats, j = lane % 32,
-// i = 8 * (r / 4) + 4 * (lane / 32) + r % 4 for register r.
-template <int LAYOUT, int FMT, int BM, int BN, int WGM>
-__global__ __launch_bounds__(256) void k_mfma(WeightView w, const uint16_t* __restrict__ x, int B,
-                                              float* __restrict__ y, int64_t ldy, int64_t col0) {
-  constexpr int BK = 64, LDK = BK + 8;
-  constexpr int WGN = 4 / WGM;
-  constexpr int WM = BM / WGM, WN = BN / WGN;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  static_assert(TM >= 1 && TN >= 1, "tile too small");
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[BN * LDK];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
-  const int64_t N = (int64_t)w.n, K = (int64_t)w.k;
-  const int64_t n0 = (int64_t)blockIdx.x * BN, m0 = (int64_t)blockIdx.y * BM;
-
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  for (int64_t k0 = 0; k0 < K; k0 += BK) {
-    for (int c = tid; c < BM * 8; c += 256) {
-      const int r = c >> 3, q = c & 7;
-      const int64_t row = m0 + r, kk = k0 + q * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < B && kk < K) v = *reinterpret_cast<const uint4*>(x + row * K + kk);
-      *reinterpret_cast<uint4*>(&Xs[r * LDK + q * 8]) = v;
-    }
-    if constexpr (LAYOUT == 0) {
-      for (int c = tid; c < BN * 4; c += 256) {
-        const int r = c >> 2, q = c & 3;
-        const int64_t n = n0 + r;
-        uint32_t o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (n < N) load16<FMT>(w, (uint64_t)(n * K + k0 + q * 16), o);
-        uint4* d = reinterpret_cast<uint4*>(&Ws[r * LDK + q * 16]);
-        d[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        d[1] = make_uint4(o[4], o[5], o[6], o[7]);
-      }
-    } else {
-      constexpr int QN = BN / 16;
-      for (int c = tid; c < BK * QN; c += 256) {
-        const int kr = c / QN, q = c % QN;
-        const int64_t k = k0 + kr, n = n0 + q * 16;
-        uint32_t o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (k < K && n < N) load16<FMT>(w, (uint64_t)(k * N + n), o);
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          Ws[(q * 16 + i) * LDK + kr] = (uint16_t)((o[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 a[TM], b[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * WM + i * 32 + (lane & 31);
-        a[i] = *reinterpret_cast<const bf16x8*>(&Xs[row * LDK + kk + 8 * (lane >> 5)]);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = wn * WN + j * 32 + (lane & 31);
-        b[j] = *reinterpret_cast<const bf16x8*>(&Ws[col * LDK + kk + 8 * (lane >> 5)]);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t col = n0 + wn * WN + j * 32 + (lane & 31);
-        if (row < B && col < N) y[row * ldy + col0 + col] = acc[i][j][r];
-      }
-}
-
-// ---- dispatch tables -------------------------------------------------------------------
-struct Variant {
-  int bm, bn, wgm;
-};
-constexpr Variant kVariants[] = {{32, 128, 1}, {64, 128, 2}, {128, 128, 2}, {128, 256, 2}, {256, 128, 4}};
-constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
-
-typedef void (*MfmaFn)(WeightView, const uint16_t*, int, float*, int64_t, int64_t);
-
-template <int L, int F>
-MfmaFn mfma_fn(int v) {
-  switch (v) {
-    case 0: return k_mfma<L, F, 32, 128, 1>;
-    case 1: return k_mfma<L, F, 64, 128, 2>;
-    case 2: return k_mfma<L, F, 128, 128, 2>;
-    case 3: return k_mfma<L, F, 128, 256, 2>;
-    default: return k_mfma<L, F, 256, 128, 4>;
-  }
-}
-
-MfmaFn pick_mfma(int layout, int fmt, int v) {
-  if (layout == 0) {
-    if (fmt == kFmtBf16) return mfma_fn<0, kFmtBf16>(v);
-    if (fmt == kFmtExp) return mfma_fn<0, kFmtExp>(v);
-    return mfma_fn<0, kFmtPal>(v);
-  }
-  if (fmt == kFmtBf16) return mfma_fn<1, kFmtBf16>(v);
-  if (fmt == kFmtExp) return mfma_fn<1, kFmtExp>(v);
-  return mfma_fn<1, kFmtPal>(v);
-}
-
 typedef void (*GemvNkFn)(WeightView, const uint16_t*, int, float*, int64_t, int64_t);
 typedef void (*GemvKnFn)(WeightView, const uint16_t*, int, float*, int64_t);
 
@@ -283,10 +158,16 @@ GemvKnFn gemv_kn_fn(int nb) {
 
 constexpr int kGemvMaxBatch = 8;
 
-int default_variant(int64_t batch) {
-  if (batch <= 32) return 0;
-  if (batch <= 64) return 1;
-  return 2;
+// largest MFMA tile whose grid alone covers the chip; else 128 x 128 with split K
+int default_tile(uint64_t n, int64_t batch) {
+  for (int t = mfma2_tile_count() - 1; t >= 0; --t) {
+    const int bm = t == 0 ? 64 : (t == 1 || t == 2) ? 128 : 256;
+    const int bn = (t == 2 || t == 4) ? 256 : 128;
+    if (bm > 2 * batch && t > 0) continue;   // no tile much taller than the batch
+    const uint64_t blocks = (n + bn - 1) / bn * (uint64_t)((batch + bm - 1) / bm);
+    if (blocks >= 256) return t;
+  }
+  return batch <= 64 ? 0 : 1;
 }
 
 // K slices of the KN GEMV: enough blocks to cover the chip a few times.
@@ -303,27 +184,35 @@ int kn_slices(const WeightView& w, const uw_kernel_cfg* cfg) {
 }  // namespace
 
 // Variant numbering seen through uw_kernel_cfg.variant: 1 = VALU GEMV (any
-// batch, eight rows per launch), 2.. = the MFMA tiles of kVariants.
-int gemm_variant_count() { return 1 + kNumVariants; }
+// batch, eight rows per launch), 2.. = the MFMA tiles of gemm_mfma.hip.
+int gemm_variant_count() { return 1 + mfma2_tile_count(); }
 
-static int resolve_variant(int64_t batch, const uw_kernel_cfg* cfg) {
-  if (cfg && cfg->variant > 0 && cfg->variant <= 1 + kNumVariants) return cfg->variant;
-  return batch <= kGemvMaxBatch ? 1 : 2 + default_variant(batch);
+static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg) {
+  if (cfg && cfg->variant > 0 && cfg->variant <= gemm_variant_count()) return cfg->variant;
+  return batch <= kGemvMaxBatch ? 1 : 2 + default_tile(w.n, batch);
 }
 
-// Partial sums of the KN GEMV (whatever variant ends up chosen, so that one
-// workspace size serves every variant).
+// Workspace floats for partial sums: enough for every variant (the KN GEMV's
+// K slices, the MFMA split-K slices), so one size serves any kernel choice.
 size_t gemm_partial_elems(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg) {
-  if (w.layout == 0) return 0;
-  const int64_t rows = batch < kGemvMaxBatch ? batch : kGemvMaxBatch;
-  return (size_t)kn_slices(w, cfg) * (size_t)rows * (size_t)w.n;
+  size_t need = 0;
+  if (w.layout == 1) {
+    const int64_t rows = batch < kGemvMaxBatch ? batch : kGemvMaxBatch;
+    need = (size_t)kn_slices(w, cfg) * (size_t)rows * (size_t)w.n;
+  }
+  const int split = cfg ? cfg->split_k : 0;
+  for (int t = 0; t < mfma2_tile_count(); ++t) {
+    const size_t e = mfma2_partial_elems(w, batch, t, split);
+    if (e > need) need = e;
+  }
+  return need;
 }
 
 hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, float* y, int64_t ldy,
                        int64_t col0, const uw_kernel_cfg* cfg, float* partial, size_t partial_elems,
                        hipStream_t s) {
   if (batch <= 0) return hipSuccess;
-  const int v = resolve_variant(batch, cfg);
+  const int v = resolve_variant(w, batch, cfg);
   if (v == 1) {
     for (int64_t b0 = 0; b0 < batch; b0 += kGemvMaxBatch) {
       const int nb = (int)(batch - b0 < kGemvMaxBatch ? batch - b0 : kGemvMaxBatch);
@@ -353,12 +242,7 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
     }
     return hipSuccess;
   }
-  const int vi = v - 2;
-  const Variant& vt = kVariants[vi];
-  MfmaFn f = pick_mfma(w.layout, w.fmt, vi);
-  dim3 grid((unsigned)((w.n + (uint64_t)vt.bn - 1) / (uint64_t)vt.bn), (unsigned)((batch + vt.bm - 1) / vt.bm));
-  hipLaunchKernelGGL(f, grid, dim3(256), 0, s, w, x, (int)batch, y, ldy, col0);
-  return hipGetLastError();
+  return launch_mfma2(w, x, batch, y, ldy, col0, v - 2, cfg ? cfg->split_k : 0, partial, partial_elems, s);
 }
 
 }  // namespace uw

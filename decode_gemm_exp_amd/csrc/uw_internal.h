@@ -108,5 +108,11 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
                        size_t partial_elems, hipStream_t s);
 size_t gemm_partial_elems(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg);
 int gemm_variant_count();
+// gemm_mfma.hip
+int mfma2_tile_count();
+int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint);
+size_t mfma2_partial_elems(const WeightView& w, int64_t batch, int tile, int split_hint);
+hipError_t launch_mfma2(const WeightView& w, const uint16_t* x, int64_t batch, float* y, int64_t ldy, int64_t col0,
+                        int tile, int split_hint, float* part, size_t part_elems, hipStream_t s);
 
 }  // namespace uw

@@ -59,6 +59,12 @@ class uw_info(ctypes.Structure):
                 ("has_palette_idx", ctypes.c_int32)]
 
 
+class uw_tune_entry(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("projection", ctypes.c_int32), ("pipeline", ctypes.c_int32),
+                ("variant", ctypes.c_int32), ("split_k", ctypes.c_int32), ("decode_cus", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("sequence_us", ctypes.c_double)]
+
+
 class uw_job(ctypes.Structure):
     _fields_ = [("m", ctypes.c_void_p), ("pipeline", ctypes.c_int32), ("cfg", uw_kernel_cfg),
                 ("x_dev", ctypes.c_void_p), ("y_dev", ctypes.c_void_p), ("batch", ctypes.c_int64)]
@@ -91,6 +97,10 @@ _SIGS = {
     "uw_sequence_workspace_size": (ctypes.c_int, [ctypes.POINTER(uw_job), ctypes.c_int, ctypes.POINTER(_sz)]),
     "uw_run_sequence": (ctypes.c_int, [ctypes.POINTER(uw_job), ctypes.c_int, ctypes.c_int32, _vp, _sz, _vp]),
     "uw_sync_status": (ctypes.c_int, [_vp, _vp]),
+    "uw_autotune": (ctypes.c_int, [ctypes.POINTER(_vp), ctypes.POINTER(ctypes.c_int32), ctypes.c_int, ctypes.c_int,
+                                   ctypes.POINTER(ctypes.c_int64), ctypes.c_int, ctypes.c_int, ctypes.c_char_p,
+                                   ctypes.POINTER(uw_tune_entry), _vp]),
+    "uw_drop_palette": (ctypes.c_int, [_vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -285,6 +295,22 @@ def uw_run_sequence(jobs, decode_cus: int, ws: torch.Tensor | None, stream=None,
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(_lib.uw_run_sequence(arr, len(jobs), decode_cus, _ptr(ws), nbytes, _stream(stream)),
            "uw_run_sequence")
+
+
+def uw_drop_palette(m: Matrix, stream=None) -> None:
+    _check(_lib.uw_drop_palette(m.handle, _stream(stream)), "uw_drop_palette")
+
+
+def uw_autotune(ms, proj, batches, max_passes: int = 3, json_path: str | None = None, stream=None):
+    """Returns a list of dicts, one per (batch, projection)."""
+    nproj = max(proj) + 1
+    arr = (ctypes.c_void_p * len(ms))(*[m.handle.value for m in ms])
+    pj = (ctypes.c_int32 * len(proj))(*proj)
+    bs = (ctypes.c_int64 * len(batches))(*batches)
+    out = (uw_tune_entry * (len(batches) * nproj))()
+    _check(_lib.uw_autotune(arr, pj, len(ms), nproj, bs, len(batches), max_passes,
+                            json_path.encode() if json_path else None, out, _stream(stream)), "uw_autotune")
+    return [{f: getattr(e, f) for f, _ in uw_tune_entry._fields_ if f != "reserved"} for e in out]
 
 
 def uw_sync_status(m: Matrix, stream=None) -> int:

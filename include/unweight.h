@@ -219,15 +219,47 @@ typedef struct {
   int64_t batch;
 } uw_job;
 
-/* Run jobs in order.  Preprocessing (decode / transcode) of later jobs runs
- * on `decode_cus` compute units while the GEMMs of earlier jobs use the rest
- * (0 = no split: everything on all CUs, in order).  The workspace holds two
- * preprocessing buffers used alternately, so preprocessing runs at most one
- * job ahead of the GEMMs.  Forks from and joins back to `stream`.
+/* Run jobs in order.  A job's preprocessing (decode / transcode) runs on a
+ * stream masked to D compute units and its GEMM on a stream masked to the
+ * remaining CUs, where D is the job's cfg.decode_cus, or `decode_cus` when
+ * that is 0; D = 0 runs both on `stream`.  GEMMs keep job order; the
+ * workspace holds two preprocessing buffers used alternately, so
+ * preprocessing runs at most one job ahead of the GEMMs and overlaps them.
+ * Forks from and joins back to `stream`.  Calls that overlap on one device
+ * share the library's split streams and must not run concurrently.
  * ([EVC] "解壓與運算資源共享", "跨層管道化") */
 uw_status uw_sequence_workspace_size(const uw_job* jobs, int count, size_t* bytes);
 uw_status uw_run_sequence(const uw_job* jobs, int count, int32_t decode_cus, void* ws_dev,
                           size_t ws_bytes, void* stream);
+
+/* One tuned choice: for `projection` at `batch`. */
+typedef struct {
+  int64_t batch;
+  int32_t projection;
+  int32_t pipeline;             /* uw_pipeline */
+  int32_t variant;              /* uw_kernel_cfg.variant */
+  int32_t split_k;
+  int32_t decode_cus;
+  int32_t reserved;
+  double sequence_us;           /* measured time of the whole tuned sequence at this batch */
+} uw_tune_entry;
+
+/* Autotuner.  ms[0..count) are the resident matrices of a model in execution
+ * order, proj[i] the projection each belongs to (e.g. 0 gate, 1 up, 2 down;
+ * matrices of one projection share a choice).  For each batch it measures
+ * uw_run_sequence over all matrices and runs coordinate descent: projection
+ * 0, then 1, ..., over pipeline x GEMM variant, then the CUs of the
+ * preprocessing kernel, repeating up to max_passes times until no choice
+ * improves the time by 1 %.  Writes out[batch_index * nproj + projection]
+ * (may be NULL) and a JSON configuration file (json_path may be NULL).
+ * Allocates its own x, y and workspace; synchronises `stream`.
+ * ([EVC] "自動調優機制", "解壓與運算資源共享") */
+uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj, int count, int nproj,
+                      const int64_t* batches, int nb, int max_passes, const char* json_path,
+                      uw_tune_entry* out, void* stream);
+
+/* Free resident palette indices (keeps the Huffman form).  Synchronises. */
+uw_status uw_drop_palette(uw_matrix* m, void* stream);
 
 /* Synchronise `stream` and report whether any decoder working on m found an
  * invalid codeword or a segment whose codes overran or underran its words

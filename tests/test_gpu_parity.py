@@ -259,3 +259,37 @@ def test_fallback_decoder_matches(uw, synth, oracle, monkeypatch, sg):
     monkeypatch.setenv("UW_DECODE_DIRECT", "1")
     w = synth.weights(1024, 1024, 0.02, 0.002, 11, seed=40 + sg).to(DEV)
     check_codec(uw, oracle, w, 1024, 1024, 0, sg)
+
+
+def test_sequence_per_job_split_and_autotune(uw, synth, oracle):
+    """Per-job CU splits in one sequence, and the autotuner's choices, keep
+    results within tolerance."""
+    say("sequence per-job split + autotune")
+    specs = [(384, 512, 0), (384, 512, 0), (512, 384, 1)]
+    mats, wnps = [], []
+    for i, (n, k, layout) in enumerate(specs):
+        r, c = (n, k) if layout == 0 else (k, n)
+        w = synth.weights(r, c, 0.02, 0.002, 10, seed=60 + i).to(DEV)
+        m = gpu_compress(uw, w, n, k, layout)
+        uw.uw_transcode_palette(m, None)
+        mats.append(m)
+        wnps.append(bits(w))
+    tuned = uw.uw_autotune(mats, [0, 1, 2], [2, 24], max_passes=1)
+    assert len(tuned) == 6
+    for e in tuned:
+        assert 0 <= e["pipeline"] <= 3 and 0 <= e["variant"] <= uw.variant_count() and e["sequence_us"] > 0
+    for batch in (2, 24):
+        choice = {e["projection"]: e for e in tuned if e["batch"] == batch}
+        jobs, refs = [], []
+        for i, (m, (n, k, layout)) in enumerate(zip(mats, specs)):
+            x = synth.activations(batch, k, seed=70 + i).to(DEV)
+            y = torch.full((batch, n), float("nan"), dtype=torch.float32, device=DEV)
+            c = choice[i]
+            cfg = {"variant": c["variant"], "decode_cus": [0, 32, 128][i]}
+            jobs.append(uw.Job(m, [1, 2, c["pipeline"]][i], x, y, cfg))
+            refs.append((bits(x), wnps[i], layout))
+        ws = torch.empty(uw.uw_sequence_workspace_size(jobs), dtype=torch.uint8, device=DEV)
+        uw.uw_run_sequence(jobs, 16, ws)
+        torch.cuda.synchronize()
+        for j, (x_np, w_np, layout) in zip(jobs, refs):
+            check_gemm(oracle, j.y.cpu().numpy(), x_np, w_np, layout, what=f"tuned batch {batch}")
