@@ -325,7 +325,8 @@ def main() -> int:
     ws_e = torch.empty(numel, dtype=torch.uint8, device=dev)
     ws_p = torch.empty(numel // 2, dtype=torch.uint8, device=dev)
     ys = [torch.empty((1, n), dtype=torch.float32, device=dev) for _ in range(4)]
-    part = torch.empty(16, dtype=torch.uint8, device=dev)   # NK GEMV needs no partials
+    part = torch.empty(max(16, max(uw.uw_workspace_size(mats[0], p, 1) for p in range(4))), dtype=torch.uint8,
+                       device=dev)
     stages = ["decode_full", "gemv_full", "decode_exponent", "gemv_exponent", "transcode", "gemv_transcode",
               "gemv_direct"]
     stream = torch.cuda.current_stream()

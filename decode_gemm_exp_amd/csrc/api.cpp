@@ -631,7 +631,9 @@ uw_status uw_drop_palette(uw_matrix* m, void* stream) {
 
 uw_status uw_workspace_size(const uw_matrix* m, uw_pipeline p, int64_t batch, size_t* bytes) {
   if (!m || !bytes || batch <= 0 || p < UW_PIPE_FULL || p > UW_PIPE_PALETTE_DIRECT) return UW_ERR_INVALID;
-  *bytes = prep_bytes(m, p) + partial_bytes(m, p, batch, nullptr);
+  // enough for any kernel variant a cfg may select at this batch
+  WeightView v = pipeline_view(m, p, nullptr);
+  *bytes = prep_bytes(m, p) + pad256(gemm_partial_elems_max(v, batch, 0) * sizeof(float));
   return UW_OK;
 }
 

@@ -37,6 +37,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---- GEMV, stored [N][K] ----------------------------------------------------------
+// One wave per output row; each lane takes U chunks of 16 weights per pass
+// (K positions lane*16 + u*1024), all loads of a pass issued before any use
+// so that U x (compressed chunk) bytes per lane are in flight.
+constexpr int kGemvU = 4;
+
 template <int FMT, int NB>
 __global__ __launch_bounds__(256) void k_gemv_nk(WeightView w, const uint16_t* __restrict__ x, int B,
                                                  float* __restrict__ y, int64_t ldy, int64_t col0) {
@@ -48,20 +53,34 @@ __global__ __launch_bounds__(256) void k_gemv_nk(WeightView w, const uint16_t* _
     float acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = 0.f;
-    for (uint64_t k = (uint64_t)lane * 16; k < K; k += 1024) {
-      uint32_t wv[8];
-      load16<FMT>(w, n * K + k, wv);
+    for (uint64_t k0 = (uint64_t)lane * 16; k0 < K; k0 += 1024 * kGemvU) {
+      uint32_t wv[kGemvU][8];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if (b < B) {
-          const uint4* xp = reinterpret_cast<const uint4*>(x + (uint64_t)b * K + k);
-          const uint4 x0 = xp[0], x1 = xp[1];
-          float a = acc[b];
-          a = dot2(wv[0], x0.x, a); a = dot2(wv[1], x0.y, a);
-          a = dot2(wv[2], x0.z, a); a = dot2(wv[3], x0.w, a);
-          a = dot2(wv[4], x1.x, a); a = dot2(wv[5], x1.y, a);
-          a = dot2(wv[6], x1.z, a); a = dot2(wv[7], x1.w, a);
-          acc[b] = a;
+      for (int u = 0; u < kGemvU; ++u) {
+        const uint64_t k = k0 + (uint64_t)u * 1024;
+        if (k < K) {
+          load16<FMT>(w, n * K + k, wv[u]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) wv[u][i] = 0;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kGemvU; ++u) {
+        const uint64_t k = k0 + (uint64_t)u * 1024;
+        if (k >= K) break;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (b < B) {
+            const uint4* xp = reinterpret_cast<const uint4*>(x + (uint64_t)b * K + k);
+            const uint4 x0 = xp[0], x1 = xp[1];
+            float a = acc[b];
+            a = dot2(wv[u][0], x0.x, a); a = dot2(wv[u][1], x0.y, a);
+            a = dot2(wv[u][2], x0.z, a); a = dot2(wv[u][3], x0.w, a);
+            a = dot2(wv[u][4], x1.x, a); a = dot2(wv[u][5], x1.y, a);
+            a = dot2(wv[u][6], x1.z, a); a = dot2(wv[u][7], x1.w, a);
+            acc[b] = a;
+          }
         }
       }
     }
@@ -74,54 +93,67 @@ __global__ __launch_bounds__(256) void k_gemv_nk(WeightView w, const uint16_t* _
 }
 
 // ---- GEMV, stored [K][N] -----------------------------------------------------------
-// grid.x: blocks of 512 outputs (64 lanes x 8); grid.y: K slices.  The 4 waves
-// of a block split the slice; their sums meet in LDS; one partial row per
-// slice is written to part[slice][b][n].
+// grid.x: blocks of 1024 outputs (64 lanes x 16); grid.y: K slices.  The 4
+// waves of a block take rows kb + wave, kb + wave + 4, ...; each lane loads
+// kGemvU rows' chunks before using any.  Every wave writes its own partial
+// row part[slice * 4 + wave][b][n]; a second kernel adds them in fixed order.
 template <int FMT, int NB>
 __global__ __launch_bounds__(256) void k_gemv_kn(WeightView w, const uint16_t* __restrict__ x, int B,
                                                  float* __restrict__ part, int64_t rows_per_slice) {
-  __shared__ float red[4][NB][512];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint64_t N = w.n, K = w.k;
-  const uint64_t n0 = (uint64_t)blockIdx.x * 512 + (uint64_t)lane * 8;
+  const uint64_t n0 = (uint64_t)blockIdx.x * 1024 + (uint64_t)lane * 16;
   const uint64_t kb = (uint64_t)blockIdx.y * (uint64_t)rows_per_slice;
   const uint64_t ke = min(kb + (uint64_t)rows_per_slice, K);
-  float acc[NB][8];
+  float acc[NB][16];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[b][i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
   if (n0 < N) {
-    for (uint64_t k = kb + (uint64_t)wave; k < ke; k += 4) {
-      uint32_t wv[4];
-      load8<FMT>(w, k * N + n0, wv);
-      float wf[8];
+    for (uint64_t k0 = kb + (uint64_t)wave; k0 < ke; k0 += 4 * kGemvU) {
+      uint32_t wv[kGemvU][8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wf[2 * i] = __uint_as_float(wv[i] << 16);
-        wf[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
+      for (int u = 0; u < kGemvU; ++u) {
+        const uint64_t k = k0 + (uint64_t)u * 4;
+        if (k < ke) {
+          load16<FMT>(w, k * N + n0, wv[u]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) wv[u][i] = 0;
+        }
       }
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if (b < B) {
-          const float xb = __uint_as_float((uint32_t)x[(uint64_t)b * K + k] << 16);
+      for (int u = 0; u < kGemvU; ++u) {
+        const uint64_t k = k0 + (uint64_t)u * 4;
+        if (k >= ke) break;
+        float wf[16];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[b][i] = fmaf(xb, wf[i], acc[b][i]);
+        for (int i = 0; i < 8; ++i) {
+          wf[2 * i] = __uint_as_float(wv[u][i] << 16);
+          wf[2 * i + 1] = __uint_as_float(wv[u][i] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (b < B) {
+            const float xb = __uint_as_float((uint32_t)x[(uint64_t)b * K + k] << 16);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[b][i] = fmaf(xb, wf[i], acc[b][i]);
+          }
         }
       }
     }
   }
+  if (n0 < N) {
+    const uint64_t slot = (uint64_t)blockIdx.y * 4 + (uint64_t)wave;
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+    for (int b = 0; b < NB; ++b) {
+      if (b < B) {
+        float4* dst = reinterpret_cast<float4*>(part + (slot * (uint64_t)B + (uint64_t)b) * N + n0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) red[wave][b][lane * 8 + i] = acc[b][i];
-  __syncthreads();
-  for (int t = threadIdx.x; t < NB * 512; t += 256) {
-    const int b = t / 512, c = t % 512;
-    const uint64_t n = (uint64_t)blockIdx.x * 512 + (uint64_t)c;
-    if (b < B && n < N) {
-      const float s = ((red[0][b][c] + red[1][b][c]) + red[2][b][c]) + red[3][b][c];
-      part[((uint64_t)blockIdx.y * (uint64_t)B + (uint64_t)b) * N + n] = s;
+        for (int i = 0; i < 4; ++i)
+          dst[i] = make_float4(acc[b][4 * i], acc[b][4 * i + 1], acc[b][4 * i + 2], acc[b][4 * i + 3]);
+      }
     }
   }
 }
@@ -170,10 +202,11 @@ int default_tile(uint64_t n, int64_t batch) {
   return batch <= 64 ? 0 : 1;
 }
 
-// K slices of the KN GEMV: enough blocks to cover the chip a few times.
+// K slices of the KN GEMV: enough blocks to cover the chip a few times
+// (each slice at least 64 rows).
 int kn_slices(const WeightView& w, const uw_kernel_cfg* cfg) {
   if (cfg && cfg->split_k > 0) return cfg->split_k;
-  const uint64_t nblocks = (w.n + 511) / 512;
+  const uint64_t nblocks = (w.n + 1023) / 1024;
   uint64_t s = (1024 + nblocks - 1) / nblocks;
   const uint64_t max_s = (w.k + 63) / 64;
   if (s > max_s) s = max_s;
@@ -192,17 +225,29 @@ static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_c
   return batch <= kGemvMaxBatch ? 1 : 2 + default_tile(w.n, batch);
 }
 
-// Workspace floats for partial sums: enough for every variant (the KN GEMV's
-// K slices, the MFMA split-K slices), so one size serves any kernel choice.
+// Workspace floats for partial sums of the kernel this call resolves to (the
+// KN GEMV's K slices or the MFMA split-K slices).
 size_t gemm_partial_elems(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg) {
-  size_t need = 0;
-  if (w.layout == 1) {
+  const int v = resolve_variant(w, batch, cfg);
+  if (v == 1) {
+    if (w.layout == 0) return 0;
     const int64_t rows = batch < kGemvMaxBatch ? batch : kGemvMaxBatch;
-    need = (size_t)kn_slices(w, cfg) * (size_t)rows * (size_t)w.n;
+    return 4 * (size_t)kn_slices(w, cfg) * (size_t)rows * (size_t)w.n;
   }
-  const int split = cfg ? cfg->split_k : 0;
-  for (int t = 0; t < mfma2_tile_count(); ++t) {
-    const size_t e = mfma2_partial_elems(w, batch, t, split);
+  return mfma2_partial_elems(w, batch, v - 2, cfg ? cfg->split_k : 0);
+}
+
+// The most any variant needs at this batch (split hint as given).
+size_t gemm_partial_elems_max(const WeightView& w, int64_t batch, int split_k) {
+  uw_kernel_cfg c;
+  c.variant = 0;
+  c.split_k = split_k;
+  c.decode_cus = 0;
+  c.reserved = 0;
+  size_t need = 0;
+  for (int v = 1; v <= gemm_variant_count(); ++v) {
+    c.variant = v;
+    const size_t e = gemm_partial_elems(w, batch, &c);
     if (e > need) need = e;
   }
   return need;
@@ -226,15 +271,15 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
         hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(256), 0, s, w, xb, nb, yb, ldy, col0);
       } else {
         const int slices = kn_slices(w, cfg);
-        if (partial == nullptr || partial_elems < (size_t)slices * (size_t)nb * w.n) return hipErrorInvalidValue;
+        if (partial == nullptr || partial_elems < 4 * (size_t)slices * (size_t)nb * w.n) return hipErrorInvalidValue;
         const int64_t rows = (int64_t)((w.k + (uint64_t)slices - 1) / (uint64_t)slices);
         GemvKnFn f = w.fmt == kFmtBf16 ? gemv_kn_fn<kFmtBf16>(nb)
                      : w.fmt == kFmtExp ? gemv_kn_fn<kFmtExp>(nb) : gemv_kn_fn<kFmtPal>(nb);
-        hipLaunchKernelGGL(f, dim3((unsigned)((w.n + 511) / 512), (unsigned)slices), dim3(256), 0, s, w, xb,
+        hipLaunchKernelGGL(f, dim3((unsigned)((w.n + 1023) / 1024), (unsigned)slices), dim3(256), 0, s, w, xb,
                            nb, partial, rows);
         uint64_t rb = ((uint64_t)nb * w.n + 255) / 256;
         if (rb > 4096) rb = 4096;
-        hipLaunchKernelGGL(k_reduce_slices, dim3((unsigned)rb), dim3(256), 0, s, partial, slices, nb, w.n, yb,
+        hipLaunchKernelGGL(k_reduce_slices, dim3((unsigned)rb), dim3(256), 0, s, partial, 4 * slices, nb, w.n, yb,
                            ldy, col0);
       }
       hipError_t e = hipGetLastError();

@@ -107,6 +107,7 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
                        int64_t ldy, int64_t col0, const uw_kernel_cfg* cfg, float* partial,
                        size_t partial_elems, hipStream_t s);
 size_t gemm_partial_elems(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg);
+size_t gemm_partial_elems_max(const WeightView& w, int64_t batch, int split_k);
 int gemm_variant_count();
 // gemm_mfma.hip
 int mfma2_tile_count();
