@@ -118,10 +118,16 @@ uint64_t len_pack(const Tables& t) {
   return p;
 }
 
-void pal_words(const Tables& t, uint32_t out[4]) {
+void pal_words(const Tables& t, PalView* out) {
   for (int i = 0; i < 4; ++i)
-    out[i] = (uint32_t)t.palette[4 * i] | ((uint32_t)t.palette[4 * i + 1] << 8) |
-             ((uint32_t)t.palette[4 * i + 2] << 16) | ((uint32_t)t.palette[4 * i + 3] << 24);
+    out->w[i] = (uint32_t)t.palette[4 * i] | ((uint32_t)t.palette[4 * i + 1] << 8) |
+                ((uint32_t)t.palette[4 * i + 2] << 16) | ((uint32_t)t.palette[4 * i + 3] << 24);
+  // slots >= palette_size never occur outside verbatim groups, so a run of
+  // palette_size consecutive exponents decodes as slot + first entry
+  const uint32_t ps = t.palette_size;
+  out->run = ps > 0 && (uint32_t)t.palette[ps - 1] - (uint32_t)t.palette[0] == ps - 1 &&
+             (uint32_t)t.palette[0] + 15u <= 255u;
+  out->base4 = out->run ? 0x01010101u * (uint32_t)t.palette[0] : 0u;
 }
 
 uw_status upload_lut(uw_matrix* m, hipStream_t s) {
@@ -211,7 +217,7 @@ WeightView base_view(const uw_matrix* m) {
   v.vflags = m->vflags;
   v.vrank = m->vrank;
   v.vexp = m->vexp;
-  pal_words(m->t, v.pal);
+  pal_words(m->t, &v.pal);
   return v;
 }
 
@@ -226,7 +232,7 @@ DecodeArgs decode_args(const uw_matrix* m, void* out) {
   a.vexp = m->vexp;
   a.sm = m->sm;
   a.lut = m->lut;
-  pal_words(m->t, a.pal);
+  pal_words(m->t, &a.pal);
   a.len_pack = len_pack(m->t);
   a.groups = m->groups;
   a.segments = m->segments;

@@ -31,7 +31,7 @@
 // keeps both the per-lane writes and the per-owner reads on distinct banks.
 #include <cstdlib>
 
-#include "uw_internal.h"
+#include "rebuild.h"
 
 namespace uw {
 namespace {
@@ -46,36 +46,6 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 __device__ __forceinline__ uint4 load_chunk(__amdgpu_buffer_rsrc_t r, uint32_t word) {
   u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(word * 4u), 0, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// 4 nibbles (low 16 bits) -> 4 bytes, byte i = nibble i
-__device__ __forceinline__ uint32_t spread_nibbles(uint32_t v) {
-  uint32_t x = v & 0xFFFFu;
-  x = (x | (x << 8)) & 0x00FF00FFu;
-  x = (x | (x << 4)) & 0x0F0F0F0Fu;
-  return x;
-}
-
-// slot bytes (0..15 each) -> palette exponent bytes
-__device__ __forceinline__ uint32_t slots_to_exp(uint32_t sel, uint32_t p0, uint32_t p1, uint32_t p2,
-                                                 uint32_t p3) {
-  const uint32_t s7 = sel & 0x07070707u;
-  const uint32_t lo = __builtin_amdgcn_perm(p1, p0, s7);
-  const uint32_t hi = __builtin_amdgcn_perm(p3, p2, s7);
-  const uint32_t m = ((sel >> 3) & 0x01010101u) * 0xFFu;
-  return (hi & m) | (lo & ~m);
-}
-
-// interleaved bytes [s0 e0 s1 e1] -> two packed bf16: sign to bit 15,
-// exponent to bits 14..7, mantissa to 6..0
-__device__ __forceinline__ uint32_t rebuild2(uint32_t x) {
-  uint32_t r = (x & 0x007F007Fu) | ((x >> 1) & 0x7F807F80u);
-  return r | ((x << 8) & 0x80008000u);
-}
-
-__device__ __forceinline__ void rebuild8(uint32_t s, uint32_t e, uint32_t& o0, uint32_t& o1) {
-  o0 = rebuild2(__builtin_amdgcn_perm(e, s, 0x05010400u));
-  o1 = rebuild2(__builtin_amdgcn_perm(e, s, 0x07030602u));
 }
 
 __device__ __forceinline__ uint32_t stage_at(uint32_t f, uint32_t L) { return f * 64u + (L ^ (f & 63u)); }
@@ -129,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_direct(DecodeArgs a) {
   uint64_t acc = 0;     // pending slot nibbles, first decoded in the low nibble
   int n = 0;
   uint32_t coded_groups = 0;
-  const uint32_t p0 = a.pal[0], p1 = a.pal[1], p2 = a.pal[2], p3 = a.pal[3];
+  const PalView pal = a.pal;
   const uint8_t* __restrict__ vexp = a.vexp;
   const uint8_t* __restrict__ smp = a.sm;
 
@@ -217,10 +187,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_direct(DecodeArgs a) {
           if (MODE == kDecodeNibble) {
             ev[u] = make_uint4(n0, n1, 0, 0);
           } else {
-            ev[u].x = slots_to_exp(spread_nibbles(n0), p0, p1, p2, p3);
-            ev[u].y = slots_to_exp(spread_nibbles(n0 >> 16), p0, p1, p2, p3);
-            ev[u].z = slots_to_exp(spread_nibbles(n1), p0, p1, p2, p3);
-            ev[u].w = slots_to_exp(spread_nibbles(n1 >> 16), p0, p1, p2, p3);
+            ev[u] = pal16(n0, n1, pal);
           }
         }
         if (MODE == kDecodeFull && ok[u]) sv[u] = *reinterpret_cast<const uint4*>(smp + el[u]);
@@ -234,10 +201,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_direct(DecodeArgs a) {
           *reinterpret_cast<uint4*>((uint8_t*)a.out + el[u]) = ev[u];
         } else {
           uint4 o0, o1;
-          rebuild8(sv[u].x, ev[u].x, o0.x, o0.y);
-          rebuild8(sv[u].y, ev[u].y, o0.z, o0.w);
-          rebuild8(sv[u].z, ev[u].z, o1.x, o1.y);
-          rebuild8(sv[u].w, ev[u].w, o1.z, o1.w);
+          rebuild4(sv[u].x, ev[u].x, o0.x, o0.y);
+          rebuild4(sv[u].y, ev[u].y, o0.z, o0.w);
+          rebuild4(sv[u].z, ev[u].z, o1.x, o1.y);
+          rebuild4(sv[u].w, ev[u].w, o1.z, o1.w);
           uint4* dst = reinterpret_cast<uint4*>((uint16_t*)a.out + el[u]);
           dst[0] = o0;
           dst[1] = o1;
@@ -351,7 +318,7 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
     nw = sbuf[p < span ? p : span - 1u];   // a corrupt stream cannot read past the copy
   };
   uint32_t coded_groups = 0;
-  const uint32_t p0 = a.pal[0], p1 = a.pal[1], p2 = a.pal[2], p3 = a.pal[3];
+  const PalView pal = a.pal;
   const uint8_t* __restrict__ vexp = a.vexp;
   const uint8_t* __restrict__ smp = a.sm;
   constexpr uint32_t per_owner = CH * 64u;
@@ -434,10 +401,7 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
         if (MODE == kDecodeNibble) {
           ex = make_uint4(n0, n1, 0, 0);
         } else {
-          ex.x = slots_to_exp(spread_nibbles(n0), p0, p1, p2, p3);
-          ex.y = slots_to_exp(spread_nibbles(n0 >> 16), p0, p1, p2, p3);
-          ex.z = slots_to_exp(spread_nibbles(n1), p0, p1, p2, p3);
-          ex.w = slots_to_exp(spread_nibbles(n1 >> 16), p0, p1, p2, p3);
+          ex = pal16(n0, n1, pal);
         }
       }
       if (MODE == kDecodeNibble) {
@@ -446,10 +410,10 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
         *reinterpret_cast<uint4*>((uint8_t*)a.out + el[u]) = ex;
       } else {
         uint4 o0, o1;
-        rebuild8(sv[u].x, ex.x, o0.x, o0.y);
-        rebuild8(sv[u].y, ex.y, o0.z, o0.w);
-        rebuild8(sv[u].z, ex.z, o1.x, o1.y);
-        rebuild8(sv[u].w, ex.w, o1.z, o1.w);
+        rebuild4(sv[u].x, ex.x, o0.x, o0.y);
+        rebuild4(sv[u].y, ex.y, o0.z, o0.w);
+        rebuild4(sv[u].z, ex.z, o1.x, o1.y);
+        rebuild4(sv[u].w, ex.w, o1.z, o1.w);
         uint4* dst = reinterpret_cast<uint4*>((uint16_t*)a.out + el[u]);
         dst[0] = o0;
         dst[1] = o1;

@@ -10,12 +10,14 @@
 // dimensions need their own kernel (the KN paths below).
 //
 // Two families:
-//   * GEMV (batch <= 8): VALU, v_dot2_f32_bf16 on rebuilt pairs.  NK: one
-//     wave per output row, lanes stride K in 16-weight chunks, wave reduce.
-//     KN: lanes own 8 consecutive outputs, waves stride K, partial sums per
-//     K slice go to the workspace and a second kernel adds them in a fixed
-//     order (deterministic).
-//   * MFMA (batch > 8): gemm_mfma.hip.
+//   * GEMV (batch <= 8 per launch): VALU, v_dot2_f32_bf16 on rebuilt pairs,
+//     software-pipelined so that the loads of the next step are in flight
+//     while the current one is rebuilt.  NK: a wave per output row, lanes
+//     stride K in 16-weight chunks, wave reduction.  KN: lanes own 16
+//     consecutive outputs, waves take row pairs, partial sums per K slice go
+//     to the workspace and a second kernel adds them in a fixed order
+//     (deterministic).
+//   * MFMA: gemm_mfma.hip.
 #include "rebuild.h"
 
 namespace uw {
@@ -36,15 +38,243 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// ---- GEMV, stored [N][K] ----------------------------------------------------------
-// One wave per output row; each lane takes U chunks of 16 weights per pass
-// (K positions lane*16 + u*1024), all loads of a pass issued before any use
-// so that U x (compressed chunk) bytes per lane are in flight.
+// ---- chunk access shared by the pipelined GEMVs ------------------------------
+// One chunk of OW (16 or 8) consecutive stored weights as loaded from HBM.
+// Every load's address is known without waiting for another load: the
+// palette format takes the chunk's verbatim flag word and rank word from an
+// earlier pipeline step and then loads either the chunk's verbatim exponent
+// bytes or the aligned index bytes that hold its OW nibbles.
+template <int OW>
+struct ChunkT {
+  uint32_t a[OW / 2];   // bf16: the OW weights | exp, pal: OW sign+mantissa bytes in a[0 .. OW/4)
+  uint32_t b[OW / 4];   // exp: OW exponent bytes | pal: 2*OW index nibbles or OW verbatim exponent bytes
+};
+
+template <int OW>
+__device__ __forceinline__ void load_words(const void* p, uint32_t* d) {   // OW / 4 dwords
+  if constexpr (OW == 16) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    d[0] = v.x; d[1] = v.y;
+  }
+}
+
+__device__ __forceinline__ uint32_t flag_index(uint64_t el) { return (uint32_t)(el >> 11); }
+
+template <int FMT, int OW>
+__device__ __forceinline__ void chunk_load(const WeightView& w, uint64_t el, uint32_t fw, uint32_t rw, ChunkT<OW>& c) {
+  if constexpr (FMT == kFmtBf16) {
+    load_words<OW>(w.bf16 + el, c.a);
+    load_words<OW>(w.bf16 + el + OW / 2, c.a + OW / 4);
+  } else if constexpr (FMT == kFmtExp) {
+    load_words<OW>(w.sm + el, c.a);
+    load_words<OW>(w.ex + el, c.b);
+  } else {
+    load_words<OW>(w.sm + el, c.a);
+    const uint64_t g = el >> 6;
+    const uint8_t* p = group_verbatim(fw, g) ? w.vexp + (uint64_t)group_rank(fw, rw, g) * 64 + (el & 63)
+                                             : w.pidx + ((el >> 1) & ~(uint64_t)(OW - 1));
+    load_words<OW>(p, c.b);
+  }
+}
+
+// OW / 2 dwords of packed bf16
+template <int FMT, int OW>
+__device__ __forceinline__ void chunk_rebuild(const WeightView& w, const ChunkT<OW>& c, uint64_t el, uint32_t fw,
+                                              uint32_t* o) {
+  if constexpr (FMT == kFmtBf16) {
+#pragma unroll
+    for (int i = 0; i < OW / 2; ++i) o[i] = c.a[i];
+  } else {
+    uint32_t e[OW / 4];
+    if constexpr (FMT == kFmtExp) {
+#pragma unroll
+      for (int i = 0; i < OW / 4; ++i) e[i] = c.b[i];
+    } else {
+      const bool verb = group_verbatim(fw, el >> 6);
+      if constexpr (OW == 16) {
+        const bool hi = (el & 16) != 0;
+        pal8(hi ? c.b[2] : c.b[0], w.pal, e[0], e[1]);
+        pal8(hi ? c.b[3] : c.b[1], w.pal, e[2], e[3]);
+      } else {
+        pal8((el & 8) ? c.b[1] : c.b[0], w.pal, e[0], e[1]);
+      }
+#pragma unroll
+      for (int i = 0; i < OW / 4; ++i) e[i] = verb ? c.b[i] : e[i];
+    }
+#pragma unroll
+    for (int i = 0; i < OW / 4; ++i) rebuild4(c.a[i], e[i], o[2 * i], o[2 * i + 1]);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void flags_load(const WeightView& w, uint64_t el, uint32_t& fw, uint32_t& rw) {
+  if constexpr (FMT == kFmtPal) {
+    fw = w.vflags[flag_index(el)];
+    rw = w.vrank[flag_index(el)];
+  } else {
+    fw = rw = 0;
+  }
+}
+
+__device__ __forceinline__ uint32_t wave_uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// ---- GEMV, stored [N][K], K a multiple of 1024 U --------------------------------
+// Blocks of 16 waves, one block per CU, x rows staged once per block in LDS.
+// A wave owns rows n = wave, wave + nwaves, ... and walks each in steps of
+// 1024 U weights (lane: U chunks of 16 at lane * 16 + u * 1024).  Software
+// pipeline over the wave's steps, two register buffers: while step j is
+// rebuilt and multiplied, the chunks of step j+1 are in flight and the
+// palette flag/rank words of steps j+2, j+3 too.  Row end: wave reduction.
+template <int FMT, int NB, int U>
+__global__ __launch_bounds__(1024) void k_gemv_nk_pipe(WeightView w, const uint16_t* __restrict__ x, int B,
+                                                       float* __restrict__ y, int64_t ldy, int64_t col0) {
+  extern __shared__ uint4 xs4[];   // B rows of K bf16
+  const uint64_t K = w.k, N = w.n;
+  {
+    const uint32_t pieces = (uint32_t)((uint64_t)B * K / 8);
+    const uint4* x4 = reinterpret_cast<const uint4*>(x);
+    for (uint32_t i = threadIdx.x; i < pieces; i += 1024) xs4[i] = x4[i];
+  }
+  __syncthreads();
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(xs4);
+  const int lane = threadIdx.x & 63;
+  const uint64_t wave = (uint64_t)blockIdx.x * 16 + wave_uniform(threadIdx.x >> 6);
+  const uint64_t nw = (uint64_t)gridDim.x * 16;
+  if (wave >= N) return;
+  const uint32_t spr = (uint32_t)(K / (1024u * U));         // steps per row
+  const uint64_t steps = ((N - 1 - wave) / nw + 1) * spr;
+
+  // cursor of a step: row and part; advanced one step at a time
+  struct Cur {
+    uint64_t row;
+    uint32_t part;
+  };
+  auto advance = [&](Cur& c) {
+    if (++c.part == spr) {
+      c.part = 0;
+      c.row += nw;
+    }
+  };
+  auto el_of = [&](const Cur& c, int u) -> uint64_t {
+    return c.row * K + (uint64_t)c.part * (1024u * U) + (uint64_t)u * 1024u + (uint64_t)lane * 16u;
+  };
+
+  ChunkT<16> da[U], db[U];
+  uint32_t fa[U], ra[U], fb[U], rb[U];   // flag/rank words of the chunks in da / db
+  uint32_t ga[U], gha[U], gb[U], ghb[U]; // flag/rank words of the next steps of each parity
+  Cur cc{wave, 0};                       // step being computed
+  Cur cl = cc;                           // next step whose chunks get loaded
+  Cur cf = cc;                           // next step whose flags get loaded
+
+#pragma unroll
+  for (int u = 0; u < U; ++u) flags_load<FMT>(w, el_of(cf, u), fa[u], ra[u]);
+  advance(cf);
+  if (steps > 1) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) flags_load<FMT>(w, el_of(cf, u), fb[u], rb[u]);
+    advance(cf);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) chunk_load<FMT, 16>(w, el_of(cl, u), fa[u], ra[u], da[u]);
+  advance(cl);
+  if (steps > 1) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) chunk_load<FMT, 16>(w, el_of(cl, u), fb[u], rb[u], db[u]);
+    advance(cl);
+  }
+  if (steps > 2) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) flags_load<FMT>(w, el_of(cf, u), ga[u], gha[u]);
+    advance(cf);
+  }
+  if (steps > 3) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) flags_load<FMT>(w, el_of(cf, u), gb[u], ghb[u]);
+    advance(cf);
+  }
+
+  float acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+
+  auto compute = [&](const ChunkT<16>* d, const uint32_t* f) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t o[8];
+      chunk_rebuild<FMT, 16>(w, d[u], el_of(cc, u), f[u], o);
+      const uint64_t k = (uint64_t)cc.part * (1024u * U) + (uint64_t)u * 1024u + (uint64_t)lane * 16u;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (b < B) {
+          const uint4* xp = reinterpret_cast<const uint4*>(xs + (uint64_t)b * K + k);
+          const uint4 x0 = xp[0], x1 = xp[1];
+          float a = acc[b];
+          a = dot2(o[0], x0.x, a); a = dot2(o[1], x0.y, a);
+          a = dot2(o[2], x0.z, a); a = dot2(o[3], x0.w, a);
+          a = dot2(o[4], x1.x, a); a = dot2(o[5], x1.y, a);
+          a = dot2(o[6], x1.z, a); a = dot2(o[7], x1.w, a);
+          acc[b] = a;
+        }
+      }
+    }
+    if (cc.part == spr - 1) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float t = wave_sum(acc[b]);
+        if (b < B && lane == 0) y[(uint64_t)b * ldy + col0 + cc.row] = t;
+        acc[b] = 0.f;
+      }
+    }
+    advance(cc);
+  };
+
+  for (uint64_t j = 0; j < steps; j += 2) {
+    compute(da, fa);
+    if (j + 2 < steps) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        fa[u] = ga[u];
+        ra[u] = gha[u];
+        chunk_load<FMT, 16>(w, el_of(cl, u), fa[u], ra[u], da[u]);
+      }
+      advance(cl);
+      if (j + 4 < steps) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) flags_load<FMT>(w, el_of(cf, u), ga[u], gha[u]);
+        advance(cf);
+      }
+    }
+    if (j + 1 < steps) {
+      compute(db, fb);
+      if (j + 3 < steps) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          fb[u] = gb[u];
+          rb[u] = ghb[u];
+          chunk_load<FMT, 16>(w, el_of(cl, u), fb[u], rb[u], db[u]);
+        }
+        advance(cl);
+        if (j + 5 < steps) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) flags_load<FMT>(w, el_of(cf, u), gb[u], ghb[u]);
+          advance(cf);
+        }
+      }
+    }
+  }
+}
+
+// ---- GEMV, stored [N][K], any K (multiple of 16) ----------------------------------
+// One wave per output row; each lane takes kGemvU chunks of 16 weights per
+// pass (K positions lane*16 + u*1024), loads first, then the products.
 constexpr int kGemvU = 4;
 
 template <int FMT, int NB>
-__global__ __launch_bounds__(256) void k_gemv_nk(WeightView w, const uint16_t* __restrict__ x, int B,
-                                                 float* __restrict__ y, int64_t ldy, int64_t col0) {
+__global__ __launch_bounds__(256) void k_gemv_nk_any(WeightView w, const uint16_t* __restrict__ x, int B,
+                                                     float* __restrict__ y, int64_t ldy, int64_t col0) {
   const int lane = threadIdx.x & 63;
   const uint64_t wave_id = ((uint64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
   const uint64_t nwaves = (uint64_t)gridDim.x * 4;
@@ -93,102 +323,238 @@ __global__ __launch_bounds__(256) void k_gemv_nk(WeightView w, const uint16_t* _
 }
 
 // ---- GEMV, stored [K][N] -----------------------------------------------------------
-// grid.x: blocks of 1024 outputs (64 lanes x 16); grid.y: K slices.  The 4
-// waves of a block take rows kb + wave, kb + wave + 4, ...; each lane loads
-// kGemvU rows' chunks before using any.  Every wave writes its own partial
-// row part[slice * 4 + wave][b][n]; a second kernel adds them in fixed order.
-template <int FMT, int NB>
-__global__ __launch_bounds__(256) void k_gemv_kn(WeightView w, const uint16_t* __restrict__ x, int B,
-                                                 float* __restrict__ part, int64_t rows_per_slice) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Blocks of 8 waves; grid.x: blocks of 64 OW columns (lane: OW = 16 or 8
+// consecutive outputs), grid.y: K slices.  A wave takes row pairs (k, k+1) of its slice,
+// pairs wave, wave + 8, ..., U pairs per pipeline step (same two-buffer
+// pipeline as the NK kernel).  The two rows' rebuilt weights are interleaved
+// per column so that one v_dot2 multiplies (w[k][n], w[k+1][n]) with
+// (x[k], x[k+1]).  x pairs are wave-uniform scalar loads.  At the end the 8
+// waves' sums meet in LDS (fixed order) and the block writes one partial row
+// per batch row: part[slice][b][n].
+constexpr int kKnWaves = 8;
+
+template <int FMT, int NB, int U, int OW>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NB <= 4 ? 4 : 2))) void k_gemv_kn(WeightView w, const uint16_t* __restrict__ x, int B,
+                                                 float* __restrict__ part, uint32_t pairs_per_slice) {
+  constexpr int BW = 64 * OW;   // columns per block
+  __shared__ float red[kKnWaves][BW];
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = wave_uniform(threadIdx.x >> 6);
   const uint64_t N = w.n, K = w.k;
-  const uint64_t n0 = (uint64_t)blockIdx.x * 1024 + (uint64_t)lane * 16;
-  const uint64_t kb = (uint64_t)blockIdx.y * (uint64_t)rows_per_slice;
-  const uint64_t ke = min(kb + (uint64_t)rows_per_slice, K);
-  float acc[NB][16];
+  const uint64_t n = (uint64_t)blockIdx.x * BW + (uint64_t)lane * OW;
+  const bool nval = n < N;
+  const uint64_t ncl = nval ? n : 0;                     // loads of columns past N read column 0
+  const uint64_t kb = (uint64_t)blockIdx.y * 2u * pairs_per_slice;
+  const uint64_t ke = kb + 2u * (uint64_t)pairs_per_slice < K ? kb + 2u * (uint64_t)pairs_per_slice : K;
+  const uint32_t pairs = kb < ke ? (uint32_t)((ke - kb + 1) / 2) : 0u;
+  const uint32_t mine = pairs > wave ? (pairs - 1 - wave) / kKnWaves + 1 : 0u;
+  const uint32_t steps = (mine + U - 1) / U;
+
+  // row of chunk h (0, 1) of pair slot u in step j; rows past the slice are
+  // clamped for addressing and get x = 0
+  auto row_of = [&](uint32_t j, int u, int h) -> uint64_t {
+    return kb + 2u * (uint64_t)(wave + kKnWaves * (j * U + (uint32_t)u)) + (uint64_t)h;
+  };
+  auto el_of = [&](uint64_t k) -> uint64_t { return (k < K ? k : K - 1) * N + ncl; };
+
+  ChunkT<OW> da[U][2], db[U][2];
+  uint32_t fa[U][2], ra[U][2], fb[U][2], rb[U][2];
+  uint32_t ga[U][2], gha[U][2], gb[U][2], ghb[U][2];
+
+  auto load_flags = [&](uint32_t j, uint32_t (*f)[2], uint32_t (*r)[2]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) flags_load<FMT>(w, el_of(row_of(j, u, h)), f[u][h], r[u][h]);
+  };
+  auto load_chunks = [&](uint32_t j, ChunkT<OW> (*d)[2], uint32_t (*f)[2], uint32_t (*r)[2]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) chunk_load<FMT, OW>(w, el_of(row_of(j, u, h)), f[u][h], r[u][h], d[u][h]);
+  };
+
+  float acc[NB][OW];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
-  if (n0 < N) {
-    for (uint64_t k0 = kb + (uint64_t)wave; k0 < ke; k0 += 4 * kGemvU) {
-      uint32_t wv[kGemvU][8];
+    for (int i = 0; i < OW; ++i) acc[b][i] = 0.f;
+
+  auto compute = [&](uint32_t j, ChunkT<OW> (*d)[2], uint32_t (*f)[2]) {
 #pragma unroll
-      for (int u = 0; u < kGemvU; ++u) {
-        const uint64_t k = k0 + (uint64_t)u * 4;
-        if (k < ke) {
-          load16<FMT>(w, k * N + n0, wv[u]);
-        } else {
+    for (int u = 0; u < U; ++u) {
+      const uint64_t k = row_of(j, u, 0);
+      uint32_t o0[OW / 2], o1[OW / 2];
+      chunk_rebuild<FMT, OW>(w, d[u][0], el_of(k), f[u][0], o0);
+      chunk_rebuild<FMT, OW>(w, d[u][1], el_of(k + 1), f[u][1], o1);
+      uint32_t xv[NB];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) wv[u][i] = 0;
+      for (int b = 0; b < NB; ++b) {
+        xv[b] = 0;
+        if (b < B) {
+          const uint16_t* xr = x + (uint64_t)b * K;
+          if (k + 1 < ke) xv[b] = *reinterpret_cast<const uint32_t*>(xr + k);
+          else if (k < ke) xv[b] = (uint32_t)xr[k];
         }
       }
 #pragma unroll
-      for (int u = 0; u < kGemvU; ++u) {
-        const uint64_t k = k0 + (uint64_t)u * 4;
-        if (k >= ke) break;
-        float wf[16];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          wf[2 * i] = __uint_as_float(wv[u][i] << 16);
-          wf[2 * i + 1] = __uint_as_float(wv[u][i] & 0xFFFF0000u);
-        }
+      for (int i = 0; i < OW / 2; ++i) {
+        const uint32_t plo = __builtin_amdgcn_perm(o1[i], o0[i], 0x05040100u);
+        const uint32_t phi = __builtin_amdgcn_perm(o1[i], o0[i], 0x07060302u);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           if (b < B) {
-            const float xb = __uint_as_float((uint32_t)x[(uint64_t)b * K + k] << 16);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[b][i] = fmaf(xb, wf[i], acc[b][i]);
+            acc[b][2 * i] = dot2(plo, xv[b], acc[b][2 * i]);
+            acc[b][2 * i + 1] = dot2(phi, xv[b], acc[b][2 * i + 1]);
           }
         }
       }
     }
-  }
-  if (n0 < N) {
-    const uint64_t slot = (uint64_t)blockIdx.y * 4 + (uint64_t)wave;
+  };
+
+  if (steps > 0) load_flags(0, fa, ra);
+  if (steps > 1) load_flags(1, fb, rb);
+  if (steps > 0) load_chunks(0, da, fa, ra);
+  if (steps > 1) load_chunks(1, db, fb, rb);
+  if (steps > 2) load_flags(2, ga, gha);
+  if (steps > 3) load_flags(3, gb, ghb);
+  for (uint32_t j = 0; j < steps; j += 2) {
+    compute(j, da, fa);
+    if (j + 2 < steps) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (b < B) {
-        float4* dst = reinterpret_cast<float4*>(part + (slot * (uint64_t)B + (uint64_t)b) * N + n0);
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          dst[i] = make_float4(acc[b][4 * i], acc[b][4 * i + 1], acc[b][4 * i + 2], acc[b][4 * i + 3]);
+        for (int h = 0; h < 2; ++h) {
+          fa[u][h] = ga[u][h];
+          ra[u][h] = gha[u][h];
+        }
+      load_chunks(j + 2, da, fa, ra);
+      if (j + 4 < steps) load_flags(j + 4, ga, gha);
+    }
+    if (j + 1 < steps) {
+      compute(j + 1, db, fb);
+      if (j + 3 < steps) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            fb[u][h] = gb[u][h];
+            rb[u][h] = ghb[u][h];
+          }
+        load_chunks(j + 3, db, fb, rb);
+        if (j + 5 < steps) load_flags(j + 5, gb, ghb);
       }
     }
   }
-}
 
-__global__ __launch_bounds__(256) void k_reduce_slices(const float* __restrict__ part, int slices, int B,
-                                                       uint64_t N, float* __restrict__ y, int64_t ldy,
-                                                       int64_t col0) {
-  const uint64_t total = (uint64_t)B * N;
-  for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (uint64_t)gridDim.x * 256) {
-    const uint64_t b = i / N, n = i % N;
-    float s = 0.f;
-    for (int p = 0; p < slices; ++p) s += part[(uint64_t)p * total + i];
-    y[b * (uint64_t)ldy + (uint64_t)col0 + n] = s;
+  // the block's waves, added in wave order, one batch row at a time
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b >= B) break;
+    float4* mine4 = reinterpret_cast<float4*>(&red[wave][lane * OW]);
+#pragma unroll
+    for (int i = 0; i < OW / 4; ++i)
+      mine4[i] = make_float4(acc[b][4 * i], acc[b][4 * i + 1], acc[b][4 * i + 2], acc[b][4 * i + 3]);
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < BW / 512; ++h) {
+      const uint32_t c = threadIdx.x + 512u * (uint32_t)h;
+      float s = red[0][c];
+#pragma unroll
+      for (int v = 1; v < kKnWaves; ++v) s += red[v][c];
+      const uint64_t col = (uint64_t)blockIdx.x * BW + c;
+      if (col < N) part[((uint64_t)blockIdx.y * (uint64_t)B + (uint64_t)b) * N + col] = s;
+    }
+    __syncthreads();
   }
 }
 
-typedef void (*GemvNkFn)(WeightView, const uint16_t*, int, float*, int64_t, int64_t);
-typedef void (*GemvKnFn)(WeightView, const uint16_t*, int, float*, int64_t);
+// y[b][col0 + n] = sum over slices p of part[p][b][n].  Block: 4 waves on 64
+// consecutive outputs of one batch row (grid.y = b); wave q adds slices
+// q*L .. q*L+L-1 in order (loads batched 8 at a time), then the four wave
+// sums are added in order q = 0..3 -- a fixed order, so results repeat
+// bit for bit.
+__global__ __launch_bounds__(256) void k_sum_slices(const float* __restrict__ part, int slices, uint64_t N,
+                                                    int64_t B, int64_t b0, float* __restrict__ y, int64_t ldy,
+                                                    int64_t col0) {
+  __shared__ float sums[4][64];
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const uint64_t n = (uint64_t)blockIdx.x * 64 + (uint64_t)lane;
+  const uint64_t b = (uint64_t)b0 + blockIdx.y;
+  const uint64_t stride = (uint64_t)B * N;
+  const int L = (slices + 3) / 4;
+  const int p0 = q * L, p1 = p0 + L < slices ? p0 + L : slices;
+  float s = 0.f;
+  if (n < N) {
+    const float* src = part + b * N + n;
+    for (int p = p0; p < p1; p += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = p + u < p1 ? src[(uint64_t)(p + u) * stride] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (p + u < p1) s += v[u];
+    }
+  }
+  sums[q][lane] = s;
+  __syncthreads();
+  if (q == 0 && n < N) y[b * (uint64_t)ldy + (uint64_t)col0 + n] = ((sums[0][lane] + sums[1][lane]) + sums[2][lane]) + sums[3][lane];
+}
 
-template <int F>
-GemvNkFn gemv_nk_fn(int nb) {
-  if (nb <= 1) return k_gemv_nk<F, 1>;
-  if (nb <= 2) return k_gemv_nk<F, 2>;
-  if (nb <= 4) return k_gemv_nk<F, 4>;
-  return k_gemv_nk<F, 8>;
+typedef void (*GemvNkFn)(WeightView, const uint16_t*, int, float*, int64_t, int64_t);
+typedef void (*GemvKnFn)(WeightView, const uint16_t*, int, float*, uint32_t);
+
+template <int F, int U>
+GemvNkFn gemv_nk_pipe_nb(int nb) {
+  if (nb <= 1) return k_gemv_nk_pipe<F, 1, U>;
+  if (nb <= 2) return k_gemv_nk_pipe<F, 2, U>;
+  if (nb <= 4) return k_gemv_nk_pipe<F, 4, (U > 2 ? 2 : U)>;
+  return k_gemv_nk_pipe<F, 8, (U > 2 ? 2 : U)>;
 }
 template <int F>
+GemvNkFn gemv_nk_pipe_fn(int nb, int u) {
+  return u == 4 ? gemv_nk_pipe_nb<F, 4>(nb) : u == 2 ? gemv_nk_pipe_nb<F, 2>(nb) : gemv_nk_pipe_nb<F, 1>(nb);
+}
+template <int F>
+GemvNkFn gemv_nk_any_fn(int nb) {
+  if (nb <= 1) return k_gemv_nk_any<F, 1>;
+  if (nb <= 2) return k_gemv_nk_any<F, 2>;
+  if (nb <= 4) return k_gemv_nk_any<F, 4>;
+  return k_gemv_nk_any<F, 8>;
+}
+// outputs per lane of the KN GEMV for a launch of nb batch rows
+int kn_ow(int nb) { return nb <= 1 ? 16 : 8; }
+template <int F>
 GemvKnFn gemv_kn_fn(int nb) {
-  if (nb <= 1) return k_gemv_kn<F, 1>;
-  if (nb <= 2) return k_gemv_kn<F, 2>;
-  if (nb <= 4) return k_gemv_kn<F, 4>;
-  return k_gemv_kn<F, 8>;
+  if (nb <= 1) return k_gemv_kn<F, 1, 1, 16>;
+  if (nb <= 2) return k_gemv_kn<F, 2, 1, 8>;
+  if (nb <= 4) return k_gemv_kn<F, 4, 1, 8>;
+  return k_gemv_kn<F, 8, 1, 8>;
 }
 
 constexpr int kGemvMaxBatch = 8;
+constexpr size_t kNkLdsMax = 160 * 1024;
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cached[dev] = c;
+  }
+  return cached[dev];
+}
+
+// chunks per lane per step of the pipelined NK GEMV (0: shape not covered)
+int nk_pipe_u(const WeightView& w, int nb) {
+  if ((uint64_t)nb * w.k * 2 > kNkLdsMax) return 0;
+  if (w.k % 4096 == 0) return 4;
+  if (w.k % 2048 == 0) return 2;
+  if (w.k % 1024 == 0) return 1;
+  return 0;
+}
 
 // largest MFMA tile whose grid alone covers the chip; else 128 x 128 with split K
 int default_tile(uint64_t n, int64_t batch) {
@@ -202,14 +568,22 @@ int default_tile(uint64_t n, int64_t batch) {
   return batch <= 64 ? 0 : 1;
 }
 
-// K slices of the KN GEMV: enough blocks to cover the chip a few times
-// (each slice at least 64 rows).
-int kn_slices(const WeightView& w, const uw_kernel_cfg* cfg) {
-  if (cfg && cfg->split_k > 0) return cfg->split_k;
-  const uint64_t nblocks = (w.n + 1023) / 1024;
-  uint64_t s = (1024 + nblocks - 1) / nblocks;
-  const uint64_t max_s = (w.k + 63) / 64;
-  if (s > max_s) s = max_s;
+// K slices of the KN GEMV: about two 8-wave blocks per CU over the grid,
+// each wave with at least two pipeline steps of row pairs.
+int kn_slices(const WeightView& w, int nb, const uw_kernel_cfg* cfg) {
+  const uint64_t pairs = (w.k + 1) / 2;
+  uint64_t s;
+  if (cfg && cfg->split_k > 0) {
+    s = (uint64_t)cfg->split_k;
+  } else {
+    const uint64_t bw = 64u * (uint64_t)kn_ow(nb);
+    const uint64_t nblocks = (w.n + bw - 1) / bw;
+    const uint64_t target = 2 * (uint64_t)device_cus();
+    s = (target + nblocks - 1) / nblocks;
+    const uint64_t max_s = pairs / (kKnWaves * 4);
+    if (s > max_s) s = max_s;
+  }
+  if (s > pairs) s = pairs;
   if (s < 1) s = 1;
   return (int)s;
 }
@@ -232,7 +606,7 @@ size_t gemm_partial_elems(const WeightView& w, int64_t batch, const uw_kernel_cf
   if (v == 1) {
     if (w.layout == 0) return 0;
     const int64_t rows = batch < kGemvMaxBatch ? batch : kGemvMaxBatch;
-    return 4 * (size_t)kn_slices(w, cfg) * (size_t)rows * (size_t)w.n;
+    return (size_t)kn_slices(w, (int)rows, cfg) * (size_t)rows * (size_t)w.n;
   }
   return mfma2_partial_elems(w, batch, v - 2, cfg ? cfg->split_k : 0);
 }
@@ -253,6 +627,18 @@ size_t gemm_partial_elems_max(const WeightView& w, int64_t batch, int split_k) {
   return need;
 }
 
+hipError_t launch_sum_slices(const float* part, int slices, uint64_t n, int64_t batch, float* y, int64_t ldy,
+                             int64_t col0, hipStream_t s) {
+  for (int64_t b0 = 0; b0 < batch; b0 += 65535) {
+    const int64_t nb = batch - b0 < 65535 ? batch - b0 : 65535;
+    hipLaunchKernelGGL(k_sum_slices, dim3((unsigned)((n + 63) / 64), (unsigned)nb), dim3(256), 0, s, part, slices, n,
+                       batch, b0, y, ldy, col0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, float* y, int64_t ldy,
                        int64_t col0, const uw_kernel_cfg* cfg, float* partial, size_t partial_elems,
                        hipStream_t s) {
@@ -264,23 +650,44 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
       const uint16_t* xb = x + (uint64_t)b0 * w.k;
       float* yb = y + (uint64_t)b0 * (uint64_t)ldy;
       if (w.layout == 0) {
-        GemvNkFn f = w.fmt == kFmtBf16 ? gemv_nk_fn<kFmtBf16>(nb)
-                     : w.fmt == kFmtExp ? gemv_nk_fn<kFmtExp>(nb) : gemv_nk_fn<kFmtPal>(nb);
-        uint64_t blocks = (w.n + 3) / 4;
-        if (blocks > 8192) blocks = 8192;
-        hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(256), 0, s, w, xb, nb, yb, ldy, col0);
+        const int u = nk_pipe_u(w, nb);
+        if (u > 0) {
+          GemvNkFn f = w.fmt == kFmtBf16 ? gemv_nk_pipe_fn<kFmtBf16>(nb, u)
+                       : w.fmt == kFmtExp ? gemv_nk_pipe_fn<kFmtExp>(nb, u) : gemv_nk_pipe_fn<kFmtPal>(nb, u);
+          const size_t lds = (size_t)nb * w.k * 2;
+          static bool lds_set[3][4][3] = {};
+          const int fi = w.fmt, ni = nb <= 1 ? 0 : nb <= 2 ? 1 : nb <= 4 ? 2 : 3, ui = u == 4 ? 2 : u == 2 ? 1 : 0;
+          if (!lds_set[fi][ni][ui]) {
+            hipError_t e = hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)kNkLdsMax);
+            if (e != hipSuccess) return e;
+            lds_set[fi][ni][ui] = true;
+          }
+          uint64_t blocks = (uint64_t)device_cus();
+          const uint64_t need = (w.n + 15) / 16;
+          if (blocks > need) blocks = need;
+          hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(1024), lds, s, w, xb, nb, yb, ldy, col0);
+        } else {
+          GemvNkFn f = w.fmt == kFmtBf16 ? gemv_nk_any_fn<kFmtBf16>(nb)
+                       : w.fmt == kFmtExp ? gemv_nk_any_fn<kFmtExp>(nb) : gemv_nk_any_fn<kFmtPal>(nb);
+          uint64_t blocks = (w.n + 3) / 4;
+          if (blocks > 8192) blocks = 8192;
+          hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(256), 0, s, w, xb, nb, yb, ldy, col0);
+        }
       } else {
-        const int slices = kn_slices(w, cfg);
-        if (partial == nullptr || partial_elems < 4 * (size_t)slices * (size_t)nb * w.n) return hipErrorInvalidValue;
-        const int64_t rows = (int64_t)((w.k + (uint64_t)slices - 1) / (uint64_t)slices);
+        const int slices = kn_slices(w, nb, cfg);
+        if (partial == nullptr || partial_elems < (size_t)slices * (size_t)nb * w.n) return hipErrorInvalidValue;
+        const uint64_t pairs = (w.k + 1) / 2;
+        const uint32_t pps = (uint32_t)((pairs + (uint64_t)slices - 1) / (uint64_t)slices);
+        const unsigned gy = (unsigned)((pairs + pps - 1) / pps);
         GemvKnFn f = w.fmt == kFmtBf16 ? gemv_kn_fn<kFmtBf16>(nb)
                      : w.fmt == kFmtExp ? gemv_kn_fn<kFmtExp>(nb) : gemv_kn_fn<kFmtPal>(nb);
-        hipLaunchKernelGGL(f, dim3((unsigned)((w.n + 1023) / 1024), (unsigned)slices), dim3(256), 0, s, w, xb,
-                           nb, partial, rows);
-        uint64_t rb = ((uint64_t)nb * w.n + 255) / 256;
-        if (rb > 4096) rb = 4096;
-        hipLaunchKernelGGL(k_reduce_slices, dim3((unsigned)rb), dim3(256), 0, s, partial, 4 * slices, nb, w.n, yb,
-                           ldy, col0);
+        const uint64_t bw = 64u * (uint64_t)kn_ow(nb);
+        hipLaunchKernelGGL(f, dim3((unsigned)((w.n + bw - 1) / bw), gy), dim3(512), 0, s, w, xb, nb, partial, pps);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        e = launch_sum_slices(partial, (int)gy, w.n, nb, yb, ldy, col0, s);
+        if (e != hipSuccess) return e;
       }
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;

@@ -34,8 +34,8 @@ constexpr int kLDK = kBK + 8;   // bf16 per LDS row: 144 bytes keeps 16-byte ali
 // Raw compressed data of one 16-weight chunk, as loaded from HBM.
 struct Raw {
   uint4 a;      // bf16: weights 0..7 | exp/pal: 16 sign+mantissa bytes
-  uint4 b;      // bf16: weights 8..15 | exp: 16 exponent bytes | pal: 8 index bytes in .x .y,
-                //   or the 16 verbatim exponent bytes when .z has bit 0 set
+  uint4 b;      // bf16: weights 8..15 | exp: 16 exponent bytes | pal: the aligned 16 index
+                //   bytes holding the chunk's 8, or its 16 verbatim exponent bytes
 };
 
 template <int FMT>
@@ -56,19 +56,16 @@ __device__ __forceinline__ void load_raw(const WeightView& w, uint64_t el, bool 
   } else {
     r.a = *reinterpret_cast<const uint4*>(w.sm + el);
     const uint64_t g = el >> 6;
-    if ((flagword >> (g & 31)) & 1u) {
-      const uint32_t rank = rankword + (uint32_t)__popc(flagword & ((1u << (g & 31)) - 1u));
-      r.b = *reinterpret_cast<const uint4*>(w.vexp + (uint64_t)rank * 64 + (el & 63));
-    } else {
-      const uint2 nib = *reinterpret_cast<const uint2*>(w.pidx + el / 2);
-      r.b = make_uint4(nib.x, nib.y, 0, 0);
-    }
+    const uint8_t* p = group_verbatim(flagword, g)
+                           ? w.vexp + (uint64_t)group_rank(flagword, rankword, g) * 64 + (el & 63)
+                           : w.pidx + ((el >> 1) & ~(uint64_t)15);
+    r.b = *reinterpret_cast<const uint4*>(p);
   }
 }
 
 // Rebuild 16 weights (8 dwords of packed bf16) from a raw chunk.
 template <int FMT>
-__device__ __forceinline__ void rebuild_raw(const WeightView& w, const Raw& r, bool valid, bool verbatim,
+__device__ __forceinline__ void rebuild_raw(const WeightView& w, const Raw& r, bool valid, bool verbatim, bool hi,
                                             uint32_t o[8]) {
   if (!valid) {   // outside the matrix: exact zeros (a K tail multiplies them by zero x)
 #pragma unroll
@@ -81,15 +78,8 @@ __device__ __forceinline__ void rebuild_raw(const WeightView& w, const Raw& r, b
   } else if constexpr (FMT == kFmtExp) {
     rebuild16(r.a, r.b, o);
   } else {
-    uint4 e;
-    if (verbatim) {
-      e = r.b;
-    } else {
-      e.x = pal_lookup(nib_spread(r.b.x), w.pal);
-      e.y = pal_lookup(nib_spread(r.b.x >> 16), w.pal);
-      e.z = pal_lookup(nib_spread(r.b.y), w.pal);
-      e.w = pal_lookup(nib_spread(r.b.y >> 16), w.pal);
-    }
+    uint4 e = pal16(hi ? r.b.z : r.b.x, hi ? r.b.w : r.b.y, w.pal);
+    if (verbatim) e = r.b;
     rebuild16(r.a, e, o);
   }
 }
@@ -133,7 +123,7 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
 
   uint4 xr[XC];
   Raw wr[WC];
-  bool wverb[WC], wval[WC];
+  bool wverb[WC], wval[WC], whi[WC];
   uint32_t fw_next[WC], rk_next[WC];   // palette: flag / rank words of the step after the loaded one
 
   auto load_flags = [&](int64_t k0, uint32_t* fw, uint32_t* rk) {
@@ -159,7 +149,8 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
       const uint64_t el = chunk_el(i, k0, v);
       load_raw<FMT>(w, el, v, fw[i], rk[i], wr[i]);
       wval[i] = v;
-      wverb[i] = FMT == kFmtPal && v && ((fw[i] >> ((el >> 6) & 31)) & 1u);
+      wverb[i] = FMT == kFmtPal && v && group_verbatim(fw[i], el >> 6);
+      whi[i] = (el & 16) != 0;
     }
   };
 
@@ -194,7 +185,7 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
 #pragma unroll
     for (int i = 0; i < WC; ++i) {
       uint32_t o[8];
-      rebuild_raw<FMT>(w, wr[i], wval[i], wverb[i], o);
+      rebuild_raw<FMT>(w, wr[i], wval[i], wverb[i], whi[i], o);
       const int c = tid + i * 256;
       if constexpr (LAYOUT == 0) {
         uint4* d = reinterpret_cast<uint4*>(&ws[(c >> 2) * kLDK + (c & 3) * 16]);
@@ -259,18 +250,6 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
         const int64_t col = n0 + wn * WN + j * 32 + (lane & 31);
         if (row < B && col < N) out[row * ld + col] = acc[i][j][r];
       }
-}
-
-// y[b][col0 + n] = sum over K slices of part[slice][b][n] (fixed order)
-__global__ __launch_bounds__(256) void k_sum_slices(const float* __restrict__ part, int slices, int B, int64_t N,
-                                                    int64_t ldy, int64_t col0, float* __restrict__ y) {
-  const uint64_t total = (uint64_t)B * (uint64_t)N;
-  for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (uint64_t)gridDim.x * 256) {
-    const uint64_t b = i / (uint64_t)N, n = i % (uint64_t)N;
-    float s = 0.f;
-    for (int p = 0; p < slices; ++p) s += part[(uint64_t)p * total + i];
-    y[b * (uint64_t)ldy + (uint64_t)col0 + n] = s;
-  }
 }
 
 typedef void (*Mfma2Fn)(WeightView, const uint16_t*, int, float*, int64_t, int64_t, int64_t, float*);
@@ -343,13 +322,9 @@ hipError_t launch_mfma2(const WeightView& w, const uint16_t* x, int64_t batch, f
   dim3 grid((unsigned)((w.n + (uint64_t)t.bn - 1) / (uint64_t)t.bn), (unsigned)((batch + t.bm - 1) / t.bm),
             (unsigned)slices);
   hipLaunchKernelGGL(f, grid, dim3(256), lds, s, w, x, (int)batch, y, ldy, col0, kslice, split ? part : nullptr);
-  if (split) {
-    uint64_t rb = ((uint64_t)batch * w.n + 255) / 256;
-    if (rb > 8192) rb = 8192;
-    hipLaunchKernelGGL(k_sum_slices, dim3((unsigned)rb), dim3(256), 0, s, part, slices, (int)batch, (int64_t)w.n, ldy,
-                       col0, y);
-  }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !split) return e;
+  return launch_sum_slices(part, slices, w.n, batch, y, ldy, col0, s);
 }
 
 }  // namespace uw

@@ -1,4 +1,5 @@
-// rebuild.h -- on-chip BF16 reconstruction shared by the GEMM kernels.
+// rebuild.h -- on-chip BF16 reconstruction shared by the decoder and the GEMM
+// kernels.
 //
 // [EVC] = "Cloudflare推出Unweight無損壓縮系統，將LLM模型大小壓縮15-22%"
 // (easyvibecoding.app/curated/736).  Section "BF16權重壓縮原理": the weight
@@ -6,39 +7,34 @@
 // "重建矩陣乘法核心運作": the matmul joins exponent and sign+mantissa back
 // into BF16 on chip.  Section "BF16權重壓縮原理" also fixes the verbatim
 // rule: one flag per 64-weight group, tested once per group, never per weight.
+//
+// Byte-parallel forms (four weights per 32-bit operation):
+//   * a BF16 weight is two bytes: lo = exponent bit 0 above the 7 mantissa
+//     bits, hi = sign above exponent bits 7..1.  From 4 sign+mantissa bytes s
+//     and 4 exponent bytes e, lo = bfi(0x80.., e << 7, s) and
+//     hi = bfi(0x80.., s, e >> 1); two byte permutes interleave them into two
+//     dwords of packed BF16 -- 6 VALU operations per 4 weights;
+//   * 8 palette slots packed as nibbles (element i in nibble i) split into
+//     even and odd elements with one mask each; a 16-entry palette is two
+//     8-byte permute tables, the slot's bit 3 picks the table through a third
+//     permute; a palette that is a run of consecutive exponents needs only a
+//     bytewise add.  Two permutes restore element order.
 #pragma once
 
 #include "uw_internal.h"
 
 namespace uw {
 
-// 4 nibbles (low 16 bits) -> 4 bytes, byte i = nibble i
-__device__ __forceinline__ uint32_t nib_spread(uint32_t v) {
-  uint32_t x = v & 0xFFFFu;
-  x = (x | (x << 8)) & 0x00FF00FFu;
-  x = (x | (x << 4)) & 0x0F0F0F0Fu;
-  return x;
-}
+constexpr uint32_t kHiBits = 0x80808080u;
 
-// 4 slot bytes -> 4 palette exponent bytes (v_perm over the 16 palette bytes)
-__device__ __forceinline__ uint32_t pal_lookup(uint32_t sel, const uint32_t* pal) {
-  const uint32_t s7 = sel & 0x07070707u;
-  const uint32_t lo = __builtin_amdgcn_perm(pal[1], pal[0], s7);
-  const uint32_t hi = __builtin_amdgcn_perm(pal[3], pal[2], s7);
-  const uint32_t m = ((sel >> 3) & 0x01010101u) * 0xFFu;
-  return (hi & m) | (lo & ~m);
-}
-
-// interleaved bytes [s0 e0 s1 e1] -> two packed bf16
-__device__ __forceinline__ uint32_t rebuild_pair(uint32_t x) {
-  uint32_t r = (x & 0x007F007Fu) | ((x >> 1) & 0x7F807F80u);
-  return r | ((x << 8) & 0x80008000u);
-}
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) { return (mask & a) | (~mask & b); }
 
 // 4 sign+mantissa bytes + 4 exponent bytes -> 4 bf16 in two dwords
 __device__ __forceinline__ void rebuild4(uint32_t s, uint32_t e, uint32_t& o0, uint32_t& o1) {
-  o0 = rebuild_pair(__builtin_amdgcn_perm(e, s, 0x05010400u));
-  o1 = rebuild_pair(__builtin_amdgcn_perm(e, s, 0x07030602u));
+  const uint32_t lo = bfi(kHiBits, e << 7, s);
+  const uint32_t hi = bfi(kHiBits, s, e >> 1);
+  o0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  o1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
 }
 
 __device__ __forceinline__ void rebuild16(const uint4& s, const uint4& e, uint32_t o[8]) {
@@ -46,6 +42,44 @@ __device__ __forceinline__ void rebuild16(const uint4& s, const uint4& e, uint32
   rebuild4(s.y, e.y, o[2], o[3]);
   rebuild4(s.z, e.z, o[4], o[5]);
   rebuild4(s.w, e.w, o[6], o[7]);
+}
+
+// 4 slot bytes (0..15) -> 4 palette exponent bytes
+__device__ __forceinline__ uint32_t pal_lookup4(uint32_t n, const PalView& p) {
+  const uint32_t n7 = n & 0x07070707u;
+  const uint32_t lo = __builtin_amdgcn_perm(p.w[1], p.w[0], n7);
+  const uint32_t hi = __builtin_amdgcn_perm(p.w[3], p.w[2], n7);
+  return __builtin_amdgcn_perm(hi, lo, ((n >> 1) & 0x04040404u) | 0x03020100u);
+}
+
+// 8 slots as nibbles (element i in bits 4i..4i+3) -> exponent bytes of
+// elements 0..3 (e03) and 4..7 (e47)
+__device__ __forceinline__ void pal8(uint32_t v, const PalView& p, uint32_t& e03, uint32_t& e47) {
+  uint32_t ev = v & 0x0F0F0F0Fu;           // elements 0 2 4 6
+  uint32_t od = (v >> 4) & 0x0F0F0F0Fu;    // elements 1 3 5 7
+  if (p.run) {
+    ev += p.base4;
+    od += p.base4;
+  } else {
+    ev = pal_lookup4(ev, p);
+    od = pal_lookup4(od, p);
+  }
+  e03 = __builtin_amdgcn_perm(od, ev, 0x05010400u);
+  e47 = __builtin_amdgcn_perm(od, ev, 0x07030602u);
+}
+
+// 16 slots (two dwords of nibbles) -> 16 exponent bytes
+__device__ __forceinline__ uint4 pal16(uint32_t v0, uint32_t v1, const PalView& p) {
+  uint4 e;
+  pal8(v0, p, e.x, e.y);
+  pal8(v1, p, e.z, e.w);
+  return e;
+}
+
+// verbatim flag and rank of group g from its flag and rank words
+__device__ __forceinline__ bool group_verbatim(uint32_t fw, uint64_t g) { return (fw >> (g & 31)) & 1u; }
+__device__ __forceinline__ uint32_t group_rank(uint32_t fw, uint32_t rw, uint64_t g) {
+  return rw + (uint32_t)__popc(fw & ((1u << (g & 31)) - 1u));
 }
 
 // 16 consecutive stored weights starting at stored index `el` (el % 16 == 0)
@@ -67,45 +101,13 @@ __device__ __forceinline__ void load16(const WeightView& w, uint64_t el, uint32_
     const uint64_t g = el >> 6;
     const uint32_t fw = w.vflags[g >> 5];
     uint4 e;
-    if ((fw >> (g & 31)) & 1u) {   // verbatim group: exponents from the side section
-      const uint32_t r = w.vrank[g >> 5] + (uint32_t)__popc(fw & ((1u << (g & 31)) - 1u));
+    if (group_verbatim(fw, g)) {   // verbatim group: exponents from the side section
+      const uint32_t r = group_rank(fw, w.vrank[g >> 5], g);
       e = *reinterpret_cast<const uint4*>(w.vexp + (uint64_t)r * 64 + (el & 63));
     } else {
-      e.x = pal_lookup(nib_spread(nib.x), w.pal);
-      e.y = pal_lookup(nib_spread(nib.x >> 16), w.pal);
-      e.z = pal_lookup(nib_spread(nib.y), w.pal);
-      e.w = pal_lookup(nib_spread(nib.y >> 16), w.pal);
+      e = pal16(nib.x, nib.y, w.pal);
     }
     rebuild16(s, e, o);
-  }
-}
-
-// 8 consecutive stored weights at `el` (el % 8 == 0) -> 4 dwords of bf16
-template <int FMT>
-__device__ __forceinline__ void load8(const WeightView& w, uint64_t el, uint32_t o[4]) {
-  if constexpr (FMT == kFmtBf16) {
-    const uint4 a = *reinterpret_cast<const uint4*>(w.bf16 + el);
-    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-  } else if constexpr (FMT == kFmtExp) {
-    const uint2 s = *reinterpret_cast<const uint2*>(w.sm + el);
-    const uint2 e = *reinterpret_cast<const uint2*>(w.ex + el);
-    rebuild4(s.x, e.x, o[0], o[1]);
-    rebuild4(s.y, e.y, o[2], o[3]);
-  } else {
-    const uint2 s = *reinterpret_cast<const uint2*>(w.sm + el);
-    const uint32_t nib = *reinterpret_cast<const uint32_t*>(w.pidx + el / 2);
-    const uint64_t g = el >> 6;
-    const uint32_t fw = w.vflags[g >> 5];
-    uint2 e;
-    if ((fw >> (g & 31)) & 1u) {
-      const uint32_t r = w.vrank[g >> 5] + (uint32_t)__popc(fw & ((1u << (g & 31)) - 1u));
-      e = *reinterpret_cast<const uint2*>(w.vexp + (uint64_t)r * 64 + (el & 63));
-    } else {
-      e.x = pal_lookup(nib_spread(nib), w.pal);
-      e.y = pal_lookup(nib_spread(nib >> 16), w.pal);
-    }
-    rebuild4(s.x, e.x, o[0], o[1]);
-    rebuild4(s.y, e.y, o[2], o[3]);
   }
 }
 

@@ -73,6 +73,14 @@ hipError_t launch_encode(const uint16_t* w, uint64_t groups, uint32_t seg_groups
                          const uint32_t* codebook, const uint32_t* vflags, const uint32_t* vrank,
                          const uint32_t* seg_off, uint32_t* stream, uint8_t* vexp, hipStream_t s);
 
+// The palette as seen by kernels: 16 exponent bytes in 4 words; when its
+// entries are consecutive exponents, run = 1 and base4 = first entry x 0x01010101.
+struct PalView {
+  uint32_t w[4];
+  uint32_t run;
+  uint32_t base4;
+};
+
 enum DecodeMode { kDecodeNibble = 0, kDecodeExponent = 1, kDecodeFull = 2 };
 struct DecodeArgs {
   const uint32_t* stream; uint64_t stream_words;   // including slack
@@ -80,7 +88,7 @@ struct DecodeArgs {
   const uint32_t* vflags; const uint32_t* vrank; const uint8_t* vexp;
   const uint8_t* sm;
   const uint32_t* lut;
-  uint32_t pal[4];                                  // palette bytes
+  PalView pal;
   uint64_t len_pack;                                // 4-bit code length per slot
   uint64_t groups, segments; uint32_t seg_groups;
   uint32_t wave_span;                               // see uw_matrix::wave_span
@@ -100,7 +108,7 @@ struct WeightView {
   const uint8_t* ex;                // kFmtExp: exponent bytes
   const uint8_t* pidx;              // kFmtPal
   const uint32_t* vflags; const uint32_t* vrank; const uint8_t* vexp;   // kFmtPal
-  uint32_t pal[4];
+  PalView pal;
 };
 // y[:, col0 : col0+n] of a row-major [batch][ldy] output
 hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, float* y,
@@ -109,6 +117,9 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
 size_t gemm_partial_elems(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg);
 size_t gemm_partial_elems_max(const WeightView& w, int64_t batch, int split_k);
 int gemm_variant_count();
+// y[b][col0 + n] = sum over slices p of part[p][b][n], fixed order
+hipError_t launch_sum_slices(const float* part, int slices, uint64_t n, int64_t batch, float* y, int64_t ldy,
+                             int64_t col0, hipStream_t s);
 // gemm_mfma.hip
 int mfma2_tile_count();
 int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint);

@@ -185,6 +185,41 @@ def test_gemm_ragged_all_pipelines(uw, synth, oracle, layout, batch):
         check_gemm(oracle, y, x_np, w_np, layout, what=f"variant {v}")
 
 
+def _palette_is_run(m):
+    info = m.info()
+    pal = list(info.palette)[:info.palette_size]
+    return pal[-1] - pal[0] == info.palette_size - 1
+
+
+# stored shapes for the vector (small-batch) kernels: NK rows with K a multiple
+# of 4096 / 2048 / 1024 (the pipelined kernel, U = 4 / 2 / 1), an NK shape it
+# does not cover, and KN shapes with several K slices, odd row-pair counts and
+# a partial last column block.  outlier_frac picks verbatim-rich weights (a
+# palette with a gap) or none (a palette that is a run of exponents).
+@pytest.mark.parametrize("n,k,layout,outliers", [
+    (300, 4096, 0, 0.01), (70, 2048, 0, 0.0), (33, 1024, 0, 0.01), (200, 3072, 0, 0.0), (40, 1088, 0, 0.01),
+    (192, 2008, 1, 0.01), (1088, 1032, 1, 0.0), (64, 520, 1, 0.01),
+])
+def test_gemv_shapes(uw, synth, oracle, n, k, layout, outliers):
+    r, c = (n, k) if layout == 0 else (k, n)
+    say(f"gemv shapes n={n} k={k} layout={layout} outliers={outliers}")
+    w = synth.weights(r, c, 0.02, outliers, 10, seed=n + k).to(DEV)
+    m = gpu_compress(uw, w, n, k, layout)
+    uw.uw_transcode_palette(m, None)
+    assert _palette_is_run(m) == (outliers == 0.0)
+    w_np = bits(w)
+    for batch in (1, 2, 3, 8, 9):
+        x = synth.activations(batch, k, seed=batch).to(DEV)
+        x_np = bits(x)
+        for p in range(4):
+            y = run_pipeline(uw, m, p, x, cfg={"variant": 1})
+            check_gemm(oracle, y, x_np, w_np, layout, what=f"batch {batch} pipeline {p}")
+        if layout == 1:
+            for split in (1, 7):
+                y = run_pipeline(uw, m, 3, x, cfg={"variant": 1, "split_k": split})
+                check_gemm(oracle, y, x_np, w_np, layout, what=f"batch {batch} split {split}")
+
+
 @pytest.mark.parametrize("layout", [0, 1])
 def test_gemm_one_hot_exact(uw, synth, oracle, layout):
     """x row j one-hot at k_j: y[j][n] must equal W[n][k_j] exactly."""
