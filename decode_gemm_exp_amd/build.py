@@ -23,8 +23,7 @@ def _compile(src: str) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, src + ".o")
     cmd = [HIPCC] + COMMON + ["-I", CSRC]
-    if src.endswith(".hip"):
-        cmd += GPU
+    cmd += GPU   # host-only sources too, so no default-arch device pass is made
     cmd += ["-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
