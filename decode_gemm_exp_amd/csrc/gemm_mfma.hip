@@ -10,14 +10,20 @@
 // every weight tile is rebuilt once per tile of batch rows.
 //
 // Structure (256 threads, 4 waves in a WGM x WGN grid, tile BM x BN, K step 64):
-//   * the x tile and the rebuilt weight tile live in LDS, double buffered;
-//   * while the waves run the MFMAs of step s, every thread already holds in
-//     registers the raw data of step s+1 (x rows and compressed weights), and
-//     for the palette format the verbatim flag words of step s+2, so the
-//     dependent side-section loads of verbatim groups never stall;
+//   * the x tile and the rebuilt weight tile live in LDS, double buffered,
+//     one barrier per step;
+//   * step s: the waves run the MFMAs of step s from one buffer while, in the
+//     same instruction stream, every thread rebuilds step s+1 from registers
+//     into the other buffer and requests the raw data of step s+2 (x rows and
+//     compressed weights); for the palette format the verbatim flag words are
+//     loaded one step earlier still, so the side-section address of a
+//     verbatim group is known when its data is requested;
 //   * each weight is rebuilt once per block (not once per wave) straight into
-//     LDS: NK rows with 16-byte stores, KN rows transposed with 16-bit stores;
+//     LDS with 16-byte stores: NK tiles n-major, KN tiles k-major; KN B
+//     fragments come from the k-major tile through transposing LDS reads
+//     (ds_read_b64_tr_b16), so no 16-bit scatter is needed;
 //   * waves read A and B fragments from LDS and issue v_mfma_f32_32x32x16_bf16;
+//   * block order is XCD-aware (see block_tile);
 //   * split K: grid.z slices of K write partial tiles to the workspace and a
 //     fixed-order reduction adds them (deterministic).
 #include "rebuild.h"
@@ -38,14 +44,14 @@ struct Raw {
                 //   bytes holding the chunk's 8, or its 16 verbatim exponent bytes
 };
 
+// Raw loads of one chunk.  Straight-line code: a chunk outside the matrix
+// reads chunk 0 instead (valid memory) and is zeroed when rebuilt, so that the
+// loads, the rebuild and the MFMAs of a step stay in one basic block for the
+// scheduler to interleave.
 template <int FMT>
 __device__ __forceinline__ void load_raw(const WeightView& w, uint64_t el, bool valid, uint32_t flagword,
                                          uint32_t rankword, Raw& r) {
-  if (!valid) {
-    r.a = make_uint4(0, 0, 0, 0);
-    r.b = make_uint4(0, 0, 0, 0);
-    return;
-  }
+  el = valid ? el : 0;
   if constexpr (FMT == kFmtBf16) {
     const uint4* p = reinterpret_cast<const uint4*>(w.bf16 + el);
     r.a = p[0];
@@ -56,22 +62,18 @@ __device__ __forceinline__ void load_raw(const WeightView& w, uint64_t el, bool 
   } else {
     r.a = *reinterpret_cast<const uint4*>(w.sm + el);
     const uint64_t g = el >> 6;
-    const uint8_t* p = group_verbatim(flagword, g)
+    const uint8_t* p = valid && group_verbatim(flagword, g)
                            ? w.vexp + (uint64_t)group_rank(flagword, rankword, g) * 64 + (el & 63)
                            : w.pidx + ((el >> 1) & ~(uint64_t)15);
     r.b = *reinterpret_cast<const uint4*>(p);
   }
 }
 
-// Rebuild 16 weights (8 dwords of packed bf16) from a raw chunk.
+// Rebuild 16 weights (8 dwords of packed bf16) from a raw chunk; chunks
+// outside the matrix give exact zeros (a K tail multiplies them by zero x).
 template <int FMT>
 __device__ __forceinline__ void rebuild_raw(const WeightView& w, const Raw& r, bool valid, bool verbatim, bool hi,
                                             uint32_t o[8]) {
-  if (!valid) {   // outside the matrix: exact zeros (a K tail multiplies them by zero x)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = 0;
-    return;
-  }
   if constexpr (FMT == kFmtBf16) {
     o[0] = r.a.x; o[1] = r.a.y; o[2] = r.a.z; o[3] = r.a.w;
     o[4] = r.b.x; o[5] = r.b.y; o[6] = r.b.z; o[7] = r.b.w;
@@ -82,32 +84,76 @@ __device__ __forceinline__ void rebuild_raw(const WeightView& w, const Raw& r, b
     if (verbatim) e = r.b;
     rebuild16(r.a, e, o);
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = valid ? o[i] : 0u;
 }
+
+typedef __attribute__((ext_vector_type(4))) short v4i16;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// B fragment (32 columns x 16 k) from a k-major LDS tile [k][n] through two
+// transposing reads: in each 16-lane group, source lane s addresses row
+// k + s/4 and columns c + 4 (s % 4); lane i of the group then holds column
+// c + i of those 4 rows.  Group g covers columns 16 (g & 1) and k rows
+// 8 (g >> 1), which is the v_mfma_f32_32x32x16_bf16 B operand layout.
+__device__ __forceinline__ bf16x8 b_frag_kmajor(const uint16_t* wt, int ldw, int kk, int col0, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int row = kk + 8 * (g >> 1) + (s >> 2);
+  const int col = col0 + 16 * (g & 1) + 4 * (s & 3);
+  const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(wt + row * ldw + col));
+  const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(wt + (row + 4) * ldw + col));
+  typedef __attribute__((ext_vector_type(8))) short v8i16;
+  const v8i16 v = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Tile of a block: when the N tiles split evenly over the 8 XCDs (blocks are
+// dealt to XCDs round-robin), all M tiles of an N tile run on one XCD, one
+// after another, so its L2 serves the rebuilt-weight tile's compressed data to
+// every M tile and the 32 blocks resident on an XCD share x rows.
+__device__ __forceinline__ void block_tile(int b, int ntiles, int mtiles, int& nt, int& mt) {
+  if ((ntiles & 7) == 0) {
+    const int xcd = b & 7, l = b >> 3;
+    nt = xcd + 8 * (l / mtiles);
+    mt = l % mtiles;
+  } else {
+    nt = b / mtiles;
+    mt = b % mtiles;
+  }
+}
+
+template <int LAYOUT, int BN>
+constexpr int w_ld() { return LAYOUT == 0 ? kLDK : BN + 16; }   // KN rows: BN + 16 keeps transposing reads conflict-light
+template <int LAYOUT, int BN>
+constexpr int w_tile_elems() { return LAYOUT == 0 ? BN * kLDK : kBK * (BN + 16); }
 
 template <int LAYOUT, int FMT, int BM, int BN, int WGM>
 __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __restrict__ x, int B,
                                                float* __restrict__ y, int64_t ldy, int64_t col0,
-                                               int64_t kslice, float* __restrict__ part) {
+                                               int64_t kslice, float* __restrict__ part, int ntiles, int mtiles) {
   constexpr int WGN = 4 / WGM;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int XC = BM * 8 / 256;     // 16-byte x chunks per thread per step
   constexpr int WC = BN * 4 / 256;     // 16-weight chunks per thread per step
+  constexpr int LDW = w_ld<LAYOUT, BN>();
+  constexpr int XS = BM * kLDK, WS = w_tile_elems<LAYOUT, BN>();
   static_assert(TM >= 1 && TN >= 1 && XC >= 1 && WC >= 1, "tile too small");
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  uint16_t* Xs = lds;                          // [2][BM * kLDK]
-  uint16_t* Ws = lds + 2 * BM * kLDK;          // [2][BN * kLDK]  (row = n, column = k)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int64_t N = (int64_t)w.n, K = (int64_t)w.k;
-  const int64_t n0 = (int64_t)blockIdx.x * BN, m0 = (int64_t)blockIdx.y * BM;
+  int nt, mt;
+  block_tile((int)blockIdx.x, ntiles, mtiles, nt, mt);
+  const int64_t n0 = (int64_t)nt * BN, m0 = (int64_t)mt * BM;
   const int64_t kb = (int64_t)blockIdx.z * kslice;
   const int64_t ke = kb + kslice < K ? kb + kslice : K;
+  const int steps = (int)((ke - kb + kBK - 1) / kBK);
 
   // chunk c of this thread (i-th): NK -> row r = c / 4, k sub-block q = c % 4;
   // KN -> k row kr = c / (BN/16), n sub-block q = c % (BN/16)
-  auto chunk_el = [&](int i, int64_t k0, bool& valid) -> uint64_t {
+  auto chunk_el = [&](int i, int64_t k0, bool& valid) __attribute__((always_inline)) -> uint64_t {
     const int c = tid + i * 256;
     if constexpr (LAYOUT == 0) {
       const int64_t n = n0 + (c >> 2), k = k0 + (c & 3) * 16;
@@ -124,33 +170,69 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
   uint4 xr[XC];
   Raw wr[WC];
   bool wverb[WC], wval[WC], whi[WC];
-  uint32_t fw_next[WC], rk_next[WC];   // palette: flag / rank words of the step after the loaded one
+  uint32_t fw_a[WC], rk_a[WC];   // palette: flag / rank words of the step whose data loads next
 
-  auto load_flags = [&](int64_t k0, uint32_t* fw, uint32_t* rk) {
+  // The per-step work is split into four parts (one per 16-wide k slice of
+  // the MFMAs); chunk i of the loads and stores belongs to part (4 i) / n.
+  auto in_part = [](int i, int n, int part) __attribute__((always_inline)) { return (4 * i) / n == part; };
+  auto load_flags = [&](int64_t k0, int part) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < WC; ++i) {
+      if (!in_part(i, WC, part)) continue;
       bool v;
       const uint64_t el = chunk_el(i, k0, v);
-      const uint64_t g = el >> 6;
-      fw[i] = v ? w.vflags[g >> 5] : 0u;
-      rk[i] = v ? w.vrank[g >> 5] : 0u;
+      const uint64_t fi = v ? el >> 11 : 0;
+      const uint32_t f = w.vflags[fi], r = w.vrank[fi];
+      fw_a[i] = v ? f : 0u;
+      rk_a[i] = v ? r : 0u;
     }
   };
-  auto load_step = [&](int64_t k0, const uint32_t* fw, const uint32_t* rk) {
+  auto load_step = [&](int64_t k0, int part) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < XC; ++i) {
+      if (!in_part(i, XC, part)) continue;
+      // rows past the batch are never stored and k past the slice meets zeroed
+      // weight rows, so x needs only a clamped (always valid) address
       const int c = tid + i * 256;
-      const int64_t row = m0 + (c >> 3), kk = k0 + (c & 7) * 8;
-      xr[i] = (row < B && kk < ke) ? *reinterpret_cast<const uint4*>(x + row * K + kk) : make_uint4(0, 0, 0, 0);
+      const int64_t row0 = m0 + (c >> 3), kk0 = k0 + (c & 7) * 8;
+      const int64_t row = row0 < B ? row0 : B - 1, kk = kk0 < K ? kk0 : K - 8;
+      const uint4 t = *reinterpret_cast<const uint4*>(x + row * K + kk);
+      xr[i] = t;
     }
 #pragma unroll
     for (int i = 0; i < WC; ++i) {
+      if (!in_part(i, WC, part)) continue;
       bool v;
       const uint64_t el = chunk_el(i, k0, v);
-      load_raw<FMT>(w, el, v, fw[i], rk[i], wr[i]);
+      load_raw<FMT>(w, el, v, fw_a[i], rk_a[i], wr[i]);
       wval[i] = v;
-      wverb[i] = FMT == kFmtPal && v && group_verbatim(fw[i], el >> 6);
+      wverb[i] = FMT == kFmtPal && v && group_verbatim(fw_a[i], el >> 6);
       whi[i] = (el & 16) != 0;
+    }
+  };
+  // registers of a step -> LDS buffer (x as is, weights rebuilt)
+  auto store_step = [&](uint16_t* xs, uint16_t* ws, int part) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      if (!in_part(i, XC, part)) continue;
+      const int c = tid + i * 256;
+      *reinterpret_cast<uint4*>(&xs[(c >> 3) * kLDK + (c & 7) * 8]) = xr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < WC; ++i) {
+      if (!in_part(i, WC, part)) continue;
+      uint32_t o[8];
+      rebuild_raw<FMT>(w, wr[i], wval[i], wverb[i], whi[i], o);
+      const int c = tid + i * 256;
+      uint4* d;
+      if constexpr (LAYOUT == 0) {
+        d = reinterpret_cast<uint4*>(&ws[(c >> 2) * kLDK + (c & 3) * 16]);
+      } else {
+        constexpr int QN = BN / 16;
+        d = reinterpret_cast<uint4*>(&ws[(c / QN) * LDW + (c % QN) * 16]);
+      }
+      d[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      d[1] = make_uint4(o[4], o[5], o[6], o[7]);
     }
   };
 
@@ -162,79 +244,85 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  uint32_t fw_cur[WC], rk_cur[WC];
-  if constexpr (FMT == kFmtPal) {
-    load_flags(kb, fw_cur, rk_cur);
-    load_flags(kb + kBK, fw_next, rk_next);
-  } else {
+  // fragments of one 16-wide k slice, two sets: the next slice is read from
+  // LDS while the MFMAs of the current one issue
+  bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+  auto read_frags = [&](const uint16_t* xs, const uint16_t* ws, int kk, bf16x8 (&a)[TM],
+                        bf16x8 (&b)[TN]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < WC; ++i) fw_cur[i] = rk_cur[i] = fw_next[i] = rk_next[i] = 0;
-  }
-  load_step(kb, fw_cur, rk_cur);
-
-  int buf = 0;
-  for (int64_t k0 = kb; k0 < ke; k0 += kBK) {
-    uint16_t* xs = Xs + buf * BM * kLDK;
-    uint16_t* ws = Ws + buf * BN * kLDK;
-    // ---- registers of step k0 -> LDS (x as is, weights rebuilt) ----
-#pragma unroll
-    for (int i = 0; i < XC; ++i) {
-      const int c = tid + i * 256;
-      *reinterpret_cast<uint4*>(&xs[(c >> 3) * kLDK + (c & 7) * 8]) = xr[i];
+    for (int i = 0; i < TM; ++i) {
+      const int row = wm * WM + i * 32 + (lane & 31);
+      a[i] = *reinterpret_cast<const bf16x8*>(&xs[row * kLDK + kk + 8 * (lane >> 5)]);
     }
 #pragma unroll
-    for (int i = 0; i < WC; ++i) {
-      uint32_t o[8];
-      rebuild_raw<FMT>(w, wr[i], wval[i], wverb[i], whi[i], o);
-      const int c = tid + i * 256;
+    for (int j = 0; j < TN; ++j) {
       if constexpr (LAYOUT == 0) {
-        uint4* d = reinterpret_cast<uint4*>(&ws[(c >> 2) * kLDK + (c & 3) * 16]);
-        d[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        d[1] = make_uint4(o[4], o[5], o[6], o[7]);
-      } else {
-        constexpr int QN = BN / 16;
-        const int kr = c / QN, q = c % QN;
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          ws[(q * 16 + e) * kLDK + kr] = (uint16_t)((o[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-      }
-    }
-    // ---- raw data of the next step -> registers (latency hidden by the MFMAs) ----
-    if (k0 + kBK < ke) {
-      if constexpr (FMT == kFmtPal) {
-#pragma unroll
-        for (int i = 0; i < WC; ++i) {
-          fw_cur[i] = fw_next[i];
-          rk_cur[i] = rk_next[i];
-        }
-        load_step(k0 + kBK, fw_cur, rk_cur);
-        if (k0 + 2 * kBK < ke) load_flags(k0 + 2 * kBK, fw_next, rk_next);
-      } else {
-        load_step(k0 + kBK, fw_cur, rk_cur);
-      }
-    }
-    __syncthreads();
-    // ---- MFMA over the step ----
-#pragma unroll
-    for (int kk = 0; kk < kBK; kk += 16) {
-      bf16x8 a[TM], b[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * WM + i * 32 + (lane & 31);
-        a[i] = *reinterpret_cast<const bf16x8*>(&xs[row * kLDK + kk + 8 * (lane >> 5)]);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
         const int col = wn * WN + j * 32 + (lane & 31);
         b[j] = *reinterpret_cast<const bf16x8*>(&ws[col * kLDK + kk + 8 * (lane >> 5)]);
+      } else {
+        b[j] = b_frag_kmajor(ws, LDW, kk, wn * WN + j * 32, lane);
       }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    buf ^= 1;
+  };
+  auto mfma_set = [&](const bf16x8 (&a)[TM], const bf16x8 (&b)[TN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+
+  uint16_t* const xs0 = lds;
+  uint16_t* const xs1 = lds + XS;
+  uint16_t* const ws0 = lds + 2 * XS;
+  uint16_t* const ws1 = lds + 2 * XS + WS;
+
+  // prologue: step 0 in LDS buffer 0, step 1 in registers, flags of step 2 loaded
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    if constexpr (FMT == kFmtPal) load_flags(kb, p);
+    load_step(kb, p);
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    if constexpr (FMT == kFmtPal) load_flags(kb + kBK, p);
+    store_step(xs0, ws0, p);
+    load_step(kb + kBK, p);
+    if constexpr (FMT == kFmtPal) load_flags(kb + 2 * kBK, p);
+  }
+
+  // step s: MFMAs from buffer s & 1 while step s+1 is rebuilt into the other
+  // buffer and the raw data of step s+2 is requested; one barrier per step.
+  // The last steps rebuild and load past the K range (clamped, zeroed, never
+  // read) instead of branching, so every part is one basic block.
+  auto body = [&](int st, const uint16_t* xs_c, const uint16_t* ws_c, uint16_t* xs_n, uint16_t* ws_n) __attribute__((always_inline)) {
+    __syncthreads();
+    const int64_t k2 = kb + (int64_t)(st + 2) * kBK, k3 = k2 + kBK;
+    // part p: the MFMAs of k slice p (fragments read one part earlier), the
+    // next slice's fragment reads, and a quarter of the next step's rebuild
+    // and of the raw loads two steps ahead
+    auto rest = [&](int p) __attribute__((always_inline)) {
+      store_step(xs_n, ws_n, p);
+      load_step(k2, p);
+      if constexpr (FMT == kFmtPal) load_flags(k3, p);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    read_frags(xs_c, ws_c, 0, fa0, fb0);
+    read_frags(xs_c, ws_c, 16, fa1, fb1);
+    mfma_set(fa0, fb0);
+    rest(0);
+    read_frags(xs_c, ws_c, 32, fa0, fb0);
+    mfma_set(fa1, fb1);
+    rest(1);
+    read_frags(xs_c, ws_c, 48, fa1, fb1);
+    mfma_set(fa0, fb0);
+    rest(2);
+    mfma_set(fa1, fb1);
+    rest(3);
+  };
+  for (int st = 0; st < steps; ++st) {
+    const bool odd = st & 1;
+    body(st, odd ? xs1 : xs0, odd ? ws1 : ws0, odd ? xs0 : xs1, odd ? ws0 : ws1);
   }
 
   // ---- epilogue: y, or this K slice's partial tile part[slice][row][col] ----
@@ -252,13 +340,13 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
       }
 }
 
-typedef void (*Mfma2Fn)(WeightView, const uint16_t*, int, float*, int64_t, int64_t, int64_t, float*);
+typedef void (*Mfma2Fn)(WeightView, const uint16_t*, int, float*, int64_t, int64_t, int64_t, float*, int, int);
 
 template <int L, int F, int BM, int BN, int WGM>
 Mfma2Fn prepared() {
   static bool done = false;
   if (!done) {
-    const int lds = (int)(2 * (BM + BN) * kLDK * sizeof(uint16_t));
+    const int lds = (int)(2 * (BM * kLDK + w_tile_elems<L, BN>()) * sizeof(uint16_t));
     (void)hipFuncSetAttribute((const void*)k_mfma2<L, F, BM, BN, WGM>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               lds);
     done = true;
@@ -318,10 +406,13 @@ hipError_t launch_mfma2(const WeightView& w, const uint16_t* x, int64_t batch, f
   } else {
     f = w.fmt == kFmtBf16 ? pick<1, kFmtBf16>(tile) : w.fmt == kFmtExp ? pick<1, kFmtExp>(tile) : pick<1, kFmtPal>(tile);
   }
-  const size_t lds = 2 * (size_t)(t.bm + t.bn) * kLDK * sizeof(uint16_t);
-  dim3 grid((unsigned)((w.n + (uint64_t)t.bn - 1) / (uint64_t)t.bn), (unsigned)((batch + t.bm - 1) / t.bm),
-            (unsigned)slices);
-  hipLaunchKernelGGL(f, grid, dim3(256), lds, s, w, x, (int)batch, y, ldy, col0, kslice, split ? part : nullptr);
+  const size_t wtile = w.layout == 0 ? (size_t)t.bn * kLDK : (size_t)kBK * (size_t)(t.bn + 16);
+  const size_t lds = 2 * ((size_t)t.bm * kLDK + wtile) * sizeof(uint16_t);
+  const int ntiles = (int)((w.n + (uint64_t)t.bn - 1) / (uint64_t)t.bn);
+  const int mtiles = (int)((batch + t.bm - 1) / t.bm);
+  dim3 grid((unsigned)(ntiles * mtiles), 1, (unsigned)slices);
+  hipLaunchKernelGGL(f, grid, dim3(256), lds, s, w, x, (int)batch, y, ldy, col0, kslice, split ? part : nullptr, ntiles,
+                     mtiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   return launch_sum_slices(part, slices, w.n, batch, y, ldy, col0, s);
