@@ -256,8 +256,8 @@ WeightView pipeline_view(const uw_matrix* m, int p, const void* buf) {
   switch (p) {
     case UW_PIPE_FULL: v.fmt = kFmtBf16; v.bf16 = static_cast<const uint16_t*>(buf); break;
     case UW_PIPE_EXPONENT: v.fmt = kFmtExp; v.ex = static_cast<const uint8_t*>(buf); break;
-    case UW_PIPE_PALETTE_TRANSCODE: v.fmt = kFmtPal; v.pidx = static_cast<const uint8_t*>(buf); break;
-    default: v.fmt = kFmtPal; v.pidx = m->pidx; break;
+    case UW_PIPE_PALETTE_TRANSCODE: v.fmt = v.pal.run ? kFmtPalRun : kFmtPal; v.pidx = static_cast<const uint8_t*>(buf); break;
+    default: v.fmt = v.pal.run ? kFmtPalRun : kFmtPal; v.pidx = m->pidx; break;
   }
   return v;
 }

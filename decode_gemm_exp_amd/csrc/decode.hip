@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_direct(DecodeArgs a) {
           if (MODE == kDecodeNibble) {
             ev[u] = make_uint4(n0, n1, 0, 0);
           } else {
-            ev[u] = pal16(n0, n1, pal);
+            ev[u] = pal16_any(n0, n1, pal);
           }
         }
         if (MODE == kDecodeFull && ok[u]) sv[u] = *reinterpret_cast<const uint4*>(smp + el[u]);
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
         if (MODE == kDecodeNibble) {
           ex = make_uint4(n0, n1, 0, 0);
         } else {
-          ex = pal16(n0, n1, pal);
+          ex = pal16_any(n0, n1, pal);
         }
       }
       if (MODE == kDecodeNibble) {

@@ -18,6 +18,8 @@
 //     to the workspace and a second kernel adds them in a fixed order
 //     (deterministic).
 //   * MFMA: gemm_mfma.hip.
+#include <cmath>
+
 #include "rebuild.h"
 
 namespace uw {
@@ -96,10 +98,10 @@ __device__ __forceinline__ void chunk_rebuild(const WeightView& w, const ChunkT<
       const bool verb = group_verbatim(fw, el >> 6);
       if constexpr (OW == 16) {
         const bool hi = (el & 16) != 0;
-        pal8(hi ? c.b[2] : c.b[0], w.pal, e[0], e[1]);
-        pal8(hi ? c.b[3] : c.b[1], w.pal, e[2], e[3]);
+        pal8<FMT == kFmtPalRun>(hi ? c.b[2] : c.b[0], w.pal, e[0], e[1]);
+        pal8<FMT == kFmtPalRun>(hi ? c.b[3] : c.b[1], w.pal, e[2], e[3]);
       } else {
-        pal8((el & 8) ? c.b[1] : c.b[0], w.pal, e[0], e[1]);
+        pal8<FMT == kFmtPalRun>((el & 8) ? c.b[1] : c.b[0], w.pal, e[0], e[1]);
       }
 #pragma unroll
       for (int i = 0; i < OW / 4; ++i) e[i] = verb ? c.b[i] : e[i];
@@ -111,7 +113,7 @@ __device__ __forceinline__ void chunk_rebuild(const WeightView& w, const ChunkT<
 
 template <int FMT>
 __device__ __forceinline__ void flags_load(const WeightView& w, uint64_t el, uint32_t& fw, uint32_t& rw) {
-  if constexpr (FMT == kFmtPal) {
+  if constexpr (fmt_is_pal(FMT)) {
     fw = w.vflags[flag_index(el)];
     rw = w.vrank[flag_index(el)];
   } else {
@@ -556,16 +558,33 @@ int nk_pipe_u(const WeightView& w, int nb) {
   return 0;
 }
 
-// largest MFMA tile whose grid alone covers the chip; else 128 x 128 with split K
-int default_tile(uint64_t n, int64_t batch) {
-  for (int t = mfma2_tile_count() - 1; t >= 0; --t) {
-    const int bm = t == 0 ? 64 : (t == 1 || t == 2) ? 128 : 256;
-    const int bn = (t == 2 || t == 4) ? 256 : 128;
-    if (bm > 2 * batch && t > 0) continue;   // no tile much taller than the batch
-    const uint64_t blocks = (n + bn - 1) / bn * (uint64_t)((batch + bm - 1) / bm);
-    if (blocks >= 256) return t;
+// MFMA tile by a small cost model: block waves over the CUs times the work
+// of one block, at each tile's relative per-block throughput (measured on
+// the 70B MLP shapes at batch 1024), plus the split-K partial sums written
+// and read back.  Tiles more than twice as tall as the batch are skipped.
+int default_tile(const WeightView& w, int64_t batch) {
+  static const double kTileEff[] = {0.55, 0.70, 0.80, 0.85, 1.0};
+  const double cu_rate = 4.6e12;   // flop/s of one CU at the best tile's throughput
+  const double hbm = 5e12;         // bytes/s for the partial sums
+  const int cus = device_cus();
+  int best = 0;
+  double best_t = 0;
+  for (int t = 0; t < mfma2_tile_count(); ++t) {
+    int bm, bn;
+    mfma2_tile_dims(t, &bm, &bn);
+    if (bm > 2 * batch && t > 0) continue;
+    const int slices = mfma2_slices(w, batch, t, 0);
+    const double tiles = (double)((w.n + bn - 1) / bn) * (double)((batch + bm - 1) / bm);
+    const double waves = std::ceil(tiles * slices / cus);
+    const double kper = std::ceil((double)w.k / slices);
+    double est = waves * 2.0 * bm * bn * kper / (kTileEff[t < 5 ? t : 4] * cu_rate);
+    if (slices > 1) est += (2.0 * slices + 1.0) * (double)batch * (double)w.n * 4.0 / hbm;
+    if (t == 0 || est < best_t) {
+      best = t;
+      best_t = est;
+    }
   }
-  return batch <= 64 ? 0 : 1;
+  return best;
 }
 
 // K slices of the KN GEMV: about two 8-wave blocks per CU over the grid,
@@ -596,7 +615,7 @@ int gemm_variant_count() { return 1 + mfma2_tile_count(); }
 
 static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg) {
   if (cfg && cfg->variant > 0 && cfg->variant <= gemm_variant_count()) return cfg->variant;
-  return batch <= kGemvMaxBatch ? 1 : 2 + default_tile(w.n, batch);
+  return batch <= kGemvMaxBatch ? 1 : 2 + default_tile(w, batch);
 }
 
 // Workspace floats for partial sums of the kernel this call resolves to (the
@@ -653,9 +672,10 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
         const int u = nk_pipe_u(w, nb);
         if (u > 0) {
           GemvNkFn f = w.fmt == kFmtBf16 ? gemv_nk_pipe_fn<kFmtBf16>(nb, u)
-                       : w.fmt == kFmtExp ? gemv_nk_pipe_fn<kFmtExp>(nb, u) : gemv_nk_pipe_fn<kFmtPal>(nb, u);
+                       : w.fmt == kFmtExp ? gemv_nk_pipe_fn<kFmtExp>(nb, u)
+                       : w.fmt == kFmtPal ? gemv_nk_pipe_fn<kFmtPal>(nb, u) : gemv_nk_pipe_fn<kFmtPalRun>(nb, u);
           const size_t lds = (size_t)nb * w.k * 2;
-          static bool lds_set[3][4][3] = {};
+          static bool lds_set[4][4][3] = {};
           const int fi = w.fmt, ni = nb <= 1 ? 0 : nb <= 2 ? 1 : nb <= 4 ? 2 : 3, ui = u == 4 ? 2 : u == 2 ? 1 : 0;
           if (!lds_set[fi][ni][ui]) {
             hipError_t e = hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -669,7 +689,8 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
           hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(1024), lds, s, w, xb, nb, yb, ldy, col0);
         } else {
           GemvNkFn f = w.fmt == kFmtBf16 ? gemv_nk_any_fn<kFmtBf16>(nb)
-                       : w.fmt == kFmtExp ? gemv_nk_any_fn<kFmtExp>(nb) : gemv_nk_any_fn<kFmtPal>(nb);
+                       : w.fmt == kFmtExp ? gemv_nk_any_fn<kFmtExp>(nb)
+                       : w.fmt == kFmtPal ? gemv_nk_any_fn<kFmtPal>(nb) : gemv_nk_any_fn<kFmtPalRun>(nb);
           uint64_t blocks = (w.n + 3) / 4;
           if (blocks > 8192) blocks = 8192;
           hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(256), 0, s, w, xb, nb, yb, ldy, col0);
@@ -681,7 +702,8 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
         const uint32_t pps = (uint32_t)((pairs + (uint64_t)slices - 1) / (uint64_t)slices);
         const unsigned gy = (unsigned)((pairs + pps - 1) / pps);
         GemvKnFn f = w.fmt == kFmtBf16 ? gemv_kn_fn<kFmtBf16>(nb)
-                     : w.fmt == kFmtExp ? gemv_kn_fn<kFmtExp>(nb) : gemv_kn_fn<kFmtPal>(nb);
+                     : w.fmt == kFmtExp ? gemv_kn_fn<kFmtExp>(nb)
+                     : w.fmt == kFmtPal ? gemv_kn_fn<kFmtPal>(nb) : gemv_kn_fn<kFmtPalRun>(nb);
         const uint64_t bw = 64u * (uint64_t)kn_ow(nb);
         hipLaunchKernelGGL(f, dim3((unsigned)((w.n + bw - 1) / bw), gy), dim3(512), 0, s, w, xb, nb, partial, pps);
         hipError_t e = hipGetLastError();

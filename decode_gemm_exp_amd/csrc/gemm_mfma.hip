@@ -80,7 +80,7 @@ __device__ __forceinline__ void rebuild_raw(const WeightView& w, const Raw& r, b
   } else if constexpr (FMT == kFmtExp) {
     rebuild16(r.a, r.b, o);
   } else {
-    uint4 e = pal16(hi ? r.b.z : r.b.x, hi ? r.b.w : r.b.y, w.pal);
+    uint4 e = pal16<FMT == kFmtPalRun>(hi ? r.b.z : r.b.x, hi ? r.b.w : r.b.y, w.pal);
     if (verbatim) e = r.b;
     rebuild16(r.a, e, o);
   }
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
       const uint64_t el = chunk_el(i, k0, v);
       load_raw<FMT>(w, el, v, fw_a[i], rk_a[i], wr[i]);
       wval[i] = v;
-      wverb[i] = FMT == kFmtPal && v && group_verbatim(fw_a[i], el >> 6);
+      wverb[i] = fmt_is_pal(FMT) && v && group_verbatim(fw_a[i], el >> 6);
       whi[i] = (el & 16) != 0;
     }
   };
@@ -280,15 +280,15 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
   // prologue: step 0 in LDS buffer 0, step 1 in registers, flags of step 2 loaded
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    if constexpr (FMT == kFmtPal) load_flags(kb, p);
+    if constexpr (fmt_is_pal(FMT)) load_flags(kb, p);
     load_step(kb, p);
   }
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    if constexpr (FMT == kFmtPal) load_flags(kb + kBK, p);
+    if constexpr (fmt_is_pal(FMT)) load_flags(kb + kBK, p);
     store_step(xs0, ws0, p);
     load_step(kb + kBK, p);
-    if constexpr (FMT == kFmtPal) load_flags(kb + 2 * kBK, p);
+    if constexpr (fmt_is_pal(FMT)) load_flags(kb + 2 * kBK, p);
   }
 
   // step s: MFMAs from buffer s & 1 while step s+1 is rebuilt into the other
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
     auto rest = [&](int p) __attribute__((always_inline)) {
       store_step(xs_n, ws_n, p);
       load_step(k2, p);
-      if constexpr (FMT == kFmtPal) load_flags(k3, p);
+      if constexpr (fmt_is_pal(FMT)) load_flags(k3, p);
       __builtin_amdgcn_sched_barrier(0);
     };
     read_frags(xs_c, ws_c, 0, fa0, fb0);
@@ -373,6 +373,10 @@ struct Tile2 {
 };
 static const Tile2 kTiles2[] = {{64, 128}, {128, 128}, {128, 256}, {256, 128}, {256, 256}};
 int mfma2_tile_count() { return (int)(sizeof(kTiles2) / sizeof(kTiles2[0])); }
+void mfma2_tile_dims(int tile, int* bm, int* bn) {
+  *bm = kTiles2[tile].bm;
+  *bn = kTiles2[tile].bn;
+}
 
 // K slices so that the grid covers the chip at least once (capped; each slice >= 8 steps)
 int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint) {
@@ -402,9 +406,11 @@ hipError_t launch_mfma2(const WeightView& w, const uint16_t* x, int64_t batch, f
     return hipErrorInvalidValue;
   Mfma2Fn f;
   if (w.layout == 0) {
-    f = w.fmt == kFmtBf16 ? pick<0, kFmtBf16>(tile) : w.fmt == kFmtExp ? pick<0, kFmtExp>(tile) : pick<0, kFmtPal>(tile);
+    f = w.fmt == kFmtBf16 ? pick<0, kFmtBf16>(tile) : w.fmt == kFmtExp ? pick<0, kFmtExp>(tile)
+        : w.fmt == kFmtPal ? pick<0, kFmtPal>(tile) : pick<0, kFmtPalRun>(tile);
   } else {
-    f = w.fmt == kFmtBf16 ? pick<1, kFmtBf16>(tile) : w.fmt == kFmtExp ? pick<1, kFmtExp>(tile) : pick<1, kFmtPal>(tile);
+    f = w.fmt == kFmtBf16 ? pick<1, kFmtBf16>(tile) : w.fmt == kFmtExp ? pick<1, kFmtExp>(tile)
+        : w.fmt == kFmtPal ? pick<1, kFmtPal>(tile) : pick<1, kFmtPalRun>(tile);
   }
   const size_t wtile = w.layout == 0 ? (size_t)t.bn * kLDK : (size_t)kBK * (size_t)(t.bn + 16);
   const size_t lds = 2 * ((size_t)t.bm * kLDK + wtile) * sizeof(uint16_t);

@@ -53,11 +53,13 @@ __device__ __forceinline__ uint32_t pal_lookup4(uint32_t n, const PalView& p) {
 }
 
 // 8 slots as nibbles (element i in bits 4i..4i+3) -> exponent bytes of
-// elements 0..3 (e03) and 4..7 (e47)
+// elements 0..3 (e03) and 4..7 (e47); RUN: the palette is p.base4's entry
+// onwards in steps of one
+template <bool RUN>
 __device__ __forceinline__ void pal8(uint32_t v, const PalView& p, uint32_t& e03, uint32_t& e47) {
   uint32_t ev = v & 0x0F0F0F0Fu;           // elements 0 2 4 6
   uint32_t od = (v >> 4) & 0x0F0F0F0Fu;    // elements 1 3 5 7
-  if (p.run) {
+  if constexpr (RUN) {
     ev += p.base4;
     od += p.base4;
   } else {
@@ -69,11 +71,17 @@ __device__ __forceinline__ void pal8(uint32_t v, const PalView& p, uint32_t& e03
 }
 
 // 16 slots (two dwords of nibbles) -> 16 exponent bytes
+template <bool RUN>
 __device__ __forceinline__ uint4 pal16(uint32_t v0, uint32_t v1, const PalView& p) {
   uint4 e;
-  pal8(v0, p, e.x, e.y);
-  pal8(v1, p, e.z, e.w);
+  pal8<RUN>(v0, p, e.x, e.y);
+  pal8<RUN>(v1, p, e.z, e.w);
   return e;
+}
+
+// the same with the palette kind decided at run time (one uniform branch)
+__device__ __forceinline__ uint4 pal16_any(uint32_t v0, uint32_t v1, const PalView& p) {
+  return p.run ? pal16<true>(v0, v1, p) : pal16<false>(v0, v1, p);
 }
 
 // verbatim flag and rank of group g from its flag and rank words
@@ -105,7 +113,7 @@ __device__ __forceinline__ void load16(const WeightView& w, uint64_t el, uint32_
       const uint32_t r = group_rank(fw, w.vrank[g >> 5], g);
       e = *reinterpret_cast<const uint4*>(w.vexp + (uint64_t)r * 64 + (el & 63));
     } else {
-      e = pal16(nib.x, nib.y, w.pal);
+      e = pal16<FMT == kFmtPalRun>(nib.x, nib.y, w.pal);
     }
     rebuild16(s, e, o);
   }

@@ -98,7 +98,10 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs& a, int mode, hipStream_t s);
 
 // weight formats seen by the GEMM kernels
-enum WFmt { kFmtBf16 = 0, kFmtExp = 1, kFmtPal = 2 };
+// kFmtPalRun: palette formats whose entries are consecutive exponents (the
+// lookup is a bytewise add); a separate format keeps kernels branch-free
+enum WFmt { kFmtBf16 = 0, kFmtExp = 1, kFmtPal = 2, kFmtPalRun = 3 };
+constexpr bool fmt_is_pal(int f) { return f == kFmtPal || f == kFmtPalRun; }
 struct WeightView {
   int fmt;
   int layout;                       // 0 = stored [N][K], 1 = stored [K][N]
@@ -122,6 +125,7 @@ hipError_t launch_sum_slices(const float* part, int slices, uint64_t n, int64_t 
                              int64_t col0, hipStream_t s);
 // gemm_mfma.hip
 int mfma2_tile_count();
+void mfma2_tile_dims(int tile, int* bm, int* bn);
 int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint);
 size_t mfma2_partial_elems(const WeightView& w, int64_t batch, int tile, int split_hint);
 hipError_t launch_mfma2(const WeightView& w, const uint16_t* x, int64_t batch, float* y, int64_t ldy, int64_t col0,
