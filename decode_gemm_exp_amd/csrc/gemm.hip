@@ -40,89 +40,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// ---- chunk access shared by the pipelined GEMVs ------------------------------
-// One chunk of OW (16 or 8) consecutive stored weights as loaded from HBM.
-// Every load's address is known without waiting for another load: the
-// palette format takes the chunk's verbatim flag word and rank word from an
-// earlier pipeline step and then loads either the chunk's verbatim exponent
-// bytes or the aligned index bytes that hold its OW nibbles.
-template <int OW>
-struct ChunkT {
-  uint32_t a[OW / 2];   // bf16: the OW weights | exp, pal: OW sign+mantissa bytes in a[0 .. OW/4)
-  uint32_t b[OW / 4];   // exp: OW exponent bytes | pal: 2*OW index nibbles or OW verbatim exponent bytes
-};
-
-template <int OW>
-__device__ __forceinline__ void load_words(const void* p, uint32_t* d) {   // OW / 4 dwords
-  if constexpr (OW == 16) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-  } else {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    d[0] = v.x; d[1] = v.y;
-  }
-}
-
-__device__ __forceinline__ uint32_t flag_index(uint64_t el) { return (uint32_t)(el >> 11); }
-
-template <int FMT, int OW>
-__device__ __forceinline__ void chunk_load(const WeightView& w, uint64_t el, uint32_t fw, uint32_t rw, ChunkT<OW>& c) {
-  if constexpr (FMT == kFmtBf16) {
-    load_words<OW>(w.bf16 + el, c.a);
-    load_words<OW>(w.bf16 + el + OW / 2, c.a + OW / 4);
-  } else if constexpr (FMT == kFmtExp) {
-    load_words<OW>(w.sm + el, c.a);
-    load_words<OW>(w.ex + el, c.b);
-  } else {
-    load_words<OW>(w.sm + el, c.a);
-    const uint64_t g = el >> 6;
-    const uint8_t* p = group_verbatim(fw, g) ? w.vexp + (uint64_t)group_rank(fw, rw, g) * 64 + (el & 63)
-                                             : w.pidx + ((el >> 1) & ~(uint64_t)(OW - 1));
-    load_words<OW>(p, c.b);
-  }
-}
-
-// OW / 2 dwords of packed bf16
-template <int FMT, int OW>
-__device__ __forceinline__ void chunk_rebuild(const WeightView& w, const ChunkT<OW>& c, uint64_t el, uint32_t fw,
-                                              uint32_t* o) {
-  if constexpr (FMT == kFmtBf16) {
-#pragma unroll
-    for (int i = 0; i < OW / 2; ++i) o[i] = c.a[i];
-  } else {
-    uint32_t e[OW / 4];
-    if constexpr (FMT == kFmtExp) {
-#pragma unroll
-      for (int i = 0; i < OW / 4; ++i) e[i] = c.b[i];
-    } else {
-      const bool verb = group_verbatim(fw, el >> 6);
-      if constexpr (OW == 16) {
-        const bool hi = (el & 16) != 0;
-        pal8<FMT == kFmtPalRun>(hi ? c.b[2] : c.b[0], w.pal, e[0], e[1]);
-        pal8<FMT == kFmtPalRun>(hi ? c.b[3] : c.b[1], w.pal, e[2], e[3]);
-      } else {
-        pal8<FMT == kFmtPalRun>((el & 8) ? c.b[1] : c.b[0], w.pal, e[0], e[1]);
-      }
-#pragma unroll
-      for (int i = 0; i < OW / 4; ++i) e[i] = verb ? c.b[i] : e[i];
-    }
-#pragma unroll
-    for (int i = 0; i < OW / 4; ++i) rebuild4(c.a[i], e[i], o[2 * i], o[2 * i + 1]);
-  }
-}
-
-template <int FMT>
-__device__ __forceinline__ void flags_load(const WeightView& w, uint64_t el, uint32_t& fw, uint32_t& rw) {
-  if constexpr (fmt_is_pal(FMT)) {
-    fw = w.vflags[flag_index(el)];
-    rw = w.vrank[flag_index(el)];
-  } else {
-    fw = rw = 0;
-  }
-}
-
-__device__ __forceinline__ uint32_t wave_uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
-
 // ---- GEMV, stored [N][K], K a multiple of 1024 U --------------------------------
 // Blocks of 16 waves, one block per CU, x rows staged once per block in LDS.
 // A wave owns rows n = wave, wave + nwaves, ... and walks each in steps of
@@ -563,7 +480,7 @@ int nk_pipe_u(const WeightView& w, int nb) {
 // the 70B MLP shapes at batch 1024), plus the split-K partial sums written
 // and read back.  Tiles more than twice as tall as the batch are skipped.
 int default_tile(const WeightView& w, int64_t batch) {
-  static const double kTileEff[] = {0.55, 0.70, 0.80, 0.85, 1.0};
+  static const double kTileEff[] = {0.55, 0.70, 0.80, 0.85, 1.0, 0.35, 0.45};
   const double cu_rate = 4.6e12;   // flop/s of one CU at the best tile's throughput
   const double hbm = 5e12;         // bytes/s for the partial sums
   const int cus = device_cus();
@@ -577,7 +494,7 @@ int default_tile(const WeightView& w, int64_t batch) {
     const double tiles = (double)((w.n + bn - 1) / bn) * (double)((batch + bm - 1) / bm);
     const double waves = std::ceil(tiles * slices / cus);
     const double kper = std::ceil((double)w.k / slices);
-    double est = waves * 2.0 * bm * bn * kper / (kTileEff[t < 5 ? t : 4] * cu_rate);
+    double est = waves * 2.0 * bm * bn * kper / (kTileEff[t < 7 ? t : 6] * cu_rate);
     if (slices > 1) est += (2.0 * slices + 1.0) * (double)batch * (double)w.n * 4.0 / hbm;
     if (t == 0 || est < best_t) {
       best = t;

@@ -361,7 +361,9 @@ Mfma2Fn pick(int tile) {
     case 1: return prepared<L, F, 128, 128, 2>();
     case 2: return prepared<L, F, 128, 256, 2>();
     case 3: return prepared<L, F, 256, 128, 2>();
-    default: return prepared<L, F, 256, 256, 2>();
+    case 4: return prepared<L, F, 256, 256, 2>();
+    case 5: return prepared<L, F, 32, 128, 1>();
+    default: return prepared<L, F, 32, 256, 1>();
   }
 }
 
@@ -371,8 +373,10 @@ Mfma2Fn pick(int tile) {
 struct Tile2 {
   int bm, bn;
 };
-static const Tile2 kTiles2[] = {{64, 128}, {128, 128}, {128, 256}, {256, 128}, {256, 256}};
+// the last two (one 32-row MFMA tile, four waves side by side) are for small batches
+static const Tile2 kTiles2[] = {{64, 128}, {128, 128}, {128, 256}, {256, 128}, {256, 256}, {32, 128}, {32, 256}};
 int mfma2_tile_count() { return (int)(sizeof(kTiles2) / sizeof(kTiles2[0])); }
+int mfma2_small_tile_first() { return 5; }
 void mfma2_tile_dims(int tile, int* bm, int* bn) {
   *bm = kTiles2[tile].bm;
   *bn = kTiles2[tile].bn;

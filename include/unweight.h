@@ -92,8 +92,8 @@ typedef struct {
 
 /* Kernel choice for one GEMM call.  Any field <= 0 means "library default". */
 typedef struct {
-  int32_t variant;      /* GEMM tile variant (see uw_variant_count)           */
-  int32_t split_k;      /* K slices for the small-batch kernels               */
+  int32_t variant;      /* GEMM variant (see uw_variant_count)                */
+  int32_t split_k;      /* K slices of the split-K kernels                    */
   int32_t decode_cus;   /* CUs given to the preprocessing kernel when it runs
                            beside GEMMs (uw_run_sequence); 0 = no split      */
   int32_t reserved;
@@ -206,7 +206,10 @@ uw_status uw_gemm_bf16(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout la
                        const uint16_t* x_dev, int64_t batch, float* y_dev,
                        const uw_kernel_cfg* cfg, void* stream);
 
-/* Number of GEMM tile variants selectable through uw_kernel_cfg.variant. */
+/* Number of GEMM variants selectable through uw_kernel_cfg.variant, numbered
+ * 1..count: 1 = VALU GEMV (v_dot2; any batch, eight rows per launch);
+ * 2..count = MFMA tiles 64x128, 128x128, 128x256, 256x128, 256x256, 32x128,
+ * 32x256 (batch rows x columns; weights rebuilt into LDS). */
 int32_t uw_variant_count(void);
 
 /* One entry of a sequence of projections run back to back. */
