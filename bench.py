@@ -149,6 +149,18 @@ def extras(uw, synth, torch, dev, iters: int = 10):
     wl = synth.WORKLOADS["down8b"]
     _, n, k, layout = wl.mats[0]
     w = synth.workload_weights(wl, 0, device=dev)
+    # compression (a1..a5) of the 58.7 M-weight down matrix: wall time of the
+    # whole call, including its three small host round trips
+    times = []
+    for r in range(3):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        mc = uw.uw_compress(w, n, k, layout)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+        del mc
+    tc = sorted(times)[1]
+    out["compress_down8b"] = {"ms": round(tc * 1e3, 3), "bf16_input_gbs": round(2 * n * k / tc / 1e9, 1)}
     m = uw.uw_compress(w, n, k, layout)
     uw.uw_transcode_palette(m, None)
     del w
@@ -170,6 +182,37 @@ def extras(uw, synth, torch, dev, iters: int = 10):
             out[f"down8b_b{b}_{PIPE_NAMES[p]}"] = {"us": round(t * 1e6, 2), "tflops": round(flops / t / 1e12, 2),
                                                  "mfma_frac": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
     return out
+
+
+def measured_peaks(torch, dev):
+    """Yardsticks measured on this machine (context for the spec peaks): a 1 GiB
+    device copy and a dense 8192^3 bf16 matmul in torch."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    s, e = ev(), ev()
+    s.record()
+    for _ in range(5):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) / (s.elapsed_time(e) / 5 / 1e3) / 1e9
+    del a, b
+    x = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    y = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    for _ in range(2):
+        torch.matmul(x, y)
+    s, e = ev(), ev()
+    s.record()
+    for _ in range(5):
+        torch.matmul(x, y)
+    e.record()
+    torch.cuda.synchronize()
+    tflops = 2 * 8192 ** 3 / (s.elapsed_time(e) / 5 / 1e3) / 1e12
+    return {"copy_gbs": round(copy_gbs, 1), "copy_frac_of_spec": round(copy_gbs / HBM_PEAK_GBS, 4),
+            "dense_bf16_tflops": round(tflops, 1), "dense_frac_of_spec": round(tflops / BF16_PEAK_TFLOPS, 4)}
 
 
 def job_bytes(info, pipeline: int, batch: int) -> float:
@@ -432,6 +475,7 @@ def main() -> int:
         del mats
         torch.cuda.empty_cache()
         res["extras"] = extras(uw, synth, torch, dev)
+        res["measured_peaks"] = measured_peaks(torch, dev)
     if not args.no_cpu:
         print("bench: oracle cpu baseline", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w_np, x_np)

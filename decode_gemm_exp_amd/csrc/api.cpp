@@ -332,11 +332,14 @@ uw_status uw_compress(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout lay
   UW_CHECK(dev_alloc(&m->corrupt, sizeof(int)));
   UW_HIP(hipMemsetAsync(m->corrupt, 0, sizeof(int), s));
 
-  // scratch: hist u32[256] | coded u32[16] | total u64 | slot/len tables | codebook u32[256] | seg words
+  // scratch: hist u32[256] | coded u32[16] | total u64 | slot/len tables | codebook u32[256] | seg words |
+  // scan tile sums u64
   const uint64_t off_coded = 1024, off_total = 1088, off_slot = 1152, off_len = 1408, off_book = 1664,
                  off_seg = 2688;
+  const uint64_t off_tiles = pad256(off_seg + 4 * m->segments);
+  const uint64_t ntiles = scan_tiles(m->segments > m->flag_words ? m->segments : m->flag_words);
   void* scratch = nullptr;
-  UW_CHECK(dev_alloc(&scratch, off_seg + 4 * m->segments + 256));
+  UW_CHECK(dev_alloc(&scratch, off_tiles + 8 * ntiles + 256));
   guard.scratch = scratch;
   uint8_t* sc = static_cast<uint8_t*>(scratch);
   uint32_t* d_hist = reinterpret_cast<uint32_t*>(sc);
@@ -346,6 +349,7 @@ uw_status uw_compress(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout lay
   uint8_t* d_len = sc + off_len;
   uint32_t* d_book = reinterpret_cast<uint32_t*>(sc + off_book);
   uint32_t* d_seg = reinterpret_cast<uint32_t*>(sc + off_seg);
+  uint64_t* d_tiles = reinterpret_cast<uint64_t*>(sc + off_tiles);
 
   // 1. exponent histogram
   UW_HIP(hipMemsetAsync(sc, 0, off_slot, s));
@@ -361,7 +365,7 @@ uw_status uw_compress(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout lay
   for (int v = 0; v < 256; ++v) slot_tab[v] = m->t.slot_of[v] < 0 ? 0xFFu : (uint8_t)m->t.slot_of[v];
   UW_HIP(hipMemcpyAsync(d_slot, slot_tab, 256, hipMemcpyHostToDevice, s));
   UW_HIP(launch_flags(w_dev, m->numel, m->groups, d_slot, m->sm, m->vflags, d_coded, s));
-  UW_HIP(launch_rank_scan(m->vflags, m->flag_words, m->vrank, d_total, s));
+  UW_HIP(launch_rank_scan(m->vflags, m->flag_words, m->vrank, d_total, d_tiles, s));
   uint32_t coded32[16];
   uint64_t vtotal = 0;
   UW_HIP(hipMemcpyAsync(coded32, d_coded, sizeof(coded32), hipMemcpyDeviceToHost, s));
@@ -384,7 +388,7 @@ uw_status uw_compress(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout lay
   UW_HIP(hipMemcpyAsync(d_book, book, sizeof(book), hipMemcpyHostToDevice, s));
   UW_HIP(hipMemsetAsync(d_seg, 0, 4 * m->segments, s));
   UW_HIP(launch_segment_bits(w_dev, m->groups, sg, m->segments, d_len, m->vflags, d_seg, s));
-  UW_HIP(launch_offsets_scan(d_seg, m->segments, m->seg_off, s));
+  UW_HIP(launch_offsets_scan(d_seg, m->segments, m->seg_off, d_tiles, s));
   UW_HIP(hipMemsetAsync(d_coded, 0, 4, s));
   UW_HIP(launch_wave_span(m->seg_off, m->segments, d_coded, s));
   uint32_t W32 = 0, span32 = 0;

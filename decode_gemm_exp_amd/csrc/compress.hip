@@ -10,7 +10,7 @@
 //   histogram     256-bin exponent counts, privatised per wave in LDS
 //   flags         per 64-weight group: any exponent outside the palette
 //                 (wave ballot), sign+mantissa bytes, coded-slot histogram
-//   rank scan     exclusive prefix of popcount(vflags) (single workgroup)
+//   rank scan     exclusive prefix of popcount(vflags) (multi-block scan)
 //   segment bits  code bits per segment -> words per segment
 //   offsets scan  exclusive prefix of words -> seg_off
 //   encode        one wave per segment: per-lane codeword, wave prefix sum of
@@ -27,22 +27,26 @@ __device__ __forceinline__ uint32_t sm_of(uint32_t b) { return ((b >> 8) & 0x80u
 // ---- histogram ----------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_histogram(const uint4* __restrict__ w, uint64_t n8,
                                                    uint32_t* __restrict__ hist) {
-  __shared__ uint32_t h[4][256];
-  const int wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < 4 * 256; i += 256) (&h[0][0])[i] = 0;
+  // 16 copies indexed by lane % 16: the few hot exponents of a weight matrix
+  // would otherwise serialise 64 lanes on one LDS word
+  __shared__ uint32_t h[16][256];
+  const int copy = threadIdx.x & 15;
+  for (int i = threadIdx.x; i < 16 * 256; i += 256) (&h[0][0])[i] = 0;
   __syncthreads();
   for (uint64_t i = blockIdx.x * 256ull + threadIdx.x; i < n8; i += (uint64_t)gridDim.x * 256ull) {
     uint4 v = w[i];
     uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      atomicAdd(&h[wave][exp_of(d[j] & 0xFFFFu)], 1u);
-      atomicAdd(&h[wave][exp_of(d[j] >> 16)], 1u);
+      atomicAdd(&h[copy][exp_of(d[j] & 0xFFFFu)], 1u);
+      atomicAdd(&h[copy][exp_of(d[j] >> 16)], 1u);
     }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < 256; i += 256) {
-    uint32_t s = h[0][i] + h[1][i] + h[2][i] + h[3][i];
+    uint32_t s = 0;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) s += h[c][i];
     if (s) atomicAdd(&hist[i], s);
   }
 }
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(256) void k_flags(const uint4* __restrict__ w, uint
   }
 }
 
-// ---- single-workgroup exclusive scans ----------------------------------------------
+// ---- exclusive scans --------------------------------------------------------------
 // Block-wide exclusive scan of one value per thread (1024 threads).
 __device__ uint64_t block_exclusive_scan(uint64_t v, uint64_t* total) {
   __shared__ uint64_t wsum[16];
@@ -131,36 +135,79 @@ __device__ uint64_t block_exclusive_scan(uint64_t v, uint64_t* total) {
   return r;
 }
 
-__global__ __launch_bounds__(1024) void k_rank_scan(const uint32_t* __restrict__ vflags, uint64_t words,
-                                                    uint32_t* __restrict__ vrank, uint64_t* __restrict__ total) {
-  __shared__ uint64_t chunk_total;
-  uint64_t carry = 0;
-  for (uint64_t base = 0; base < words; base += 1024) {
-    const uint64_t i = base + threadIdx.x;
-    const uint64_t v = i < words ? (uint64_t)__popc(vflags[i]) : 0;
-    const uint64_t ex = block_exclusive_scan(v, &chunk_total);
-    if (i < words) vrank[i] = (uint32_t)(carry + ex);
-    __syncthreads();
-    carry += chunk_total;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) *total = carry;
+// Multi-block exclusive scan of n u32 values (or their popcounts), 64-bit
+// running sums: tile sums, a one-block scan of the tile sums, then each tile
+// scans itself from its offset.  A tile is 1024 threads x 8 values.
+constexpr int kScanPer = 8;
+constexpr uint64_t kScanTile = 1024ull * kScanPer;
+
+template <bool POPC>
+__device__ __forceinline__ uint64_t scan_in(const uint32_t* in, uint64_t i, uint64_t n) {
+  if (i >= n) return 0;
+  const uint32_t v = in[i];
+  return POPC ? (uint64_t)__popc(v) : (uint64_t)v;
 }
 
-__global__ __launch_bounds__(1024) void k_offsets_scan(const uint32_t* __restrict__ seg_words, uint64_t segments,
-                                                       uint32_t* __restrict__ seg_off) {
+template <bool POPC>
+__global__ __launch_bounds__(1024) void k_scan_tiles(const uint32_t* __restrict__ in, uint64_t n,
+                                                     uint64_t* __restrict__ sums) {
+  __shared__ uint64_t tot;
+  const uint64_t base = (uint64_t)blockIdx.x * kScanTile;
+  uint64_t s = 0;
+#pragma unroll
+  for (int j = 0; j < kScanPer; ++j) s += scan_in<POPC>(in, base + (uint64_t)j * 1024 + threadIdx.x, n);
+  (void)block_exclusive_scan(s, &tot);
+  if (threadIdx.x == 0) sums[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(1024) void k_scan_sums(uint64_t* __restrict__ sums, uint64_t tiles,
+                                                    uint64_t* __restrict__ total, uint32_t* __restrict__ total32) {
   __shared__ uint64_t chunk_total;
   uint64_t carry = 0;
-  for (uint64_t base = 0; base < segments; base += 1024) {
+  for (uint64_t base = 0; base < tiles; base += 1024) {
     const uint64_t i = base + threadIdx.x;
-    const uint64_t v = i < segments ? (uint64_t)seg_words[i] : 0;
+    const uint64_t v = i < tiles ? sums[i] : 0;
     const uint64_t ex = block_exclusive_scan(v, &chunk_total);
-    if (i < segments) seg_off[i] = (uint32_t)(carry + ex);
+    if (i < tiles) sums[i] = carry + ex;
     __syncthreads();
     carry += chunk_total;
     __syncthreads();
   }
-  if (threadIdx.x == 0) seg_off[segments] = (uint32_t)carry;
+  if (threadIdx.x == 0) {
+    if (total) *total = carry;
+    if (total32) *total32 = (uint32_t)carry;
+  }
+}
+
+template <bool POPC>
+__global__ __launch_bounds__(1024) void k_scan_apply(const uint32_t* __restrict__ in, uint64_t n,
+                                                     const uint64_t* __restrict__ offs, uint32_t* __restrict__ out) {
+  __shared__ uint64_t tot;
+  const uint64_t base = (uint64_t)blockIdx.x * kScanTile + (uint64_t)threadIdx.x * kScanPer;
+  uint64_t v[kScanPer];
+  uint64_t s = 0;
+#pragma unroll
+  for (int j = 0; j < kScanPer; ++j) {
+    v[j] = scan_in<POPC>(in, base + j, n);
+    s += v[j];
+  }
+  uint64_t run = offs[blockIdx.x] + block_exclusive_scan(s, &tot);
+#pragma unroll
+  for (int j = 0; j < kScanPer; ++j) {
+    if (base + j < n) out[base + j] = (uint32_t)run;
+    run += v[j];
+  }
+}
+
+template <bool POPC>
+hipError_t scan3(const uint32_t* in, uint64_t n, uint32_t* out, uint64_t* total, uint32_t* total32, uint64_t* tiles_ws,
+                 hipStream_t s) {
+  const uint64_t tiles = (n + kScanTile - 1) / kScanTile;
+  if (tiles == 0 || tiles > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_scan_tiles<POPC>, dim3((unsigned)tiles), dim3(1024), 0, s, in, n, tiles_ws);
+  hipLaunchKernelGGL(k_scan_sums, dim3(1), dim3(1024), 0, s, tiles_ws, tiles, total, total32);
+  hipLaunchKernelGGL(k_scan_apply<POPC>, dim3((unsigned)tiles), dim3(1024), 0, s, in, n, tiles_ws, out);
+  return hipGetLastError();
 }
 
 // ---- per-segment code bits -------------------------------------------------------
@@ -226,9 +273,18 @@ __global__ __launch_bounds__(256) void k_encode(const uint16_t* __restrict__ w, 
     uint32_t bitbase = 0;
     const uint64_t g0 = s * seg_groups;
     const uint64_t g1 = min(g0 + seg_groups, groups);
+    // a segment's groups share one flag word (segments are <= 32 groups or
+    // whole words); weights are loaded four groups ahead of their coding
+    uint32_t bq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bq[q] = g0 + q < g1 ? w[(g0 + q) * 64 + (uint64_t)lane] : 0u;
     for (uint64_t g = g0; g < g1; ++g) {
       const uint32_t fw = vflags[g >> 5];
-      const uint32_t b = w[g * 64 + (uint64_t)lane];
+      const uint32_t b = bq[0];
+      bq[0] = bq[1];
+      bq[1] = bq[2];
+      bq[2] = bq[3];
+      bq[3] = g + 4 < g1 ? w[(g + 4) * 64 + (uint64_t)lane] : 0u;
       const uint32_t e = exp_of(b);
       if ((fw >> (g & 31)) & 1u) {
         const uint32_t rank = vrank[g >> 5] + (uint32_t)__popc(fw & ((1u << (g & 31)) - 1u));
@@ -302,9 +358,8 @@ hipError_t launch_flags(const uint16_t* w, uint64_t numel, uint64_t groups, cons
 }
 
 hipError_t launch_rank_scan(const uint32_t* vflags, uint64_t words, uint32_t* vrank, uint64_t* total,
-                            hipStream_t s) {
-  hipLaunchKernelGGL(k_rank_scan, dim3(1), dim3(1024), 0, s, vflags, words, vrank, total);
-  return hipGetLastError();
+                            uint64_t* tiles_ws, hipStream_t s) {
+  return scan3<true>(vflags, words, vrank, total, nullptr, tiles_ws, s);
 }
 
 hipError_t launch_segment_bits(const uint16_t* w, uint64_t groups, uint32_t seg_groups, uint64_t segments,
@@ -319,10 +374,11 @@ hipError_t launch_segment_bits(const uint16_t* w, uint64_t groups, uint32_t seg_
 }
 
 hipError_t launch_offsets_scan(const uint32_t* seg_words, uint64_t segments, uint32_t* seg_off,
-                               hipStream_t s) {
-  hipLaunchKernelGGL(k_offsets_scan, dim3(1), dim3(1024), 0, s, seg_words, segments, seg_off);
-  return hipGetLastError();
+                               uint64_t* tiles_ws, hipStream_t s) {
+  return scan3<false>(seg_words, segments, seg_off, nullptr, seg_off + segments, tiles_ws, s);
 }
+
+uint64_t scan_tiles(uint64_t n) { return (n + kScanTile - 1) / kScanTile; }
 
 hipError_t launch_wave_span(const uint32_t* seg_off, uint64_t segments, uint32_t* out, hipStream_t s) {
   hipLaunchKernelGGL(k_wave_span, dim3(grid_for((segments + 63) / 64, 256, 1024)), dim3(256), 0, s, seg_off,

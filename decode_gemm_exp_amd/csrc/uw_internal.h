@@ -62,12 +62,13 @@ hipError_t launch_histogram(const uint16_t* w, uint64_t numel, uint32_t* hist, h
 hipError_t launch_flags(const uint16_t* w, uint64_t numel, uint64_t groups, const uint8_t* slot_tab,
                         uint8_t* sm, uint32_t* vflags, uint32_t* coded, hipStream_t s);
 hipError_t launch_rank_scan(const uint32_t* vflags, uint64_t words, uint32_t* vrank,
-                            uint64_t* total, hipStream_t s);
+                            uint64_t* total, uint64_t* tiles_ws, hipStream_t s);
+uint64_t scan_tiles(uint64_t n);   // u64 tile sums a scan of n values needs
 hipError_t launch_segment_bits(const uint16_t* w, uint64_t groups, uint32_t seg_groups,
                                uint64_t segments, const uint8_t* len_tab, const uint32_t* vflags,
                                uint32_t* seg_words, hipStream_t s);
 hipError_t launch_offsets_scan(const uint32_t* seg_words, uint64_t segments, uint32_t* seg_off,
-                               hipStream_t s);
+                               uint64_t* tiles_ws, hipStream_t s);
 hipError_t launch_wave_span(const uint32_t* seg_off, uint64_t segments, uint32_t* out, hipStream_t s);
 hipError_t launch_encode(const uint16_t* w, uint64_t groups, uint32_t seg_groups, uint64_t segments,
                          const uint32_t* codebook, const uint32_t* vflags, const uint32_t* vrank,
