@@ -324,8 +324,28 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
   constexpr uint32_t per_owner = CH * 64u;
   constexpr int STEPS = 4 * CH;   // 64 owners * per_owner weights / 1024 per step
 
+  // Full decode with one-group rounds: an owner's sign+mantissa bytes of
+  // rounds 2i and 2i+1 are the two halves of one 128-byte line, so both are
+  // loaded in round 2i (the second half waits in svn) and each line is read
+  // once instead of twice.
+  // Exponent decode likewise writes an owner's rounds 2i and 2i+1 together:
+  // round 2i's 16-byte pieces wait in exn and are stored beside round 2i+1's,
+  // so every 128-byte line of output is written whole.
+  uint4 svn[STEPS], exn[STEPS];
+  uint32_t deferred = 0;   // bit u: exn[u] holds a piece of the previous round
+#pragma unroll
+  for (int u = 0; u < STEPS; ++u) {
+    svn[u] = make_uint4(0, 0, 0, 0);
+    exn[u] = make_uint4(0, 0, 0, 0);
+  }
+
   for (uint32_t r = 0; r < rounds; ++r) {
     const uint32_t ng = seg_ng > r * CH ? (seg_ng - r * CH < CH ? seg_ng - r * CH : CH) : 0u;
+    const uint32_t ng_next = seg_ng > (r + 1) * CH ? 1u : 0u;   // round r+1 has a group (CH == 1)
+    const bool pair_first = MODE == kDecodeFull && CH == 1 && (r & 1u) == 0;
+    const bool pair_second = MODE == kDecodeFull && CH == 1 && (r & 1u) == 1;
+    const bool defer_first = MODE == kDecodeExponent && CH == 1 && (r & 1u) == 0;
+    uint32_t has_next = 0;   // bit u: this step's owner has a group in round r+1
     const uint32_t vbits = (uint32_t)(segbits >> (r * CH)) & ((1u << CH) - 1u) & ((1u << ng) - 1u);
     const uint32_t rank0 = rank_seg + (uint32_t)__popcll(segbits & ((1ull << (r * CH)) - 1ull));
     const uint32_t ncoded = ng - (uint32_t)__popc(vbits);
@@ -354,7 +374,20 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
       sv[u] = make_uint4(0, 0, 0, 0);
       if (MODE != kDecodeNibble && verb)
         ev[u] = *reinterpret_cast<const uint4*>(vexp + (uint64_t)(rk + (uint32_t)__popc(below)) * 64u + w16);
-      if (MODE == kDecodeFull && ok) sv[u] = *reinterpret_cast<const uint4*>(smp + el[u]);
+      if (pair_second) {
+        sv[u] = svn[u];
+      } else if (MODE == kDecodeFull && ok) {
+        sv[u] = *reinterpret_cast<const uint4*>(smp + el[u]);
+      }
+      if (defer_first) {
+        const uint32_t gnn = (uint32_t)__shfl((int)ng_next, (int)L, 64);
+        has_next |= (sL < a.segments && gnn > 0) ? (1u << u) : 0u;
+      }
+      if (pair_first) {
+        const uint32_t gnn = (uint32_t)__shfl((int)ng_next, (int)L, 64);
+        svn[u] = (sL < a.segments && gnn > 0) ? *reinterpret_cast<const uint4*>(smp + el[u] + 64u)
+                                              : make_uint4(0, 0, 0, 0);
+      }
     }
 
     // ---- decode every coded group of the round (LDS only) ----
@@ -407,7 +440,13 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
       if (MODE == kDecodeNibble) {
         *reinterpret_cast<uint2*>((uint8_t*)a.out + el[u] / 2) = make_uint2(ex.x, ex.y);
       } else if (MODE == kDecodeExponent) {
-        *reinterpret_cast<uint4*>((uint8_t*)a.out + el[u]) = ex;
+        if (CH == 1 && ((deferred >> u) & 1u))   // the other half of this line, from the previous round
+          *reinterpret_cast<uint4*>((uint8_t*)a.out + el[u] - 64u) = exn[u];
+        if (defer_first && ((has_next >> u) & 1u)) {
+          exn[u] = ex;
+        } else {
+          *reinterpret_cast<uint4*>((uint8_t*)a.out + el[u]) = ex;
+        }
       } else {
         uint4 o0, o1;
         rebuild4(sv[u].x, ex.x, o0.x, o0.y);
@@ -419,6 +458,7 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
         dst[1] = o1;
       }
     }
+    deferred = defer_first ? has_next : 0u;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
   }
