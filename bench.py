@@ -111,33 +111,36 @@ def cpu_baseline(w_np, x_np, min_seconds: float = 10.0):
                       f"{dt:.1f} s"}
 
 
-def extras(uw, synth, torch, dev, iters: int = 10):
+def extras(uw, synth, torch, dev, iters: int = 12, copies: int = 4):
     """Short measurements of the larger-batch rows: fused gate+up (2 x
-    14336x4096) and the transposed down projection (stored [14336][4096])."""
+    14336x4096) and the transposed down projection (stored [14336][4096]).
+    Each row cycles through `copies` compressed copies, so the working set is
+    larger than the 256 MB last-level cache."""
     out = {}
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     wl = synth.WORKLOADS["gateup8b"]
-    ms = []
+    sets = [[] for _ in range(copies)]
     for i in range(2):
         _, n, k, layout = wl.mats[i]
         w = synth.workload_weights(wl, i, device=dev)
-        m = uw.uw_compress(w, n, k, layout)
-        uw.uw_transcode_palette(m, None)
-        ms.append(m)
+        for c in range(copies):
+            m = uw.uw_compress(w, n, k, layout)
+            uw.uw_transcode_palette(m, None)
+            sets[c].append(m)
         del w
-    N = sum(m.info().n for m in ms)
+    N = sum(m.info().n for m in sets[0])
     for b in wl.batches:
         x = synth.activations(b, 4096, seed=wl.seed, device=dev)
         y = torch.empty((b, N), dtype=torch.float32, device=dev)
         for p in (2, 3):
-            ws = torch.empty(max(16, sum(uw.uw_workspace_size(m, p, b) for m in ms)), dtype=torch.uint8,
+            ws = torch.empty(max(16, sum(uw.uw_workspace_size(m, p, b) for m in sets[0])), dtype=torch.uint8,
                              device=dev)
-            for _ in range(3):
-                uw.uw_matmul_reconstruct_grouped(ms, p, x, y, ws)
+            for c in range(copies):
+                uw.uw_matmul_reconstruct_grouped(sets[c], p, x, y, ws)
             s, e = ev(), ev()
             s.record()
-            for _ in range(iters):
-                uw.uw_matmul_reconstruct_grouped(ms, p, x, y, ws)
+            for it in range(iters):
+                uw.uw_matmul_reconstruct_grouped(sets[it % copies], p, x, y, ws)
             e.record()
             torch.cuda.synchronize()
             t = s.elapsed_time(e) / iters / 1e3
@@ -145,7 +148,7 @@ def extras(uw, synth, torch, dev, iters: int = 10):
             out[f"gateup8b_b{b}_{PIPE_NAMES[p]}"] = {"us": round(t * 1e6, 2),
                                                    "tflops": round(flops / t / 1e12, 3),
                                                    "decoded_gbs": round(2 * 2 * 14336 * 4096 / t / 1e9, 1)}
-    del ms
+    del sets
     wl = synth.WORKLOADS["down8b"]
     _, n, k, layout = wl.mats[0]
     w = synth.workload_weights(wl, 0, device=dev)
@@ -161,20 +164,23 @@ def extras(uw, synth, torch, dev, iters: int = 10):
         del mc
     tc = sorted(times)[1]
     out["compress_down8b"] = {"ms": round(tc * 1e3, 3), "bf16_input_gbs": round(2 * n * k / tc / 1e9, 1)}
-    m = uw.uw_compress(w, n, k, layout)
-    uw.uw_transcode_palette(m, None)
+    ms = []
+    for c in range(copies):
+        m = uw.uw_compress(w, n, k, layout)
+        uw.uw_transcode_palette(m, None)
+        ms.append(m)
     del w
     for b in wl.batches:
         x = synth.activations(b, k, seed=wl.seed, device=dev)
         y = torch.empty((b, n), dtype=torch.float32, device=dev)
         for p in (1, 2, 3):
-            ws = torch.empty(max(16, uw.uw_workspace_size(m, p, b)), dtype=torch.uint8, device=dev)
-            for _ in range(2):
-                uw.uw_matmul_reconstruct(m, p, x, y, ws)
+            ws = torch.empty(max(16, uw.uw_workspace_size(ms[0], p, b)), dtype=torch.uint8, device=dev)
+            for c in range(copies):
+                uw.uw_matmul_reconstruct(ms[c], p, x, y, ws)
             s, e = ev(), ev()
             s.record()
-            for _ in range(iters):
-                uw.uw_matmul_reconstruct(m, p, x, y, ws)
+            for it in range(iters):
+                uw.uw_matmul_reconstruct(ms[it % copies], p, x, y, ws)
             e.record()
             torch.cuda.synchronize()
             t = s.elapsed_time(e) / iters / 1e3
@@ -391,35 +397,32 @@ def main() -> int:
         else:
             uw.uw_matmul_stage(m, 3, None, x, ys[3], part, stream=stream)
 
-    def step(i, events=None):
+    def step(i):
         m = mats[i % len(mats)]
-        for j, st in enumerate(stages):
-            if events is not None:
-                events[j][0].record(stream)
+        for st in stages:
             run_stage(st, m)
-            if events is not None:
-                events[j][1].record(stream)
 
-    def new_events(n):
-        return [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in stages]
-                for _ in range(n)]
-
-    def stage_times(evs, n, which):
-        return {st: 1e3 * sum(evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(n)) / n
-                for j, st in enumerate(stages) if st in which}
+    def burst_us(st, n, i0):
+        """Average launch of one stage: one pair of events around n
+        back-to-back launches over the rotated inputs.  A timing marker between
+        two kernels holds the next dispatch back by about 5 us, so events
+        around single launches would overstate these short kernels."""
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for i in range(n):
+            run_stage(st, mats[(i0 + i) % len(mats)])
+        d1.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * d0.elapsed_time(d1) / n
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # per-stage breakdown, a separate pass before the timed region (events around
-    # every stage); its longest stage is the kernel the roofline reports
+    # per-stage breakdown, a separate pass before the timed region; its
+    # longest stage is the kernel the roofline reports
     nb = max(5, args.steps // 4)
-    bev = new_events(nb)
-    for i in range(nb):
-        step(args.warmup + i, bev[i])
-    torch.cuda.synchronize()
-    stage_us = stage_times(bev, nb, stages)
+    stage_us = {st: burst_us(st, nb, args.warmup) for st in stages}
     gpu_step_us = sum(stage_us.values())
     dom = max(stages, key=lambda st: stage_us[st])
 
@@ -428,22 +431,13 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + nb + i)
+        step(args.warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    # the dominant kernel's average launch: one pair of events around as many
-    # back-to-back launches as timed steps, over the same rotated inputs.  A
-    # timing marker between two kernels holds the next dispatch back by about
-    # 5 us, so events around single launches overstate short kernels.
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    d0.record(stream)
-    for i in range(args.steps):
-        run_stage(dom, mats[(args.warmup + nb + i) % len(mats)])
-    d1.record(stream)
-    torch.cuda.synchronize()
-    dom_us = 1e3 * d0.elapsed_time(d1) / args.steps
+    # the dominant kernel's average launch, over as many launches as timed steps
+    dom_us = burst_us(dom, args.steps, args.warmup)
     for m in mats:
         assert uw.uw_sync_status(m) == 0, "decoder reported corrupt data"
 
@@ -477,7 +471,7 @@ def main() -> int:
                                "outliers x2^10, batch 1, pipelines full/exponent/transcode/direct",
                    "batch": 1, "rotated_copies": args.rotate, "seg_groups": args.seg_groups, "bits_per_weight": round(info.bits_per_weight, 3),
                    "verbatim_groups": int(info.verbatim_groups), "parallelism": "single GPU"},
-        "gpu_step_us": round(gpu_step_us, 2), "breakdown": f"kernels: separate pass of {nb} steps before the timed region",
+        "gpu_step_us": round(gpu_step_us, 2), "breakdown": f"kernels: {nb} back-to-back launches per stage before the timed region",
         "pipelines": pipes, "kernels": kernels, "roofline": roofline,
     }
     if not args.no_extras:

@@ -12,7 +12,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libunweight.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "autotune.cpp", "tables.cpp", "compress.hip", "decode.hip", "gemm.hip", "gemm_mfma.hip"]
+SOURCES = ["api.cpp", "autotune.cpp", "tables.cpp", "compress.hip", "decode.hip", "gemm.hip", "gemm_mfma.hip", "gemm_rf.hip"]
 HEADERS = ["uw_internal.h", "rebuild.h"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function"]
 # packed fp32 instructions are kept out of every kernel

@@ -28,7 +28,8 @@ namespace {
       if (std::getenv("UW_LOG"))                       \
         std::fprintf(stderr, "unweight: %s failed: %s (%s:%d)\n", #call, hipGetErrorString(e_), \
                      __FILE__, __LINE__);              \
-      return e_ == hipErrorOutOfMemory ? UW_ERR_NOMEM : UW_ERR_DEVICE; \
+      return e_ == hipErrorOutOfMemory ? UW_ERR_NOMEM : e_ == hipErrorNotSupported ? UW_ERR_UNSUPPORTED \
+                                                                                 : UW_ERR_DEVICE; \
     }                                                  \
   } while (0)
 

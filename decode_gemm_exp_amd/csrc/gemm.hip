@@ -527,8 +527,11 @@ int kn_slices(const WeightView& w, int nb, const uw_kernel_cfg* cfg) {
 }  // namespace
 
 // Variant numbering seen through uw_kernel_cfg.variant: 1 = VALU GEMV (any
-// batch, eight rows per launch), 2.. = the MFMA tiles of gemm_mfma.hip.
-int gemm_variant_count() { return 1 + mfma2_tile_count(); }
+// batch, eight rows per launch), 2.. = the MFMA tiles of gemm_mfma.hip, then
+// the register-fed MFMA kernels of gemm_rf.hip (stored [N][K] only).
+int rf_first_variant() { return 2 + mfma2_tile_count(); }
+int gemm_variant_count() { return 1 + mfma2_tile_count() + mfma_rf_kinds(); }
+bool gemm_variant_supported(int v, int layout) { return v < rf_first_variant() || layout == 0; }
 
 static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg) {
   if (cfg && cfg->variant > 0 && cfg->variant <= gemm_variant_count()) return cfg->variant;
@@ -544,6 +547,10 @@ size_t gemm_partial_elems(const WeightView& w, int64_t batch, const uw_kernel_cf
     const int64_t rows = batch < kGemvMaxBatch ? batch : kGemvMaxBatch;
     return (size_t)kn_slices(w, (int)rows, cfg) * (size_t)rows * (size_t)w.n;
   }
+  if (v >= rf_first_variant())
+    return w.layout == 0 ? mfma_rf_partial_elems(w, batch, v - rf_first_variant(), cfg ? cfg->split_k : 0,
+                                                 device_cus())
+                         : 0;
   return mfma2_partial_elems(w, batch, v - 2, cfg ? cfg->split_k : 0);
 }
 
@@ -633,6 +640,9 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
     }
     return hipSuccess;
   }
+  if (v >= rf_first_variant())
+    return launch_mfma_rf(w, x, batch, y, ldy, col0, v - rf_first_variant(), cfg ? cfg->split_k : 0, device_cus(),
+                          partial, partial_elems, s);
   return launch_mfma2(w, x, batch, y, ldy, col0, v - 2, cfg ? cfg->split_k : 0, partial, partial_elems, s);
 }
 

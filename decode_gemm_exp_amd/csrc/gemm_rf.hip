@@ -1,0 +1,404 @@
+// gemm_rf.hip -- register-fed reconstructive MFMA GEMM for small batches
+// (up to 64 rows of x per launch), y = x . W^T with W stored [N][K].
+//
+// [EVC] = "Cloudflare推出Unweight無損壓縮系統，將LLM模型大小壓縮15-22%"
+// (easyvibecoding.app/curated/736).  Section "重建矩陣乘法核心運作": the
+// compressed weights are rebuilt to BF16 on chip and fed straight to the
+// matrix units; section "四種執行管道" lists the weight forms the matmul
+// reads (BF16, exponent + sign/mantissa, palette + sign/mantissa).
+//
+// At small batch the matmul is a stream over the weights: every weight is used
+// by at most 64 rows of x, so the kernel is designed to keep many bytes of
+// compressed weights in flight rather than to reuse tiles.
+//   * No block-wide LDS staging: each wave loads its weights straight into
+//     registers, rebuilds BF16 there and issues v_mfma_f32_16x16x32_bf16 with
+//     the rebuilt weights as the A operand (16 output features) and x as the
+//     B operand (16 batch rows per MFMA, up to four groups of 16).
+//   * The order of k inside an MFMA is free as long as A and B agree, so lane
+//     group g (= lane / 16) of a wave takes 32 consecutive k of its row in a
+//     128-wide window: the four lane groups read one whole 128-byte line of
+//     sign+mantissa bytes per row, and MFMA m of the window takes the lane's
+//     weights 8m .. 8m+7.  The lane loads the matching 64 bytes of each x row.
+//   * A wave owns R row tiles (16 R output features) and walks the windows
+//     wave, wave + 4, ... of its K range, double buffered in registers; the
+//     palette format's verbatim flag and rank words are loaded one window
+//     ahead of the data, so a verbatim group's exponents are requested from
+//     the side section directly.
+//   * The four waves of a block cover the same rows and interleaved windows;
+//     their partial sums meet in LDS and are added in a fixed order.  K may be
+//     split further over grid.y, then a fixed-order reduction adds the slices.
+#include "rebuild.h"
+
+namespace uw {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kWin = 128;   // k per window (32 per lane group)
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Which 32 weights of a 128-wide window lane group g (= lane / 16) owns, so
+// that every load instruction reads 64 contiguous bytes of each of its 16 rows:
+//   BF16 (two bytes a weight): MFMA m takes k0 + 32 m + 8 g .. +7;
+//   byte formats: piece p = m / 2 is k0 + 64 p + 16 g .. +15, MFMA m takes
+//   its half m % 2.
+// The x fragment of MFMA m uses the same k (kx_off).
+template <int FMT>
+__device__ __forceinline__ int kx_off(int m, int g) {
+  return FMT == kFmtBf16 ? 32 * m + 8 * g : 64 * (m >> 1) + 16 * g + 8 * (m & 1);
+}
+
+// Compressed data of one lane's 32 weights of one row.
+//   bf16: w[m] = the 8 weights of MFMA m
+//   exp:  s[p] = 16 sign+mantissa bytes of piece p, e[p] = its 16 exponent bytes
+//   pal:  s[p] as above, e[p] = the aligned 16 index bytes holding the
+//         piece's 16 nibbles (in bytes 8 .. 15 for odd lane groups), or its 16
+//         exponent bytes when its group is verbatim
+struct Raw32 {
+  uint4 s0, s1, e0, e1;
+};
+
+// Loads of one lane's 32 weights of a row; el = stored index of the window
+// start plus 16 g (byte formats) or 8 g (BF16).  ok0 / ok1: the window's first
+// / second 64 weights exist.  Invalid pieces read index 0 (valid memory) and
+// are zeroed when rebuilt.  The two pieces of a byte format sit in the
+// window's two groups; fw / fh are the verbatim flag words holding the first
+// and the second group (the same word unless the pair straddles two), rw the
+// rank word of the first.
+template <int FMT>
+__device__ __forceinline__ void load32(const WeightView& w, uint64_t el, bool ok0, bool ok1, uint32_t fw, uint32_t fh,
+                                       uint32_t rw, Raw32& r, uint32_t& verb) {
+  verb = 0;
+  if constexpr (FMT == kFmtBf16) {
+    const uint64_t a = ok0 ? el : 0, b = ok1 ? el + 64 : 0;
+    r.s0 = *reinterpret_cast<const uint4*>(w.bf16 + a);
+    r.s1 = *reinterpret_cast<const uint4*>(w.bf16 + a + 32);
+    r.e0 = *reinterpret_cast<const uint4*>(w.bf16 + b);
+    r.e1 = *reinterpret_cast<const uint4*>(w.bf16 + b + 32);
+  } else if constexpr (FMT == kFmtExp) {
+    const uint64_t a = ok0 ? el : 0, b = ok1 ? el + 64 : 0;
+    r.s0 = *reinterpret_cast<const uint4*>(w.sm + a);
+    r.s1 = *reinterpret_cast<const uint4*>(w.sm + b);
+    r.e0 = *reinterpret_cast<const uint4*>(w.ex + a);
+    r.e1 = *reinterpret_cast<const uint4*>(w.ex + b);
+  } else {
+    const uint64_t a = ok0 ? el : 0, b = ok1 ? el + 64 : 0;
+    r.s0 = *reinterpret_cast<const uint4*>(w.sm + a);
+    r.s1 = *reinterpret_cast<const uint4*>(w.sm + b);
+    const uint64_t g0 = el >> 6;   // the window's first group
+    const bool v0 = ok0 & group_verbatim(fw, g0);
+    const bool v1 = ok1 & group_verbatim(fh, g0 + 1);
+    const uint32_t r0 = group_rank(fw, rw, g0);
+    const uint32_t r1 = r0 + (group_verbatim(fw, g0) ? 1u : 0u);
+    // index nibbles: the aligned 16 bytes that hold the piece's 8 (the half is
+    // picked when rebuilding), so the read never passes the end of the array
+    const uint8_t* p0 = v0 ? w.vexp + (uint64_t)r0 * 64 + (el & 63) : w.pidx + ((a >> 1) & ~(uint64_t)15);
+    const uint8_t* p1 = v1 ? w.vexp + (uint64_t)r1 * 64 + (el & 63) : w.pidx + ((b >> 1) & ~(uint64_t)15);
+    r.e0 = *reinterpret_cast<const uint4*>(p0);
+    r.e1 = *reinterpret_cast<const uint4*>(p1);
+    verb = (v0 ? 1u : 0u) | (v1 ? 2u : 0u);
+  }
+}
+
+// A operand of MFMA m as BF16 (ok: the piece holding it exists)
+template <int FMT>
+__device__ __forceinline__ bf16x8 a_frag(const WeightView& w, const Raw32& r, uint32_t verb, bool ok, int m,
+                                         int g) {
+  uint4 o;
+  if constexpr (FMT == kFmtBf16) {
+    o = m == 0 ? r.s0 : m == 1 ? r.s1 : m == 2 ? r.e0 : r.e1;
+  } else {
+    const uint4& sp = (m >> 1) ? r.s1 : r.s0;
+    const uint4& ep = (m >> 1) ? r.e1 : r.e0;
+    const int h = m & 1;   // half of the piece
+    const uint32_t s0 = word(sp, 2 * h), s1 = word(sp, 2 * h + 1);
+    uint32_t e0, e1;
+    if constexpr (FMT == kFmtExp) {
+      e0 = word(ep, 2 * h);
+      e1 = word(ep, 2 * h + 1);
+    } else {
+      pal8<FMT == kFmtPalRun>(word(ep, h + 2 * (g & 1)), w.pal, e0, e1);
+      const bool vb = (verb >> (m >> 1)) & 1u;
+      e0 = vb ? word(ep, 2 * h) : e0;
+      e1 = vb ? word(ep, 2 * h + 1) : e1;
+    }
+    rebuild4(s0, e0, o.x, o.y);
+    rebuild4(s1, e1, o.z, o.w);
+  }
+  o.x = ok ? o.x : 0u;
+  o.y = ok ? o.y : 0u;
+  o.z = ok ? o.z : 0u;
+  o.w = ok ? o.w : 0u;
+  return __builtin_bit_cast(bf16x8, o);
+}
+
+template <int FMT, int R, int NBG>
+__global__ __launch_bounds__(256) void k_mfma_rf(WeightView w, const uint16_t* __restrict__ x, int B,
+                                                 float* __restrict__ y, int64_t ldy, int64_t col0, int64_t kslice,
+                                                 float* __restrict__ part, uint32_t fwords) {
+  constexpr int SLOT = R * NBG * 64;   // float4 per wave in the reduction buffer
+  __shared__ f32x4 red[4 * SLOT];
+  extern __shared__ uint32_t fl[];     // palette: the block's verbatim flag words, then their rank words
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int64_t N = (int64_t)w.n, K = (int64_t)w.k;
+  const int64_t n0 = (int64_t)blockIdx.x * (16 * R);
+  const int64_t kb = (int64_t)blockIdx.y * kslice;
+  const int64_t ke = kb + kslice < K ? kb + kslice : K;
+  const int nwin = (int)((ke - kb + kWin - 1) / kWin);
+  const int mine = nwin > wave ? (nwin - wave + 3) / 4 : 0;   // windows wave, wave + 4, ...
+
+  // The block's rows are contiguous in storage, so the flag and rank words of
+  // their groups are too: at most fwords of each, staged in LDS once.
+  uint64_t fbase = 0;
+  if constexpr (fmt_is_pal(FMT)) {
+    const int64_t nl = n0 + 16 * R < N ? n0 + 16 * R : N;
+    fbase = (uint64_t)(n0 * K) >> 11;
+    const uint32_t cnt = (uint32_t)((((uint64_t)(nl * K) + 2047) >> 11) - fbase);
+    for (uint32_t i = threadIdx.x; i < cnt; i += 256) {
+      fl[i] = w.vflags[fbase + i];
+      fl[fwords + i] = w.vrank[fbase + i];
+    }
+    __syncthreads();
+  }
+
+  // x rows of this lane (rows past the batch are clamped: their columns are never stored)
+  int64_t xrow[NBG];
+#pragma unroll
+  for (int q = 0; q < NBG; ++q) {
+    const int b = 16 * q + i16;
+    xrow[q] = (int64_t)(b < B ? b : B - 1) * K;
+  }
+
+  // each block starts its walk at a different window, so the chip's
+  // concurrent reads spread over the memory channels instead of all rows
+  // being read at the same column offset
+  const int rot = mine > 0 ? (int)((blockIdx.x * 5u + blockIdx.y * 3u) % (unsigned)mine) : 0;
+  auto win_k = [&](int j) __attribute__((always_inline)) {
+    int jj = j + rot;
+    jj -= jj >= mine ? mine : 0;
+    return kb + (int64_t)kWin * (wave + 4 * jj);
+  };
+  const int goff = FMT == kFmtBf16 ? 8 * g : 16 * g;   // lane group's offset in a window
+  // flag and rank words of a window's groups (from LDS).  With K / 64 odd,
+  // the two groups of a window may straddle two flag words.
+  auto load_flags = [&](int j, uint32_t (&fw)[R], uint32_t (&fh)[R], uint32_t (&rw)[R]) __attribute__((always_inline)) {
+    if constexpr (fmt_is_pal(FMT)) {
+      const int64_t k0 = win_k(j);
+      const bool kv = (j < mine) & (k0 < ke);
+      const bool h1 = k0 + 64 < ke;
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        const int64_t n = n0 + 16 * t + i16;
+        const bool v = kv & (n < N);
+        const uint64_t g0 = (uint64_t)(n * K + k0) >> 6;
+        const uint32_t fi = v ? (uint32_t)((g0 >> 5) - fbase) : 0u;
+        const uint32_t fj = (v & h1 & ((g0 & 31) == 31)) ? fi + 1 : fi;
+        fw[t] = fl[fi];
+        fh[t] = fl[fj];
+        rw[t] = fl[fwords + fi];
+      }
+    }
+  };
+  // okbits: bit 2t = row tile t's first 64 weights exist, bit 2t+1 = its second 64
+  auto load_win = [&](int j, Raw32 (&r)[R], uint4 (&xr)[NBG][4], const uint32_t (&fw)[R], const uint32_t (&fh)[R],
+                      const uint32_t (&rw)[R], uint32_t& vbits, uint32_t& okbits) __attribute__((always_inline)) {
+    const int64_t k0 = win_k(j);
+    const bool kv = (j < mine) & (k0 < ke);
+    const bool h1 = k0 + 64 < ke;
+    vbits = 0;
+    okbits = 0;
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      const int64_t n = n0 + 16 * t + i16;
+      const bool v = kv & (n < N);
+      uint32_t vb;
+      load32<FMT>(w, (uint64_t)(n * K + k0 + goff), v, v & h1, fmt_is_pal(FMT) ? fw[t] : 0u,
+                  fmt_is_pal(FMT) ? fh[t] : 0u, fmt_is_pal(FMT) ? rw[t] : 0u, r[t], vb);
+      vbits |= vb << (2 * t);
+      okbits |= (v ? 1u : 0u) << (2 * t);
+      okbits |= (v & h1 ? 1u : 0u) << (2 * t + 1);
+    }
+    const int64_t kx = kv ? k0 : 0;
+#pragma unroll
+    for (int q = 0; q < NBG; ++q)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int64_t kk = (kv & (h1 | (kx_off<FMT>(m, g) < 64))) ? kx + kx_off<FMT>(m, g) : 0;
+        const uint4 v = *reinterpret_cast<const uint4*>(x + xrow[q] + kk);
+        xr[q][m] = v;
+      }
+  };
+
+  f32x4 acc[R][NBG];
+#pragma unroll
+  for (int t = 0; t < R; ++t)
+#pragma unroll
+    for (int q = 0; q < NBG; ++q) acc[t][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Raw32 (&r)[R], const uint4 (&xr)[NBG][4], uint32_t vbits,
+                     uint32_t okbits) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        // the piece holding MFMA m: BF16 first half m < 2, byte formats piece m / 2
+        const bool ok = (okbits >> (2 * t + (m >> 1))) & 1u;
+        const bf16x8 a = a_frag<FMT>(w, r[t], (vbits >> (2 * t)) & 3u, ok, m, g);
+#pragma unroll
+        for (int q = 0; q < NBG; ++q)
+          acc[t][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, xr[q][m]), acc[t][q],
+                                                              0, 0, 0);
+      }
+  };
+
+  // two windows in registers: the loads of window j+2 (and the flag words of
+  // j+4) are issued as soon as window j has been consumed.  Windows past the
+  // range load index 0 and add zeros, so the loop has no tail.
+  Raw32 rA[R], rB[R];
+  uint4 xA[NBG][4], xB[NBG][4];
+  uint32_t fA[R], hA[R], gA[R], fB[R], hB[R], gB[R];
+  uint32_t vA, oA, vB, oB;
+#pragma unroll
+  for (int t = 0; t < R; ++t) fA[t] = hA[t] = gA[t] = fB[t] = hB[t] = gB[t] = 0u;
+  // the prologue issues its loads in the loop's order (A before B), so the
+  // waits at the loop head can count only the loads it needs
+  load_flags(0, fA, hA, gA);
+  load_flags(1, fB, hB, gB);
+  __builtin_amdgcn_sched_barrier(0);
+  load_win(0, rA, xA, fA, hA, gA, vA, oA);
+  load_flags(2, fA, hA, gA);
+  __builtin_amdgcn_sched_barrier(0);
+  load_win(1, rB, xB, fB, hB, gB, vB, oB);
+  load_flags(3, fB, hB, gB);
+  __builtin_amdgcn_sched_barrier(0);
+  // (the scheduling barriers keep each buffer's reloads behind the MFMAs that
+  // read it: hoisted above them, the loads land in other registers and the
+  // loop's back edge has to wait for every load in flight)
+  // (a do-while: with no guard in front of the loop, the compiler cannot sink
+  // the prologue's x loads behind the second window's weights)
+  int j = 0;
+  do {
+    compute(rA, xA, vA, oA);
+    __builtin_amdgcn_sched_barrier(0);
+    load_win(j + 2, rA, xA, fA, hA, gA, vA, oA);
+    load_flags(j + 4, fA, hA, gA);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(rB, xB, vB, oB);
+    __builtin_amdgcn_sched_barrier(0);
+    load_win(j + 3, rB, xB, fB, hB, gB, vB, oB);
+    load_flags(j + 5, fB, hB, gB);
+    __builtin_amdgcn_sched_barrier(0);
+    j += 2;
+  } while (j < mine);
+
+  // the four waves' sums, added in wave order.  D of v_mfma_f32_16x16x32_bf16:
+  // lane l holds rows 4 (l / 16) .. +3 (output features) of column l % 16 (batch row)
+#pragma unroll
+  for (int t = 0; t < R; ++t)
+#pragma unroll
+    for (int q = 0; q < NBG; ++q) red[wave * SLOT + (t * NBG + q) * 64 + lane] = acc[t][q];
+  __syncthreads();
+  float* out = part ? part + (uint64_t)blockIdx.y * (uint64_t)B * (uint64_t)N : y + col0;
+  const int64_t ld = part ? N : ldy;
+  for (int e = threadIdx.x; e < SLOT; e += 256) {
+    const f32x4 s = ((red[e] + red[SLOT + e]) + red[2 * SLOT + e]) + red[3 * SLOT + e];
+    const int ln = e & 63, tq = e >> 6, q = tq % NBG, t = tq / NBG;
+    const int64_t n = n0 + 16 * t + 4 * (ln >> 4);
+    const int b = 16 * q + (ln & 15);
+    if (b < B) {
+      float* o = out + (int64_t)b * ld + n;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N) o[r] = s[r];
+    }
+  }
+}
+
+typedef void (*RfFn)(WeightView, const uint16_t*, int, float*, int64_t, int64_t, int64_t, float*, uint32_t);
+
+template <int F, int R>
+RfFn rf_fn(int nbg) {
+  if (nbg <= 1) return k_mfma_rf<F, R, 1>;
+  if (nbg <= 2) return k_mfma_rf<F, R, 2>;
+  return k_mfma_rf<F, R, 4>;
+}
+
+template <int R>
+RfFn rf_pick(int fmt, int nbg) {
+  return fmt == kFmtBf16 ? rf_fn<kFmtBf16, R>(nbg)
+         : fmt == kFmtExp ? rf_fn<kFmtExp, R>(nbg)
+         : fmt == kFmtPal ? rf_fn<kFmtPal, R>(nbg) : rf_fn<kFmtPalRun, R>(nbg);
+}
+
+constexpr int kRfMaxBatch = 64;
+constexpr uint64_t kRfMaxFlagLds = 64 * 1024;   // bytes of staged flag and rank words (K up to 256 Ki at 4 row tiles)
+
+int rf_nbg(int64_t nb) { return nb <= 16 ? 1 : nb <= 32 ? 2 : 4; }
+
+}  // namespace
+
+int mfma_rf_kinds() { return 2; }   // row tiles per wave: 2 (kind 0) or 4 (kind 1)
+int mfma_rf_max_batch() { return kRfMaxBatch; }
+
+// K slices over grid.y: none unless the row blocks leave the chip under two
+// blocks per CU, and never below 16 windows per slice (4 per wave).
+int mfma_rf_slices(const WeightView& w, int kind, int split_hint, int cus) {
+  const int R = kind == 0 ? 2 : 4;
+  const int64_t rowblocks = ((int64_t)w.n + 16 * R - 1) / (16 * R);
+  const int64_t wins = ((int64_t)w.k + kWin - 1) / kWin;
+  int s = 1;
+  if (split_hint > 0) {
+    s = split_hint;
+  } else {
+    while (rowblocks * s < 2 * cus && wins / (2 * s) >= 16) s *= 2;
+  }
+  if (s > wins) s = (int)wins;
+  if (s < 1) s = 1;
+  return s;
+}
+
+size_t mfma_rf_partial_elems(const WeightView& w, int64_t batch, int kind, int split_hint, int cus) {
+  const int s = mfma_rf_slices(w, kind, split_hint, cus);
+  const int64_t nb = batch < kRfMaxBatch ? batch : kRfMaxBatch;
+  return s > 1 ? (size_t)s * (size_t)nb * (size_t)w.n : 0;
+}
+
+hipError_t launch_mfma_rf(const WeightView& w, const uint16_t* x, int64_t batch, float* y, int64_t ldy,
+                          int64_t col0, int kind, int split_hint, int cus, float* part, size_t part_elems,
+                          hipStream_t s) {
+  if (w.layout != 0) return hipErrorNotSupported;
+  const int R = kind == 0 ? 2 : 4;
+  const int slices = mfma_rf_slices(w, kind, split_hint, cus);
+  const int64_t wins = ((int64_t)w.k + kWin - 1) / kWin;
+  const int64_t kslice = ((wins + slices - 1) / slices) * kWin;
+  const unsigned rowblocks = (unsigned)(((int64_t)w.n + 16 * R - 1) / (16 * R));
+  // flag words of one block's rows (palette formats), staged in LDS
+  const uint64_t fw64 = fmt_is_pal(w.fmt) ? (uint64_t)16 * R * w.k / 2048 + 2 : 0;
+  if (fw64 * 8 > kRfMaxFlagLds) return hipErrorNotSupported;
+  const uint32_t fwords = (uint32_t)fw64;
+  for (int64_t b0 = 0; b0 < batch; b0 += kRfMaxBatch) {
+    const int64_t nb = batch - b0 < kRfMaxBatch ? batch - b0 : kRfMaxBatch;
+    const bool split = slices > 1;
+    if (split && (part == nullptr || part_elems < (size_t)slices * (size_t)nb * (size_t)w.n))
+      return hipErrorInvalidValue;
+    const RfFn f = kind == 0 ? rf_pick<2>(w.fmt, rf_nbg(nb)) : rf_pick<4>(w.fmt, rf_nbg(nb));
+    const uint16_t* xb = x + (uint64_t)b0 * w.k;
+    float* yb = y + (uint64_t)b0 * (uint64_t)ldy;
+    hipLaunchKernelGGL(f, dim3(rowblocks, (unsigned)slices), dim3(256), (size_t)fwords * 8, s, w, xb, (int)nb, yb,
+                       ldy, col0, kslice, split ? part : nullptr, fwords);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (split) {
+      e = launch_sum_slices(part, slices, w.n, nb, yb, ldy, col0, s);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace uw

@@ -121,6 +121,8 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
 size_t gemm_partial_elems(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg);
 size_t gemm_partial_elems_max(const WeightView& w, int64_t batch, int split_k);
 int gemm_variant_count();
+int rf_first_variant();                          // first register-fed MFMA variant
+bool gemm_variant_supported(int v, int layout);  // register-fed variants: stored [N][K] only
 // y[b][col0 + n] = sum over slices p of part[p][b][n], fixed order
 hipError_t launch_sum_slices(const float* part, int slices, uint64_t n, int64_t batch, float* y, int64_t ldy,
                              int64_t col0, hipStream_t s);
@@ -132,5 +134,13 @@ int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint);
 size_t mfma2_partial_elems(const WeightView& w, int64_t batch, int tile, int split_hint);
 hipError_t launch_mfma2(const WeightView& w, const uint16_t* x, int64_t batch, float* y, int64_t ldy, int64_t col0,
                         int tile, int split_hint, float* part, size_t part_elems, hipStream_t s);
+// gemm_rf.hip (kind 0: two 16-row tiles per wave, kind 1: four)
+int mfma_rf_kinds();
+int mfma_rf_max_batch();
+int mfma_rf_slices(const WeightView& w, int kind, int split_hint, int cus);
+size_t mfma_rf_partial_elems(const WeightView& w, int64_t batch, int kind, int split_hint, int cus);
+hipError_t launch_mfma_rf(const WeightView& w, const uint16_t* x, int64_t batch, float* y, int64_t ldy,
+                          int64_t col0, int kind, int split_hint, int cus, float* part, size_t part_elems,
+                          hipStream_t s);
 
 }  // namespace uw

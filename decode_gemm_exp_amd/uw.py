@@ -23,6 +23,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 UW_OK = 0
+UW_ERR_UNSUPPORTED = -2
 STATUS = {0: "ok", -1: "invalid", -2: "unsupported", -3: "nomem", -4: "device", -5: "corrupt",
           -6: "state", -7: "workspace"}
 PIPE_FULL, PIPE_EXPONENT, PIPE_PALETTE_TRANSCODE, PIPE_PALETTE_DIRECT = 0, 1, 2, 3

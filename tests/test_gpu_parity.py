@@ -83,7 +83,7 @@ def run_pipeline(uw, m, pipeline, x, cfg=None):
     y = torch.full((x.shape[0], info.n), float("nan"), dtype=torch.float32, device=DEV)
     ws_bytes = uw.uw_workspace_size(m, pipeline, x.shape[0])
     if cfg and cfg.get("split_k"):
-        ws_bytes = max(ws_bytes, 4 * cfg["split_k"] * min(x.shape[0], 8) * info.n + 2 * info.numel + 4096)
+        ws_bytes = max(ws_bytes, 4 * cfg["split_k"] * min(x.shape[0], 64) * info.n + 2 * info.numel + 4096)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV)
     uw.uw_matmul_reconstruct(m, pipeline, x, y, ws, cfg=cfg)
     torch.cuda.synchronize()
@@ -179,10 +179,43 @@ def test_gemm_ragged_all_pipelines(uw, synth, oracle, layout, batch):
     for p in range(4):
         y = run_pipeline(uw, m, p, x)
         check_gemm(oracle, y, x_np, w_np, layout, what=f"pipeline {p}")
-    # every variant, forced
+    # every variant, forced (the register-fed ones, last two, take stored [N][K] only)
     for v in range(1, uw.variant_count() + 1):
+        if layout == 1 and v >= RF_FIRST(uw):
+            with pytest.raises(uw.UwError) as ei:
+                run_pipeline(uw, m, 3, x, cfg={"variant": v})
+            assert ei.value.status == uw.UW_ERR_UNSUPPORTED
+            continue
         y = run_pipeline(uw, m, 3, x, cfg={"variant": v})
         check_gemm(oracle, y, x_np, w_np, layout, what=f"variant {v}")
+
+
+def RF_FIRST(uw):
+    return uw.variant_count() - 1
+
+
+# register-fed MFMA kernels (stored [N][K]): row counts that leave partial
+# 32- and 64-row blocks, K with a partial 128-wide window (K % 128 == 64), a
+# K whose windows split unevenly over the four waves, batches across the
+# 16-row groups and past the 64-row launch limit, K slices, verbatim-rich and
+# run palettes
+@pytest.mark.parametrize("n,k,outliers", [(200, 1088, 0.01), (70, 4096, 0.0), (96, 320, 0.02)])
+def test_register_fed_mfma(uw, synth, oracle, n, k, outliers):
+    say(f"register-fed mfma n={n} k={k} outliers={outliers}")
+    w = synth.weights(n, k, 0.02, outliers, 10, seed=n * 7 + k).to(DEV)
+    m = gpu_compress(uw, w, n, k, 0)
+    uw.uw_transcode_palette(m, None)
+    w_np = bits(w)
+    for batch in (1, 5, 16, 17, 40, 64, 65, 130):
+        x = synth.activations(batch, k, seed=batch + 11).to(DEV)
+        x_np = bits(x)
+        for v in (RF_FIRST(uw), RF_FIRST(uw) + 1):
+            for p in range(4):
+                y = run_pipeline(uw, m, p, x, cfg={"variant": v})
+                check_gemm(oracle, y, x_np, w_np, 0, what=f"batch {batch} variant {v} pipeline {p}")
+            for split in (2, 3):
+                y = run_pipeline(uw, m, 3, x, cfg={"variant": v, "split_k": split})
+                check_gemm(oracle, y, x_np, w_np, 0, what=f"batch {batch} variant {v} split {split}")
 
 
 def _palette_is_run(m):
@@ -240,6 +273,10 @@ def test_gemm_one_hot_exact(uw, synth, oracle, layout):
         for p in range(4):
             y = run_pipeline(uw, m, p, x)
             assert np.array_equal(y, expect), f"batch {batch} pipeline {p}"
+        if layout == 0:   # output placement of the register-fed kernels
+            for v in (RF_FIRST(uw), RF_FIRST(uw) + 1):
+                y = run_pipeline(uw, m, 2, x, cfg={"variant": v})
+                assert np.array_equal(y, expect), f"batch {batch} variant {v}"
 
 
 def test_gemm_identity_exact(uw, synth):
