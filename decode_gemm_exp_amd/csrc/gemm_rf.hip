@@ -368,19 +368,26 @@ size_t mfma_rf_partial_elems(const WeightView& w, int64_t batch, int kind, int s
   return s > 1 ? (size_t)s * (size_t)nb * (size_t)w.n : 0;
 }
 
+// flag and rank words one block stages (palette formats)
+static uint64_t rf_flag_words(const WeightView& w, int kind) {
+  const int R = kind == 0 ? 2 : 4;
+  return fmt_is_pal(w.fmt) ? (uint64_t)16 * R * w.k / 2048 + 2 : 0;
+}
+
+bool mfma_rf_supported(const WeightView& w, int kind) {
+  return w.layout == 0 && rf_flag_words(w, kind) * 8 <= kRfMaxFlagLds;
+}
+
 hipError_t launch_mfma_rf(const WeightView& w, const uint16_t* x, int64_t batch, float* y, int64_t ldy,
                           int64_t col0, int kind, int split_hint, int cus, float* part, size_t part_elems,
                           hipStream_t s) {
-  if (w.layout != 0) return hipErrorNotSupported;
+  if (!mfma_rf_supported(w, kind)) return hipErrorNotSupported;
   const int R = kind == 0 ? 2 : 4;
   const int slices = mfma_rf_slices(w, kind, split_hint, cus);
   const int64_t wins = ((int64_t)w.k + kWin - 1) / kWin;
   const int64_t kslice = ((wins + slices - 1) / slices) * kWin;
   const unsigned rowblocks = (unsigned)(((int64_t)w.n + 16 * R - 1) / (16 * R));
-  // flag words of one block's rows (palette formats), staged in LDS
-  const uint64_t fw64 = fmt_is_pal(w.fmt) ? (uint64_t)16 * R * w.k / 2048 + 2 : 0;
-  if (fw64 * 8 > kRfMaxFlagLds) return hipErrorNotSupported;
-  const uint32_t fwords = (uint32_t)fw64;
+  const uint32_t fwords = (uint32_t)rf_flag_words(w, kind);   // staged in LDS per block
   for (int64_t b0 = 0; b0 < batch; b0 += kRfMaxBatch) {
     const int64_t nb = batch - b0 < kRfMaxBatch ? batch - b0 : kRfMaxBatch;
     const bool split = slices > 1;

@@ -137,6 +137,7 @@ hipError_t launch_mfma2(const WeightView& w, const uint16_t* x, int64_t batch, f
 // gemm_rf.hip (kind 0: two 16-row tiles per wave, kind 1: four)
 int mfma_rf_kinds();
 int mfma_rf_max_batch();
+bool mfma_rf_supported(const WeightView& w, int kind);   // stored [N][K], flag words fit in LDS
 int mfma_rf_slices(const WeightView& w, int kind, int split_hint, int cus);
 size_t mfma_rf_partial_elems(const WeightView& w, int64_t batch, int kind, int split_hint, int cus);
 hipError_t launch_mfma_rf(const WeightView& w, const uint16_t* x, int64_t batch, float* y, int64_t ldy,

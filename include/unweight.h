@@ -208,8 +208,12 @@ uw_status uw_gemm_bf16(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout la
 
 /* Number of GEMM variants selectable through uw_kernel_cfg.variant, numbered
  * 1..count: 1 = VALU GEMV (v_dot2; any batch, eight rows per launch);
- * 2..count = MFMA tiles 64x128, 128x128, 128x256, 256x128, 256x256, 32x128,
- * 32x256 (batch rows x columns; weights rebuilt into LDS). */
+ * 2..count-2 = MFMA tiles 64x128, 128x128, 128x256, 256x128, 256x256,
+ * 32x128, 32x256 (batch rows x columns; weights rebuilt into LDS);
+ * count-1, count = register-fed MFMA with two or four 16-row weight tiles per
+ * wave (weights rebuilt in registers; 64 batch rows per launch; stored
+ * [N][K] only: UW_ERR_UNSUPPORTED for [K][N]).  split_k applies to the KN
+ * GEMV, the LDS-tiled and the register-fed MFMA kernels. */
 int32_t uw_variant_count(void);
 
 /* One entry of a sequence of projections run back to back. */
