@@ -535,12 +535,12 @@ bool gemm_variant_supported(int v, int layout) { return v < rf_first_variant() |
 
 // Default kernel by batch (measured on the 8B and 70B MLP shapes): the VALU
 // GEMV while the batch is tiny; for stored [N][K] the register-fed MFMA
-// kernel up to 64 rows (two row tiles per wave up to 16 rows, four above);
+// kernel up to 64 rows (two row tiles per wave up to 32 rows, four above);
 // otherwise the LDS-tiled MFMA kernel with the cost model's tile.
 static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg) {
   if (cfg && cfg->variant > 0 && cfg->variant <= gemm_variant_count()) return cfg->variant;
   if (w.layout == 0) {
-    const int kind = batch <= 16 ? 0 : 1;
+    const int kind = batch <= 32 ? 0 : 1;
     if (batch <= 4) return 1;
     if (batch <= mfma_rf_max_batch() && mfma_rf_supported(w, kind)) return rf_first_variant() + kind;
   }

@@ -27,6 +27,8 @@
 //   * The four waves of a block cover the same rows and interleaved windows;
 //     their partial sums meet in LDS and are added in a fixed order.  K may be
 //     split further over grid.y, then a fixed-order reduction adds the slices.
+#include <algorithm>
+
 #include "rebuild.h"
 
 namespace uw {
@@ -139,7 +141,8 @@ __device__ __forceinline__ bf16x8 a_frag(const WeightView& w, const Raw32& r, ui
 template <int FMT, int R, int NBG>
 __global__ __launch_bounds__(256) void k_mfma_rf(WeightView w, const uint16_t* __restrict__ x, int B,
                                                  float* __restrict__ y, int64_t ldy, int64_t col0, int64_t kslice,
-                                                 float* __restrict__ part, uint32_t fwords) {
+                                                 float* __restrict__ part, uint32_t fwords,
+                                                 const uint4* __restrict__ xp) {
   constexpr int SLOT = R * NBG * 64;   // float4 per wave in the reduction buffer
   __shared__ f32x4 red[4 * SLOT];
   extern __shared__ uint32_t fl[];     // palette: the block's verbatim flag words, then their rank words
@@ -224,12 +227,15 @@ __global__ __launch_bounds__(256) void k_mfma_rf(WeightView w, const uint16_t* _
       okbits |= (v & h1 ? 1u : 0u) << (2 * t + 1);
     }
     const int64_t kx = kv ? k0 : 0;
+    const uint64_t wabs = (uint64_t)(kx / kWin);   // window index along K (packed x)
 #pragma unroll
     for (int q = 0; q < NBG; ++q)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int64_t kk = (kv & (h1 | (kx_off<FMT>(m, g) < 64))) ? kx + kx_off<FMT>(m, g) : 0;
-        const uint4 v = *reinterpret_cast<const uint4*>(x + xrow[q] + kk);
+        const uint4* pa = xp ? xp + ((wabs * NBG + q) * 4 + m) * 64 + lane
+                             : reinterpret_cast<const uint4*>(x + xrow[q] + kk);
+        const uint4 v = *pa;
         xr[q][m] = v;
       }
   };
@@ -319,7 +325,28 @@ __global__ __launch_bounds__(256) void k_mfma_rf(WeightView w, const uint16_t* _
   }
 }
 
-typedef void (*RfFn)(WeightView, const uint16_t*, int, float*, int64_t, int64_t, int64_t, float*, uint32_t);
+// x in the order the kernel's lanes read it: entry ((w * NBG + q) * 4 + m) * 64
+// + lane holds the 8 x values of batch row 16 q + lane % 16 (clamped to the
+// last row) that MFMA m of window w multiplies, so each of the kernel's x
+// loads reads 1 KB of contiguous memory instead of 16 rows in 16-byte pieces.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_rf_pack_x(const uint16_t* __restrict__ x, int B, int64_t K, int nbg,
+                                                   uint4* __restrict__ xp, uint64_t entries) {
+  for (uint64_t e = (uint64_t)blockIdx.x * 256 + threadIdx.x; e < entries; e += (uint64_t)gridDim.x * 256) {
+    const int lane = (int)(e & 63), m = (int)((e >> 6) & 3);
+    const uint64_t r = e >> 8;
+    const int q = (int)(r % (uint64_t)nbg);
+    const int64_t wabs = (int64_t)(r / (uint64_t)nbg);
+    const int b0 = 16 * q + (lane & 15), b = b0 < B ? b0 : B - 1;
+    const int64_t k = wabs * kWin + kx_off<FMT>(m, lane >> 4);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (k + 8 <= K) v = *reinterpret_cast<const uint4*>(x + (int64_t)b * K + k);
+    xp[e] = v;
+  }
+}
+
+typedef void (*RfFn)(WeightView, const uint16_t*, int, float*, int64_t, int64_t, int64_t, float*, uint32_t,
+                     const uint4*);
 
 template <int F, int R>
 RfFn rf_fn(int nbg) {
@@ -362,10 +389,21 @@ int mfma_rf_slices(const WeightView& w, int kind, int split_hint, int cus) {
   return s;
 }
 
+// x is packed (k_rf_pack_x) for launches of more than 8 rows: below that the
+// rows past the batch repeat the last one and the plain loads are cheaper
+static bool rf_packs(int64_t nb) { return nb > 8; }
+static size_t rf_part_floats(const WeightView& w, int slices, int64_t nb) {   // 16-byte multiple
+  return slices > 1 ? ((size_t)slices * (size_t)nb * (size_t)w.n + 3) & ~(size_t)3 : 0;
+}
+static size_t rf_pack_entries(const WeightView& w, int64_t nb) {
+  const int64_t wins = ((int64_t)w.k + kWin - 1) / kWin;
+  return rf_packs(nb) ? (size_t)wins * (size_t)rf_nbg(nb) * 4 * 64 : 0;
+}
+
 size_t mfma_rf_partial_elems(const WeightView& w, int64_t batch, int kind, int split_hint, int cus) {
   const int s = mfma_rf_slices(w, kind, split_hint, cus);
   const int64_t nb = batch < kRfMaxBatch ? batch : kRfMaxBatch;
-  return s > 1 ? (size_t)s * (size_t)nb * (size_t)w.n : 0;
+  return rf_part_floats(w, s, nb) + 4 * rf_pack_entries(w, nb);
 }
 
 // flag and rank words one block stages (palette formats)
@@ -391,13 +429,26 @@ hipError_t launch_mfma_rf(const WeightView& w, const uint16_t* x, int64_t batch,
   for (int64_t b0 = 0; b0 < batch; b0 += kRfMaxBatch) {
     const int64_t nb = batch - b0 < kRfMaxBatch ? batch - b0 : kRfMaxBatch;
     const bool split = slices > 1;
-    if (split && (part == nullptr || part_elems < (size_t)slices * (size_t)nb * (size_t)w.n))
-      return hipErrorInvalidValue;
+    const size_t pf = rf_part_floats(w, slices, nb), pe = rf_pack_entries(w, nb);
+    if ((split || pe > 0) && (part == nullptr || part_elems < pf + 4 * pe)) return hipErrorInvalidValue;
     const RfFn f = kind == 0 ? rf_pick<2>(w.fmt, rf_nbg(nb)) : rf_pick<4>(w.fmt, rf_nbg(nb));
     const uint16_t* xb = x + (uint64_t)b0 * w.k;
     float* yb = y + (uint64_t)b0 * (uint64_t)ldy;
+    uint4* xp = nullptr;
+    if (pe > 0) {
+      xp = reinterpret_cast<uint4*>(part + pf);
+      const unsigned grid = (unsigned)std::min<size_t>((pe + 255) / 256, 4096);
+      if (w.fmt == kFmtBf16)
+        hipLaunchKernelGGL(k_rf_pack_x<kFmtBf16>, dim3(grid), dim3(256), 0, s, xb, (int)nb, (int64_t)w.k, rf_nbg(nb),
+                           xp, (uint64_t)pe);
+      else
+        hipLaunchKernelGGL(k_rf_pack_x<kFmtExp>, dim3(grid), dim3(256), 0, s, xb, (int)nb, (int64_t)w.k, rf_nbg(nb),
+                           xp, (uint64_t)pe);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(f, dim3(rowblocks, (unsigned)slices), dim3(256), (size_t)fwords * 8, s, w, xb, (int)nb, yb,
-                       ldy, col0, kslice, split ? part : nullptr, fwords);
+                       ldy, col0, kslice, split ? part : nullptr, fwords, (const uint4*)xp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (split) {

@@ -83,7 +83,9 @@ def run_pipeline(uw, m, pipeline, x, cfg=None):
     y = torch.full((x.shape[0], info.n), float("nan"), dtype=torch.float32, device=DEV)
     ws_bytes = uw.uw_workspace_size(m, pipeline, x.shape[0])
     if cfg and cfg.get("split_k"):
-        ws_bytes = max(ws_bytes, 4 * cfg["split_k"] * min(x.shape[0], 64) * info.n + 2 * info.numel + 4096)
+        # partial slices, preprocessed weights and the register-fed kernel's packed x
+        packed = (info.k // 128 + 1) * 4 * 4096
+        ws_bytes = max(ws_bytes, 4 * cfg["split_k"] * min(x.shape[0], 64) * info.n + 2 * info.numel + packed + 4096)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV)
     uw.uw_matmul_reconstruct(m, pipeline, x, y, ws, cfg=cfg)
     torch.cuda.synchronize()
