@@ -536,15 +536,20 @@ bool gemm_variant_supported(int v, int layout) { return v < rf_first_variant() |
 // Default kernel by batch (measured on the 8B and 70B MLP shapes): the VALU
 // GEMV while the batch is tiny; for stored [N][K] the register-fed MFMA
 // kernel up to 64 rows (two row tiles per wave up to 32 rows, four above);
-// otherwise the LDS-tiled MFMA kernel with the cost model's tile.
+// otherwise the LDS-tiled MFMA kernel.
 static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg) {
   if (cfg && cfg->variant > 0 && cfg->variant <= gemm_variant_count()) return cfg->variant;
   if (w.layout == 0) {
     const int kind = batch <= 32 ? 0 : 1;
     if (batch <= 4) return 1;
     if (batch <= mfma_rf_max_batch() && mfma_rf_supported(w, kind)) return rf_first_variant() + kind;
+    return batch <= kGemvMaxBatch ? 1 : 2 + default_tile(w, batch);
   }
-  return batch <= kGemvMaxBatch ? 1 : 2 + default_tile(w, batch);
+  // stored [K][N]: the GEMV for one row; the 32 x 256 MFMA tile (with K split
+  // for two blocks per CU) up to 32 rows; then the cost model
+  if (batch == 1) return 1;
+  if (batch <= 32) return 2 + mfma2_small_tile_first() + 1;
+  return 2 + default_tile(w, batch);
 }
 
 // Workspace floats for partial sums of the kernel this call resolves to (the

@@ -382,13 +382,17 @@ void mfma2_tile_dims(int tile, int* bm, int* bn) {
   *bn = kTiles2[tile].bn;
 }
 
-// K slices so that the grid covers the chip at least once (capped; each slice >= 8 steps)
+// K slices so that the grid covers the chip at least once; twice for the
+// palette formats at small batch, whose data loads wait on flag words and
+// need a second resident block per CU to hide that, while the partial sums
+// stay small next to the weights (capped; each slice >= 8 steps)
 int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint) {
   const Tile2 t = kTiles2[tile];
   const int64_t blocks = ((int64_t)w.n + t.bn - 1) / t.bn * ((batch + t.bm - 1) / t.bm);
+  const int64_t target = fmt_is_pal(w.fmt) && batch <= 64 ? 512 : 256;
   int s = split_hint > 0 ? split_hint : 1;
   if (split_hint <= 0)
-    while (blocks * s < 256 && (int64_t)w.k / (64 * (s * 2)) >= 8) s *= 2;
+    while (blocks * s < target && (int64_t)w.k / (64 * (s * 2)) >= 8) s *= 2;
   const int64_t steps = ((int64_t)w.k + 63) / 64;
   if (s > steps) s = (int)steps;
   return s;
