@@ -111,6 +111,13 @@ def cpu_baseline(w_np, x_np, min_seconds: float = 10.0):
                       f"{dt:.1f} s"}
 
 
+def hold_gpu(torch, launches: int) -> None:
+    """Keep the GPU busy (a spin kernel, about 40 us per launch to come) while
+    the host queues a timed burst, so the burst measures the kernels and not
+    the host's call rate."""
+    torch.cuda._sleep(int(launches * 1e5))
+
+
 def extras(uw, synth, torch, dev, iters: int = 12, copies: int = 4):
     """Short measurements of the larger-batch rows: fused gate+up (2 x
     14336x4096) and the transposed down projection (stored [14336][4096]).
@@ -138,6 +145,7 @@ def extras(uw, synth, torch, dev, iters: int = 12, copies: int = 4):
             for c in range(copies):
                 uw.uw_matmul_reconstruct_grouped(sets[c], p, x, y, ws)
             s, e = ev(), ev()
+            hold_gpu(torch, iters)
             s.record()
             for it in range(iters):
                 uw.uw_matmul_reconstruct_grouped(sets[it % copies], p, x, y, ws)
@@ -178,6 +186,7 @@ def extras(uw, synth, torch, dev, iters: int = 12, copies: int = 4):
             for c in range(copies):
                 uw.uw_matmul_reconstruct(ms[c], p, x, y, ws)
             s, e = ev(), ev()
+            hold_gpu(torch, iters)
             s.record()
             for it in range(iters):
                 uw.uw_matmul_reconstruct(ms[it % copies], p, x, y, ws)
@@ -408,6 +417,7 @@ def main() -> int:
         two kernels holds the next dispatch back by about 5 us, so events
         around single launches would overstate these short kernels."""
         d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        hold_gpu(torch, n)
         d0.record(stream)
         for i in range(n):
             run_stage(st, mats[(i0 + i) % len(mats)])
