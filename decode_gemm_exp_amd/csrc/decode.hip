@@ -339,15 +339,27 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
     exn[u] = make_uint4(0, 0, 0, 0);
   }
 
+  // Copy-out step u of a lane serves the same owner lane in every round, so
+  // the owner's verbatim flags, first rank and group count are fetched once
+  // here; each round then finds its flags and ranks without cross-lane
+  // shuffles.  Owners past the last segment have no groups.
+  uint32_t obl[STEPS], obh[STEPS], ork[STEPS], ong[STEPS];
+#pragma unroll
+  for (int u = 0; u < STEPS; ++u) {
+    const int L = (int)(((uint32_t)u * 1024u + (uint32_t)lane * 16u) / per_owner);
+    obl[u] = (uint32_t)__shfl((int)(uint32_t)segbits, L, 64);
+    obh[u] = (uint32_t)__shfl((int)(uint32_t)(segbits >> 32), L, 64);
+    ork[u] = (uint32_t)__shfl((int)rank_seg, L, 64);
+    ong[u] = (uint32_t)__shfl((int)seg_ng, L, 64);
+  }
+
   for (uint32_t r = 0; r < rounds; ++r) {
     const uint32_t ng = seg_ng > r * CH ? (seg_ng - r * CH < CH ? seg_ng - r * CH : CH) : 0u;
-    const uint32_t ng_next = seg_ng > (r + 1) * CH ? 1u : 0u;   // round r+1 has a group (CH == 1)
     const bool pair_first = MODE == kDecodeFull && CH == 1 && (r & 1u) == 0;
     const bool pair_second = MODE == kDecodeFull && CH == 1 && (r & 1u) == 1;
     const bool defer_first = MODE == kDecodeExponent && CH == 1 && (r & 1u) == 0;
     uint32_t has_next = 0;   // bit u: this step's owner has a group in round r+1
     const uint32_t vbits = (uint32_t)(segbits >> (r * CH)) & ((1u << CH) - 1u) & ((1u << ng) - 1u);
-    const uint32_t rank0 = rank_seg + (uint32_t)__popcll(segbits & ((1ull << (r * CH)) - 1ull));
     const uint32_t ncoded = ng - (uint32_t)__popc(vbits);
     coded_groups += ncoded;
     const uint32_t ftarget = ncoded * 8;
@@ -360,34 +372,30 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
     for (int u = 0; u < STEPS; ++u) {
       const uint32_t e = (uint32_t)u * 1024u + (uint32_t)lane * 16u;
       const uint32_t L = e / per_owner, o = e % per_owner, j = o >> 6, w16 = o & 63u;
-      const uint32_t fl = (uint32_t)__shfl((int)vbits, (int)L, 64);
-      const uint32_t rk = (uint32_t)__shfl((int)rank0, (int)L, 64);
-      const uint32_t gn = (uint32_t)__shfl((int)ng, (int)L, 64);
+      const uint32_t gi = r * CH + j;   // group index in the owner's segment
+      const uint64_t ob = ((uint64_t)obh[u] << 32) | obl[u];
+      const bool ok = gi < ong[u];
+      const bool verb = ok && ((ob >> gi) & 1u);
+      const uint32_t below = (uint32_t)(ob >> (r * CH)) & ((1u << j) - 1u);   // the round's verbatim groups before j
       const uint64_t sL = sbase + L;
-      const bool ok = sL < a.segments && j < gn;
-      const bool verb = ok && ((fl >> j) & 1u);
-      const uint32_t below = fl & ((1u << j) - 1u);
-      el[u] = (sL * SG + (uint64_t)r * CH + j) * 64u + w16;
+      el[u] = (sL * SG + gi) * 64u + w16;
       info[u] = (ok ? 0x80000000u : 0u) | (verb ? 0x40000000u : 0u) | (L << 8) |
                 (8u * (j - (uint32_t)__popc(below)) + (w16 >> 3));
       ev[u] = make_uint4(0, 0, 0, 0);
       sv[u] = make_uint4(0, 0, 0, 0);
-      if (MODE != kDecodeNibble && verb)
-        ev[u] = *reinterpret_cast<const uint4*>(vexp + (uint64_t)(rk + (uint32_t)__popc(below)) * 64u + w16);
+      if (MODE != kDecodeNibble && verb) {
+        const uint32_t rank = ork[u] + (uint32_t)__popcll(ob & ((1ull << gi) - 1ull));
+        ev[u] = *reinterpret_cast<const uint4*>(vexp + (uint64_t)rank * 64u + w16);
+      }
       if (pair_second) {
         sv[u] = svn[u];
       } else if (MODE == kDecodeFull && ok) {
         sv[u] = *reinterpret_cast<const uint4*>(smp + el[u]);
       }
-      if (defer_first) {
-        const uint32_t gnn = (uint32_t)__shfl((int)ng_next, (int)L, 64);
-        has_next |= (sL < a.segments && gnn > 0) ? (1u << u) : 0u;
-      }
-      if (pair_first) {
-        const uint32_t gnn = (uint32_t)__shfl((int)ng_next, (int)L, 64);
-        svn[u] = (sL < a.segments && gnn > 0) ? *reinterpret_cast<const uint4*>(smp + el[u] + 64u)
-                                              : make_uint4(0, 0, 0, 0);
-      }
+      const bool next = (r + 1) * CH < ong[u];   // the owner has a group in round r+1 (CH == 1)
+      if (defer_first) has_next |= next ? (1u << u) : 0u;
+      if (pair_first)
+        svn[u] = next ? *reinterpret_cast<const uint4*>(smp + el[u] + 64u) : make_uint4(0, 0, 0, 0);
     }
 
     // ---- decode every coded group of the round (LDS only) ----
