@@ -205,7 +205,14 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
       bool v;
       const uint64_t el = chunk_el(i, k0, v);
       load_raw<FMT>(w, el, v, fw_a[i], rk_a[i], wr[i]);
-      wval[i] = v;
+      // zeroed when rebuilt: only [K][N] chunks past K.  Chunks past N only
+      // feed output columns that are never stored, and a stored [N][K] row is
+      // a multiple of 64 long, so none of its steps that are read reach past K
+      if constexpr (LAYOUT == 0) {
+        wval[i] = true;
+      } else {
+        wval[i] = k0 + (int64_t)((tid + i * 256) / (BN / 16)) < ke;
+      }
       wverb[i] = fmt_is_pal(FMT) && v && group_verbatim(fw_a[i], el >> 6);
       whi[i] = (el & 16) != 0;
     }
