@@ -535,14 +535,14 @@ bool gemm_variant_supported(int v, int layout) { return v < rf_first_variant() |
 
 // Default kernel by batch (measured on the 8B and 70B MLP shapes): the VALU
 // GEMV while the batch is tiny; for stored [N][K] the register-fed MFMA
-// kernel up to 64 rows (two row tiles per wave up to 32 rows, four above);
-// otherwise the LDS-tiled MFMA kernel.
+// kernel (two row tiles per wave) up to 32 rows and the 64 x 128 LDS tile up
+// to 64; otherwise the LDS-tiled MFMA kernel.
 static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg) {
   if (cfg && cfg->variant > 0 && cfg->variant <= gemm_variant_count()) return cfg->variant;
   if (w.layout == 0) {
-    const int kind = batch <= 32 ? 0 : 1;
     if (batch <= 4) return 1;
-    if (batch <= mfma_rf_max_batch() && mfma_rf_supported(w, kind)) return rf_first_variant() + kind;
+    if (batch <= 32 && mfma_rf_supported(w, 0)) return rf_first_variant();
+    if (batch <= 64) return 2;   // the 64 x 128 tile
     return batch <= kGemvMaxBatch ? 1 : 2 + default_tile(w, batch);
   }
   // stored [K][N]: the GEMV for one row; the 32 x 256 MFMA tile (with K split

@@ -138,7 +138,7 @@ __device__ __forceinline__ bf16x8 a_frag(const WeightView& w, const Raw32& r, ui
   return __builtin_bit_cast(bf16x8, o);
 }
 
-template <int FMT, int R, int NBG>
+template <int FMT, int R, int NBG, bool XS = (NBG >= 2)>
 __global__ __launch_bounds__(256) void k_mfma_rf(WeightView w, const uint16_t* __restrict__ x, int B,
                                                  float* __restrict__ y, int64_t ldy, int64_t col0, int64_t kslice,
                                                  float* __restrict__ part, uint32_t fwords,
@@ -207,6 +207,24 @@ __global__ __launch_bounds__(256) void k_mfma_rf(WeightView w, const uint16_t* _
       }
     }
   };
+  // x fragments of window j (the window's MFMA operands, from the packed copy when there is one)
+  auto load_x = [&](int j, uint4 (&xr)[NBG][4]) __attribute__((always_inline)) {
+    const int64_t k0 = win_k(j);
+    const bool kv = (j < mine) & (k0 < ke);
+    const bool h1 = k0 + 64 < ke;
+    const int64_t kx = kv ? k0 : 0;
+    const uint64_t wabs = (uint64_t)(kx / kWin);   // window index along K (packed x)
+#pragma unroll
+    for (int q = 0; q < NBG; ++q)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int64_t kk = (kv & (h1 | (kx_off<FMT>(m, g) < 64))) ? kx + kx_off<FMT>(m, g) : 0;
+        const uint4* pa = xp ? xp + ((wabs * NBG + q) * 4 + m) * 64 + lane
+                             : reinterpret_cast<const uint4*>(x + xrow[q] + kk);
+        const uint4 v = *pa;
+        xr[q][m] = v;
+      }
+  };
   // okbits: bit 2t = row tile t's first 64 weights exist, bit 2t+1 = its second 64
   auto load_win = [&](int j, Raw32 (&r)[R], uint4 (&xr)[NBG][4], const uint32_t (&fw)[R], const uint32_t (&fh)[R],
                       const uint32_t (&rw)[R], uint32_t& vbits, uint32_t& okbits) __attribute__((always_inline)) {
@@ -226,18 +244,7 @@ __global__ __launch_bounds__(256) void k_mfma_rf(WeightView w, const uint16_t* _
       okbits |= (v ? 1u : 0u) << (2 * t);
       okbits |= (v & h1 ? 1u : 0u) << (2 * t + 1);
     }
-    const int64_t kx = kv ? k0 : 0;
-    const uint64_t wabs = (uint64_t)(kx / kWin);   // window index along K (packed x)
-#pragma unroll
-    for (int q = 0; q < NBG; ++q)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int64_t kk = (kv & (h1 | (kx_off<FMT>(m, g) < 64))) ? kx + kx_off<FMT>(m, g) : 0;
-        const uint4* pa = xp ? xp + ((wabs * NBG + q) * 4 + m) * 64 + lane
-                             : reinterpret_cast<const uint4*>(x + xrow[q] + kk);
-        const uint4 v = *pa;
-        xr[q][m] = v;
-      }
+    if constexpr (!XS) load_x(j, xr);
   };
 
   f32x4 acc[R][NBG];
@@ -246,6 +253,10 @@ __global__ __launch_bounds__(256) void k_mfma_rf(WeightView w, const uint16_t* _
 #pragma unroll
     for (int q = 0; q < NBG; ++q) acc[t][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  auto xbuf_b = [](uint4 (&a)[NBG][4], auto& b) __attribute__((always_inline)) -> uint4 (&)[NBG][4] {
+    if constexpr (XS) return a;
+    else return b;
+  };
   auto compute = [&](const Raw32 (&r)[R], const uint4 (&xr)[NBG][4], uint32_t vbits,
                      uint32_t okbits) __attribute__((always_inline)) {
 #pragma unroll
@@ -265,8 +276,11 @@ __global__ __launch_bounds__(256) void k_mfma_rf(WeightView w, const uint16_t* _
   // two windows in registers: the loads of window j+2 (and the flag words of
   // j+4) are issued as soon as window j has been consumed.  Windows past the
   // range load index 0 and add zeros, so the loop has no tail.
+  // With XS (two or more batch groups) x is single buffered, one window
+  // ahead: it comes from L2, and a second buffer would cost the registers
+  // that keep two windows of weights in flight.
   Raw32 rA[R], rB[R];
-  uint4 xA[NBG][4], xB[NBG][4];
+  uint4 xA[NBG][4], xB[XS ? 1 : NBG][4];
   uint32_t fA[R], hA[R], gA[R], fB[R], hB[R], gB[R];
   uint32_t vA, oA, vB, oB;
 #pragma unroll
@@ -276,10 +290,11 @@ __global__ __launch_bounds__(256) void k_mfma_rf(WeightView w, const uint16_t* _
   load_flags(0, fA, hA, gA);
   load_flags(1, fB, hB, gB);
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (XS) load_x(0, xA);
   load_win(0, rA, xA, fA, hA, gA, vA, oA);
   load_flags(2, fA, hA, gA);
   __builtin_amdgcn_sched_barrier(0);
-  load_win(1, rB, xB, fB, hB, gB, vB, oB);
+  load_win(1, rB, xbuf_b(xA, xB), fB, hB, gB, vB, oB);
   load_flags(3, fB, hB, gB);
   __builtin_amdgcn_sched_barrier(0);
   // (the scheduling barriers keep each buffer's reloads behind the MFMAs that
@@ -291,12 +306,14 @@ __global__ __launch_bounds__(256) void k_mfma_rf(WeightView w, const uint16_t* _
   do {
     compute(rA, xA, vA, oA);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (XS) load_x(j + 1, xA);
     load_win(j + 2, rA, xA, fA, hA, gA, vA, oA);
     load_flags(j + 4, fA, hA, gA);
     __builtin_amdgcn_sched_barrier(0);
-    compute(rB, xB, vB, oB);
+    compute(rB, xbuf_b(xA, xB), vB, oB);
     __builtin_amdgcn_sched_barrier(0);
-    load_win(j + 3, rB, xB, fB, hB, gB, vB, oB);
+    if constexpr (XS) load_x(j + 2, xA);
+    load_win(j + 3, rB, xbuf_b(xA, xB), fB, hB, gB, vB, oB);
     load_flags(j + 5, fB, hB, gB);
     __builtin_amdgcn_sched_barrier(0);
     j += 2;
