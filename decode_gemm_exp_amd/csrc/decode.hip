@@ -249,7 +249,7 @@ template <int CH>
 constexpr uint32_t staged_stride() { return 8u * CH + 1u; }
 constexpr uint32_t kStagedMaxThreads = 512;
 
-template <int MODE, int CH>
+template <int MODE, int CH, bool RUN>
 __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs a) {
   constexpr uint32_t kStagedStride = staged_stride<CH>();
   constexpr uint32_t kStagedStage = 64 * kStagedStride;
@@ -387,15 +387,15 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
         const uint32_t rank = ork[u] + (uint32_t)__popcll(ob & ((1ull << gi) - 1ull));
         ev[u] = *reinterpret_cast<const uint4*>(vexp + (uint64_t)rank * 64u + w16);
       }
+      // sign+mantissa loads read index 0 for steps that store nothing
       if (pair_second) {
         sv[u] = svn[u];
-      } else if (MODE == kDecodeFull && ok) {
-        sv[u] = *reinterpret_cast<const uint4*>(smp + el[u]);
+      } else if (MODE == kDecodeFull) {
+        sv[u] = *reinterpret_cast<const uint4*>(smp + (ok ? el[u] : 0u));
       }
       const bool next = (r + 1) * CH < ong[u];   // the owner has a group in round r+1 (CH == 1)
       if (defer_first) has_next |= next ? (1u << u) : 0u;
-      if (pair_first)
-        svn[u] = next ? *reinterpret_cast<const uint4*>(smp + el[u] + 64u) : make_uint4(0, 0, 0, 0);
+      if (pair_first) svn[u] = *reinterpret_cast<const uint4*>(smp + (next ? el[u] + 64u : 0u));
     }
 
     // ---- decode every coded group of the round (LDS only) ----
@@ -432,38 +432,42 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
     __builtin_amdgcn_wave_barrier();
 
     // ---- copy-out ----
+    // straight-line data path (the stage words are read for every step: the
+    // slot stays inside the owner's stage row); only the stores are predicated
 #pragma unroll
     for (int u = 0; u < STEPS; ++u) {
-      if (!(info[u] & 0x80000000u)) continue;
-      uint4 ex = ev[u];
-      if (!(info[u] & 0x40000000u)) {
-        const uint32_t L = (info[u] >> 8) & 63u, slot = info[u] & 0xFFu;
-        const uint32_t n0 = stage[L * kStagedStride + slot], n1 = stage[L * kStagedStride + slot + 1];
-        if (MODE == kDecodeNibble) {
-          ex = make_uint4(n0, n1, 0, 0);
-        } else {
-          ex = pal16_any(n0, n1, pal);
-        }
+      const bool ok = (info[u] >> 31) & 1u, verb = (info[u] >> 30) & 1u;
+      const uint32_t L = (info[u] >> 8) & 63u, slot = info[u] & 0xFFu;
+      const uint32_t n0 = stage[L * kStagedStride + slot], n1 = stage[L * kStagedStride + slot + 1];
+      uint4 ex;
+      if constexpr (MODE == kDecodeNibble) {
+        ex = make_uint4(verb ? 0u : n0, verb ? 0u : n1, 0u, 0u);   // verbatim groups: slot 0
+      } else {
+        const uint4 pe = pal16<RUN>(n0, n1, pal);
+        ex.x = verb ? ev[u].x : pe.x;
+        ex.y = verb ? ev[u].y : pe.y;
+        ex.z = verb ? ev[u].z : pe.z;
+        ex.w = verb ? ev[u].w : pe.w;
       }
-      if (MODE == kDecodeNibble) {
-        *reinterpret_cast<uint2*>((uint8_t*)a.out + el[u] / 2) = make_uint2(ex.x, ex.y);
-      } else if (MODE == kDecodeExponent) {
+      if constexpr (MODE == kDecodeNibble) {
+        if (ok) *reinterpret_cast<uint2*>((uint8_t*)a.out + el[u] / 2) = make_uint2(ex.x, ex.y);
+      } else if constexpr (MODE == kDecodeExponent) {
         if (CH == 1 && ((deferred >> u) & 1u))   // the other half of this line, from the previous round
           *reinterpret_cast<uint4*>((uint8_t*)a.out + el[u] - 64u) = exn[u];
-        if (defer_first && ((has_next >> u) & 1u)) {
-          exn[u] = ex;
-        } else {
-          *reinterpret_cast<uint4*>((uint8_t*)a.out + el[u]) = ex;
-        }
+        const bool hold = defer_first && ((has_next >> u) & 1u);
+        if (ok && !hold) *reinterpret_cast<uint4*>((uint8_t*)a.out + el[u]) = ex;
+        exn[u] = ex;   // used next round only when held
       } else {
         uint4 o0, o1;
         rebuild4(sv[u].x, ex.x, o0.x, o0.y);
         rebuild4(sv[u].y, ex.y, o0.z, o0.w);
         rebuild4(sv[u].z, ex.z, o1.x, o1.y);
         rebuild4(sv[u].w, ex.w, o1.z, o1.w);
-        uint4* dst = reinterpret_cast<uint4*>((uint16_t*)a.out + el[u]);
-        dst[0] = o0;
-        dst[1] = o1;
+        if (ok) {
+          uint4* dst = reinterpret_cast<uint4*>((uint16_t*)a.out + el[u]);
+          dst[0] = o0;
+          dst[1] = o1;
+        }
       }
     }
     deferred = defer_first ? has_next : 0u;
@@ -517,20 +521,30 @@ void staged_shape(const DecodeArgs& a, uint32_t* wpb_out, uint32_t* resident_out
   *resident_out = best_res;
 }
 
-template <int MODE, int CH>
-hipError_t launch_staged(const DecodeArgs& a, uint32_t wpb, hipStream_t s) {
+template <int MODE, int CH, bool RUN>
+hipError_t launch_staged_pal(const DecodeArgs& a, uint32_t wpb, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_decode_staged<MODE, CH>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_decode_staged<MODE, CH, RUN>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const uint64_t threads = 64ull * wpb;
   const uint64_t blocks = (a.segments + threads - 1) / threads;
-  hipLaunchKernelGGL((k_decode_staged<MODE, CH>), dim3((uint32_t)blocks), dim3((uint32_t)threads),
+  hipLaunchKernelGGL((k_decode_staged<MODE, CH, RUN>), dim3((uint32_t)blocks), dim3((uint32_t)threads),
                      wpb * staged_wave_bytes<CH>(a), s, a);
   return hipGetLastError();
+}
+
+// the palette kind is a template parameter (a run of exponents is a bytewise
+// add); the transcode never looks the palette up
+template <int MODE, int CH>
+hipError_t launch_staged(const DecodeArgs& a, uint32_t wpb, hipStream_t s) {
+  if constexpr (MODE != kDecodeNibble) {
+    if (a.pal.run) return launch_staged_pal<MODE, CH, true>(a, wpb, s);
+  }
+  return launch_staged_pal<MODE, CH, false>(a, wpb, s);
 }
 
 template <int MODE>
