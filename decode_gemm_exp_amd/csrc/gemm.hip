@@ -475,35 +475,6 @@ int nk_pipe_u(const WeightView& w, int nb) {
   return 0;
 }
 
-// MFMA tile by a small cost model: block waves over the CUs times the work
-// of one block, at each tile's relative per-block throughput (measured on
-// the 70B MLP shapes at batch 1024), plus the split-K partial sums written
-// and read back.  Tiles more than twice as tall as the batch are skipped.
-int default_tile(const WeightView& w, int64_t batch) {
-  static const double kTileEff[] = {0.55, 0.70, 0.80, 0.85, 1.0, 0.35, 0.45};
-  const double cu_rate = 4.6e12;   // flop/s of one CU at the best tile's throughput
-  const double hbm = 5e12;         // bytes/s for the partial sums
-  const int cus = device_cus();
-  int best = 0;
-  double best_t = 0;
-  for (int t = 0; t < mfma2_tile_count(); ++t) {
-    int bm, bn;
-    mfma2_tile_dims(t, &bm, &bn);
-    if (bm > 2 * batch && t > 0) continue;
-    const int slices = mfma2_slices(w, batch, t, 0);
-    const double tiles = (double)((w.n + bn - 1) / bn) * (double)((batch + bm - 1) / bm);
-    const double waves = std::ceil(tiles * slices / cus);
-    const double kper = std::ceil((double)w.k / slices);
-    double est = waves * 2.0 * bm * bn * kper / (kTileEff[t < 7 ? t : 6] * cu_rate);
-    if (slices > 1) est += (2.0 * slices + 1.0) * (double)batch * (double)w.n * 4.0 / hbm;
-    if (t == 0 || est < best_t) {
-      best = t;
-      best_t = est;
-    }
-  }
-  return best;
-}
-
 // K slices of the KN GEMV: about two 8-wave blocks per CU over the grid,
 // each wave with at least two pipeline steps of row pairs.
 int kn_slices(const WeightView& w, int nb, const uw_kernel_cfg* cfg) {
@@ -533,23 +504,28 @@ int rf_first_variant() { return 2 + mfma2_tile_count(); }
 int gemm_variant_count() { return 1 + mfma2_tile_count() + mfma_rf_kinds(); }
 bool gemm_variant_supported(int v, int layout) { return v < rf_first_variant() || layout == 0; }
 
-// Default kernel by batch (measured on the 8B and 70B MLP shapes): the VALU
-// GEMV while the batch is tiny; for stored [N][K] the register-fed MFMA
-// kernel (two row tiles per wave) up to 32 rows and the 64 x 128 LDS tile up
-// to 64; otherwise the LDS-tiled MFMA kernel.
+// Default kernel by batch, from sweeps over the 8B and 70B MLP shapes (every
+// variant, both layouts, palette-direct and BF16 weights):
+//   stored [N][K]: VALU GEMV up to 4 rows, register-fed MFMA (two row tiles
+//     per wave) up to 32, then LDS tiles 64x128 up to 64, 128x128 up to 512,
+//     256x256 beyond;
+//   stored [K][N]: VALU GEMV for one row, then LDS tiles 32x256 up to 32,
+//     64x128 up to 64, 128x256 up to 192, 256x256 beyond.
+// Tile indices are those of gemm_mfma.hip (variant = 2 + index).
 static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg) {
   if (cfg && cfg->variant > 0 && cfg->variant <= gemm_variant_count()) return cfg->variant;
   if (w.layout == 0) {
     if (batch <= 4) return 1;
     if (batch <= 32 && mfma_rf_supported(w, 0)) return rf_first_variant();
-    if (batch <= 64) return 2;   // the 64 x 128 tile
-    return batch <= kGemvMaxBatch ? 1 : 2 + default_tile(w, batch);
+    if (batch <= 64) return 2 + 0;
+    if (batch <= 512) return 2 + 1;
+    return 2 + 4;
   }
-  // stored [K][N]: the GEMV for one row; the 32 x 256 MFMA tile (with K split
-  // for two blocks per CU) up to 32 rows; then the cost model
   if (batch == 1) return 1;
-  if (batch <= 32) return 2 + mfma2_small_tile_first() + 1;
-  return 2 + default_tile(w, batch);
+  if (batch <= 32) return 2 + 6;
+  if (batch <= 64) return 2 + 0;
+  if (batch <= 192) return 2 + 2;
+  return 2 + 4;
 }
 
 // Workspace floats for partial sums of the kernel this call resolves to (the
