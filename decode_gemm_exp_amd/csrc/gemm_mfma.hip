@@ -138,6 +138,7 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
   constexpr int WC = BN * 4 / 256;     // 16-weight chunks per thread per step
   constexpr int LDW = w_ld<LAYOUT, BN>();
   constexpr int XS = BM * kLDK, WS = w_tile_elems<LAYOUT, BN>();
+  constexpr int kValuPerMfma = FMT == kFmtBf16 ? 1 : 4;
   static_assert(TM >= 1 && TN >= 1 && XC >= 1 && WC >= 1, "tile too small");
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
@@ -312,6 +313,13 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
       store_step(xs_n, ws_n, p);
       load_step(k2, p);
       if constexpr (fmt_is_pal(FMT)) load_flags(k3, p);
+      // ask the scheduler to alternate one MFMA with a few VALU operations of
+      // the rebuild, so the vector ALU works while the matrix core runs
+#pragma unroll
+      for (int q = 0; q < TM * TN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // VALU
+      }
       __builtin_amdgcn_sched_barrier(0);
     };
     read_frags(xs_c, ws_c, 0, fa0, fb0);
