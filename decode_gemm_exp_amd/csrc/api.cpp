@@ -179,6 +179,9 @@ uw_status split_streams(int decode_cus, SplitStreams* out) {
   int dev = 0;
   UW_HIP(hipGetDevice(&dev));
   std::lock_guard<std::mutex> lk(g_split_mu);
+  int total_cus = 0;
+  UW_HIP(hipDeviceGetAttribute(&total_cus, hipDeviceAttributeMultiprocessorCount, dev));
+  if (decode_cus > total_cus) decode_cus = total_cus;
   auto it = g_split.find({dev, decode_cus});
   if (it != g_split.end()) {
     *out = it->second;
@@ -187,13 +190,19 @@ uw_status split_streams(int decode_cus, SplitStreams* out) {
   hipDeviceProp_t prop;
   UW_HIP(hipGetDeviceProperties(&prop, dev));
   const int total = prop.multiProcessorCount;
-  if (decode_cus <= 0 || decode_cus >= total) return UW_ERR_INVALID;
+  if (decode_cus <= 0) return UW_ERR_INVALID;
   SplitStreams ss;
-  std::vector<uint32_t> md = cu_mask(total, 0, decode_cus);
-  std::vector<uint32_t> mg = cu_mask(total, decode_cus, total - decode_cus);
-  UW_HIP(hipExtStreamCreateWithCUMask(&ss.dec, (uint32_t)md.size(), md.data()));
-  UW_HIP(hipExtStreamCreateWithCUMask(&ss.gemm, (uint32_t)mg.size(), mg.data()));
-  g_split[{dev, decode_cus}] = ss;
+  if (decode_cus >= total) {
+    // no mask: the two kernels share every CU, the hardware interleaves their blocks
+    UW_HIP(hipStreamCreateWithFlags(&ss.dec, hipStreamNonBlocking));
+    UW_HIP(hipStreamCreateWithFlags(&ss.gemm, hipStreamNonBlocking));
+  } else {
+    std::vector<uint32_t> md = cu_mask(total, 0, decode_cus);
+    std::vector<uint32_t> mg = cu_mask(total, decode_cus, total - decode_cus);
+    UW_HIP(hipExtStreamCreateWithCUMask(&ss.dec, (uint32_t)md.size(), md.data()));
+    UW_HIP(hipExtStreamCreateWithCUMask(&ss.gemm, (uint32_t)mg.size(), mg.data()));
+  }
+  g_split[{dev, decode_cus >= total ? total : decode_cus}] = ss;
   *out = ss;
   return UW_OK;
 }

@@ -182,6 +182,25 @@ extern "C" uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj
             improved = true;
           }
         }
+        // stage 1b: the preprocessing pipelines again, with preprocessing of
+        // the next matrix running beside the GEMM on every CU
+        for (const Choice& c0 : cands) {
+          if (result != UW_OK) break;
+          if (c0.pipeline == UW_PIPE_PALETTE_DIRECT) continue;
+          Choice c = c0;
+          c.decode_cus = cus;
+          if (c == cfg[(size_t)p]) continue;
+          std::vector<Choice> trial = cfg;
+          trial[(size_t)p] = c;
+          double t = 0;
+          result = measure(trial, &t);
+          if (result != UW_OK) break;
+          if (t < best * 0.99) {
+            best = t;
+            cfg = trial;
+            improved = true;
+          }
+        }
         // stage 2: CUs for the preprocessing kernel of the chosen pipeline
         if (result == UW_OK && cfg[(size_t)p].pipeline != UW_PIPE_PALETTE_DIRECT) {
           for (int frac : {8, 4, 2}) {

@@ -95,7 +95,9 @@ typedef struct {
   int32_t variant;      /* GEMM variant (see uw_variant_count)                */
   int32_t split_k;      /* K slices of the split-K kernels                    */
   int32_t decode_cus;   /* CUs given to the preprocessing kernel when it runs
-                           beside GEMMs (uw_run_sequence); 0 = no split      */
+                           beside GEMMs (uw_run_sequence); 0 = no split, in
+                           order on one stream; >= the device's CU count =
+                           both kernels on every CU, on two unmasked streams */
   int32_t reserved;
 } uw_kernel_cfg;
 

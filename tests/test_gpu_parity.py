@@ -359,7 +359,10 @@ def test_sequence_per_job_split_and_autotune(uw, synth, oracle):
             x = synth.activations(batch, k, seed=70 + i).to(DEV)
             y = torch.full((batch, n), float("nan"), dtype=torch.float32, device=DEV)
             c = choice[i]
-            cfg = {"variant": c["variant"], "decode_cus": [0, 32, 128][i]}
+            # CU splits: none, masked, and (a count past the device's CUs)
+            # both kernels on every CU on two unmasked streams
+            splits = [100000, 32, 128] if batch == 2 else [0, 100000, 32]
+            cfg = {"variant": c["variant"], "decode_cus": splits[i]}
             jobs.append(uw.Job(m, [1, 2, c["pipeline"]][i], x, y, cfg))
             refs.append((bits(x), wnps[i], layout))
         ws = torch.empty(uw.uw_sequence_workspace_size(jobs), dtype=torch.uint8, device=DEV)
