@@ -114,6 +114,17 @@ def test_codec_small_shapes(uw, synth, oracle, shape, layout, sg):
     check_codec(uw, oracle, w, n, k, layout, sg)
 
 
+@pytest.mark.parametrize("shape,sg", [((512, 1024), 4), ((300, 192), 1)])
+def test_codec_run_palette(uw, synth, oracle, shape, sg):
+    """Weights without outliers: the palette is a run of consecutive
+    exponents, which the decoders look up with a bytewise add."""
+    r, c = shape
+    say(f"codec run palette shape={shape} sg={sg}")
+    w = synth.weights(r, c, 0.02, 0.0, 0, seed=5 + r).to(DEV)
+    m, _ = check_codec(uw, oracle, w, r, c, 0, sg)
+    assert _palette_is_run(m)
+
+
 def test_codec_all_bf16_patterns(uw, oracle):
     say("codec all 65536 bf16 patterns")
     rng = np.random.default_rng(1)
