@@ -41,7 +41,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---- GEMV, stored [N][K], K a multiple of 1024 U --------------------------------
-// Blocks of 16 waves, one block per CU, x rows staged once per block in LDS.
+// One block per CU of 8..16 waves (the host picks the count that spreads the
+// rows most evenly over CUs), x rows staged once per block in LDS.
 // A wave owns rows n = wave, wave + nwaves, ... and walks each in steps of
 // 1024 U weights (lane: U chunks of 16 at lane * 16 + u * 1024).  Software
 // pipeline over the wave's steps, two register buffers: while step j is
@@ -55,13 +56,14 @@ __global__ __launch_bounds__(1024) void k_gemv_nk_pipe(WeightView w, const uint1
   {
     const uint32_t pieces = (uint32_t)((uint64_t)B * K / 8);
     const uint4* x4 = reinterpret_cast<const uint4*>(x);
-    for (uint32_t i = threadIdx.x; i < pieces; i += 1024) xs4[i] = x4[i];
+    for (uint32_t i = threadIdx.x; i < pieces; i += blockDim.x) xs4[i] = x4[i];
   }
   __syncthreads();
   const uint16_t* xs = reinterpret_cast<const uint16_t*>(xs4);
   const int lane = threadIdx.x & 63;
-  const uint64_t wave = (uint64_t)blockIdx.x * 16 + wave_uniform(threadIdx.x >> 6);
-  const uint64_t nw = (uint64_t)gridDim.x * 16;
+  const uint32_t wpb = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);   // keeps the wave math scalar
+  const uint64_t wave = (uint64_t)blockIdx.x * wpb + wave_uniform(threadIdx.x >> 6);
+  const uint64_t nw = (uint64_t)gridDim.x * wpb;
   if (wave >= N) return;
   const uint32_t spr = (uint32_t)(K / (1024u * U));         // steps per row
   const uint64_t steps = ((N - 1 - wave) / nw + 1) * spr;
@@ -475,6 +477,32 @@ int nk_pipe_u(const WeightView& w, int nb) {
   return 0;
 }
 
+// Waves per block (8..16) and blocks (at most one per CU) of the pipelined
+// NK GEMV.  Rows go to waves round-robin, so a CU's share is its waves times
+// the most rows any wave gets; the count that makes the largest share
+// smallest wins (ties: more waves).  Example: 14336 rows on 256 CUs take 14
+// waves of 4 rows each, where 16 waves would leave half the CUs 64 rows and
+// the other half 48.
+int nk_pipe_waves(uint64_t n, uint64_t* blocks) {
+  const uint64_t cus = (uint64_t)device_cus();
+  int best = 16;
+  uint64_t best_share = ~0ull;
+  for (int wpb = 16; wpb >= 8; --wpb) {
+    uint64_t g = (n + (uint64_t)wpb - 1) / (uint64_t)wpb;
+    if (g > cus) g = cus;
+    const uint64_t per_wave = (n + g * wpb - 1) / (g * wpb);
+    const uint64_t share = per_wave * (uint64_t)wpb;
+    if (share < best_share) {
+      best_share = share;
+      best = wpb;
+    }
+  }
+  uint64_t g = (n + (uint64_t)best - 1) / (uint64_t)best;
+  if (g > cus) g = cus;
+  *blocks = g;
+  return best;
+}
+
 // K slices of the KN GEMV: about two 8-wave blocks per CU over the grid,
 // each wave with at least two pipeline steps of row pairs.
 int kn_slices(const WeightView& w, int nb, const uw_kernel_cfg* cfg) {
@@ -597,10 +625,9 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
             if (e != hipSuccess) return e;
             lds_set[fi][ni][ui] = true;
           }
-          uint64_t blocks = (uint64_t)device_cus();
-          const uint64_t need = (w.n + 15) / 16;
-          if (blocks > need) blocks = need;
-          hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(1024), lds, s, w, xb, nb, yb, ldy, col0);
+          uint64_t blocks = 0;
+          const int wpb = nk_pipe_waves(w.n, &blocks);
+          hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(64 * wpb), lds, s, w, xb, nb, yb, ldy, col0);
         } else {
           GemvNkFn f = w.fmt == kFmtBf16 ? gemv_nk_any_fn<kFmtBf16>(nb)
                        : w.fmt == kFmtExp ? gemv_nk_any_fn<kFmtExp>(nb)
