@@ -240,6 +240,7 @@ DecodeArgs decode_args(const uw_matrix* m, void* out) {
   a.vflags = m->vflags;
   a.vrank = m->vrank;
   a.vexp = m->vexp;
+  a.vexp_bytes = 64 * m->V;
   a.sm = m->sm;
   a.lut = m->lut;
   pal_words(m->t, &a.pal);

@@ -48,6 +48,42 @@ __device__ __forceinline__ uint4 load_chunk(__amdgpu_buffer_rsrc_t r, uint32_t w
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+// byte-addressed raw buffer accesses: an offset at or past the resource's
+// end reads zero and drops the write
+constexpr uint32_t kPastEnd = 0x7FFF0000u;    // offset past every resource below
+constexpr uint32_t kRecordsMax = 0x40000000u; // resources span at most 1 GiB
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte) {
+  u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// Cache policy of the 16-byte output stores.  NT (non-temporal) streams
+// data written once to HBM: exponent decode on the 8B gate 37 -> 31 us with
+// outputs rotating over more than the 256 MB last-level cache, 33 -> 31 us
+// with one output buffer reused per call.  The full decode's BF16 output is
+// read back by the GEMM right after it; while it fits in half of that cache
+// a reused buffer stays there and cached stores win (49 vs 54 us on the 8B
+// gate), above that NT wins (rotated: 56 -> 52 us).  The transcode's 8-byte
+// stores always stay cached: L2 merges the two halves of each 16-byte piece,
+// as NT stores they took 26 -> 42 us.
+constexpr int kCachePolicyNT = 2;
+constexpr uint64_t kCachedOutputMax = 128ull << 20;
+template <bool NT>
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t byte, uint4 d) {
+  u32x4 v = {d.x, d.y, d.z, d.w};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte, 0, NT ? kCachePolicyNT : 0);
+}
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t byte, uint32_t lo, uint32_t hi) {
+  u32x2 v = {lo, hi};
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)byte, 0, 0);
+}
+// output bytes before weight el: 4-bit slots, exponent bytes or BF16
+template <int MODE>
+__device__ __forceinline__ uint64_t out_bytes(uint64_t el) {
+  return MODE == kDecodeNibble ? el >> 1 : MODE == kDecodeExponent ? el : el * 2u;
+}
+
 __device__ __forceinline__ uint32_t stage_at(uint32_t f, uint32_t L) { return f * 64u + (L ^ (f & 63u)); }
 
 template <int MODE>
@@ -249,13 +285,13 @@ template <int CH>
 constexpr uint32_t staged_stride() { return 8u * CH + 1u; }
 constexpr uint32_t kStagedMaxThreads = 512;
 
-template <int MODE, int CH, bool RUN>
+template <int MODE, int CH, bool RUN, bool NT>
 __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs a) {
   constexpr uint32_t kStagedStride = staged_stride<CH>();
   constexpr uint32_t kStagedStage = 64 * kStagedStride;
   __shared__ __attribute__((aligned(16))) uint32_t lut[1 << kLutBits];
   extern __shared__ uint32_t dyn[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t span = (a.wave_span + 8u + 3u) & ~3u;   // + read slack, 16-byte multiple
   uint32_t* stage = dyn + (uint32_t)wave * (kStagedStage + span);
   uint32_t* sbuf = stage + kStagedStage;
@@ -290,6 +326,20 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
 
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)a.stream, (short)0, (int)(a.stream_words * 4u), 0x00020000);
+  // The copy-out's verbatim-exponent loads and all its stores go through
+  // buffer resources, lanes with nothing to move giving an offset past the
+  // end: no branches, so every path issues the same memory operations and
+  // the waits at the head of the next round count only the loads they need
+  // (behind branches they drained the previous round's stores).  The output
+  // resource starts at the wave's first weight; the host keeps the verbatim
+  // section under kRecordsMax.
+  const uint64_t wel0 = wval ? sbase * SG * 64u : 0u;
+  const uint64_t ob0 = out_bytes<MODE>(wel0), oend = out_bytes<MODE>(a.groups * 64u);
+  const uint64_t oleft = oend > ob0 ? oend - ob0 : 0u;
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+      (uint8_t*)a.out + ob0, (short)0, (int)(oleft < kRecordsMax ? oleft : kRecordsMax), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.vexp, (short)0, (int)(a.vexp_bytes < kRecordsMax ? a.vexp_bytes : kRecordsMax), 0x00020000);
   // stream range of this wave -> LDS (16 bytes per lane per step)
   const uint32_t nwords = we1 - ws0;
   for (uint32_t i = (uint32_t)lane * 4u; i < nwords; i += 256u) {
@@ -319,7 +369,6 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
   };
   uint32_t coded_groups = 0;
   const PalView pal = a.pal;
-  const uint8_t* __restrict__ vexp = a.vexp;
   const uint8_t* __restrict__ smp = a.sm;
   constexpr uint32_t per_owner = CH * 64u;
   constexpr int STEPS = 4 * CH;   // 64 owners * per_owner weights / 1024 per step
@@ -383,9 +432,9 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
                 (8u * (j - (uint32_t)__popc(below)) + (w16 >> 3));
       ev[u] = make_uint4(0, 0, 0, 0);
       sv[u] = make_uint4(0, 0, 0, 0);
-      if (MODE != kDecodeNibble && verb) {
+      if constexpr (MODE != kDecodeNibble) {
         const uint32_t rank = ork[u] + (uint32_t)__popcll(ob & ((1ull << gi) - 1ull));
-        ev[u] = *reinterpret_cast<const uint4*>(vexp + (uint64_t)rank * 64u + w16);
+        ev[u] = buf_load16(rv, verb ? rank * 64u + w16 : kPastEnd);
       }
       // sign+mantissa loads read index 0 for steps that store nothing
       if (pair_second) {
@@ -449,13 +498,14 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
         ex.z = verb ? ev[u].z : pe.z;
         ex.w = verb ? ev[u].w : pe.w;
       }
+      const uint32_t rel = (uint32_t)(el[u] - wel0);   // weights past the wave's first (when ok)
       if constexpr (MODE == kDecodeNibble) {
-        if (ok) *reinterpret_cast<uint2*>((uint8_t*)a.out + el[u] / 2) = make_uint2(ex.x, ex.y);
+        buf_store8(ro, ok ? rel / 2u : kPastEnd, ex.x, ex.y);
       } else if constexpr (MODE == kDecodeExponent) {
-        if (CH == 1 && ((deferred >> u) & 1u))   // the other half of this line, from the previous round
-          *reinterpret_cast<uint4*>((uint8_t*)a.out + el[u] - 64u) = exn[u];
+        if constexpr (CH == 1)   // the other half of this line, from the previous round
+          buf_store16<NT>(ro, ((deferred >> u) & 1u) ? rel - 64u : kPastEnd, exn[u]);
         const bool hold = defer_first && ((has_next >> u) & 1u);
-        if (ok && !hold) *reinterpret_cast<uint4*>((uint8_t*)a.out + el[u]) = ex;
+        buf_store16<NT>(ro, ok && !hold ? rel : kPastEnd, ex);
         exn[u] = ex;   // used next round only when held
       } else {
         uint4 o0, o1;
@@ -463,11 +513,9 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
         rebuild4(sv[u].y, ex.y, o0.z, o0.w);
         rebuild4(sv[u].z, ex.z, o1.x, o1.y);
         rebuild4(sv[u].w, ex.w, o1.z, o1.w);
-        if (ok) {
-          uint4* dst = reinterpret_cast<uint4*>((uint16_t*)a.out + el[u]);
-          dst[0] = o0;
-          dst[1] = o1;
-        }
+        const uint32_t off = ok ? rel * 2u : kPastEnd;
+        buf_store16<NT>(ro, off, o0);
+        buf_store16<NT>(ro, off + 16u, o1);
       }
     }
     deferred = defer_first ? has_next : 0u;
@@ -521,36 +569,44 @@ void staged_shape(const DecodeArgs& a, uint32_t* wpb_out, uint32_t* resident_out
   *resident_out = best_res;
 }
 
-template <int MODE, int CH, bool RUN>
+template <int MODE, int CH, bool RUN, bool NT>
 hipError_t launch_staged_pal(const DecodeArgs& a, uint32_t wpb, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_decode_staged<MODE, CH, RUN>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_decode_staged<MODE, CH, RUN, NT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const uint64_t threads = 64ull * wpb;
   const uint64_t blocks = (a.segments + threads - 1) / threads;
-  hipLaunchKernelGGL((k_decode_staged<MODE, CH, RUN>), dim3((uint32_t)blocks), dim3((uint32_t)threads),
+  hipLaunchKernelGGL((k_decode_staged<MODE, CH, RUN, NT>), dim3((uint32_t)blocks), dim3((uint32_t)threads),
                      wpb * staged_wave_bytes<CH>(a), s, a);
   return hipGetLastError();
 }
 
 // the palette kind is a template parameter (a run of exponents is a bytewise
-// add); the transcode never looks the palette up
+// add); the transcode never looks the palette up.  Store policy: see
+// buf_store16.
 template <int MODE, int CH>
 hipError_t launch_staged(const DecodeArgs& a, uint32_t wpb, hipStream_t s) {
-  if constexpr (MODE != kDecodeNibble) {
-    if (a.pal.run) return launch_staged_pal<MODE, CH, true>(a, wpb, s);
+  if constexpr (MODE == kDecodeNibble) {
+    return launch_staged_pal<MODE, CH, false, false>(a, wpb, s);
+  } else if constexpr (MODE == kDecodeExponent) {
+    return a.pal.run ? launch_staged_pal<MODE, CH, true, true>(a, wpb, s)
+                     : launch_staged_pal<MODE, CH, false, true>(a, wpb, s);
+  } else {
+    const bool nt = a.groups * 64u * 2u > kCachedOutputMax;
+    if (a.pal.run)
+      return nt ? launch_staged_pal<MODE, CH, true, true>(a, wpb, s) : launch_staged_pal<MODE, CH, true, false>(a, wpb, s);
+    return nt ? launch_staged_pal<MODE, CH, false, true>(a, wpb, s) : launch_staged_pal<MODE, CH, false, false>(a, wpb, s);
   }
-  return launch_staged_pal<MODE, CH, false>(a, wpb, s);
 }
 
 template <int MODE>
 hipError_t launch_mode(const DecodeArgs& a, uint32_t blocks, hipStream_t s) {
   const char* force = std::getenv("UW_DECODE_DIRECT");   // selects the fallback kernel (tests)
-  if (a.wave_span > 0 && !(force && force[0] == '1')) {
+  if (a.wave_span > 0 && a.vexp_bytes <= kRecordsMax && !(force && force[0] == '1')) {
     // rounds of two groups where that keeps as many waves resident as rounds of one
     uint32_t w1 = 0, r1 = 0, w2 = 0, r2 = 0;
     staged_shape<1>(a, &w1, &r1);

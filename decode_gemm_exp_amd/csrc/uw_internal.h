@@ -87,6 +87,7 @@ struct DecodeArgs {
   const uint32_t* stream; uint64_t stream_words;   // including slack
   const uint32_t* seg_off;
   const uint32_t* vflags; const uint32_t* vrank; const uint8_t* vexp;
+  uint64_t vexp_bytes;                              // 64 x verbatim groups
   const uint8_t* sm;
   const uint32_t* lut;
   PalView pal;
