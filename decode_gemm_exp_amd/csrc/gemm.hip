@@ -53,21 +53,13 @@ __global__ __launch_bounds__(1024) void k_gemv_nk_pipe(WeightView w, const uint1
                                                        float* __restrict__ y, int64_t ldy, int64_t col0) {
   extern __shared__ uint4 xs4[];   // B rows of K bf16
   const uint64_t K = w.k, N = w.n;
-  {
-    const uint32_t pieces = (uint32_t)((uint64_t)B * K / 8);
-    const uint4* x4 = reinterpret_cast<const uint4*>(x);
-    for (uint32_t i = threadIdx.x; i < pieces; i += blockDim.x) xs4[i] = x4[i];
-  }
-  __syncthreads();
   const uint16_t* xs = reinterpret_cast<const uint16_t*>(xs4);
   const int lane = threadIdx.x & 63;
   const uint32_t wpb = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);   // keeps the wave math scalar
   const uint64_t wave = (uint64_t)blockIdx.x * wpb + wave_uniform(threadIdx.x >> 6);
   const uint64_t nw = (uint64_t)gridDim.x * wpb;
-  if (wave >= N) return;
   const uint32_t spr = (uint32_t)(K / (1024u * U));         // steps per row
-  const uint64_t steps = ((N - 1 - wave) / nw + 1) * spr;
-
+  const uint64_t steps = wave < N ? ((N - 1 - wave) / nw + 1) * spr : 0u;
   // cursor of a step: row and part; advanced one step at a time
   struct Cur {
     uint64_t row;
@@ -83,44 +75,80 @@ __global__ __launch_bounds__(1024) void k_gemv_nk_pipe(WeightView w, const uint1
     return c.row * K + (uint64_t)c.part * (1024u * U) + (uint64_t)u * 1024u + (uint64_t)lane * 16u;
   };
 
+  // The steady-state loop issues the same loads on every path, so the
+  // compiler's wait counts are exact and step j's products wait only for
+  // step j's data (loads behind branches made them wait for every load in
+  // flight).  Load cursors stop at the wave's last step; a wave without
+  // rows reads row 0 and leaves after the barrier.  The palette flag and rank words of a
+  // step are the same for all lanes (lanes cover 1024 weights from a
+  // 1024-aligned start, a flag word 2048), so with no global store before
+  // them they are scalar loads and never wait behind the chunks: the row
+  // sums stay in registers (lane i keeps the wave's i-th row, at most 64)
+  // and go to y after the loop.
   ChunkT<16> da[U], db[U];
   uint32_t fa[U], ra[U], fb[U], rb[U];   // flag/rank words of the chunks in da / db
   uint32_t ga[U], gha[U], gb[U], ghb[U]; // flag/rank words of the next steps of each parity
-  Cur cc{wave, 0};                       // step being computed
+  Cur cc{wave < N ? wave : 0u, 0};       // step being computed
   Cur cl = cc;                           // next step whose chunks get loaded
   Cur cf = cc;                           // next step whose flags get loaded
+  uint64_t li = 0, fi = 0;               // step indices of cl and cf
+  auto next = [&](Cur& c, uint64_t& i) {
+    if (i + 1 < steps) {
+      advance(c);
+      ++i;
+    }
+  };
+  auto load_flags = [&](uint32_t* f, uint32_t* r) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if constexpr (fmt_is_pal(FMT)) {
+        const uint64_t fw = (cf.row * K + (uint64_t)cf.part * (1024u * U) + (uint64_t)u * 1024u) >> 11;
+        f[u] = w.vflags[fw];
+        r[u] = w.vrank[fw];
+      } else {
+        f[u] = r[u] = 0;
+      }
+    }
+    next(cf, fi);
+  };
+  // live = false: the prologue's second step of a one-step wave; every lane
+  // reads the matrix's first 16 bytes (one line) instead of a whole step
+  auto load_chunks = [&](ChunkT<16>* d, const uint32_t* f, const uint32_t* r, bool live) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) chunk_load<FMT, 16>(w, live ? el_of(cl, u) : 0u, live ? f[u] : 0u, r[u], d[u]);
+    next(cl, li);
+  };
 
-#pragma unroll
-  for (int u = 0; u < U; ++u) flags_load<FMT>(w, el_of(cf, u), fa[u], ra[u]);
-  advance(cf);
-  if (steps > 1) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) flags_load<FMT>(w, el_of(cf, u), fb[u], rb[u]);
-    advance(cf);
+  // The first two steps' loads go out before x is staged and the block
+  // meets at the barrier, so their latency overlaps both.  Palette chunks
+  // need their flag words for the address: flags first, chunks after the
+  // x copy.
+  load_flags(fa, ra);
+  load_flags(fb, rb);
+  if constexpr (!fmt_is_pal(FMT)) {
+    load_chunks(da, fa, ra, true);
+    load_chunks(db, fb, rb, steps > 1);
   }
-#pragma unroll
-  for (int u = 0; u < U; ++u) chunk_load<FMT, 16>(w, el_of(cl, u), fa[u], ra[u], da[u]);
-  advance(cl);
-  if (steps > 1) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) chunk_load<FMT, 16>(w, el_of(cl, u), fb[u], rb[u], db[u]);
-    advance(cl);
+  {
+    const uint32_t pieces = (uint32_t)((uint64_t)B * K / 8);
+    const uint4* x4 = reinterpret_cast<const uint4*>(x);
+    for (uint32_t i = threadIdx.x; i < pieces; i += blockDim.x) xs4[i] = x4[i];
   }
-  if (steps > 2) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) flags_load<FMT>(w, el_of(cf, u), ga[u], gha[u]);
-    advance(cf);
+  if constexpr (fmt_is_pal(FMT)) {
+    load_chunks(da, fa, ra, true);
+    load_chunks(db, fb, rb, steps > 1);
   }
-  if (steps > 3) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) flags_load<FMT>(w, el_of(cf, u), gb[u], ghb[u]);
-    advance(cf);
-  }
+  load_flags(ga, gha);
+  load_flags(gb, ghb);
+  __syncthreads();
+  if (steps == 0) return;
 
-  float acc[NB];
+  float acc[NB], res[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+  for (int b = 0; b < NB; ++b) acc[b] = res[b] = 0.f;
+  uint32_t rows_done = 0;
 
+  // products of the step at cc; at a row end lane rows_done keeps the sums
   auto compute = [&](const ChunkT<16>* d, const uint32_t* f) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -145,46 +173,51 @@ __global__ __launch_bounds__(1024) void k_gemv_nk_pipe(WeightView w, const uint1
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const float t = wave_sum(acc[b]);
-        if (b < B && lane == 0) y[(uint64_t)b * ldy + col0 + cc.row] = t;
+        res[b] = (uint32_t)lane == rows_done ? t : res[b];
         acc[b] = 0.f;
       }
+      ++rows_done;
     }
     advance(cc);
   };
 
-  for (uint64_t j = 0; j < steps; j += 2) {
-    compute(da, fa);
-    if (j + 2 < steps) {
+  // steady state: da/db hold steps j, j+1 and the loads of j+2, j+3 all
+  // exist; the last one to three steps run after the loop
+  uint64_t j = 0;
+  for (; j + 3 < steps; j += 2) {
+    compute(da, fa);               // step j
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        fa[u] = ga[u];
-        ra[u] = gha[u];
-        chunk_load<FMT, 16>(w, el_of(cl, u), fa[u], ra[u], da[u]);
-      }
-      advance(cl);
-      if (j + 4 < steps) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) flags_load<FMT>(w, el_of(cf, u), ga[u], gha[u]);
-        advance(cf);
-      }
+    for (int u = 0; u < U; ++u) {
+      fa[u] = ga[u];
+      ra[u] = gha[u];
     }
-    if (j + 1 < steps) {
-      compute(db, fb);
-      if (j + 3 < steps) {
+    load_chunks(da, fa, ra, true);   // step j+2
+    load_flags(ga, gha);             // step j+4 (or the last)
+    compute(db, fb);               // step j+1
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          fb[u] = gb[u];
-          rb[u] = ghb[u];
-          chunk_load<FMT, 16>(w, el_of(cl, u), fb[u], rb[u], db[u]);
-        }
-        advance(cl);
-        if (j + 5 < steps) {
-#pragma unroll
-          for (int u = 0; u < U; ++u) flags_load<FMT>(w, el_of(cf, u), gb[u], ghb[u]);
-          advance(cf);
-        }
-      }
+    for (int u = 0; u < U; ++u) {
+      fb[u] = gb[u];
+      rb[u] = ghb[u];
     }
+    load_chunks(db, fb, rb, true);   // step j+3
+    load_flags(gb, ghb);             // step j+5 (or the last)
+  }
+  compute(da, fa);                 // step j
+  if (j + 2 < steps) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      fa[u] = ga[u];
+      ra[u] = gha[u];
+    }
+    load_chunks(da, fa, ra, true);   // step j+2
+  }
+  if (j + 1 < steps) compute(db, fb);
+  if (j + 2 < steps) compute(da, fa);
+  // row i of this wave is wave + i * nw
+  if ((uint32_t)lane < rows_done) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (b < B) y[(uint64_t)b * ldy + col0 + wave + (uint64_t)lane * nw] = res[b];
   }
 }
 
@@ -612,7 +645,9 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
       float* yb = y + (uint64_t)b0 * (uint64_t)ldy;
       if (w.layout == 0) {
         const int u = nk_pipe_u(w, nb);
-        if (u > 0) {
+        uint64_t pipe_blocks = 0;
+        const int pipe_wpb = nk_pipe_waves(w.n, &pipe_blocks);
+        if (u > 0 && (w.n + pipe_blocks * pipe_wpb - 1) / (pipe_blocks * pipe_wpb) <= 64) {
           GemvNkFn f = w.fmt == kFmtBf16 ? gemv_nk_pipe_fn<kFmtBf16>(nb, u)
                        : w.fmt == kFmtExp ? gemv_nk_pipe_fn<kFmtExp>(nb, u)
                        : w.fmt == kFmtPal ? gemv_nk_pipe_fn<kFmtPal>(nb, u) : gemv_nk_pipe_fn<kFmtPalRun>(nb, u);
@@ -625,9 +660,7 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
             if (e != hipSuccess) return e;
             lds_set[fi][ni][ui] = true;
           }
-          uint64_t blocks = 0;
-          const int wpb = nk_pipe_waves(w.n, &blocks);
-          hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(64 * wpb), lds, s, w, xb, nb, yb, ldy, col0);
+          hipLaunchKernelGGL(f, dim3((unsigned)pipe_blocks), dim3(64 * pipe_wpb), lds, s, w, xb, nb, yb, ldy, col0);
         } else {
           GemvNkFn f = w.fmt == kFmtBf16 ? gemv_nk_any_fn<kFmtBf16>(nb)
                        : w.fmt == kFmtExp ? gemv_nk_any_fn<kFmtExp>(nb)
