@@ -282,16 +282,22 @@ __global__ __launch_bounds__(256) void k_gemv_nk_any(WeightView w, const uint16_
 // pairs wave, wave + 8, ..., U pairs per pipeline step (same two-buffer
 // pipeline as the NK kernel).  The two rows' rebuilt weights are interleaved
 // per column so that one v_dot2 multiplies (w[k][n], w[k+1][n]) with
-// (x[k], x[k+1]).  x pairs are wave-uniform scalar loads.  At the end the 8
-// waves' sums meet in LDS (fixed order) and the block writes one partial row
-// per batch row: part[slice][b][n].
+// (x[k], x[k+1]).  The slice of x is staged in LDS (zero past the slice), so
+// the products never wait on a global load.  At the end the 8 waves' sums
+// meet in LDS (fixed order) and the block writes one partial row per batch
+// row: part[slice][b][n].
 constexpr int kKnWaves = 8;
+constexpr uint32_t kKnXLdsMax = 32u * 1024u;   // staged x bytes per block
 
-template <int FMT, int NB, int U, int OW>
+// SF (palette formats, N a multiple of the block's 64 OW columns): the
+// block's columns of a row lie in one 2048-weight flag word, so the flag and
+// rank words are wave-uniform scalar loads and never wait behind the chunks.
+template <int FMT, int NB, int U, int OW, bool SF>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NB <= 4 ? 4 : 2))) void k_gemv_kn(WeightView w, const uint16_t* __restrict__ x, int B,
                                                  float* __restrict__ part, uint32_t pairs_per_slice) {
   constexpr int BW = 64 * OW;   // columns per block
   __shared__ float red[kKnWaves][BW];
+  extern __shared__ uint32_t xs2[];   // [B][pairs_per_slice] x pairs of the slice
   const int lane = threadIdx.x & 63;
   const uint32_t wave = wave_uniform(threadIdx.x >> 6);
   const uint64_t N = w.n, K = w.k;
@@ -305,28 +311,62 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NB <= 4 ? 4
   const uint32_t steps = (mine + U - 1) / U;
 
   // row of chunk h (0, 1) of pair slot u in step j; rows past the slice are
-  // clamped for addressing and get x = 0
+  // clamped for addressing, their rebuilt weights are zeroed
   auto row_of = [&](uint32_t j, int u, int h) -> uint64_t {
     return kb + 2u * (uint64_t)(wave + kKnWaves * (j * U + (uint32_t)u)) + (uint64_t)h;
   };
   auto el_of = [&](uint64_t k) -> uint64_t { return (k < K ? k : K - 1) * N + ncl; };
+  // loads of steps past the wave's last read its last step again
+  auto clampj = [&](uint32_t j) -> uint32_t { return j < steps ? j : (steps > 0 ? steps - 1 : 0u); };
 
   ChunkT<OW> da[U][2], db[U][2];
   uint32_t fa[U][2], ra[U][2], fb[U][2], rb[U][2];
   uint32_t ga[U][2], gha[U][2], gb[U][2], ghb[U][2];
 
   auto load_flags = [&](uint32_t j, uint32_t (*f)[2], uint32_t (*r)[2]) {
+    j = clampj(j);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) flags_load<FMT>(w, el_of(row_of(j, u, h)), f[u][h], r[u][h]);
+      for (int h = 0; h < 2; ++h) {
+        if constexpr (SF) {
+          const uint64_t k = row_of(j, u, h);
+          const uint64_t fw = ((k < K ? k : K - 1) * N + (uint64_t)blockIdx.x * BW) >> 11;
+          f[u][h] = w.vflags[fw];
+          r[u][h] = w.vrank[fw];
+        } else {
+          flags_load<FMT>(w, el_of(row_of(j, u, h)), f[u][h], r[u][h]);
+        }
+      }
   };
   auto load_chunks = [&](uint32_t j, ChunkT<OW> (*d)[2], uint32_t (*f)[2], uint32_t (*r)[2]) {
+    j = clampj(j);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int h = 0; h < 2; ++h) chunk_load<FMT, OW>(w, el_of(row_of(j, u, h)), f[u][h], r[u][h], d[u][h]);
   };
+
+  // The steady-state loop issues the same loads on every path, so the
+  // compiler's wait counts are exact (as in the NK kernel); the first two
+  // steps' loads go out before x is staged.
+  load_flags(0, fa, ra);
+  load_flags(1, fb, rb);
+  load_chunks(0, da, fa, ra);
+  load_chunks(1, db, fb, rb);
+  {
+    const uint32_t total = (uint32_t)B * pairs_per_slice;
+    for (uint32_t i = threadIdx.x; i < total; i += 512u) {
+      const uint32_t b = i / pairs_per_slice, q = i - b * pairs_per_slice;
+      const uint64_t k = kb + 2u * (uint64_t)q;
+      const uint16_t* xr = x + (uint64_t)b * K;
+      const uint32_t lo = k < ke ? xr[k] : 0u, hi = k + 1 < ke ? xr[k + 1] : 0u;
+      xs2[i] = lo | (hi << 16);
+    }
+  }
+  load_flags(2, ga, gha);
+  load_flags(3, gb, ghb);
+  __syncthreads();
 
   float acc[NB][OW];
 #pragma unroll
@@ -341,16 +381,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NB <= 4 ? 4
       uint32_t o0[OW / 2], o1[OW / 2];
       chunk_rebuild<FMT, OW>(w, d[u][0], el_of(k), f[u][0], o0);
       chunk_rebuild<FMT, OW>(w, d[u][1], el_of(k + 1), f[u][1], o1);
-      uint32_t xv[NB];
+      // a row past the slice (clamped load) contributes nothing, even where
+      // its clamped weights are not finite
+      if (k + 1 >= ke) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        xv[b] = 0;
-        if (b < B) {
-          const uint16_t* xr = x + (uint64_t)b * K;
-          if (k + 1 < ke) xv[b] = *reinterpret_cast<const uint32_t*>(xr + k);
-          else if (k < ke) xv[b] = (uint32_t)xr[k];
+        for (int i = 0; i < OW / 2; ++i) {
+          o1[i] = 0u;
+          if (k >= ke) o0[i] = 0u;
         }
       }
+      const uint32_t q = (uint32_t)((k - kb) / 2u);
+      uint32_t xv[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) xv[b] = (b < B && k < ke) ? xs2[(uint32_t)b * pairs_per_slice + q] : 0u;
 #pragma unroll
       for (int i = 0; i < OW / 2; ++i) {
         const uint32_t plo = __builtin_amdgcn_perm(o1[i], o0[i], 0x05040100u);
@@ -366,40 +409,43 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NB <= 4 ? 4
     }
   };
 
-  if (steps > 0) load_flags(0, fa, ra);
-  if (steps > 1) load_flags(1, fb, rb);
-  if (steps > 0) load_chunks(0, da, fa, ra);
-  if (steps > 1) load_chunks(1, db, fb, rb);
-  if (steps > 2) load_flags(2, ga, gha);
-  if (steps > 3) load_flags(3, gb, ghb);
-  for (uint32_t j = 0; j < steps; j += 2) {
+  uint32_t j = 0;
+  for (; j + 3 < steps; j += 2) {
     compute(j, da, fa);
-    if (j + 2 < steps) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          fa[u][h] = ga[u][h];
-          ra[u][h] = gha[u][h];
-        }
-      load_chunks(j + 2, da, fa, ra);
-      if (j + 4 < steps) load_flags(j + 4, ga, gha);
-    }
-    if (j + 1 < steps) {
-      compute(j + 1, db, fb);
-      if (j + 3 < steps) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            fb[u][h] = gb[u][h];
-            rb[u][h] = ghb[u][h];
-          }
-        load_chunks(j + 3, db, fb, rb);
-        if (j + 5 < steps) load_flags(j + 5, gb, ghb);
+      for (int h = 0; h < 2; ++h) {
+        fa[u][h] = ga[u][h];
+        ra[u][h] = gha[u][h];
       }
-    }
+    load_chunks(j + 2, da, fa, ra);
+    load_flags(j + 4, ga, gha);
+    compute(j + 1, db, fb);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        fb[u][h] = gb[u][h];
+        rb[u][h] = ghb[u][h];
+      }
+    load_chunks(j + 3, db, fb, rb);
+    load_flags(j + 5, gb, ghb);
   }
+  // the last one to three steps
+  if (j < steps) compute(j, da, fa);
+  if (j + 2 < steps) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        fa[u][h] = ga[u][h];
+        ra[u][h] = gha[u][h];
+      }
+    load_chunks(j + 2, da, fa, ra);
+  }
+  if (j + 1 < steps) compute(j + 1, db, fb);
+  if (j + 2 < steps) compute(j + 2, da, fa);
 
   // the block's waves, added in wave order, one batch row at a time
 #pragma unroll
@@ -478,12 +524,20 @@ GemvNkFn gemv_nk_any_fn(int nb) {
 }
 // outputs per lane of the KN GEMV for a launch of nb batch rows
 int kn_ow(int nb) { return nb <= 1 ? 16 : 8; }
+template <int F, bool SF>
+GemvKnFn gemv_kn_fn_sf(int nb) {
+  if (nb <= 1) return k_gemv_kn<F, 1, 1, 16, SF>;
+  if (nb <= 2) return k_gemv_kn<F, 2, 1, 8, SF>;
+  if (nb <= 4) return k_gemv_kn<F, 4, 1, 8, SF>;
+  return k_gemv_kn<F, 8, 1, 8, SF>;
+}
+// scalar flag loads for palette formats when N is a multiple of the block width
 template <int F>
-GemvKnFn gemv_kn_fn(int nb) {
-  if (nb <= 1) return k_gemv_kn<F, 1, 1, 16>;
-  if (nb <= 2) return k_gemv_kn<F, 2, 1, 8>;
-  if (nb <= 4) return k_gemv_kn<F, 4, 1, 8>;
-  return k_gemv_kn<F, 8, 1, 8>;
+GemvKnFn gemv_kn_fn(int nb, uint64_t n) {
+  if constexpr (fmt_is_pal(F)) {
+    if (n % (64u * (uint64_t)kn_ow(nb)) == 0) return gemv_kn_fn_sf<F, true>(nb);
+  }
+  return gemv_kn_fn_sf<F, false>(nb);
 }
 
 constexpr int kGemvMaxBatch = 8;
@@ -551,6 +605,10 @@ int kn_slices(const WeightView& w, int nb, const uw_kernel_cfg* cfg) {
     const uint64_t max_s = pairs / (kKnWaves * 4);
     if (s > max_s) s = max_s;
   }
+  // enough slices that a slice's x pairs fit the block's LDS stage
+  const uint64_t per_slice_max = kKnXLdsMax / (4u * (uint64_t)(nb > 0 ? nb : 1));
+  const uint64_t s_min = (pairs + per_slice_max - 1) / per_slice_max;
+  if (s < s_min) s = s_min;
   if (s > pairs) s = pairs;
   if (s < 1) s = 1;
   return (int)s;
@@ -675,11 +733,12 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
         const uint64_t pairs = (w.k + 1) / 2;
         const uint32_t pps = (uint32_t)((pairs + (uint64_t)slices - 1) / (uint64_t)slices);
         const unsigned gy = (unsigned)((pairs + pps - 1) / pps);
-        GemvKnFn f = w.fmt == kFmtBf16 ? gemv_kn_fn<kFmtBf16>(nb)
-                     : w.fmt == kFmtExp ? gemv_kn_fn<kFmtExp>(nb)
-                     : w.fmt == kFmtPal ? gemv_kn_fn<kFmtPal>(nb) : gemv_kn_fn<kFmtPalRun>(nb);
+        GemvKnFn f = w.fmt == kFmtBf16 ? gemv_kn_fn<kFmtBf16>(nb, w.n)
+                     : w.fmt == kFmtExp ? gemv_kn_fn<kFmtExp>(nb, w.n)
+                     : w.fmt == kFmtPal ? gemv_kn_fn<kFmtPal>(nb, w.n) : gemv_kn_fn<kFmtPalRun>(nb, w.n);
         const uint64_t bw = 64u * (uint64_t)kn_ow(nb);
-        hipLaunchKernelGGL(f, dim3((unsigned)((w.n + bw - 1) / bw), gy), dim3(512), 0, s, w, xb, nb, partial, pps);
+        hipLaunchKernelGGL(f, dim3((unsigned)((w.n + bw - 1) / bw), gy), dim3(512), (size_t)nb * pps * 4u, s, w, xb, nb,
+                           partial, pps);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         e = launch_sum_slices(partial, (int)gy, w.n, nb, yb, ldy, col0, s);

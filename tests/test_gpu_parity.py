@@ -240,13 +240,14 @@ def _palette_is_run(m):
 # stored shapes for the vector (small-batch) kernels: NK rows with K a multiple
 # of 4096 / 2048 / 1024 (the pipelined kernel, U = 4 / 2 / 1), an NK shape it
 # does not cover, and KN shapes with several K slices, odd row-pair counts and
-# a partial last column block; 7173 rows spread over 256 CUs take 15 waves per
-# block with a partly filled last round.  outlier_frac picks verbatim-rich weights (a
+# a partial last column block (1024 columns: whole blocks, the flag words
+# are wave-uniform scalar loads); 7173 rows spread over 256 CUs take 15
+# waves per block with a partly filled last round.  outlier_frac picks verbatim-rich weights (a
 # palette with a gap) or none (a palette that is a run of exponents).
 @pytest.mark.parametrize("n,k,layout,outliers", [
     (300, 4096, 0, 0.01), (70, 2048, 0, 0.0), (33, 1024, 0, 0.01), (200, 3072, 0, 0.0), (40, 1088, 0, 0.01),
     (7173, 1024, 0, 0.01),
-    (192, 2008, 1, 0.01), (1088, 1032, 1, 0.0), (64, 520, 1, 0.01),
+    (192, 2008, 1, 0.01), (1088, 1032, 1, 0.0), (64, 520, 1, 0.01), (1024, 2056, 1, 0.01),
 ])
 def test_gemv_shapes(uw, synth, oracle, n, k, layout, outliers):
     r, c = (n, k) if layout == 0 else (k, n)
