@@ -725,6 +725,20 @@ uw_status uw_matmul_reconstruct_grouped(const uw_matrix* const* ms, int count, u
     workspace_for(ms[i], p, batch, cfg, &b);
     off += b;
   }
+  // matrices that all run the VALU GEMV share one launch
+  if (count >= 2 && count <= 4) {
+    WeightView vs[4];
+    int64_t c0[4];
+    int64_t col = 0;
+    for (int i = 0; i < count; ++i) {
+      vs[i] = pipeline_view(ms[i], p, ws + offs[(size_t)i]);
+      c0[i] = col;
+      col += (int64_t)vs[i].n;
+    }
+    const hipError_t e = launch_gemm_group(vs, count, x_dev, batch, y_dev, (int64_t)total_n, c0, cfg, s);
+    if (e == hipSuccess) return UW_OK;
+    if (e != hipErrorNotSupported) return UW_ERR_DEVICE;
+  }
   uint64_t col0 = 0;
   for (int i = 0; i < count; ++i) {
     WeightView v = pipeline_view(ms[i], p, ws + offs[(size_t)i]);

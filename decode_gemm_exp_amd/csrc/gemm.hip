@@ -19,6 +19,7 @@
 //     (deterministic).
 //   * MFMA: gemm_mfma.hip.
 #include <cmath>
+#include <cstring>
 
 #include "rebuild.h"
 
@@ -48,18 +49,39 @@ __device__ __forceinline__ float wave_sum(float v) {
 // pipeline over the wave's steps, two register buffers: while step j is
 // rebuilt and multiplied, the chunks of step j+1 are in flight and the
 // palette flag/rank words of steps j+2, j+3 too.  Row end: wave reduction.
+//
+// One launch can serve up to kGemvGroupMax matrices with the same K and x
+// (fused q+k+v, gate+up): matrix i owns the waves [wave0[i], wave0[i+1]) and
+// writes output columns col0[i] ..; a single matrix is a group of one.
+// Small matrices give each wave only a step or two, so one launch instead
+// of one per matrix saves the pipeline's fill and drain per matrix.
+constexpr int kGemvGroupMax = 4;
+struct GemvGroup {
+  WeightView w[kGemvGroupMax];
+  int64_t col0[kGemvGroupMax];
+  uint32_t wave0[kGemvGroupMax + 1];
+  int count;
+};
+
 template <int FMT, int NB, int U>
-__global__ __launch_bounds__(1024) void k_gemv_nk_pipe(WeightView w, const uint16_t* __restrict__ x, int B,
-                                                       float* __restrict__ y, int64_t ldy, int64_t col0) {
+__global__ __launch_bounds__(1024) void k_gemv_nk_pipe(GemvGroup grp, const uint16_t* __restrict__ x, int B,
+                                                       float* __restrict__ y, int64_t ldy) {
   extern __shared__ uint4 xs4[];   // B rows of K bf16
-  const uint64_t K = w.k, N = w.n;
   const uint16_t* xs = reinterpret_cast<const uint16_t*>(xs4);
   const int lane = threadIdx.x & 63;
   const uint32_t wpb = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);   // keeps the wave math scalar
-  const uint64_t wave = (uint64_t)blockIdx.x * wpb + wave_uniform(threadIdx.x >> 6);
-  const uint64_t nw = (uint64_t)gridDim.x * wpb;
+  const uint32_t gwave = blockIdx.x * wpb + wave_uniform(threadIdx.x >> 6);
+  int gi = 0;
+#pragma unroll
+  for (int i = 1; i < kGemvGroupMax; ++i) gi += (i < grp.count && gwave >= grp.wave0[i]) ? 1 : 0;
+  gi = (int)wave_uniform((uint32_t)gi);
+  const WeightView w = grp.w[gi];
+  const int64_t col0 = grp.col0[gi];
+  const uint64_t K = w.k, N = w.n;
+  const uint64_t wave = gwave - grp.wave0[gi];
+  const uint64_t nw = grp.wave0[gi + 1] - grp.wave0[gi];
   const uint32_t spr = (uint32_t)(K / (1024u * U));         // steps per row
-  const uint64_t steps = wave < N ? ((N - 1 - wave) / nw + 1) * spr : 0u;
+  const uint64_t steps = (gwave < grp.wave0[grp.count] && wave < N) ? ((N - 1 - wave) / nw + 1) * spr : 0u;
   // cursor of a step: row and part; advanced one step at a time
   struct Cur {
     uint64_t row;
@@ -502,17 +524,18 @@ __global__ __launch_bounds__(256) void k_sum_slices(const float* __restrict__ pa
 }
 
 typedef void (*GemvNkFn)(WeightView, const uint16_t*, int, float*, int64_t, int64_t);
+typedef void (*GemvPipeFn)(GemvGroup, const uint16_t*, int, float*, int64_t);
 typedef void (*GemvKnFn)(WeightView, const uint16_t*, int, float*, uint32_t);
 
 template <int F, int U>
-GemvNkFn gemv_nk_pipe_nb(int nb) {
+GemvPipeFn gemv_nk_pipe_nb(int nb) {
   if (nb <= 1) return k_gemv_nk_pipe<F, 1, U>;
   if (nb <= 2) return k_gemv_nk_pipe<F, 2, U>;
   if (nb <= 4) return k_gemv_nk_pipe<F, 4, (U > 2 ? 2 : U)>;
   return k_gemv_nk_pipe<F, 8, (U > 2 ? 2 : U)>;
 }
 template <int F>
-GemvNkFn gemv_nk_pipe_fn(int nb, int u) {
+GemvPipeFn gemv_nk_pipe_fn(int nb, int u) {
   return u == 4 ? gemv_nk_pipe_nb<F, 4>(nb) : u == 2 ? gemv_nk_pipe_nb<F, 2>(nb) : gemv_nk_pipe_nb<F, 1>(nb);
 }
 template <int F>
@@ -614,6 +637,61 @@ int kn_slices(const WeightView& w, int nb, const uw_kernel_cfg* cfg) {
   return (int)s;
 }
 
+// Waves of a group launch: (blocks, waves per block) as for one matrix of
+// all the group's rows, then each matrix gets waves in proportion to its
+// rows (at least one, at most one per row).  False when the pipelined
+// kernel cannot run the group: K not a multiple of 1024, x too large for
+// LDS, or a wave left with more than 64 rows (one lane keeps each row's sum).
+bool gemv_group_plan(GemvGroup& g, int nb, uint64_t* blocks, int* wpb) {
+  if (nk_pipe_u(g.w[0], nb) == 0) return false;
+  uint64_t total = 0;
+  for (int i = 0; i < g.count; ++i) total += g.w[i].n;
+  *wpb = nk_pipe_waves(total, blocks);
+  const uint64_t T = *blocks * (uint64_t)*wpb;
+  uint64_t wv[kGemvGroupMax] = {0, 0, 0, 0}, sum = 0;
+  for (int i = 0; i < g.count; ++i) {
+    uint64_t c = (T * g.w[i].n + total / 2) / total;
+    if (c < 1) c = 1;
+    if (c > g.w[i].n) c = g.w[i].n;
+    wv[i] = c;
+    sum += c;
+  }
+  while (sum > T) {   // rounding up the small ones: take the excess from the largest share
+    int big = 0;
+    for (int i = 1; i < g.count; ++i)
+      if (wv[i] > wv[big]) big = i;
+    if (wv[big] <= 1) return false;
+    --wv[big];
+    --sum;
+  }
+  g.wave0[0] = 0;
+  for (int i = 0; i < g.count; ++i) {
+    if ((g.w[i].n + wv[i] - 1) / wv[i] > 64) return false;
+    g.wave0[i + 1] = g.wave0[i] + (uint32_t)wv[i];
+  }
+  for (int i = g.count + 1; i <= kGemvGroupMax; ++i) g.wave0[i] = g.wave0[g.count];
+  return true;
+}
+
+// fmt: the weight format all matrices of the group are run in
+hipError_t launch_gemv_group(const GemvGroup& g, int fmt, const uint16_t* x, int nb, float* y, int64_t ldy,
+                             uint64_t blocks, int wpb, hipStream_t s) {
+  const int u = nk_pipe_u(g.w[0], nb);
+  GemvPipeFn f = fmt == kFmtBf16 ? gemv_nk_pipe_fn<kFmtBf16>(nb, u)
+                 : fmt == kFmtExp ? gemv_nk_pipe_fn<kFmtExp>(nb, u)
+                 : fmt == kFmtPal ? gemv_nk_pipe_fn<kFmtPal>(nb, u) : gemv_nk_pipe_fn<kFmtPalRun>(nb, u);
+  static bool lds_set[4][4][3] = {};
+  const int ni = nb <= 1 ? 0 : nb <= 2 ? 1 : nb <= 4 ? 2 : 3, ui = u == 4 ? 2 : u == 2 ? 1 : 0;
+  if (!lds_set[fmt][ni][ui]) {
+    hipError_t e = hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kNkLdsMax);
+    if (e != hipSuccess) return e;
+    lds_set[fmt][ni][ui] = true;
+  }
+  const size_t lds = (size_t)nb * g.w[0].k * 2;
+  hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(64 * wpb), lds, s, g, x, nb, y, ldy);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // Variant numbering seen through uw_kernel_cfg.variant: 1 = VALU GEMV (any
@@ -645,6 +723,43 @@ static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_c
   if (batch <= 64) return 2 + 0;
   if (batch <= 192) return 2 + 2;
   return 2 + 4;
+}
+
+// One launch for a group of stored [N][K] matrices with the same K and x
+// whose calls resolve to the VALU GEMV: output columns col0s[i] .. of y.
+// hipErrorNotSupported when the group does not qualify (the caller then
+// launches the matrices one by one).  Palette matrices of both kinds run
+// with the general lookup unless all palettes are runs.
+hipError_t launch_gemm_group(const WeightView* ws, int count, const uint16_t* x, int64_t batch, float* y,
+                             int64_t ldy, const int64_t* col0s, const uw_kernel_cfg* cfg, hipStream_t s) {
+  if (count < 2 || count > kGemvGroupMax || batch <= 0) return hipErrorNotSupported;
+  const bool pal = fmt_is_pal(ws[0].fmt);
+  bool all_run = true;
+  for (int i = 0; i < count; ++i) {
+    if (ws[i].layout != 0 || ws[i].k != ws[0].k || resolve_variant(ws[i], batch, cfg) != 1) return hipErrorNotSupported;
+    if (fmt_is_pal(ws[i].fmt) != pal || (!pal && ws[i].fmt != ws[0].fmt)) return hipErrorNotSupported;
+    all_run = all_run && ws[i].fmt == kFmtPalRun;
+  }
+  const int fmt = pal ? (all_run ? kFmtPalRun : kFmtPal) : ws[0].fmt;
+  GemvGroup grp;
+  std::memset(&grp, 0, sizeof(grp));
+  grp.count = count;
+  for (int i = 0; i < count; ++i) {
+    grp.w[i] = ws[i];
+    grp.col0[i] = col0s[i];
+  }
+  // the plan does not depend on the batch chunk beyond the LDS check of the largest one
+  const int nb_max = (int)(batch < kGemvMaxBatch ? batch : kGemvMaxBatch);
+  uint64_t blocks = 0;
+  int wpb = 0;
+  if (!gemv_group_plan(grp, nb_max, &blocks, &wpb)) return hipErrorNotSupported;
+  for (int64_t b0 = 0; b0 < batch; b0 += kGemvMaxBatch) {
+    const int nb = (int)(batch - b0 < kGemvMaxBatch ? batch - b0 : kGemvMaxBatch);
+    hipError_t e = launch_gemv_group(grp, fmt, x + (uint64_t)b0 * ws[0].k, nb, y + (uint64_t)b0 * (uint64_t)ldy, ldy,
+                                     blocks, wpb, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // Workspace floats for partial sums of the kernel this call resolves to (the
@@ -702,23 +817,16 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
       const uint16_t* xb = x + (uint64_t)b0 * w.k;
       float* yb = y + (uint64_t)b0 * (uint64_t)ldy;
       if (w.layout == 0) {
-        const int u = nk_pipe_u(w, nb);
+        GemvGroup grp;
+        std::memset(&grp, 0, sizeof(grp));
+        grp.w[0] = w;
+        grp.col0[0] = col0;
+        grp.count = 1;
         uint64_t pipe_blocks = 0;
-        const int pipe_wpb = nk_pipe_waves(w.n, &pipe_blocks);
-        if (u > 0 && (w.n + pipe_blocks * pipe_wpb - 1) / (pipe_blocks * pipe_wpb) <= 64) {
-          GemvNkFn f = w.fmt == kFmtBf16 ? gemv_nk_pipe_fn<kFmtBf16>(nb, u)
-                       : w.fmt == kFmtExp ? gemv_nk_pipe_fn<kFmtExp>(nb, u)
-                       : w.fmt == kFmtPal ? gemv_nk_pipe_fn<kFmtPal>(nb, u) : gemv_nk_pipe_fn<kFmtPalRun>(nb, u);
-          const size_t lds = (size_t)nb * w.k * 2;
-          static bool lds_set[4][4][3] = {};
-          const int fi = w.fmt, ni = nb <= 1 ? 0 : nb <= 2 ? 1 : nb <= 4 ? 2 : 3, ui = u == 4 ? 2 : u == 2 ? 1 : 0;
-          if (!lds_set[fi][ni][ui]) {
-            hipError_t e = hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)kNkLdsMax);
-            if (e != hipSuccess) return e;
-            lds_set[fi][ni][ui] = true;
-          }
-          hipLaunchKernelGGL(f, dim3((unsigned)pipe_blocks), dim3(64 * pipe_wpb), lds, s, w, xb, nb, yb, ldy, col0);
+        int pipe_wpb = 0;
+        if (gemv_group_plan(grp, nb, &pipe_blocks, &pipe_wpb)) {
+          hipError_t e = launch_gemv_group(grp, w.fmt, xb, nb, yb, ldy, pipe_blocks, pipe_wpb, s);
+          if (e != hipSuccess) return e;
         } else {
           GemvNkFn f = w.fmt == kFmtBf16 ? gemv_nk_any_fn<kFmtBf16>(nb)
                        : w.fmt == kFmtExp ? gemv_nk_any_fn<kFmtExp>(nb)

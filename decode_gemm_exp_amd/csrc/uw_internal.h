@@ -120,6 +120,10 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
                        int64_t ldy, int64_t col0, const uw_kernel_cfg* cfg, float* partial,
                        size_t partial_elems, hipStream_t s);
 size_t gemm_partial_elems(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg);
+// one launch for up to 4 stored [N][K] matrices sharing K and x that resolve
+// to the VALU GEMV; hipErrorNotSupported otherwise
+hipError_t launch_gemm_group(const WeightView* ws, int count, const uint16_t* x, int64_t batch, float* y,
+                             int64_t ldy, const int64_t* col0s, const uw_kernel_cfg* cfg, hipStream_t s);
 size_t gemm_partial_elems_max(const WeightView& w, int64_t batch, int split_k);
 int gemm_variant_count();
 int rf_first_variant();                          // first register-fed MFMA variant
