@@ -196,6 +196,56 @@ def extras(uw, synth, torch, dev, iters: int = 12, copies: int = 4):
             flops = 2.0 * b * n * k
             out[f"down8b_b{b}_{PIPE_NAMES[p]}"] = {"us": round(t * 1e6, 2), "tflops": round(flops / t / 1e12, 2),
                                                  "mfma_frac": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    del ms
+    out.update(attention_rows(uw, synth, torch, dev, iters, copies))
+    return out
+
+
+def attention_rows(uw, synth, torch, dev, iters: int, copies: int):
+    """The attention projections of Llama-3.1-8B and Llama-70B with the
+    palette-direct pipeline: q, k and v fused into one call (they share x)
+    and o on its own, at each workload's batches.  `roofline` is the larger
+    of the HBM time of the algorithmic bytes and the MFMA time of the flops,
+    over the measured time."""
+    out = {}
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    for name in ("attn8b", "attn70b"):
+        wl = synth.WORKLOADS[name]
+        sets = [[] for _ in range(copies)]
+        for i, (_, n, k, layout) in enumerate(wl.mats):
+            w = synth.workload_weights(wl, i, device=dev)
+            for c in range(copies):
+                m = uw.uw_compress(w, n, k, layout)
+                uw.uw_transcode_palette(m, None)
+                sets[c].append(m)
+            del w
+        infos = [m.info() for m in sets[0]]
+        k = infos[0].k
+        for b in wl.batches:
+            x = synth.activations(b, k, seed=wl.seed, device=dev)
+            for part, idx in (("qkv", (0, 1, 2)), ("o", (3,))):
+                N = sum(infos[i].n for i in idx)
+                y = torch.empty((b, N), dtype=torch.float32, device=dev)
+                ws = torch.empty(max(16, sum(uw.uw_workspace_size(sets[0][i], 3, b) for i in idx)),
+                                 dtype=torch.uint8, device=dev)
+                run = lambda c: uw.uw_matmul_reconstruct_grouped([sets[c][i] for i in idx], 3, x, y, ws)  # noqa: E731
+                for c in range(copies):
+                    run(c)
+                s, e = ev(), ev()
+                hold_gpu(torch, iters)
+                s.record()
+                for it in range(iters):
+                    run(it % copies)
+                e.record()
+                torch.cuda.synchronize()
+                t = s.elapsed_time(e) / iters / 1e3
+                flops = 2.0 * b * N * k
+                nbytes = sum(algorithmic_bytes(infos[i], "gemv_direct", b) for i in idx)
+                out[f"{name}_{part}_b{b}_direct"] = {
+                    "us": round(t * 1e6, 2), "tflops": round(flops / t / 1e12, 3),
+                    "decoded_gbs": round(2 * sum(infos[i].numel for i in idx) / t / 1e9, 1),
+                    "roofline": round(max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)) / t, 4)}
+        del sets
     return out
 
 

@@ -39,7 +39,10 @@ class Workload:
     extra: dict = field(default_factory=dict)
 
 
-# The five workloads: shapes of Llama-3.1-8B / Llama-70B MLP projections.
+# The five MLP workloads (shapes of Llama-3.1-8B / Llama-70B MLP projections),
+# then the attention projections of the same two models (q/o: hidden x
+# hidden; k/v: 8 key-value heads of 128, stored [N][K] as nn.Linear keeps
+# them), the next step after the MLP: the same codec on new shapes.
 WORKLOADS = {
     "w256x512": Workload(
         "w256x512", mats=(("w", 256, 512, 0),), outlier_frac=0.002, outlier_shift=12,
@@ -61,6 +64,14 @@ WORKLOADS = {
                         ("down", 8192, 28672, 1)),
         batches=(1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024), layers=80, seed=SEED_BASE + 5,
         notes="80 layers of Llama-70B MLP, compressed-resident; autotuned"),
+    "attn8b": Workload(
+        "attn8b", mats=(("q", 4096, 4096, 0), ("k", 1024, 4096, 0), ("v", 1024, 4096, 0), ("o", 4096, 4096, 0)),
+        outlier_frac=0.0002, outlier_shift=8, batches=(1, 8, 64), seed=SEED_BASE + 6,
+        notes="Llama-3.1-8B attention q/k/v/o, 0.02% outliers x2^8; fused q+k+v and o at B=1, 8, 64"),
+    "attn70b": Workload(
+        "attn70b", mats=(("q", 8192, 8192, 0), ("k", 1024, 8192, 0), ("v", 1024, 8192, 0), ("o", 8192, 8192, 0)),
+        outlier_frac=0.0002, outlier_shift=8, batches=(1, 64, 1024), seed=SEED_BASE + 7,
+        notes="Llama-70B attention q/k/v/o, 0.02% outliers x2^8; fused q+k+v and o at B=1, 64, 1024"),
 }
 
 

@@ -1,4 +1,4 @@
-"""Parity at the full sizes of the five workloads, in the launch configuration
+"""Parity at the full sizes of the workloads, in the launch configuration
 the benchmark times.
 
   w256x512 : 256x512, 0.2% outliers x2^12 -- compress, full decode, B=1 GEMM
@@ -8,6 +8,8 @@ the benchmark times.
   mlp70b   : Llama-70B MLP layer shapes (gate/up 28672x8192, down 8192x28672
              stored [28672][8192]); streams of one full layer against the
              oracle, GEMMs on sampled output columns at B=1,64,1024
+  attn8b, attn70b : attention q/k/v/o of the same models (q, o hidden x
+             hidden; k, v 1024 x hidden); fused q+k+v and o
 
 Streams and decoded weights are compared whole; GEMMs whole where the fp64
 reference takes seconds, else on sampled output columns.
@@ -166,3 +168,42 @@ def test_mlp70b_one_layer(uw, synth, oracle):
                         what=f"mlp70b {label}")
         del m, w_np
         torch.cuda.empty_cache()
+
+
+def _attention(uw, synth, oracle, name, cols_for):
+    """q/k/v/o of one attention layer: codec parity per matrix (blob equals
+    the oracle's, decodes bit-exact), the fused q+k+v GEMM (one x, N = q+k+v)
+    and o on their own, every pipeline at one row, the palette pipelines at
+    the larger batches; output columns sampled where the fp64 reference
+    would take long."""
+    wl = synth.WORKLOADS[name]
+    ms, wnps = [], []
+    for i, (label, n, k, layout) in enumerate(wl.mats):
+        say(f"{name} {label}: codec")
+        w = synth.workload_weights(wl, i, device=DEV)
+        m, w_np, _ = codec_parity(uw, oracle, w, n, k, layout)
+        ms.append(m)
+        wnps.append(w_np)
+        del w
+    k = wl.mats[0][2]
+    rng = np.random.default_rng(3)
+    for b in wl.batches:
+        x = synth.activations(b, k, seed=wl.seed + b, device=DEV)
+        pipes = range(4) if b == 1 else (2, 3)
+        gemm_parity(uw, oracle, None, wnps[:3], 0, x, pipes, grouped=ms[:3], what=f"{name} qkv b{b}")
+        n_o = wl.mats[3][1]
+        cols = cols_for(b, n_o, rng)
+        gemm_parity(uw, oracle, ms[3], wnps[3], 0, x, pipes, cols=cols, what=f"{name} o b{b}")
+    del ms, wnps
+    torch.cuda.empty_cache()
+
+
+def test_attn8b_qkv_fused_and_o(uw, synth, oracle):
+    _attention(uw, synth, oracle, "attn8b", lambda b, n, rng: None)
+
+
+@pytest.mark.timeout(600)
+def test_attn70b_qkv_fused_and_o(uw, synth, oracle):
+    _attention(uw, synth, oracle, "attn70b",
+               lambda b, n, rng: None if b == 1 else np.sort(rng.choice(n, 64, replace=False)))
+
