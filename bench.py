@@ -295,6 +295,18 @@ def job_bytes(info, pipeline: int, batch: int) -> float:
             3: 1.5 * M + Aux + Vb + X + Y}[pipeline]
 
 
+def resident_bytes(info) -> int:
+    """HBM bytes a matrix keeps: the UWF1 sections that are still resident
+    (the Huffman stream and its offsets may have been dropped) plus the
+    4-bit palette indices when resident."""
+    b = info.compressed_bytes
+    if not info.has_stream:
+        b -= 4 * (info.segments + 1) + 4 * (info.stream_words + 2)
+    if info.has_palette_idx:
+        b += info.numel // 2
+    return b
+
+
 def run_mlp70b(args) -> int:
     """80 Llama-70B MLP layers (gate/up 28672x8192, down 8192x28672 stored
     transposed) compressed-resident in HBM; the autotuner picks pipeline,
@@ -309,14 +321,22 @@ def run_mlp70b(args) -> int:
     L = args.layers
     batches = [int(b) for b in args.batches.split(",")] if args.batches else list(wl.batches)
     mats, proj = [], []
+    alternate = args.residency == "alternate"
     t0 = time.perf_counter()
     for layer in range(L):
+        # alternate: even layers easy (palette indices resident, Huffman
+        # stream dropped: direct palette only), odd layers hard (Huffman stream
+        # only: decoded at run time); the tuner sees (parity, projection)
+        easy = not alternate or layer % 2 == 0
         for i, (label, n, k, layout) in enumerate(wl.mats):
             w = synth.workload_weights(wl, i, layer=layer, device=dev)
             m = uw.uw_compress(w, n, k, layout, seg_groups=args.seg_groups)
-            uw.uw_transcode_palette(m, None)
+            if easy:
+                uw.uw_transcode_palette(m, None)
+                if alternate:
+                    uw.uw_drop_stream(m)
             mats.append(m)
-            proj.append(i)
+            proj.append((layer % 2) * 3 + i if alternate else i)
             del w
         if layer % 10 == 9:
             print(f"bench: {layer + 1}/{L} layers resident ({time.perf_counter() - t0:.0f} s)", file=sys.stderr,
@@ -324,8 +344,10 @@ def run_mlp70b(args) -> int:
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     infos = [m.info() for m in mats]
-    resident = sum(i.compressed_bytes + (i.numel // 2) for i in infos)
+    resident = sum(resident_bytes(i) for i in infos)
     nt = min(args.tune_layers, L) * 3
+    if alternate and nt < 6:
+        nt = 6   # at least one layer of each kind
     print(f"bench: autotune on {nt // 3} layers, batches {batches}", file=sys.stderr, flush=True)
     t_tune = time.perf_counter()
     tuned = uw.uw_autotune(mats[:nt], proj[:nt], batches, max_passes=2,
@@ -363,12 +385,15 @@ def run_mlp70b(args) -> int:
                      "hbm_frac": round(nbytes / t / 1e3 / HBM_PEAK_GBS, 4),
                      "mfma_frac": round(flops / t / 1e6 / BF16_PEAK_TFLOPS, 4),
                      "roofline_frac": round(max(nbytes / 8e12, flops / 2.5e15) / (t * 1e-6), 4),
-                     "choice": {wl.mats[p][0]: {k2: choice[p][k2] for k2 in ("pipeline", "variant", "decode_cus")}
-                                for p in range(3)}})
+                     "choice": {(("easy_" if p < 3 else "hard_") if alternate else "") + wl.mats[p % 3][0]:
+                                {k2: choice[p][k2] for k2 in ("pipeline", "variant", "decode_cus")}
+                                for p in range(6 if alternate else 3)}})
         print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
         del x, y, ws
     res = {"metric": METRIC, "workload": f"mlp70b: {L} layers of Llama-70B MLP (gate/up 28672x8192, down "
                                         f"8192x28672 stored transposed) bf16 N(0,0.02), compressed-resident",
+           "residency": "even layers palette indices only, odd layers Huffman stream only" if alternate
+                        else "palette indices and Huffman stream in every layer",
            "resident_gb": round(resident / 1e9, 2), "dense_bf16_gb": round(sum(2 * i.numel for i in infos) / 1e9, 2),
            "tune_layers": nt // 3, "tune_seconds": round(t_tune, 1), "rows": rows}
     print(json.dumps(res), flush=True)
@@ -390,6 +415,9 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=80, help="mlp70b: resident layers")
     ap.add_argument("--tune-layers", type=int, default=4, help="mlp70b: layers the autotuner times")
     ap.add_argument("--batches", default="", help="mlp70b: comma-separated batch sizes")
+    ap.add_argument("--residency", default="both", choices=["both", "alternate"],
+                    help="mlp70b: both forms in every layer, or alternating easy (palette indices) and hard "
+                         "(Huffman stream) layers")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; the path shards per matrix "

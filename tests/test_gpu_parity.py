@@ -339,6 +339,47 @@ def test_sequence_runner_matches_single_calls(uw, synth, oracle):
             check_gemm(oracle, j.y.cpu().numpy(), x_np, w_np, layout, what=f"seq cus={dcus}")
 
 
+def test_alternating_residency_sequence(uw, synth, oracle):
+    """Hard/easy layers: easy matrices keep only their palette indices
+    (Huffman stream dropped, direct palette), hard ones only the Huffman
+    stream (decoded at run time).  A sequence alternating them, with each
+    hard matrix's decode running beside the previous GEMM on every CU or on
+    a CU share, matches the fp64 reference; sections that were dropped are
+    refused."""
+    say("alternating residency")
+    k = 1024
+    x = synth.activations(3, k, seed=12).to(DEV)
+    jobs, ref = [], []
+    for layer in range(4):
+        for i, (n, layout) in enumerate([(640, 0), (320, 0), (512, 1)]):
+            r, c = (n, k) if layout == 0 else (k, n)
+            w = synth.weights(r, c, 0.02, 0.002, 9, seed=200 + 10 * layer + i).to(DEV)
+            m = gpu_compress(uw, w, n, k, layout)
+            if layer % 2 == 0:
+                uw.uw_transcode_palette(m, None)
+                uw.uw_drop_stream(m)
+                info = m.info()
+                assert info.has_palette_idx and not info.has_stream
+                with pytest.raises(uw.UwError):
+                    uw.uw_decode_exponent(m, torch.empty(r * c, dtype=torch.uint8, device=DEV))
+                pipe = 3
+            else:
+                assert not m.info().has_palette_idx
+                pipe = 1 if i != 1 else 2
+            y = torch.full((3, n), float("nan"), dtype=torch.float32, device=DEV)
+            jobs.append(uw.Job(m, pipe, x, y))
+            ref.append((bits(w), layout))
+    ws = torch.empty(uw.uw_sequence_workspace_size(jobs), dtype=torch.uint8, device=DEV)
+    x_np = bits(x)
+    for dcus in (0, 96, 100000):
+        for j in jobs:
+            j.y.fill_(float("nan"))
+        uw.uw_run_sequence(jobs, dcus, ws)
+        torch.cuda.synchronize()
+        for j, (w_np, layout) in zip(jobs, ref):
+            check_gemm(oracle, j.y.cpu().numpy(), x_np, w_np, layout, what=f"alternating cus={dcus}")
+
+
 @pytest.mark.parametrize("sg", [1, 8, 64])
 def test_fallback_decoder_matches(uw, synth, oracle, monkeypatch, sg):
     """The direct-from-HBM decoder (used when a wave's stream does not fit in
