@@ -269,6 +269,47 @@ def test_gemv_shapes(uw, synth, oracle, n, k, layout, outliers):
                 check_gemm(oracle, y, x_np, w_np, layout, what=f"batch {batch} split {split}")
 
 
+def test_grouped_matmul(uw, synth, oracle):
+    """uw_matmul_reconstruct_grouped: matrices that all take the GEMV share
+    one launch (a run palette next to a palette with gaps runs with the
+    general lookup; more than eight rows go in chunks); a group of five, a
+    group holding a [K][N] matrix and batches that resolve to MFMA kernels
+    are launched one matrix at a time.  Every column block is checked
+    against the fp64 reference."""
+    say("grouped matmul")
+    k = 2048
+    specs = [(700, 0, 0.0), (300, 0, 0.002), (1100, 0, 0.0), (64, 0, 0.002), (520, 0, 0.0), (384, 1, 0.002)]
+    ms, wnps = [], []
+    for i, (n, layout, out) in enumerate(specs):
+        r, c = (n, k) if layout == 0 else (k, n)
+        w = synth.weights(r, c, 0.02, out, 10, seed=300 + i).to(DEV)
+        m = gpu_compress(uw, w, n, k, layout)
+        uw.uw_transcode_palette(m, None)
+        ms.append(m)
+        wnps.append(bits(w))
+    assert _palette_is_run(ms[0]) and not _palette_is_run(ms[1])
+    groups = [(0, 1), (0, 1, 2, 3), (1, 3), (0, 1, 2, 3, 4), (0, 5, 1)]
+    for idx in groups:
+        sub = [ms[i] for i in idx]
+        N = sum(ms[i].info().n for i in idx)
+        for batch, cfg in ((1, None), (3, None), (9, {"variant": 1}), (24, None)):
+            x = synth.activations(batch, k, seed=batch + 7).to(DEV)
+            x_np = bits(x)
+            for p in (0, 1, 3):
+                y = torch.full((batch, N), float("nan"), dtype=torch.float32, device=DEV)
+                ws_bytes = sum(uw.uw_workspace_size(m, p, batch) for m in sub)
+                ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV)
+                uw.uw_matmul_reconstruct_grouped(sub, p, x, y, ws, cfg=cfg)
+                torch.cuda.synchronize()
+                yn = y.cpu().numpy()
+                col = 0
+                for i in idx:
+                    n = ms[i].info().n
+                    check_gemm(oracle, yn[:, col:col + n], x_np, wnps[i], specs[i][1],
+                               what=f"group {idx} batch {batch} pipeline {p} matrix {i}")
+                    col += n
+
+
 @pytest.mark.parametrize("layout", [0, 1])
 def test_gemm_one_hot_exact(uw, synth, oracle, layout):
     """x row j one-hot at k_j: y[j][n] must equal W[n][k_j] exactly."""
