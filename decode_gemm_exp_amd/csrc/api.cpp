@@ -14,10 +14,26 @@
 #include <mutex>
 #include <new>
 #include <vector>
+#include <tuple>
+#include <set>
 
 #include "uw_internal.h"
 
 using namespace uw;
+
+hipError_t uw::allow_dynamic_lds(const void* kernel, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::set<std::tuple<const void*, int, int>> done;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_tuple(kernel, dev, bytes);
+  if (done.count(key)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert(key);
+  return e;
+}
 
 namespace {
 

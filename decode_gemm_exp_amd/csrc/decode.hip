@@ -571,13 +571,8 @@ void staged_shape(const DecodeArgs& a, uint32_t* wpb_out, uint32_t* resident_out
 
 template <int MODE, int CH, bool RUN, bool NT>
 hipError_t launch_staged_pal(const DecodeArgs& a, uint32_t wpb, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_decode_staged<MODE, CH, RUN, NT>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = allow_dynamic_lds((const void*)k_decode_staged<MODE, CH, RUN, NT>, (int)kMaxDynLds);
+  if (e != hipSuccess) return e;
   const uint64_t threads = 64ull * wpb;
   const uint64_t blocks = (a.segments + threads - 1) / threads;
   hipLaunchKernelGGL((k_decode_staged<MODE, CH, RUN, NT>), dim3((uint32_t)blocks), dim3((uint32_t)threads),

@@ -680,13 +680,8 @@ hipError_t launch_gemv_group(const GemvGroup& g, int fmt, const uint16_t* x, int
   GemvPipeFn f = fmt == kFmtBf16 ? gemv_nk_pipe_fn<kFmtBf16>(nb, u)
                  : fmt == kFmtExp ? gemv_nk_pipe_fn<kFmtExp>(nb, u)
                  : fmt == kFmtPal ? gemv_nk_pipe_fn<kFmtPal>(nb, u) : gemv_nk_pipe_fn<kFmtPalRun>(nb, u);
-  static bool lds_set[4][4][3] = {};
-  const int ni = nb <= 1 ? 0 : nb <= 2 ? 1 : nb <= 4 ? 2 : 3, ui = u == 4 ? 2 : u == 2 ? 1 : 0;
-  if (!lds_set[fmt][ni][ui]) {
-    hipError_t e = hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kNkLdsMax);
-    if (e != hipSuccess) return e;
-    lds_set[fmt][ni][ui] = true;
-  }
+  hipError_t e = allow_dynamic_lds((const void*)f, (int)kNkLdsMax);
+  if (e != hipSuccess) return e;
   const size_t lds = (size_t)nb * g.w[0].k * 2;
   hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(64 * wpb), lds, s, g, x, nb, y, ldy);
   return hipGetLastError();

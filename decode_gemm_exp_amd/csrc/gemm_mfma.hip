@@ -357,28 +357,16 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
 
 typedef void (*Mfma2Fn)(WeightView, const uint16_t*, int, float*, int64_t, int64_t, int64_t, float*, int, int);
 
-template <int L, int F, int BM, int BN, int WGM>
-Mfma2Fn prepared() {
-  static bool done = false;
-  if (!done) {
-    const int lds = (int)(2 * (BM * kLDK + w_tile_elems<L, BN>()) * sizeof(uint16_t));
-    (void)hipFuncSetAttribute((const void*)k_mfma2<L, F, BM, BN, WGM>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              lds);
-    done = true;
-  }
-  return k_mfma2<L, F, BM, BN, WGM>;
-}
-
 template <int L, int F>
 Mfma2Fn pick(int tile) {
   switch (tile) {
-    case 0: return prepared<L, F, 64, 128, 2>();
-    case 1: return prepared<L, F, 128, 128, 2>();
-    case 2: return prepared<L, F, 128, 256, 2>();
-    case 3: return prepared<L, F, 256, 128, 2>();
-    case 4: return prepared<L, F, 256, 256, 2>();
-    case 5: return prepared<L, F, 32, 128, 1>();
-    default: return prepared<L, F, 32, 256, 1>();
+    case 0: return k_mfma2<L, F, 64, 128, 2>;
+    case 1: return k_mfma2<L, F, 128, 128, 2>;
+    case 2: return k_mfma2<L, F, 128, 256, 2>;
+    case 3: return k_mfma2<L, F, 256, 128, 2>;
+    case 4: return k_mfma2<L, F, 256, 256, 2>;
+    case 5: return k_mfma2<L, F, 32, 128, 1>;
+    default: return k_mfma2<L, F, 32, 256, 1>;
   }
 }
 
@@ -437,6 +425,10 @@ hipError_t launch_mfma2(const WeightView& w, const uint16_t* x, int64_t batch, f
   }
   const size_t wtile = w.layout == 0 ? (size_t)t.bn * kLDK : (size_t)kBK * (size_t)(t.bn + 16);
   const size_t lds = 2 * ((size_t)t.bm * kLDK + wtile) * sizeof(uint16_t);
+  {
+    hipError_t e = allow_dynamic_lds((const void*)f, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   const int ntiles = (int)((w.n + (uint64_t)t.bn - 1) / (uint64_t)t.bn);
   const int mtiles = (int)((batch + t.bm - 1) / t.bm);
   dim3 grid((unsigned)(ntiles * mtiles), 1, (unsigned)slices);

@@ -443,6 +443,7 @@ hipError_t launch_mfma_rf(const WeightView& w, const uint16_t* x, int64_t batch,
   const int64_t kslice = ((wins + slices - 1) / slices) * kWin;
   const unsigned rowblocks = (unsigned)(((int64_t)w.n + 16 * R - 1) / (16 * R));
   const uint32_t fwords = (uint32_t)rf_flag_words(w, kind);   // staged in LDS per block
+  hipError_t e0 = hipSuccess;
   for (int64_t b0 = 0; b0 < batch; b0 += kRfMaxBatch) {
     const int64_t nb = batch - b0 < kRfMaxBatch ? batch - b0 : kRfMaxBatch;
     const bool split = slices > 1;
@@ -464,6 +465,8 @@ hipError_t launch_mfma_rf(const WeightView& w, const uint16_t* x, int64_t batch,
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
+    e0 = allow_dynamic_lds((const void*)f, (int)(fwords * 8));
+    if (e0 != hipSuccess) return e0;
     hipLaunchKernelGGL(f, dim3(rowblocks, (unsigned)slices), dim3(256), (size_t)fwords * 8, s, w, xb, (int)nb, yb,
                        ldy, col0, kslice, split ? part : nullptr, fwords, (const uint4*)xp);
     hipError_t e = hipGetLastError();

@@ -57,6 +57,10 @@ bool limited_lengths(const uint64_t* w, int n, int lmax, uint8_t* len);
 void assign_codes(Tables& t);                          // from code_len
 void build_decode_lut(const Tables& t, uint32_t* lut4096);
 
+// Raise a kernel's dynamic LDS limit to `bytes` on the current device, once
+// per (kernel, device, size); thread safe (api.cpp).
+hipError_t allow_dynamic_lds(const void* kernel, int bytes);
+
 // ---- kernel launchers (compress.hip, decode.hip, gemm*.hip) ------------------
 hipError_t launch_histogram(const uint16_t* w, uint64_t numel, uint32_t* hist, hipStream_t s);
 hipError_t launch_flags(const uint16_t* w, uint64_t numel, uint64_t groups, const uint8_t* slot_tab,
