@@ -152,15 +152,16 @@ extern "C" uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj
           for (int i = 0; i < count; ++i)
             if (proj[i] == p && !feasible(ms[i], pl)) ok = false;
           if (!ok) continue;
-          const int small = 2 + uw::mfma2_small_tile_first();   // the 32-row MFMA tiles
           const int rf = uw::rf_first_variant();                  // the register-fed MFMA kernels
           bool all_nk = true;
           for (int i = 0; i < count; ++i)
             if (proj[i] == p && ms[i]->layout != 0) all_nk = false;
           for (int v = 1; v <= nvar; ++v) {
+            int bm = 0, bn = 0;
+            if (v > 1 && v < rf) uw::mfma2_tile_dims(v - 2, &bm, &bn);
             if (v == 1 && batch > 32) continue;                 // the VALU kernel only for small batches
-            if (v > 1 && v < small && batch < 8) continue;      // 64- to 256-row tiles from batch 8 on
-            if (v >= small && v < rf && (batch < 2 || batch > 128)) continue;   // 32-row tiles for batches 2..128
+            if (bm > 32 && batch < 8) continue;                 // 64- to 256-row tiles from batch 8 on
+            if (bm == 32 && (batch < 2 || batch > 128)) continue;   // 32-row tiles for batches 2..128
             if (v >= rf && (!all_nk || batch > 2 * uw::mfma_rf_max_batch())) continue;   // [N][K] only, <= 128 rows
             Choice c;
             c.pipeline = pl;

@@ -700,24 +700,30 @@ bool gemm_variant_supported(int v, int layout) { return v < rf_first_variant() |
 // variant, both layouts, palette-direct and BF16 weights):
 //   stored [N][K]: VALU GEMV up to 4 rows, register-fed MFMA (two row tiles
 //     per wave) up to 32, then LDS tiles 64x128 up to 64, 128x128 up to 512,
-//     256x256 beyond;
+//     256x256 beyond when its tiles cover every CU (else 128x128: 8B gate at
+//     1024 rows 149 vs 235 us);
 //   stored [K][N]: VALU GEMV for one row, then LDS tiles 32x256 up to 32,
 //     64x128 up to 64, 128x256 up to 192, 256x256 beyond.
-// Tile indices are those of gemm_mfma.hip (variant = 2 + index).
+// The 256x256 tile runs with eight waves (two per SIMD) for palette weights,
+// whose rebuild then issues beside the other wave's MFMAs (70B gate,
+// palette-direct, 1024 rows: 737 -> 602 us); BF16 and exponent weights gain
+// nothing from it.  Tile indices are those of gemm_mfma.hip (variant = 2 + index).
 static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg) {
   if (cfg && cfg->variant > 0 && cfg->variant <= gemm_variant_count()) return cfg->variant;
+  const int big = fmt_is_pal(w.fmt) ? 2 + 7 : 2 + 4;
   if (w.layout == 0) {
     if (batch <= 4) return 1;
     if (batch <= 32 && mfma_rf_supported(w, 0)) return rf_first_variant();
     if (batch <= 64) return 2 + 0;
     if (batch <= 512) return 2 + 1;
-    return 2 + 4;
+    const int64_t tiles = (int64_t)((w.n + 255) / 256) * ((batch + 255) / 256);
+    return tiles >= (int64_t)device_cus() ? big : 2 + 1;
   }
   if (batch == 1) return 1;
   if (batch <= 32) return 2 + 6;
   if (batch <= 64) return 2 + 0;
   if (batch <= 192) return 2 + 2;
-  return 2 + 4;
+  return big;
 }
 
 // One launch for a group of stored [N][K] matrices with the same K and x

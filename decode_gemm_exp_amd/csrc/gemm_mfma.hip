@@ -9,7 +9,7 @@
 // HBM.  Section "Llama 3.1 8B測試結果" names the cost this design has to hide:
 // every weight tile is rebuilt once per tile of batch rows.
 //
-// Structure (256 threads, 4 waves in a WGM x WGN grid, tile BM x BN, K step 64):
+// Structure (4 or 8 waves in a WGM x WGN grid, tile BM x BN, K step 64):
 //   * the x tile and the rebuilt weight tile live in LDS, double buffered,
 //     one barrier per step;
 //   * step s: the waves run the MFMAs of step s from one buffer while, in the
@@ -127,15 +127,18 @@ constexpr int w_ld() { return LAYOUT == 0 ? kLDK : BN + 16; }   // KN rows: BN +
 template <int LAYOUT, int BN>
 constexpr int w_tile_elems() { return LAYOUT == 0 ? BN * kLDK : kBK * (BN + 16); }
 
-template <int LAYOUT, int FMT, int BM, int BN, int WGM>
-__global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __restrict__ x, int B,
-                                               float* __restrict__ y, int64_t ldy, int64_t col0,
-                                               int64_t kslice, float* __restrict__ part, int ntiles, int mtiles) {
-  constexpr int WGN = 4 / WGM;
+// NW waves per block (4 or 8); with 8 two waves share each SIMD, so one
+// wave's rebuild arithmetic can issue while the other's MFMAs run.
+template <int LAYOUT, int FMT, int BM, int BN, int WGM, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void k_mfma2(WeightView w, const uint16_t* __restrict__ x, int B,
+                                                   float* __restrict__ y, int64_t ldy, int64_t col0,
+                                                   int64_t kslice, float* __restrict__ part, int ntiles, int mtiles) {
+  constexpr int NT = 64 * NW;
+  constexpr int WGN = NW / WGM;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int XC = BM * 8 / 256;     // 16-byte x chunks per thread per step
-  constexpr int WC = BN * 4 / 256;     // 16-weight chunks per thread per step
+  constexpr int XC = BM * 8 / NT;      // 16-byte x chunks per thread per step
+  constexpr int WC = BN * 4 / NT;      // 16-weight chunks per thread per step
   constexpr int LDW = w_ld<LAYOUT, BN>();
   constexpr int XS = BM * kLDK, WS = w_tile_elems<LAYOUT, BN>();
   constexpr int kValuPerMfma = FMT == kFmtBf16 ? 1 : 4;
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
   // chunk c of this thread (i-th): NK -> row r = c / 4, k sub-block q = c % 4;
   // KN -> k row kr = c / (BN/16), n sub-block q = c % (BN/16)
   auto chunk_el = [&](int i, int64_t k0, bool& valid) __attribute__((always_inline)) -> uint64_t {
-    const int c = tid + i * 256;
+    const int c = tid + i * NT;
     if constexpr (LAYOUT == 0) {
       const int64_t n = n0 + (c >> 2), k = k0 + (c & 3) * 16;
       valid = n < N && k < ke;
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
       if (!in_part(i, XC, part)) continue;
       // rows past the batch are never stored and k past the slice meets zeroed
       // weight rows, so x needs only a clamped (always valid) address
-      const int c = tid + i * 256;
+      const int c = tid + i * NT;
       const int64_t row0 = m0 + (c >> 3), kk0 = k0 + (c & 7) * 8;
       const int64_t row = row0 < B ? row0 : B - 1, kk = kk0 < K ? kk0 : K - 8;
       const uint4 t = *reinterpret_cast<const uint4*>(x + row * K + kk);
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
       if constexpr (LAYOUT == 0) {
         wval[i] = true;
       } else {
-        wval[i] = k0 + (int64_t)((tid + i * 256) / (BN / 16)) < ke;
+        wval[i] = k0 + (int64_t)((tid + i * NT) / (BN / 16)) < ke;
       }
       wverb[i] = fmt_is_pal(FMT) && v && group_verbatim(fw_a[i], el >> 6);
       whi[i] = (el & 16) != 0;
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
 #pragma unroll
     for (int i = 0; i < XC; ++i) {
       if (!in_part(i, XC, part)) continue;
-      const int c = tid + i * 256;
+      const int c = tid + i * NT;
       *reinterpret_cast<uint4*>(&xs[(c >> 3) * kLDK + (c & 7) * 8]) = xr[i];
     }
 #pragma unroll
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(256) void k_mfma2(WeightView w, const uint16_t* __r
       if (!in_part(i, WC, part)) continue;
       uint32_t o[8];
       rebuild_raw<FMT>(w, wr[i], wval[i], wverb[i], whi[i], o);
-      const int c = tid + i * 256;
+      const int c = tid + i * NT;
       uint4* d;
       if constexpr (LAYOUT == 0) {
         d = reinterpret_cast<uint4*>(&ws[(c >> 2) * kLDK + (c & 3) * 16]);
@@ -366,7 +369,8 @@ Mfma2Fn pick(int tile) {
     case 3: return k_mfma2<L, F, 256, 128, 2>;
     case 4: return k_mfma2<L, F, 256, 256, 2>;
     case 5: return k_mfma2<L, F, 32, 128, 1>;
-    default: return k_mfma2<L, F, 32, 256, 1>;
+    case 6: return k_mfma2<L, F, 32, 256, 1>;
+    default: return k_mfma2<L, F, 256, 256, 2, 8>;
   }
 }
 
@@ -374,12 +378,13 @@ Mfma2Fn pick(int tile) {
 
 // Tiles of the big-tile kernel: {BM, BN}.
 struct Tile2 {
-  int bm, bn;
+  int bm, bn, waves;
 };
-// the last two (one 32-row MFMA tile, four waves side by side) are for small batches
-static const Tile2 kTiles2[] = {{64, 128}, {128, 128}, {128, 256}, {256, 128}, {256, 256}, {32, 128}, {32, 256}};
+// 32-row tiles (one MFMA row tile, four waves side by side) are for small
+// batches; the last is 256x256 with eight waves (two per SIMD)
+static const Tile2 kTiles2[] = {{64, 128, 4},  {128, 128, 4}, {128, 256, 4}, {256, 128, 4},
+                                {256, 256, 4}, {32, 128, 4},  {32, 256, 4},  {256, 256, 8}};
 int mfma2_tile_count() { return (int)(sizeof(kTiles2) / sizeof(kTiles2[0])); }
-int mfma2_small_tile_first() { return 5; }
 void mfma2_tile_dims(int tile, int* bm, int* bn) {
   *bm = kTiles2[tile].bm;
   *bn = kTiles2[tile].bn;
@@ -432,8 +437,8 @@ hipError_t launch_mfma2(const WeightView& w, const uint16_t* x, int64_t batch, f
   const int ntiles = (int)((w.n + (uint64_t)t.bn - 1) / (uint64_t)t.bn);
   const int mtiles = (int)((batch + t.bm - 1) / t.bm);
   dim3 grid((unsigned)(ntiles * mtiles), 1, (unsigned)slices);
-  hipLaunchKernelGGL(f, grid, dim3(256), lds, s, w, x, (int)batch, y, ldy, col0, kslice, split ? part : nullptr, ntiles,
-                     mtiles);
+  hipLaunchKernelGGL(f, grid, dim3(64 * t.waves), lds, s, w, x, (int)batch, y, ldy, col0, kslice, split ? part : nullptr,
+                     ntiles, mtiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   return launch_sum_slices(part, slices, w.n, batch, y, ldy, col0, s);

@@ -137,7 +137,6 @@ hipError_t launch_sum_slices(const float* part, int slices, uint64_t n, int64_t 
                              int64_t col0, hipStream_t s);
 // gemm_mfma.hip
 int mfma2_tile_count();
-int mfma2_small_tile_first();   // index of the first 32-row tile
 void mfma2_tile_dims(int tile, int* bm, int* bn);
 int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint);
 size_t mfma2_partial_elems(const WeightView& w, int64_t batch, int tile, int split_hint);
