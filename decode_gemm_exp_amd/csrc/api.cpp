@@ -21,6 +21,18 @@
 
 using namespace uw;
 
+int uw::device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cached[dev] = c;
+  }
+  return cached[dev];
+}
+
 hipError_t uw::allow_dynamic_lds(const void* kernel, int bytes) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -148,7 +160,7 @@ void pal_words(const Tables& t, PalView* out) {
 }
 
 uw_status upload_lut(uw_matrix* m, hipStream_t s) {
-  std::vector<uint32_t> lut(1u << kLutBits);
+  std::vector<uint32_t> lut((size_t)kLutWords << kLutBits);
   build_decode_lut(m->t, lut.data());
   if (!m->lut) UW_CHECK(dev_alloc(&m->lut, lut.size() * 4));
   UW_HIP(hipMemcpyAsync(m->lut, lut.data(), lut.size() * 4, hipMemcpyHostToDevice, s));

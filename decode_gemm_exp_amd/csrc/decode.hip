@@ -5,8 +5,8 @@
 // [EVC] = "Cloudflare推出Unweight無損壓縮系統，將LLM模型大小壓縮15-22%"
 // (easyvibecoding.app/curated/736): section "四種執行管道" defines the
 // three preprocessing outputs; section "解壓與運算資源共享" gives the
-// decoder a 16 KB lookup table in on-chip memory, which is what this kernel
-// keeps in LDS (4096 x 32-bit entries).
+// decoder a 16 KB lookup table in on-chip memory; this kernel keeps a 32 KB
+// one in LDS (4096 two-word entries, up to eight codewords per window).
 //
 // Work split.  One lane owns one segment (seg_groups consecutive groups whose
 // codes start on a word boundary), so every lane knows where its output goes
@@ -17,7 +17,7 @@
 // past the stream return zero instead of faulting), so a chunk is requested
 // about 8 words before it is needed.  Each step refills 32 bits if fewer than
 // 24 remain and then looks up two 12-bit windows in the LDS table; an entry
-// gives up to six whole codewords (their palette slots as nibbles) and their
+// gives up to eight whole codewords (their palette slots as nibbles) and their
 // total length.  Slots accumulate in a 16-nibble register and leave 8 at a
 // time into the wave's LDS stage.  A lane decodes all coded groups of a round
 // (up to 8 groups) in one loop, so lanes only meet at the end of a round.
@@ -88,7 +88,7 @@ __device__ __forceinline__ uint32_t stage_at(uint32_t f, uint32_t L) { return f 
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void k_decode_direct(DecodeArgs a) {
-  __shared__ uint32_t lut[1 << kLutBits];
+  __shared__ uint2 lut[1 << kLutBits];
   __shared__ uint32_t stage_all[kWaves][64 * kStageWords];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t* stage = stage_all[wave];
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_direct(DecodeArgs a) {
   uint4 q1 = load_chunk(rs, cw + 4);
   uint4 q2 = load_chunk(rs, cw + 8);
 
-  for (int i = threadIdx.x; i < (1 << kLutBits); i += kThreads) lut[i] = a.lut[i];
+  for (int i = threadIdx.x; i < (1 << kLutBits); i += kThreads) lut[i] = reinterpret_cast<const uint2*>(a.lut)[i];
   __syncthreads();
 
   uint64_t buf = 0;
@@ -168,13 +168,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_direct(DecodeArgs a) {
       if (avail < 24) refill();
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const uint32_t e = lut[(uint32_t)(buf >> (64 - kLutBits))];
-        uint32_t cnt = e & 7u, nb = (e >> 4) & 15u, syms = e >> 8;
+        const uint2 e = lut[(uint32_t)(buf >> (64 - kLutBits))];
+        uint32_t cnt = ((e.x >> 8) & 0xFFu) >> 2, nb = e.x & 0xFFu, syms = e.y;
         if (f >= ftarget) {   // second lookup after the round is complete: discard it
           cnt = 0;
           nb = 0;
           syms = 0;
-        } else if (e & 8u) {   // no codeword starts here: corrupt stream (entry still advances)
+        } else if (e.x & kLutInvalid) {   // no codeword starts here: corrupt stream (entry still advances)
           bad = true;
         }
         buf <<= nb;
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_direct(DecodeArgs a) {
 // is read from LDS one refill ahead.  Rounds are CH groups (1 or 2) and the
 // global loads that the copy-out needs (sign+mantissa bytes for the BF16
 // rebuild, exponents of verbatim groups) are issued before the round's decode
-// loop so that the loop hides their latency.  LDS per block: the 16 KB table
+// loop so that the loop hides their latency.  LDS per block: the 32 KB table
 // (static), then per wave a 64 x (8 CH + 1)-word stage and a wave_span-word
 // stream copy (dynamic).  The host picks CH and the waves per block that keep
 // the most waves resident under the 160 KB LDS of a CU.
@@ -283,13 +283,16 @@ __global__ __launch_bounds__(kThreads) void k_decode_direct(DecodeArgs a) {
 // stride spreads lanes over the LDS banks
 template <int CH>
 constexpr uint32_t staged_stride() { return 8u * CH + 1u; }
-constexpr uint32_t kStagedMaxThreads = 512;
+// Largest block: sixteen waves for one-group rounds (their kernels fit the
+// 128 registers a wave then gets), eight for two-group rounds.
+template <int CH>
+constexpr uint32_t staged_max_threads() { return CH == 1 ? 1024u : 512u; }
 
 template <int MODE, int CH, bool RUN, bool NT>
-__global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs a) {
+__global__ __launch_bounds__(staged_max_threads<CH>()) void k_decode_staged(DecodeArgs a) {
   constexpr uint32_t kStagedStride = staged_stride<CH>();
   constexpr uint32_t kStagedStage = 64 * kStagedStride;
-  __shared__ __attribute__((aligned(16))) uint32_t lut[1 << kLutBits];
+  __shared__ __attribute__((aligned(16))) uint2 lut[1 << kLutBits];
   extern __shared__ uint32_t dyn[];
   const int lane = threadIdx.x & 63, wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t span = (a.wave_span + 8u + 3u) & ~3u;   // + read slack, 16-byte multiple
@@ -346,26 +349,30 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
     const uint4 v = load_chunk(rs, ws0 + i);
     *reinterpret_cast<uint4*>(&sbuf[i]) = v;
   }
-  for (int i = threadIdx.x; i < (1 << kLutBits) / 4; i += (int)blockDim.x)
+  for (int i = threadIdx.x; i < (int)(kLutBytes / 16u); i += (int)blockDim.x)
     reinterpret_cast<uint4*>(lut)[i] = reinterpret_cast<const uint4*>(a.lut)[i];
   __syncthreads();
   if (!wval) return;
 
-  uint32_t p = sval ? w0 - ws0 : 0u;   // next LDS word to shift into the buffer
+  const uint32_t p0 = sval ? w0 - ws0 : 0u;
+  uint32_t p = p0;   // next LDS word to shift into the buffer
   uint64_t buf = ((uint64_t)sbuf[p] << 32) | (uint64_t)sbuf[p + 1];
   p += 2;
   uint32_t nw = sbuf[p];
   int avail = 64;
-  uint32_t words_in = 2;
-  uint32_t flags = 0;     // OR of all table entries used: bit 3 = invalid codeword
+  uint32_t flags = 0;     // OR of the first words of all table entries used
   uint64_t acc = 0;
   uint32_t sh4 = 0;       // 4 x pending nibbles in acc
+  // Takes the next word when fewer than 24 bits are buffered (enough for two
+  // lookups).  Selects instead of a branch: the lanes of a wave need words at
+  // different times, and a branch would run the refill under an exec mask
+  // almost every time anyway.
   auto refill = [&]() {
-    buf |= (uint64_t)nw << (32 - avail);
-    avail += 32;
-    ++words_in;
-    ++p;
-    nw = sbuf[p < span ? p : span - 1u];   // a corrupt stream cannot read past the copy
+    const bool need = avail < 24;
+    buf |= (uint64_t)(need ? nw : 0u) << ((uint32_t)(32 - avail) & 63u);
+    avail += need ? 32 : 0;
+    p += need ? 1u : 0u;
+    nw = sbuf[min(p, span - 1u)];   // a corrupt stream cannot read past the copy
   };
   uint32_t coded_groups = 0;
   const PalView pal = a.pal;
@@ -448,33 +455,35 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
     }
 
     // ---- decode every coded group of the round (LDS only) ----
-    // one lookup: the entry's codewords join the nibble accumulator, whose
-    // low 8 nibbles go to the stage once complete
-    uint32_t f = 0;
-    uint32_t* my = stage + (uint32_t)lane * kStagedStride;
+    // One lookup: the entry's slots join the nibble accumulator and its low
+    // word is written to the lane's current stage word; once 32 bits are
+    // pending the write was the complete word and the pointer moves on.
+    // Straight-line, so lanes never wait on each other's branches.
+    uint32_t* wp = stage + (uint32_t)lane * kStagedStride;
+    uint32_t* const wend = wp + ftarget;
+    uint32_t* const wlast = wend - 1;
     auto lookup = [&]() {
-      const uint32_t e = lut[(uint32_t)(buf >> (64 - kLutBits))];
-      const uint32_t nb = (e >> 4) & 15u;
-      flags |= e;
-      buf <<= nb;
-      avail -= (int)nb;
-      acc |= (uint64_t)(e >> 8) << sh4;
-      sh4 += 4u * (e & 7u);
-      if (sh4 >= 32u) {
-        my[f++] = (uint32_t)acc;
-        acc >>= 32;
-        sh4 -= 32u;
-      }
+      const uint2 e = lut[(uint32_t)(buf >> (64 - kLutBits))];
+      flags |= e.x;
+      buf <<= (e.x & 63u);
+      avail -= (int)(e.x & 0xFFu);
+      acc |= (uint64_t)e.y << sh4;
+      sh4 += (e.x >> 8) & 0xFFu;
+      *wp = (uint32_t)acc;
+      const uint32_t full = sh4 & 32u;
+      acc >>= full;
+      sh4 -= full;
+      wp += full >> 5;
     };
     // two lookups per refill while at least two stage words remain (each
     // lookup completes at most one word), then single lookups
-    while (f + 1 < ftarget) {
-      if (avail < 24) refill();
+    while (wp < wlast) {
+      refill();
       lookup();
       lookup();
     }
-    while (f < ftarget) {
-      if (avail < 24) refill();
+    while (wp < wend) {
+      refill();
       lookup();
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -523,11 +532,12 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
     __builtin_amdgcn_wave_barrier();
   }
 
-  bool bad = (flags & 8u) != 0;
+  bool bad = (flags & kLutInvalid) != 0;
   if (sval) {
     uint32_t left_bits = 0;
     for (uint32_t i = 0; i < sh4 / 4u; ++i)
       left_bits += (uint32_t)((a.len_pack >> (4 * ((acc >> (4 * i)) & 15u))) & 15u);
+    const uint32_t words_in = p - p0;
     const uint32_t used = 32u * words_in - (uint32_t)avail - left_bits;
     const uint32_t words = w1 - w0;
     if (coded_groups == 0) {
@@ -540,7 +550,7 @@ __global__ __launch_bounds__(kStagedMaxThreads) void k_decode_staged(DecodeArgs 
 }
 
 constexpr uint32_t kMaxLds = 160u * 1024u;                      // per workgroup on gfx950
-constexpr uint32_t kMaxDynLds = kMaxLds - 4u * (1u << kLutBits);  // the table is static
+constexpr uint32_t kMaxDynLds = kMaxLds - kLutBytes;  // the table is static
 
 // dynamic LDS of the staged kernel per wave (the table is static)
 template <int CH>
@@ -548,25 +558,43 @@ uint32_t staged_wave_bytes(const DecodeArgs& a) {
   return 4u * (64u * staged_stride<CH>() + ((a.wave_span + 8u + 3u) & ~3u));
 }
 
-// waves per block that keep the most waves resident per CU (LDS-limited,
-// at most 16 per CU), and that count; 0 waves if one wave does not fit
+// Waves per block.  Every block copies the table, so on a small grid larger
+// blocks leave CUs idle and on a large one smaller blocks spend LDS on copies
+// of the table that could hold more waves.  The choice minimises the most
+// waves any CU runs over the launch (blocks are dealt to CUs in turn), then
+// maximises the waves a CU holds at once (LDS permitting; at most 16, and 8
+// for two-group rounds, whose full-decode kernel takes about 200 registers),
+// then takes the smaller block.  0 waves if one wave does not fit.
+struct StagedShape {
+  uint32_t wpb = 0;        // waves per block
+  uint64_t load = 0;       // most waves one CU runs
+  uint32_t resident = 0;   // waves a CU holds at once
+};
+
 template <int CH>
-void staged_shape(const DecodeArgs& a, uint32_t* wpb_out, uint32_t* resident_out) {
+StagedShape staged_shape(const DecodeArgs& a) {
   const uint32_t per_wave = staged_wave_bytes<CH>(a);
-  uint32_t best_w = 0, best_res = 0;
-  for (uint32_t wpb = 1; wpb <= kStagedMaxThreads / 64; ++wpb) {
+  const uint64_t waves = (a.segments + 63u) / 64u;
+  const uint64_t cus = (uint64_t)device_cus();
+  StagedShape best;
+  for (uint32_t wpb = 1; wpb <= staged_max_threads<CH>() / 64u; ++wpb) {
     const uint32_t dyn = wpb * per_wave;
     if (dyn > kMaxDynLds) break;
-    const uint32_t blocks = kMaxLds / (dyn + 4u * (1u << kLutBits));
-    uint32_t res = blocks * wpb;
-    if (res > 16) res = 16;
-    if (res > best_res) {   // ties keep the smaller block: more blocks balance better over CUs
-      best_res = res;
-      best_w = wpb;
+    uint32_t per_cu = kMaxLds / (dyn + kLutBytes);   // blocks a CU holds at once
+    constexpr uint32_t cap = CH == 1 ? 16u : 8u;
+    if (per_cu * wpb > cap) per_cu = cap / wpb;
+    if (per_cu == 0) break;
+    const uint64_t blocks = (waves + wpb - 1) / wpb;
+    const uint64_t rounds = (blocks + cus - 1) / cus;   // blocks dealt to the busiest CU
+    const uint64_t load = rounds * wpb;
+    const uint32_t resident = (uint32_t)((rounds < per_cu ? rounds : per_cu) * wpb);
+    if (best.wpb == 0 || load < best.load || (load == best.load && resident > best.resident)) {
+      best.wpb = wpb;
+      best.load = load;
+      best.resident = resident;
     }
   }
-  *wpb_out = best_w;
-  *resident_out = best_res;
+  return best;
 }
 
 template <int MODE, int CH, bool RUN, bool NT>
@@ -602,12 +630,12 @@ template <int MODE>
 hipError_t launch_mode(const DecodeArgs& a, uint32_t blocks, hipStream_t s) {
   const char* force = std::getenv("UW_DECODE_DIRECT");   // selects the fallback kernel (tests)
   if (a.wave_span > 0 && a.vexp_bytes <= kRecordsMax && !(force && force[0] == '1')) {
-    // rounds of two groups where that keeps as many waves resident as rounds of one
-    uint32_t w1 = 0, r1 = 0, w2 = 0, r2 = 0;
-    staged_shape<1>(a, &w1, &r1);
-    if (a.seg_groups >= 2) staged_shape<2>(a, &w2, &r2);
-    if (r2 > 0 && r2 >= r1) return launch_staged<MODE, 2>(a, w2, s);
-    if (r1 > 0) return launch_staged<MODE, 1>(a, w1, s);
+    // rounds of two groups where that spreads the waves as well as rounds of one
+    const StagedShape s1 = staged_shape<1>(a);
+    const StagedShape s2 = a.seg_groups >= 2 ? staged_shape<2>(a) : StagedShape{};
+    if (s2.wpb > 0 && (s1.wpb == 0 || (s2.load <= s1.load && s2.resident >= s1.resident)))
+      return launch_staged<MODE, 2>(a, s2.wpb, s);
+    if (s1.wpb > 0) return launch_staged<MODE, 1>(a, s1.wpb, s);
   }
   hipLaunchKernelGGL(k_decode_direct<MODE>, dim3(blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();

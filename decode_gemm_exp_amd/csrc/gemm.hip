@@ -566,17 +566,6 @@ GemvKnFn gemv_kn_fn(int nb, uint64_t n) {
 constexpr int kGemvMaxBatch = 8;
 constexpr size_t kNkLdsMax = 160 * 1024;
 
-int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int c = 0;
-    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
-    cached[dev] = c;
-  }
-  return cached[dev];
-}
 
 // chunks per lane per step of the pipelined NK GEMV (0: shape not covered)
 int nk_pipe_u(const WeightView& w, int nb) {

@@ -108,16 +108,16 @@ void assign_codes(Tables& t) {
 }
 
 // Decoder table: entry v describes the 12-bit window v (first stream bit =
-// bit 11): bits 0-2 how many whole codewords it starts with (up to 6), bits
-// 4-7 how many bits they take, bits 8-31 their slots as nibbles.  A window
-// that starts with no valid codeword (possible only with a one-symbol code)
-// gets count 1, length 1, no slots and bit 3 set, so decoders always make
+// bit 11): the whole codewords it starts with (up to 8), the bits they take
+// and their slots, in the two-word layout of kLutWords.  A window that starts
+// with no valid codeword (possible only with a one-symbol code) gets one
+// codeword of one bit, slot 0 and the invalid bit, so decoders always make
 // progress and can OR the entries to detect corruption.
 void build_decode_lut(const Tables& t, uint32_t* lut) {
   for (uint32_t v = 0; v < (1u << kLutBits); ++v) {
     int pos = 0, cnt = 0;
     uint32_t syms = 0;
-    while (cnt < 6) {
+    while (cnt < 8) {
       int found = -1, flen = 0;
       for (int s = 0; s < kPal && found < 0; ++s) {
         int l = t.code_len[s];
@@ -133,7 +133,13 @@ void build_decode_lut(const Tables& t, uint32_t* lut) {
       pos += flen;
       ++cnt;
     }
-    lut[v] = cnt == 0 ? (1u | 8u | (1u << 4)) : ((uint32_t)cnt | ((uint32_t)pos << 4) | (syms << 8));
+    if (cnt == 0) {
+      lut[2 * v] = 1u | (4u << 8) | kLutInvalid;
+      lut[2 * v + 1] = 0;
+    } else {
+      lut[2 * v] = (uint32_t)pos | ((uint32_t)(4 * cnt) << 8);
+      lut[2 * v + 1] = syms;
+    }
   }
 }
 

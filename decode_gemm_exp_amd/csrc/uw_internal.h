@@ -13,7 +13,16 @@ namespace uw {
 constexpr int kGroup = 64;        // weights per verbatim decision
 constexpr int kPal = 16;          // palette entries
 constexpr int kMaxLen = 12;       // longest codeword
-constexpr int kLutBits = 12;      // decode table index width (4096 entries, 16 KB)
+constexpr int kLutBits = 12;      // decode table index width (4096 entries)
+// Decode table entry for a 12-bit window, two words:
+//   word 0: bits 0-4 the bits its whole codewords take (bit 5 clear, so a
+//           64-bit shift can take the word as its count), bits 8-15 four
+//           times the codeword count (up to 8), bit 16 set when no codeword
+//           starts in the window (a one-symbol code only);
+//   word 1: the codewords' slots as nibbles, first codeword lowest.
+constexpr int kLutWords = 2;
+constexpr uint32_t kLutBytes = 4u * kLutWords << kLutBits;   // 32 KB
+constexpr uint32_t kLutInvalid = 1u << 16;
 constexpr uint64_t kHeaderBytes = 2304;
 
 // Host-side tables of one matrix (all tiny).
@@ -43,7 +52,7 @@ struct uw_matrix {
   uint8_t* vexp = nullptr;        // 64 * V (may be null when V == 0)
   uint32_t* seg_off = nullptr;    // segments + 1
   uint32_t* stream = nullptr;     // W + 2
-  uint32_t* lut = nullptr;        // 4096 decode entries
+  uint32_t* lut = nullptr;        // 4096 decode entries of kLutWords words
   uint8_t* pidx = nullptr;        // resident palette indices (numel / 2) or null
   int* corrupt = nullptr;         // device flag set by decoders
   uint32_t wave_span = 0;         // most stream words any 64-segment wave covers (from a 4-word boundary)
@@ -55,7 +64,10 @@ namespace uw {
 void choose_palette(Tables& t);                        // from t.hist
 bool limited_lengths(const uint64_t* w, int n, int lmax, uint8_t* len);
 void assign_codes(Tables& t);                          // from code_len
-void build_decode_lut(const Tables& t, uint32_t* lut4096);
+void build_decode_lut(const Tables& t, uint32_t* lut);   // kLutWords << kLutBits words
+
+// Compute units of the current device (256 if the query fails).
+int device_cus();
 
 // Raise a kernel's dynamic LDS limit to `bytes` on the current device, once
 // per (kernel, device, size); thread safe (api.cpp).
