@@ -394,6 +394,21 @@ __global__ __launch_bounds__(staged_max_threads<CH>()) void k_decode_staged(Deco
     svn[u] = make_uint4(0, 0, 0, 0);
     exn[u] = make_uint4(0, 0, 0, 0);
   }
+  // Transcode with one-group rounds: a group's slots are a quarter of a
+  // 128-byte line whose other quarters come in the owner's next rounds.
+  // Stored round by round, L2 sometimes wrote the line back between rounds
+  // (twice the bytes, depending on how blocks fell on the XCDs).  When
+  // segments are whole lines (groups per segment a multiple of 4) the quarter
+  // is the round mod 4 for every owner, so each step keeps its quarters in
+  // fixed registers and stores the four back to back in the line's last
+  // round (or the segment's last, for a short final segment).
+  constexpr int HOLD = MODE == kDecodeNibble && CH == 1 ? 3 : 1;
+  const bool whole_lines = (SG & 3u) == 0;
+  uint2 held[STEPS][HOLD];
+#pragma unroll
+  for (int u = 0; u < STEPS; ++u)
+#pragma unroll
+    for (int h = 0; h < HOLD; ++h) held[u][h] = make_uint2(0, 0);
 
   // Copy-out step u of a lane serves the same owner lane in every round, so
   // the owner's verbatim flags, first rank and group count are fetched once
@@ -508,7 +523,25 @@ __global__ __launch_bounds__(staged_max_threads<CH>()) void k_decode_staged(Deco
         ex.w = verb ? ev[u].w : pe.w;
       }
       const uint32_t rel = (uint32_t)(el[u] - wel0);   // weights past the wave's first (when ok)
-      if constexpr (MODE == kDecodeNibble) {
+      if constexpr (MODE == kDecodeNibble && CH == 1) {
+        if (whole_lines) {
+          const uint32_t q = r & 3u;   // the group's quarter of its line, the same for every owner
+          // no loads in this mode's rounds, so branching around stores costs no waits
+          if (ok && (q == 3u || r + 1u >= ong[u])) {
+            const uint32_t b = rel / 2u;   // quarter i of the line sits at b - 32 (q - i)
+            buf_store8(ro, q >= 1u ? b - 32u * q : kPastEnd, held[u][0].x, held[u][0].y);
+            buf_store8(ro, q >= 2u ? b - 32u * (q - 1u) : kPastEnd, held[u][1].x, held[u][1].y);
+            buf_store8(ro, q >= 3u ? b - 32u : kPastEnd, held[u][2].x, held[u][2].y);
+            buf_store8(ro, b, ex.x, ex.y);
+          }
+          // fixed registers: q is uniform, so these are scalar-conditioned moves
+          if (q == 0u) held[u][0] = make_uint2(ex.x, ex.y);
+          if (q == 1u) held[u][1] = make_uint2(ex.x, ex.y);
+          if (q == 2u) held[u][2] = make_uint2(ex.x, ex.y);
+        } else {
+          buf_store8(ro, ok ? rel / 2u : kPastEnd, ex.x, ex.y);
+        }
+      } else if constexpr (MODE == kDecodeNibble) {
         buf_store8(ro, ok ? rel / 2u : kPastEnd, ex.x, ex.y);
       } else if constexpr (MODE == kDecodeExponent) {
         if constexpr (CH == 1)   // the other half of this line, from the previous round
