@@ -12,7 +12,11 @@ Recipe (all draws from ``torch.Generator`` seeded per tensor):
   * outliers: exactly round(frac * numel) distinct positions (a random
     permutation prefix), multiplied by 2**shift -- exact in bf16 for normal
     values, so the outlier keeps its mantissa and gains ``shift`` in exponent;
-  * x = bf16(N(0,1)).
+  * x = bf16(N(0,1));
+  * FP8 weights (the already-quantised case): N(0, sigma) in fp32 scaled per
+    tensor by 448 / max|w| (448 = the largest finite E4M3 value, the usual
+    per-tensor FP8 checkpoint scale) and converted by torch to E4M3
+    (round to nearest even), returned as raw bytes.
 """
 from __future__ import annotations
 
@@ -98,6 +102,16 @@ def weights(rows: int, cols: int, sigma: float = 0.02, outlier_frac: float = 0.0
         flat = w.view(-1)
         flat[idx] = flat[idx] * float(2 ** outlier_shift)
     return w.to(torch.bfloat16)
+
+
+def fp8_weights(rows: int, cols: int, sigma: float = 0.02, seed: int = SEED_BASE, stream: int = 500,
+                device="cpu") -> torch.Tensor:
+    """uint8 tensor [rows][cols] of FP8 E4M3 bytes (the stored array)."""
+    g = _gen(seed, stream, device)
+    w = torch.randn(rows, cols, generator=g, device=device, dtype=torch.float32)
+    w.mul_(sigma)
+    w.mul_(448.0 / float(w.abs().max().clamp_min(1e-30)))
+    return w.to(torch.float8_e4m3fn).view(torch.uint8)
 
 
 def activations(batch: int, k: int, seed: int = SEED_BASE, stream: int = 1_000,

@@ -46,6 +46,9 @@ def lib():
         vp, u64, u32, i32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int
         L.uwo_compress.restype = vp
         L.uwo_compress.argtypes = [vp, u64, u64, u32, u32, ctypes.POINTER(i32)]
+        L.uwo_compress_fp8.restype = vp
+        L.uwo_compress_fp8.argtypes = [vp, u64, u64, u32, u32, ctypes.POINTER(i32)]
+        L.uwo_decode_fp8.argtypes = [vp, vp]
         L.uwo_free.argtypes = [vp]
         L.uwo_scalars.argtypes = [vp, vp]
         L.uwo_tables.argtypes = [vp, vp, vp, vp, vp, vp]
@@ -87,6 +90,7 @@ class Compressed:
     code: np.ndarray
     hist: np.ndarray
     coded_count: np.ndarray
+    fp8: bool = False
 
     def section(self, name: str) -> np.ndarray:
         ptr, nbytes = ctypes.c_void_p(), ctypes.c_uint64()
@@ -110,6 +114,12 @@ class Compressed:
         st = lib().uwo_decode_full(self.handle, _ptr(out))
         return st, out
 
+    def decode_fp8(self) -> tuple[int, np.ndarray]:
+        """UWF8 handles: the original E4M3 bytes."""
+        out = np.zeros(self.numel, dtype=np.uint8)
+        st = lib().uwo_decode_fp8(self.handle, _ptr(out))
+        return st, out
+
     def transcode(self) -> tuple[int, np.ndarray]:
         out = np.zeros(self.numel // 2, dtype=np.uint8)
         st = lib().uwo_transcode(self.handle, _ptr(out))
@@ -122,8 +132,10 @@ class Compressed:
         return buf.tobytes()
 
     def total_bytes(self, header: int = 2304) -> int:
-        """Compressed size: header plus the six sections, unpadded."""
-        return (header + self.numel + 8 * self.flag_words + 64 * self.V
+        """Compressed size: header plus the six sections, unpadded (the kept
+        section is one byte per weight for BF16, half a byte for FP8)."""
+        kept = self.numel // 2 if self.fp8 else self.numel
+        return (header + kept + 8 * self.flag_words + 64 * self.V
                 + 4 * (self.segments + 1) + 4 * (self.W + 2))
 
     def free(self) -> None:
@@ -146,6 +158,25 @@ def compress(w_stored: np.ndarray, seg_groups: int = 4, layout: int = 0) -> Comp
     h = lib().uwo_compress(_ptr(w), w.shape[0], w.shape[1], seg_groups, layout, ctypes.byref(st))
     if not h:
         raise ValueError(f"oracle compress failed with status {st.value}")
+    return _wrap(h)
+
+
+def compress_fp8(w_stored: np.ndarray, seg_groups: int = 4, layout: int = 0) -> Compressed:
+    """Compress the stored 2-D uint8 array of FP8 E4M3 bytes (UWF8 reading:
+    the exponent field coded as the BF16 exponent byte is, sign+mantissa
+    nibbles kept)."""
+    w = np.ascontiguousarray(w_stored, dtype=np.uint8)
+    assert w.ndim == 2
+    st = ctypes.c_int(0)
+    h = lib().uwo_compress_fp8(_ptr(w), w.shape[0], w.shape[1], seg_groups, layout, ctypes.byref(st))
+    if not h:
+        raise ValueError(f"oracle FP8 compress failed with status {st.value}")
+    c = _wrap(h)
+    c.fp8 = True
+    return c
+
+
+def _wrap(h) -> Compressed:
     sc = np.zeros(14, dtype=np.uint64)
     lib().uwo_scalars(h, _ptr(sc))
     pal = np.zeros(16, np.uint8)

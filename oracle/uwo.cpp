@@ -15,6 +15,9 @@
 //   [RFC1951] DEFLATE, section 3.2.2 (canonical Huffman code assignment).
 //   [LH90] Larmore & Hirschberg, "A fast algorithm for optimal length-limited
 //          Huffman codes", JACM 1990 (package-merge).
+//   [SP]   saidapartage.blog, "Cloudflare Unweight : -22 % sur le poids de vos
+//          LLM, sans perdre un bit", section "Un complément, pas un remplaçant".
+//   [OFP8] OCP 8-bit Floating Point Specification (OFP8), the E4M3 format.
 //
 // What the pages fix and what is a reading (the UWF1 encoding):
 //   * BF16 = 1 sign bit, 8 exponent bits, 7 mantissa bits; sign and mantissa
@@ -27,6 +30,14 @@
 //   * Everything else (byte packing of sign+mantissa, the length limit of the
 //     code, tie-breaks, bit order, segmenting) is the UWF1 reading documented
 //     alongside the library; this file is the executable statement of it.
+//
+// Already-quantised weights ([SP]; [GT] section "Open source"): the pages say
+// the coding also applies on top of quantisation and give no more.  The
+// reading here (UWF8) is the plainest one for FP8 E4M3 weights: the 4-bit
+// exponent field is the coded symbol, exactly as the BF16 exponent byte is,
+// and sign plus mantissa are kept as a 4-bit nibble.  E4M3 has at most 16
+// exponent values, so the palette always holds them all and no group is ever
+// verbatim.
 //
 // Parity pins for each function live in tests/test_oracle_*.py.
 
@@ -75,6 +86,7 @@ struct Oracle {
   std::vector<uint8_t> vexp;        // 64 raw exponents per verbatim group
   std::vector<uint32_t> seg_off;    // word offset of each segment, S+1 entries
   std::vector<uint32_t> stream;     // W + 2 words, MSB-first codes
+  bool fp8 = false;                 // UWF8: sm holds packed sign+mantissa nibbles
 };
 
 // ---- field split and rebuild ([EVC] "BF16權重壓縮原理") ----------------------
@@ -90,6 +102,22 @@ inline uint16_t rebuild(uint8_t sm, uint8_t e) {
   uint16_t sign = (uint16_t)((sm >> 7) & 1);
   uint16_t mant = (uint16_t)(sm & 0x7F);
   return (uint16_t)((sign << 15) | ((uint16_t)e << 7) | mant);
+}
+
+// ---- FP8 E4M3 field split and rebuild ([OFP8]; UWF8 reading) ---------------
+// sign = bit 7, exponent = bits 6..3, mantissa = bits 2..0.
+// UWF8 reading: the kept nibble is (sign << 3) | mantissa, two per byte, the
+// element with the even index in the low nibble.
+inline uint8_t fp8_exponent_of(uint8_t b) { return (uint8_t)((b >> 3) & 0xF); }
+inline uint8_t fp8_sign_mantissa_of(uint8_t b) {
+  uint8_t sign = (uint8_t)((b >> 7) & 1);
+  uint8_t mant = (uint8_t)(b & 0x7);
+  return (uint8_t)((sign << 3) | mant);
+}
+inline uint8_t fp8_rebuild(uint8_t smn, uint8_t e) {
+  uint8_t sign = (uint8_t)((smn >> 3) & 1);
+  uint8_t mant = (uint8_t)(smn & 0x7);
+  return (uint8_t)((sign << 7) | ((e & 0xF) << 3) | mant);
 }
 
 // ---- package-merge ([LH90]) --------------------------------------------------
@@ -370,10 +398,45 @@ int decode_exponents(const Oracle& o, uint8_t* e_out) {
 }
 
 int decode_full(const Oracle& o, uint16_t* w_out) {
+  if (o.fp8) return UWO_ERR_UNSUPPORTED;
   std::vector<uint8_t> e(o.numel);
   int st = decode_exponents(o, e.data());
   if (st != UWO_OK) return st;
   for (uint64_t i = 0; i < o.numel; ++i) w_out[i] = rebuild(o.sm[i], e[i]);
+  return UWO_OK;
+}
+
+// UWF8: the same coding applied to the E4M3 exponent field.  Each weight's
+// exponent field is placed where a BF16 exponent byte sits (sign and mantissa
+// bits left zero; the sign+mantissa section is replaced below), so the
+// histogram, palette, flags, code and stream are exactly those steps over the
+// field.  The kept section becomes the packed sign+mantissa nibbles.
+int compress_fp8(const uint8_t* w, uint64_t rows, uint64_t cols, uint32_t seg_groups,
+                 uint32_t layout, Oracle& o) {
+  if (w == nullptr || rows == 0 || cols == 0) return UWO_ERR_INVALID;
+  const uint64_t numel = rows * cols;
+  std::vector<uint16_t> field(numel);
+  for (uint64_t i = 0; i < numel; ++i) field[i] = (uint16_t)((uint16_t)fp8_exponent_of(w[i]) << 7);
+  int st = compress(field.data(), rows, cols, seg_groups, layout, o);
+  if (st != UWO_OK) return st;
+  o.sm.assign(numel / 2, 0);   // numel is a multiple of 64
+  for (uint64_t i = 0; i < numel; ++i) {
+    uint8_t nib = fp8_sign_mantissa_of(w[i]);
+    o.sm[i / 2] = (uint8_t)(o.sm[i / 2] | (i % 2 == 0 ? nib : (uint8_t)(nib << 4)));
+  }
+  o.fp8 = true;
+  return UWO_OK;
+}
+
+int decode_fp8(const Oracle& o, uint8_t* w_out) {
+  if (!o.fp8) return UWO_ERR_UNSUPPORTED;
+  std::vector<uint8_t> e(o.numel);
+  int st = decode_exponents(o, e.data());
+  if (st != UWO_OK) return st;
+  for (uint64_t i = 0; i < o.numel; ++i) {
+    uint8_t nib = (uint8_t)(i % 2 == 0 ? (o.sm[i / 2] & 0xF) : (o.sm[i / 2] >> 4));
+    w_out[i] = fp8_rebuild(nib, e[i]);
+  }
   return UWO_OK;
 }
 
@@ -469,6 +532,26 @@ void* uwo_compress(const uint16_t* w, uint64_t rows, uint64_t cols, uint32_t seg
   return o;
 }
 
+void* uwo_compress_fp8(const uint8_t* w, uint64_t rows, uint64_t cols, uint32_t seg_groups,
+                       uint32_t layout, int* status) {
+  Oracle* o = new (std::nothrow) Oracle();
+  if (o == nullptr) {
+    if (status) *status = UWO_ERR_NOMEM;
+    return nullptr;
+  }
+  int st = compress_fp8(w, rows, cols, seg_groups, layout, *o);
+  if (status) *status = st;
+  if (st != UWO_OK) {
+    delete o;
+    return nullptr;
+  }
+  return o;
+}
+
+int uwo_decode_fp8(const void* h, uint8_t* out) {
+  return decode_fp8(*static_cast<const Oracle*>(h), out);
+}
+
 void uwo_free(void* h) { delete static_cast<Oracle*>(h); }
 
 // scalars: rows, cols, numel, groups, segments, flag_words, seg_groups, layout,
@@ -533,6 +616,7 @@ int uwo_transcode(const void* h, uint8_t* out) {
 
 // Serialised UWF1 blob; cap == 0 returns the size only.
 uint64_t uwo_export(const void* h, uint8_t* buf, uint64_t cap) {
+  if (static_cast<const Oracle*>(h)->fp8) return 0;   // UWF1 is the BF16 format only
   std::vector<uint8_t> b = serialise(*static_cast<const Oracle*>(h));
   if (buf != nullptr && cap >= b.size()) std::memcpy(buf, b.data(), b.size());
   return b.size();
