@@ -168,8 +168,10 @@ uw_status upload_lut(uw_matrix* m, hipStream_t s) {
   return UW_OK;
 }
 
+uint64_t sm_bytes(const uw_matrix* m) { return m->fp8 ? m->numel / 2 : m->numel; }
+
 uint64_t compressed_bytes(const uw_matrix* m) {
-  return kHeaderBytes + m->numel + 8 * m->flag_words + 64 * m->V + 4 * (m->segments + 1) + 4 * (m->W + 2);
+  return kHeaderBytes + sm_bytes(m) + 8 * m->flag_words + 64 * m->V + 4 * (m->segments + 1) + 4 * (m->W + 2);
 }
 
 uint64_t export_bytes(const uw_matrix* m) {
@@ -308,6 +310,7 @@ size_t partial_bytes(const uw_matrix* m, int p, int64_t batch, const uw_kernel_c
 
 uw_status check_matmul_args(const uw_matrix* m, int p, const uint16_t* x, int64_t batch, const float* y) {
   if (!m || !x || !y || batch <= 0) return UW_ERR_INVALID;
+  if (m->fp8) return UW_ERR_UNSUPPORTED;   // the GEMMs rebuild BF16 weights
   if (p < UW_PIPE_FULL || p > UW_PIPE_PALETTE_DIRECT) return UW_ERR_INVALID;
   if (!aligned16(x) || (reinterpret_cast<uintptr_t>(y) & 3u)) return UW_ERR_INVALID;
   if (logical_k(m) % 8 != 0) return UW_ERR_UNSUPPORTED;
@@ -337,20 +340,30 @@ const char* uw_status_str(uw_status st) {
 
 uint32_t uw_version(void) { return (1u << 16) | 0u; }
 
-uw_status uw_compress(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout layout,
-                      const uw_compress_opts* opts, void* stream, uw_matrix** out) try {
+}  // extern "C"
+
+namespace {
+
+// Arguments shared by the BF16 and FP8 compress entry points.
+uw_status compress_args(const void* w_dev, int64_t n, int64_t k, uw_layout layout, const uw_compress_opts* opts,
+                        uw_matrix** out, uint32_t* sg, uint64_t* rows, uint64_t* cols) {
   if (!out) return UW_ERR_INVALID;
   *out = nullptr;
   if (!w_dev || n <= 0 || k <= 0 || (layout != UW_LAYOUT_NK && layout != UW_LAYOUT_KN)) return UW_ERR_INVALID;
   if (!aligned16(w_dev)) return UW_ERR_INVALID;
-  const uint32_t sg = (opts && opts->seg_groups) ? opts->seg_groups : 4u;
-  if (!valid_seg_groups(sg) || (opts && opts->flags)) return UW_ERR_INVALID;
-  const uint64_t rows = layout == UW_LAYOUT_NK ? (uint64_t)n : (uint64_t)k;
-  const uint64_t cols = layout == UW_LAYOUT_NK ? (uint64_t)k : (uint64_t)n;
-  if (cols % kGroup != 0) return UW_ERR_UNSUPPORTED;
-  if (rows * cols >= (1ull << 32)) return UW_ERR_UNSUPPORTED;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  *sg = (opts && opts->seg_groups) ? opts->seg_groups : 4u;
+  if (!valid_seg_groups(*sg) || (opts && opts->flags)) return UW_ERR_INVALID;
+  *rows = layout == UW_LAYOUT_NK ? (uint64_t)n : (uint64_t)k;
+  *cols = layout == UW_LAYOUT_NK ? (uint64_t)k : (uint64_t)n;
+  if (*cols % kGroup != 0) return UW_ERR_UNSUPPORTED;
+  if (*rows * *cols >= (1ull << 32)) return UW_ERR_UNSUPPORTED;
+  return UW_OK;
+}
 
+// The coding passes over a device array of 16-bit words whose bits 14..7
+// are the coded exponent (BF16 weights, or FP8 exponent fields placed there).
+uw_status compress_words(const uint16_t* w_dev, uint64_t rows, uint64_t cols, uw_layout layout, uint32_t sg,
+                         hipStream_t s, uw_matrix** out) {
   uw_matrix* m = new (std::nothrow) uw_matrix();
   if (!m) return UW_ERR_NOMEM;
   struct Guard {
@@ -449,6 +462,49 @@ uw_status uw_compress(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout lay
   guard.m = nullptr;
   *out = m;
   return UW_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+uw_status uw_compress(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout layout,
+                      const uw_compress_opts* opts, void* stream, uw_matrix** out) try {
+  uint32_t sg = 0;
+  uint64_t rows = 0, cols = 0;
+  UW_CHECK(compress_args(w_dev, n, k, layout, opts, out, &sg, &rows, &cols));
+  return compress_words(w_dev, rows, cols, layout, sg, static_cast<hipStream_t>(stream), out);
+} catch (...) {
+  return UW_ERR_NOMEM;
+}
+
+uw_status uw_compress_fp8(const uint8_t* w_dev, int64_t n, int64_t k, uw_layout layout,
+                          const uw_compress_opts* opts, void* stream, uw_matrix** out) try {
+  uint32_t sg = 0;
+  uint64_t rows = 0, cols = 0;
+  UW_CHECK(compress_args(w_dev, n, k, layout, opts, out, &sg, &rows, &cols));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint64_t numel = rows * cols;
+  struct Temp {
+    uint16_t* fields = nullptr;
+    uint8_t* nib = nullptr;
+    ~Temp() {
+      dev_free(fields);
+      dev_free(nib);
+    }
+  } t;
+  UW_CHECK(dev_alloc(&t.fields, 2 * numel));
+  UW_CHECK(dev_alloc(&t.nib, numel / 2));
+  UW_HIP(launch_fp8_fields(w_dev, numel, t.fields, s));
+  UW_HIP(launch_fp8_pack(w_dev, numel, t.nib, s));
+  uw_matrix* m = nullptr;
+  UW_CHECK(compress_words(t.fields, rows, cols, layout, sg, s, &m));   // synchronises at its end
+  dev_free(m->sm);   // the byte section of the field array: replaced by the nibbles
+  m->sm = t.nib;
+  t.nib = nullptr;
+  m->fp8 = true;
+  *out = m;
+  return UW_OK;
 } catch (...) {
   return UW_ERR_NOMEM;
 }
@@ -480,10 +536,12 @@ uw_status uw_get_info(const uw_matrix* m, uw_info* o) {
   o->bits_per_weight = 8.0 * (double)o->compressed_bytes / (double)m->numel;
   o->has_stream = m->stream != nullptr;
   o->has_palette_idx = m->pidx != nullptr;
+  o->element_bits = m->fp8 ? 8 : 16;
   return UW_OK;
 }
 
 uw_status uw_export(const uw_matrix* m, void* host_buf, size_t cap, size_t* bytes) try {
+  if (m && m->fp8) return UW_ERR_UNSUPPORTED;   // UWF1 carries BF16 matrices
   if (!m || !bytes) return UW_ERR_INVALID;
   const uint64_t total = export_bytes(m);
   *bytes = total;
@@ -644,7 +702,13 @@ static uw_status decode_to(const uw_matrix* m, void* out, int mode, hipStream_t 
 }
 
 uw_status uw_decode_full(const uw_matrix* m, uint16_t* w_out_dev, void* stream) {
+  if (m && m->fp8) return UW_ERR_UNSUPPORTED;
   return decode_to(m, w_out_dev, kDecodeFull, static_cast<hipStream_t>(stream));
+}
+
+uw_status uw_decode_fp8(const uw_matrix* m, uint8_t* w_out_dev, void* stream) {
+  if (m && !m->fp8) return UW_ERR_UNSUPPORTED;
+  return decode_to(m, w_out_dev, kDecodeFp8, static_cast<hipStream_t>(stream));
 }
 
 uw_status uw_decode_exponent(const uw_matrix* m, uint8_t* e_out_dev, void* stream) {
@@ -680,6 +744,7 @@ uw_status uw_drop_palette(uw_matrix* m, void* stream) {
 
 uw_status uw_workspace_size(const uw_matrix* m, uw_pipeline p, int64_t batch, size_t* bytes) {
   if (!m || !bytes || batch <= 0 || p < UW_PIPE_FULL || p > UW_PIPE_PALETTE_DIRECT) return UW_ERR_INVALID;
+  if (m->fp8) return UW_ERR_UNSUPPORTED;
   // enough for any kernel variant a cfg may select at this batch
   WeightView v = pipeline_view(m, p, nullptr);
   *bytes = prep_bytes(m, p) + pad256(gemm_partial_elems_max(v, batch, 0) * sizeof(float));

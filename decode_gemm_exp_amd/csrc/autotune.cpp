@@ -54,8 +54,10 @@ extern "C" uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj
                                  const int64_t* batches, int nb, int max_passes, const char* json_path,
                                  uw_tune_entry* out, void* stream) {
   if (!ms || !proj || count <= 0 || nproj <= 0 || !batches || nb <= 0) return UW_ERR_INVALID;
-  for (int i = 0; i < count; ++i)
+  for (int i = 0; i < count; ++i) {
     if (!ms[i] || proj[i] < 0 || proj[i] >= nproj) return UW_ERR_INVALID;
+    if (ms[i]->fp8) return UW_ERR_UNSUPPORTED;
+  }
   for (int b = 0; b < nb; ++b)
     if (batches[b] <= 0) return UW_ERR_INVALID;
   if (max_passes <= 0) max_passes = 3;

@@ -16,6 +16,13 @@
 //   encode        one wave per segment: per-lane codeword, wave prefix sum of
 //                 lengths gives bit positions, LDS atomic-or packs the words;
 //                 verbatim groups copy their exponents to the side section.
+//
+// FP8 E4M3 weights (UWF8 reading of saidapartage.blog, "Cloudflare Unweight :
+// -22 % sur le poids de vos LLM, sans perdre un bit", section "Un complément,
+// pas un remplaçant": the coding also applies on top of quantisation): two
+// more passes put each weight's 4-bit exponent field where a BF16 exponent
+// byte sits, so the passes above code it unchanged, and pack the kept
+// sign+mantissa nibbles two per byte.
 #include "uw_internal.h"
 
 namespace uw {
@@ -331,6 +338,43 @@ __global__ __launch_bounds__(256) void k_wave_span(const uint32_t* __restrict__ 
   }
 }
 
+// ---- FP8 E4M3 field passes (16 weights per thread and step) --------------------
+// exponent field (bits 6..3) -> bits 14..7 of a 16-bit word, all else zero
+__global__ __launch_bounds__(256) void k_fp8_fields(const uint4* __restrict__ w, uint64_t n16,
+                                                    uint4* __restrict__ out) {
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (uint64_t)gridDim.x * blockDim.x) {
+    const uint4 v = w[i];
+    const uint32_t src[4] = {v.x, v.y, v.z, v.w};
+    uint32_t dst[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t e = (src[j] >> 3) & 0x0F0F0F0Fu;   // byte b holds element 4j+b's field
+      dst[2 * j] = ((e & 0xFFu) << 7) | (((e >> 8) & 0xFFu) << 23);
+      dst[2 * j + 1] = (((e >> 16) & 0xFFu) << 7) | ((e >> 24) << 23);
+    }
+    out[2 * i] = make_uint4(dst[0], dst[1], dst[2], dst[3]);
+    out[2 * i + 1] = make_uint4(dst[4], dst[5], dst[6], dst[7]);
+  }
+}
+
+// sign << 3 | mantissa per weight, element 2i in the low nibble of byte i
+__global__ __launch_bounds__(256) void k_fp8_pack(const uint4* __restrict__ w, uint64_t n16,
+                                                  uint2* __restrict__ out) {
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (uint64_t)gridDim.x * blockDim.x) {
+    const uint4 v = w[i];
+    const uint32_t src[4] = {v.x, v.y, v.z, v.w};
+    uint32_t half[4];   // 16 bits: the nibbles of 4 weights
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t nib = ((src[j] >> 4) & 0x08080808u) | (src[j] & 0x07070707u);   // byte b: element 4j+b
+      half[j] = (nib & 0xFu) | (((nib >> 8) & 0xFu) << 4) | (((nib >> 16) & 0xFu) << 8) | ((nib >> 24) << 12);
+    }
+    out[i] = make_uint2(half[0] | (half[1] << 16), half[2] | (half[3] << 16));
+  }
+}
+
 unsigned grid_for(uint64_t items, unsigned per_block, unsigned cap = 65535u * 4u) {
   uint64_t b = (items + per_block - 1) / per_block;
   if (b == 0) b = 1;
@@ -339,6 +383,20 @@ unsigned grid_for(uint64_t items, unsigned per_block, unsigned cap = 65535u * 4u
 }
 
 }  // namespace
+
+hipError_t launch_fp8_fields(const uint8_t* w, uint64_t numel, uint16_t* out, hipStream_t s) {
+  const uint64_t n16 = numel / 16;   // numel is a multiple of 64
+  hipLaunchKernelGGL(k_fp8_fields, dim3(grid_for(n16, 256 * 4, 8192)), dim3(256), 0, s,
+                     reinterpret_cast<const uint4*>(w), n16, reinterpret_cast<uint4*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_pack(const uint8_t* w, uint64_t numel, uint8_t* out, hipStream_t s) {
+  const uint64_t n16 = numel / 16;
+  hipLaunchKernelGGL(k_fp8_pack, dim3(grid_for(n16, 256 * 4, 8192)), dim3(256), 0, s,
+                     reinterpret_cast<const uint4*>(w), n16, reinterpret_cast<uint2*>(out));
+  return hipGetLastError();
+}
 
 hipError_t launch_histogram(const uint16_t* w, uint64_t numel, uint32_t* hist, hipStream_t s) {
   const uint64_t n8 = numel / 8;   // numel is a multiple of 64

@@ -81,7 +81,7 @@ __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t by
 // output bytes before weight el: 4-bit slots, exponent bytes or BF16
 template <int MODE>
 __device__ __forceinline__ uint64_t out_bytes(uint64_t el) {
-  return MODE == kDecodeNibble ? el >> 1 : MODE == kDecodeExponent ? el : el * 2u;
+  return MODE == kDecodeNibble ? el >> 1 : (MODE == kDecodeExponent || MODE == kDecodeFp8) ? el : el * 2u;
 }
 
 __device__ __forceinline__ uint32_t stage_at(uint32_t f, uint32_t L) { return f * 64u + (L ^ (f & 63u)); }
@@ -227,6 +227,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_direct(DecodeArgs a) {
           }
         }
         if (MODE == kDecodeFull && ok[u]) sv[u] = *reinterpret_cast<const uint4*>(smp + el[u]);
+        if (MODE == kDecodeFp8 && ok[u]) {
+          const uint2 q = *reinterpret_cast<const uint2*>(smp + el[u] / 2u);
+          sv[u] = make_uint4(q.x, q.y, 0u, 0u);
+        }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -235,6 +239,11 @@ __global__ __launch_bounds__(kThreads) void k_decode_direct(DecodeArgs a) {
           *reinterpret_cast<uint2*>((uint8_t*)a.out + el[u] / 2) = make_uint2(ev[u].x, ev[u].y);
         } else if (MODE == kDecodeExponent) {
           *reinterpret_cast<uint4*>((uint8_t*)a.out + el[u]) = ev[u];
+        } else if (MODE == kDecodeFp8) {
+          uint4 o;
+          fp8_rebuild8(sv[u].x, ev[u].x, ev[u].y, o.x, o.y);
+          fp8_rebuild8(sv[u].y, ev[u].z, ev[u].w, o.z, o.w);
+          *reinterpret_cast<uint4*>((uint8_t*)a.out + el[u]) = o;
         } else {
           uint4 o0, o1;
           rebuild4(sv[u].x, ev[u].x, o0.x, o0.y);
@@ -428,7 +437,9 @@ __global__ __launch_bounds__(staged_max_threads<CH>()) void k_decode_staged(Deco
     const uint32_t ng = seg_ng > r * CH ? (seg_ng - r * CH < CH ? seg_ng - r * CH : CH) : 0u;
     const bool pair_first = MODE == kDecodeFull && CH == 1 && (r & 1u) == 0;
     const bool pair_second = MODE == kDecodeFull && CH == 1 && (r & 1u) == 1;
-    const bool defer_first = MODE == kDecodeExponent && CH == 1 && (r & 1u) == 0;
+    // one output byte per weight (exponents, FP8): an owner's two groups of a
+    // 128-byte line are stored together in the odd round
+    const bool defer_first = (MODE == kDecodeExponent || MODE == kDecodeFp8) && CH == 1 && (r & 1u) == 0;
     uint32_t has_next = 0;   // bit u: this step's owner has a group in round r+1
     const uint32_t vbits = (uint32_t)(segbits >> (r * CH)) & ((1u << CH) - 1u) & ((1u << ng) - 1u);
     const uint32_t ncoded = ng - (uint32_t)__popc(vbits);
@@ -463,6 +474,9 @@ __global__ __launch_bounds__(staged_max_threads<CH>()) void k_decode_staged(Deco
         sv[u] = svn[u];
       } else if (MODE == kDecodeFull) {
         sv[u] = *reinterpret_cast<const uint4*>(smp + (ok ? el[u] : 0u));
+      } else if (MODE == kDecodeFp8) {   // 16 packed sign+mantissa nibbles
+        const uint2 q = *reinterpret_cast<const uint2*>(smp + (ok ? el[u] / 2u : 0u));
+        sv[u] = make_uint4(q.x, q.y, 0u, 0u);
       }
       const bool next = (r + 1) * CH < ong[u];   // the owner has a group in round r+1 (CH == 1)
       if (defer_first) has_next |= next ? (1u << u) : 0u;
@@ -543,12 +557,17 @@ __global__ __launch_bounds__(staged_max_threads<CH>()) void k_decode_staged(Deco
         }
       } else if constexpr (MODE == kDecodeNibble) {
         buf_store8(ro, ok ? rel / 2u : kPastEnd, ex.x, ex.y);
-      } else if constexpr (MODE == kDecodeExponent) {
+      } else if constexpr (MODE == kDecodeExponent || MODE == kDecodeFp8) {
+        uint4 ob = ex;
+        if constexpr (MODE == kDecodeFp8) {
+          fp8_rebuild8(sv[u].x, ex.x, ex.y, ob.x, ob.y);
+          fp8_rebuild8(sv[u].y, ex.z, ex.w, ob.z, ob.w);
+        }
         if constexpr (CH == 1)   // the other half of this line, from the previous round
           buf_store16<NT>(ro, ((deferred >> u) & 1u) ? rel - 64u : kPastEnd, exn[u]);
         const bool hold = defer_first && ((has_next >> u) & 1u);
-        buf_store16<NT>(ro, ok && !hold ? rel : kPastEnd, ex);
-        exn[u] = ex;   // used next round only when held
+        buf_store16<NT>(ro, ok && !hold ? rel : kPastEnd, ob);
+        exn[u] = ob;   // used next round only when held
       } else {
         uint4 o0, o1;
         rebuild4(sv[u].x, ex.x, o0.x, o0.y);
@@ -652,7 +671,7 @@ hipError_t launch_staged(const DecodeArgs& a, uint32_t wpb, hipStream_t s) {
     return a.pal.run ? launch_staged_pal<MODE, CH, true, true>(a, wpb, s)
                      : launch_staged_pal<MODE, CH, false, true>(a, wpb, s);
   } else {
-    const bool nt = a.groups * 64u * 2u > kCachedOutputMax;
+    const bool nt = a.groups * 64u * (MODE == kDecodeFp8 ? 1u : 2u) > kCachedOutputMax;
     if (a.pal.run)
       return nt ? launch_staged_pal<MODE, CH, true, true>(a, wpb, s) : launch_staged_pal<MODE, CH, true, false>(a, wpb, s);
     return nt ? launch_staged_pal<MODE, CH, false, true>(a, wpb, s) : launch_staged_pal<MODE, CH, false, false>(a, wpb, s);
@@ -683,6 +702,7 @@ hipError_t launch_decode(const DecodeArgs& a, int mode, hipStream_t s) {
   switch (mode) {
     case kDecodeNibble: return launch_mode<kDecodeNibble>(a, (uint32_t)blocks, s);
     case kDecodeExponent: return launch_mode<kDecodeExponent>(a, (uint32_t)blocks, s);
+    case kDecodeFp8: return launch_mode<kDecodeFp8>(a, (uint32_t)blocks, s);
     default: return launch_mode<kDecodeFull>(a, (uint32_t)blocks, s);
   }
 }

@@ -44,6 +44,20 @@ __device__ __forceinline__ void rebuild16(const uint4& s, const uint4& e, uint32
   rebuild4(s.w, e.w, o[6], o[7]);
 }
 
+// FP8 E4M3 weights (OCP OFP8 E4M3: sign bit 7, exponent bits 6..3, mantissa
+// bits 2..0): 8 kept sign+mantissa nibbles (element i in bits 4i..4i+3,
+// nibble = sign << 3 | mantissa) and the exponent fields of the same
+// elements as bytes (e03: elements 0..3, e47: 4..7) -> 8 E4M3 bytes.
+__device__ __forceinline__ void fp8_rebuild8(uint32_t nib, uint32_t e03, uint32_t e47, uint32_t& o03,
+                                             uint32_t& o47) {
+  const uint32_t ev = nib & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6
+  const uint32_t od = (nib >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
+  const uint32_t s03 = __builtin_amdgcn_perm(od, ev, 0x05010400u);
+  const uint32_t s47 = __builtin_amdgcn_perm(od, ev, 0x07030602u);
+  o03 = ((s03 & 0x08080808u) << 4) | (e03 << 3) | (s03 & 0x07070707u);
+  o47 = ((s47 & 0x08080808u) << 4) | (e47 << 3) | (s47 & 0x07070707u);
+}
+
 // 4 slot bytes (0..15) -> 4 palette exponent bytes
 __device__ __forceinline__ uint32_t pal_lookup4(uint32_t n, const PalView& p) {
   const uint32_t n7 = n & 0x07070707u;

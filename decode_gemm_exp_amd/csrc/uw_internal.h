@@ -46,7 +46,7 @@ struct uw_matrix {
   uint64_t V = 0, W = 0, code_bits = 0;
   uw::Tables t{};
   // device sections
-  uint8_t* sm = nullptr;          // numel
+  uint8_t* sm = nullptr;          // numel (BF16) or numel / 2 (FP8) bytes
   uint32_t* vflags = nullptr;     // flag_words
   uint32_t* vrank = nullptr;      // flag_words
   uint8_t* vexp = nullptr;        // 64 * V (may be null when V == 0)
@@ -56,6 +56,7 @@ struct uw_matrix {
   uint8_t* pidx = nullptr;        // resident palette indices (numel / 2) or null
   int* corrupt = nullptr;         // device flag set by decoders
   uint32_t wave_span = 0;         // most stream words any 64-segment wave covers (from a 4-word boundary)
+  bool fp8 = false;               // FP8 E4M3 weights: sm holds numel / 2 bytes of sign+mantissa nibbles
 };
 
 namespace uw {
@@ -74,6 +75,8 @@ int device_cus();
 hipError_t allow_dynamic_lds(const void* kernel, int bytes);
 
 // ---- kernel launchers (compress.hip, decode.hip, gemm*.hip) ------------------
+hipError_t launch_fp8_fields(const uint8_t* w, uint64_t numel, uint16_t* out, hipStream_t s);
+hipError_t launch_fp8_pack(const uint8_t* w, uint64_t numel, uint8_t* out, hipStream_t s);
 hipError_t launch_histogram(const uint16_t* w, uint64_t numel, uint32_t* hist, hipStream_t s);
 hipError_t launch_flags(const uint16_t* w, uint64_t numel, uint64_t groups, const uint8_t* slot_tab,
                         uint8_t* sm, uint32_t* vflags, uint32_t* coded, hipStream_t s);
@@ -98,7 +101,7 @@ struct PalView {
   uint32_t base4;
 };
 
-enum DecodeMode { kDecodeNibble = 0, kDecodeExponent = 1, kDecodeFull = 2 };
+enum DecodeMode { kDecodeNibble = 0, kDecodeExponent = 1, kDecodeFull = 2, kDecodeFp8 = 3 };
 struct DecodeArgs {
   const uint32_t* stream; uint64_t stream_words;   // including slack
   const uint32_t* seg_off;

@@ -57,7 +57,7 @@ class uw_info(ctypes.Structure):
                 ("stream_words", ctypes.c_uint64), ("code_bits", ctypes.c_uint64),
                 ("compressed_bytes", ctypes.c_uint64), ("export_bytes", ctypes.c_uint64),
                 ("bits_per_weight", ctypes.c_double), ("has_stream", ctypes.c_int32),
-                ("has_palette_idx", ctypes.c_int32)]
+                ("has_palette_idx", ctypes.c_int32), ("element_bits", ctypes.c_int32)]
 
 
 class uw_tune_entry(ctypes.Structure):
@@ -77,11 +77,14 @@ _SIGS = {
     "uw_version": (ctypes.c_uint32, []),
     "uw_compress": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, ctypes.POINTER(uw_compress_opts), _vp,
                                    ctypes.POINTER(_vp)]),
+    "uw_compress_fp8": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, ctypes.POINTER(uw_compress_opts), _vp,
+                                   ctypes.POINTER(_vp)]),
     "uw_get_info": (ctypes.c_int, [_vp, ctypes.POINTER(uw_info)]),
     "uw_export": (ctypes.c_int, [_vp, _vp, _sz, ctypes.POINTER(_sz)]),
     "uw_import": (ctypes.c_int, [_vp, _sz, _vp, ctypes.POINTER(_vp)]),
     "uw_free": (None, [_vp]),
     "uw_decode_full": (ctypes.c_int, [_vp, _vp, _vp]),
+    "uw_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp]),
     "uw_decode_exponent": (ctypes.c_int, [_vp, _vp, _vp]),
     "uw_transcode_palette": (ctypes.c_int, [_vp, _vp, _vp]),
     "uw_drop_stream": (ctypes.c_int, [_vp, _vp]),
@@ -213,6 +216,20 @@ def uw_import_status(blob: bytes) -> int:
 
 def uw_free(m: Matrix) -> None:
     m.free()
+
+
+def uw_compress_fp8(w_dev: torch.Tensor, n: int, k: int, layout: int = LAYOUT_NK, seg_groups: int = 4,
+                    stream=None) -> Matrix:
+    """FP8 E4M3 weights given as a uint8 device tensor of the stored shape."""
+    opts = uw_compress_opts(seg_groups, 0)
+    h = ctypes.c_void_p()
+    _check(_lib.uw_compress_fp8(_ptr(w_dev), n, k, layout, ctypes.byref(opts), _stream(stream), ctypes.byref(h)),
+           "uw_compress_fp8")
+    return Matrix(h.value)
+
+
+def uw_decode_fp8(m: Matrix, out: torch.Tensor, stream=None) -> None:
+    _check(_lib.uw_decode_fp8(m.handle, _ptr(out), _stream(stream)), "uw_decode_fp8")
 
 
 def uw_decode_full(m: Matrix, out: torch.Tensor, stream=None) -> None:

@@ -120,6 +120,7 @@ typedef struct {
   double bits_per_weight;       /* 8 * compressed_bytes / numel            */
   int32_t has_stream;           /* Huffman stream resident                 */
   int32_t has_palette_idx;      /* 4-bit indices resident                  */
+  int32_t element_bits;         /* 16: BF16 weights; 8: FP8 E4M3 weights   */
 } uw_info;
 
 const char* uw_status_str(uw_status st);
@@ -134,6 +135,24 @@ uint32_t uw_version(void);      /* (major << 16) | minor */
  * copies).  On success *out owns the sections.  ([EVC] "BF16權重壓縮原理") */
 uw_status uw_compress(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout layout,
                       const uw_compress_opts* opts, void* stream, uw_matrix** out);
+
+/* Compress a device FP8 E4M3 matrix (OCP OFP8 E4M3: sign bit 7, exponent
+ * bits 6..3, mantissa bits 2..0; any byte, NaN included, round-trips).
+ * `w_dev` is the stored array of bytes, 16-byte aligned, shaped and
+ * constrained as for uw_compress.  The 4-bit exponent field is coded exactly
+ * as the BF16 exponent byte is (histogram, palette, code, segmented stream);
+ * E4M3 has at most 16 exponent values, so every group is coded and none is
+ * verbatim.  Sign and mantissa are kept as a nibble, two weights per byte
+ * (numel / 2 bytes).  Allocates 2.5 x numel bytes of temporary device memory
+ * and synchronises `stream` like uw_compress.  The handle serves
+ * uw_decode_fp8, uw_decode_exponent (the exponent fields, one byte each),
+ * uw_transcode_palette, uw_get_info, uw_sync_status and uw_free; the BF16
+ * calls (uw_decode_full, uw_export, the matmul and sequence calls) return
+ * UW_ERR_UNSUPPORTED.  (saidapartage.blog, "Cloudflare Unweight : -22 % sur
+ * le poids de vos LLM, sans perdre un bit", section "Un complément, pas un
+ * remplaçant": the coding stacks on top of quantisation.) */
+uw_status uw_compress_fp8(const uint8_t* w_dev, int64_t n, int64_t k, uw_layout layout,
+                          const uw_compress_opts* opts, void* stream, uw_matrix** out);
 
 uw_status uw_get_info(const uw_matrix* m, uw_info* out);
 
@@ -153,6 +172,12 @@ void uw_free(uw_matrix* m);
 /* Full Huffman decode: writes the original stored array (numel x 16 bit) to
  * w_out_dev.  ([EVC] "四種執行管道", first pipeline) */
 uw_status uw_decode_full(const uw_matrix* m, uint16_t* w_out_dev, void* stream);
+
+/* Full decode of an FP8 handle: writes the original stored array (numel
+ * E4M3 bytes, 16-byte aligned) to w_out_dev.  UW_ERR_UNSUPPORTED for a BF16
+ * handle, UW_ERR_STATE once the stream was dropped; corruption is reported
+ * by uw_sync_status. */
+uw_status uw_decode_fp8(const uw_matrix* m, uint8_t* w_out_dev, void* stream);
 
 /* Exponent-only decode: writes numel exponent bytes in stored order,
  * verbatim groups included.  ([EVC] "四種執行管道", second pipeline) */
