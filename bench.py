@@ -198,6 +198,7 @@ def extras(uw, synth, torch, dev, iters: int = 12, copies: int = 4):
                                                  "mfma_frac": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
     del ms
     out.update(attention_rows(uw, synth, torch, dev, iters, copies))
+    out.update(fp8_rows(uw, synth, torch, dev, iters, copies))
     return out
 
 
@@ -247,6 +248,44 @@ def attention_rows(uw, synth, torch, dev, iters: int, copies: int):
                     "roofline": round(max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)) / t, 4)}
         del sets
     return out
+
+
+def fp8_rows(uw, synth, torch, dev, iters: int, copies: int):
+    """Lossless coding over FP8 E4M3 weights at the 8B gate shape (14336 x
+    4096, N(0, 0.02) scaled per tensor to the E4M3 maximum): the three decode
+    outputs (E4M3 bytes, exponent fields, palette slots), each over `copies`
+    compressed copies.  Algorithmic bytes: stream, offsets and flag words
+    read, plus the sign+mantissa nibbles for the full decode, plus the output
+    written."""
+    n, k = 14336, 4096
+    w = synth.fp8_weights(n, k, device=dev)
+    ms = [uw.uw_compress_fp8(w, n, k, 0) for _ in range(copies)]
+    del w
+    info = ms[0].info()
+    M = info.numel
+    base = 4 * (info.stream_words + 2) + 4 * (info.segments + 1) + 8 * ((info.groups + 31) // 32)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    out8 = torch.empty(M, dtype=torch.uint8, device=dev)
+    outp = torch.empty(M // 2, dtype=torch.uint8, device=dev)
+    rows = {}
+    for name, call, nbytes in (("decode_fp8", lambda c: uw.uw_decode_fp8(ms[c], out8), base + M // 2 + M),
+                               ("decode_exponent", lambda c: uw.uw_decode_exponent(ms[c], out8), base + M),
+                               ("transcode", lambda c: uw.uw_transcode_palette(ms[c], outp), base + M // 2)):
+        for c in range(copies):
+            call(c)
+        s, e = ev(), ev()
+        hold_gpu(torch, iters)
+        s.record()
+        for it in range(iters):
+            call(it % copies)
+        e.record()
+        torch.cuda.synchronize()
+        t = s.elapsed_time(e) / iters / 1e3
+        rows[f"fp8_gate8b_{name}"] = {"us": round(t * 1e6, 2), "gbs": round(nbytes / t / 1e9, 1),
+                                      "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                                      "bits_per_weight": round(info.bits_per_weight, 3)}
+    del ms
+    return rows
 
 
 def measured_peaks(torch, dev):
