@@ -491,6 +491,42 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NB <= 4 ? 4
   }
 }
 
+// y[b][col0 + n] = sum over slices p of part[p][b][n], four consecutive
+// outputs per lane (N a multiple of 4): every slice is read with 16-byte
+// loads, 1 KB per wave instruction, and added in slice order, so results
+// repeat bit for bit.  The kernel below serves other N.
+__global__ __launch_bounds__(256) void k_sum_slices4(const float4* __restrict__ part, int slices, uint64_t N4,
+                                                     int64_t B, int64_t b0, float* __restrict__ y, int64_t ldy,
+                                                     int64_t col0) {
+  const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= N4) return;
+  const uint64_t b = (uint64_t)b0 + blockIdx.y;
+  const uint64_t stride = (uint64_t)B * N4;
+  const float4* src = part + b * N4 + i;
+  float4 s = src[0];
+  int p = 1;
+  for (; p + 3 < slices; p += 4) {   // four loads in flight, added in order
+    const float4 v0 = src[(uint64_t)p * stride], v1 = src[(uint64_t)(p + 1) * stride];
+    const float4 v2 = src[(uint64_t)(p + 2) * stride], v3 = src[(uint64_t)(p + 3) * stride];
+    s.x = (((s.x + v0.x) + v1.x) + v2.x) + v3.x;
+    s.y = (((s.y + v0.y) + v1.y) + v2.y) + v3.y;
+    s.z = (((s.z + v0.z) + v1.z) + v2.z) + v3.z;
+    s.w = (((s.w + v0.w) + v1.w) + v2.w) + v3.w;
+  }
+  for (; p < slices; ++p) {
+    const float4 v = src[(uint64_t)p * stride];
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  float* dst = y + b * (uint64_t)ldy + (uint64_t)col0 + 4 * i;
+  dst[0] = s.x;
+  dst[1] = s.y;
+  dst[2] = s.z;
+  dst[3] = s.w;
+}
+
 // y[b][col0 + n] = sum over slices p of part[p][b][n].  Block: 4 waves on 64
 // consecutive outputs of one batch row (grid.y = b); wave q adds slices
 // q*L .. q*L+L-1 in order (loads batched 8 at a time), then the four wave
@@ -786,10 +822,15 @@ size_t gemm_partial_elems_max(const WeightView& w, int64_t batch, int split_k) {
 
 hipError_t launch_sum_slices(const float* part, int slices, uint64_t n, int64_t batch, float* y, int64_t ldy,
                              int64_t col0, hipStream_t s) {
+  const bool vec = n % 4 == 0 && (reinterpret_cast<uintptr_t>(part) & 15u) == 0;
   for (int64_t b0 = 0; b0 < batch; b0 += 65535) {
     const int64_t nb = batch - b0 < 65535 ? batch - b0 : 65535;
-    hipLaunchKernelGGL(k_sum_slices, dim3((unsigned)((n + 63) / 64), (unsigned)nb), dim3(256), 0, s, part, slices, n,
-                       batch, b0, y, ldy, col0);
+    if (vec)
+      hipLaunchKernelGGL(k_sum_slices4, dim3((unsigned)((n / 4 + 255) / 256), (unsigned)nb), dim3(256), 0, s,
+                         reinterpret_cast<const float4*>(part), slices, n / 4, batch, b0, y, ldy, col0);
+    else
+      hipLaunchKernelGGL(k_sum_slices, dim3((unsigned)((n + 63) / 64), (unsigned)nb), dim3(256), 0, s, part,
+                         slices, n, batch, b0, y, ldy, col0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
