@@ -724,11 +724,14 @@ bool gemm_variant_supported(int v, int layout) { return v < rf_first_variant() |
 // Default kernel by batch, from sweeps over the 8B and 70B MLP shapes (every
 // variant, both layouts, palette-direct and BF16 weights):
 //   stored [N][K]: VALU GEMV up to 4 rows, register-fed MFMA (two row tiles
-//     per wave) up to 32, then LDS tiles 64x128 up to 64, 128x128 up to 512,
-//     256x256 beyond when its tiles cover every CU (else 128x128: 8B gate at
-//     1024 rows 149 vs 235 us);
+//     per wave) up to 32, then LDS tiles 64x128 up to 64, 128x128 up to 128,
+//     the eight-wave 256x256 up to 512 (K split to fill the CUs: 70B gate at
+//     512 rows, palette-direct 466 -> 319 us, BF16 295 -> 234 us), and beyond
+//     256x256 when its tiles cover every CU (else 128x128: 8B gate at 1024
+//     rows 149 vs 235 us);
 //   stored [K][N]: VALU GEMV for one row, then LDS tiles 32x256 up to 32,
-//     64x128 up to 64, 128x256 up to 192, 256x256 beyond.
+//     64x128 up to 64, 128x256 up to 128, 256x256 beyond (70B down at 192
+//     rows, palette-direct: 292 -> 186 us).
 // The 256x256 tile runs with eight waves (two per SIMD) for palette weights,
 // whose rebuild then issues beside the other wave's MFMAs (70B gate,
 // palette-direct, 1024 rows: 737 -> 602 us); BF16 and exponent weights gain
@@ -740,14 +743,15 @@ static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_c
     if (batch <= 4) return 1;
     if (batch <= 32 && mfma_rf_supported(w, 0)) return rf_first_variant();
     if (batch <= 64) return 2 + 0;
-    if (batch <= 512) return 2 + 1;
+    if (batch <= 128) return 2 + 1;
+    if (batch <= 512) return 2 + 7;
     const int64_t tiles = (int64_t)((w.n + 255) / 256) * ((batch + 255) / 256);
     return tiles >= (int64_t)device_cus() ? big : 2 + 1;
   }
   if (batch == 1) return 1;
   if (batch <= 32) return 2 + 6;
   if (batch <= 64) return 2 + 0;
-  if (batch <= 192) return 2 + 2;
+  if (batch <= 128) return 2 + 2;
   return big;
 }
 

@@ -390,14 +390,21 @@ void mfma2_tile_dims(int tile, int* bm, int* bn) {
   *bn = kTiles2[tile].bn;
 }
 
-// K slices so that the grid covers the chip at least once; twice for the
-// palette formats at small batch, whose data loads wait on flag words and
-// need a second resident block per CU to hide that, while the partial sums
-// stay small next to the weights (capped; each slice >= 8 steps)
+// K slices (powers of two, each slice >= 8 steps): until the grid covers the
+// chip once, twice for the palette formats up to 64 rows, whose data loads
+// wait on flag words and need a second resident block per CU to hide that.
+// Tiles of 256 rows beyond 64 rows stop at the first split that fills seven
+// eighths of the CUs instead: every slice adds a pass of B x N partial sums
+// (70B gate at 256 rows, 112 tiles: 2 slices, 224 blocks, palette-direct
+// 177 us against 203 us for the 4 slices that fill the chip; at 512 rows,
+// 224 tiles: no split, 319 against 355 us).  Smaller tiles keep the full
+// cover (palette-direct at 128 rows with 128x128 tiles: 149 us with 2
+// slices, 187 us with none).
 int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint) {
   const Tile2 t = kTiles2[tile];
   const int64_t blocks = ((int64_t)w.n + t.bn - 1) / t.bn * ((batch + t.bm - 1) / t.bm);
-  const int64_t target = fmt_is_pal(w.fmt) && batch <= 64 ? 512 : 256;
+  const int64_t target = batch <= 64 ? (fmt_is_pal(w.fmt) ? 512 : 256)
+                         : t.bm >= 256 ? ((int64_t)device_cus() * 7 + 7) / 8 : 256;
   int s = split_hint > 0 ? split_hint : 1;
   if (split_hint <= 0)
     while (blocks * s < target && (int64_t)w.k / (64 * (s * 2)) >= 8) s *= 2;
