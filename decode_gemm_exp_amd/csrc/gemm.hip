@@ -727,8 +727,9 @@ bool gemm_variant_supported(int v, int layout) { return v < rf_first_variant() |
 //     per wave) up to 32, then LDS tiles 64x128 up to 64, 128x128 up to 128,
 //     the eight-wave 256x256 up to 512 (K split to fill the CUs: 70B gate at
 //     512 rows, palette-direct 466 -> 319 us, BF16 295 -> 234 us), and beyond
-//     256x256 when its tiles cover every CU (else 128x128: 8B gate at 1024
-//     rows 149 vs 235 us);
+//     256x256 when its tiles cover seven eighths of the CUs (8B gate at 1024
+//     rows, 224 tiles: palette-direct 252 -> 164 us), else 128x128 (8B q at
+//     1024 rows, 64 tiles: 80 vs 81 us palette-direct, 46 vs 64 us BF16);
 //   stored [K][N]: VALU GEMV for one row, then LDS tiles 32x256 up to 32,
 //     64x128 up to 64, 128x256 up to 128, 256x256 beyond (70B down at 192
 //     rows, palette-direct: 292 -> 186 us).
@@ -746,7 +747,7 @@ static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_c
     if (batch <= 128) return 2 + 1;
     if (batch <= 512) return 2 + 7;
     const int64_t tiles = (int64_t)((w.n + 255) / 256) * ((batch + 255) / 256);
-    return tiles >= (int64_t)device_cus() ? big : 2 + 1;
+    return tiles * 8 >= (int64_t)device_cus() * 7 ? big : 2 + 1;
   }
   if (batch == 1) return 1;
   if (batch <= 32) return 2 + 6;
