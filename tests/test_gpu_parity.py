@@ -85,7 +85,7 @@ def run_pipeline(uw, m, pipeline, x, cfg=None):
     if cfg and cfg.get("split_k"):
         # partial slices, preprocessed weights and the register-fed kernel's packed x
         packed = (info.k // 128 + 1) * 4 * 4096
-        ws_bytes = max(ws_bytes, 4 * cfg["split_k"] * min(x.shape[0], 64) * info.n + 2 * info.numel + packed + 4096)
+        ws_bytes = max(ws_bytes, 4 * cfg["split_k"] * x.shape[0] * info.n + 2 * info.numel + packed + 4096)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV)
     uw.uw_matmul_reconstruct(m, pipeline, x, y, ws, cfg=cfg)
     torch.cuda.synchronize()
@@ -205,6 +205,29 @@ def test_gemm_ragged_all_pipelines(uw, synth, oracle, layout, batch):
 
 def RF_FIRST(uw):
     return uw.variant_count() - 1
+
+
+# mid batch: the default 256x256 tiles with K split across blocks (33 K
+# steps, so slices are uneven), ragged N and batch tiles, both layouts, all
+# pipelines; then the four- and eight-wave tiles with forced odd splits
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("batch", [200, 300])
+def test_gemm_mid_batch_split(uw, synth, oracle, layout, batch):
+    n, k = (600, 2112) if layout == 0 else (576, 2112)
+    r, c = (n, k) if layout == 0 else (k, n)
+    say(f"gemm mid batch layout={layout} batch={batch}")
+    w = synth.weights(r, c, 0.02, 0.005, 10, seed=91 + batch + layout).to(DEV)
+    x = synth.activations(batch, k, seed=5 + batch).to(DEV)
+    m = gpu_compress(uw, w, n, k, layout)
+    uw.uw_transcode_palette(m, None)
+    w_np, x_np = bits(w), bits(x)
+    for p in range(4):
+        y = run_pipeline(uw, m, p, x)
+        check_gemm(oracle, y, x_np, w_np, layout, what=f"pipeline {p}")
+    for v, sk in ((2 + 7, 3), (2 + 4, 5)):
+        for p in (0, 3):
+            y = run_pipeline(uw, m, p, x, cfg={"variant": v, "split_k": sk})
+            check_gemm(oracle, y, x_np, w_np, layout, what=f"pipeline {p} variant {v} split {sk}")
 
 
 # register-fed MFMA kernels (stored [N][K]): row counts that leave partial
