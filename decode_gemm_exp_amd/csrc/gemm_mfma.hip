@@ -400,14 +400,25 @@ void mfma2_tile_dims(int tile, int* bm, int* bn) {
 // 224 tiles: no split, 319 against 355 us).  Smaller tiles keep the full
 // cover (palette-direct at 128 rows with 128x128 tiles: 149 us with 2
 // slices, 187 us with none).
+// LDS of one block: x and weight tiles, double buffered
+size_t mfma2_lds_bytes(int layout, const Tile2& t) {
+  const size_t wtile = layout == 0 ? (size_t)t.bn * kLDK : (size_t)kBK * (size_t)(t.bn + 16);
+  return 2 * ((size_t)t.bm * kLDK + wtile) * sizeof(uint16_t);
+}
+
 int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint) {
   const Tile2 t = kTiles2[tile];
   const int64_t blocks = ((int64_t)w.n + t.bn - 1) / t.bn * ((batch + t.bm - 1) / t.bm);
-  const int64_t target = batch <= 64 ? (fmt_is_pal(w.fmt) ? 512 : 256)
-                         : t.bm >= 256 ? ((int64_t)device_cus() * 7 + 7) / 8 : 256;
+  const int64_t cus = (int64_t)device_cus();
+  const int64_t target = batch <= 64 ? (fmt_is_pal(w.fmt) ? 512 : 256) : t.bm >= 256 ? (cus * 7 + 7) / 8 : 256;
+  // up to 64 rows, never past the blocks the CUs hold at once (a second
+  // round of blocks runs on a mostly idle chip: 8B gate, palette-direct, 64
+  // rows, 64x128 tiles: 4 slices 40.6 us, 8 slices 47.7 us)
+  const int64_t per_cu = (int64_t)(160 * 1024 / mfma2_lds_bytes((int)w.layout, t));
+  const int64_t hold = batch <= 64 ? cus * (per_cu > 0 ? per_cu : 1) : INT64_MAX;
   int s = split_hint > 0 ? split_hint : 1;
   if (split_hint <= 0)
-    while (blocks * s < target && (int64_t)w.k / (64 * (s * 2)) >= 8) s *= 2;
+    while (blocks * s < target && blocks * s * 2 <= hold && (int64_t)w.k / (64 * (s * 2)) >= 8) s *= 2;
   const int64_t steps = ((int64_t)w.k + 63) / 64;
   if (s > steps) s = (int)steps;
   return s;
@@ -435,8 +446,7 @@ hipError_t launch_mfma2(const WeightView& w, const uint16_t* x, int64_t batch, f
     f = w.fmt == kFmtBf16 ? pick<1, kFmtBf16>(tile) : w.fmt == kFmtExp ? pick<1, kFmtExp>(tile)
         : w.fmt == kFmtPal ? pick<1, kFmtPal>(tile) : pick<1, kFmtPalRun>(tile);
   }
-  const size_t wtile = w.layout == 0 ? (size_t)t.bn * kLDK : (size_t)kBK * (size_t)(t.bn + 16);
-  const size_t lds = 2 * ((size_t)t.bm * kLDK + wtile) * sizeof(uint16_t);
+  const size_t lds = mfma2_lds_bytes((int)w.layout, t);
   {
     hipError_t e = allow_dynamic_lds((const void*)f, (int)lds);
     if (e != hipSuccess) return e;
