@@ -387,11 +387,18 @@ def run_mlp70b(args) -> int:
     nt = min(args.tune_layers, L) * 3
     if alternate and nt < 6:
         nt = 6   # at least one layer of each kind
-    print(f"bench: autotune on {nt // 3} layers, batches {batches}", file=sys.stderr, flush=True)
     t_tune = time.perf_counter()
-    tuned = uw.uw_autotune(mats[:nt], proj[:nt], batches, max_passes=2,
-                           json_path=os.path.join(ROOT, "gpurun_out", "mlp70b_tuned.json")
-                           if os.path.isdir(os.path.join(ROOT, "gpurun_out")) else None)
+    if args.fixed_pipeline >= 0:   # the library's default kernels, one stream, no tuning
+        print(f"bench: pipeline {args.fixed_pipeline} with default kernels, batches {batches}", file=sys.stderr,
+              flush=True)
+        tuned = [{"projection": pj, "batch": b, "pipeline": args.fixed_pipeline, "variant": 0, "split_k": 0,
+                  "decode_cus": 0} for b in batches for pj in range(6 if alternate else 3)]
+        nt = 0
+    else:
+        print(f"bench: autotune on {nt // 3} layers, batches {batches}", file=sys.stderr, flush=True)
+        tuned = uw.uw_autotune(mats[:nt], proj[:nt], batches, max_passes=2,
+                               json_path=os.path.join(ROOT, "gpurun_out", "mlp70b_tuned.json")
+                               if os.path.isdir(os.path.join(ROOT, "gpurun_out")) else None)
     t_tune = time.perf_counter() - t_tune
     rows = []
     for b in batches:
@@ -454,6 +461,8 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=80, help="mlp70b: resident layers")
     ap.add_argument("--tune-layers", type=int, default=4, help="mlp70b: layers the autotuner times")
     ap.add_argument("--batches", default="", help="mlp70b: comma-separated batch sizes")
+    ap.add_argument("--fixed-pipeline", type=int, default=-1, choices=[-1, 0, 1, 2, 3],
+                    help="mlp70b: skip the autotuner; every projection runs this pipeline with the default kernels")
     ap.add_argument("--residency", default="both", choices=["both", "alternate"],
                     help="mlp70b: both forms in every layer, or alternating easy (palette indices) and hard "
                          "(Huffman stream) layers")
