@@ -297,8 +297,9 @@ def test_grouped_matmul(uw, synth, oracle):
     one launch (a run palette next to a palette with gaps runs with the
     general lookup; more than eight rows go in chunks); a group of five, a
     group holding a [K][N] matrix and batches that resolve to MFMA kernels
-    are launched one matrix at a time.  Every column block is checked
-    against the fp64 reference."""
+    are launched one matrix at a time; at 5 to 8 rows a group of small
+    matrices takes the grouped GEMV by default.  Every column block is
+    checked against the fp64 reference."""
     say("grouped matmul")
     k = 2048
     specs = [(700, 0, 0.0), (300, 0, 0.002), (1100, 0, 0.0), (64, 0, 0.002), (520, 0, 0.0), (384, 1, 0.002)]
@@ -315,7 +316,7 @@ def test_grouped_matmul(uw, synth, oracle):
     for idx in groups:
         sub = [ms[i] for i in idx]
         N = sum(ms[i].info().n for i in idx)
-        for batch, cfg in ((1, None), (3, None), (9, {"variant": 1}), (24, None)):
+        for batch, cfg in ((1, None), (3, None), (7, None), (9, {"variant": 1}), (24, None)):
             x = synth.activations(batch, k, seed=batch + 7).to(DEV)
             x_np = bits(x)
             for p in (0, 1, 3):
