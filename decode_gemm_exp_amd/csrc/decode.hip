@@ -1,7 +1,8 @@
-// decode.hip -- chunked-bitstream Huffman decoder for gfx950, three outputs:
+// decode.hip -- chunked-bitstream Huffman decoder for gfx950, four outputs:
 //   nibble   : 4-bit palette indices (palette transcode)
 //   exponent : exponent bytes (exponent-only decode)
 //   full     : rebuilt BF16 (full decode)
+//   fp8      : rebuilt E4M3 bytes (FP8 handles: exponent fields + kept nibbles)
 // [EVC] = "Cloudflare推出Unweight無損壓縮系統，將LLM模型大小壓縮15-22%"
 // (easyvibecoding.app/curated/736): section "四種執行管道" defines the
 // three preprocessing outputs; section "解壓與運算資源共享" gives the
