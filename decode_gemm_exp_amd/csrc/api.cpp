@@ -797,7 +797,7 @@ uw_status uw_matmul_reconstruct_grouped(const uw_matrix* const* ms, int count, u
                                         size_t ws_bytes, const uw_kernel_cfg* cfg, void* stream) {
   if (!ms || count <= 0) return UW_ERR_INVALID;
   uint64_t total_n = 0;
-  size_t need = 0;
+  size_t need = 0, prep_total = 0;
   for (int i = 0; i < count; ++i) {
     UW_CHECK(check_matmul_args(ms[i], p, x_dev, batch, y_dev));
     if (logical_k(ms[i]) != logical_k(ms[0])) return UW_ERR_INVALID;
@@ -805,17 +805,30 @@ uw_status uw_matmul_reconstruct_grouped(const uw_matrix* const* ms, int count, u
     size_t b = 0;
     workspace_for(ms[i], p, batch, cfg, &b);
     need += b;
+    prep_total += prep_bytes(ms[i], p);
   }
   if (need > ws_bytes || (need && !ws_dev) || !aligned16(ws_dev)) return UW_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
+  // Matrices whose kernel (as one matrix as wide as the group) is an LDS tile
+  // share one launch: fixed per-launch costs are paid once and K is split for
+  // the group's tiles together.  Its workspace: the preprocessed weights
+  // packed first, the group's partial rows after them.
+  size_t tile_part = SIZE_MAX;
+  if (count >= 2 && count <= kMfma2GroupMax) {
+    WeightView plan[kMfma2GroupMax];
+    for (int i = 0; i < count; ++i) plan[i] = pipeline_view(ms[i], p, nullptr);
+    tile_part = gemm_tile_group_partial_elems(plan, count, batch, cfg);
+  }
+  const size_t part_off = pad256(prep_total);
+  const bool tile_group = tile_part != SIZE_MAX && part_off + tile_part * sizeof(float) <= ws_bytes;
   size_t off = 0;
   std::vector<size_t> offs((size_t)count);
   for (int i = 0; i < count; ++i) {
     offs[(size_t)i] = off;
     UW_CHECK(preprocess(ms[i], p, ws + off, s));
-    size_t b = 0;
-    workspace_for(ms[i], p, batch, cfg, &b);
+    size_t b = prep_bytes(ms[i], p);
+    if (!tile_group) workspace_for(ms[i], p, batch, cfg, &b);
     off += b;
   }
   // matrices that all run the VALU GEMV share one launch
@@ -831,6 +844,11 @@ uw_status uw_matmul_reconstruct_grouped(const uw_matrix* const* ms, int count, u
     const hipError_t e = launch_gemm_group(vs, count, x_dev, batch, y_dev, (int64_t)total_n, c0, cfg, s);
     if (e == hipSuccess) return UW_OK;
     if (e != hipErrorNotSupported) return UW_ERR_DEVICE;
+    if (tile_group) {
+      float* part = tile_part ? reinterpret_cast<float*>(ws + part_off) : nullptr;
+      UW_HIP(launch_gemm_tile_group(vs, count, x_dev, batch, y_dev, (int64_t)total_n, c0, cfg, part, tile_part, s));
+      return UW_OK;
+    }
   }
   uint64_t col0 = 0;
   for (int i = 0; i < count; ++i) {

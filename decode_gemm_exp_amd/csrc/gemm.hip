@@ -852,6 +852,38 @@ hipError_t launch_sum_slices(const float* part, int slices, uint64_t n, int64_t 
   return hipSuccess;
 }
 
+// A group (2..4 matrices of one layout, K and format class) that fits one
+// LDS-tiled launch: the tile is the default (or forced) one of a matrix as
+// wide as the group.  Returns the tile index, or -1.
+static int tile_group_plan(const WeightView* ws, int count, int64_t batch, const uw_kernel_cfg* cfg) {
+  if (count < 2 || count > kMfma2GroupMax || batch <= 0) return -1;
+  WeightView wide = ws[0];
+  uint64_t ntot = 0;
+  for (int i = 0; i < count; ++i) {
+    if (ws[i].layout != ws[0].layout || ws[i].k != ws[0].k) return -1;
+    if (fmt_is_pal(ws[i].fmt) != fmt_is_pal(ws[0].fmt) || (!fmt_is_pal(ws[0].fmt) && ws[i].fmt != ws[0].fmt)) return -1;
+    if (ws[i].fmt != ws[0].fmt) wide.fmt = kFmtPal;
+    ntot += ws[i].n;
+  }
+  wide.n = ntot;
+  const int v = resolve_variant(wide, batch, cfg);
+  return v >= 2 && v < rf_first_variant() ? v - 2 : -1;
+}
+
+size_t gemm_tile_group_partial_elems(const WeightView* ws, int count, int64_t batch, const uw_kernel_cfg* cfg) {
+  const int tile = tile_group_plan(ws, count, batch, cfg);
+  if (tile < 0) return SIZE_MAX;
+  return mfma2_group_partial_elems(ws, count, batch, tile, cfg ? cfg->split_k : 0);
+}
+
+hipError_t launch_gemm_tile_group(const WeightView* ws, int count, const uint16_t* x, int64_t batch, float* y,
+                                  int64_t ldy, const int64_t* col0s, const uw_kernel_cfg* cfg, float* part,
+                                  size_t part_elems, hipStream_t s) {
+  const int tile = tile_group_plan(ws, count, batch, cfg);
+  if (tile < 0) return hipErrorNotSupported;
+  return launch_mfma2_group(ws, count, x, batch, y, ldy, col0s, tile, cfg ? cfg->split_k : 0, part, part_elems, s);
+}
+
 hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, float* y, int64_t ldy,
                        int64_t col0, const uw_kernel_cfg* cfg, float* partial, size_t partial_elems,
                        hipStream_t s) {

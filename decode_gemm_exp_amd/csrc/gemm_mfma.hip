@@ -26,6 +26,8 @@
 //   * block order is XCD-aware (see block_tile);
 //   * split K: grid.z slices of K write partial tiles to the workspace and a
 //     fixed-order reduction adds them (deterministic).
+#include <cstring>
+
 #include "rebuild.h"
 
 namespace uw {
@@ -129,10 +131,14 @@ constexpr int w_tile_elems() { return LAYOUT == 0 ? BN * kLDK : kBK * (BN + 16);
 
 // NW waves per block (4 or 8); with 8 two waves share each SIMD, so one
 // wave's rebuild arithmetic can issue while the other's MFMAs run.
+// One launch serves a group of up to four matrices with the same K, layout
+// and format (blockIdx.y picks the matrix; blocks past a smaller matrix's
+// tiles return at once): matrix g writes columns ycol[g].. of y, or columns
+// pcol[g].. of the partial rows (pld wide) when K is split.
 template <int LAYOUT, int FMT, int BM, int BN, int WGM, int NW = 4>
-__global__ __launch_bounds__(64 * NW) void k_mfma2(WeightView w, const uint16_t* __restrict__ x, int B,
-                                                   float* __restrict__ y, int64_t ldy, int64_t col0,
-                                                   int64_t kslice, float* __restrict__ part, int ntiles, int mtiles) {
+__global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_t* __restrict__ x, int B,
+                                                   float* __restrict__ y, int64_t ldy, int64_t kslice,
+                                                   float* __restrict__ part, int64_t pld, int mtiles) {
   constexpr int NT = 64 * NW;
   constexpr int WGN = NW / WGM;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -145,6 +151,10 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(WeightView w, const uint16_t*
   static_assert(TM >= 1 && TN >= 1 && XC >= 1 && WC >= 1, "tile too small");
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
+  const int g = (int)blockIdx.y;
+  const int ntiles = grp.ntiles[g];
+  if ((int)blockIdx.x >= ntiles * mtiles) return;   // uniform: before any barrier
+  const WeightView w = grp.w[g];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int64_t N = (int64_t)w.n, K = (int64_t)w.k;
@@ -344,8 +354,8 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(WeightView w, const uint16_t*
   }
 
   // ---- epilogue: y, or this K slice's partial tile part[slice][row][col] ----
-  float* out = part ? part + (uint64_t)blockIdx.z * (uint64_t)B * (uint64_t)N : y + col0;
-  const int64_t ld = part ? N : ldy;
+  float* out = part ? part + (uint64_t)blockIdx.z * (uint64_t)B * (uint64_t)pld + grp.pcol[g] : y + grp.ycol[g];
+  const int64_t ld = part ? pld : ldy;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -358,7 +368,7 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(WeightView w, const uint16_t*
       }
 }
 
-typedef void (*Mfma2Fn)(WeightView, const uint16_t*, int, float*, int64_t, int64_t, int64_t, float*, int, int);
+typedef void (*Mfma2Fn)(Mfma2Group, const uint16_t*, int, float*, int64_t, int64_t, float*, int64_t, int);
 
 template <int L, int F>
 Mfma2Fn pick(int tile) {
@@ -429,36 +439,93 @@ size_t mfma2_partial_elems(const WeightView& w, int64_t batch, int tile, int spl
   return s > 1 ? (size_t)s * (size_t)batch * (size_t)w.n : 0;
 }
 
-hipError_t launch_mfma2(const WeightView& w, const uint16_t* x, int64_t batch, float* y, int64_t ldy, int64_t col0,
-                        int tile, int split_hint, float* part, size_t part_elems, hipStream_t s) {
+// One launch over the group's tiles; K split as for one matrix as wide as the
+// group, the partial rows group-wide so one reduction serves every matrix.
+// The matrices' output columns in y must be consecutive from ycol[0].
+static hipError_t launch_group(const Mfma2Group& grp, const uint16_t* x, int64_t batch, float* y, int64_t ldy,
+                               int tile, int split_hint, float* part, size_t part_elems, hipStream_t s) {
   const Tile2 t = kTiles2[tile];
-  const int slices = mfma2_slices(w, batch, tile, split_hint);
-  const int64_t steps = ((int64_t)w.k + 63) / 64;
+  const WeightView& w0 = grp.w[0];
+  WeightView wide = w0;   // the group as one matrix: tiles, slices, partial rows
+  int fmt = w0.fmt;
+  uint64_t ntot = 0;
+  int ntmax = 0;
+  for (int i = 0; i < grp.count; ++i) {
+    ntot += grp.w[i].n;
+    if (grp.ntiles[i] > ntmax) ntmax = grp.ntiles[i];
+    if (grp.w[i].fmt != fmt) fmt = kFmtPal;   // palette kinds mixed: the general lookup
+  }
+  wide.n = ntot;
+  wide.fmt = fmt;
+  const int slices = mfma2_slices(wide, batch, tile, split_hint);
+  const int64_t steps = ((int64_t)w0.k + 63) / 64;
   const int64_t kslice = ((steps + slices - 1) / slices) * 64;
   const bool split = slices > 1;
-  if (split && (part == nullptr || part_elems < (size_t)slices * (size_t)batch * (size_t)w.n))
+  if (split && (part == nullptr || part_elems < (size_t)slices * (size_t)batch * (size_t)ntot))
     return hipErrorInvalidValue;
   Mfma2Fn f;
-  if (w.layout == 0) {
-    f = w.fmt == kFmtBf16 ? pick<0, kFmtBf16>(tile) : w.fmt == kFmtExp ? pick<0, kFmtExp>(tile)
-        : w.fmt == kFmtPal ? pick<0, kFmtPal>(tile) : pick<0, kFmtPalRun>(tile);
+  if (w0.layout == 0) {
+    f = fmt == kFmtBf16 ? pick<0, kFmtBf16>(tile) : fmt == kFmtExp ? pick<0, kFmtExp>(tile)
+        : fmt == kFmtPal ? pick<0, kFmtPal>(tile) : pick<0, kFmtPalRun>(tile);
   } else {
-    f = w.fmt == kFmtBf16 ? pick<1, kFmtBf16>(tile) : w.fmt == kFmtExp ? pick<1, kFmtExp>(tile)
-        : w.fmt == kFmtPal ? pick<1, kFmtPal>(tile) : pick<1, kFmtPalRun>(tile);
+    f = fmt == kFmtBf16 ? pick<1, kFmtBf16>(tile) : fmt == kFmtExp ? pick<1, kFmtExp>(tile)
+        : fmt == kFmtPal ? pick<1, kFmtPal>(tile) : pick<1, kFmtPalRun>(tile);
   }
-  const size_t lds = mfma2_lds_bytes((int)w.layout, t);
+  const size_t lds = mfma2_lds_bytes((int)w0.layout, t);
   {
     hipError_t e = allow_dynamic_lds((const void*)f, (int)lds);
     if (e != hipSuccess) return e;
   }
-  const int ntiles = (int)((w.n + (uint64_t)t.bn - 1) / (uint64_t)t.bn);
   const int mtiles = (int)((batch + t.bm - 1) / t.bm);
-  dim3 grid((unsigned)(ntiles * mtiles), 1, (unsigned)slices);
-  hipLaunchKernelGGL(f, grid, dim3(64 * t.waves), lds, s, w, x, (int)batch, y, ldy, col0, kslice, split ? part : nullptr,
-                     ntiles, mtiles);
+  dim3 grid((unsigned)(ntmax * mtiles), (unsigned)grp.count, (unsigned)slices);
+  hipLaunchKernelGGL(f, grid, dim3(64 * t.waves), lds, s, grp, x, (int)batch, y, ldy, kslice, split ? part : nullptr,
+                     (int64_t)ntot, mtiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
-  return launch_sum_slices(part, slices, w.n, batch, y, ldy, col0, s);
+  return launch_sum_slices(part, slices, ntot, batch, y, ldy, grp.ycol[0], s);
+}
+
+hipError_t launch_mfma2(const WeightView& w, const uint16_t* x, int64_t batch, float* y, int64_t ldy, int64_t col0,
+                        int tile, int split_hint, float* part, size_t part_elems, hipStream_t s) {
+  Mfma2Group grp;
+  std::memset(&grp, 0, sizeof(grp));
+  grp.w[0] = w;
+  grp.ycol[0] = col0;
+  grp.pcol[0] = 0;
+  grp.ntiles[0] = (int)((w.n + (uint64_t)kTiles2[tile].bn - 1) / (uint64_t)kTiles2[tile].bn);
+  grp.count = 1;
+  return launch_group(grp, x, batch, y, ldy, tile, split_hint, part, part_elems, s);
+}
+
+// 2..4 matrices of one layout, K and format class (palette kinds may mix),
+// their outputs consecutive in y from col0s[0]
+hipError_t launch_mfma2_group(const WeightView* ws, int count, const uint16_t* x, int64_t batch, float* y,
+                              int64_t ldy, const int64_t* col0s, int tile, int split_hint, float* part,
+                              size_t part_elems, hipStream_t s) {
+  if (count < 2 || count > kMfma2GroupMax) return hipErrorInvalidValue;
+  Mfma2Group grp;
+  std::memset(&grp, 0, sizeof(grp));
+  for (int i = 0; i < count; ++i) {
+    if (ws[i].layout != ws[0].layout || ws[i].k != ws[0].k) return hipErrorInvalidValue;
+    if (fmt_is_pal(ws[i].fmt) != fmt_is_pal(ws[0].fmt) || (!fmt_is_pal(ws[0].fmt) && ws[i].fmt != ws[0].fmt))
+      return hipErrorInvalidValue;
+    if (col0s[i] != col0s[0] + (i ? grp.pcol[i - 1] + (int64_t)ws[i - 1].n : 0)) return hipErrorInvalidValue;
+    grp.w[i] = ws[i];
+    grp.ycol[i] = col0s[i];
+    grp.pcol[i] = col0s[i] - col0s[0];
+    grp.ntiles[i] = (int)((ws[i].n + (uint64_t)kTiles2[tile].bn - 1) / (uint64_t)kTiles2[tile].bn);
+  }
+  grp.count = count;
+  return launch_group(grp, x, batch, y, ldy, tile, split_hint, part, part_elems, s);
+}
+
+// partial floats of a group launch (0 when K is not split)
+size_t mfma2_group_partial_elems(const WeightView* ws, int count, int64_t batch, int tile, int split_hint) {
+  WeightView wide = ws[0];
+  uint64_t ntot = 0;
+  for (int i = 0; i < count; ++i) ntot += ws[i].n;
+  wide.n = ntot;
+  return mfma2_partial_elems(wide, batch, tile, split_hint);
 }
 
 }  // namespace uw

@@ -153,6 +153,25 @@ hipError_t launch_sum_slices(const float* part, int slices, uint64_t n, int64_t 
 // gemm_mfma.hip
 int mfma2_tile_count();
 void mfma2_tile_dims(int tile, int* bm, int* bn);
+// A group of matrices in one LDS-tiled launch (same K, layout, format class)
+constexpr int kMfma2GroupMax = 4;
+struct Mfma2Group {
+  WeightView w[kMfma2GroupMax];
+  int64_t ycol[kMfma2GroupMax];   // first output column of each matrix in y
+  int64_t pcol[kMfma2GroupMax];   // ... in the group's partial rows (split K)
+  int ntiles[kMfma2GroupMax];     // N tiles of each matrix
+  int count;
+};
+hipError_t launch_mfma2_group(const WeightView* ws, int count, const uint16_t* x, int64_t batch, float* y,
+                              int64_t ldy, const int64_t* col0s, int tile, int split_hint, float* part,
+                              size_t part_elems, hipStream_t s);
+size_t mfma2_group_partial_elems(const WeightView* ws, int count, int64_t batch, int tile, int split_hint);
+// Grouped matmul in one LDS-tiled launch when the group's default (or forced)
+// kernel is an LDS tile: SIZE_MAX when not, else the partial floats it needs.
+size_t gemm_tile_group_partial_elems(const WeightView* ws, int count, int64_t batch, const uw_kernel_cfg* cfg);
+hipError_t launch_gemm_tile_group(const WeightView* ws, int count, const uint16_t* x, int64_t batch, float* y,
+                                  int64_t ldy, const int64_t* col0s, const uw_kernel_cfg* cfg, float* part,
+                                  size_t part_elems, hipStream_t s);
 int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint);
 size_t mfma2_partial_elems(const WeightView& w, int64_t batch, int tile, int split_hint);
 hipError_t launch_mfma2(const WeightView& w, const uint16_t* x, int64_t batch, float* y, int64_t ldy, int64_t col0,
