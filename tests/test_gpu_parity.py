@@ -298,11 +298,14 @@ def test_grouped_matmul(uw, synth, oracle):
     general lookup; more than eight rows go in chunks); a group of five, a
     group holding a [K][N] matrix and batches that resolve to MFMA kernels
     are launched one matrix at a time; at 5 to 8 rows a group of small
-    matrices takes the grouped GEMV by default.  Every column block is
-    checked against the fp64 reference."""
+    matrices takes the grouped GEMV by default; where the group's kernel is
+    an LDS tile (80 and 300 rows, a forced odd split, a [K][N]-only group)
+    the whole group is one launch.  Every column block is checked against
+    the fp64 reference."""
     say("grouped matmul")
     k = 2048
-    specs = [(700, 0, 0.0), (300, 0, 0.002), (1100, 0, 0.0), (64, 0, 0.002), (520, 0, 0.0), (384, 1, 0.002)]
+    specs = [(700, 0, 0.0), (300, 0, 0.002), (1100, 0, 0.0), (64, 0, 0.002), (520, 0, 0.0), (384, 1, 0.002),
+             (320, 1, 0.0)]
     ms, wnps = [], []
     for i, (n, layout, out) in enumerate(specs):
         r, c = (n, k) if layout == 0 else (k, n)
@@ -312,16 +315,19 @@ def test_grouped_matmul(uw, synth, oracle):
         ms.append(m)
         wnps.append(bits(w))
     assert _palette_is_run(ms[0]) and not _palette_is_run(ms[1])
-    groups = [(0, 1), (0, 1, 2, 3), (1, 3), (0, 1, 2, 3, 4), (0, 5, 1)]
+    groups = [(0, 1), (0, 1, 2, 3), (1, 3), (0, 1, 2, 3, 4), (0, 5, 1), (5, 6)]
     for idx in groups:
         sub = [ms[i] for i in idx]
         N = sum(ms[i].info().n for i in idx)
-        for batch, cfg in ((1, None), (3, None), (7, None), (9, {"variant": 1}), (24, None)):
+        for batch, cfg in ((1, None), (3, None), (7, None), (9, {"variant": 1}), (24, None), (80, None),
+                           (300, None), (100, {"variant": 2 + 7, "split_k": 3})):
             x = synth.activations(batch, k, seed=batch + 7).to(DEV)
             x_np = bits(x)
             for p in (0, 1, 3):
                 y = torch.full((batch, N), float("nan"), dtype=torch.float32, device=DEV)
                 ws_bytes = sum(uw.uw_workspace_size(m, p, batch) for m in sub)
+                if cfg and cfg.get("split_k"):   # forced slices: partial rows of every matrix
+                    ws_bytes += 4 * cfg["split_k"] * batch * N + 4096
                 ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV)
                 uw.uw_matmul_reconstruct_grouped(sub, p, x, y, ws, cfg=cfg)
                 torch.cuda.synchronize()
