@@ -132,8 +132,10 @@ constexpr int w_tile_elems() { return LAYOUT == 0 ? BN * kLDK : kBK * (BN + 16);
 // NW waves per block (4 or 8); with 8 two waves share each SIMD, so one
 // wave's rebuild arithmetic can issue while the other's MFMAs run.
 // One launch serves a group of up to four matrices with the same K, layout
-// and format (blockIdx.y picks the matrix; blocks past a smaller matrix's
-// tiles return at once): matrix g writes columns ycol[g].. of y, or columns
+// and format.  Grid x holds every matrix's tiles back to back (matrix g from
+// block bstart[g]), so no block is idle and the hardware's round-robin deal
+// of blocks to XCDs spreads each matrix evenly; matrix g writes columns
+// ycol[g].. of y, or columns
 // pcol[g].. of the partial rows (pld wide) when K is split.
 template <int LAYOUT, int FMT, int BM, int BN, int WGM, int NW = 4>
 __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_t* __restrict__ x, int B,
@@ -151,15 +153,15 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
   static_assert(TM >= 1 && TN >= 1 && XC >= 1 && WC >= 1, "tile too small");
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
-  const int g = (int)blockIdx.y;
+  int g = 0;
+  while (g + 1 < grp.count && (int)blockIdx.x >= grp.bstart[g + 1]) ++g;
   const int ntiles = grp.ntiles[g];
-  if ((int)blockIdx.x >= ntiles * mtiles) return;   // uniform: before any barrier
   const WeightView w = grp.w[g];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int64_t N = (int64_t)w.n, K = (int64_t)w.k;
   int nt, mt;
-  block_tile((int)blockIdx.x, ntiles, mtiles, nt, mt);
+  block_tile((int)blockIdx.x - grp.bstart[g], ntiles, mtiles, nt, mt);
   const int64_t n0 = (int64_t)nt * BN, m0 = (int64_t)mt * BM;
   const int64_t kb = (int64_t)blockIdx.z * kslice;
   const int64_t ke = kb + kslice < K ? kb + kslice : K;
@@ -442,19 +444,22 @@ size_t mfma2_partial_elems(const WeightView& w, int64_t batch, int tile, int spl
 // One launch over the group's tiles; K split as for one matrix as wide as the
 // group, the partial rows group-wide so one reduction serves every matrix.
 // The matrices' output columns in y must be consecutive from ycol[0].
-static hipError_t launch_group(const Mfma2Group& grp, const uint16_t* x, int64_t batch, float* y, int64_t ldy,
+static hipError_t launch_group(Mfma2Group grp, const uint16_t* x, int64_t batch, float* y, int64_t ldy,
                                int tile, int split_hint, float* part, size_t part_elems, hipStream_t s) {
   const Tile2 t = kTiles2[tile];
   const WeightView& w0 = grp.w[0];
   WeightView wide = w0;   // the group as one matrix: tiles, slices, partial rows
   int fmt = w0.fmt;
   uint64_t ntot = 0;
-  int ntmax = 0;
+  const int mtiles = (int)((batch + t.bm - 1) / t.bm);
+  int64_t nblocks = 0;
   for (int i = 0; i < grp.count; ++i) {
     ntot += grp.w[i].n;
-    if (grp.ntiles[i] > ntmax) ntmax = grp.ntiles[i];
+    grp.bstart[i] = (int)nblocks;
+    nblocks += (int64_t)grp.ntiles[i] * mtiles;
     if (grp.w[i].fmt != fmt) fmt = kFmtPal;   // palette kinds mixed: the general lookup
   }
+  if (nblocks <= 0 || nblocks > INT32_MAX) return hipErrorInvalidValue;
   wide.n = ntot;
   wide.fmt = fmt;
   const int slices = mfma2_slices(wide, batch, tile, split_hint);
@@ -476,8 +481,7 @@ static hipError_t launch_group(const Mfma2Group& grp, const uint16_t* x, int64_t
     hipError_t e = allow_dynamic_lds((const void*)f, (int)lds);
     if (e != hipSuccess) return e;
   }
-  const int mtiles = (int)((batch + t.bm - 1) / t.bm);
-  dim3 grid((unsigned)(ntmax * mtiles), (unsigned)grp.count, (unsigned)slices);
+  dim3 grid((unsigned)nblocks, 1, (unsigned)slices);
   hipLaunchKernelGGL(f, grid, dim3(64 * t.waves), lds, s, grp, x, (int)batch, y, ldy, kslice, split ? part : nullptr,
                      (int64_t)ntot, mtiles);
   hipError_t e = hipGetLastError();

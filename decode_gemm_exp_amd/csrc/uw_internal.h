@@ -160,6 +160,7 @@ struct Mfma2Group {
   int64_t ycol[kMfma2GroupMax];   // first output column of each matrix in y
   int64_t pcol[kMfma2GroupMax];   // ... in the group's partial rows (split K)
   int ntiles[kMfma2GroupMax];     // N tiles of each matrix
+  int bstart[kMfma2GroupMax];     // first block (grid x) of each matrix, set at launch
   int count;
 };
 hipError_t launch_mfma2_group(const WeightView* ws, int count, const uint16_t* x, int64_t batch, float* y,
