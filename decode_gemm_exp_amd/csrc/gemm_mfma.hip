@@ -134,9 +134,9 @@ constexpr int w_tile_elems() { return LAYOUT == 0 ? BN * kLDK : kBK * (BN + 16);
 // One launch serves a group of up to four matrices with the same K, layout
 // and format.  Grid x holds every matrix's tiles back to back (matrix g from
 // block bstart[g]), so no block is idle and the hardware's round-robin deal
-// of blocks to XCDs spreads each matrix evenly; matrix g writes columns
-// ycol[g].. of y, or columns
-// pcol[g].. of the partial rows (pld wide) when K is split.
+// of blocks to XCDs spreads each matrix evenly.  Matrix g writes columns
+// ycol[g].. of y, or columns pcol[g].. of the partial rows (pld wide) when K
+// is split.
 template <int LAYOUT, int FMT, int BM, int BN, int WGM, int NW = 4>
 __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_t* __restrict__ x, int B,
                                                    float* __restrict__ y, int64_t ldy, int64_t kslice,
@@ -431,6 +431,17 @@ int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint) {
   int s = split_hint > 0 ? split_hint : 1;
   if (split_hint <= 0)
     while (blocks * s < target && blocks * s * 2 <= hold && (int64_t)w.k / (64 * (s * 2)) >= 8) s *= 2;
+  // beyond 64 rows, an unsplit palette grid that spills at most a quarter
+  // round past whole rounds of resident blocks runs its last round of
+  // full-length tiles on a mostly idle chip; two slices halve that tail
+  // (70B q+k+v grouped, 640 128x128 tiles on 512 slots: 1024 rows 361 ->
+  // 326 us, 896 rows 342 -> 319 us; 8B gate, 640 rows: 182 -> 173 us).
+  // BF16 tiles run closer to the MFMA rate and lose more to the reduction
+  // pass than the tail costs (the same three cases 5-10 % slower split).
+  if (split_hint <= 0 && batch > 64 && s == 1 && fmt_is_pal(w.fmt)) {
+    const int64_t slots = cus * (per_cu > 0 ? per_cu : 1), tail = blocks % slots;
+    if (blocks > slots && tail > 0 && tail <= slots / 4 && (int64_t)w.k / (64 * 2) >= 8) s = 2;
+  }
   const int64_t steps = ((int64_t)w.k + 63) / 64;
   if (s > steps) s = (int)steps;
   return s;
