@@ -230,6 +230,25 @@ def test_gemm_mid_batch_split(uw, synth, oracle, layout, batch):
             check_gemm(oracle, y, x_np, w_np, layout, what=f"pipeline {p} variant {v} split {sk}")
 
 
+# a palette grid whose last round of resident blocks is short: 72 N tiles x 8
+# M tiles of 128x128 on 256 CUs holding two blocks each leaves 64 blocks for a
+# second round, so the default splits K in two; the BF16 pipeline keeps one
+# slice; a ragged batch (1000 rows)
+def test_gemm_palette_tail_split(uw, synth, oracle):
+    n, k, batch = 9216, 1024, 1000
+    say(f"gemm palette tail split n={n} k={k} batch={batch}")
+    w = synth.weights(n, k, 0.02, 0.005, 10, seed=417).to(DEV)
+    x = synth.activations(batch, k, seed=418).to(DEV)
+    m = gpu_compress(uw, w, n, k, 0)
+    uw.uw_transcode_palette(m, None)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert uw.uw_workspace_size(m, 3, batch) >= 2 * batch * n * 4, "expected a two-slice K split"
+    w_np, x_np = bits(w), bits(x)
+    for p in range(4):
+        y = run_pipeline(uw, m, p, x)
+        check_gemm(oracle, y, x_np, w_np, 0, what=f"pipeline {p}")
+
+
 # register-fed MFMA kernels (stored [N][K]): row counts that leave partial
 # 32- and 64-row blocks, K with a partial 128-wide window (K % 128 == 64), a
 # K whose windows split unevenly over the four waves, batches across the
