@@ -60,6 +60,7 @@ def lib():
         L.uwo_export.argtypes = [vp, vp, u64]
         L.uwo_package_merge.argtypes = [vp, i32, i32, vp]
         L.uwo_canonical.argtypes = [vp, i32, vp]
+        L.uwo_gemm_ref.argtypes = [vp, u64, u64, vp, u64, u32, vp, u64, vp, vp]
         _lib = L
     return _lib
 
@@ -211,7 +212,9 @@ def canonical(lengths) -> np.ndarray:
 # fp64, with the magnitude sum A[b][n] = sum_k |x[b][k] * W[n][k]| used by the
 # per-element bound |y_gpu - y| <= 2^-10 * A.  ([EVC] "重建矩陣乘法核心運作":
 # the reconstructive matmul computes the same product as a matmul on the
-# uncompressed weights; the bound is the stated acceptance rule.)
+# uncompressed weights; the bound is the stated acceptance rule.)  The sums are
+# uwo.cpp's ``gemm_ref`` (k ascending, one column at a time); this wrapper only
+# hands disjoint column ranges to worker threads.
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns to float64."""
@@ -224,16 +227,46 @@ def logical_weight(w_stored: np.ndarray, layout: int) -> np.ndarray:
     return w_stored if layout == 0 else w_stored.T
 
 
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
 def gemm_ref(x_bits: np.ndarray, w_stored: np.ndarray, layout: int,
-             cols: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
+             cols: np.ndarray | None = None, threads: int | None = None) -> tuple[np.ndarray, np.ndarray]:
     """(y, A) in fp64 for y = x . W^T; ``cols`` restricts to output columns n."""
-    x = bf16_to_f64(x_bits)
-    W = logical_weight(w_stored, layout)
-    if cols is not None:
-        W = W[cols]
-    Wf = bf16_to_f64(np.ascontiguousarray(W))
-    y = x @ Wf.T
-    A = np.abs(x) @ np.abs(Wf).T
+    import concurrent.futures as cf
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    w = np.ascontiguousarray(w_stored, dtype=np.uint16)
+    assert x.ndim == 2 and w.ndim == 2
+    batch, K = x.shape
+    N = w.shape[0] if layout == 0 else w.shape[1]
+    assert (w.shape[1] if layout == 0 else w.shape[0]) == K
+    sel = np.arange(N, dtype=np.int64) if cols is None else np.ascontiguousarray(cols, dtype=np.int64)
+    nc = len(sel)
+    y = np.zeros((batch, nc), np.float64)
+    A = np.zeros((batch, nc), np.float64)
+    nt = max(1, min(threads or default_threads(), nc))
+    bounds = [nc * t // nt for t in range(nt + 1)]
+
+    def run(t: int) -> int:
+        c0, c1 = bounds[t], bounds[t + 1]
+        if c1 <= c0:
+            return UWO_OK
+        yp = np.zeros((batch, c1 - c0), np.float64)
+        ap = np.zeros((batch, c1 - c0), np.float64)
+        part = np.ascontiguousarray(sel[c0:c1])
+        st = lib().uwo_gemm_ref(_ptr(x), batch, K, _ptr(w), N, layout, _ptr(part), c1 - c0,
+                                _ptr(yp), _ptr(ap))
+        y[:, c0:c1] = yp
+        A[:, c0:c1] = ap
+        return st
+
+    if nt == 1:
+        sts = [run(0)]
+    else:
+        with cf.ThreadPoolExecutor(max_workers=nt) as ex:
+            sts = list(ex.map(run, range(nt)))
+    assert all(st == UWO_OK for st in sts), "oracle gemm_ref rejected its arguments"
     return y, A
 
 

@@ -511,6 +511,48 @@ std::vector<uint8_t> serialise(const Oracle& o) {
   return b;
 }
 
+// ---- GEMM reference ([EVC] "重建矩陣乘法核心運作") ---------------------------
+// The reconstructive matmul computes the product a matmul on the uncompressed
+// weights gives: y = x . W^T.  The reference is that definition in fp64 on the
+// ORIGINAL bf16 weights, k ascending:
+//   y[b][n] = sum_k x[b][k] * W[n][k],   A[b][n] = sum_k |x[b][k] * W[n][k]|,
+// where W[n][k] = stored[n][k] (layout 0) or stored[k][n] (layout 1).  A is the
+// magnitude the acceptance bound |y_gpu - y| <= 2^-10 * A scales with.
+
+// Exact widening of a bf16 bit pattern: the pattern is the top half of the
+// fp32 with the same value, and every fp32 is exact in fp64.
+inline double bf16_value(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+// Columns cols[0..ncols) of y and A (row-major [batch][ncols]); every column
+// when cols is null (ncols must then be N).
+int gemm_ref(const uint16_t* x, uint64_t batch, uint64_t K, const uint16_t* stored, uint64_t N,
+             uint32_t layout, const int64_t* cols, uint64_t ncols, double* y, double* A) {
+  if (!x || !stored || !y || !A || layout > 1) return UWO_ERR_INVALID;
+  std::vector<double> wrow(K);
+  for (uint64_t j = 0; j < ncols; ++j) {
+    const uint64_t n = cols ? (uint64_t)cols[j] : j;
+    if (n >= N) return UWO_ERR_INVALID;
+    for (uint64_t k = 0; k < K; ++k)
+      wrow[k] = bf16_value(layout == 0 ? stored[n * K + k] : stored[k * N + n]);
+    for (uint64_t b = 0; b < batch; ++b) {
+      double sum = 0.0, mag = 0.0;
+      for (uint64_t k = 0; k < K; ++k) {
+        const double p = bf16_value(x[b * K + k]) * wrow[k];
+        sum += p;
+        mag += p < 0 ? -p : p;
+      }
+      y[b * ncols + j] = sum;
+      A[b * ncols + j] = mag;
+    }
+  }
+  return UWO_OK;
+}
+
 }  // namespace
 
 // ---- C entry points used by oracle/oracle.py ---------------------------------
@@ -629,6 +671,11 @@ int uwo_package_merge(const uint64_t* weights, int n, int lmax, uint8_t* len_out
 int uwo_canonical(const uint8_t* len, int n, uint16_t* code_out) {
   canonical_codes(len, n, code_out);
   return UWO_OK;
+}
+
+int uwo_gemm_ref(const uint16_t* x, uint64_t batch, uint64_t K, const uint16_t* stored, uint64_t N,
+                 uint32_t layout, const int64_t* cols, uint64_t ncols, double* y, double* A) {
+  return gemm_ref(x, batch, K, stored, N, layout, cols, ncols, y, A);
 }
 
 }  // extern "C"

@@ -435,17 +435,29 @@ def test_gemm_check_rule(oracle):
 
 def test_export_header_fields(oracle):
     import struct
+    g = load("uwf1_three_groups.json")
     m = oracle.compress(three_group_input(), seg_groups=2)
     blob = m.export()
     assert blob[:4] == b"UWF1"
     ver, layout, sg = struct.unpack_from("<III", blob, 4)
     rows, cols = struct.unpack_from("<QQ", blob, 16)
     P, ncoded = struct.unpack_from("<II", blob, 32)
-    assert (ver, layout, sg, rows, cols, P, ncoded) == (1, 0, 2, 1, 192, 16, 3)
-    assert list(blob[40:56]) == m.palette.tolist()
-    assert list(blob[56:72]) == m.code_len.tolist()
+    assert (ver, layout, sg, rows, cols, P, ncoded) == (1, 0, 2, 1, 192, g["palette_size"], g["n_coded"])
+    assert list(blob[40:56]) == g["palette"]
+    assert list(blob[56:72]) == g["code_len"]
     V, W = struct.unpack_from("<QQ", blob, 72)
-    assert (V, W) == (1, 6)
+    assert (V, W) == (g["V"], g["cases"]["seg_groups_2"]["W"])
+    # the histogram block: 256 little-endian u64, entry v at 88 + 8 v
+    hist = struct.unpack_from("<256Q", blob, g["header_hist_offset"])
+    want = [0] * 256
+    for v, c in g["hist_nonzero"].items():
+        want[int(v)] = c
+    assert list(hist) == want
+    assert sum(hist) == 192
+    # the coded-count block: 16 u64, slot s at 2136 + 8 s, then zero padding
+    coded = struct.unpack_from("<16Q", blob, g["header_coded_offset"])
+    assert list(coded) == g["coded_count"]
+    assert blob[2136 + 128:2304] == bytes(2304 - 2136 - 128)
     # sections start at 2304 and are padded to 256 bytes
     assert blob[2304:2304 + 192] == m.section("sm").tobytes()
     assert len(blob) == 2304 + 256 * 6
