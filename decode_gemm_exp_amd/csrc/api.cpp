@@ -70,33 +70,32 @@ namespace {
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline uint64_t pad256(uint64_t n) { return (n + 255) / 256 * 256; }
 
+// device memory through allocator a (uw_set_allocator's hooks, or hipMalloc)
 template <typename T>
-uw_status dev_alloc(T** p, uint64_t bytes) {
-  *p = nullptr;
-  if (bytes == 0) return UW_OK;
+uw_status dev_alloc(const uw_allocator& a, T** p, uint64_t bytes) {
   void* q = nullptr;
-  hipError_t e = hipMalloc(&q, bytes);
-  if (e != hipSuccess) return e == hipErrorOutOfMemory ? UW_ERR_NOMEM : UW_ERR_DEVICE;
+  const uw_status st = alloc_with(a, &q, bytes);
   *p = static_cast<T*>(q);
-  return UW_OK;
+  return st;
 }
 
 template <typename T>
-void dev_free(T*& p) {
-  if (p) (void)hipFree((void*)p);
+void dev_free(const uw_allocator& a, T*& p) {
+  if (p) free_with(a, (void*)p);
   p = nullptr;
 }
 
 void free_sections(uw_matrix* m) {
-  dev_free(m->sm);
-  dev_free(m->vflags);
-  dev_free(m->vrank);
-  dev_free(m->vexp);
-  dev_free(m->seg_off);
-  dev_free(m->stream);
-  dev_free(m->lut);
-  dev_free(m->pidx);
-  dev_free(m->corrupt);
+  const uw_allocator a = m->alloc;
+  dev_free(a, m->sm);
+  dev_free(a, m->vflags);
+  dev_free(a, m->vrank);
+  dev_free(a, m->vexp);
+  dev_free(a, m->seg_off);
+  dev_free(a, m->stream);
+  dev_free(a, m->lut);
+  dev_free(a, m->pidx);
+  dev_free(a, m->corrupt);
 }
 
 // Stream allocation: W + 2 words, rounded up so that the decoder's aligned
@@ -162,7 +161,7 @@ void pal_words(const Tables& t, PalView* out) {
 uw_status upload_lut(uw_matrix* m, hipStream_t s) {
   std::vector<uint32_t> lut((size_t)kLutWords << kLutBits);
   build_decode_lut(m->t, lut.data());
-  if (!m->lut) UW_CHECK(dev_alloc(&m->lut, lut.size() * 4));
+  if (!m->lut) UW_CHECK(dev_alloc(m->alloc, &m->lut, lut.size() * 4));
   UW_HIP(hipMemcpyAsync(m->lut, lut.data(), lut.size() * 4, hipMemcpyHostToDevice, s));
   UW_HIP(hipStreamSynchronize(s));
   return UW_OK;
@@ -190,52 +189,6 @@ enum : uint32_t {
   kOffPalSize = 32, kOffNCoded = 36, kOffPalette = 40, kOffLen = 56, kOffV = 72, kOffW = 80,
   kOffHist = 88, kOffCoded = 2136
 };
-
-// ---- CU-masked streams for the sequence runner -------------------------------------
-struct SplitStreams {
-  hipStream_t dec = nullptr, gemm = nullptr;
-};
-std::mutex g_split_mu;
-std::map<std::pair<int, int>, SplitStreams> g_split;   // (device, decode CUs)
-
-// Mask of `count` CUs starting at `first`, in the runtime's CU numbering.
-std::vector<uint32_t> cu_mask(int total, int first, int count) {
-  std::vector<uint32_t> m((size_t)(total + 31) / 32, 0u);
-  for (int i = first; i < first + count && i < total; ++i) m[(size_t)i / 32] |= 1u << (i % 32);
-  return m;
-}
-
-uw_status split_streams(int decode_cus, SplitStreams* out) {
-  int dev = 0;
-  UW_HIP(hipGetDevice(&dev));
-  std::lock_guard<std::mutex> lk(g_split_mu);
-  int total_cus = 0;
-  UW_HIP(hipDeviceGetAttribute(&total_cus, hipDeviceAttributeMultiprocessorCount, dev));
-  if (decode_cus > total_cus) decode_cus = total_cus;
-  auto it = g_split.find({dev, decode_cus});
-  if (it != g_split.end()) {
-    *out = it->second;
-    return UW_OK;
-  }
-  hipDeviceProp_t prop;
-  UW_HIP(hipGetDeviceProperties(&prop, dev));
-  const int total = prop.multiProcessorCount;
-  if (decode_cus <= 0) return UW_ERR_INVALID;
-  SplitStreams ss;
-  if (decode_cus >= total) {
-    // no mask: the two kernels share every CU, the hardware interleaves their blocks
-    UW_HIP(hipStreamCreateWithFlags(&ss.dec, hipStreamNonBlocking));
-    UW_HIP(hipStreamCreateWithFlags(&ss.gemm, hipStreamNonBlocking));
-  } else {
-    std::vector<uint32_t> md = cu_mask(total, 0, decode_cus);
-    std::vector<uint32_t> mg = cu_mask(total, decode_cus, total - decode_cus);
-    UW_HIP(hipExtStreamCreateWithCUMask(&ss.dec, (uint32_t)md.size(), md.data()));
-    UW_HIP(hipExtStreamCreateWithCUMask(&ss.gemm, (uint32_t)mg.size(), mg.data()));
-  }
-  g_split[{dev, decode_cus >= total ? total : decode_cus}] = ss;
-  *out = ss;
-  return UW_OK;
-}
 
 // ---- preprocessing + GEMM of one matrix -------------------------------------------------
 size_t prep_bytes(const uw_matrix* m, int p) {
@@ -308,6 +261,71 @@ size_t partial_bytes(const uw_matrix* m, int p, int64_t batch, const uw_kernel_c
   return pad256(gemm_partial_elems(v, batch, cfg) * sizeof(float));
 }
 
+bool pipeline_feasible(const uw_matrix* m, int p) {
+  if (p == UW_PIPE_PALETTE_DIRECT) return m->pidx != nullptr;
+  return p >= UW_PIPE_FULL && p <= UW_PIPE_PALETTE_TRANSCODE && m->stream != nullptr;
+}
+
+bool pipeline_arg(int p) { return (p >= UW_PIPE_FULL && p <= UW_PIPE_PALETTE_DIRECT) || p == UW_PIPE_AUTO; }
+
+bool cfg_empty(const uw_kernel_cfg& c) { return c.variant <= 0 && c.split_k <= 0 && c.decode_cus <= 0; }
+
+// What one call on m runs: the pipeline (UW_PIPE_AUTO resolved) and the
+// kernel configuration (the caller's; without one, the tuned entry's when it
+// names that pipeline; else none, i.e. the library default).
+struct Plan {
+  int p = UW_PIPE_EXPONENT;
+  uw_kernel_cfg cfg{};
+  bool has_cfg = false;
+  const uw_kernel_cfg* cfgp() const { return has_cfg ? &cfg : nullptr; }
+};
+
+Plan plan_call(const uw_matrix* m, int p, int64_t batch, const uw_kernel_cfg* cfg) {
+  Plan r;
+  uw_tune_entry e;
+  const bool tuned = batch > 0 && !m->fp8 &&
+                     tuned_lookup(logical_n(m), logical_k(m), (int)m->layout, residency_of(m), batch, &e);
+  if (p == UW_PIPE_AUTO)
+    r.p = tuned && pipeline_feasible(m, e.pipeline) ? e.pipeline
+          : m->pidx ? UW_PIPE_PALETTE_DIRECT : UW_PIPE_EXPONENT;
+  else
+    r.p = p;
+  if (cfg) {
+    r.cfg = *cfg;
+    r.has_cfg = true;
+  } else if (tuned && e.pipeline == r.p) {
+    r.cfg.variant = e.variant;
+    r.cfg.split_k = e.split_k;
+    r.cfg.decode_cus = e.decode_cus;
+    r.cfg.reserved = 0;
+    r.has_cfg = true;
+  }
+  return r;
+}
+
+// The pipeline a grouped call runs: the tuned one when every matrix's entry
+// names the same feasible pipeline, else direct palette when every matrix
+// has resident indices, else exponent.
+int plan_group_pipeline(const uw_matrix* const* ms, int count, int p, int64_t batch) {
+  if (p != UW_PIPE_AUTO) return p;
+  int tp = -1;
+  bool same = true, all_pidx = true;
+  for (int i = 0; i < count; ++i) {
+    const uw_matrix* m = ms[i];
+    all_pidx = all_pidx && m->pidx != nullptr;
+    uw_tune_entry e;
+    if (!m->fp8 && tuned_lookup(logical_n(m), logical_k(m), (int)m->layout, residency_of(m), batch, &e) &&
+        pipeline_feasible(m, e.pipeline)) {
+      if (tp < 0) tp = e.pipeline;
+      else if (tp != e.pipeline) same = false;
+    } else {
+      same = false;
+    }
+  }
+  if (same && tp >= 0) return tp;
+  return all_pidx ? UW_PIPE_PALETTE_DIRECT : UW_PIPE_EXPONENT;
+}
+
 uw_status check_matmul_args(const uw_matrix* m, int p, const uint16_t* x, int64_t batch, const float* y) {
   if (!m || !x || !y || batch <= 0) return UW_ERR_INVALID;
   if (m->fp8) return UW_ERR_UNSUPPORTED;   // the GEMMs rebuild BF16 weights
@@ -363,25 +381,27 @@ uw_status compress_args(const void* w_dev, int64_t n, int64_t k, uw_layout layou
 // The coding passes over a device array of 16-bit words whose bits 14..7
 // are the coded exponent (BF16 weights, or FP8 exponent fields placed there).
 uw_status compress_words(const uint16_t* w_dev, uint64_t rows, uint64_t cols, uw_layout layout, uint32_t sg,
-                         hipStream_t s, uw_matrix** out) {
+                         const uw_allocator& alloc, hipStream_t s, uw_matrix** out) {
   uw_matrix* m = new (std::nothrow) uw_matrix();
   if (!m) return UW_ERR_NOMEM;
+  m->alloc = alloc;
   struct Guard {
     uw_matrix* m;
+    uw_allocator a;
     void* scratch = nullptr;
     ~Guard() {
-      if (scratch) (void)hipFree(scratch);
+      if (scratch) free_with(a, scratch);
       if (m) { free_sections(m); delete m; }
     }
-  } guard{m};
+  } guard{m, alloc};
   UW_HIP(hipGetDevice(&m->device));
   shape_from(m, rows, cols, (uint32_t)layout, sg);
 
-  UW_CHECK(dev_alloc(&m->sm, m->numel));
-  UW_CHECK(dev_alloc(&m->vflags, 4 * m->flag_words));
-  UW_CHECK(dev_alloc(&m->vrank, 4 * m->flag_words));
-  UW_CHECK(dev_alloc(&m->seg_off, 4 * (m->segments + 1)));
-  UW_CHECK(dev_alloc(&m->corrupt, sizeof(int)));
+  UW_CHECK(dev_alloc(m->alloc, &m->sm, m->numel));
+  UW_CHECK(dev_alloc(m->alloc, &m->vflags, 4 * m->flag_words));
+  UW_CHECK(dev_alloc(m->alloc, &m->vrank, 4 * m->flag_words));
+  UW_CHECK(dev_alloc(m->alloc, &m->seg_off, 4 * (m->segments + 1)));
+  UW_CHECK(dev_alloc(m->alloc, &m->corrupt, sizeof(int)));
   UW_HIP(hipMemsetAsync(m->corrupt, 0, sizeof(int), s));
 
   // scratch: hist u32[256] | coded u32[16] | total u64 | slot/len tables | codebook u32[256] | seg words |
@@ -391,7 +411,7 @@ uw_status compress_words(const uint16_t* w_dev, uint64_t rows, uint64_t cols, uw
   const uint64_t off_tiles = pad256(off_seg + 4 * m->segments);
   const uint64_t ntiles = scan_tiles(m->segments > m->flag_words ? m->segments : m->flag_words);
   void* scratch = nullptr;
-  UW_CHECK(dev_alloc(&scratch, off_tiles + 8 * ntiles + 256));
+  UW_CHECK(dev_alloc(m->alloc, &scratch, off_tiles + 8 * ntiles + 256));
   guard.scratch = scratch;
   uint8_t* sc = static_cast<uint8_t*>(scratch);
   uint32_t* d_hist = reinterpret_cast<uint32_t*>(sc);
@@ -426,7 +446,7 @@ uw_status compress_words(const uint16_t* w_dev, uint64_t rows, uint64_t cols, uw
   m->V = vtotal;
   for (int i = 0; i < kPal; ++i) m->t.coded_count[i] = coded32[i];
   finish_code(m->t);
-  UW_CHECK(dev_alloc(&m->vexp, 64 * m->V));
+  UW_CHECK(dev_alloc(m->alloc, &m->vexp, 64 * m->V));
 
   // 3. segment lengths and offsets
   uint8_t len_tab[256];
@@ -452,7 +472,7 @@ uw_status compress_words(const uint16_t* w_dev, uint64_t rows, uint64_t cols, uw
 
   // 4. encode
   const uint64_t sw = stream_alloc_words(m->W);
-  UW_CHECK(dev_alloc(&m->stream, 4 * sw));
+  UW_CHECK(dev_alloc(m->alloc, &m->stream, 4 * sw));
   UW_HIP(hipMemsetAsync(m->stream, 0, 4 * sw, s));
   UW_HIP(launch_encode(w_dev, m->groups, sg, m->segments, d_book, m->vflags, m->vrank, m->seg_off, m->stream,
                        m->vexp, s));
@@ -473,7 +493,7 @@ uw_status uw_compress(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout lay
   uint32_t sg = 0;
   uint64_t rows = 0, cols = 0;
   UW_CHECK(compress_args(w_dev, n, k, layout, opts, out, &sg, &rows, &cols));
-  return compress_words(w_dev, rows, cols, layout, sg, static_cast<hipStream_t>(stream), out);
+  return compress_words(w_dev, rows, cols, layout, sg, current_allocator(), static_cast<hipStream_t>(stream), out);
 } catch (...) {
   return UW_ERR_NOMEM;
 }
@@ -485,21 +505,23 @@ uw_status uw_compress_fp8(const uint8_t* w_dev, int64_t n, int64_t k, uw_layout 
   UW_CHECK(compress_args(w_dev, n, k, layout, opts, out, &sg, &rows, &cols));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint64_t numel = rows * cols;
+  const uw_allocator alloc = current_allocator();
   struct Temp {
+    uw_allocator a;
     uint16_t* fields = nullptr;
     uint8_t* nib = nullptr;
     ~Temp() {
-      dev_free(fields);
-      dev_free(nib);
+      dev_free(a, fields);
+      dev_free(a, nib);
     }
-  } t;
-  UW_CHECK(dev_alloc(&t.fields, 2 * numel));
-  UW_CHECK(dev_alloc(&t.nib, numel / 2));
+  } t{alloc};
+  UW_CHECK(dev_alloc(alloc, &t.fields, 2 * numel));
+  UW_CHECK(dev_alloc(alloc, &t.nib, numel / 2));
   UW_HIP(launch_fp8_fields(w_dev, numel, t.fields, s));
   UW_HIP(launch_fp8_pack(w_dev, numel, t.nib, s));
   uw_matrix* m = nullptr;
-  UW_CHECK(compress_words(t.fields, rows, cols, layout, sg, s, &m));   // synchronises at its end
-  dev_free(m->sm);   // the byte section of the field array: replaced by the nibbles
+  UW_CHECK(compress_words(t.fields, rows, cols, layout, sg, alloc, s, &m));   // synchronises at its end
+  dev_free(m->alloc, m->sm);   // the byte section of the field array: replaced by the nibbles
   m->sm = t.nib;
   t.nib = nullptr;
   m->fp8 = true;
@@ -654,6 +676,7 @@ uw_status uw_import(const void* host_blob, size_t nbytes, void* stream, uw_matri
     ~Guard() { if (m) { free_sections(m); delete m; } }
   } guard{m};
   UW_HIP(hipGetDevice(&m->device));
+  m->alloc = current_allocator();
   shape_from(m, rows, cols, layout, sg);
   m->V = tmp.V;
   m->W = tmp.W;
@@ -665,13 +688,13 @@ uw_status uw_import(const void* host_blob, size_t nbytes, void* stream, uw_matri
   m->code_bits = 0;
   for (int i = 0; i < kPal; ++i) m->code_bits += m->t.coded_count[i] * m->t.code_len[i];
   const uint64_t sw = stream_alloc_words(m->W);
-  UW_CHECK(dev_alloc(&m->sm, m->numel));
-  UW_CHECK(dev_alloc(&m->vflags, 4 * m->flag_words));
-  UW_CHECK(dev_alloc(&m->vrank, 4 * m->flag_words));
-  UW_CHECK(dev_alloc(&m->vexp, 64 * m->V));
-  UW_CHECK(dev_alloc(&m->seg_off, 4 * (m->segments + 1)));
-  UW_CHECK(dev_alloc(&m->stream, 4 * sw));
-  UW_CHECK(dev_alloc(&m->corrupt, sizeof(int)));
+  UW_CHECK(dev_alloc(m->alloc, &m->sm, m->numel));
+  UW_CHECK(dev_alloc(m->alloc, &m->vflags, 4 * m->flag_words));
+  UW_CHECK(dev_alloc(m->alloc, &m->vrank, 4 * m->flag_words));
+  UW_CHECK(dev_alloc(m->alloc, &m->vexp, 64 * m->V));
+  UW_CHECK(dev_alloc(m->alloc, &m->seg_off, 4 * (m->segments + 1)));
+  UW_CHECK(dev_alloc(m->alloc, &m->stream, 4 * sw));
+  UW_CHECK(dev_alloc(m->alloc, &m->corrupt, sizeof(int)));
   UW_HIP(hipMemsetAsync(m->corrupt, 0, sizeof(int), s));
   UW_HIP(hipMemsetAsync(m->stream, 0, 4 * sw, s));
   UW_HIP(hipMemcpyAsync(m->sm, b + o_sm, m->numel, hipMemcpyHostToDevice, s));
@@ -720,7 +743,7 @@ uw_status uw_transcode_palette(uw_matrix* m, uint8_t* idx_out_dev, void* stream)
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (idx_out_dev) return decode_to(m, idx_out_dev, kDecodeNibble, s);
   if (!m->stream) return m->pidx ? UW_OK : UW_ERR_STATE;
-  if (!m->pidx) UW_CHECK(dev_alloc(&m->pidx, m->numel / 2));
+  if (!m->pidx) UW_CHECK(dev_alloc(m->alloc, &m->pidx, m->numel / 2));
   return decode_to(m, m->pidx, kDecodeNibble, s);
 }
 
@@ -728,9 +751,9 @@ uw_status uw_drop_stream(uw_matrix* m, void* stream) {
   if (!m) return UW_ERR_INVALID;
   if (!m->pidx) return UW_ERR_STATE;
   UW_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
-  dev_free(m->stream);
-  dev_free(m->seg_off);
-  dev_free(m->lut);
+  dev_free(m->alloc, m->stream);
+  dev_free(m->alloc, m->seg_off);
+  dev_free(m->alloc, m->lut);
   return UW_OK;
 }
 
@@ -738,16 +761,28 @@ uw_status uw_drop_palette(uw_matrix* m, void* stream) {
   if (!m) return UW_ERR_INVALID;
   if (!m->stream) return UW_ERR_STATE;   // would leave no form to decode from
   UW_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
-  dev_free(m->pidx);
+  dev_free(m->alloc, m->pidx);
   return UW_OK;
 }
 
 uw_status uw_workspace_size(const uw_matrix* m, uw_pipeline p, int64_t batch, size_t* bytes) {
-  if (!m || !bytes || batch <= 0 || p < UW_PIPE_FULL || p > UW_PIPE_PALETTE_DIRECT) return UW_ERR_INVALID;
+  if (!m || !bytes || batch <= 0 || !pipeline_arg(p)) return UW_ERR_INVALID;
   if (m->fp8) return UW_ERR_UNSUPPORTED;
-  // enough for any kernel variant a cfg may select at this batch
-  WeightView v = pipeline_view(m, p, nullptr);
-  *bytes = prep_bytes(m, p) + pad256(gemm_partial_elems_max(v, batch, 0) * sizeof(float));
+  // enough for any kernel variant a cfg may select at this batch without a
+  // forced split, and for the tuned choice
+  const Plan r = plan_call(m, p, batch, nullptr);
+  WeightView v = pipeline_view(m, r.p, nullptr);
+  const size_t part = std::max(gemm_partial_elems_max(v, batch, 0), gemm_partial_elems(v, batch, r.cfgp()));
+  *bytes = prep_bytes(m, r.p) + pad256(part * sizeof(float));
+  return UW_OK;
+}
+
+uw_status uw_workspace_size_cfg(const uw_matrix* m, uw_pipeline p, int64_t batch, const uw_kernel_cfg* cfg,
+                                size_t* bytes) {
+  if (!m || !bytes || batch <= 0 || !pipeline_arg(p)) return UW_ERR_INVALID;
+  if (m->fp8) return UW_ERR_UNSUPPORTED;
+  const Plan r = plan_call(m, p, batch, cfg);
+  *bytes = prep_bytes(m, r.p) + partial_bytes(m, r.p, batch, r.cfgp());
   return UW_OK;
 }
 
@@ -759,17 +794,20 @@ static uw_status workspace_for(const uw_matrix* m, int p, int64_t batch, const u
 uw_status uw_matmul_reconstruct(const uw_matrix* m, uw_pipeline p, const uint16_t* x_dev, int64_t batch,
                                 float* y_dev, void* ws_dev, size_t ws_bytes, const uw_kernel_cfg* cfg,
                                 void* stream) {
-  UW_CHECK(check_matmul_args(m, p, x_dev, batch, y_dev));
+  if (!m || !pipeline_arg(p) || batch <= 0) return UW_ERR_INVALID;
+  if (m->fp8) return UW_ERR_UNSUPPORTED;
+  const Plan r = plan_call(m, p, batch, cfg);
+  UW_CHECK(check_matmul_args(m, r.p, x_dev, batch, y_dev));
   size_t need = 0;
-  workspace_for(m, p, batch, cfg, &need);
+  workspace_for(m, r.p, batch, r.cfgp(), &need);
   if (need > ws_bytes || (need && !ws_dev) || !aligned16(ws_dev)) return UW_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
-  UW_CHECK(preprocess(m, p, ws, s));
-  WeightView v = pipeline_view(m, p, ws);
-  const size_t pb = prep_bytes(m, p);
+  UW_CHECK(preprocess(m, r.p, ws, s));
+  WeightView v = pipeline_view(m, r.p, ws);
+  const size_t pb = prep_bytes(m, r.p);
   float* part = reinterpret_cast<float*>(ws + pb);
-  UW_HIP(launch_gemm(v, x_dev, batch, y_dev, (int64_t)v.n, 0, cfg, part, (need - pb) / sizeof(float), s));
+  UW_HIP(launch_gemm(v, x_dev, batch, y_dev, (int64_t)v.n, 0, r.cfgp(), part, (need - pb) / sizeof(float), s));
   return UW_OK;
 }
 
@@ -777,6 +815,7 @@ uw_status uw_matmul_stage(const uw_matrix* m, uw_pipeline p, const void* prep_de
                           int64_t batch, float* y_dev, void* ws_dev, size_t ws_bytes, const uw_kernel_cfg* cfg,
                           void* stream) {
   if (!m || !x_dev || !y_dev || batch <= 0 || p < UW_PIPE_FULL || p > UW_PIPE_PALETTE_DIRECT) return UW_ERR_INVALID;
+  if (m->fp8) return UW_ERR_UNSUPPORTED;
   if (!aligned16(x_dev) || (reinterpret_cast<uintptr_t>(y_dev) & 3u)) return UW_ERR_INVALID;
   if (logical_k(m) % 8 != 0) return UW_ERR_UNSUPPORTED;
   if (p == UW_PIPE_PALETTE_DIRECT) {
@@ -784,63 +823,121 @@ uw_status uw_matmul_stage(const uw_matrix* m, uw_pipeline p, const void* prep_de
   } else if (!prep_dev || !aligned16(prep_dev)) {
     return UW_ERR_INVALID;
   }
-  const size_t need = partial_bytes(m, p, batch, cfg);
+  const Plan r = plan_call(m, p, batch, cfg);
+  const size_t need = partial_bytes(m, p, batch, r.cfgp());
   if (need > ws_bytes || (need && !ws_dev) || !aligned16(ws_dev)) return UW_ERR_WORKSPACE;
   WeightView v = pipeline_view(m, p, prep_dev);
-  UW_HIP(launch_gemm(v, x_dev, batch, y_dev, (int64_t)v.n, 0, cfg, static_cast<float*>(ws_dev),
+  UW_HIP(launch_gemm(v, x_dev, batch, y_dev, (int64_t)v.n, 0, r.cfgp(), static_cast<float*>(ws_dev),
                      need / sizeof(float), static_cast<hipStream_t>(stream)));
   return UW_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of a grouped call: the per-matrix layout (each matrix's
+// preprocessed form and partial sums back to back), or when the group runs
+// as one LDS-tiled launch, the preprocessed forms packed and the group's
+// partial rows after them; the larger of the two, so the one-launch form is
+// always available.  *tile_part = partial floats of that launch (SIZE_MAX:
+// the group does not run as one).
+uw_status grouped_need(const uw_matrix* const* ms, int count, int p, int64_t batch, const uw_kernel_cfg* cfg,
+                       size_t* need, size_t* prep_total, size_t* tile_part) {
+  size_t per = 0, prep = 0;
+  for (int i = 0; i < count; ++i) {
+    size_t b = 0;
+    workspace_for(ms[i], p, batch, cfg, &b);
+    per += b;
+    prep += prep_bytes(ms[i], p);
+  }
+  size_t tp = SIZE_MAX;
+  if (count >= 2 && count <= kGroupMax) {
+    WeightView plan[kGroupMax];
+    for (int i = 0; i < count; ++i) plan[i] = pipeline_view(ms[i], p, nullptr);
+    tp = gemm_tile_group_partial_elems(plan, count, batch, cfg);
+  }
+  *need = tp == SIZE_MAX ? per : std::max(per, (size_t)pad256(prep) + tp * sizeof(float));
+  *prep_total = prep;
+  *tile_part = tp;
+  return UW_OK;
+}
+
+uw_status check_group_args(const uw_matrix* const* ms, int count, int p, const uint16_t* x_dev, int64_t batch,
+                           const float* y_dev) {
+  if (!ms || count <= 0) return UW_ERR_INVALID;
+  for (int i = 0; i < count; ++i) {
+    UW_CHECK(check_matmul_args(ms[i], p, x_dev, batch, y_dev));
+    if (logical_k(ms[i]) != logical_k(ms[0])) return UW_ERR_INVALID;
+  }
+  return UW_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+uw_status uw_workspace_size_grouped(const uw_matrix* const* ms, int count, uw_pipeline p, int64_t batch,
+                                    const uw_kernel_cfg* cfg, size_t* bytes) {
+  if (!ms || count <= 0 || !bytes || batch <= 0 || !pipeline_arg(p)) return UW_ERR_INVALID;
+  for (int i = 0; i < count; ++i) {
+    if (!ms[i]) return UW_ERR_INVALID;
+    if (ms[i]->fp8) return UW_ERR_UNSUPPORTED;
+  }
+  const int rp = plan_group_pipeline(ms, count, p, batch);
+  size_t prep = 0, tp = 0;
+  return grouped_need(ms, count, rp, batch, cfg, bytes, &prep, &tp);
 }
 
 uw_status uw_matmul_reconstruct_grouped(const uw_matrix* const* ms, int count, uw_pipeline p,
                                         const uint16_t* x_dev, int64_t batch, float* y_dev, void* ws_dev,
                                         size_t ws_bytes, const uw_kernel_cfg* cfg, void* stream) {
-  if (!ms || count <= 0) return UW_ERR_INVALID;
-  uint64_t total_n = 0;
-  size_t need = 0, prep_total = 0;
+  if (!ms || count <= 0 || !pipeline_arg(p) || batch <= 0) return UW_ERR_INVALID;
   for (int i = 0; i < count; ++i) {
-    UW_CHECK(check_matmul_args(ms[i], p, x_dev, batch, y_dev));
-    if (logical_k(ms[i]) != logical_k(ms[0])) return UW_ERR_INVALID;
-    total_n += logical_n(ms[i]);
-    size_t b = 0;
-    workspace_for(ms[i], p, batch, cfg, &b);
-    need += b;
-    prep_total += prep_bytes(ms[i], p);
+    if (!ms[i]) return UW_ERR_INVALID;
+    if (ms[i]->fp8) return UW_ERR_UNSUPPORTED;
   }
-  if (need > ws_bytes || (need && !ws_dev) || !aligned16(ws_dev)) return UW_ERR_WORKSPACE;
+  const int rp = plan_group_pipeline(ms, count, p, batch);
+  UW_CHECK(check_group_args(ms, count, rp, x_dev, batch, y_dev));
+  uint64_t total_n = 0;
+  for (int i = 0; i < count; ++i) total_n += logical_n(ms[i]);
+  // the smallest workspace that runs the matrices one by one
+  size_t need_per = 0;
+  for (int i = 0; i < count; ++i) {
+    size_t b = 0;
+    workspace_for(ms[i], rp, batch, cfg, &b);
+    need_per += b;
+  }
+  if (need_per > ws_bytes || (need_per && !ws_dev) || !aligned16(ws_dev)) return UW_ERR_WORKSPACE;
+  size_t need_all = 0, prep_total = 0, tile_part = SIZE_MAX;
+  UW_CHECK(grouped_need(ms, count, rp, batch, cfg, &need_all, &prep_total, &tile_part));
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
   // Matrices whose kernel (as one matrix as wide as the group) is an LDS tile
   // share one launch: fixed per-launch costs are paid once and K is split for
   // the group's tiles together.  Its workspace: the preprocessed weights
   // packed first, the group's partial rows after them.
-  size_t tile_part = SIZE_MAX;
-  if (count >= 2 && count <= kMfma2GroupMax) {
-    WeightView plan[kMfma2GroupMax];
-    for (int i = 0; i < count; ++i) plan[i] = pipeline_view(ms[i], p, nullptr);
-    tile_part = gemm_tile_group_partial_elems(plan, count, batch, cfg);
-  }
   const size_t part_off = pad256(prep_total);
   const bool tile_group = tile_part != SIZE_MAX && part_off + tile_part * sizeof(float) <= ws_bytes;
   size_t off = 0;
   std::vector<size_t> offs((size_t)count);
   for (int i = 0; i < count; ++i) {
     offs[(size_t)i] = off;
-    UW_CHECK(preprocess(ms[i], p, ws + off, s));
-    size_t b = prep_bytes(ms[i], p);
-    if (!tile_group) workspace_for(ms[i], p, batch, cfg, &b);
+    UW_CHECK(preprocess(ms[i], rp, ws + off, s));
+    size_t b = prep_bytes(ms[i], rp);
+    if (!tile_group) workspace_for(ms[i], rp, batch, cfg, &b);
     off += b;
   }
-  // matrices that all run the VALU GEMV share one launch
-  if (count >= 2 && count <= 4) {
-    WeightView vs[4];
-    int64_t c0[4];
+  if (count >= 2 && count <= kGroupMax) {
+    WeightView vs[kGroupMax];
+    int64_t c0[kGroupMax];
     int64_t col = 0;
     for (int i = 0; i < count; ++i) {
-      vs[i] = pipeline_view(ms[i], p, ws + offs[(size_t)i]);
+      vs[i] = pipeline_view(ms[i], rp, ws + offs[(size_t)i]);
       c0[i] = col;
       col += (int64_t)vs[i].n;
     }
+    // matrices that all run the VALU GEMV share one launch
     const hipError_t e = launch_gemm_group(vs, count, x_dev, batch, y_dev, (int64_t)total_n, c0, cfg, s);
     if (e == hipSuccess) return UW_OK;
     if (e != hipErrorNotSupported) return UW_ERR_DEVICE;
@@ -852,10 +949,10 @@ uw_status uw_matmul_reconstruct_grouped(const uw_matrix* const* ms, int count, u
   }
   uint64_t col0 = 0;
   for (int i = 0; i < count; ++i) {
-    WeightView v = pipeline_view(ms[i], p, ws + offs[(size_t)i]);
-    const size_t pb = prep_bytes(ms[i], p);
+    WeightView v = pipeline_view(ms[i], rp, ws + offs[(size_t)i]);
+    const size_t pb = prep_bytes(ms[i], rp);
     size_t b = 0;
-    workspace_for(ms[i], p, batch, cfg, &b);
+    workspace_for(ms[i], rp, batch, cfg, &b);
     float* part = reinterpret_cast<float*>(ws + offs[(size_t)i] + pb);
     UW_HIP(launch_gemm(v, x_dev, batch, y_dev, (int64_t)total_n, (int64_t)col0, cfg, part,
                        (b - pb) / sizeof(float), s));
@@ -880,45 +977,103 @@ uw_status uw_gemm_bf16(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout la
   v.bf16 = w_dev;
   const size_t pe = gemm_partial_elems(v, batch, cfg);
   float* part = nullptr;
-  if (pe) UW_CHECK(dev_alloc(&part, pe * sizeof(float)));   // yardstick path only
+  const uw_allocator alloc = current_allocator();
+  if (pe) UW_CHECK(dev_alloc(alloc, &part, pe * sizeof(float)));   // yardstick path only
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_gemm(v, x_dev, batch, y_dev, n, 0, cfg, part, pe, s);
   if (part) {
     (void)hipStreamSynchronize(s);
-    dev_free(part);
+    dev_free(alloc, part);
   }
   return e == hipSuccess ? UW_OK : UW_ERR_DEVICE;
 }
 
 int32_t uw_variant_count(void) { return gemm_variant_count(); }
 
-uw_status uw_sequence_workspace_size(const uw_job* jobs, int count, size_t* bytes) {
-  if (!jobs || count <= 0 || !bytes) return UW_ERR_INVALID;
-  size_t prep = 0, part = 0;
+}  // extern "C"
+
+namespace {
+
+// Jobs with UW_PIPE_AUTO resolved and empty cfgs replaced by the tuned choice.
+uw_status resolve_jobs(const uw_job* jobs, int count, std::vector<uw_job>& out) {
+  if (!jobs || count <= 0) return UW_ERR_INVALID;
+  out.assign(jobs, jobs + count);
   for (int i = 0; i < count; ++i) {
-    if (!jobs[i].m) return UW_ERR_INVALID;
-    prep = std::max(prep, prep_bytes(jobs[i].m, jobs[i].pipeline));
-    part = std::max(part, partial_bytes(jobs[i].m, jobs[i].pipeline, jobs[i].batch, &jobs[i].cfg));
+    uw_job& j = out[(size_t)i];
+    if (!j.m || !pipeline_arg(j.pipeline) || j.batch <= 0) return UW_ERR_INVALID;
+    if (j.m->fp8) return UW_ERR_UNSUPPORTED;
+    const Plan r = plan_call(j.m, j.pipeline, j.batch, cfg_empty(j.cfg) ? nullptr : &j.cfg);
+    j.pipeline = r.p;
+    if (r.has_cfg) j.cfg = r.cfg;
   }
+  return UW_OK;
+}
+
+uw_status sequence_need(const std::vector<uw_job>& jobs, size_t* prep_out, size_t* bytes) {
+  size_t prep = 0, part = 0;
+  for (const uw_job& j : jobs) {
+    prep = std::max(prep, prep_bytes(j.m, j.pipeline));
+    part = std::max(part, partial_bytes(j.m, j.pipeline, j.batch, &j.cfg));
+  }
+  *prep_out = prep;
   *bytes = 2 * prep + part;
   return UW_OK;
 }
 
-uw_status uw_run_sequence(const uw_job* jobs, int count, int32_t decode_cus, void* ws_dev, size_t ws_bytes,
-                          void* stream) {
+}  // namespace
+
+extern "C" {
+
+uw_status uw_sequence_workspace_size(const uw_job* jobs, int count, size_t* bytes) try {
+  if (!jobs || count <= 0 || !bytes) return UW_ERR_INVALID;
+  std::vector<uw_job> rj;
+  UW_CHECK(resolve_jobs(jobs, count, rj));
+  size_t prep = 0;
+  return sequence_need(rj, &prep, bytes);
+} catch (...) {
+  return UW_ERR_NOMEM;
+}
+
+uw_status uw_run_sequence(const uw_job* jobs_in, int count, int32_t decode_cus, void* ws_dev, size_t ws_bytes,
+                          void* stream) try {
+  if (!jobs_in || count <= 0) return UW_ERR_INVALID;
+  std::vector<uw_job> rj;
+  UW_CHECK(resolve_jobs(jobs_in, count, rj));
+  return uw::run_jobs(rj.data(), count, decode_cus, ws_dev, ws_bytes, static_cast<hipStream_t>(stream));
+} catch (...) {
+  return UW_ERR_NOMEM;
+}
+
+}  // extern "C"
+
+// Jobs as given: explicit pipelines, each cfg used as it is (fields <= 0 are
+// the library defaults).  The autotuner times candidates through this, so
+// the tuning table never stands in for a candidate.
+uw_status uw::jobs_workspace(const uw_job* jobs, int count, size_t* bytes) try {
+  if (!jobs || count <= 0 || !bytes) return UW_ERR_INVALID;
+  for (int i = 0; i < count; ++i)
+    if (!jobs[i].m || jobs[i].pipeline < UW_PIPE_FULL || jobs[i].pipeline > UW_PIPE_PALETTE_DIRECT)
+      return UW_ERR_INVALID;
+  std::vector<uw_job> v(jobs, jobs + count);
+  size_t prep = 0;
+  return sequence_need(v, &prep, bytes);
+} catch (...) {
+  return UW_ERR_NOMEM;
+}
+
+uw_status uw::run_jobs(const uw_job* jobs, int count, int32_t decode_cus, void* ws_dev, size_t ws_bytes,
+                       hipStream_t s) try {
   if (!jobs || count <= 0) return UW_ERR_INVALID;
+  std::vector<uw_job> rj(jobs, jobs + count);
   for (int i = 0; i < count; ++i)
     UW_CHECK(check_matmul_args(jobs[i].m, jobs[i].pipeline, jobs[i].x_dev, jobs[i].batch, jobs[i].y_dev));
-  size_t need = 0;
-  UW_CHECK(uw_sequence_workspace_size(jobs, count, &need));
+  size_t need = 0, prep = 0;
+  UW_CHECK(sequence_need(rj, &prep, &need));
   if (need > ws_bytes || (need && !ws_dev) || !aligned16(ws_dev)) return UW_ERR_WORKSPACE;
-  size_t prep = 0;
-  for (int i = 0; i < count; ++i) prep = std::max(prep, prep_bytes(jobs[i].m, jobs[i].pipeline));
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
   uint8_t* bufs[2] = {ws, ws + prep};
   float* part = reinterpret_cast<float*>(ws + 2 * prep);
   const size_t part_elems = (need - 2 * prep) / sizeof(float);
-  hipStream_t s = static_cast<hipStream_t>(stream);
 
   bool any_split = false;
   for (int i = 0; i < count; ++i) {
@@ -939,17 +1094,14 @@ uw_status uw_run_sequence(const uw_job* jobs, int count, int32_t decode_cus, voi
   // a stream masked to the other CUs (D = the job's decode_cus, else the
   // sequence default; D = 0 puts both on the caller's stream).  GEMMs stay in
   // job order; preprocessing of job i waits for the GEMM of job i-2, which
-  // used the same buffer.
-  thread_local std::vector<hipEvent_t> pool;
-  const size_t need_ev = 2 * (size_t)count + 1;
-  while (pool.size() < need_ev) {
-    hipEvent_t e;
-    UW_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
-    pool.push_back(e);
-  }
+  // used the same buffer.  The streams and events belong to the library
+  // (runtime.cpp); one sequence runs at a time.
+  std::lock_guard<std::mutex> seq(sequence_mutex());
+  hipEvent_t* pool = nullptr;
+  UW_CHECK(pooled_events(2 * (size_t)count + 1, &pool));
   hipEvent_t fork = pool[0];
-  hipEvent_t* prep_done = pool.data() + 1;
-  hipEvent_t* gemm_done = pool.data() + 1 + count;
+  hipEvent_t* prep_done = pool + 1;
+  hipEvent_t* gemm_done = pool + 1 + count;
   UW_HIP(hipEventRecord(fork, s));
   std::vector<hipStream_t> used;
   auto enter = [&](hipStream_t st) -> uw_status {
@@ -992,7 +1144,11 @@ uw_status uw_run_sequence(const uw_job* jobs, int count, int32_t decode_cus, voi
     UW_HIP(hipStreamWaitEvent(s, prep_done[0], 0));
   }
   return UW_OK;
+} catch (...) {
+  return UW_ERR_NOMEM;
 }
+
+extern "C" {
 
 uw_status uw_sync_status(const uw_matrix* m, void* stream) {
   if (!m) return UW_ERR_INVALID;

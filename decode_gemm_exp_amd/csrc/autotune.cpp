@@ -12,11 +12,16 @@
 //
 // Objective: wall time (HIP events) of one pass over every given matrix in
 // order, run by uw_run_sequence with the candidate configuration, median of
-// three runs after a warm-up.  Candidates per projection: every pipeline all
-// its matrices can run (direct palette needs resident indices, the others the
-// Huffman stream) x every GEMM variant that suits the batch; then, for a
-// pipeline with preprocessing, the CUs given to the preprocessing kernel.
+// three runs after a warm-up, with activations drawn from N(0,1) in BF16 (the
+// matrix cores' power, and so the clock they hold, depends on the operand
+// values; all-zero activations would tune for a faster chip than the one that
+// runs).  Candidates per projection: every pipeline all its matrices can run
+// (direct palette needs resident indices, the others the Huffman stream) x
+// every GEMM variant that suits the batch; then the K split of the chosen
+// kernel; then, for a pipeline with preprocessing, the CUs given to the
+// preprocessing kernel.
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <vector>
@@ -32,20 +37,53 @@ struct Choice {
   }
 };
 
+// Device buffers and HIP objects of one tuning run, released on every return.
 struct Bufs {
+  uw_allocator a = uw::current_allocator();
   void* x = nullptr;
   void* y = nullptr;
   void* ws = nullptr;
   size_t ws_bytes = 0;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  FILE* json = nullptr;
   ~Bufs() {
-    if (x) (void)hipFree(x);
-    if (y) (void)hipFree(y);
-    if (ws) (void)hipFree(ws);
+    uw::free_with(a, x);
+    uw::free_with(a, y);
+    uw::free_with(a, ws);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (json) std::fclose(json);
   }
 };
 
 bool feasible(const uw_matrix* m, int p) {
   return p == UW_PIPE_PALETTE_DIRECT ? m->pidx != nullptr : m->stream != nullptr;
+}
+
+// n values from N(0,1) as BF16 bit patterns: a 64-bit xorshift generator,
+// Box-Muller, then round to nearest even from fp32 (x has no NaNs).
+std::vector<uint16_t> normal_bf16(size_t n, uint64_t seed) {
+  std::vector<uint16_t> out(n);
+  uint64_t st = seed ? seed : 0x9E3779B97F4A7C15ull;
+  auto next = [&]() {
+    st ^= st << 13;
+    st ^= st >> 7;
+    st ^= st << 17;
+    return st;
+  };
+  for (size_t i = 0; i < n; i += 2) {
+    const double u1 = ((next() >> 11) + 1.0) * 0x1.0p-53;   // (0, 1]
+    const double u2 = (next() >> 11) * 0x1.0p-53;
+    const double r = std::sqrt(-2.0 * std::log(u1));
+    const float v[2] = {(float)(r * std::cos(6.283185307179586 * u2)), (float)(r * std::sin(6.283185307179586 * u2))};
+    for (int t = 0; t < 2 && i + t < n; ++t) {
+      uint32_t b;
+      std::memcpy(&b, &v[t], 4);
+      b += 0x7FFFu + ((b >> 16) & 1u);
+      out[i + t] = (uint16_t)(b >> 16);
+    }
+  }
+  return out;
 }
 
 }  // namespace
@@ -58,6 +96,21 @@ extern "C" uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj
     if (!ms[i] || proj[i] < 0 || proj[i] >= nproj) return UW_ERR_INVALID;
     if (ms[i]->fp8) return UW_ERR_UNSUPPORTED;
   }
+  // a projection's matrices share shape, layout and residency: the choice is
+  // recorded under that key
+  std::vector<int> first((size_t)nproj, -1);
+  for (int i = 0; i < count; ++i) {
+    int& f = first[(size_t)proj[i]];
+    if (f < 0) {
+      f = i;
+      continue;
+    }
+    const uw_matrix* a = ms[f];
+    const uw_matrix* b = ms[i];
+    if (a->rows != b->rows || a->cols != b->cols || a->layout != b->layout ||
+        uw::residency_of(a) != uw::residency_of(b))
+      return UW_ERR_INVALID;
+  }
   for (int b = 0; b < nb; ++b)
     if (batches[b] <= 0) return UW_ERR_INVALID;
   if (max_passes <= 0) max_passes = 3;
@@ -68,7 +121,7 @@ extern "C" uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return UW_ERR_DEVICE;
   const int cus = prop.multiProcessorCount;
 
-  // shared x (max K) and y (max N) for the largest batch; contents are zero
+  // shared x (max K) and y (max N) for the largest batch; x ~ N(0,1) in BF16
   int64_t maxb = 0;
   uint64_t maxk = 0, maxn = 0;
   for (int b = 0; b < nb; ++b) maxb = std::max(maxb, batches[b]);
@@ -79,16 +132,25 @@ extern "C" uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj
     maxn = std::max<uint64_t>(maxn, inf.n);
   }
   Bufs bufs;
-  if (hipMalloc(&bufs.x, (size_t)maxb * maxk * 2 + 256) != hipSuccess) return UW_ERR_NOMEM;
-  if (hipMalloc(&bufs.y, (size_t)maxb * maxn * 4 + 256) != hipSuccess) return UW_ERR_NOMEM;
-  if (hipMemsetAsync(bufs.x, 0, (size_t)maxb * maxk * 2, s) != hipSuccess) return UW_ERR_DEVICE;
-
-  hipEvent_t e0, e1;
-  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return UW_ERR_DEVICE;
+  uw_status ast = uw::alloc_with(bufs.a, &bufs.x, (size_t)maxb * maxk * 2 + 256);
+  if (ast != UW_OK) return ast;
+  ast = uw::alloc_with(bufs.a, &bufs.y, (size_t)maxb * maxn * 4 + 256);
+  if (ast != UW_OK) return ast;
+  {
+    const std::vector<uint16_t> xh = normal_bf16((size_t)maxb * maxk, 0x5555000000000001ull);
+    if (hipMemcpyAsync(bufs.x, xh.data(), xh.size() * 2, hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return UW_ERR_DEVICE;
+  }
+  if (hipEventCreate(&bufs.e0) != hipSuccess || hipEventCreate(&bufs.e1) != hipSuccess) return UW_ERR_DEVICE;
+  const hipEvent_t e0 = bufs.e0, e1 = bufs.e1;
   std::vector<uw_job> jobs((size_t)count);
-  FILE* jf = json_path ? std::fopen(json_path, "w") : nullptr;
-  if (json_path && !jf) return UW_ERR_INVALID;
-  if (jf) std::fprintf(jf, "{\n  \"entries\": [\n");
+  FILE* jf = nullptr;
+  if (json_path) {
+    jf = bufs.json = std::fopen(json_path, "w");
+    if (!jf) return UW_ERR_INVALID;
+    std::fprintf(jf, "{\n  \"entries\": [\n");
+  }
   bool first_entry = true;
   uw_status result = UW_OK;
 
@@ -117,19 +179,20 @@ extern "C" uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj
         j.batch = batch;
       }
       size_t need = 0;
-      uw_status st = uw_sequence_workspace_size(jobs.data(), count, &need);
+      uw_status st = uw::jobs_workspace(jobs.data(), count, &need);
       if (st != UW_OK) return st;
       if (need > bufs.ws_bytes) {
-        if (bufs.ws) (void)hipFree(bufs.ws);
+        uw::free_with(bufs.a, bufs.ws);
         bufs.ws = nullptr;
         bufs.ws_bytes = 0;
-        if (hipMalloc(&bufs.ws, need) != hipSuccess) return UW_ERR_NOMEM;
+        st = uw::alloc_with(bufs.a, &bufs.ws, need);
+        if (st != UW_OK) return st;
         bufs.ws_bytes = need;
       }
       double t[3];
       for (int r = -1; r < 3; ++r) {
         if (hipEventRecord(e0, s) != hipSuccess) return UW_ERR_DEVICE;
-        st = uw_run_sequence(jobs.data(), count, 0, bufs.ws, bufs.ws_bytes, s);
+        st = uw::run_jobs(jobs.data(), count, 0, bufs.ws, bufs.ws_bytes, s);
         if (st != UW_OK) return st;
         if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) return UW_ERR_DEVICE;
         float ms_ = 0.f;
@@ -204,6 +267,33 @@ extern "C" uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj
             improved = true;
           }
         }
+        // stage 1c: the K split of the chosen kernel (0 = the library's rule;
+        // 1 = no split); the register-fed, LDS-tiled and [K][N] GEMV kernels
+        // take it, the [N][K] GEMV ignores it
+        if (result == UW_OK) {
+          const Choice base = cfg[(size_t)p];
+          bool splits = true;
+          if (base.variant == 1 || (base.variant <= 0 && batch <= 4)) {
+            for (int i = 0; i < count; ++i)
+              if (proj[i] == p && ms[i]->layout == 0) splits = false;
+          }
+          for (int sk : {1, 2, 4, 8}) {
+            if (!splits) break;
+            Choice c = base;
+            c.split_k = sk;
+            if (c == cfg[(size_t)p]) continue;
+            std::vector<Choice> trial = cfg;
+            trial[(size_t)p] = c;
+            double t = 0;
+            result = measure(trial, &t);
+            if (result != UW_OK) break;
+            if (t < best * 0.99) {
+              best = t;
+              cfg = trial;
+              improved = true;
+            }
+          }
+        }
         // stage 2: CUs for the preprocessing kernel of the chosen pipeline
         if (result == UW_OK && cfg[(size_t)p].pipeline != UW_PIPE_PALETTE_DIRECT) {
           for (int frac : {8, 4, 2}) {
@@ -228,20 +318,30 @@ extern "C" uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj
     if (result != UW_OK) break;
     for (int p = 0; p < nproj; ++p) {
       const Choice& c = cfg[(size_t)p];
-      if (out) {
-        uw_tune_entry& e = out[(size_t)bi * (size_t)nproj + (size_t)p];
-        e.batch = batch;
-        e.projection = p;
-        e.pipeline = c.pipeline;
-        e.variant = c.variant;
-        e.split_k = c.split_k;
-        e.decode_cus = c.decode_cus;
-        e.sequence_us = best;
+      const int fi = first[(size_t)p];
+      uw_tune_entry e;
+      std::memset(&e, 0, sizeof(e));
+      e.batch = batch;
+      e.projection = p;
+      e.pipeline = c.pipeline;
+      e.variant = c.variant;
+      e.split_k = c.split_k;
+      e.decode_cus = c.decode_cus;
+      if (fi >= 0) {
+        uw_get_info(ms[fi], &inf);
+        e.layout = (int32_t)inf.layout;
+        e.n = inf.n;
+        e.k = inf.k;
+        e.residency = uw::residency_of(ms[fi]);
       }
-      if (jf) {
-        std::fprintf(jf, "%s    {\"batch\": %lld, \"projection\": %d, \"pipeline\": %d, \"variant\": %d, "
-                         "\"split_k\": %d, \"decode_cus\": %d, \"sequence_us\": %.2f}",
-                     first_entry ? "" : ",\n", (long long)batch, p, c.pipeline, c.variant, c.split_k,
+      e.sequence_us = best;
+      if (out) out[(size_t)bi * (size_t)nproj + (size_t)p] = e;
+      if (jf && fi >= 0) {
+        std::fprintf(jf, "%s    {\"batch\": %lld, \"projection\": %d, \"n\": %llu, \"k\": %llu, \"layout\": %d, "
+                         "\"residency\": %d, \"pipeline\": %d, \"variant\": %d, \"split_k\": %d, "
+                         "\"decode_cus\": %d, \"sequence_us\": %.2f}",
+                     first_entry ? "" : ",\n", (long long)batch, p, (unsigned long long)e.n,
+                     (unsigned long long)e.k, e.layout, e.residency, c.pipeline, c.variant, c.split_k,
                      c.decode_cus, best);
         first_entry = false;
       }
@@ -249,9 +349,8 @@ extern "C" uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj
   }
   if (jf) {
     std::fprintf(jf, "\n  ]\n}\n");
-    std::fclose(jf);
+    bufs.json = nullptr;
+    if (std::fclose(jf) != 0 && result == UW_OK) result = UW_ERR_INVALID;
   }
-  (void)hipEventDestroy(e0);
-  (void)hipEventDestroy(e1);
   return result;
 }

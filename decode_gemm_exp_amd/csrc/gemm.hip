@@ -55,7 +55,6 @@ __device__ __forceinline__ float wave_sum(float v) {
 // writes output columns col0[i] ..; a single matrix is a group of one.
 // Small matrices give each wave only a step or two, so one launch instead
 // of one per matrix saves the pipeline's fill and drain per matrix.
-constexpr int kGemvGroupMax = 4;
 struct GemvGroup {
   WeightView w[kGemvGroupMax];
   int64_t col0[kGemvGroupMax];

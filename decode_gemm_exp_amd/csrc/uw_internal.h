@@ -5,6 +5,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/unweight.h"
 
@@ -57,6 +58,7 @@ struct uw_matrix {
   int* corrupt = nullptr;         // device flag set by decoders
   uint32_t wave_span = 0;         // most stream words any 64-segment wave covers (from a 4-word boundary)
   bool fp8 = false;               // FP8 E4M3 weights: sm holds numel / 2 bytes of sign+mantissa nibbles
+  uw_allocator alloc{};           // the hooks its sections came from (alloc == NULL: hipMalloc)
 };
 
 namespace uw {
@@ -69,6 +71,33 @@ void build_decode_lut(const Tables& t, uint32_t* lut);   // kLutWords << kLutBit
 
 // Compute units of the current device (256 if the query fails).
 int device_cus();
+
+// ---- runtime.cpp: allocator, sequence-runner HIP objects, tuned choices -------
+uw_allocator current_allocator();
+// bytes of device memory from allocator a (hipMalloc when a.alloc is NULL);
+// UW_ERR_NOMEM when a hook returns NULL, UW_ERR_INVALID when its block is not
+// 256-byte aligned
+uw_status alloc_with(const uw_allocator& a, void** p, size_t bytes);
+void free_with(const uw_allocator& a, void* p);
+struct SplitStreams {
+  hipStream_t dec = nullptr, gemm = nullptr;
+};
+// the stream pair of the current device for a decode share of `decode_cus`
+// CUs (>= the CU count: two unmasked streams); owned by the library
+uw_status split_streams(int decode_cus, SplitStreams* out);
+// held by uw_run_sequence for its whole call
+std::mutex& sequence_mutex();
+// at least `count` events of the current device; caller holds sequence_mutex()
+uw_status pooled_events(size_t count, hipEvent_t** out);
+// the sequence runner on jobs as given (api.cpp): explicit pipelines, cfgs
+// used as they are; uw_run_sequence resolves UW_PIPE_AUTO and tuned cfgs first
+uw_status jobs_workspace(const uw_job* jobs, int count, size_t* bytes);
+uw_status run_jobs(const uw_job* jobs, int count, int32_t decode_cus, void* ws, size_t ws_bytes, hipStream_t s);
+// bit 0: Huffman stream resident, bit 1: palette indices resident
+int residency_of(const uw_matrix* m);
+// the tuned choice for a shape, residency and batch (nearest tuned batch on a
+// log scale); false when the table holds none
+bool tuned_lookup(uint64_t n, uint64_t k, int layout, int residency, int64_t batch, uw_tune_entry* out);
 
 // Raise a kernel's dynamic LDS limit to `bytes` on the current device, once
 // per (kernel, device, size); thread safe (api.cpp).
@@ -155,6 +184,11 @@ int mfma2_tile_count();
 void mfma2_tile_dims(int tile, int* bm, int* bn);
 // A group of matrices in one LDS-tiled launch (same K, layout, format class)
 constexpr int kMfma2GroupMax = 4;
+// ... or in one grouped GEMV launch (gemm.hip)
+constexpr int kGemvGroupMax = 4;
+// grouped calls plan both launches over one array of weight views
+static_assert(kGemvGroupMax == kMfma2GroupMax, "grouped launches share their matrix limit");
+constexpr int kGroupMax = kMfma2GroupMax;
 struct Mfma2Group {
   WeightView w[kMfma2GroupMax];
   int64_t ycol[kMfma2GroupMax];   // first output column of each matrix in y

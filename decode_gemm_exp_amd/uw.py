@@ -27,7 +27,8 @@ UW_ERR_UNSUPPORTED = -2
 STATUS = {0: "ok", -1: "invalid", -2: "unsupported", -3: "nomem", -4: "device", -5: "corrupt",
           -6: "state", -7: "workspace"}
 PIPE_FULL, PIPE_EXPONENT, PIPE_PALETTE_TRANSCODE, PIPE_PALETTE_DIRECT = 0, 1, 2, 3
-PIPELINES = {"full": 0, "exponent": 1, "transcode": 2, "direct": 3}
+PIPE_AUTO = 15
+PIPELINES = {"full": 0, "exponent": 1, "transcode": 2, "direct": 3, "auto": 15}
 LAYOUT_NK, LAYOUT_KN = 0, 1
 
 
@@ -63,7 +64,16 @@ class uw_info(ctypes.Structure):
 class uw_tune_entry(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("projection", ctypes.c_int32), ("pipeline", ctypes.c_int32),
                 ("variant", ctypes.c_int32), ("split_k", ctypes.c_int32), ("decode_cus", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("sequence_us", ctypes.c_double)]
+                ("layout", ctypes.c_int32), ("residency", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("n", ctypes.c_uint64), ("k", ctypes.c_uint64), ("sequence_us", ctypes.c_double)]
+
+
+ALLOC_FN = ctypes.CFUNCTYPE(ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p)
+FREE_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_void_p)
+
+
+class uw_allocator(ctypes.Structure):
+    _fields_ = [("alloc", ALLOC_FN), ("free", FREE_FN), ("ctx", ctypes.c_void_p)]
 
 
 class uw_job(ctypes.Structure):
@@ -105,6 +115,17 @@ _SIGS = {
                                    ctypes.POINTER(ctypes.c_int64), ctypes.c_int, ctypes.c_int, ctypes.c_char_p,
                                    ctypes.POINTER(uw_tune_entry), _vp]),
     "uw_drop_palette": (ctypes.c_int, [_vp, _vp]),
+    "uw_workspace_size_cfg": (ctypes.c_int, [_vp, ctypes.c_int, _i64, ctypes.POINTER(uw_kernel_cfg),
+                                             ctypes.POINTER(_sz)]),
+    "uw_workspace_size_grouped": (ctypes.c_int, [ctypes.POINTER(_vp), ctypes.c_int, ctypes.c_int, _i64,
+                                                 ctypes.POINTER(uw_kernel_cfg), ctypes.POINTER(_sz)]),
+    "uw_set_allocator": (ctypes.c_int, [ctypes.POINTER(uw_allocator)]),
+    "uw_release_resources": (ctypes.c_int, []),
+    "uw_set_tuning": (ctypes.c_int, [ctypes.POINTER(uw_tune_entry), ctypes.c_int]),
+    "uw_load_tuning": (ctypes.c_int, [ctypes.c_char_p]),
+    "uw_clear_tuning": (ctypes.c_int, []),
+    "uw_lookup_tuning": (ctypes.c_int, [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, _i64,
+                                        ctypes.POINTER(uw_tune_entry)]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -254,6 +275,21 @@ def uw_workspace_size(m: Matrix, pipeline: int, batch: int) -> int:
     return n.value
 
 
+def uw_workspace_size_cfg(m: Matrix, pipeline: int, batch: int, cfg=None) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.uw_workspace_size_cfg(m.handle, pipeline, batch, _cfg(cfg), ctypes.byref(n)),
+           "uw_workspace_size_cfg")
+    return n.value
+
+
+def uw_workspace_size_grouped(ms, pipeline: int, batch: int, cfg=None) -> int:
+    arr = (ctypes.c_void_p * len(ms))(*[m.handle.value for m in ms])
+    n = ctypes.c_size_t()
+    _check(_lib.uw_workspace_size_grouped(arr, len(ms), pipeline, batch, _cfg(cfg), ctypes.byref(n)),
+           "uw_workspace_size_grouped")
+    return n.value
+
+
 def uw_matmul_reconstruct(m: Matrix, pipeline: int, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor | None,
                           cfg=None, stream=None) -> None:
     batch = x.shape[0]
@@ -328,8 +364,84 @@ def uw_autotune(ms, proj, batches, max_passes: int = 3, json_path: str | None = 
     out = (uw_tune_entry * (len(batches) * nproj))()
     _check(_lib.uw_autotune(arr, pj, len(ms), nproj, bs, len(batches), max_passes,
                             json_path.encode() if json_path else None, out, _stream(stream)), "uw_autotune")
-    return [{f: getattr(e, f) for f, _ in uw_tune_entry._fields_ if f != "reserved"} for e in out]
+    return [_entry_dict(e) for e in out]
 
 
 def uw_sync_status(m: Matrix, stream=None) -> int:
     return _lib.uw_sync_status(m.handle, _stream(stream))
+
+
+_TUNE_FIELDS = [f for f, _ in uw_tune_entry._fields_ if f != "reserved"]
+
+
+def _entry_dict(e: uw_tune_entry) -> dict:
+    return {f: getattr(e, f) for f in _TUNE_FIELDS}
+
+
+def uw_set_tuning(entries) -> None:
+    """entries: dicts with the uw_tune_entry fields (as uw_autotune returns)."""
+    arr = (uw_tune_entry * max(1, len(entries)))()
+    for i, d in enumerate(entries):
+        for f in _TUNE_FIELDS:
+            if f in d:
+                setattr(arr[i], f, d[f])
+    _check(_lib.uw_set_tuning(arr, len(entries)), "uw_set_tuning")
+
+
+def uw_load_tuning(json_path: str) -> None:
+    _check(_lib.uw_load_tuning(json_path.encode()), "uw_load_tuning")
+
+
+def uw_clear_tuning() -> None:
+    _check(_lib.uw_clear_tuning(), "uw_clear_tuning")
+
+
+def uw_lookup_tuning(n: int, k: int, layout: int, residency: int, batch: int) -> dict | None:
+    e = uw_tune_entry()
+    st = _lib.uw_lookup_tuning(n, k, layout, residency, batch, ctypes.byref(e))
+    if st == -6:
+        return None
+    _check(st, "uw_lookup_tuning")
+    return _entry_dict(e)
+
+
+def uw_release_resources() -> None:
+    _check(_lib.uw_release_resources(), "uw_release_resources")
+
+
+# The hooks given to uw_set_allocator must outlive every handle made under
+# them; the binding keeps the last ones alive for the life of the process.
+_ALLOCATORS: list = []
+
+
+def uw_set_allocator(alloc=None, free=None, ctx: int | None = None) -> None:
+    """alloc(bytes) -> device pointer (int, 0 for failure); free(ptr).  Both
+    None restores hipMalloc / hipFree."""
+    if alloc is None and free is None:
+        _check(_lib.uw_set_allocator(None), "uw_set_allocator")
+        return
+    a = uw_allocator(ALLOC_FN(lambda n, c: alloc(n) or None), FREE_FN(lambda p, c: free(p)), ctx)
+    _ALLOCATORS.append(a)
+    _check(_lib.uw_set_allocator(ctypes.byref(a)), "uw_set_allocator")
+
+
+class TorchAllocator:
+    """Device memory from torch's caching allocator for uw_set_allocator:
+    each block is a uint8 tensor kept alive until the library frees it."""
+
+    def __init__(self, device="cuda:0"):
+        self.device = device
+        self.live: dict[int, torch.Tensor] = {}
+        self.allocs = 0
+        self.frees = 0
+
+    def alloc(self, nbytes: int) -> int:
+        t = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        p = (t.data_ptr() + 255) // 256 * 256
+        self.live[p] = t
+        self.allocs += 1
+        return p
+
+    def free(self, p: int) -> None:
+        self.live.pop(p, None)
+        self.frees += 1

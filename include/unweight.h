@@ -82,7 +82,13 @@ typedef enum {
   UW_PIPE_FULL = 0,
   UW_PIPE_EXPONENT = 1,
   UW_PIPE_PALETTE_TRANSCODE = 2,
-  UW_PIPE_PALETTE_DIRECT = 3
+  UW_PIPE_PALETTE_DIRECT = 3,
+  /* The tuned pipeline for this matrix's shape, residency and batch (see
+   * uw_set_tuning / uw_load_tuning) when the table holds one that the handle
+   * can run; otherwise direct palette when the indices are resident, else the
+   * exponent pipeline.  ([EVC] "自動調優機制": the configuration chosen by
+   * measurement is looked up per projection and batch at run time.) */
+  UW_PIPE_AUTO = 15
 } uw_pipeline;
 
 typedef struct {
@@ -90,7 +96,10 @@ typedef struct {
   uint32_t flags;       /* reserved, must be 0                               */
 } uw_compress_opts;
 
-/* Kernel choice for one GEMM call.  Any field <= 0 means "library default". */
+/* Kernel choice for one GEMM call.  Any field <= 0 means "library default".
+ * Calls that take a cfg treat cfg == NULL as "the tuned choice": the kernel
+ * fields of the tuning-table entry for this shape, residency and batch when
+ * that entry names the pipeline the call runs, else the library default. */
 typedef struct {
   int32_t variant;      /* GEMM variant (see uw_variant_count)                */
   int32_t split_k;      /* K slices of the split-K kernels                    */
@@ -125,6 +134,35 @@ typedef struct {
 
 const char* uw_status_str(uw_status st);
 uint32_t uw_version(void);      /* (major << 16) | minor */
+
+/* Device memory hooks.  alloc(bytes, ctx) returns device memory on the
+ * current device, 256-byte aligned, or NULL; free(ptr, ctx) returns it.  */
+typedef struct {
+  void* (*alloc)(size_t bytes, void* ctx);
+  void (*free)(void* ptr, void* ctx);
+  void* ctx;
+} uw_allocator;
+
+/* Route the library's device allocations through caller hooks, e.g. a
+ * framework's caching allocator: every section a handle owns, compress
+ * scratch, the autotuner's buffers and uw_gemm_bf16's partial sums.  NULL (or
+ * alloc == free == NULL) restores hipMalloc / hipFree.  A handle keeps the
+ * hooks its sections came from and frees them through those, so the hooks
+ * (and ctx) must stay valid until every handle made under them is freed.  A
+ * hook returning NULL makes the allocating call fail with UW_ERR_NOMEM; a
+ * block that is not 256-byte aligned is handed back and the call fails with
+ * UW_ERR_INVALID.  Process-wide; UW_ERR_INVALID when exactly one hook is set.
+ * (The pages state no interface; this serves the ownership rule that the
+ * handle owns its compressed sections.) */
+uw_status uw_set_allocator(const uw_allocator* a);
+
+/* Destroy the HIP objects the library keeps between calls: the CU-masked
+ * stream pairs and the event pool of uw_run_sequence, on every device.  It
+ * synchronises those streams first.  They are made again on demand.  If never
+ * called, an exit handler registered when the first of them is created
+ * destroys them at exit(), before the HIP runtime's own teardown.  Must not
+ * overlap a uw_run_sequence or uw_autotune call. */
+uw_status uw_release_resources(void);
 
 /* Compress a device BF16 matrix.  `w_dev` is the stored array: [n][k] for
  * UW_LAYOUT_NK, [k][n] for UW_LAYOUT_KN, given as raw 16-bit patterns.  The
@@ -195,8 +233,16 @@ uw_status uw_transcode_palette(uw_matrix* m, uint8_t* idx_out_dev, void* stream)
 uw_status uw_drop_stream(uw_matrix* m, void* stream);
 
 /* Workspace bytes uw_matmul_reconstruct needs for pipeline p at this batch
- * (decoded BF16 / exponents / indices plus split-K partials). */
+ * (decoded BF16 / exponents / indices plus split-K partials): enough for
+ * cfg == NULL (the tuned or the default kernel) and for any cfg whose
+ * split_k is 0.  p may be UW_PIPE_AUTO (resolved with the current tuning
+ * table; query again after changing the table).  A cfg that forces split_k
+ * needs uw_workspace_size_cfg. */
 uw_status uw_workspace_size(const uw_matrix* m, uw_pipeline p, int64_t batch, size_t* bytes);
+
+/* Exactly what uw_matmul_reconstruct(m, p, ..., batch, ..., cfg) needs. */
+uw_status uw_workspace_size_cfg(const uw_matrix* m, uw_pipeline p, int64_t batch, const uw_kernel_cfg* cfg,
+                                size_t* bytes);
 
 /* y[b][n] = sum_k x[b][k] * W[n][k] for b < batch, fp32 output, computed from
  * the compressed W by pipeline p.  x_dev is [batch][K] BF16 (row-major),
@@ -210,25 +256,37 @@ uw_status uw_matmul_reconstruct(const uw_matrix* m, uw_pipeline p, const uint16_
 
 /* The GEMM stage alone, from a buffer already holding what uw_decode_full
  * (pipeline 0), uw_decode_exponent (1) or uw_transcode_palette (2) wrote for
- * this matrix; prep_dev is ignored for pipeline 3 (resident indices).  The
- * workspace holds only the small-batch KN kernel's partial sums; a workspace
- * of uw_workspace_size bytes is always enough.  Lets a caller run the
+ * this matrix; prep_dev is ignored for pipeline 3 (resident indices).  p must
+ * be explicit (not UW_PIPE_AUTO).  The workspace holds only split-K partial
+ * sums (of the [K][N] GEMV and of the MFMA kernels); uw_workspace_size bytes
+ * are always enough for cfg == NULL or split_k == 0.  Lets a caller run the
  * preprocessing and the GEMM on different streams or at different times.
  * ([EVC] "解壓與運算資源共享": decoder and matmul are separate kernels) */
 uw_status uw_matmul_stage(const uw_matrix* m, uw_pipeline p, const void* prep_dev, const uint16_t* x_dev,
                           int64_t batch, float* y_dev, void* ws_dev, size_t ws_bytes,
                           const uw_kernel_cfg* cfg, void* stream);
 
-/* Several matrices with the same K sharing one x (e.g. gate and up), one
- * launch per stage: y_dev is [batch][sum of N] with matrix i's columns at
- * offset sum_{j<i} N_j.  Workspace: uw_workspace_size summed over matrices. */
+/* Several matrices with the same K sharing one x, one launch per stage where
+ * the kernels allow (groups of 2 to 4): y_dev is [batch][sum of N] with matrix i's
+ * columns at offset sum_{j<i} N_j.  Serves the fused gate+up projection
+ * (and q+k+v): the pages tune gate and up as separate projections that read
+ * the same activations ([EVC] "四種執行管道", "自動調優機制"); here they stay
+ * two compressed matrices and only x and the launches are shared.
+ * UW_PIPE_AUTO takes the tuned pipeline when every matrix's entry names the
+ * same one, else direct palette when every matrix has resident indices, else
+ * exponent; cfg == NULL uses the grouped kernels' defaults.  Workspace: see
+ * uw_workspace_size_grouped. */
 uw_status uw_matmul_reconstruct_grouped(const uw_matrix* const* ms, int count, uw_pipeline p,
                                         const uint16_t* x_dev, int64_t batch, float* y_dev,
                                         void* ws_dev, size_t ws_bytes,
                                         const uw_kernel_cfg* cfg, void* stream);
+uw_status uw_workspace_size_grouped(const uw_matrix* const* ms, int count, uw_pipeline p, int64_t batch,
+                                    const uw_kernel_cfg* cfg, size_t* bytes);
 
-/* Dense BF16 GEMM on an uncompressed stored array (the GEMM stage of the
- * full-decode pipeline, also usable as a yardstick). */
+/* Dense BF16 GEMM on an uncompressed stored array: the GEMM stage of the
+ * full-decode pipeline ([EVC] "四種執行管道", first pipeline: decode to BF16,
+ * then a standard matmul), also usable as a yardstick.  Partial sums of a
+ * split K come from the allocator and are freed after a stream sync. */
 uw_status uw_gemm_bf16(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout layout,
                        const uint16_t* x_dev, int64_t batch, float* y_dev,
                        const uw_kernel_cfg* cfg, void* stream);
@@ -253,7 +311,9 @@ typedef struct {
   int64_t batch;
 } uw_job;
 
-/* Run jobs in order.  A job's preprocessing (decode / transcode) runs on a
+/* Run jobs in order.  A job's pipeline may be UW_PIPE_AUTO and a job cfg
+ * whose fields are all <= 0 takes the tuned choice, as for a NULL cfg.  A
+ * job's preprocessing (decode / transcode) runs on a
  * stream masked to D compute units and its GEMM on a stream masked to the
  * remaining CUs, where D is the job's cfg.decode_cus, or `decode_cus` when
  * that is 0; D = 0 runs both on `stream`.  GEMMs keep job order; the
@@ -266,7 +326,8 @@ uw_status uw_sequence_workspace_size(const uw_job* jobs, int count, size_t* byte
 uw_status uw_run_sequence(const uw_job* jobs, int count, int32_t decode_cus, void* ws_dev,
                           size_t ws_bytes, void* stream);
 
-/* One tuned choice: for `projection` at `batch`. */
+/* One tuned choice: for `projection` at `batch`.  n, k, layout and residency
+ * describe the projection's matrices and key the library's tuning table. */
 typedef struct {
   int64_t batch;
   int32_t projection;
@@ -274,23 +335,46 @@ typedef struct {
   int32_t variant;              /* uw_kernel_cfg.variant */
   int32_t split_k;
   int32_t decode_cus;
+  int32_t layout;               /* uw_layout of the stored arrays            */
+  int32_t residency;            /* bit 0: Huffman stream resident; bit 1:
+                                   palette indices resident                  */
   int32_t reserved;
+  uint64_t n, k;                /* logical W[N][K] shape                     */
   double sequence_us;           /* measured time of the whole tuned sequence at this batch */
 } uw_tune_entry;
 
 /* Autotuner.  ms[0..count) are the resident matrices of a model in execution
- * order, proj[i] the projection each belongs to (e.g. 0 gate, 1 up, 2 down;
- * matrices of one projection share a choice).  For each batch it measures
- * uw_run_sequence over all matrices and runs coordinate descent: projection
- * 0, then 1, ..., over pipeline x GEMM variant, then the CUs of the
+ * order, proj[i] the projection each belongs to (e.g. 0 gate, 1 up, 2 down);
+ * matrices of one projection share a choice and must share shape, layout
+ * and residency (UW_ERR_INVALID otherwise).  For each batch it measures
+ * uw_run_sequence over all matrices, x drawn from N(0,1) in BF16, and runs
+ * coordinate descent: projection 0, then 1, ..., over pipeline x GEMM
+ * variant, then the K split of the chosen kernel, then the CUs of the
  * preprocessing kernel, repeating up to max_passes times until no choice
  * improves the time by 1 %.  Writes out[batch_index * nproj + projection]
- * (may be NULL) and a JSON configuration file (json_path may be NULL).
+ * (may be NULL) and a JSON configuration file that uw_load_tuning reads
+ * (json_path may be NULL).  It does not change the library's tuning table.
  * Allocates its own x, y and workspace; synchronises `stream`.
  * ([EVC] "自動調優機制", "解壓與運算資源共享") */
 uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj, int count, int nproj,
                       const int64_t* batches, int nb, int max_passes, const char* json_path,
                       uw_tune_entry* out, void* stream);
+
+/* The tuning table that UW_PIPE_AUTO and cfg == NULL consult, keyed by
+ * (n, k, layout, residency) with one entry per tuned batch; a call at batch B
+ * takes the entry whose batch is nearest to B on a log scale (ties: the
+ * smaller batch).  uw_set_tuning adds entries (an entry with the same key
+ * and batch is replaced; UW_ERR_INVALID if any entry is malformed, and then
+ * none is added); uw_load_tuning adds the entries of a JSON file written by
+ * uw_autotune (UW_ERR_CORRUPT if it cannot be read as one, and then none is
+ * added); uw_clear_tuning empties the table; uw_lookup_tuning reports the
+ * entry a call would use (UW_ERR_STATE when there is none).  Process-wide
+ * and thread safe.  ([EVC] "自動調優機制") */
+uw_status uw_set_tuning(const uw_tune_entry* entries, int count);
+uw_status uw_load_tuning(const char* json_path);
+uw_status uw_clear_tuning(void);
+uw_status uw_lookup_tuning(uint64_t n, uint64_t k, int32_t layout, int32_t residency, int64_t batch,
+                           uw_tune_entry* out);
 
 /* Free resident palette indices (keeps the Huffman form).  Synchronises. */
 uw_status uw_drop_palette(uw_matrix* m, void* stream);

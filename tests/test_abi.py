@@ -102,3 +102,91 @@ def test_import_rejects_corrupt_blobs(uw, oracle, mutate):
 def test_import_rejects_empty_and_short(uw):
     assert uw.uw_import_status(b"") == -1          # NULL blob: invalid argument
     assert uw.uw_import_status(b"UWF1" + bytes(12)) == -5
+
+
+# ------------------------------------------------------ tuning table ------
+# The table that UW_PIPE_AUTO and cfg == NULL consult is host state: its
+# parsing, keying and nearest-batch rule are checked here without a GPU.
+
+def _entry(uw, batch, pipeline, variant=0, split_k=0, n=28672, k=8192, layout=0, residency=3):
+    return {"batch": batch, "projection": 0, "pipeline": pipeline, "variant": variant, "split_k": split_k,
+            "decode_cus": 0, "layout": layout, "residency": residency, "n": n, "k": k, "sequence_us": 1.0}
+
+
+def test_tuning_table_nearest_batch(uw):
+    uw.uw_clear_tuning()
+    try:
+        uw.uw_set_tuning([_entry(uw, 1, 3, 1), _entry(uw, 4, 3, 11), _entry(uw, 64, 3, 2),
+                          _entry(uw, 1024, 1, 9, 2)])
+        pick = lambda b: uw.uw_lookup_tuning(28672, 8192, 0, 3, b)["batch"]  # noqa: E731
+        assert pick(1) == 1
+        assert pick(2) == 1          # log2 distance 1 to both 1 and 4: the smaller
+        assert pick(3) == 4
+        assert pick(16) == 4         # distance 2 to both 4 and 64: the smaller
+        assert pick(200) == 64
+        assert pick(700) == 1024
+        assert pick(1 << 20) == 1024
+        e = uw.uw_lookup_tuning(28672, 8192, 0, 3, 1024)
+        assert (e["pipeline"], e["variant"], e["split_k"]) == (1, 9, 2)
+        # other keys are separate: residency, layout and shape
+        assert uw.uw_lookup_tuning(28672, 8192, 0, 1, 64) is None
+        assert uw.uw_lookup_tuning(28672, 8192, 1, 3, 64) is None
+        assert uw.uw_lookup_tuning(8192, 28672, 0, 3, 64) is None
+        # the same key and batch replaces
+        uw.uw_set_tuning([_entry(uw, 64, 2, 3)])
+        assert uw.uw_lookup_tuning(28672, 8192, 0, 3, 64)["pipeline"] == 2
+    finally:
+        uw.uw_clear_tuning()
+    assert uw.uw_lookup_tuning(28672, 8192, 0, 3, 64) is None
+
+
+def test_tuning_table_rejects_malformed_entries(uw):
+    uw.uw_clear_tuning()
+    bad = [_entry(uw, 1, 3), _entry(uw, 0, 3), _entry(uw, 8, 7), _entry(uw, 8, 3, residency=0),
+           _entry(uw, 8, 3, variant=99), _entry(uw, 8, 3, layout=2)]
+    for b in bad[1:]:
+        with pytest.raises(uw.UwError) as ei:
+            uw.uw_set_tuning([bad[0], b])
+        assert ei.value.status == -1
+        assert uw.uw_lookup_tuning(28672, 8192, 0, 3, 1) is None   # none of the call's entries was added
+    # register-fed variants are [N][K] only
+    with pytest.raises(uw.UwError):
+        uw.uw_set_tuning([_entry(uw, 8, 3, variant=uw.variant_count(), layout=1)])
+    assert uw._lib.uw_lookup_tuning(1, 1, 0, 3, 0, None) == -1
+
+
+def test_load_tuning_json(uw, tmp_path):
+    import json
+    uw.uw_clear_tuning()
+    entries = [_entry(uw, 1, 3, 1), _entry(uw, 1, 3, 1, n=8192, k=28672, layout=1),
+               _entry(uw, 1024, 1, 6, n=8192, k=28672, layout=1)]
+    path = tmp_path / "tuned.json"
+    path.write_text(json.dumps({"entries": entries}, indent=2))
+    try:
+        uw.uw_load_tuning(str(path))
+        assert uw.uw_lookup_tuning(28672, 8192, 0, 3, 1)["variant"] == 1
+        e = uw.uw_lookup_tuning(8192, 28672, 1, 3, 512)
+        assert (e["batch"], e["pipeline"], e["variant"]) == (1024, 1, 6)
+        # an unreadable or malformed file adds nothing
+        uw.uw_clear_tuning()
+        for text in ("{}", '{"entries": [{"batch": 4}]}', '{"entries": [' + json.dumps(dict(entries[0], pipeline=9)) + "]}"):
+            path.write_text(text)
+            with pytest.raises(uw.UwError) as ei:
+                uw.uw_load_tuning(str(path))
+            assert ei.value.status == -5
+        with pytest.raises(uw.UwError):
+            uw.uw_load_tuning(str(tmp_path / "missing.json"))
+        assert uw.uw_lookup_tuning(28672, 8192, 0, 3, 1) is None
+    finally:
+        uw.uw_clear_tuning()
+
+
+def test_allocator_and_release_host_rules(uw):
+    a = uw.uw_allocator()
+    a.alloc = uw.ALLOC_FN(lambda n, c: None)
+    assert uw._lib.uw_set_allocator(ctypes.byref(a)) == -1     # one hook without the other
+    assert uw._lib.uw_set_allocator(None) == 0
+    assert uw._lib.uw_release_resources() == 0                 # nothing was created
+    n = ctypes.c_size_t()
+    assert uw._lib.uw_workspace_size_cfg(None, 15, 1, None, ctypes.byref(n)) == -1
+    assert uw._lib.uw_workspace_size_grouped(None, 1, 15, 1, None, ctypes.byref(n)) == -1

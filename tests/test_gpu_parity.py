@@ -81,11 +81,8 @@ def check_codec(uw, oracle, w_dev, n, k, layout, sg=4, check_transcode=True):
 def run_pipeline(uw, m, pipeline, x, cfg=None):
     info = m.info()
     y = torch.full((x.shape[0], info.n), float("nan"), dtype=torch.float32, device=DEV)
-    ws_bytes = uw.uw_workspace_size(m, pipeline, x.shape[0])
-    if cfg and cfg.get("split_k"):
-        # partial slices, preprocessed weights and the register-fed kernel's packed x
-        packed = (info.k // 128 + 1) * 4 * 4096
-        ws_bytes = max(ws_bytes, 4 * cfg["split_k"] * x.shape[0] * info.n + 2 * info.numel + packed + 4096)
+    ws_bytes = uw.uw_workspace_size_cfg(m, pipeline, x.shape[0], cfg) if cfg else uw.uw_workspace_size(
+        m, pipeline, x.shape[0])
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV)
     uw.uw_matmul_reconstruct(m, pipeline, x, y, ws, cfg=cfg)
     torch.cuda.synchronize()
@@ -344,9 +341,7 @@ def test_grouped_matmul(uw, synth, oracle):
             x_np = bits(x)
             for p in (0, 1, 3):
                 y = torch.full((batch, N), float("nan"), dtype=torch.float32, device=DEV)
-                ws_bytes = sum(uw.uw_workspace_size(m, p, batch) for m in sub)
-                if cfg and cfg.get("split_k"):   # forced slices: partial rows of every matrix
-                    ws_bytes += 4 * cfg["split_k"] * batch * N + 4096
+                ws_bytes = uw.uw_workspace_size_grouped(sub, p, batch, cfg)
                 ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV)
                 uw.uw_matmul_reconstruct_grouped(sub, p, x, y, ws, cfg=cfg)
                 torch.cuda.synchronize()

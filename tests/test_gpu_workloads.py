@@ -76,8 +76,8 @@ def gemm_parity(uw, oracle, m, w_np, layout, x, pipelines, cols=None, grouped=No
     N = sum(mm.info().n for mm in ms)
     for p in pipelines:
         y = torch.full((batch, N), float("nan"), dtype=torch.float32, device=DEV)
-        ws = torch.empty(max(16, sum(uw.uw_workspace_size(mm, p, batch) for mm in ms)), dtype=torch.uint8,
-                         device=DEV)
+        nbytes = uw.uw_workspace_size_grouped(ms, p, batch) if grouped else uw.uw_workspace_size(m, p, batch)
+        ws = torch.empty(max(16, nbytes), dtype=torch.uint8, device=DEV)
         if grouped:
             uw.uw_matmul_reconstruct_grouped(ms, p, x, y, ws)
         else:
