@@ -814,6 +814,17 @@ uw_status uw_matmul_reconstruct(const uw_matrix* m, uw_pipeline p, const uint16_
 uw_status uw_matmul_stage(const uw_matrix* m, uw_pipeline p, const void* prep_dev, const uint16_t* x_dev,
                           int64_t batch, float* y_dev, void* ws_dev, size_t ws_bytes, const uw_kernel_cfg* cfg,
                           void* stream) {
+  size_t need = 0;
+  return uw::matmul_stage_into(m, p, prep_dev, x_dev, batch, y_dev, ws_dev, ws_bytes, cfg,
+                               static_cast<hipStream_t>(stream), &need);
+}
+
+}  // extern "C"
+
+uw_status uw::matmul_stage_into(const uw_matrix* m, int p, const void* prep_dev, const uint16_t* x_dev,
+                                int64_t batch, float* y_dev, void* part, size_t part_bytes,
+                                const uw_kernel_cfg* cfg, hipStream_t s, size_t* need_out) {
+  *need_out = 0;
   if (!m || !x_dev || !y_dev || batch <= 0 || p < UW_PIPE_FULL || p > UW_PIPE_PALETTE_DIRECT) return UW_ERR_INVALID;
   if (m->fp8) return UW_ERR_UNSUPPORTED;
   if (!aligned16(x_dev) || (reinterpret_cast<uintptr_t>(y_dev) & 3u)) return UW_ERR_INVALID;
@@ -825,12 +836,15 @@ uw_status uw_matmul_stage(const uw_matrix* m, uw_pipeline p, const void* prep_de
   }
   const Plan r = plan_call(m, p, batch, cfg);
   const size_t need = partial_bytes(m, p, batch, r.cfgp());
-  if (need > ws_bytes || (need && !ws_dev) || !aligned16(ws_dev)) return UW_ERR_WORKSPACE;
+  *need_out = need;
+  if (need > part_bytes || (need && !part) || !aligned16(part)) return UW_ERR_WORKSPACE;
   WeightView v = pipeline_view(m, p, prep_dev);
-  UW_HIP(launch_gemm(v, x_dev, batch, y_dev, (int64_t)v.n, 0, r.cfgp(), static_cast<float*>(ws_dev),
-                     need / sizeof(float), static_cast<hipStream_t>(stream)));
+  UW_HIP(launch_gemm(v, x_dev, batch, y_dev, (int64_t)v.n, 0, r.cfgp(), static_cast<float*>(part),
+                     need / sizeof(float), s));
   return UW_OK;
 }
+
+extern "C" {
 
 }  // extern "C"
 

@@ -93,6 +93,10 @@ uw_status pooled_events(size_t count, hipEvent_t** out);
 // used as they are; uw_run_sequence resolves UW_PIPE_AUTO and tuned cfgs first
 uw_status jobs_workspace(const uw_job* jobs, int count, size_t* bytes);
 uw_status run_jobs(const uw_job* jobs, int count, int32_t decode_cus, void* ws, size_t ws_bytes, hipStream_t s);
+// the GEMM stage of uw_matmul_stage with its partial sums in `part`
+// (part_bytes); *need = the bytes the call needs, set before the size check
+uw_status matmul_stage_into(const uw_matrix* m, int p, const void* prep, const uint16_t* x, int64_t batch, float* y,
+                            void* part, size_t part_bytes, const uw_kernel_cfg* cfg, hipStream_t s, size_t* need);
 // bit 0: Huffman stream resident, bit 1: palette indices resident
 int residency_of(const uw_matrix* m);
 // the tuned choice for a shape, residency and batch (nearest tuned batch on a

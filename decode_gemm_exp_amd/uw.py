@@ -119,6 +119,8 @@ _SIGS = {
                                              ctypes.POINTER(_sz)]),
     "uw_workspace_size_grouped": (ctypes.c_int, [ctypes.POINTER(_vp), ctypes.c_int, ctypes.c_int, _i64,
                                                  ctypes.POINTER(uw_kernel_cfg), ctypes.POINTER(_sz)]),
+    "uw_matmul_stage_static": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _i64, _vp,
+                                              ctypes.POINTER(uw_kernel_cfg), _vp]),
     "uw_set_allocator": (ctypes.c_int, [ctypes.POINTER(uw_allocator)]),
     "uw_release_resources": (ctypes.c_int, []),
     "uw_set_tuning": (ctypes.c_int, [ctypes.POINTER(uw_tune_entry), ctypes.c_int]),
@@ -303,6 +305,15 @@ def uw_matmul_stage(m: Matrix, pipeline: int, prep: torch.Tensor | None, x: torc
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(_lib.uw_matmul_stage(m.handle, pipeline, _ptr(prep), _ptr(x), x.shape[0], _ptr(y), _ptr(ws), nbytes,
                                 _cfg(cfg), _stream(stream)), "uw_matmul_stage")
+
+
+STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def uw_matmul_stage_static(m: Matrix, pipeline: int, prep: torch.Tensor | None, x: torch.Tensor, y: torch.Tensor,
+                           cfg=None, stream=None) -> None:
+    _check(_lib.uw_matmul_stage_static(m.handle, pipeline, _ptr(prep), _ptr(x), x.shape[0], _ptr(y), _cfg(cfg),
+                                       _stream(stream)), "uw_matmul_stage_static")
 
 
 def uw_matmul_reconstruct_grouped(ms, pipeline: int, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor | None,

@@ -266,6 +266,23 @@ uw_status uw_matmul_stage(const uw_matrix* m, uw_pipeline p, const void* prep_de
                           int64_t batch, float* y_dev, void* ws_dev, size_t ws_bytes,
                           const uw_kernel_cfg* cfg, void* stream);
 
+/* Size of the static scratch array of uw_matmul_stage_static, per GPU. */
+#define UW_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* uw_matmul_stage for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and kernels, but the split-K partial sums live in a
+ * static device array of UW_STATIC_SCRATCH_BYTES that each GPU the library
+ * runs on holds until the process ends, instead of a caller workspace.  It
+ * calls no allocating routine.  A call that would need more scratch than the
+ * array holds (large batch x N with a K split) returns UW_ERR_WORKSPACE
+ * before anything is enqueued: ask for fewer slices (cfg->split_k = 1 needs
+ * none for the tiled kernels) or use uw_matmul_stage.  Every call on one GPU
+ * shares the array: calls that overlap on one GPU (several streams or
+ * threads) race and must be serialised by the caller. */
+uw_status uw_matmul_stage_static(const uw_matrix* m, uw_pipeline p, const void* prep_dev, const uint16_t* x_dev,
+                                 int64_t batch, float* y_dev, const uw_kernel_cfg* cfg, void* stream);
+
 /* Several matrices with the same K sharing one x, one launch per stage where
  * the kernels allow (groups of 2 to 4): y_dev is [batch][sum of N] with matrix i's
  * columns at offset sum_{j<i} N_j.  Serves the fused gate+up projection
