@@ -42,6 +42,7 @@
 // Parity pins for each function live in tests/test_oracle_*.py.
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -544,7 +545,7 @@ int gemm_ref(const uint16_t* x, uint64_t batch, uint64_t K, const uint16_t* stor
       for (uint64_t k = 0; k < K; ++k) {
         const double p = bf16_value(x[b * K + k]) * wrow[k];
         sum += p;
-        mag += p < 0 ? -p : p;
+        mag += std::fabs(p);
       }
       y[b * ncols + j] = sum;
       A[b * ncols + j] = mag;
