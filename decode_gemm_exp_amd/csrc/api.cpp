@@ -1004,6 +1004,18 @@ uw_status uw_gemm_bf16(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout la
 
 int32_t uw_variant_count(void) { return gemm_variant_count(); }
 
+uw_status uw_plan_gemm(const uw_matrix* m, uw_pipeline p, int64_t batch, const uw_kernel_cfg* cfg,
+                       uw_gemm_plan* out) {
+  if (!m || !out || batch <= 0 || !pipeline_arg(p)) return UW_ERR_INVALID;
+  if (m->fp8) return UW_ERR_UNSUPPORTED;
+  std::memset(out, 0, sizeof(*out));
+  const Plan r = plan_call(m, p, batch, cfg);
+  if (!pipeline_feasible(m, r.p)) return UW_ERR_STATE;
+  out->pipeline = r.p;
+  describe_gemm(pipeline_view(m, r.p, nullptr), batch, r.cfgp(), out);
+  return UW_OK;
+}
+
 }  // extern "C"
 
 namespace {

@@ -21,6 +21,8 @@
 #include <cmath>
 #include <cstring>
 
+#include <cstdio>
+
 #include "rebuild.h"
 
 namespace uw {
@@ -754,6 +756,56 @@ static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_c
   if (batch <= 64) return 2 + 0;
   if (batch <= 128) return 2 + 2;
   return big;
+}
+
+// The kernel one matrix call runs (uw_plan_gemm): variant, tile, K slices and
+// the kernel's name as a profiler shows it (template arguments for the MFMA
+// kernels, the family name for the GEMVs).
+void describe_gemm(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg, uw_gemm_plan* out) {
+  const int v = resolve_variant(w, batch, cfg);
+  out->variant = v;
+  out->fmt = w.fmt;
+  out->tile_m = out->tile_n = out->waves = 0;
+  out->k_slices = 1;
+  if (v == 1) {
+    const int nb = (int)(batch < kGemvMaxBatch ? batch : kGemvMaxBatch);
+    if (w.layout == 0) {
+      GemvGroup grp;
+      std::memset(&grp, 0, sizeof(grp));
+      grp.w[0] = w;
+      grp.count = 1;
+      uint64_t blocks = 0;
+      int wpb = 0;
+      const bool pipe = gemv_group_plan(grp, nb, &blocks, &wpb);
+      std::snprintf(out->kernel, sizeof(out->kernel), "%s<%d, %d", pipe ? "k_gemv_nk_pipe" : "k_gemv_nk_any",
+                    w.fmt, nb);
+      out->waves = pipe ? wpb : 4;
+    } else {
+      out->k_slices = kn_slices(w, nb, cfg);
+      std::snprintf(out->kernel, sizeof(out->kernel), "k_gemv_kn<%d, ", w.fmt);
+      out->waves = 8;
+    }
+    return;
+  }
+  if (v >= rf_first_variant()) {
+    const int kind = v - rf_first_variant();
+    out->tile_n = 32 * (kind + 1);
+    out->tile_m = 16;
+    out->waves = 4;
+    out->k_slices = mfma_rf_slices(w, kind, cfg ? cfg->split_k : 0, device_cus());
+    std::snprintf(out->kernel, sizeof(out->kernel), "k_mfma_rf<%d, %d, ", w.fmt, 2 * (kind + 1));
+    return;
+  }
+  const int tile = v - 2;
+  int bm = 0, bn = 0;
+  mfma2_tile_dims(tile, &bm, &bn);
+  out->tile_m = bm;
+  out->tile_n = bn;
+  out->waves = tile == 7 ? 8 : 4;
+  const int wgm = tile == 5 || tile == 6 ? 1 : 2;
+  out->k_slices = mfma2_slices(w, batch, tile, cfg ? cfg->split_k : 0);
+  std::snprintf(out->kernel, sizeof(out->kernel), "k_mfma2<%d, %d, %d, %d, %d, %d>", w.layout, w.fmt, bm, bn, wgm,
+                out->waves);
 }
 
 // One launch for a group of stored [N][K] matrices with the same K and x

@@ -177,6 +177,7 @@ size_t gemm_partial_elems(const WeightView& w, int64_t batch, const uw_kernel_cf
 hipError_t launch_gemm_group(const WeightView* ws, int count, const uint16_t* x, int64_t batch, float* y,
                              int64_t ldy, const int64_t* col0s, const uw_kernel_cfg* cfg, hipStream_t s);
 size_t gemm_partial_elems_max(const WeightView& w, int64_t batch, int split_k);
+void describe_gemm(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg, uw_gemm_plan* out);
 int gemm_variant_count();
 int rf_first_variant();                          // first register-fed MFMA variant
 bool gemm_variant_supported(int v, int layout);  // register-fed variants: stored [N][K] only

@@ -76,6 +76,12 @@ class uw_allocator(ctypes.Structure):
     _fields_ = [("alloc", ALLOC_FN), ("free", FREE_FN), ("ctx", ctypes.c_void_p)]
 
 
+class uw_gemm_plan(ctypes.Structure):
+    _fields_ = [("pipeline", ctypes.c_int32), ("variant", ctypes.c_int32), ("fmt", ctypes.c_int32),
+                ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("waves", ctypes.c_int32),
+                ("k_slices", ctypes.c_int32), ("reserved", ctypes.c_int32), ("kernel", ctypes.c_char * 64)]
+
+
 class uw_job(ctypes.Structure):
     _fields_ = [("m", ctypes.c_void_p), ("pipeline", ctypes.c_int32), ("cfg", uw_kernel_cfg),
                 ("x_dev", ctypes.c_void_p), ("y_dev", ctypes.c_void_p), ("batch", ctypes.c_int64)]
@@ -121,6 +127,9 @@ _SIGS = {
                                                  ctypes.POINTER(uw_kernel_cfg), ctypes.POINTER(_sz)]),
     "uw_matmul_stage_static": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _i64, _vp,
                                               ctypes.POINTER(uw_kernel_cfg), _vp]),
+    "uw_plan_gemm": (ctypes.c_int, [_vp, ctypes.c_int, _i64, ctypes.POINTER(uw_kernel_cfg),
+                                    ctypes.POINTER(uw_gemm_plan)]),
+    "uw_yardstick": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _sz, _i64, _vp, ctypes.POINTER(ctypes.c_double)]),
     "uw_set_allocator": (ctypes.c_int, [ctypes.POINTER(uw_allocator)]),
     "uw_release_resources": (ctypes.c_int, []),
     "uw_set_tuning": (ctypes.c_int, [ctypes.POINTER(uw_tune_entry), ctypes.c_int]),
@@ -376,6 +385,25 @@ def uw_autotune(ms, proj, batches, max_passes: int = 3, json_path: str | None = 
     _check(_lib.uw_autotune(arr, pj, len(ms), nproj, bs, len(batches), max_passes,
                             json_path.encode() if json_path else None, out, _stream(stream)), "uw_autotune")
     return [_entry_dict(e) for e in out]
+
+
+def uw_plan_gemm(m: Matrix, pipeline: int, batch: int, cfg=None) -> dict:
+    pl = uw_gemm_plan()
+    _check(_lib.uw_plan_gemm(m.handle, pipeline, batch, _cfg(cfg), ctypes.byref(pl)), "uw_plan_gemm")
+    d = {f: getattr(pl, f) for f, _ in uw_gemm_plan._fields_ if f != "reserved"}
+    d["kernel"] = pl.kernel.decode()
+    return d
+
+
+YARDSTICK_SINK_BYTES = 4 << 20
+
+
+def uw_yardstick(kind: int, src, dst, nbytes: int = 0, iters: int = 0, stream=None) -> float:
+    """kind 0 copy, 1 read, 2 MFMA loop; returns the work (bytes or flops)."""
+    w = ctypes.c_double()
+    _check(_lib.uw_yardstick(kind, _ptr(src), _ptr(dst), nbytes, iters, _stream(stream), ctypes.byref(w)),
+           "uw_yardstick")
+    return w.value
 
 
 def uw_sync_status(m: Matrix, stream=None) -> int:

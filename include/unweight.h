@@ -308,6 +308,26 @@ uw_status uw_gemm_bf16(const uint16_t* w_dev, int64_t n, int64_t k, uw_layout la
                        const uint16_t* x_dev, int64_t batch, float* y_dev,
                        const uw_kernel_cfg* cfg, void* stream);
 
+/* The GEMM kernel a call would run, resolved as the call resolves it
+ * (UW_PIPE_AUTO, the tuning table, the default kernel table).  Introspection
+ * for profiling and logs; enqueues nothing. */
+typedef struct {
+  int32_t pipeline;     /* resolved uw_pipeline                                  */
+  int32_t variant;      /* resolved uw_kernel_cfg.variant (1..uw_variant_count) */
+  int32_t fmt;          /* weights as the kernel reads them: 0 BF16, 1 exponent
+                           + sign/mantissa, 2 palette, 3 palette of consecutive
+                           exponents                                            */
+  int32_t tile_m;       /* batch rows per block tile (0 for the GEMVs)           */
+  int32_t tile_n;       /* output columns per block (per wave for the
+                           register-fed kernels; 0 for the GEMVs)               */
+  int32_t waves;        /* waves per block                                       */
+  int32_t k_slices;     /* K split (1 = none)                                    */
+  int32_t reserved;
+  char kernel[64];      /* kernel name, or its prefix, as a profiler lists it   */
+} uw_gemm_plan;
+uw_status uw_plan_gemm(const uw_matrix* m, uw_pipeline p, int64_t batch, const uw_kernel_cfg* cfg,
+                       uw_gemm_plan* out);
+
 /* Number of GEMM variants selectable through uw_kernel_cfg.variant, numbered
  * 1..count: 1 = VALU GEMV (v_dot2; any batch, eight rows per launch);
  * 2..count-2 = MFMA tiles 64x128, 128x128, 128x256, 256x128, 256x256,
@@ -395,6 +415,21 @@ uw_status uw_lookup_tuning(uint64_t n, uint64_t k, int32_t layout, int32_t resid
 
 /* Free resident palette indices (keeps the Huffman form).  Synchronises. */
 uw_status uw_drop_palette(uw_matrix* m, void* stream);
+
+/* Yardsticks: the device's achievable rates, measured by the library's own
+ * kernels (no compressed data involved), to read the codec and GEMM figures
+ * against.  ([EVC] "GPU記憶體瓶頸成關鍵": memory bandwidth bounds inference.)
+ *   kind 0: copy `bytes` (a multiple of 16) from src_dev to dst_dev with
+ *           16-byte loads and stores; *work = 2 * bytes moved;
+ *   kind 1: read `bytes` from src_dev; each thread stores one word of what it
+ *           read to dst_dev (at most UW_YARDSTICK_SINK_BYTES); *work = bytes;
+ *   kind 2: `iters` rounds of four v_mfma_f32_32x32x16_bf16 per wave on
+ *           register operands, two waves per SIMD on every CU; one float per
+ *           thread to dst_dev; *work = flops.
+ * Pointers 16-byte aligned.  Asynchronous on `stream`. */
+#define UW_YARDSTICK_SINK_BYTES (4u << 20)
+uw_status uw_yardstick(int kind, const void* src_dev, void* dst_dev, size_t bytes, int64_t iters, void* stream,
+                       double* work);
 
 /* Synchronise `stream` and report whether any decoder working on m found an
  * invalid codeword or a segment whose codes overran or underran its words
