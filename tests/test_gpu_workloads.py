@@ -162,10 +162,13 @@ def test_mlp70b_one_layer(uw, synth, oracle):
         m, w_np, om = codec_parity(uw, oracle, w, n, k, layout)
         del w, om
         cols = np.sort(rng.choice(n, 64, replace=False))
-        for b in (1, 64, 1024):
+        # all four pipelines at 1, 192 and 512 rows (the 256-row tiles with
+        # the one-round K cap and the palette tail split act from 65 to 512
+        # rows); exponent and direct palette at 64 and 1024
+        for b in (1, 64, 192, 512, 1024):
             x = synth.activations(b, k, seed=wl.seed + b, device=DEV)
-            gemm_parity(uw, oracle, m, w_np, layout, x, (1, 3) if b > 1 else range(4), cols=cols,
-                        what=f"mlp70b {label}")
+            gemm_parity(uw, oracle, m, w_np, layout, x, (1, 3) if b in (64, 1024) else range(4), cols=cols,
+                        what=f"mlp70b {label} b{b}")
         del m, w_np
         torch.cuda.empty_cache()
 
