@@ -15,7 +15,7 @@ pass over all 240 matrices through uw_run_sequence (x ~ N(0,1) bf16
 are resident in HBM before the timed region.
 
 value = decoded-weight GB/s of the step: the bf16 bytes of weights delivered
-to the GEMMs (11 passes x 2 x 18.79 G weights) over the step's wall time.
+to the GEMMs (11 passes x 2 x 56.37 G weights) over the step's wall time.
 Per-batch rows report decoded GB/s, TFLOP/s and the roofline fraction; the
 roofline object reports the kernel launch configuration with the largest
 share of the sweep.  Prints one JSON line.
@@ -722,7 +722,7 @@ def run_c5(args) -> int:
                    "bits_per_weight": round(8 * sum(i.compressed_bytes for i in infos) / M_total, 3),
                    "seg_groups": args.seg_groups, "parallelism": "single GPU"},
         "value_definition": "sum over the sweep's batches of the bf16 weight bytes delivered to the GEMMs "
-                            "(2 x 18.79 G weights per pass) / step wall time",
+                            "(2 x 56.37 G weights per pass) / step wall time",
         "tflops_step": round(flops_step / (ms_per_step * 1e-3) / 1e12, 1),
         "tune_seconds": round(t_tune, 1), "rows": rows, "roofline": roof, "measured_peaks": peaks,
         "breakdown_top": breakdown[:12],

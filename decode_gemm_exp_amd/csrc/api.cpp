@@ -210,6 +210,7 @@ WeightView base_view(const uw_matrix* m) {
   v.vflags = m->vflags;
   v.vrank = m->vrank;
   v.vexp = m->vexp;
+  v.vexp_bytes = 64 * m->V;
   pal_words(m->t, &v.pal);
   return v;
 }

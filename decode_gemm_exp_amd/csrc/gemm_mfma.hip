@@ -43,32 +43,26 @@ constexpr int kLDK = kBK + 8;   // bf16 per LDS row: 144 bytes keeps 16-byte ali
 struct Raw {
   uint4 a;      // bf16: weights 0..7 | exp/pal: 16 sign+mantissa bytes
   uint4 b;      // bf16: weights 8..15 | exp: 16 exponent bytes | pal: the aligned 16 index
-                //   bytes holding the chunk's 8, or its 16 verbatim exponent bytes
+                //   bytes holding the chunk's 8
+  uint4 v;      // pal: the chunk's 16 verbatim exponent bytes (zero unless verbatim)
 };
 
-// Raw loads of one chunk.  Straight-line code: a chunk outside the matrix
-// reads chunk 0 instead (valid memory) and is zeroed when rebuilt, so that the
-// loads, the rebuild and the MFMAs of a step stay in one basic block for the
-// scheduler to interleave.
-template <int FMT>
-__device__ __forceinline__ void load_raw(const WeightView& w, uint64_t el, bool valid, uint32_t flagword,
-                                         uint32_t rankword, Raw& r) {
-  el = valid ? el : 0;
-  if constexpr (FMT == kFmtBf16) {
-    const uint4* p = reinterpret_cast<const uint4*>(w.bf16 + el);
-    r.a = p[0];
-    r.b = p[1];
-  } else if constexpr (FMT == kFmtExp) {
-    r.a = *reinterpret_cast<const uint4*>(w.sm + el);
-    r.b = *reinterpret_cast<const uint4*>(w.ex + el);
-  } else {
-    r.a = *reinterpret_cast<const uint4*>(w.sm + el);
-    const uint64_t g = el >> 6;
-    const uint8_t* p = valid && group_verbatim(flagword, g)
-                           ? w.vexp + (uint64_t)group_rank(flagword, rankword, g) * 64 + (el & 63)
-                           : w.pidx + ((el >> 1) & ~(uint64_t)15);
-    r.b = *reinterpret_cast<const uint4*>(p);
-  }
+// Byte-addressed buffer resources: a read at or past the resource's end
+// returns zero, so loads need neither clamps nor branches, and every load of
+// a step sits in one basic block with the step's MFMAs.
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+constexpr uint32_t kRecMax = 0x40000000u;     // a resource spans at most 1 GiB
+constexpr uint32_t kPastEnd = 0x7FFF0000u;    // an offset past every resource
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
+                                           (int)(bytes < kRecMax ? bytes : kRecMax), 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t byte) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t byte) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte, 0, 0);
 }
 
 // Rebuild 16 weights (8 dwords of packed bf16) from a raw chunk; chunks
@@ -83,7 +77,10 @@ __device__ __forceinline__ void rebuild_raw(const WeightView& w, const Raw& r, b
     rebuild16(r.a, r.b, o);
   } else {
     uint4 e = pal16<FMT == kFmtPalRun>(hi ? r.b.z : r.b.x, hi ? r.b.w : r.b.y, w.pal);
-    if (verbatim) e = r.b;
+    // a verbatim group's own exponents, selected without a branch so the
+    // step stays one basic block
+    const uint32_t vm = verbatim ? ~0u : 0u;
+    e = make_uint4(bfi(vm, r.v.x, e.x), bfi(vm, r.v.y, e.y), bfi(vm, r.v.z, e.z), bfi(vm, r.v.w, e.w));
     rebuild16(r.a, e, o);
   }
 #pragma unroll
@@ -167,70 +164,125 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
   const int64_t ke = kb + kslice < K ? kb + kslice : K;
   const int steps = (int)((ke - kb + kBK - 1) / kBK);
 
-  // chunk c of this thread (i-th): NK -> row r = c / 4, k sub-block q = c % 4;
-  // KN -> k row kr = c / (BN/16), n sub-block q = c % (BN/16)
-  auto chunk_el = [&](int i, int64_t k0, bool& valid) __attribute__((always_inline)) -> uint64_t {
-    const int c = tid + i * NT;
-    if constexpr (LAYOUT == 0) {
-      const int64_t n = n0 + (c >> 2), k = k0 + (c & 3) * 16;
-      valid = n < N && k < ke;
-      return (uint64_t)(n * K + k);
-    } else {
-      constexpr int QN = BN / 16;
-      const int64_t k = k0 + c / QN, n = n0 + (c % QN) * 16;
-      valid = k < ke && n < N;
-      return (uint64_t)(k * N + n);
-    }
-  };
+  // Resources over what the block reads; offsets are 32-bit and advance by a
+  // constant per step.  [N][K]: rows [n0, min(n0 + BN, N)) from column kb
+  // (reads past the slice's K end belong to steps whose data is never
+  // multiplied); [K][N]: rows [kb, ke) from column n0 (rows past ke read
+  // zero, and are zeroed when rebuilt, since a K tail multiplies them).  The
+  // host keeps every span under kRecMax.
+  const uint64_t wbase = LAYOUT == 0 ? (uint64_t)n0 * (uint64_t)K + (uint64_t)kb
+                                     : (uint64_t)kb * (uint64_t)N + (uint64_t)n0;
+  const uint64_t wlim = LAYOUT == 0 ? (uint64_t)(n0 + BN < N ? n0 + BN : N) * (uint64_t)K
+                                    : (uint64_t)ke * (uint64_t)N;
+  const uint64_t wspan = wlim > wbase ? wlim - wbase : 0;
+  const uint32_t wb32 = (uint32_t)wbase;   // element indices fit 32 bits (numel < 2^32)
+  __amdgpu_buffer_rsrc_t rwa, rwb, rvx, rfl, rrk;
+  if constexpr (FMT == kFmtBf16) {
+    rwa = rsrc(w.bf16 + wbase, 2 * wspan);
+    rwb = rwa;
+  } else if constexpr (FMT == kFmtExp) {
+    rwa = rsrc(w.sm + wbase, wspan);
+    rwb = rsrc(w.ex + wbase, wspan);
+  } else {
+    rwa = rsrc(w.sm + wbase, wspan);
+    rwb = rsrc(w.pidx + wbase / 2, (wspan + 1) / 2);
+    rvx = rsrc(w.vexp, w.vexp_bytes);
+    const uint64_t fwords = (w.n * w.k / 64 + 31) / 32;
+    rfl = rsrc(w.vflags, 4 * fwords);
+    rrk = rsrc(w.vrank, 4 * fwords);
+  }
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x, (uint64_t)B * (uint64_t)K * 2);
+  constexpr int QN = BN / 16;
+  // per step: a stored [N][K] chunk moves 64 columns on, a [K][N] chunk 64 rows
+  const uint32_t wadv = LAYOUT == 0 ? (uint32_t)kBK : (uint32_t)kBK * (uint32_t)N;
+
+  // chunk i of this thread (c = tid + i NT): [N][K] -> row c / 4, columns
+  // 16 (c % 4) of the step; [K][N] -> k row c / QN, columns 16 (c % QN).  The
+  // chunks of one thread differ only in their row, by NT / 4 (or NT / QN)
+  // rows, so one offset register serves all of them: wo = element offset of
+  // chunk 0 in the step whose data loads next, chunk i at wo + i wstride.
+  // The column within the row is the same for every chunk and every step
+  // (steps move by multiples of 64 elements): whi = the chunk's 8 index bytes
+  // are the upper half of their aligned 16, wsub = its offset in its group.
+  static_assert(NT % 16 == 0 && NT % QN == 0, "chunk columns must repeat across a thread's chunks");
+  const uint32_t wstride = LAYOUT == 0 ? (uint32_t)(NT / 4) * (uint32_t)K : (uint32_t)(NT / QN) * (uint32_t)N;
+  uint32_t wo;
+  int wkr;
+  if constexpr (LAYOUT == 0) {
+    wo = (uint32_t)(tid >> 2) * (uint32_t)K + 16u * (uint32_t)(tid & 3);
+    wkr = 0;
+  } else {
+    wo = (uint32_t)(tid / QN) * (uint32_t)N + 16u * (uint32_t)(tid % QN);
+    wkr = tid / QN;
+  }
+  const uint32_t wsub = (wb32 + wo) & 48u;
+  const bool whi = (wsub & 16u) != 0;
+  // x chunk i: row m0 + c / 8, columns 8 (c % 8) of the step, at xo + i
+  // xstride bytes; rows past the batch read zero (never stored), columns past
+  // K read the next row's values (finite; a K tail meets zeroed weight rows)
+  const uint32_t xstride = (uint32_t)(NT / 8) * (uint32_t)K * 2u;
+  uint32_t xo = (uint32_t)((uint64_t)(m0 + (tid >> 3)) * (uint64_t)K + (uint64_t)kb + 8u * (uint32_t)(tid & 7)) * 2u;
+  int kstep = 0;   // k of the step whose data loads next, from kb
+  const int klen = (int)(ke - kb);
 
   uint4 xr[XC];
   Raw wr[WC];
-  bool wverb[WC], wval[WC], whi[WC];
+  bool wverb[WC], wval[WC];
   uint32_t fw_a[WC], rk_a[WC];   // palette: flag / rank words of the step whose data loads next
 
   // The per-step work is split into four parts (one per 16-wide k slice of
   // the MFMAs); chunk i of the loads and stores belongs to part (4 i) / n.
   auto in_part = [](int i, int n, int part) __attribute__((always_inline)) { return (4 * i) / n == part; };
-  auto load_flags = [&](int64_t k0, int part) __attribute__((always_inline)) {
+  // Flag and rank words of the step whose data loads next for the chunks of
+  // `part`.  Called just after load_step(part) (after = true) that is the
+  // step after the one wo points to, until part 3's load moves wo on.
+  auto load_flags = [&](int part, bool after) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < WC; ++i) {
       if (!in_part(i, WC, part)) continue;
-      bool v;
-      const uint64_t el = chunk_el(i, k0, v);
-      const uint64_t fi = v ? el >> 11 : 0;
-      const uint32_t f = w.vflags[fi], r = w.vrank[fi];
-      fw_a[i] = v ? f : 0u;
-      rk_a[i] = v ? r : 0u;
+      const uint32_t next = after && part != 3 ? wadv : 0u;
+      const uint32_t fo = ((wb32 + wo + next + (uint32_t)i * wstride) >> 11) * 4u;
+      fw_a[i] = bload4(rfl, fo);
+      rk_a[i] = bload4(rrk, fo);
     }
   };
-  auto load_step = [&](int64_t k0, int part) __attribute__((always_inline)) {
+  auto load_step = [&](int part) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < XC; ++i) {
       if (!in_part(i, XC, part)) continue;
-      // rows past the batch are never stored and k past the slice meets zeroed
-      // weight rows, so x needs only a clamped (always valid) address
-      const int c = tid + i * NT;
-      const int64_t row0 = m0 + (c >> 3), kk0 = k0 + (c & 7) * 8;
-      const int64_t row = row0 < B ? row0 : B - 1, kk = kk0 < K ? kk0 : K - 8;
-      const uint4 t = *reinterpret_cast<const uint4*>(x + row * K + kk);
-      xr[i] = t;
+      xr[i] = bload16(rx, xo + (uint32_t)i * xstride);
     }
 #pragma unroll
     for (int i = 0; i < WC; ++i) {
       if (!in_part(i, WC, part)) continue;
-      bool v;
-      const uint64_t el = chunk_el(i, k0, v);
-      load_raw<FMT>(w, el, v, fw_a[i], rk_a[i], wr[i]);
-      // zeroed when rebuilt: only [K][N] chunks past K.  Chunks past N only
-      // feed output columns that are never stored, and a stored [N][K] row is
-      // a multiple of 64 long, so none of its steps that are read reach past K
+      const uint32_t o = wo + (uint32_t)i * wstride;
+      if constexpr (FMT == kFmtBf16) {
+        wr[i].a = bload16(rwa, 2u * o);
+        wr[i].b = bload16(rwa, 2u * o + 16u);
+      } else if constexpr (FMT == kFmtExp) {
+        wr[i].a = bload16(rwa, o);
+        wr[i].b = bload16(rwb, o);
+      } else {
+        const uint32_t bit = ((wb32 + o) >> 6) & 31u;
+        const bool verb = (fw_a[i] >> bit) & 1u;
+        const uint32_t rank = rk_a[i] + (uint32_t)__popc(fw_a[i] & ((1u << bit) - 1u));
+        wr[i].a = bload16(rwa, o);
+        wr[i].b = bload16(rwb, (o >> 1) & ~15u);
+        wr[i].v = bload16(rvx, verb ? rank * 64u + wsub : kPastEnd);
+        wverb[i] = verb;
+      }
+      // zeroed when rebuilt: only [K][N] rows past the slice.  Chunks past N
+      // only feed output columns that are never stored.
       if constexpr (LAYOUT == 0) {
         wval[i] = true;
       } else {
-        wval[i] = k0 + (int64_t)((tid + i * NT) / (BN / 16)) < ke;
+        wval[i] = kstep + wkr + i * (NT / QN) < klen;
       }
-      wverb[i] = fmt_is_pal(FMT) && v && group_verbatim(fw_a[i], el >> 6);
-      whi[i] = (el & 16) != 0;
+    }
+    if (part == 3) {   // the step's last part: every chunk of the step has loaded
+      xo += 2u * kBK;
+      wo += wadv;
+      kstep += kBK;
     }
   };
   // registers of a step -> LDS buffer (x as is, weights rebuilt)
@@ -245,13 +297,12 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
     for (int i = 0; i < WC; ++i) {
       if (!in_part(i, WC, part)) continue;
       uint32_t o[8];
-      rebuild_raw<FMT>(w, wr[i], wval[i], wverb[i], whi[i], o);
+      rebuild_raw<FMT>(w, wr[i], wval[i], wverb[i], whi, o);
       const int c = tid + i * NT;
       uint4* d;
       if constexpr (LAYOUT == 0) {
         d = reinterpret_cast<uint4*>(&ws[(c >> 2) * kLDK + (c & 3) * 16]);
       } else {
-        constexpr int QN = BN / 16;
         d = reinterpret_cast<uint4*>(&ws[(c / QN) * LDW + (c % QN) * 16]);
       }
       d[0] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -303,15 +354,15 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
   // prologue: step 0 in LDS buffer 0, step 1 in registers, flags of step 2 loaded
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    if constexpr (fmt_is_pal(FMT)) load_flags(kb, p);
-    load_step(kb, p);
+    if constexpr (fmt_is_pal(FMT)) load_flags(p, false);
+    load_step(p);
   }
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    if constexpr (fmt_is_pal(FMT)) load_flags(kb + kBK, p);
+    if constexpr (fmt_is_pal(FMT)) load_flags(p, false);
     store_step(xs0, ws0, p);
-    load_step(kb + kBK, p);
-    if constexpr (fmt_is_pal(FMT)) load_flags(kb + 2 * kBK, p);
+    load_step(p);
+    if constexpr (fmt_is_pal(FMT)) load_flags(p, true);
   }
 
   // step s: MFMAs from buffer s & 1 while step s+1 is rebuilt into the other
@@ -320,14 +371,13 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
   // read) instead of branching, so every part is one basic block.
   auto body = [&](int st, const uint16_t* xs_c, const uint16_t* ws_c, uint16_t* xs_n, uint16_t* ws_n) __attribute__((always_inline)) {
     __syncthreads();
-    const int64_t k2 = kb + (int64_t)(st + 2) * kBK, k3 = k2 + kBK;
     // part p: the MFMAs of k slice p (fragments read one part earlier), the
     // next slice's fragment reads, and a quarter of the next step's rebuild
     // and of the raw loads two steps ahead
     auto rest = [&](int p) __attribute__((always_inline)) {
       store_step(xs_n, ws_n, p);
-      load_step(k2, p);
-      if constexpr (fmt_is_pal(FMT)) load_flags(k3, p);
+      load_step(p);
+      if constexpr (fmt_is_pal(FMT)) load_flags(p, true);
       // ask the scheduler to alternate one MFMA with a few VALU operations of
       // the rebuild, so the vector ALU works while the matrix core runs
 #pragma unroll
@@ -435,6 +485,12 @@ int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint) {
   int s = split_hint > 0 ? split_hint : 1;
   if (split_hint <= 0)
     while (blocks * s < target && blocks * s * 2 <= hold && (int64_t)w.k / (64 * (s * 2)) >= 8) s *= 2;
+  // a [K][N] block reads rows [kb, ke) of every column through one buffer
+  // resource: at least enough slices that a slice's rows stay under its span
+  if (w.layout == 1)
+    while ((((int64_t)w.k + 64 * s - 1) / (64 * s)) * 64 * (int64_t)w.n * 2 > (int64_t)kRecMax &&
+           (int64_t)w.k / (64 * (s * 2)) >= 1)
+      s *= 2;
   // beyond 64 rows, an unsplit palette grid that spills at most a quarter
   // round past whole rounds of resident blocks runs its last round of
   // full-length tiles on a mostly idle chip; two slices halve that tail
@@ -480,6 +536,14 @@ static hipError_t launch_group(Mfma2Group grp, const uint16_t* x, int64_t batch,
   const int slices = mfma2_slices(wide, batch, tile, split_hint);
   const int64_t steps = ((int64_t)w0.k + 63) / 64;
   const int64_t kslice = ((steps + slices - 1) / slices) * 64;
+  // every buffer resource the kernel builds spans at most kRecMax bytes:
+  // x, a [N][K] block's rows, a [K][N] slice's rows, the verbatim section
+  if ((uint64_t)batch * w0.k * 2 > kRecMax) return hipErrorNotSupported;
+  for (int i = 0; i < grp.count; ++i) {
+    const WeightView& wi = grp.w[i];
+    const uint64_t span = wi.layout == 0 ? (uint64_t)t.bn * wi.k : (uint64_t)kslice * wi.n;
+    if (span * 2 > kRecMax || wi.vexp_bytes > kRecMax) return hipErrorNotSupported;
+  }
   const bool split = slices > 1;
   if (split && (part == nullptr || part_elems < (size_t)slices * (size_t)batch * (size_t)ntot))
     return hipErrorInvalidValue;

@@ -165,6 +165,7 @@ struct WeightView {
   const uint8_t* ex;                // kFmtExp: exponent bytes
   const uint8_t* pidx;              // kFmtPal
   const uint32_t* vflags; const uint32_t* vrank; const uint8_t* vexp;   // kFmtPal
+  uint64_t vexp_bytes;              // kFmtPal: 64 x verbatim groups
   PalView pal;
 };
 // y[:, col0 : col0+n] of a row-major [batch][ldy] output
