@@ -227,6 +227,7 @@ extern "C" uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj
             if (v == 1 && batch > 32) continue;                 // the VALU kernel only for small batches
             if (bm > 32 && batch < 8) continue;                 // 64- to 256-row tiles from batch 8 on
             if (bm == 32 && (batch < 2 || batch > 128)) continue;   // 32-row tiles for batches 2..128
+            if (bm == 512 && batch < 256) continue;                 // the 512-row tile from batch 256
             if (v >= rf && (!all_nk || batch > 2 * uw::mfma_rf_max_batch())) continue;   // [N][K] only, <= 128 rows
             Choice c;
             c.pipeline = pl;

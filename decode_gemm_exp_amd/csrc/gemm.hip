@@ -742,6 +742,11 @@ bool gemm_variant_supported(int v, int layout) { return v < rf_first_variant() |
 static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg) {
   if (cfg && cfg->variant > 0 && cfg->variant <= gemm_variant_count()) return cfg->variant;
   const int big = fmt_is_pal(w.fmt) ? 2 + 7 : 2 + 4;
+  // the single-rebuild 512x128 tile (x in registers) beyond 256 rows when it
+  // pads no more rows than 256-row tiles (an even number of 256-row tiles):
+  // 70B at 1024 rows, palette-direct gate 507 -> 477 us, down 502 -> 457 us,
+  // exponent gate 471 -> 435 us; at 512 rows palette-direct 267 -> 244 us
+  if (batch > 256 && ((batch + 255) / 256) % 2 == 0) return 2 + 8;
   if (w.layout == 0) {
     if (batch <= 4) return 1;
     if (batch <= 32 && mfma_rf_supported(w, 0)) return rf_first_variant();
@@ -801,11 +806,15 @@ void describe_gemm(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg,
   mfma2_tile_dims(tile, &bm, &bn);
   out->tile_m = bm;
   out->tile_n = bn;
-  out->waves = tile == 7 ? 8 : 4;
-  const int wgm = tile == 5 || tile == 6 ? 1 : 2;
+  out->waves = tile >= 7 ? 8 : 4;
+  const int wgm = tile == 5 || tile == 6 ? 1 : tile == 8 ? 8 : 2;
   out->k_slices = mfma2_slices(w, batch, tile, cfg ? cfg->split_k : 0);
-  std::snprintf(out->kernel, sizeof(out->kernel), "k_mfma2<%d, %d, %d, %d, %d, %d>", w.layout, w.fmt, bm, bn, wgm,
-                out->waves);
+  if (tile == 8)
+    std::snprintf(out->kernel, sizeof(out->kernel), "k_mfma2<%d, %d, %d, %d, %d, %d, true>", w.layout, w.fmt, bm,
+                  bn, wgm, out->waves);
+  else
+    std::snprintf(out->kernel, sizeof(out->kernel), "k_mfma2<%d, %d, %d, %d, %d, %d, false>", w.layout, w.fmt, bm,
+                  bn, wgm, out->waves);
 }
 
 // One launch for a group of stored [N][K] matrices with the same K and x

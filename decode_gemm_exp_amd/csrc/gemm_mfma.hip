@@ -126,6 +126,25 @@ constexpr int w_ld() { return LAYOUT == 0 ? kLDK : BN + 16; }   // KN rows: BN +
 template <int LAYOUT, int BN>
 constexpr int w_tile_elems() { return LAYOUT == 0 ? BN * kLDK : kBK * (BN + 16); }
 
+// x [B][K] -> the A fragments of v_mfma_f32_32x32x16_bf16 in the lanes'
+// read order, for the tiles that keep x in registers: fragment (R, S) (rows
+// 32 R.., columns 16 S..) is 1 KB at (R SK + S) KB with SK = ceil(K / 16), and
+// lane l's 16 bytes are row 32 R + (l % 32), columns 16 S + 8 (l / 32) .. + 7.
+// Each fragment load then reads 1 KB of contiguous memory instead of 32 rows
+// of 32 bytes.  Rows past B and columns past K are zero.
+__global__ __launch_bounds__(256) void k_pack_xa(const uint16_t* __restrict__ x, int B, int64_t K, int64_t SK,
+                                                 int64_t pieces, uint4* __restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= pieces) return;
+  const int64_t f = t >> 6;
+  const int l = (int)(t & 63);
+  const int64_t R = f / SK, S = f - R * SK;
+  const int64_t row = 32 * R + (l & 31), col = 16 * S + 8 * (l >> 5);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row < B && col < K) v = *reinterpret_cast<const uint4*>(x + row * K + col);   // K % 8 == 0
+  out[t] = v;
+}
+
 // NW waves per block (4 or 8); with 8 two waves share each SIMD, so one
 // wave's rebuild arithmetic can issue while the other's MFMAs run.
 // One launch serves a group of up to four matrices with the same K, layout
@@ -134,7 +153,14 @@ constexpr int w_tile_elems() { return LAYOUT == 0 ? BN * kLDK : kBK * (BN + 16);
 // of blocks to XCDs spreads each matrix evenly.  Matrix g writes columns
 // ycol[g].. of y, or columns pcol[g].. of the partial rows (pld wide) when K
 // is split.
-template <int LAYOUT, int FMT, int BM, int BN, int WGM, int NW = 4>
+//
+// XREG (single rebuild): x never enters LDS.  Each wave owns BM / NW batch
+// rows across the whole tile width and loads its MFMA A fragments straight
+// from memory into registers, one k slice at a time, a step ahead; only the
+// rebuilt weight tile is shared through LDS.  With BM = 512 every weight is
+// rebuilt once per 512 batch rows (the 256-row tiles rebuild it once per 256),
+// LDS carries a third less per MFMA, and the LDS tile is small.
+template <int LAYOUT, int FMT, int BM, int BN, int WGM, int NW = 4, bool XREG = false>
 __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_t* __restrict__ x, int B,
                                                    float* __restrict__ y, int64_t ldy, int64_t kslice,
                                                    float* __restrict__ part, int64_t pld, int mtiles) {
@@ -142,12 +168,13 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
   constexpr int WGN = NW / WGM;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int XC = BM * 8 / NT;      // 16-byte x chunks per thread per step
-  constexpr int WC = BN * 4 / NT;      // 16-weight chunks per thread per step
+  constexpr int XC = XREG ? 0 : BM * 8 / NT;   // 16-byte x chunks per thread per step (LDS-staged x)
+  constexpr int WC = BN * 4 / NT;              // 16-weight chunks per thread per step
   constexpr int LDW = w_ld<LAYOUT, BN>();
-  constexpr int XS = BM * kLDK, WS = w_tile_elems<LAYOUT, BN>();
+  constexpr int XS = XREG ? 0 : BM * kLDK, WS = w_tile_elems<LAYOUT, BN>();
   constexpr int kValuPerMfma = FMT == kFmtBf16 ? 1 : 4;
-  static_assert(TM >= 1 && TN >= 1 && XC >= 1 && WC >= 1, "tile too small");
+  static_assert(TM >= 1 && TN >= 1 && (XREG || XC >= 1) && WC >= 1, "tile too small");
+  static_assert(!XREG || WGN == 1, "x in registers: a wave owns its rows across the tile width");
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
   int g = 0;
@@ -191,7 +218,11 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
     rfl = rsrc(w.vflags, 4 * fwords);
     rrk = rsrc(w.vrank, 4 * fwords);
   }
-  const __amdgpu_buffer_rsrc_t rx = rsrc(x, (uint64_t)B * (uint64_t)K * 2);
+  // x as given ([B][K]), or XREG: packed into fragments (k_pack_xa) for the
+  // mtiles x BM rows of the grid
+  const int64_t SK = (K + 15) / 16;
+  const __amdgpu_buffer_rsrc_t rx =
+      XREG ? rsrc(x, (uint64_t)mtiles * (BM / 32) * (uint64_t)SK * 1024u) : rsrc(x, (uint64_t)B * (uint64_t)K * 2);
   constexpr int QN = BN / 16;
   // per step: a stored [N][K] chunk moves 64 columns on, a [K][N] chunk 64 rows
   const uint32_t wadv = LAYOUT == 0 ? (uint32_t)kBK : (uint32_t)kBK * (uint32_t)N;
@@ -224,8 +255,22 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
   uint32_t xo = (uint32_t)((uint64_t)(m0 + (tid >> 3)) * (uint64_t)K + (uint64_t)kb + 8u * (uint32_t)(tid & 7)) * 2u;
   int kstep = 0;   // k of the step whose data loads next, from kb
   const int klen = (int)(ke - kb);
+  // XREG: this lane's piece of the packed A fragment (row fragment 0, k slice
+  // 0) of the step whose x loads next; row fragment i is SK fragments on,
+  // slice s one fragment (1 KB), a step four
+  uint32_t xao = 0;
+  if constexpr (XREG)
+    xao = (uint32_t)((((uint64_t)(m0 + wm * WM) / 32) * (uint64_t)SK + (uint64_t)kb / 16) * 1024u) +
+          16u * (uint32_t)lane;
+  const uint32_t xa_frag = (uint32_t)SK * 1024u;
+  bf16x8 xa[4][TM];
+  auto load_xa = [&](int sl) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      xa[sl][i] = __builtin_bit_cast(bf16x8, bload16(rx, xao + (uint32_t)i * xa_frag + 1024u * (uint32_t)sl));
+  };
 
-  uint4 xr[XC];
+  uint4 xr[XC > 0 ? XC : 1];
   Raw wr[WC];
   bool wverb[WC], wval[WC];
   uint32_t fw_a[WC], rk_a[WC];   // palette: flag / rank words of the step whose data loads next
@@ -323,10 +368,12 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
   bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
   auto read_frags = [&](const uint16_t* xs, const uint16_t* ws, int kk, bf16x8 (&a)[TM],
                         bf16x8 (&b)[TN]) __attribute__((always_inline)) {
+    if constexpr (!XREG) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int row = wm * WM + i * 32 + (lane & 31);
-      a[i] = *reinterpret_cast<const bf16x8*>(&xs[row * kLDK + kk + 8 * (lane >> 5)]);
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * WM + i * 32 + (lane & 31);
+        a[i] = *reinterpret_cast<const bf16x8*>(&xs[row * kLDK + kk + 8 * (lane >> 5)]);
+      }
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -338,12 +385,18 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
       }
     }
   };
-  auto mfma_set = [&](const bf16x8 (&a)[TM], const bf16x8 (&b)[TN]) __attribute__((always_inline)) {
+  // the MFMAs of k slice sl; XREG takes A from the slice's registers, which
+  // then load the next step's slice
+  auto mfma_set = [&](int sl, const bf16x8 (&a)[TM], const bf16x8 (&b)[TN]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(XREG ? xa[sl][i] : a[i], b[j], acc[i][j], 0, 0, 0);
+    if constexpr (XREG) {
+      load_xa(sl);
+      if (sl == 3) xao += 4u * 1024u;
+    }
   };
 
   uint16_t* const xs0 = lds;
@@ -351,7 +404,13 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
   uint16_t* const ws0 = lds + 2 * XS;
   uint16_t* const ws1 = lds + 2 * XS + WS;
 
-  // prologue: step 0 in LDS buffer 0, step 1 in registers, flags of step 2 loaded
+  // prologue: step 0 in LDS buffer 0, step 1 in registers, flags of step 2
+  // loaded (XREG: x of step 0 in registers)
+  if constexpr (XREG) {
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) load_xa(sl);
+    xao += 4u * 1024u;
+  }
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     if constexpr (fmt_is_pal(FMT)) load_flags(p, false);
@@ -389,15 +448,15 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
     };
     read_frags(xs_c, ws_c, 0, fa0, fb0);
     read_frags(xs_c, ws_c, 16, fa1, fb1);
-    mfma_set(fa0, fb0);
+    mfma_set(0, fa0, fb0);
     rest(0);
     read_frags(xs_c, ws_c, 32, fa0, fb0);
-    mfma_set(fa1, fb1);
+    mfma_set(1, fa1, fb1);
     rest(1);
     read_frags(xs_c, ws_c, 48, fa1, fb1);
-    mfma_set(fa0, fb0);
+    mfma_set(2, fa0, fb0);
     rest(2);
-    mfma_set(fa1, fb1);
+    mfma_set(3, fa1, fb1);
     rest(3);
   };
   for (int st = 0; st < steps; ++st) {
@@ -432,7 +491,8 @@ Mfma2Fn pick(int tile) {
     case 4: return k_mfma2<L, F, 256, 256, 2>;
     case 5: return k_mfma2<L, F, 32, 128, 1>;
     case 6: return k_mfma2<L, F, 32, 256, 1>;
-    default: return k_mfma2<L, F, 256, 256, 2, 8>;
+    case 7: return k_mfma2<L, F, 256, 256, 2, 8>;
+    default: return k_mfma2<L, F, 512, 128, 8, 8, true>;
   }
 }
 
@@ -441,11 +501,14 @@ Mfma2Fn pick(int tile) {
 // Tiles of the big-tile kernel: {BM, BN}.
 struct Tile2 {
   int bm, bn, waves;
+  bool xreg;   // x in registers, only the weight tile in LDS (single rebuild per 512 rows)
 };
 // 32-row tiles (one MFMA row tile, four waves side by side) are for small
-// batches; the last is 256x256 with eight waves (two per SIMD)
-static const Tile2 kTiles2[] = {{64, 128, 4},  {128, 128, 4}, {128, 256, 4}, {256, 128, 4},
-                                {256, 256, 4}, {32, 128, 4},  {32, 256, 4},  {256, 256, 8}};
+// batches; then 256x256 with eight waves (two per SIMD); the last is the
+// single-rebuild tile, 512 rows x 128 columns, eight waves of 64 rows
+static const Tile2 kTiles2[] = {{64, 128, 4, false},  {128, 128, 4, false}, {128, 256, 4, false},
+                                {256, 128, 4, false}, {256, 256, 4, false}, {32, 128, 4, false},
+                                {32, 256, 4, false},  {256, 256, 8, false}, {512, 128, 8, true}};
 int mfma2_tile_count() { return (int)(sizeof(kTiles2) / sizeof(kTiles2[0])); }
 void mfma2_tile_dims(int tile, int* bm, int* bn) {
   *bm = kTiles2[tile].bm;
@@ -465,7 +528,14 @@ void mfma2_tile_dims(int tile, int* bm, int* bn) {
 // LDS of one block: x and weight tiles, double buffered
 size_t mfma2_lds_bytes(int layout, const Tile2& t) {
   const size_t wtile = layout == 0 ? (size_t)t.bn * kLDK : (size_t)kBK * (size_t)(t.bn + 16);
-  return 2 * ((size_t)t.bm * kLDK + wtile) * sizeof(uint16_t);
+  return 2 * ((t.xreg ? 0 : (size_t)t.bm * kLDK) + wtile) * sizeof(uint16_t);
+}
+// blocks a CU holds at once: by LDS, and one for the eight-wave tiles (their
+// registers fill the SIMDs at two waves each)
+int64_t mfma2_blocks_per_cu(int layout, const Tile2& t) {
+  const int64_t by_lds = (int64_t)(160 * 1024 / mfma2_lds_bytes(layout, t));
+  const int64_t b = t.waves == 8 ? 1 : by_lds;
+  return b > 0 ? b : 1;
 }
 
 int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint) {
@@ -479,7 +549,7 @@ int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint) {
   // 40.6 us, 8 slices 47.7 us; 70B q+k+v grouped, 40 256x256 tiles at 192
   // rows: 4 slices 90 us, 8 slices 107 us; 8B q+k+v, 48 tiles at 384 rows:
   // 4 slices 52 us, 8 slices 66 us)
-  const int64_t per_cu = (int64_t)(160 * 1024 / mfma2_lds_bytes((int)w.layout, t));
+  const int64_t per_cu = mfma2_blocks_per_cu((int)w.layout, t);
   const bool one_round = batch <= 64 || (t.bm >= 256 && batch <= 512);
   const int64_t hold = one_round ? cus * (per_cu > 0 ? per_cu : 1) : INT64_MAX;
   int s = split_hint > 0 ? split_hint : 1;
@@ -507,9 +577,20 @@ int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint) {
   return s;
 }
 
+// bytes of x packed into A fragments for a tile that keeps x in registers
+static size_t packed_x_bytes(const Tile2& t, int64_t batch, uint64_t k) {
+  if (!t.xreg) return 0;
+  const uint64_t mtiles = (uint64_t)((batch + t.bm - 1) / t.bm);
+  return (size_t)(mtiles * (uint64_t)t.bm / 32 * ((k + 15) / 16) * 1024u);
+}
+
+// partial floats: the K slices' partial rows, then (x-in-register tiles)
+// the packed x, 256-byte aligned
 size_t mfma2_partial_elems(const WeightView& w, int64_t batch, int tile, int split_hint) {
   const int s = mfma2_slices(w, batch, tile, split_hint);
-  return s > 1 ? (size_t)s * (size_t)batch * (size_t)w.n : 0;
+  const size_t slices = s > 1 ? (size_t)s * (size_t)batch * (size_t)w.n : 0;
+  const size_t px = packed_x_bytes(kTiles2[tile], batch, w.k);
+  return px ? (slices + 63) / 64 * 64 + px / 4 : slices;
 }
 
 // One launch over the group's tiles; K split as for one matrix as wide as the
@@ -545,8 +626,21 @@ static hipError_t launch_group(Mfma2Group grp, const uint16_t* x, int64_t batch,
     if (span * 2 > kRecMax || wi.vexp_bytes > kRecMax) return hipErrorNotSupported;
   }
   const bool split = slices > 1;
-  if (split && (part == nullptr || part_elems < (size_t)slices * (size_t)batch * (size_t)ntot))
-    return hipErrorInvalidValue;
+  const size_t split_elems = split ? (size_t)slices * (size_t)batch * (size_t)ntot : 0;
+  const size_t px = packed_x_bytes(t, batch, w0.k);
+  if (px > kRecMax) return hipErrorNotSupported;
+  const size_t px_off = px ? (split_elems + 63) / 64 * 64 : split_elems;   // floats
+  if ((split || px) && (part == nullptr || part_elems < px_off + px / 4)) return hipErrorInvalidValue;
+  const uint16_t* xk = x;   // what the kernel reads as x
+  if (px) {
+    uint4* packed = reinterpret_cast<uint4*>(part + px_off);
+    const int64_t pieces = (int64_t)(px / 16);
+    hipLaunchKernelGGL(k_pack_xa, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, x, (int)batch,
+                       (int64_t)w0.k, (int64_t)((w0.k + 15) / 16), pieces, packed);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    xk = reinterpret_cast<const uint16_t*>(packed);
+  }
   Mfma2Fn f;
   if (w0.layout == 0) {
     f = fmt == kFmtBf16 ? pick<0, kFmtBf16>(tile) : fmt == kFmtExp ? pick<0, kFmtExp>(tile)
@@ -561,7 +655,7 @@ static hipError_t launch_group(Mfma2Group grp, const uint16_t* x, int64_t batch,
     if (e != hipSuccess) return e;
   }
   dim3 grid((unsigned)nblocks, 1, (unsigned)slices);
-  hipLaunchKernelGGL(f, grid, dim3(64 * t.waves), lds, s, grp, x, (int)batch, y, ldy, kslice, split ? part : nullptr,
+  hipLaunchKernelGGL(f, grid, dim3(64 * t.waves), lds, s, grp, xk, (int)batch, y, ldy, kslice, split ? part : nullptr,
                      (int64_t)ntot, mtiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;

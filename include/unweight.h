@@ -331,7 +331,9 @@ uw_status uw_plan_gemm(const uw_matrix* m, uw_pipeline p, int64_t batch, const u
 /* Number of GEMM variants selectable through uw_kernel_cfg.variant, numbered
  * 1..count: 1 = VALU GEMV (v_dot2; any batch, eight rows per launch);
  * 2..count-2 = MFMA tiles 64x128, 128x128, 128x256, 256x128, 256x256,
- * 32x128, 32x256 (batch rows x columns; weights rebuilt into LDS);
+ * 32x128, 32x256, 256x256 with eight waves, and 512x128 with x in registers
+ * (batch rows x columns; weights rebuilt into LDS once per block, so the
+ * 512-row tile rebuilds each weight once per 512 batch rows);
  * count-1, count = register-fed MFMA with two or four 16-row weight tiles per
  * wave (weights rebuilt in registers; 64 batch rows per launch; stored
  * [N][K] only: UW_ERR_UNSUPPORTED for [K][N]).  split_k applies to the KN

@@ -221,7 +221,8 @@ def test_gemm_mid_batch_split(uw, synth, oracle, layout, batch):
     for p in range(4):
         y = run_pipeline(uw, m, p, x)
         check_gemm(oracle, y, x_np, w_np, layout, what=f"pipeline {p}")
-    for v, sk in ((2 + 7, 3), (2 + 4, 5)):
+    # ... and the single-rebuild 512x128 tile (x in registers), split and not
+    for v, sk in ((2 + 7, 3), (2 + 4, 5), (2 + 8, 3), (2 + 8, 1)):
         for p in (0, 3):
             y = run_pipeline(uw, m, p, x, cfg={"variant": v, "split_k": sk})
             check_gemm(oracle, y, x_np, w_np, layout, what=f"pipeline {p} variant {v} split {sk}")
