@@ -459,6 +459,12 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
     mfma_set(3, fa1, fb1);
     rest(3);
   };
+  // XREG: drain the prologue's loads here, once.  Otherwise the compiler's
+  // wait-count merge of the loop entry (where the last loads issued are the
+  // ones the first step's rebuild reads) with the back edge (where x of the
+  // next step loads last) puts a wait for every load in flight at the top of
+  // each step, which exposes the x reloads' full latency once per step.
+  if constexpr (XREG) __builtin_amdgcn_s_waitcnt(0);
   for (int st = 0; st < steps; ++st) {
     const bool odd = st & 1;
     body(st, odd ? xs1 : xs0, odd ? ws1 : ws0, odd ? xs0 : xs1, odd ? ws0 : ws1);
