@@ -138,7 +138,7 @@ __global__ __launch_bounds__(1024) void k_gemv_nk_pipe(GemvGroup grp, const uint
   // reads the matrix's first 16 bytes (one line) instead of a whole step
   auto load_chunks = [&](ChunkT<16>* d, const uint32_t* f, const uint32_t* r, bool live) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) chunk_load<FMT, 16>(w, live ? el_of(cl, u) : 0u, live ? f[u] : 0u, r[u], d[u]);
+    for (int u = 0; u < U; ++u) chunk_load<FMT, 16, true>(w, live ? el_of(cl, u) : 0u, live ? f[u] : 0u, r[u], d[u]);
     next(cl, li);
   };
 
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NB <= 4 ? 4
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) chunk_load<FMT, OW>(w, el_of(row_of(j, u, h)), f[u][h], r[u][h], d[u][h]);
+      for (int h = 0; h < 2; ++h) chunk_load<FMT, OW, true>(w, el_of(row_of(j, u, h)), f[u][h], r[u][h], d[u][h]);
   };
 
   // The steady-state loop issues the same loads on every path, so the

@@ -145,33 +145,38 @@ struct ChunkT {
   uint32_t b[OW / 4];   // exp: OW exponent bytes | pal: 2*OW index nibbles or OW verbatim exponent bytes
 };
 
-template <int OW>
+// NT: a streaming (non-temporal) load, for weight data read once per call
+template <int OW, bool NT = false>
 __device__ __forceinline__ void load_words(const void* p, uint32_t* d) {   // OW / 4 dwords
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
   if constexpr (OW == 16) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const u32x4_t v = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p))
+                         : *reinterpret_cast<const u32x4_t*>(p);
     d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
   } else {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    const u32x2_t v = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p))
+                         : *reinterpret_cast<const u32x2_t*>(p);
     d[0] = v.x; d[1] = v.y;
   }
 }
 
 __device__ __forceinline__ uint32_t flag_index(uint64_t el) { return (uint32_t)(el >> 11); }
 
-template <int FMT, int OW>
+template <int FMT, int OW, bool NT = false>
 __device__ __forceinline__ void chunk_load(const WeightView& w, uint64_t el, uint32_t fw, uint32_t rw, ChunkT<OW>& c) {
   if constexpr (FMT == kFmtBf16) {
-    load_words<OW>(w.bf16 + el, c.a);
-    load_words<OW>(w.bf16 + el + OW / 2, c.a + OW / 4);
+    load_words<OW, NT>(w.bf16 + el, c.a);
+    load_words<OW, NT>(w.bf16 + el + OW / 2, c.a + OW / 4);
   } else if constexpr (FMT == kFmtExp) {
-    load_words<OW>(w.sm + el, c.a);
-    load_words<OW>(w.ex + el, c.b);
+    load_words<OW, NT>(w.sm + el, c.a);
+    load_words<OW, NT>(w.ex + el, c.b);
   } else {
-    load_words<OW>(w.sm + el, c.a);
+    load_words<OW, NT>(w.sm + el, c.a);
     const uint64_t g = el >> 6;
     const uint8_t* p = group_verbatim(fw, g) ? w.vexp + (uint64_t)group_rank(fw, rw, g) * 64 + (el & 63)
                                              : w.pidx + ((el >> 1) & ~(uint64_t)(OW - 1));
-    load_words<OW>(p, c.b);
+    load_words<OW, NT>(p, c.b);
   }
 }
 

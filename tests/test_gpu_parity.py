@@ -204,6 +204,29 @@ def RF_FIRST(uw):
     return uw.variant_count() - 1
 
 
+# the small tiles (64x128, 32x128, 32x256) over K slices of 1, 2, 5 and an
+# odd or even number of steps, forced K splits that leave uneven slices,
+# both layouts, a ragged batch (and a ragged N where the layout allows it:
+# stored [K][N] keeps N a multiple of 64)
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("k", [64, 128, 320, 2112])
+def test_gemm_small_tiles_step_counts(uw, synth, oracle, layout, k):
+    n, batch = (328 if layout == 0 else 320), 45
+    r, c = (n, k) if layout == 0 else (k, n)
+    say(f"gemm small tiles layout={layout} k={k}")
+    w = synth.weights(r, c, 0.02, 0.01, 10, seed=501 + k + layout).to(DEV)
+    x = synth.activations(batch, k, seed=502 + k).to(DEV)
+    m = gpu_compress(uw, w, n, k, layout)
+    uw.uw_transcode_palette(m, None)
+    w_np, x_np = bits(w), bits(x)
+    splits = (1, 3, 7) if k == 2112 else (1,)
+    for v in (2 + 0, 2 + 5, 2 + 6):
+        for sk in splits:
+            for p in (0, 1, 3):
+                y = run_pipeline(uw, m, p, x, cfg={"variant": v, "split_k": sk})
+                check_gemm(oracle, y, x_np, w_np, layout, what=f"pipeline {p} variant {v} split {sk}")
+
+
 # mid batch: the default 256x256 tiles with K split across blocks (33 K
 # steps, so slices are uneven), ragged N and batch tiles, both layouts, all
 # pipelines; then the four- and eight-wave tiles with forced odd splits
