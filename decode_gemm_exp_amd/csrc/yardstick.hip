@@ -1,8 +1,9 @@
 // yardstick.hip -- the achievable rates of the device, measured with this
 // library's own kernels so the codec and GEMM figures can be read against
 // them as well as against the published peaks:
-//   * a streaming copy and a streaming read of HBM (16-byte vector accesses,
-//     four in flight per thread, a grid-stride loop over every CU);
+//   * a streaming copy and a streaming read of HBM (each block a contiguous
+//     span, 16-byte non-temporal vector accesses, four in flight per thread,
+//     eight blocks per CU);
 //   * an MFMA-only loop: v_mfma_f32_32x32x16_bf16 on register operands, four
 //     independent accumulators per wave, two waves per SIMD on every CU, no
 //     memory traffic.
@@ -21,33 +22,56 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int kThreads = 256;
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Each block streams its own contiguous span, 16-byte vector accesses, four
+// in flight per thread, non-temporal (read once, written once).  Of the read
+// patterns measured on MI355X this one reads fastest: 6.7-6.8 TB/s on 1 GiB,
+// against 6.0 for the same spans with cached loads and 5.2 for a grid-stride
+// loop over the whole buffer.
+__device__ __forceinline__ void span_of(uint64_t n16, uint64_t& b0, uint64_t& b1) {
+  const uint64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  b0 = (uint64_t)blockIdx.x * per;
+  b1 = b0 + per < n16 ? b0 + per : n16;
+  if (b0 > n16) b0 = n16;
+}
+
 __global__ __launch_bounds__(kThreads) void k_copy16(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                       uint64_t n16) {
-  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-  uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    dst[i] = a;
-    dst[i + stride] = b;
-    dst[i + 2 * stride] = c;
-    dst[i + 3 * stride] = d;
+  uint64_t b0, b1;
+  span_of(n16, b0, b1);
+  const u32x4_t* s = reinterpret_cast<const u32x4_t*>(src);
+  u32x4_t* d = reinterpret_cast<u32x4_t*>(dst);
+  uint64_t i = b0 + threadIdx.x;
+  for (; i + 3 * kThreads < b1; i += 4 * kThreads) {
+    const u32x4_t a = __builtin_nontemporal_load(s + i), b = __builtin_nontemporal_load(s + i + kThreads),
+                  c = __builtin_nontemporal_load(s + i + 2 * kThreads),
+                  e = __builtin_nontemporal_load(s + i + 3 * kThreads);
+    __builtin_nontemporal_store(a, d + i);
+    __builtin_nontemporal_store(b, d + i + kThreads);
+    __builtin_nontemporal_store(c, d + i + 2 * kThreads);
+    __builtin_nontemporal_store(e, d + i + 3 * kThreads);
   }
-  for (; i < n16; i += stride) dst[i] = src[i];
+  for (; i < b1; i += kThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
 }
 
 // Every thread folds what it read into one word and stores it, so no load can
 // be dropped; the sink is one word per thread.
 __global__ __launch_bounds__(kThreads) void k_read16(const uint4* __restrict__ src, uint64_t n16,
                                                       uint32_t* __restrict__ sink) {
-  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-  uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+  uint64_t b0, b1;
+  span_of(n16, b0, b1);
+  const u32x4_t* s = reinterpret_cast<const u32x4_t*>(src);
   uint32_t acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  uint64_t i = b0 + threadIdx.x;
+  for (; i + 3 * kThreads < b1; i += 4 * kThreads) {
+    const u32x4_t a = __builtin_nontemporal_load(s + i), b = __builtin_nontemporal_load(s + i + kThreads),
+                  c = __builtin_nontemporal_load(s + i + 2 * kThreads),
+                  e = __builtin_nontemporal_load(s + i + 3 * kThreads);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ e.x ^ e.y ^ e.z ^ e.w;
   }
-  for (; i < n16; i += stride) {
-    const uint4 a = src[i];
+  for (; i < b1; i += kThreads) {
+    const u32x4_t a = __builtin_nontemporal_load(s + i);
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   sink[(uint64_t)blockIdx.x * kThreads + threadIdx.x] = acc;
