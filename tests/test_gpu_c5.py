@@ -6,9 +6,10 @@
   GPU transcode equals the oracle's.
 * Sequence: all 80 layers resident with both forms, the autotuner's choices
   loaded into the tuning table, one uw_run_sequence pass over the 240 matrices
-  with UW_PIPE_AUTO jobs at 1, 64 and 1024 rows, every job with its own
-  output; each output checked on 64 sampled columns against the oracle's fp64
-  GEMM on the original weights (|y - y_ref| <= 2^-10 sum|x w|).
+  with UW_PIPE_AUTO jobs at 1, 8, 64, 256, 512 and 1024 rows (the GEMVs, the
+  register-fed kernel, the LDS tiles and the single-rebuild tile), every job
+  with its own output; each output checked on 64 sampled columns against the
+  oracle's fp64 GEMM on the original weights (|y - y_ref| <= 2^-10 sum|x w|).
 """
 import concurrent.futures as cf
 import os
@@ -114,7 +115,7 @@ def test_c5_tuned_sequence_all_layers(uw, synth, oracle):
             del w
     torch.cuda.synchronize()
     say("c5 sequence: 80 layers resident; tuning on 4 layers")
-    batches = [1, 64, 1024]
+    batches = [1, 8, 64, 256, 512, 1024]
     tuned = uw.uw_autotune(mats[:12], proj[:12], batches, max_passes=1)
     uw.uw_clear_tuning()
     uw.uw_set_tuning(tuned)
