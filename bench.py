@@ -627,10 +627,7 @@ def run_c5(args) -> int:
         nt = 0
     else:
         print(f"bench: autotune on {nt // 3} layers, batches {batches}", file=sys.stderr, flush=True)
-        out_dir = os.path.join(ROOT, "gpurun_out")
-        tuned = uw.uw_autotune(mats[:nt], proj[:nt], batches, max_passes=2,
-                               json_path=os.path.join(out_dir, "mlp70b_tuned.json") if os.path.isdir(out_dir)
-                               else None)
+        tuned = uw.uw_autotune(mats[:nt], proj[:nt], batches, max_passes=2, json_path=args.tuning_json or None)
     uw.uw_set_tuning(tuned)
     t_tune = time.perf_counter() - t_tune
 
@@ -948,9 +945,10 @@ def main() -> int:
                     help="mlp70b: both forms in every layer, or alternating easy (palette indices) and hard "
                          "(Huffman stream) layers")
     ap.add_argument("--probe", default="", help="counter run: stage,projection,batch,pipeline,variant,split")
+    ap.add_argument("--tuning-json", default="", help="mlp70b: also write the autotuner's choices to this file")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; the path shards per matrix "
+        print(json.dumps({"error": "this benchmark measures one GPU only; the path shards per matrix "
                                    "(see the design notes) but no multi-GPU run is made", "n_gpus": args.gpus}))
         return 2
     if args.probe:
