@@ -369,8 +369,9 @@ def yardsticks(uw, torch, dev, copy_mib: int = 1024, reps: int = 5):
     out["copy_frac_of_spec"] = round(out["copy_gbs"] / HBM_PEAK_GBS, 4)
     out["read_frac_of_spec"] = round(out["read_gbs"] / HBM_PEAK_GBS, 4)
     out["mfma_frac_of_spec"] = round(out["mfma_bf16_tflops"] / BF16_PEAK_TFLOPS, 4)
-    out["how"] = (f"uw_yardstick: copy and read of {copy_mib} MiB (each block a contiguous span, 16-byte non-temporal accesses, 8 blocks per CU), "
-                  f"MFMA loop of {iters} x 4 v_mfma_f32_32x32x16_bf16 per wave; median of {reps}")
+    out["how"] = (f"uw_yardstick: copy and read of {copy_mib} MiB (each block a contiguous span, 16-byte "
+                  f"non-temporal accesses, 8 blocks per CU), MFMA loop of {iters} x 4 "
+                  f"v_mfma_f32_32x32x16_bf16 per wave; median of {reps}")
     return out
 
 
