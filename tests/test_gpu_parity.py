@@ -117,7 +117,7 @@ def test_codec_run_palette(uw, synth, oracle, shape, sg):
     exponents, which the decoders look up with a bytewise add."""
     r, c = shape
     say(f"codec run palette shape={shape} sg={sg}")
-    w = synth.weights(r, c, 0.02, 0.0, 0, seed=5 + r).to(DEV)
+    w = run_palette_weights(synth, r, c, 5 + r).to(DEV)
     m, _ = check_codec(uw, oracle, w, r, c, 0, sg)
     assert _palette_is_run(m)
 
@@ -300,6 +300,17 @@ def _palette_is_run(m):
     return pal[-1] - pal[0] == info.palette_size - 1
 
 
+def run_palette_weights(synth, r, c, seed):
+    """N(0, 0.02) weights with magnitudes below 2^-12 raised to it: every
+    exponent lies in one window narrower than the palette, so the palette is
+    a run by construction (drawn values alone leave a few rare small
+    exponents whose sampled counts can put a gap into the top 16)."""
+    f = synth.weights(r, c, 0.02, 0.0, 0, seed=seed).float()
+    small = f.abs() < 2.0 ** -12
+    f = torch.where(small, torch.where(f < 0, -(2.0 ** -12), 2.0 ** -12), f)
+    return f.to(torch.bfloat16)
+
+
 # stored shapes for the vector (small-batch) kernels: NK rows with K a multiple
 # of 4096 / 2048 / 1024 (the pipelined kernel, U = 4 / 2 / 1), an NK shape it
 # does not cover, and KN shapes with several K slices, odd row-pair counts and
@@ -315,7 +326,8 @@ def _palette_is_run(m):
 def test_gemv_shapes(uw, synth, oracle, n, k, layout, outliers):
     r, c = (n, k) if layout == 0 else (k, n)
     say(f"gemv shapes n={n} k={k} layout={layout} outliers={outliers}")
-    w = synth.weights(r, c, 0.02, outliers, 10, seed=n + k).to(DEV)
+    w = (run_palette_weights(synth, r, c, n + k) if outliers == 0.0
+         else synth.weights(r, c, 0.02, outliers, 10, seed=n + k)).to(DEV)
     m = gpu_compress(uw, w, n, k, layout)
     uw.uw_transcode_palette(m, None)
     assert _palette_is_run(m) == (outliers == 0.0)
@@ -349,7 +361,8 @@ def test_grouped_matmul(uw, synth, oracle):
     ms, wnps = [], []
     for i, (n, layout, out) in enumerate(specs):
         r, c = (n, k) if layout == 0 else (k, n)
-        w = synth.weights(r, c, 0.02, out, 10, seed=300 + i).to(DEV)
+        w = (run_palette_weights(synth, r, c, 300 + i) if out == 0.0
+             else synth.weights(r, c, 0.02, out, 10, seed=300 + i)).to(DEV)
         m = gpu_compress(uw, w, n, k, layout)
         uw.uw_transcode_palette(m, None)
         ms.append(m)
