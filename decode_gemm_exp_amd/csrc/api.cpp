@@ -327,6 +327,41 @@ int plan_group_pipeline(const uw_matrix* const* ms, int count, int p, int64_t ba
   return all_pidx ? UW_PIPE_PALETTE_DIRECT : UW_PIPE_EXPONENT;
 }
 
+// What a grouped call runs.  The group's own tuning entry (its matrix count,
+// total N, K, layout and residency) decides first: its pipeline for AUTO when
+// every matrix can run it, and its kernel configuration when the caller gives
+// none and the call's pipeline is the entry's.  Without one, AUTO takes
+// plan_group_pipeline and cfg == NULL the grouped kernels' defaults.
+Plan plan_group(const uw_matrix* const* ms, int count, int p, int64_t batch, const uw_kernel_cfg* cfg) {
+  Plan r;
+  uw_tune_entry e;
+  bool tuned = count >= 2 && count <= kTuneGroupMax && batch > 0;
+  uint64_t ntot = 0;
+  for (int i = 0; i < count && tuned; ++i) {
+    const uw_matrix* m = ms[i];
+    tuned = !m->fp8 && m->layout == ms[0]->layout && logical_k(m) == logical_k(ms[0]) &&
+            residency_of(m) == residency_of(ms[0]);
+    ntot += logical_n(m);
+  }
+  tuned = tuned && tuned_lookup(ntot, logical_k(ms[0]), (int)ms[0]->layout, residency_of(ms[0]), batch, &e, count);
+  for (int i = 0; i < count && tuned; ++i) tuned = pipeline_feasible(ms[i], e.pipeline);
+  if (p == UW_PIPE_AUTO)
+    r.p = tuned ? e.pipeline : plan_group_pipeline(ms, count, p, batch);
+  else
+    r.p = p;
+  if (cfg) {
+    r.cfg = *cfg;
+    r.has_cfg = true;
+  } else if (tuned && e.pipeline == r.p) {
+    r.cfg.variant = e.variant;
+    r.cfg.split_k = e.split_k;
+    r.cfg.decode_cus = e.decode_cus;
+    r.cfg.reserved = 0;
+    r.has_cfg = true;
+  }
+  return r;
+}
+
 uw_status check_matmul_args(const uw_matrix* m, int p, const uint16_t* x, int64_t batch, const float* y) {
   if (!m || !x || !y || batch <= 0) return UW_ERR_INVALID;
   if (m->fp8) return UW_ERR_UNSUPPORTED;   // the GEMMs rebuild BF16 weights
@@ -899,20 +934,22 @@ uw_status uw_workspace_size_grouped(const uw_matrix* const* ms, int count, uw_pi
     if (!ms[i]) return UW_ERR_INVALID;
     if (ms[i]->fp8) return UW_ERR_UNSUPPORTED;
   }
-  const int rp = plan_group_pipeline(ms, count, p, batch);
+  const Plan gp = plan_group(ms, count, p, batch, cfg);
   size_t prep = 0, tp = 0;
-  return grouped_need(ms, count, rp, batch, cfg, bytes, &prep, &tp);
+  return grouped_need(ms, count, gp.p, batch, gp.cfgp(), bytes, &prep, &tp);
 }
 
 uw_status uw_matmul_reconstruct_grouped(const uw_matrix* const* ms, int count, uw_pipeline p,
                                         const uint16_t* x_dev, int64_t batch, float* y_dev, void* ws_dev,
-                                        size_t ws_bytes, const uw_kernel_cfg* cfg, void* stream) {
+                                        size_t ws_bytes, const uw_kernel_cfg* cfg_in, void* stream) {
   if (!ms || count <= 0 || !pipeline_arg(p) || batch <= 0) return UW_ERR_INVALID;
   for (int i = 0; i < count; ++i) {
     if (!ms[i]) return UW_ERR_INVALID;
     if (ms[i]->fp8) return UW_ERR_UNSUPPORTED;
   }
-  const int rp = plan_group_pipeline(ms, count, p, batch);
+  const Plan gp = plan_group(ms, count, p, batch, cfg_in);
+  const int rp = gp.p;
+  const uw_kernel_cfg* cfg = gp.cfgp();
   UW_CHECK(check_group_args(ms, count, rp, x_dev, batch, y_dev));
   uint64_t total_n = 0;
   for (int i = 0; i < count; ++i) total_n += logical_n(ms[i]);

@@ -355,3 +355,187 @@ extern "C" uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj
   }
   return result;
 }
+
+// Grouped calls (gate+up, q+k+v): one choice for the whole call, measured on
+// uw_matmul_reconstruct_grouped itself, since a group runs kernels of its own
+// (the grouped GEMV and the grouped LDS tile, which split K over the group's
+// tiles together) whose best configuration is not either matrix's.  No
+// coordinate descent: the call has one choice, so every candidate is timed.
+extern "C" uw_status uw_autotune_grouped(const uw_matrix* const* ms, int group, int ngroups,
+                                         const int64_t* batches, int nb, const char* json_path,
+                                         uw_tune_entry* out, void* stream) {
+  if (!ms || group < 2 || group > uw::kTuneGroupMax || ngroups <= 0 || !batches || nb <= 0) return UW_ERR_INVALID;
+  const int count = group * ngroups;
+  for (int i = 0; i < count; ++i) {
+    if (!ms[i]) return UW_ERR_INVALID;
+    if (ms[i]->fp8) return UW_ERR_UNSUPPORTED;
+  }
+  // one table key per group: its matrices share K, layout and residency, and
+  // every group matches the first matrix for matrix
+  for (int i = 0; i < count; ++i) {
+    const uw_matrix* a = ms[i % group];
+    const uw_matrix* b = ms[i];
+    const uw_matrix* g0 = ms[0];
+    if (a->rows != b->rows || a->cols != b->cols || a->layout != b->layout ||
+        uw::residency_of(a) != uw::residency_of(b) || b->layout != g0->layout ||
+        uw::residency_of(b) != uw::residency_of(g0))
+      return UW_ERR_INVALID;
+  }
+  uw_info inf;
+  uint64_t k = 0, ntot = 0;
+  for (int i = 0; i < group; ++i) {
+    uw_get_info(ms[i], &inf);
+    if (i == 0) k = inf.k;
+    if (inf.k != k) return UW_ERR_INVALID;
+    ntot += inf.n;
+  }
+  const int layout = (int)ms[0]->layout;
+  const int residency = uw::residency_of(ms[0]);
+  int64_t maxb = 0;
+  for (int b = 0; b < nb; ++b) {
+    if (batches[b] <= 0) return UW_ERR_INVALID;
+    maxb = std::max(maxb, batches[b]);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  Bufs bufs;
+  uw_status st = uw::alloc_with(bufs.a, &bufs.x, (size_t)maxb * k * 2 + 256);
+  if (st != UW_OK) return st;
+  st = uw::alloc_with(bufs.a, &bufs.y, (size_t)maxb * ntot * 4 + 256);
+  if (st != UW_OK) return st;
+  {
+    const std::vector<uint16_t> xh = normal_bf16((size_t)maxb * k, 0x5555000000000003ull);
+    if (hipMemcpyAsync(bufs.x, xh.data(), xh.size() * 2, hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return UW_ERR_DEVICE;
+  }
+  if (hipEventCreate(&bufs.e0) != hipSuccess || hipEventCreate(&bufs.e1) != hipSuccess) return UW_ERR_DEVICE;
+  FILE* jf = nullptr;
+  if (json_path) {
+    jf = bufs.json = std::fopen(json_path, "w");
+    if (!jf) return UW_ERR_INVALID;
+    std::fprintf(jf, "{\n  \"entries\": [\n");
+  }
+
+  // one pass of grouped calls over the groups under a choice (microseconds);
+  // UW_ERR_UNSUPPORTED when the choice cannot run
+  auto measure = [&](const Choice& c, int64_t batch, double* us) -> uw_status {
+    uw_kernel_cfg cfg;
+    cfg.variant = c.variant;
+    cfg.split_k = c.split_k;
+    cfg.decode_cus = c.decode_cus;
+    cfg.reserved = 0;
+    size_t need = 0;
+    uw_status r = uw_workspace_size_grouped(ms, group, (uw_pipeline)c.pipeline, batch, &cfg, &need);
+    if (r != UW_OK) return r;
+    if (need > bufs.ws_bytes) {
+      uw::free_with(bufs.a, bufs.ws);
+      bufs.ws = nullptr;
+      bufs.ws_bytes = 0;
+      r = uw::alloc_with(bufs.a, &bufs.ws, need);
+      if (r != UW_OK) return r;
+      bufs.ws_bytes = need;
+    }
+    double t[3];
+    for (int rep = -1; rep < 3; ++rep) {
+      if (hipEventRecord(bufs.e0, s) != hipSuccess) return UW_ERR_DEVICE;
+      for (int g = 0; g < ngroups; ++g) {
+        r = uw_matmul_reconstruct_grouped(ms + (size_t)g * group, group, (uw_pipeline)c.pipeline,
+                                          static_cast<const uint16_t*>(bufs.x), batch, static_cast<float*>(bufs.y),
+                                          bufs.ws, bufs.ws_bytes, &cfg, stream);
+        if (r != UW_OK) return r;
+      }
+      if (hipEventRecord(bufs.e1, s) != hipSuccess || hipEventSynchronize(bufs.e1) != hipSuccess)
+        return UW_ERR_DEVICE;
+      float ms_ = 0.f;
+      if (hipEventElapsedTime(&ms_, bufs.e0, bufs.e1) != hipSuccess) return UW_ERR_DEVICE;
+      if (rep >= 0) t[rep] = 1e3 * (double)ms_;
+    }
+    std::sort(t, t + 3);
+    *us = t[1];
+    return UW_OK;
+  };
+
+  const int nvar = uw_variant_count();
+  const int rf = uw::rf_first_variant();
+  bool first_entry = true;
+  for (int bi = 0; bi < nb; ++bi) {
+    const int64_t batch = batches[bi];
+    std::vector<Choice> cands;
+    for (int pl = UW_PIPE_FULL; pl <= UW_PIPE_PALETTE_DIRECT; ++pl) {
+      bool ok = true;
+      for (int i = 0; i < group; ++i) ok = ok && feasible(ms[i], pl);
+      if (!ok) continue;
+      for (int v = 0; v <= nvar; ++v) {
+        if (v > 0 && !uw::gemm_variant_supported(v, layout)) continue;
+        int bm = 0, bn = 0;
+        if (v > 1 && v < rf) uw::mfma2_tile_dims(v - 2, &bm, &bn);
+        if (v == 1 && batch > 32) continue;                     // the same filters as uw_autotune
+        if (bm > 32 && batch < 8) continue;
+        if (bm == 32 && (batch < 2 || batch > 128)) continue;
+        if (bm == 512 && batch < 256) continue;
+        if (v >= rf && (layout != 0 || batch > 2 * uw::mfma_rf_max_batch())) continue;
+        Choice c;
+        c.pipeline = pl;
+        c.variant = v;
+        cands.push_back(c);
+      }
+    }
+    Choice best_c;
+    double best = -1;
+    for (const Choice& c : cands) {
+      double t = 0;
+      st = measure(c, batch, &t);
+      if (st == UW_ERR_UNSUPPORTED) continue;
+      if (st != UW_OK) return st;
+      if (best < 0 || t < best * 0.99) {
+        best = t;
+        best_c = c;
+      }
+    }
+    if (best < 0) return UW_ERR_UNSUPPORTED;
+    // the K split of the fastest (0 = the library's rule, 1 = none)
+    const Choice base = best_c;
+    for (int sk : {1, 2, 4, 8}) {
+      Choice c = base;
+      c.split_k = sk;
+      double t = 0;
+      st = measure(c, batch, &t);
+      if (st == UW_ERR_UNSUPPORTED) continue;
+      if (st != UW_OK) return st;
+      if (t < best * 0.99) {
+        best = t;
+        best_c = c;
+      }
+    }
+    uw_tune_entry e;
+    std::memset(&e, 0, sizeof(e));
+    e.batch = batch;
+    e.projection = 0;
+    e.pipeline = best_c.pipeline;
+    e.variant = best_c.variant;
+    e.split_k = best_c.split_k;
+    e.decode_cus = 0;
+    e.layout = layout;
+    e.residency = residency;
+    e.group = group;
+    e.n = ntot;
+    e.k = k;
+    e.sequence_us = best;
+    if (out) out[bi] = e;
+    if (jf) {
+      std::fprintf(jf, "%s    {\"batch\": %lld, \"projection\": 0, \"group\": %d, \"n\": %llu, \"k\": %llu, "
+                       "\"layout\": %d, \"residency\": %d, \"pipeline\": %d, \"variant\": %d, \"split_k\": %d, "
+                       "\"decode_cus\": 0, \"sequence_us\": %.2f}",
+                   first_entry ? "" : ",\n", (long long)batch, group, (unsigned long long)ntot,
+                   (unsigned long long)k, layout, residency, e.pipeline, e.variant, e.split_k, best);
+      first_entry = false;
+    }
+  }
+  if (jf) {
+    std::fprintf(jf, "\n  ]\n}\n");
+    bufs.json = nullptr;
+    if (std::fclose(jf) != 0) return UW_ERR_INVALID;
+  }
+  return UW_OK;
+}

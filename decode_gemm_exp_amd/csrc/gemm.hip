@@ -602,6 +602,7 @@ GemvKnFn gemv_kn_fn(int nb, uint64_t n) {
 
 constexpr int kGemvMaxBatch = 8;
 constexpr uint64_t kGroupGemvMaxWeights = 96ull << 20;   // see launch_gemm_group
+constexpr uint64_t kGroupTile32MaxWeights = 128ull << 20;   // see group_takes_tile32
 constexpr size_t kNkLdsMax = 160 * 1024;
 
 
@@ -817,6 +818,27 @@ void describe_gemm(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg,
                   bn, wgm, out->waves);
 }
 
+// From 8 to 32 rows a group of stored [N][K] matrices of at most 128 M
+// weights runs as one launch of 32x128 LDS tiles over the whole group
+// (unless a variant is forced).  Alone, each matrix would take the grouped
+// GEMV (8 rows) or the register-fed kernel, launched once per matrix, and
+// small matrices leave most of the chip idle in those launches.  Direct
+// palette, default vs the 32-row group tile: 8B q+k+v at 8 / 16 / 32 rows
+// 18.3 / 39.0 / 42.2 -> 16.6 / 17.0 / 18.1 us; 70B q+k+v 48.7 / 61.3 / 67.2
+// -> 43.9 / 44.9 / 47.5 us; 8B gate+up 65.1 / 69.8 / 78.1 -> 55.6 / 57.4 /
+// ~56 us.  The 70B gate+up pair (470 M weights) fills the chip matrix by
+// matrix and gains nothing at 8 and 16 rows.  At 4 rows the grouped GEMV
+// stays faster.
+static bool group_takes_tile32(const WeightView* ws, int count, int64_t batch, const uw_kernel_cfg* cfg) {
+  if (count < 2 || count > kMfma2GroupMax || batch < 8 || batch > 32 || (cfg && cfg->variant > 0)) return false;
+  uint64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    if (ws[i].layout != 0 || ws[i].k != ws[0].k) return false;
+    total += ws[i].n * ws[i].k;
+  }
+  return total <= kGroupTile32MaxWeights;
+}
+
 // One launch for a group of stored [N][K] matrices with the same K and x
 // whose calls resolve to the VALU GEMV: output columns col0s[i] .. of y.
 // hipErrorNotSupported when the group does not qualify (the caller then
@@ -825,6 +847,7 @@ void describe_gemm(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg,
 hipError_t launch_gemm_group(const WeightView* ws, int count, const uint16_t* x, int64_t batch, float* y,
                              int64_t ldy, const int64_t* col0s, const uw_kernel_cfg* cfg, hipStream_t s) {
   if (count < 2 || count > kGemvGroupMax || batch <= 0) return hipErrorNotSupported;
+  if (group_takes_tile32(ws, count, batch, cfg)) return hipErrorNotSupported;
   const bool pal = fmt_is_pal(ws[0].fmt);
   // Up to 8 rows a group of small matrices takes the grouped GEMV even where
   // each matrix alone would take the register-fed kernel: one launch instead
@@ -926,6 +949,7 @@ static int tile_group_plan(const WeightView* ws, int count, int64_t batch, const
     ntot += ws[i].n;
   }
   wide.n = ntot;
+  if (group_takes_tile32(ws, count, batch, cfg)) return 5;   // the 32x128 tile
   const int v = resolve_variant(wide, batch, cfg);
   return v >= 2 && v < rf_first_variant() ? v - 2 : -1;
 }

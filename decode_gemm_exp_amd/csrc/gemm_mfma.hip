@@ -560,14 +560,16 @@ int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint) {
   const int64_t blocks = ((int64_t)w.n + t.bn - 1) / t.bn * ((batch + t.bm - 1) / t.bm);
   const int64_t cus = (int64_t)device_cus();
   const int64_t target = batch <= 64 ? (fmt_is_pal(w.fmt) ? 512 : 256) : t.bm >= 256 ? (cus * 7 + 7) / 8 : 256;
-  // up to 64 rows, and for 256-row tiles up to 512 rows, never past the
-  // blocks the CUs hold at once (a second round of blocks runs on a mostly
-  // idle chip: 8B gate, palette-direct, 64 rows, 64x128 tiles: 4 slices
-  // 40.6 us, 8 slices 47.7 us; 70B q+k+v grouped, 40 256x256 tiles at 192
-  // rows: 4 slices 90 us, 8 slices 107 us; 8B q+k+v, 48 tiles at 384 rows:
-  // 4 slices 52 us, 8 slices 66 us)
+  // up to 64 rows, and for tiles of 256 rows and more at any batch, never
+  // past the blocks the CUs hold at once (a second round of blocks runs on
+  // a mostly idle chip: 8B gate, palette-direct, 64 rows, 64x128 tiles: 4
+  // slices 40.6 us, 8 slices 47.7 us; 70B q+k+v grouped, 40 256x256 tiles
+  // at 192 rows: 4 slices 90 us, 8 slices 107 us; 8B q+k+v, 48 tiles at 384
+  // rows: 4 slices 52 us, 8 slices 66 us; at 1024 rows with 512x128 tiles,
+  // 8B q+k+v 96 tiles: 4 slices 91 us, 2 slices 71 us; 70B q+k+v 160 tiles:
+  // 2 slices 239 us, none 198 us)
   const int64_t per_cu = mfma2_blocks_per_cu((int)w.layout, t);
-  const bool one_round = batch <= 64 || (t.bm >= 256 && batch <= 512);
+  const bool one_round = batch <= 64 || t.bm >= 256;
   const int64_t hold = one_round ? cus * (per_cu > 0 ? per_cu : 1) : INT64_MAX;
   int s = split_hint > 0 ? split_hint : 1;
   if (split_hint <= 0)

@@ -86,7 +86,7 @@ std::vector<uint32_t> cu_mask(int total, int first, int count) {
 }
 
 // ---- tuned choices ---------------------------------------------------------------------
-using TuneKey = std::tuple<uint64_t, uint64_t, int32_t, int32_t>;   // n, k, layout, residency
+using TuneKey = std::tuple<uint64_t, uint64_t, int32_t, int32_t, int32_t>;   // n, k, layout, residency, group
 std::mutex g_tune_mu;
 std::map<TuneKey, std::vector<uw_tune_entry>> g_tune;
 
@@ -94,11 +94,12 @@ bool entry_valid(const uw_tune_entry& e) {
   return e.batch > 0 && e.n > 0 && e.k > 0 && (e.layout == 0 || e.layout == 1) && e.residency >= 1 &&
          e.residency <= 3 && e.pipeline >= UW_PIPE_FULL && e.pipeline <= UW_PIPE_PALETTE_DIRECT &&
          e.variant >= 0 && e.variant <= gemm_variant_count() && e.split_k >= 0 && e.decode_cus >= 0 &&
+         (e.group == 0 || (e.group >= 2 && e.group <= kTuneGroupMax)) &&
          gemm_variant_supported(e.variant <= 0 ? 1 : e.variant, e.layout);
 }
 
 void add_locked(const uw_tune_entry& e) {
-  auto& v = g_tune[TuneKey{e.n, e.k, e.layout, e.residency}];
+  auto& v = g_tune[TuneKey{e.n, e.k, e.layout, e.residency, e.group}];
   for (auto& old : v)
     if (old.batch == e.batch) {
       old = e;
@@ -231,9 +232,10 @@ uw_status pooled_events(size_t count, hipEvent_t** out) {
 
 int residency_of(const uw_matrix* m) { return (m->stream ? 1 : 0) | (m->pidx ? 2 : 0); }
 
-bool tuned_lookup(uint64_t n, uint64_t k, int layout, int residency, int64_t batch, uw_tune_entry* out) {
+bool tuned_lookup(uint64_t n, uint64_t k, int layout, int residency, int64_t batch, uw_tune_entry* out,
+                  int group) {
   std::lock_guard<std::mutex> lk(g_tune_mu);
-  auto it = g_tune.find(TuneKey{n, k, layout, residency});
+  auto it = g_tune.find(TuneKey{n, k, layout, residency, group});
   if (it == g_tune.end() || it->second.empty() || batch <= 0) return false;
   // the tuned batch nearest on a log scale; ties go to the smaller batch
   const double lb = std::log2((double)batch);
@@ -328,6 +330,11 @@ uw_status uw_load_tuning(const char* json_path) try {
     e.variant = (int32_t)v[7];
     e.split_k = (int32_t)v[8];
     e.decode_cus = (int32_t)v[9];
+    long long g = 0;
+    if (json_int(obj, "group", &g)) {   // absent: an entry for calls on one matrix
+      if (g < 0 || g > kTuneGroupMax) return UW_ERR_CORRUPT;
+      e.group = (int32_t)g;
+    }
     double us = 0;
     if (json_double(obj, "sequence_us", &us)) e.sequence_us = us;
     if (!entry_valid(e)) return UW_ERR_CORRUPT;
@@ -345,6 +352,14 @@ uw_status uw_lookup_tuning(uint64_t n, uint64_t k, int32_t layout, int32_t resid
                            uw_tune_entry* out) {
   if (!out || batch <= 0 || (layout != 0 && layout != 1) || residency < 1 || residency > 3) return UW_ERR_INVALID;
   return tuned_lookup(n, k, layout, residency, batch, out) ? UW_OK : UW_ERR_STATE;
+}
+
+uw_status uw_lookup_tuning_grouped(uint64_t n, uint64_t k, int32_t layout, int32_t residency, int32_t group,
+                                   int64_t batch, uw_tune_entry* out) {
+  if (!out || batch <= 0 || (layout != 0 && layout != 1) || residency < 1 || residency > 3 || group < 2 ||
+      group > kTuneGroupMax)
+    return UW_ERR_INVALID;
+  return tuned_lookup(n, k, layout, residency, batch, out, group) ? UW_OK : UW_ERR_STATE;
 }
 
 }  // extern "C"

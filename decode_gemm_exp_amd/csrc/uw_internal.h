@@ -99,9 +99,12 @@ uw_status matmul_stage_into(const uw_matrix* m, int p, const void* prep, const u
                             void* part, size_t part_bytes, const uw_kernel_cfg* cfg, hipStream_t s, size_t* need);
 // bit 0: Huffman stream resident, bit 1: palette indices resident
 int residency_of(const uw_matrix* m);
-// the tuned choice for a shape, residency and batch (nearest tuned batch on a
-// log scale); false when the table holds none
-bool tuned_lookup(uint64_t n, uint64_t k, int layout, int residency, int64_t batch, uw_tune_entry* out);
+// the tuned choice for a shape, residency, group (0: one matrix; g >= 2: a
+// grouped call on g matrices of total N n) and batch (nearest tuned batch on
+// a log scale); false when the table holds none
+bool tuned_lookup(uint64_t n, uint64_t k, int layout, int residency, int64_t batch, uw_tune_entry* out,
+                  int group = 0);
+constexpr int kTuneGroupMax = 64;
 
 // Raise a kernel's dynamic LDS limit to `bytes` on the current device, once
 // per (kernel, device, size); thread safe (api.cpp).

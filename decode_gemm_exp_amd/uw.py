@@ -64,7 +64,7 @@ class uw_info(ctypes.Structure):
 class uw_tune_entry(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("projection", ctypes.c_int32), ("pipeline", ctypes.c_int32),
                 ("variant", ctypes.c_int32), ("split_k", ctypes.c_int32), ("decode_cus", ctypes.c_int32),
-                ("layout", ctypes.c_int32), ("residency", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("layout", ctypes.c_int32), ("residency", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("n", ctypes.c_uint64), ("k", ctypes.c_uint64), ("sequence_us", ctypes.c_double)]
 
 
@@ -120,6 +120,9 @@ _SIGS = {
     "uw_autotune": (ctypes.c_int, [ctypes.POINTER(_vp), ctypes.POINTER(ctypes.c_int32), ctypes.c_int, ctypes.c_int,
                                    ctypes.POINTER(ctypes.c_int64), ctypes.c_int, ctypes.c_int, ctypes.c_char_p,
                                    ctypes.POINTER(uw_tune_entry), _vp]),
+    "uw_autotune_grouped": (ctypes.c_int, [ctypes.POINTER(_vp), ctypes.c_int, ctypes.c_int,
+                                           ctypes.POINTER(ctypes.c_int64), ctypes.c_int, ctypes.c_char_p,
+                                           ctypes.POINTER(uw_tune_entry), _vp]),
     "uw_drop_palette": (ctypes.c_int, [_vp, _vp]),
     "uw_workspace_size_cfg": (ctypes.c_int, [_vp, ctypes.c_int, _i64, ctypes.POINTER(uw_kernel_cfg),
                                              ctypes.POINTER(_sz)]),
@@ -137,6 +140,8 @@ _SIGS = {
     "uw_clear_tuning": (ctypes.c_int, []),
     "uw_lookup_tuning": (ctypes.c_int, [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, _i64,
                                         ctypes.POINTER(uw_tune_entry)]),
+    "uw_lookup_tuning_grouped": (ctypes.c_int, [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int32, _i64, ctypes.POINTER(uw_tune_entry)]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -387,6 +392,22 @@ def uw_autotune(ms, proj, batches, max_passes: int = 3, json_path: str | None = 
     return [_entry_dict(e) for e in out]
 
 
+def uw_autotune_grouped(groups, batches, json_path: str | None = None, stream=None):
+    """groups: a list of equal-shaped groups (lists of Matrix), e.g. the gate
+    and up matrices of successive layers.  Returns one dict per batch."""
+    size = len(groups[0])
+    flat = [m for g in groups for m in g]
+    if any(len(g) != size for g in groups):
+        raise ValueError("uw_autotune_grouped: groups of different sizes")
+    arr = (ctypes.c_void_p * len(flat))(*[m.handle.value for m in flat])
+    bs = (ctypes.c_int64 * len(batches))(*batches)
+    out = (uw_tune_entry * len(batches))()
+    _check(_lib.uw_autotune_grouped(arr, size, len(groups), bs, len(batches),
+                                    json_path.encode() if json_path else None, out, _stream(stream)),
+           "uw_autotune_grouped")
+    return [_entry_dict(e) for e in out]
+
+
 def uw_plan_gemm(m: Matrix, pipeline: int, batch: int, cfg=None) -> dict:
     pl = uw_gemm_plan()
     _check(_lib.uw_plan_gemm(m.handle, pipeline, batch, _cfg(cfg), ctypes.byref(pl)), "uw_plan_gemm")
@@ -441,6 +462,15 @@ def uw_lookup_tuning(n: int, k: int, layout: int, residency: int, batch: int) ->
     if st == -6:
         return None
     _check(st, "uw_lookup_tuning")
+    return _entry_dict(e)
+
+
+def uw_lookup_tuning_grouped(n: int, k: int, layout: int, residency: int, group: int, batch: int) -> dict | None:
+    e = uw_tune_entry()
+    st = _lib.uw_lookup_tuning_grouped(n, k, layout, residency, group, batch, ctypes.byref(e))
+    if st == -6:
+        return None
+    _check(st, "uw_lookup_tuning_grouped")
     return _entry_dict(e)
 
 

@@ -289,10 +289,11 @@ uw_status uw_matmul_stage_static(const uw_matrix* m, uw_pipeline p, const void* 
  * (and q+k+v): the pages tune gate and up as separate projections that read
  * the same activations ([EVC] "四種執行管道", "自動調優機制"); here they stay
  * two compressed matrices and only x and the launches are shared.
- * UW_PIPE_AUTO takes the tuned pipeline when every matrix's entry names the
- * same one, else direct palette when every matrix has resident indices, else
- * exponent; cfg == NULL uses the grouped kernels' defaults.  Workspace: see
- * uw_workspace_size_grouped. */
+ * UW_PIPE_AUTO and cfg == NULL consult the tuning table: the group's own
+ * entry first (uw_autotune_grouped), then the matrices' entries for the
+ * pipeline (see uw_lookup_tuning_grouped); without an entry cfg == NULL uses
+ * the grouped kernels' defaults.  Workspace: see uw_workspace_size_grouped,
+ * which resolves AUTO and cfg == NULL the same way. */
 uw_status uw_matmul_reconstruct_grouped(const uw_matrix* const* ms, int count, uw_pipeline p,
                                         const uint16_t* x_dev, int64_t batch, float* y_dev,
                                         void* ws_dev, size_t ws_bytes,
@@ -365,8 +366,11 @@ uw_status uw_sequence_workspace_size(const uw_job* jobs, int count, size_t* byte
 uw_status uw_run_sequence(const uw_job* jobs, int count, int32_t decode_cus, void* ws_dev,
                           size_t ws_bytes, void* stream);
 
-/* One tuned choice: for `projection` at `batch`.  n, k, layout and residency
- * describe the projection's matrices and key the library's tuning table. */
+/* One tuned choice: for `projection` at `batch`.  n, k, layout, residency and
+ * group describe the projection's matrices and key the library's tuning
+ * table.  group 0: an entry for calls on one matrix (n its N).  group g in
+ * 2..64: an entry for grouped calls (uw_matmul_reconstruct_grouped) on g
+ * matrices that share k, layout and residency, n being their total N. */
 typedef struct {
   int64_t batch;
   int32_t projection;
@@ -377,7 +381,7 @@ typedef struct {
   int32_t layout;               /* uw_layout of the stored arrays            */
   int32_t residency;            /* bit 0: Huffman stream resident; bit 1:
                                    palette indices resident                  */
-  int32_t reserved;
+  int32_t group;                /* 0, or the matrix count of a grouped call  */
   uint64_t n, k;                /* logical W[N][K] shape                     */
   double sequence_us;           /* measured time of the whole tuned sequence at this batch */
 } uw_tune_entry;
@@ -399,21 +403,48 @@ uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj, int count
                       const int64_t* batches, int nb, int max_passes, const char* json_path,
                       uw_tune_entry* out, void* stream);
 
+/* Autotuner of grouped calls.  ms[0..group * ngroups) holds ngroups groups of
+ * `group` matrices (2..64) in call order: group j is ms[j * group ..
+ * (j + 1) * group), e.g. the gate and up matrices of successive layers.  The
+ * matrices of a group share k, layout and residency (they key one table
+ * entry), and every group matches the first matrix for matrix in shape,
+ * layout and residency (UW_ERR_INVALID otherwise; fp8 matrices:
+ * UW_ERR_UNSUPPORTED).  For each batch it measures one pass of
+ * uw_matmul_reconstruct_grouped over the groups, x drawn from N(0,1) in
+ * BF16, median of three timed passes after a warm-up, for every pipeline all
+ * matrices can run x every GEMM variant that suits the batch (variant 0, the
+ * library's rule, included), then the K split of the fastest.  Writes out[b]
+ * (may be NULL) with group = `group` and n the group's total N, and a JSON
+ * file in uw_autotune's format with a "group" field (json_path may be NULL).
+ * It does not change the library's tuning table.  Allocates its own x, y and
+ * workspace; synchronises `stream`.  ([EVC] "自動調優機制") */
+uw_status uw_autotune_grouped(const uw_matrix* const* ms, int group, int ngroups, const int64_t* batches, int nb,
+                              const char* json_path, uw_tune_entry* out, void* stream);
+
 /* The tuning table that UW_PIPE_AUTO and cfg == NULL consult, keyed by
- * (n, k, layout, residency) with one entry per tuned batch; a call at batch B
+ * (n, k, layout, residency, group) with one entry per tuned batch; a call at batch B
  * takes the entry whose batch is nearest to B on a log scale (ties: the
  * smaller batch).  uw_set_tuning adds entries (an entry with the same key
  * and batch is replaced; UW_ERR_INVALID if any entry is malformed, and then
  * none is added); uw_load_tuning adds the entries of a JSON file written by
  * uw_autotune (UW_ERR_CORRUPT if it cannot be read as one, and then none is
  * added); uw_clear_tuning empties the table; uw_lookup_tuning reports the
- * entry a call would use (UW_ERR_STATE when there is none).  Process-wide
- * and thread safe.  ([EVC] "自動調優機制") */
+ * entry a call on one matrix would use, uw_lookup_tuning_grouped the one a
+ * grouped call on `group` matrices of total N `n` would use (UW_ERR_STATE
+ * when there is none).  A grouped call with UW_PIPE_AUTO or cfg == NULL
+ * takes its group entry when there is one (the pipeline, and the kernel
+ * configuration when the call's pipeline is the entry's); without one, AUTO
+ * takes the pipeline the matrices' own entries agree on, else direct palette
+ * when every matrix has resident indices, else exponent, and cfg == NULL the
+ * library's rule.  uw_load_tuning reads a missing "group" as 0.
+ * Process-wide and thread safe.  ([EVC] "自動調優機制") */
 uw_status uw_set_tuning(const uw_tune_entry* entries, int count);
 uw_status uw_load_tuning(const char* json_path);
 uw_status uw_clear_tuning(void);
 uw_status uw_lookup_tuning(uint64_t n, uint64_t k, int32_t layout, int32_t residency, int64_t batch,
                            uw_tune_entry* out);
+uw_status uw_lookup_tuning_grouped(uint64_t n, uint64_t k, int32_t layout, int32_t residency, int32_t group,
+                                   int64_t batch, uw_tune_entry* out);
 
 /* Free resident palette indices (keeps the Huffman form).  Synchronises. */
 uw_status uw_drop_palette(uw_matrix* m, void* stream);

@@ -108,9 +108,10 @@ def test_import_rejects_empty_and_short(uw):
 # The table that UW_PIPE_AUTO and cfg == NULL consult is host state: its
 # parsing, keying and nearest-batch rule are checked here without a GPU.
 
-def _entry(uw, batch, pipeline, variant=0, split_k=0, n=28672, k=8192, layout=0, residency=3):
+def _entry(uw, batch, pipeline, variant=0, split_k=0, n=28672, k=8192, layout=0, residency=3, group=0):
     return {"batch": batch, "projection": 0, "pipeline": pipeline, "variant": variant, "split_k": split_k,
-            "decode_cus": 0, "layout": layout, "residency": residency, "n": n, "k": k, "sequence_us": 1.0}
+            "decode_cus": 0, "layout": layout, "residency": residency, "n": n, "k": k, "sequence_us": 1.0,
+            "group": group}
 
 
 def test_tuning_table_nearest_batch(uw):
@@ -153,6 +154,63 @@ def test_tuning_table_rejects_malformed_entries(uw):
     with pytest.raises(uw.UwError):
         uw.uw_set_tuning([_entry(uw, 8, 3, variant=uw.variant_count(), layout=1)])
     assert uw._lib.uw_lookup_tuning(1, 1, 0, 3, 0, None) == -1
+
+
+def test_tuning_table_group_entries_are_separate(uw):
+    """A grouped call's entry (gate+up of 8B: 2 matrices, total N 28672) is
+    keyed apart from a single matrix of the same N, and apart from groups of
+    another size; group 1, negative and beyond 64 are malformed."""
+    uw.uw_clear_tuning()
+    try:
+        uw.uw_set_tuning([_entry(uw, 64, 3, 2), _entry(uw, 64, 1, 3, group=2), _entry(uw, 64, 2, 4, group=3)])
+        assert uw.uw_lookup_tuning(28672, 8192, 0, 3, 64)["pipeline"] == 3
+        e2 = uw.uw_lookup_tuning_grouped(28672, 8192, 0, 3, 2, 64)
+        assert (e2["pipeline"], e2["variant"], e2["group"]) == (1, 3, 2)
+        assert uw.uw_lookup_tuning_grouped(28672, 8192, 0, 3, 3, 100)["pipeline"] == 2
+        assert uw.uw_lookup_tuning_grouped(28672, 8192, 0, 3, 4, 64) is None
+        assert uw.uw_lookup_tuning_grouped(28672, 8192, 1, 3, 2, 64) is None
+        for g in (1, -1, 65):
+            with pytest.raises(uw.UwError) as ei:
+                uw.uw_set_tuning([_entry(uw, 8, 3, group=g)])
+            assert ei.value.status == -1
+        for g in (0, 1, 65):
+            assert uw._lib.uw_lookup_tuning_grouped(28672, 8192, 0, 3, g, 64, ctypes.byref(uw.uw_tune_entry())) == -1
+    finally:
+        uw.uw_clear_tuning()
+
+
+def test_load_tuning_json_group_field(uw, tmp_path):
+    """uw_load_tuning reads "group" (as uw_autotune_grouped writes it) and
+    takes a missing one as 0."""
+    import json
+    uw.uw_clear_tuning()
+    single = {k: v for k, v in _entry(uw, 8, 3, 1).items() if k != "group"}
+    grouped = _entry(uw, 8, 1, 4, split_k=2, n=6144, k=4096, group=3)
+    path = tmp_path / "grouped.json"
+    path.write_text(json.dumps({"entries": [single, grouped]}))
+    try:
+        uw.uw_load_tuning(str(path))
+        assert uw.uw_lookup_tuning(28672, 8192, 0, 3, 8)["group"] == 0
+        e = uw.uw_lookup_tuning_grouped(6144, 4096, 0, 3, 3, 8)
+        assert (e["pipeline"], e["variant"], e["split_k"]) == (1, 4, 2)
+        assert uw.uw_lookup_tuning(6144, 4096, 0, 3, 8) is None
+        uw.uw_clear_tuning()
+        path.write_text(json.dumps({"entries": [dict(grouped, group=99)]}))
+        with pytest.raises(uw.UwError) as ei:
+            uw.uw_load_tuning(str(path))
+        assert ei.value.status == -5
+    finally:
+        uw.uw_clear_tuning()
+
+
+def test_autotune_grouped_host_checks(uw):
+    """Argument checks that fail before any device work."""
+    bs = (ctypes.c_int64 * 1)(8)
+    assert uw._lib.uw_autotune_grouped(None, 2, 1, bs, 1, None, None, None) == -1
+    arr = (ctypes.c_void_p * 2)(None, None)
+    assert uw._lib.uw_autotune_grouped(arr, 1, 2, bs, 1, None, None, None) == -1   # group of one
+    assert uw._lib.uw_autotune_grouped(arr, 2, 1, bs, 1, None, None, None) == -1   # NULL matrices
+    assert uw._lib.uw_autotune_grouped(arr, 2, 0, bs, 1, None, None, None) == -1
 
 
 def test_load_tuning_json(uw, tmp_path):

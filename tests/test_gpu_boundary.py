@@ -159,6 +159,64 @@ def test_sequence_auto_jobs_and_release(uw, synth, oracle, clean_table):
     uw.uw_release_resources()
 
 
+def grouped(uw, ms, pipeline, x, cfg=None):
+    n = sum(m.info().n for m in ms)
+    y = torch.full((x.shape[0], n), float("nan"), dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(16, uw.uw_workspace_size_grouped(ms, pipeline, x.shape[0], cfg)), dtype=torch.uint8,
+                     device=DEV)
+    uw.uw_matmul_reconstruct_grouped(ms, pipeline, x, y, ws, cfg=cfg)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("shape", ["qkv", "gate_up"])
+def test_grouped_auto_equals_tuned_choice(uw, synth, oracle, clean_table, tmp_path, shape):
+    """uw_autotune_grouped on two layers of the 8B q+k+v (4096, 1024, 1024 x
+    4096) or gate+up (2 x 14336 x 4096) calls, its JSON loaded: a grouped
+    AUTO call and a grouped call with cfg == NULL run exactly the tuned
+    pipeline and kernel (bit-identical to the explicit choice), each
+    matrix's columns within the fp64 bound on 48 sampled columns."""
+    k = 4096
+    ns = [4096, 1024, 1024] if shape == "qkv" else [14336, 14336]
+    say(f"boundary: grouped autotune {shape}")
+    ws_ = [[synth.weights(n, k, 0.02, 0.001, 10, seed=400 + 10 * g + i).to(DEV) for i, n in enumerate(ns)]
+           for g in range(2)]
+    ms = [[uw.uw_compress(w, n, k, 0) for w, n in zip(gw, ns)] for gw in ws_]
+    for g in ms:
+        for m in g:
+            uw.uw_transcode_palette(m, None)
+    batches = [1, 24, 300]
+    path = str(tmp_path / "grouped.json")
+    tuned = uw.uw_autotune_grouped(ms, batches, json_path=path)
+    assert len(tuned) == len(batches)
+    for b, e in zip(batches, tuned):
+        assert (e["batch"], e["n"], e["k"], e["layout"], e["residency"], e["group"]) == (b, sum(ns), k, 0, 3, len(ns))
+        say(f"  batch {b}: pipeline {e['pipeline']} variant {e['variant']} split {e['split_k']} "
+            f"{e['sequence_us']:.1f} us")
+    uw.uw_load_tuning(path)
+    rng = np.random.default_rng(17)
+    for b, e in zip(batches, tuned):
+        got = uw.uw_lookup_tuning_grouped(sum(ns), k, 0, 3, len(ns), b)
+        assert (got["pipeline"], got["variant"], got["split_k"]) == (e["pipeline"], e["variant"], e["split_k"])
+        x = synth.activations(b, k, seed=31 + b).to(DEV)
+        cfg = {"variant": e["variant"], "split_k": e["split_k"], "decode_cus": 0}
+        y_auto = grouped(uw, ms[1], uw.PIPE_AUTO, x)
+        y_tuned = grouped(uw, ms[1], e["pipeline"], x, cfg)
+        y_null = grouped(uw, ms[1], e["pipeline"], x)
+        assert np.array_equal(y_auto, y_tuned), f"batch {b}"
+        assert np.array_equal(y_null, y_tuned), f"batch {b}"
+        x_np = bits(x)
+        col = 0
+        for i, n in enumerate(ns):
+            c = np.sort(rng.choice(n, 48, replace=False))
+            w_sel = bits(ws_[1][i].index_select(0, torch.from_numpy(c).to(DEV)))
+            y_ref, A = oracle.gemm_ref(x_np, w_sel, 0)
+            ok, worst = oracle.gemm_check(y_auto[:, col + c], y_ref, A)
+            assert ok, f"batch {b} matrix {i}: worst err/bound {worst:.3g}"
+            col += n
+    uw.uw_release_resources()
+
+
 def test_allocator_hooks(uw, synth, oracle):
     """Sections, scratch and resident indices come from the hooks and go back
     through them; a NULL from the hook is UW_ERR_NOMEM."""

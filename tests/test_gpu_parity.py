@@ -349,10 +349,10 @@ def test_grouped_matmul(uw, synth, oracle):
     one launch (a run palette next to a palette with gaps runs with the
     general lookup; more than eight rows go in chunks); a group of five, a
     group holding a [K][N] matrix and batches that resolve to MFMA kernels
-    are launched one matrix at a time; at 5 to 8 rows a group of small
-    matrices takes the grouped GEMV by default; where the group's kernel is
-    an LDS tile (80 and 300 rows, a forced odd split, a [K][N]-only group)
-    the whole group is one launch.  Every column block is checked against
+    are launched one matrix at a time; at 5 to 7 rows a group of small
+    matrices takes the grouped GEMV by default, at 8 to 32 rows one launch of
+    32-row tiles; where the group's kernel is an LDS tile (80 and 300 rows,
+    a forced odd split, a [K][N]-only group) the whole group is one launch.  Every column block is checked against
     the fp64 reference."""
     say("grouped matmul")
     k = 2048
