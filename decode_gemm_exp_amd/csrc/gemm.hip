@@ -726,8 +726,13 @@ bool gemm_variant_supported(int v, int layout) { return v < rf_first_variant() |
 
 // Default kernel by batch, from sweeps over the 8B and 70B MLP shapes (every
 // variant, both layouts, palette-direct and BF16 weights):
-//   stored [N][K]: VALU GEMV up to 4 rows, register-fed MFMA (two row tiles
-//     per wave) up to 32, then LDS tiles 64x128 up to 64, 128x128 up to 128,
+//   stored [N][K]: VALU GEMV up to 4 rows, register-fed MFMA up to 32 (x
+//     shared through LDS, one row tile per wave, when its 64-row blocks
+//     cover seven eighths of the CUs: 70B gate, palette, 8 / 16 / 32 rows
+//     99.8 / 95.0 / 108.4 -> 84.6 / 83.5 / 96.7 us, 8B gate 8 / 16 rows 34.2
+//     / 36.1 -> 31.6 / 32.1 us; on narrower matrices it loses, 8B q with 64
+//     blocks at 8 rows 20.5 vs 13.2 us, and x per wave with two row tiles
+//     per wave stays), then LDS tiles 64x128 up to 64, 128x128 up to 128,
 //     the eight-wave 256x256 up to 512 (K split to fill the CUs: 70B gate at
 //     512 rows, palette-direct 466 -> 319 us, BF16 295 -> 234 us), and beyond
 //     256x256 when its tiles cover seven eighths of the CUs (8B gate at 1024
@@ -750,6 +755,8 @@ static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_c
   if (batch > 256 && ((batch + 255) / 256) % 2 == 0) return 2 + 8;
   if (w.layout == 0) {
     if (batch <= 4) return 1;
+    if (batch <= 32 && mfma_rf_supported(w, 2) && (int64_t)((w.n + 63) / 64) * 8 >= (int64_t)device_cus() * 7)
+      return rf_first_variant() + 2;
     if (batch <= 32 && mfma_rf_supported(w, 0)) return rf_first_variant();
     if (batch <= 64) return 2 + 0;
     if (batch <= 128) return 2 + 1;
@@ -795,11 +802,13 @@ void describe_gemm(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg,
   }
   if (v >= rf_first_variant()) {
     const int kind = v - rf_first_variant();
-    out->tile_n = 32 * (kind + 1);
+    const int tiles = kind == 0 ? 2 : kind == 1 ? 4 : kind == 2 ? 1 : 2;   // row tiles per wave
+    out->tile_n = 16 * tiles;                                               // rows of W per wave
     out->tile_m = 16;
     out->waves = 4;
     out->k_slices = mfma_rf_slices(w, kind, cfg ? cfg->split_k : 0, device_cus());
-    std::snprintf(out->kernel, sizeof(out->kernel), "k_mfma_rf<%d, %d, ", w.fmt, 2 * (kind + 1));
+    std::snprintf(out->kernel, sizeof(out->kernel), kind < 2 ? "k_mfma_rf<%d, %d, " : "k_mfma_rfx<%d, %d, ", w.fmt,
+                  tiles);
     return;
   }
   const int tile = v - 2;

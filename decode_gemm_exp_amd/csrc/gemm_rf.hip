@@ -36,6 +36,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWin = 128;   // k per window (32 per lane group)
 
@@ -362,6 +363,208 @@ __global__ __launch_bounds__(256) void k_rf_pack_x(const uint16_t* __restrict__ 
   }
 }
 
+// Register-fed kernel with x shared through LDS (kinds 2 and 3).  The four
+// waves of a block own different rows (wave w: R row tiles from
+// 16 R w) and walk the same windows of the block's K range together, so each
+// window's x fragments are read from memory once per block, a quarter by
+// each wave, into a double-buffered LDS stage, and every wave reads them
+// from there.  In the kernel above every wave loads its own windows' x from
+// L2: at 64 rows that is 16 KB per window per wave, more than the wave's
+// compressed weights, and with x loads taken out (a timing copy) it ran
+// 133 -> 84 us on the 70B gate, palette-direct.  One barrier per window: a
+// window's x is stored in the half step after it is read from memory and
+// read in the next, and a buffer is rewritten only after the barrier that
+// follows its last reads.  No cross-wave reduction: each wave stores its
+// own rows.  x comes packed (k_rf_pack_x), one window contiguous.
+template <int FMT, int R, int NBG, int DP>
+__global__ __launch_bounds__(256) void k_mfma_rfx(WeightView w, int B, float* __restrict__ y, int64_t ldy,
+                                                  int64_t col0, int64_t kslice, float* __restrict__ part,
+                                                  uint32_t fwords, const uint4* __restrict__ xp) {
+  static_assert(DP % 2 == 0, "x buffers alternate with the windows");
+  constexpr int XE = NBG * 4 * 64;   // uint4 entries of x per window
+  extern __shared__ u32x4 dyn4[];
+  u32x4* const xs = dyn4;                                          // two windows of x fragments
+  uint32_t* const fl = reinterpret_cast<uint32_t*>(dyn4 + 2 * XE);   // palette: flag words, then rank words
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int64_t N = (int64_t)w.n, K = (int64_t)w.k;
+  const int64_t nblk = (int64_t)blockIdx.x * (64 * R);   // the block's first row
+  const int64_t n0 = nblk + (int64_t)wave * (16 * R);    // the wave's first row
+  const int64_t kb = (int64_t)blockIdx.y * kslice;
+  const int64_t ke = kb + kslice < K ? kb + kslice : K;
+  const int nwin = (int)((ke - kb + kWin - 1) / kWin);
+
+  uint64_t fbase = 0;
+  if constexpr (fmt_is_pal(FMT)) {
+    const int64_t nl = nblk + 64 * R < N ? nblk + 64 * R : N;
+    fbase = (uint64_t)(nblk * K) >> 11;
+    const uint32_t cnt = (uint32_t)((((uint64_t)(nl * K) + 2047) >> 11) - fbase);
+    for (uint32_t i = threadIdx.x; i < cnt; i += 256) {
+      fl[i] = w.vflags[fbase + i];
+      fl[fwords + i] = w.vrank[fbase + i];
+    }
+    __syncthreads();
+  }
+
+  // blocks start their walks at different windows (reads spread over channels)
+  const int rot = nwin > 0 ? (int)((blockIdx.x * 5u + blockIdx.y * 3u) % (unsigned)nwin) : 0;
+  auto win_k = [&](int j) __attribute__((always_inline)) {
+    int jj = j + rot;
+    jj -= jj >= nwin ? nwin : 0;
+    return kb + (int64_t)kWin * jj;
+  };
+  const int goff = FMT == kFmtBf16 ? 8 * g : 16 * g;
+  auto load_flags = [&](int j, uint32_t (&fw)[R], uint32_t (&fh)[R], uint32_t (&rw)[R]) __attribute__((always_inline)) {
+    if constexpr (fmt_is_pal(FMT)) {
+      const int64_t k0 = win_k(j);
+      const bool kv = (j < nwin) & (k0 < ke);
+      const bool h1 = k0 + 64 < ke;
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        const int64_t n = n0 + 16 * t + i16;
+        const bool v = kv & (n < N);
+        const uint64_t g0 = (uint64_t)(n * K + k0) >> 6;
+        const uint32_t fi = v ? (uint32_t)((g0 >> 5) - fbase) : 0u;
+        const uint32_t fj = (v & h1 & ((g0 & 31) == 31)) ? fi + 1 : fi;
+        fw[t] = fl[fi];
+        fh[t] = fl[fj];
+        rw[t] = fl[fwords + fi];
+      }
+    }
+  };
+  auto load_win = [&](int j, Raw32 (&r)[R], const uint32_t (&fw)[R], const uint32_t (&fh)[R],
+                      const uint32_t (&rw)[R], uint32_t& vbits, uint32_t& okbits) __attribute__((always_inline)) {
+    const int64_t k0 = win_k(j);
+    const bool kv = (j < nwin) & (k0 < ke);
+    const bool h1 = k0 + 64 < ke;
+    vbits = 0;
+    okbits = 0;
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      const int64_t n = n0 + 16 * t + i16;
+      const bool v = kv & (n < N);
+      uint32_t vb;
+      load32<FMT>(w, (uint64_t)(n * K + k0 + goff), v, v & h1, fmt_is_pal(FMT) ? fw[t] : 0u,
+                  fmt_is_pal(FMT) ? fh[t] : 0u, fmt_is_pal(FMT) ? rw[t] : 0u, r[t], vb);
+      vbits |= vb << (2 * t);
+      okbits |= (v ? 1u : 0u) << (2 * t);
+      okbits |= (v & h1 ? 1u : 0u) << (2 * t + 1);
+    }
+  };
+  // this thread's share of a window's packed x (windows past the range read
+  // window 0: their weights are zero)
+  auto load_xs = [&](int j, u32x4 (&xg)[NBG]) __attribute__((always_inline)) {
+    const int64_t k0 = win_k(j);
+    const bool kv = (j < nwin) & (k0 < ke);
+    const u32x4* src = reinterpret_cast<const u32x4*>(xp) + (uint64_t)(kv ? k0 / kWin : 0) * XE + threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < NBG; ++i) xg[i] = src[256 * i];
+  };
+  auto store_xs = [&](int buf, const u32x4 (&xg)[NBG]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NBG; ++i) xs[buf * XE + 256 * i + (int)threadIdx.x] = xg[i];
+  };
+
+  f32x4 acc[R][NBG];
+#pragma unroll
+  for (int t = 0; t < R; ++t)
+#pragma unroll
+    for (int q = 0; q < NBG; ++q) acc[t][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const Raw32 (&r)[R], int buf, uint32_t vbits, uint32_t okbits) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      u32x4 xr[NBG];
+#pragma unroll
+      for (int q = 0; q < NBG; ++q) xr[q] = xs[buf * XE + (q * 4 + m) * 64 + lane];
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        const bool ok = (okbits >> (2 * t + (m >> 1))) & 1u;
+        const bf16x8 a = a_frag<FMT>(w, r[t], (vbits >> (2 * t)) & 3u, ok, m, g);
+#pragma unroll
+        for (int q = 0; q < NBG; ++q)
+          acc[t][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, xr[q]), acc[t][q], 0, 0, 0);
+      }
+    }
+  };
+
+  // DP windows of weights in registers: the loads of window j + DP (and the
+  // flag words of j + 2 DP) are issued as soon as window j has been consumed;
+  // x is staged one window ahead.  Windows past the range load index 0 and
+  // add zeros, so the loop has no tail.
+  Raw32 rw[DP][R];
+  u32x4 xg[NBG];
+  uint32_t fw[DP][R], fh[DP][R], fr[DP][R];
+  uint32_t vb[DP], ob[DP];
+#pragma unroll
+  for (int d = 0; d < DP; ++d)
+#pragma unroll
+    for (int t = 0; t < R; ++t) fw[d][t] = fh[d][t] = fr[d][t] = 0u;
+#pragma unroll
+  for (int d = 0; d < DP; ++d) load_flags(d, fw[d], fh[d], fr[d]);
+  __builtin_amdgcn_sched_barrier(0);
+  load_xs(0, xg);
+#pragma unroll
+  for (int d = 0; d < DP; ++d) {
+    load_win(d, rw[d], fw[d], fh[d], fr[d], vb[d], ob[d]);
+    load_flags(d + DP, fw[d], fh[d], fr[d]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  store_xs(0, xg);
+  load_xs(1, xg);
+  __syncthreads();
+  int j = 0;
+  do {
+#pragma unroll
+    for (int d = 0; d < DP; ++d) {   // window j + d, its x in buffer d % 2 (DP is even)
+      compute(rw[d], d & 1, vb[d], ob[d]);
+      __builtin_amdgcn_sched_barrier(0);
+      load_win(j + d + DP, rw[d], fw[d], fh[d], fr[d], vb[d], ob[d]);
+      load_flags(j + d + 2 * DP, fw[d], fh[d], fr[d]);
+      __builtin_amdgcn_sched_barrier(0);
+      store_xs((d + 1) & 1, xg);   // window j + d + 1
+      load_xs(j + d + 2, xg);
+      __syncthreads();
+    }
+    j += DP;
+  } while (j < nwin);
+
+  // D of v_mfma_f32_16x16x32_bf16: lane l holds rows 4 (l / 16) .. +3 (output
+  // features) of column l % 16 (batch row)
+  float* out = part ? part + (uint64_t)blockIdx.y * (uint64_t)B * (uint64_t)N : y + col0;
+  const int64_t ld = part ? N : ldy;
+#pragma unroll
+  for (int t = 0; t < R; ++t)
+#pragma unroll
+    for (int q = 0; q < NBG; ++q) {
+      const int64_t n = n0 + 16 * t + 4 * (lane >> 4);
+      const int b = 16 * q + i16;
+      if (b < B) {
+        float* o = out + (int64_t)b * ld + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) o[r] = acc[t][q][r];
+      }
+    }
+}
+
+typedef void (*RfxFn)(WeightView, int, float*, int64_t, int64_t, int64_t, float*, uint32_t, const uint4*);
+
+constexpr int kRfxDepth = 2;   // windows of weights in flight per wave
+
+template <int F, int R>
+RfxFn rfx_fn(int nbg) {
+  if (nbg <= 1) return k_mfma_rfx<F, R, 1, kRfxDepth>;
+  if (nbg <= 2) return k_mfma_rfx<F, R, 2, kRfxDepth>;
+  return k_mfma_rfx<F, R, 4, kRfxDepth>;
+}
+
+template <int R>
+RfxFn rfx_pick(int fmt, int nbg) {
+  return fmt == kFmtBf16 ? rfx_fn<kFmtBf16, R>(nbg)
+         : fmt == kFmtExp ? rfx_fn<kFmtExp, R>(nbg)
+         : fmt == kFmtPal ? rfx_fn<kFmtPal, R>(nbg) : rfx_fn<kFmtPalRun, R>(nbg);
+}
+
 typedef void (*RfFn)(WeightView, const uint16_t*, int, float*, int64_t, int64_t, int64_t, float*, uint32_t,
                      const uint4*);
 
@@ -386,47 +589,57 @@ int rf_nbg(int64_t nb) { return nb <= 16 ? 1 : nb <= 32 ? 2 : 4; }
 
 }  // namespace
 
-int mfma_rf_kinds() { return 2; }   // row tiles per wave: 2 (kind 0) or 4 (kind 1)
+// kinds: 0 and 1, x per wave from L2 with two and four row tiles per wave
+// (a block: 32 or 64 rows); 2 and 3, x shared through LDS with one and two
+// row tiles per wave (a block: 64 or 128 rows)
+int mfma_rf_kinds() { return 4; }
 int mfma_rf_max_batch() { return kRfMaxBatch; }
+static bool rf_shared_x(int kind) { return kind >= 2; }
+static int rf_tiles(int kind) { return kind == 0 ? 2 : kind == 1 ? 4 : kind == 2 ? 1 : 2; }   // per wave
+static int64_t rf_block_rows(int kind) { return 16 * (int64_t)rf_tiles(kind) * (rf_shared_x(kind) ? 4 : 1); }
 
 // K slices over grid.y: none unless the row blocks leave the chip under two
-// blocks per CU, and never below 16 windows per slice (4 per wave).
+// blocks per CU (one for the shared-x kinds), and never below 16 windows per
+// slice (4 per wave when the waves take turns, 16 when they walk the windows
+// together).  The shared-x kinds gain less from a second block per CU than
+// the partial sums cost: 70B gate (448 64-row blocks), palette-direct, 16
+// rows: 81 us unsplit, 92 us in two slices.
 int mfma_rf_slices(const WeightView& w, int kind, int split_hint, int cus) {
-  const int R = kind == 0 ? 2 : 4;
-  const int64_t rowblocks = ((int64_t)w.n + 16 * R - 1) / (16 * R);
+  const int64_t rowblocks = ((int64_t)w.n + rf_block_rows(kind) - 1) / rf_block_rows(kind);
   const int64_t wins = ((int64_t)w.k + kWin - 1) / kWin;
+  const int64_t cover = rf_shared_x(kind) ? cus : 2 * (int64_t)cus;
   int s = 1;
   if (split_hint > 0) {
     s = split_hint;
   } else {
-    while (rowblocks * s < 2 * cus && wins / (2 * s) >= 16) s *= 2;
+    while (rowblocks * s < cover && wins / (2 * s) >= 16) s *= 2;
   }
   if (s > wins) s = (int)wins;
   if (s < 1) s = 1;
   return s;
 }
 
-// x is packed (k_rf_pack_x) for launches of more than 8 rows: below that the
-// rows past the batch repeat the last one and the plain loads are cheaper
-static bool rf_packs(int64_t nb) { return nb > 8; }
+// x is packed (k_rf_pack_x) for launches of more than 8 rows, and always for
+// the shared-x kinds: below that the rows past the batch repeat the last one
+// and the plain loads are cheaper
+static bool rf_packs(int kind, int64_t nb) { return rf_shared_x(kind) || nb > 8; }
 static size_t rf_part_floats(const WeightView& w, int slices, int64_t nb) {   // 16-byte multiple
   return slices > 1 ? ((size_t)slices * (size_t)nb * (size_t)w.n + 3) & ~(size_t)3 : 0;
 }
-static size_t rf_pack_entries(const WeightView& w, int64_t nb) {
+static size_t rf_pack_entries(const WeightView& w, int kind, int64_t nb) {
   const int64_t wins = ((int64_t)w.k + kWin - 1) / kWin;
-  return rf_packs(nb) ? (size_t)wins * (size_t)rf_nbg(nb) * 4 * 64 : 0;
+  return rf_packs(kind, nb) ? (size_t)wins * (size_t)rf_nbg(nb) * 4 * 64 : 0;
 }
 
 size_t mfma_rf_partial_elems(const WeightView& w, int64_t batch, int kind, int split_hint, int cus) {
   const int s = mfma_rf_slices(w, kind, split_hint, cus);
   const int64_t nb = batch < kRfMaxBatch ? batch : kRfMaxBatch;
-  return rf_part_floats(w, s, nb) + 4 * rf_pack_entries(w, nb);
+  return rf_part_floats(w, s, nb) + 4 * rf_pack_entries(w, kind, nb);
 }
 
 // flag and rank words one block stages (palette formats)
 static uint64_t rf_flag_words(const WeightView& w, int kind) {
-  const int R = kind == 0 ? 2 : 4;
-  return fmt_is_pal(w.fmt) ? (uint64_t)16 * R * w.k / 2048 + 2 : 0;
+  return fmt_is_pal(w.fmt) ? (uint64_t)rf_block_rows(kind) * w.k / 2048 + 2 : 0;
 }
 
 bool mfma_rf_supported(const WeightView& w, int kind) {
@@ -437,19 +650,17 @@ hipError_t launch_mfma_rf(const WeightView& w, const uint16_t* x, int64_t batch,
                           int64_t col0, int kind, int split_hint, int cus, float* part, size_t part_elems,
                           hipStream_t s) {
   if (!mfma_rf_supported(w, kind)) return hipErrorNotSupported;
-  const int R = kind == 0 ? 2 : 4;
   const int slices = mfma_rf_slices(w, kind, split_hint, cus);
   const int64_t wins = ((int64_t)w.k + kWin - 1) / kWin;
   const int64_t kslice = ((wins + slices - 1) / slices) * kWin;
-  const unsigned rowblocks = (unsigned)(((int64_t)w.n + 16 * R - 1) / (16 * R));
+  const unsigned rowblocks = (unsigned)(((int64_t)w.n + rf_block_rows(kind) - 1) / rf_block_rows(kind));
   const uint32_t fwords = (uint32_t)rf_flag_words(w, kind);   // staged in LDS per block
   hipError_t e0 = hipSuccess;
   for (int64_t b0 = 0; b0 < batch; b0 += kRfMaxBatch) {
     const int64_t nb = batch - b0 < kRfMaxBatch ? batch - b0 : kRfMaxBatch;
     const bool split = slices > 1;
-    const size_t pf = rf_part_floats(w, slices, nb), pe = rf_pack_entries(w, nb);
+    const size_t pf = rf_part_floats(w, slices, nb), pe = rf_pack_entries(w, kind, nb);
     if ((split || pe > 0) && (part == nullptr || part_elems < pf + 4 * pe)) return hipErrorInvalidValue;
-    const RfFn f = kind == 0 ? rf_pick<2>(w.fmt, rf_nbg(nb)) : rf_pick<4>(w.fmt, rf_nbg(nb));
     const uint16_t* xb = x + (uint64_t)b0 * w.k;
     float* yb = y + (uint64_t)b0 * (uint64_t)ldy;
     uint4* xp = nullptr;
@@ -465,10 +676,20 @@ hipError_t launch_mfma_rf(const WeightView& w, const uint16_t* x, int64_t batch,
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    e0 = allow_dynamic_lds((const void*)f, (int)(fwords * 8));
-    if (e0 != hipSuccess) return e0;
-    hipLaunchKernelGGL(f, dim3(rowblocks, (unsigned)slices), dim3(256), (size_t)fwords * 8, s, w, xb, (int)nb, yb,
-                       ldy, col0, kslice, split ? part : nullptr, fwords, (const uint4*)xp);
+    if (rf_shared_x(kind)) {
+      const RfxFn f = kind == 2 ? rfx_pick<1>(w.fmt, rf_nbg(nb)) : rfx_pick<2>(w.fmt, rf_nbg(nb));
+      const size_t lds = 2 * (size_t)rf_nbg(nb) * 4 * 64 * sizeof(uint4) + (size_t)fwords * 8;
+      e0 = allow_dynamic_lds((const void*)f, (int)lds);
+      if (e0 != hipSuccess) return e0;
+      hipLaunchKernelGGL(f, dim3(rowblocks, (unsigned)slices), dim3(256), lds, s, w, (int)nb, yb, ldy, col0, kslice,
+                         split ? part : nullptr, fwords, (const uint4*)xp);
+    } else {
+      const RfFn f = kind == 0 ? rf_pick<2>(w.fmt, rf_nbg(nb)) : rf_pick<4>(w.fmt, rf_nbg(nb));
+      e0 = allow_dynamic_lds((const void*)f, (int)(fwords * 8));
+      if (e0 != hipSuccess) return e0;
+      hipLaunchKernelGGL(f, dim3(rowblocks, (unsigned)slices), dim3(256), (size_t)fwords * 8, s, w, xb, (int)nb, yb,
+                         ldy, col0, kslice, split ? part : nullptr, fwords, (const uint4*)xp);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (split) {

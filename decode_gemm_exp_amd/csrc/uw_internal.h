@@ -220,7 +220,8 @@ int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint);
 size_t mfma2_partial_elems(const WeightView& w, int64_t batch, int tile, int split_hint);
 hipError_t launch_mfma2(const WeightView& w, const uint16_t* x, int64_t batch, float* y, int64_t ldy, int64_t col0,
                         int tile, int split_hint, float* part, size_t part_elems, hipStream_t s);
-// gemm_rf.hip (kind 0: two 16-row tiles per wave, kind 1: four)
+// gemm_rf.hip (kind 0: two 16-row tiles per wave, kind 1: four; kinds 2 and
+// 3: x shared through LDS, one and two tiles per wave)
 int mfma_rf_kinds();
 int mfma_rf_max_batch();
 bool mfma_rf_supported(const WeightView& w, int kind);   // stored [N][K], flag words fit in LDS

@@ -189,7 +189,7 @@ def test_gemm_ragged_all_pipelines(uw, synth, oracle, layout, batch):
     for p in range(4):
         y = run_pipeline(uw, m, p, x)
         check_gemm(oracle, y, x_np, w_np, layout, what=f"pipeline {p}")
-    # every variant, forced (the register-fed ones, last two, take stored [N][K] only)
+    # every variant, forced (the register-fed ones, last, take stored [N][K] only)
     for v in range(1, uw.variant_count() + 1):
         if layout == 1 and v >= RF_FIRST(uw):
             with pytest.raises(uw.UwError) as ei:
@@ -201,7 +201,16 @@ def test_gemm_ragged_all_pipelines(uw, synth, oracle, layout, batch):
 
 
 def RF_FIRST(uw):
-    return uw.variant_count() - 1
+    """The first register-fed variant (they follow the GEMV and the LDS tiles)."""
+    return min(rf_variants(uw))
+
+
+def rf_variants(uw):
+    """The register-fed variants, found from the kernel each one plans."""
+    w = torch.zeros(64, 128, dtype=torch.bfloat16, device=DEV)
+    m = uw.uw_compress(w, 64, 128, 0)
+    return [v for v in range(1, uw.variant_count() + 1)
+            if uw.uw_plan_gemm(m, 0, 16, {"variant": v})["kernel"].startswith("k_mfma_rf")]
 
 
 # the small tiles (64x128, 32x128, 32x256) over K slices of 1, 2, 5 and an
@@ -270,11 +279,12 @@ def test_gemm_palette_tail_split(uw, synth, oracle):
         check_gemm(oracle, y, x_np, w_np, 0, what=f"pipeline {p}")
 
 
-# register-fed MFMA kernels (stored [N][K]): row counts that leave partial
-# 32- and 64-row blocks, K with a partial 128-wide window (K % 128 == 64), a
-# K whose windows split unevenly over the four waves, batches across the
-# 16-row groups and past the 64-row launch limit, K slices, verbatim-rich and
-# run palettes
+# register-fed MFMA kernels (stored [N][K]), x per wave and x shared through
+# LDS: row counts that leave partial 32-, 64- and 128-row blocks (waves with
+# no rows left still stage x), K with a partial 128-wide window (K % 128 ==
+# 64), a K whose windows split unevenly over the four waves, batches across
+# the 16-row groups and past the 64-row launch limit, K slices, verbatim-rich
+# and run palettes
 @pytest.mark.parametrize("n,k,outliers", [(200, 1088, 0.01), (70, 4096, 0.0), (96, 320, 0.02)])
 def test_register_fed_mfma(uw, synth, oracle, n, k, outliers):
     say(f"register-fed mfma n={n} k={k} outliers={outliers}")
@@ -285,7 +295,7 @@ def test_register_fed_mfma(uw, synth, oracle, n, k, outliers):
     for batch in (1, 5, 16, 17, 40, 64, 65, 130):
         x = synth.activations(batch, k, seed=batch + 11).to(DEV)
         x_np = bits(x)
-        for v in (RF_FIRST(uw), RF_FIRST(uw) + 1):
+        for v in rf_variants(uw):
             for p in range(4):
                 y = run_pipeline(uw, m, p, x, cfg={"variant": v})
                 check_gemm(oracle, y, x_np, w_np, 0, what=f"batch {batch} variant {v} pipeline {p}")
@@ -412,7 +422,7 @@ def test_gemm_one_hot_exact(uw, synth, oracle, layout):
             y = run_pipeline(uw, m, p, x)
             assert np.array_equal(y, expect), f"batch {batch} pipeline {p}"
         if layout == 0:   # output placement of the register-fed kernels
-            for v in (RF_FIRST(uw), RF_FIRST(uw) + 1):
+            for v in rf_variants(uw):
                 y = run_pipeline(uw, m, 2, x, cfg={"variant": v})
                 assert np.array_equal(y, expect), f"batch {batch} variant {v}"
 
