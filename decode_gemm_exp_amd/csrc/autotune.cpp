@@ -38,8 +38,12 @@ struct Choice {
 };
 
 // Device buffers and HIP objects of one tuning run, released on every return.
+// A return in the middle of a timed pass may leave launches that use x, y and
+// the workspace in flight, so the stream is drained before they are freed (an
+// allocator hook may hand them out again at once).
 struct Bufs {
   uw_allocator a = uw::current_allocator();
+  hipStream_t stream = nullptr;
   void* x = nullptr;
   void* y = nullptr;
   void* ws = nullptr;
@@ -47,6 +51,7 @@ struct Bufs {
   hipEvent_t e0 = nullptr, e1 = nullptr;
   FILE* json = nullptr;
   ~Bufs() {
+    if (x || y || ws) (void)hipStreamSynchronize(stream);
     uw::free_with(a, x);
     uw::free_with(a, y);
     uw::free_with(a, ws);
@@ -132,6 +137,7 @@ extern "C" uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj
     maxn = std::max<uint64_t>(maxn, inf.n);
   }
   Bufs bufs;
+  bufs.stream = s;
   uw_status ast = uw::alloc_with(bufs.a, &bufs.x, (size_t)maxb * maxk * 2 + 256);
   if (ast != UW_OK) return ast;
   ast = uw::alloc_with(bufs.a, &bufs.y, (size_t)maxb * maxn * 4 + 256);
@@ -399,6 +405,7 @@ extern "C" uw_status uw_autotune_grouped(const uw_matrix* const* ms, int group, 
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   Bufs bufs;
+  bufs.stream = s;
   uw_status st = uw::alloc_with(bufs.a, &bufs.x, (size_t)maxb * k * 2 + 256);
   if (st != UW_OK) return st;
   st = uw::alloc_with(bufs.a, &bufs.y, (size_t)maxb * ntot * 4 + 256);
