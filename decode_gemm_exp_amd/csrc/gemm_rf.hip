@@ -44,37 +44,50 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// Which 32 weights of a 128-wide window lane group g (= lane / 16) owns, so
-// that every load instruction reads 64 contiguous bytes of each of its 16 rows:
-//   BF16 (two bytes a weight): MFMA m takes k0 + 32 m + 8 g .. +7;
-//   byte formats: piece p = m / 2 is k0 + 64 p + 16 g .. +15, MFMA m takes
-//   its half m % 2.
+// Which 32 weights of a 128-wide window lane group g (= lane / 16) owns:
+//   BF16 (two bytes a weight): MFMA m takes k0 + 32 m + 8 g .. +7, so every
+//   load instruction reads 64 contiguous bytes of each of its 16 rows;
+//   byte formats: lane group g takes k0 + 32 g .. +31, all in one group, and
+//   MFMA m its weights 8 m .. +7.  A lane's 32 index nibbles are then one
+//   aligned 16-byte load and its group's verbatim flag one bit.
 // The x fragment of MFMA m uses the same k (kx_off).
 template <int FMT>
 __device__ __forceinline__ int kx_off(int m, int g) {
-  return FMT == kFmtBf16 ? 32 * m + 8 * g : 64 * (m >> 1) + 16 * g + 8 * (m & 1);
+  return FMT == kFmtBf16 ? 32 * m + 8 * g : 32 * g + 8 * m;
 }
 
 // Compressed data of one lane's 32 weights of one row.
 //   bf16: w[m] = the 8 weights of MFMA m
-//   exp:  s[p] = 16 sign+mantissa bytes of piece p, e[p] = its 16 exponent bytes
-//   pal:  s[p] as above, e[p] = the aligned 16 index bytes holding the
-//         piece's 16 nibbles (in bytes 8 .. 15 for odd lane groups), or its 16
-//         exponent bytes when its group is verbatim
+//   exp:  s0, s1 = the 32 sign+mantissa bytes, e0, e1 = the 32 exponent bytes
+//   pal:  s0, s1 as above; e0 = the 16 index bytes (32 nibbles), e1 = zero;
+//         or, when the lane's group is verbatim, e0, e1 = its 32 exponent bytes
 struct Raw32 {
   uint4 s0, s1, e0, e1;
 };
 
+// An offset past the end of every buffer resource: its loads return zero
+// without touching memory.
+constexpr uint32_t kRfPastEnd = 0x7FFF0000u;
+constexpr uint64_t kRfVexpMax = 0x40000000u;   // the verbatim section's resource spans at most 1 GiB
+typedef unsigned int u32x4_rf __attribute__((ext_vector_type(4)));
+
 // Loads of one lane's 32 weights of a row; el = stored index of the window
-// start plus 16 g (byte formats) or 8 g (BF16).  ok0 / ok1: the window's first
-// / second 64 weights exist.  Invalid pieces read index 0 (valid memory) and
-// are zeroed when rebuilt.  The two pieces of a byte format sit in the
-// window's two groups; fw / fh are the verbatim flag words holding the first
-// and the second group (the same word unless the pair straddles two), rw the
-// rank word of the first.
+// start plus 32 g (byte formats) or 8 g (BF16).  ok0 / ok1: the window's first
+// / second 64 weights exist (byte formats: the lane's group is the window's
+// first for lane groups 0 and 1, its second for 2 and 3).  Invalid pieces read
+// index 0 (valid memory) and are zeroed when rebuilt.  fw / fh are the
+// verbatim flag words holding the window's first and second group (the same
+// word unless the pair straddles two), rw the rank word of the first; rvx
+// covers the verbatim section.
+// The palette formats issue three loads per 32 weights: the second half of a
+// verbatim group's exponents comes through rvx at an offset past its end for
+// every other lane, so no memory is read for it.  Loading it for every lane,
+// or the quarter pieces of both groups that lane pairs used to read twice,
+// took a fourth load instruction: 70B gate, palette-direct, x shared through
+// LDS, 8 / 32 / 64 rows 85 / 96.7 / 114.5 -> 79.8 / 91.4 / 110.7 us.
 template <int FMT>
 __device__ __forceinline__ void load32(const WeightView& w, uint64_t el, bool ok0, bool ok1, uint32_t fw, uint32_t fh,
-                                       uint32_t rw, Raw32& r, uint32_t& verb) {
+                                       uint32_t rw, int g, __amdgpu_buffer_rsrc_t rvx, Raw32& r, uint32_t& verb) {
   verb = 0;
   if constexpr (FMT == kFmtBf16) {
     const uint64_t a = ok0 ? el : 0, b = ok1 ? el + 64 : 0;
@@ -82,52 +95,52 @@ __device__ __forceinline__ void load32(const WeightView& w, uint64_t el, bool ok
     r.s1 = *reinterpret_cast<const uint4*>(w.bf16 + a + 32);
     r.e0 = *reinterpret_cast<const uint4*>(w.bf16 + b);
     r.e1 = *reinterpret_cast<const uint4*>(w.bf16 + b + 32);
-  } else if constexpr (FMT == kFmtExp) {
-    const uint64_t a = ok0 ? el : 0, b = ok1 ? el + 64 : 0;
-    r.s0 = *reinterpret_cast<const uint4*>(w.sm + a);
-    r.s1 = *reinterpret_cast<const uint4*>(w.sm + b);
-    r.e0 = *reinterpret_cast<const uint4*>(w.ex + a);
-    r.e1 = *reinterpret_cast<const uint4*>(w.ex + b);
   } else {
-    const uint64_t a = ok0 ? el : 0, b = ok1 ? el + 64 : 0;
+    const bool second = g >= 2;   // the lane's weights lie in the window's second group
+    const bool ok = second ? ok1 : ok0;
+    const uint64_t a = ok ? el : 0;
     r.s0 = *reinterpret_cast<const uint4*>(w.sm + a);
-    r.s1 = *reinterpret_cast<const uint4*>(w.sm + b);
-    const uint64_t g0 = el >> 6;   // the window's first group
-    const bool v0 = ok0 & group_verbatim(fw, g0);
-    const bool v1 = ok1 & group_verbatim(fh, g0 + 1);
-    const uint32_t r0 = group_rank(fw, rw, g0);
-    const uint32_t r1 = r0 + (group_verbatim(fw, g0) ? 1u : 0u);
-    // index nibbles: the aligned 16 bytes that hold the piece's 8 (the half is
-    // picked when rebuilding), so the read never passes the end of the array
-    const uint8_t* p0 = v0 ? w.vexp + (uint64_t)r0 * 64 + (el & 63) : w.pidx + ((a >> 1) & ~(uint64_t)15);
-    const uint8_t* p1 = v1 ? w.vexp + (uint64_t)r1 * 64 + (el & 63) : w.pidx + ((b >> 1) & ~(uint64_t)15);
-    r.e0 = *reinterpret_cast<const uint4*>(p0);
-    r.e1 = *reinterpret_cast<const uint4*>(p1);
-    verb = (v0 ? 1u : 0u) | (v1 ? 2u : 0u);
+    r.s1 = *reinterpret_cast<const uint4*>(w.sm + a + 16);
+    if constexpr (FMT == kFmtExp) {
+      r.e0 = *reinterpret_cast<const uint4*>(w.ex + a);
+      r.e1 = *reinterpret_cast<const uint4*>(w.ex + a + 16);
+    } else {
+      const uint64_t gl = el >> 6;                 // the lane's group
+      const uint64_t g0 = second ? gl - 1 : gl;    // the window's first group
+      const bool v = ok & group_verbatim(second ? fh : fw, gl);
+      const uint32_t rk = group_rank(fw, rw, g0) + (second && group_verbatim(fw, g0) ? 1u : 0u);
+      const uint32_t vo = rk * 64u + (uint32_t)(el & 63);   // the lane's exponents in the verbatim section
+      // a is a multiple of 32 weights, so the 16 index bytes are aligned
+      r.e0 = *reinterpret_cast<const uint4*>(v ? w.vexp + vo : w.pidx + (a >> 1));
+      const u32x4_rf q = __builtin_amdgcn_raw_buffer_load_b128(rvx, (int)(v ? vo + 16u : kRfPastEnd), 0, 0);
+      r.e1 = make_uint4(q.x, q.y, q.z, q.w);
+      verb = v ? 1u : 0u;
+    }
   }
 }
 
-// A operand of MFMA m as BF16 (ok: the piece holding it exists)
+// A operand of MFMA m as BF16 (ok: the weights it takes exist)
 template <int FMT>
-__device__ __forceinline__ bf16x8 a_frag(const WeightView& w, const Raw32& r, uint32_t verb, bool ok, int m,
-                                         int g) {
+__device__ __forceinline__ bf16x8 a_frag(const WeightView& w, const Raw32& r, uint32_t verb, bool ok, int m) {
   uint4 o;
   if constexpr (FMT == kFmtBf16) {
     o = m == 0 ? r.s0 : m == 1 ? r.s1 : m == 2 ? r.e0 : r.e1;
   } else {
+    // weights 8 m .. +7 of the lane's 32: words 2 (m % 2) and 2 (m % 2) + 1
+    // of the 16-byte half m / 2
     const uint4& sp = (m >> 1) ? r.s1 : r.s0;
-    const uint4& ep = (m >> 1) ? r.e1 : r.e0;
-    const int h = m & 1;   // half of the piece
-    const uint32_t s0 = word(sp, 2 * h), s1 = word(sp, 2 * h + 1);
+    const int wi = 2 * (m & 1);
+    const uint32_t s0 = word(sp, wi), s1 = word(sp, wi + 1);
     uint32_t e0, e1;
     if constexpr (FMT == kFmtExp) {
-      e0 = word(ep, 2 * h);
-      e1 = word(ep, 2 * h + 1);
+      const uint4& ep = (m >> 1) ? r.e1 : r.e0;
+      e0 = word(ep, wi);
+      e1 = word(ep, wi + 1);
     } else {
-      pal8<FMT == kFmtPalRun>(word(ep, h + 2 * (g & 1)), w.pal, e0, e1);
-      const bool vb = (verb >> (m >> 1)) & 1u;
-      e0 = vb ? word(ep, 2 * h) : e0;
-      e1 = vb ? word(ep, 2 * h + 1) : e1;
+      pal8<FMT == kFmtPalRun>(word(r.e0, m), w.pal, e0, e1);
+      const uint4& ep = (m >> 1) ? r.e1 : r.e0;   // verbatim: the exponent bytes
+      e0 = verb ? word(ep, wi) : e0;
+      e1 = verb ? word(ep, wi + 1) : e1;
     }
     rebuild4(s0, e0, o.x, o.y);
     rebuild4(s1, e1, o.z, o.w);
@@ -149,6 +162,8 @@ __global__ __launch_bounds__(256) void k_mfma_rf(WeightView w, const uint16_t* _
   extern __shared__ uint32_t fl[];     // palette: the block's verbatim flag words, then their rank words
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g = lane >> 4;
+  const __amdgpu_buffer_rsrc_t rvx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(w.vexp), (short)0, (int)(fmt_is_pal(FMT) ? w.vexp_bytes : 0u), 0x00020000);
   const int64_t N = (int64_t)w.n, K = (int64_t)w.k;
   const int64_t n0 = (int64_t)blockIdx.x * (16 * R);
   const int64_t kb = (int64_t)blockIdx.y * kslice;
@@ -187,7 +202,7 @@ __global__ __launch_bounds__(256) void k_mfma_rf(WeightView w, const uint16_t* _
     jj -= jj >= mine ? mine : 0;
     return kb + (int64_t)kWin * (wave + 4 * jj);
   };
-  const int goff = FMT == kFmtBf16 ? 8 * g : 16 * g;   // lane group's offset in a window
+  const int goff = FMT == kFmtBf16 ? 8 * g : 32 * g;   // lane group's offset in a window
   // flag and rank words of a window's groups (from LDS).  With K / 64 odd,
   // the two groups of a window may straddle two flag words.
   auto load_flags = [&](int j, uint32_t (&fw)[R], uint32_t (&fh)[R], uint32_t (&rw)[R]) __attribute__((always_inline)) {
@@ -240,7 +255,7 @@ __global__ __launch_bounds__(256) void k_mfma_rf(WeightView w, const uint16_t* _
       const bool v = kv & (n < N);
       uint32_t vb;
       load32<FMT>(w, (uint64_t)(n * K + k0 + goff), v, v & h1, fmt_is_pal(FMT) ? fw[t] : 0u,
-                  fmt_is_pal(FMT) ? fh[t] : 0u, fmt_is_pal(FMT) ? rw[t] : 0u, r[t], vb);
+                  fmt_is_pal(FMT) ? fh[t] : 0u, fmt_is_pal(FMT) ? rw[t] : 0u, g, rvx, r[t], vb);
       vbits |= vb << (2 * t);
       okbits |= (v ? 1u : 0u) << (2 * t);
       okbits |= (v & h1 ? 1u : 0u) << (2 * t + 1);
@@ -265,8 +280,10 @@ __global__ __launch_bounds__(256) void k_mfma_rf(WeightView w, const uint16_t* _
 #pragma unroll
       for (int t = 0; t < R; ++t) {
         // the piece holding MFMA m: BF16 first half m < 2, byte formats piece m / 2
-        const bool ok = (okbits >> (2 * t + (m >> 1))) & 1u;
-        const bf16x8 a = a_frag<FMT>(w, r[t], (vbits >> (2 * t)) & 3u, ok, m, g);
+        // the weights exist: BF16, the window half of MFMA m; byte formats,
+        // the half holding the lane's group
+        const bool ok = (okbits >> (2 * t + (FMT == kFmtBf16 ? (m >> 1) : (g >> 1)))) & 1u;
+        const bf16x8 a = a_frag<FMT>(w, r[t], (vbits >> (2 * t)) & 1u, ok, m);
 #pragma unroll
         for (int q = 0; q < NBG; ++q)
           acc[t][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, xr[q][m]), acc[t][q],
@@ -387,6 +404,8 @@ __global__ __launch_bounds__(256) void k_mfma_rfx(WeightView w, int B, float* __
   uint32_t* const fl = reinterpret_cast<uint32_t*>(dyn4 + 2 * XE);   // palette: flag words, then rank words
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g = lane >> 4;
+  const __amdgpu_buffer_rsrc_t rvx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(w.vexp), (short)0, (int)(fmt_is_pal(FMT) ? w.vexp_bytes : 0u), 0x00020000);
   const int64_t N = (int64_t)w.n, K = (int64_t)w.k;
   const int64_t nblk = (int64_t)blockIdx.x * (64 * R);   // the block's first row
   const int64_t n0 = nblk + (int64_t)wave * (16 * R);    // the wave's first row
@@ -413,7 +432,7 @@ __global__ __launch_bounds__(256) void k_mfma_rfx(WeightView w, int B, float* __
     jj -= jj >= nwin ? nwin : 0;
     return kb + (int64_t)kWin * jj;
   };
-  const int goff = FMT == kFmtBf16 ? 8 * g : 16 * g;
+  const int goff = FMT == kFmtBf16 ? 8 * g : 32 * g;
   auto load_flags = [&](int j, uint32_t (&fw)[R], uint32_t (&fh)[R], uint32_t (&rw)[R]) __attribute__((always_inline)) {
     if constexpr (fmt_is_pal(FMT)) {
       const int64_t k0 = win_k(j);
@@ -445,7 +464,7 @@ __global__ __launch_bounds__(256) void k_mfma_rfx(WeightView w, int B, float* __
       const bool v = kv & (n < N);
       uint32_t vb;
       load32<FMT>(w, (uint64_t)(n * K + k0 + goff), v, v & h1, fmt_is_pal(FMT) ? fw[t] : 0u,
-                  fmt_is_pal(FMT) ? fh[t] : 0u, fmt_is_pal(FMT) ? rw[t] : 0u, r[t], vb);
+                  fmt_is_pal(FMT) ? fh[t] : 0u, fmt_is_pal(FMT) ? rw[t] : 0u, g, rvx, r[t], vb);
       vbits |= vb << (2 * t);
       okbits |= (v ? 1u : 0u) << (2 * t);
       okbits |= (v & h1 ? 1u : 0u) << (2 * t + 1);
@@ -478,8 +497,10 @@ __global__ __launch_bounds__(256) void k_mfma_rfx(WeightView w, int B, float* __
       for (int q = 0; q < NBG; ++q) xr[q] = xs[buf * XE + (q * 4 + m) * 64 + lane];
 #pragma unroll
       for (int t = 0; t < R; ++t) {
-        const bool ok = (okbits >> (2 * t + (m >> 1))) & 1u;
-        const bf16x8 a = a_frag<FMT>(w, r[t], (vbits >> (2 * t)) & 3u, ok, m, g);
+        // the weights exist: BF16, the window half of MFMA m; byte formats,
+        // the half holding the lane's group
+        const bool ok = (okbits >> (2 * t + (FMT == kFmtBf16 ? (m >> 1) : (g >> 1)))) & 1u;
+        const bf16x8 a = a_frag<FMT>(w, r[t], (vbits >> (2 * t)) & 1u, ok, m);
 #pragma unroll
         for (int q = 0; q < NBG; ++q)
           acc[t][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, xr[q]), acc[t][q], 0, 0, 0);
@@ -643,7 +664,8 @@ static uint64_t rf_flag_words(const WeightView& w, int kind) {
 }
 
 bool mfma_rf_supported(const WeightView& w, int kind) {
-  return w.layout == 0 && rf_flag_words(w, kind) * 8 <= kRfMaxFlagLds;
+  return w.layout == 0 && rf_flag_words(w, kind) * 8 <= kRfMaxFlagLds &&
+         (!fmt_is_pal(w.fmt) || w.vexp_bytes <= kRfVexpMax);
 }
 
 hipError_t launch_mfma_rf(const WeightView& w, const uint16_t* x, int64_t batch, float* y, int64_t ldy,
