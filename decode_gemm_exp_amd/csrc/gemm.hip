@@ -758,6 +758,13 @@ static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_c
     if (batch <= 32 && mfma_rf_supported(w, 2) && (int64_t)((w.n + 63) / 64) * 8 >= (int64_t)device_cus() * 7)
       return rf_first_variant() + 2;
     if (batch <= 32 && mfma_rf_supported(w, 0)) return rf_first_variant();
+    // 33 to 64 rows: x shared, two row tiles per wave, when its 128-row
+    // blocks cover seven eighths of the CUs (70B gate, palette, 40 / 48 / 64
+    // rows: 115.4 / 110.9 / 113.5 us against 119.0 / 119.8 / 123.9 for the
+    // 64x128 tile); narrower matrices keep the tile (8B gate 42.5 vs 38.1 us
+    // at 64 rows)
+    if (batch <= 64 && mfma_rf_supported(w, 3) && (int64_t)((w.n + 127) / 128) * 8 >= (int64_t)device_cus() * 7)
+      return rf_first_variant() + 3;
     if (batch <= 64) return 2 + 0;
     if (batch <= 128) return 2 + 1;
     if (batch <= 512) return 2 + 7;
