@@ -967,7 +967,22 @@ static int tile_group_plan(const WeightView* ws, int count, int64_t batch, const
   wide.n = ntot;
   if (group_takes_tile32(ws, count, batch, cfg)) return 5;   // the 32x128 tile
   const int v = resolve_variant(wide, batch, cfg);
-  return v >= 2 && v < rf_first_variant() ? v - 2 : -1;
+  if (v >= 2 && v < rf_first_variant()) return v - 2;
+  // The group as one matrix would take a register-fed kernel, which the
+  // default picks by width.  From 33 to 64 rows the group is one launch of
+  // 64x128 tiles instead (70B gate+up at 64 rows: 219.7 us against 228.9 us
+  // matrix by matrix with the register-fed kernel; 8B gate+up, whose
+  // matrices alone each take the tile: 63 us against 2 x 38 us).  Up to 32
+  // rows it is one launch of the tile a matrix alone would take, if any;
+  // matrices that each take the register-fed kernel run one by one.
+  if (v >= rf_first_variant() && !(cfg && cfg->variant > 0)) {
+    if (batch > 32) return 0;
+    for (int i = 0; i < count; ++i) {
+      const int vi = resolve_variant(ws[i], batch, cfg);
+      if (vi >= 2 && vi < rf_first_variant()) return vi - 2;
+    }
+  }
+  return -1;
 }
 
 size_t gemm_tile_group_partial_elems(const WeightView* ws, int count, int64_t batch, const uw_kernel_cfg* cfg) {
