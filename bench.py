@@ -490,22 +490,47 @@ def c5_breakdown(uw, torch, dev, wl, mats, proj, infos, batches, plan, alternate
                 torch.cuda.synchronize()
                 return 1e3 * d0.elapsed_time(d1) / launches
 
+            def kernel_burst(fn):
+                # the same launches, each call's main kernel alone between two
+                # events the library records around its launch
+                # (uw_set_kernel_events); the events are recorded once first
+                # so that they exist
+                pairs = [(ev(), ev()) for _ in range(launches)]
+                for a, b_ in pairs:
+                    a.record(stream)
+                    b_.record(stream)
+                for i in range(2):
+                    fn(i)
+                hold_gpu(torch, launches)
+                try:
+                    for i in range(launches):
+                        uw.uw_set_kernel_events(pairs[i][0], pairs[i][1])
+                        fn(i)
+                finally:
+                    uw.uw_set_kernel_events(None, None)
+                torch.cuda.synchronize()
+                return 1e3 * sum(a.elapsed_time(b_) for a, b_ in pairs) / launches
+
             stages = []
             if p != 3:
                 t = burst(lambda i: call(mats[idx[i % len(idx)]], preps[i % len(idx)], stream))
                 stages.append(("prep", {0: "decode_full", 1: "decode_exponent", 2: "transcode"}[p],
                                {0: "k_decode_staged<2,", 1: "k_decode_staged<1,", 2: "k_decode_staged<0,"}[p],
-                               t, prep_stage_bytes(info, p), 0.0))
-            t = burst(lambda i: uw.uw_matmul_stage(mats[idx[i % len(idx)]], p, preps[i % len(idx)] if preps else None,
-                                                   xin, y, part, stream=stream))
+                               t, prep_stage_bytes(info, p), 0.0, t))
+            def gemm_call(i):
+                uw.uw_matmul_stage(mats[idx[i % len(idx)]], p, preps[i % len(idx)] if preps else None,
+                                   xin, y, part, stream=stream)
+            t = burst(gemm_call)
+            tk = kernel_burst(gemm_call) if gp["kernel"].startswith("k_mfma") else None
             stages.append(("gemm", f"gemm_{PIPE_NAMES[p]}", gp["kernel"], t, gemm_stage_bytes(info, p, b),
-                           2.0 * b * info.n * info.k))
+                           2.0 * b * info.n * info.k, tk))
             count = sum(1 for q in proj if q == pj)
             label = ("easy_" if pj < 3 else "hard_") + wl.mats[pj % 3][0] if alternate else wl.mats[pj][0]
-            for kind, stage, kernel, t, nbytes, flops in stages:
+            for kind, stage, kernel, t, nbytes, flops, tk in stages:
                 rows.append({"batch": b, "projection": label, "stage": stage, "kernel": kernel,
                              "variant": gp["variant"], "tile": [gp["tile_m"], gp["tile_n"], gp["waves"]],
-                             "k_slices": gp["k_slices"], "us": round(t, 2), "launches_per_sweep": count,
+                             "k_slices": gp["k_slices"], "us": round(t, 2),
+                             "kernel_us": round(tk, 2) if tk is not None else None, "launches_per_sweep": count,
                              "share_us": round(t * count, 1), "alg_bytes": int(nbytes), "flops": flops,
                              "launches_timed": launches})
             del preps, part
@@ -514,7 +539,8 @@ def c5_breakdown(uw, torch, dev, wl, mats, proj, infos, batches, plan, alternate
 
 
 def roofline_of(row, peaks):
-    t = row["us"] * 1e-6
+    # the kernel alone where it was timed so (MFMA stages), else the stage
+    t = (row.get("kernel_us") or row["us"]) * 1e-6
     t_hbm = row["alg_bytes"] / (HBM_PEAK_GBS * 1e9)
     t_mfma = row["flops"] / (BF16_PEAK_TFLOPS * 1e12)
     if t_mfma >= t_hbm:
@@ -700,11 +726,15 @@ def run_c5(args) -> int:
     roof.update({"traffic": load_traffic(f"{dom['stage']}_{dom['projection']}_b{dom['batch']}", "mlp70b"),
                  "kernel": dom["kernel"], "stage": dom["stage"], "projection": dom["projection"],
                  "batch": dom["batch"], "alg_bytes_per_launch": dom["alg_bytes"],
-                 "flops_per_launch": dom["flops"], "avg_launch_us": dom["us"],
-                 "launches_timed": dom["launches_timed"],
+                 "flops_per_launch": dom["flops"], "avg_launch_us": dom.get("kernel_us") or dom["us"],
+                 "stage_us": dom["us"], "launches_timed": dom["launches_timed"],
                  "share_of_step": round(dom["share_us"] / (ms_per_step * 1e3), 4),
-                 "timing": f"HIP events on the launch stream around {dom['launches_timed']} back-to-back launches "
-                           f"(rotating over 4 layers) after the timed steps"})
+                 "timing": f"avg_launch_us: the kernel alone, between HIP events the library records on the launch "
+                           f"stream immediately around its launch (uw_set_kernel_events), over "
+                           f"{dom['launches_timed']} launches rotating over 4 layers after the timed steps; "
+                           f"stage_us: HIP events around the whole stage call over the same launches back to back "
+                           f"(with x packing and any split-K reduction); the dominant stage is the one with the "
+                           f"largest share of the step"})
     value = len(batches) * 2 * M_total / (ms_per_step * 1e-3) / 1e9
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

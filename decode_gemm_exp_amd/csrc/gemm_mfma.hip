@@ -674,9 +674,11 @@ static hipError_t launch_group(Mfma2Group grp, const uint16_t* x, int64_t batch,
     if (e != hipSuccess) return e;
   }
   dim3 grid((unsigned)nblocks, 1, (unsigned)slices);
+  kernel_event_before(s);
   hipLaunchKernelGGL(f, grid, dim3(64 * t.waves), lds, s, grp, xk, (int)batch, y, ldy, kslice, split ? part : nullptr,
                      (int64_t)ntot, mtiles);
   hipError_t e = hipGetLastError();
+  kernel_event_after(s);
   if (e != hipSuccess || !split) return e;
   return launch_sum_slices(part, slices, ntot, batch, y, ldy, grp.ycol[0], s);
 }

@@ -698,21 +698,25 @@ hipError_t launch_mfma_rf(const WeightView& w, const uint16_t* x, int64_t batch,
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
+    const bool first = b0 == 0, last = b0 + kRfMaxBatch >= batch;
     if (rf_shared_x(kind)) {
       const RfxFn f = kind == 2 ? rfx_pick<1>(w.fmt, rf_nbg(nb)) : rfx_pick<2>(w.fmt, rf_nbg(nb));
       const size_t lds = 2 * (size_t)rf_nbg(nb) * 4 * 64 * sizeof(uint4) + (size_t)fwords * 8;
       e0 = allow_dynamic_lds((const void*)f, (int)lds);
       if (e0 != hipSuccess) return e0;
+      if (first) kernel_event_before(s);
       hipLaunchKernelGGL(f, dim3(rowblocks, (unsigned)slices), dim3(256), lds, s, w, (int)nb, yb, ldy, col0, kslice,
                          split ? part : nullptr, fwords, (const uint4*)xp);
     } else {
       const RfFn f = kind == 0 ? rf_pick<2>(w.fmt, rf_nbg(nb)) : rf_pick<4>(w.fmt, rf_nbg(nb));
       e0 = allow_dynamic_lds((const void*)f, (int)(fwords * 8));
       if (e0 != hipSuccess) return e0;
+      if (first) kernel_event_before(s);
       hipLaunchKernelGGL(f, dim3(rowblocks, (unsigned)slices), dim3(256), (size_t)fwords * 8, s, w, xb, (int)nb, yb,
                          ldy, col0, kslice, split ? part : nullptr, fwords, (const uint4*)xp);
     }
     hipError_t e = hipGetLastError();
+    if (last) kernel_event_after(s);
     if (e != hipSuccess) return e;
     if (split) {
       e = launch_sum_slices(part, slices, w.n, nb, yb, ldy, col0, s);

@@ -16,6 +16,7 @@
 // engine looks the choice up instead of deciding again.
 #include <hip/hip_ext.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -232,6 +233,16 @@ uw_status pooled_events(size_t count, hipEvent_t** out) {
 
 int residency_of(const uw_matrix* m) { return (m->stream ? 1 : 0) | (m->pidx ? 2 : 0); }
 
+// ---- timing aid (uw_set_kernel_events) -------------------------------------------------
+std::atomic<void*> g_kev_before{nullptr}, g_kev_after{nullptr};
+
+void kernel_event_before(hipStream_t s) {
+  if (void* e = g_kev_before.load(std::memory_order_relaxed)) (void)hipEventRecord(static_cast<hipEvent_t>(e), s);
+}
+void kernel_event_after(hipStream_t s) {
+  if (void* e = g_kev_after.load(std::memory_order_relaxed)) (void)hipEventRecord(static_cast<hipEvent_t>(e), s);
+}
+
 bool tuned_lookup(uint64_t n, uint64_t k, int layout, int residency, int64_t batch, uw_tune_entry* out,
                   int group) {
   std::lock_guard<std::mutex> lk(g_tune_mu);
@@ -266,6 +277,13 @@ uw_status uw_set_allocator(const uw_allocator* a) {
   } else {
     std::memset(&g_alloc, 0, sizeof(g_alloc));
   }
+  return UW_OK;
+}
+
+uw_status uw_set_kernel_events(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr)) return UW_ERR_INVALID;
+  g_kev_before.store(before, std::memory_order_relaxed);
+  g_kev_after.store(after, std::memory_order_relaxed);
   return UW_OK;
 }
 

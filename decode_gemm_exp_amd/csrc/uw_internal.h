@@ -106,6 +106,11 @@ bool tuned_lookup(uint64_t n, uint64_t k, int layout, int residency, int64_t bat
                   int group = 0);
 constexpr int kTuneGroupMax = 64;
 
+// uw_set_kernel_events: record the caller's events around a main kernel's
+// launch on stream s (nothing when none are set)
+void kernel_event_before(hipStream_t s);
+void kernel_event_after(hipStream_t s);
+
 // Raise a kernel's dynamic LDS limit to `bytes` on the current device, once
 // per (kernel, device, size); thread safe (api.cpp).
 hipError_t allow_dynamic_lds(const void* kernel, int bytes);

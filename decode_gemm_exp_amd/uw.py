@@ -135,6 +135,7 @@ _SIGS = {
     "uw_yardstick": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _sz, _i64, _vp, ctypes.POINTER(ctypes.c_double)]),
     "uw_set_allocator": (ctypes.c_int, [ctypes.POINTER(uw_allocator)]),
     "uw_release_resources": (ctypes.c_int, []),
+    "uw_set_kernel_events": (ctypes.c_int, [_vp, _vp]),
     "uw_set_tuning": (ctypes.c_int, [ctypes.POINTER(uw_tune_entry), ctypes.c_int]),
     "uw_load_tuning": (ctypes.c_int, [ctypes.c_char_p]),
     "uw_clear_tuning": (ctypes.c_int, []),
@@ -472,6 +473,14 @@ def uw_lookup_tuning_grouped(n: int, k: int, layout: int, residency: int, group:
         return None
     _check(st, "uw_lookup_tuning_grouped")
     return _entry_dict(e)
+
+
+def uw_set_kernel_events(before, after) -> None:
+    """before, after: torch.cuda.Event objects already recorded once (so that
+    they exist), or None for both to clear."""
+    b = ctypes.c_void_p(before.cuda_event) if before is not None else None
+    a = ctypes.c_void_p(after.cuda_event) if after is not None else None
+    _check(_lib.uw_set_kernel_events(b, a), "uw_set_kernel_events")
 
 
 def uw_release_resources() -> None:

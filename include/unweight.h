@@ -164,6 +164,19 @@ uw_status uw_set_allocator(const uw_allocator* a);
  * overlap a uw_run_sequence or uw_autotune call. */
 uw_status uw_release_resources(void);
 
+/* Timing aid for profilers and benchmarks.  While set, every GEMM stage call
+ * that runs an MFMA kernel (the LDS-tiled and the register-fed kernels)
+ * records `before` (a hipEvent_t) on the call's stream immediately before
+ * its main kernel's launch and `after` immediately after it, so that the
+ * elapsed time between them is that kernel alone: not the packing of x nor
+ * the reduction of split-K partial sums the call may also run.  A call that
+ * launches the main kernel several times (more than 64 rows on the
+ * register-fed kernels) records around the first and the last launch.  Both
+ * NULL clears (the default); one NULL alone is UW_ERR_INVALID.  Process-wide
+ * and not synchronised with concurrent calls: for a single-threaded timing
+ * loop.  It enqueues nothing by itself and changes no result. */
+uw_status uw_set_kernel_events(void* before, void* after);
+
 /* Compress a device BF16 matrix.  `w_dev` is the stored array: [n][k] for
  * UW_LAYOUT_NK, [k][n] for UW_LAYOUT_KN, given as raw 16-bit patterns.  The
  * stored row length (k for NK, n for KN) must be a multiple of 64 and the

@@ -239,6 +239,14 @@ def test_load_tuning_json(uw, tmp_path):
         uw.uw_clear_tuning()
 
 
+def test_kernel_events_host_rules(uw):
+    """uw_set_kernel_events: both NULL clears, one NULL alone is invalid."""
+    assert uw._lib.uw_set_kernel_events(None, None) == 0
+    assert uw._lib.uw_set_kernel_events(ctypes.c_void_p(16), None) == -1
+    assert uw._lib.uw_set_kernel_events(None, ctypes.c_void_p(16)) == -1
+    assert uw._lib.uw_set_kernel_events(None, None) == 0
+
+
 def test_allocator_and_release_host_rules(uw):
     a = uw.uw_allocator()
     a.alloc = uw.ALLOC_FN(lambda n, c: None)

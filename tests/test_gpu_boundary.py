@@ -217,6 +217,40 @@ def test_grouped_auto_equals_tuned_choice(uw, synth, oracle, clean_table, tmp_pa
     uw.uw_release_resources()
 
 
+@pytest.mark.parametrize("batch,cfg", [(512, None), (16, {"variant": 13}), (100, {"variant": 11}), (48, {"variant": 3, "split_k": 3})])
+def test_kernel_events_bracket_the_kernel(uw, synth, batch, cfg):
+    """uw_set_kernel_events: the output is unchanged, and the events bracket
+    the main kernel alone (a positive time no longer than the whole call's);
+    the 512-row call packs x first, the 100-row register-fed call launches
+    its kernel twice (64 + 36 rows), the 48-row one reduces three K slices."""
+    n, k = 1024, 2048
+    say(f"boundary: kernel events, batch {batch}, cfg {cfg}")
+    w = synth.weights(n, k, 0.02, 0.001, 10, seed=131).to(DEV)
+    m = uw.uw_compress(w, n, k, 0)
+    uw.uw_transcode_palette(m, None)
+    x = synth.activations(batch, k, seed=132).to(DEV)
+    y_ref = matmul(uw, m, 3, x, cfg)
+    stream = torch.cuda.current_stream()
+    y = torch.full((batch, n), float("nan"), dtype=torch.float32, device=DEV)
+    nb = uw.uw_workspace_size_cfg(m, 3, batch, cfg) if cfg else uw.uw_workspace_size(m, 3, batch)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV)
+    ka, kb, ca, cb = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    for e in (ka, kb):
+        e.record(stream)
+    torch.cuda.synchronize()
+    try:
+        uw.uw_set_kernel_events(ka, kb)
+        ca.record(stream)
+        uw.uw_matmul_reconstruct(m, 3, x, y, ws, cfg=cfg, stream=stream)
+        cb.record(stream)
+    finally:
+        uw.uw_set_kernel_events(None, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), y_ref)
+    t_kernel, t_call = ka.elapsed_time(kb), ca.elapsed_time(cb)
+    assert 0.0 < t_kernel <= t_call, (t_kernel, t_call)
+
+
 def test_allocator_hooks(uw, synth, oracle):
     """Sections, scratch and resident indices come from the hooks and go back
     through them; a NULL from the hook is UW_ERR_NOMEM."""
