@@ -223,18 +223,19 @@ extern "C" uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj
           for (int i = 0; i < count; ++i)
             if (proj[i] == p && !feasible(ms[i], pl)) ok = false;
           if (!ok) continue;
-          const int rf = uw::rf_first_variant();                  // the register-fed MFMA kernels
           bool all_nk = true;
           for (int i = 0; i < count; ++i)
             if (proj[i] == p && ms[i]->layout != 0) all_nk = false;
           for (int v = 1; v <= nvar; ++v) {
+            if (!uw::gemm_variant_supported(v, all_nk ? 0 : 1)) continue;   // [N][K]-only kernels
             int bm = 0, bn = 0;
-            if (v > 1 && v < rf) uw::mfma2_tile_dims(v - 2, &bm, &bn);
+            const int tile = uw::gemm_variant_tile(v);
+            if (tile >= 0) uw::mfma2_tile_dims(tile, &bm, &bn);
             if (v == 1 && batch > 32) continue;                 // the VALU kernel only for small batches
             if (bm > 32 && batch < 8) continue;                 // 64- to 256-row tiles from batch 8 on
             if (bm == 32 && (batch < 2 || batch > 128)) continue;   // 32-row tiles for batches 2..128
             if (bm == 512 && batch < 256) continue;                 // the 512-row tile from batch 256
-            if (v >= rf && (!all_nk || batch > 2 * uw::mfma_rf_max_batch())) continue;   // [N][K] only, <= 128 rows
+            if (uw::gemm_variant_is_rf(v) && batch > 2 * uw::mfma_rf_max_batch()) continue;   // <= 128 rows
             Choice c;
             c.pipeline = pl;
             c.variant = v;
@@ -464,7 +465,6 @@ extern "C" uw_status uw_autotune_grouped(const uw_matrix* const* ms, int group, 
   };
 
   const int nvar = uw_variant_count();
-  const int rf = uw::rf_first_variant();
   bool first_entry = true;
   for (int bi = 0; bi < nb; ++bi) {
     const int64_t batch = batches[bi];
@@ -476,12 +476,13 @@ extern "C" uw_status uw_autotune_grouped(const uw_matrix* const* ms, int group, 
       for (int v = 0; v <= nvar; ++v) {
         if (v > 0 && !uw::gemm_variant_supported(v, layout)) continue;
         int bm = 0, bn = 0;
-        if (v > 1 && v < rf) uw::mfma2_tile_dims(v - 2, &bm, &bn);
+        const int tile = uw::gemm_variant_tile(v);
+        if (tile >= 0) uw::mfma2_tile_dims(tile, &bm, &bn);
         if (v == 1 && batch > 32) continue;                     // the same filters as uw_autotune
         if (bm > 32 && batch < 8) continue;
         if (bm == 32 && (batch < 2 || batch > 128)) continue;
         if (bm == 512 && batch < 256) continue;
-        if (v >= rf && (layout != 0 || batch > 2 * uw::mfma_rf_max_batch())) continue;
+        if (uw::gemm_variant_is_rf(v) && batch > 2 * uw::mfma_rf_max_batch()) continue;
         Choice c;
         c.pipeline = pl;
         c.variant = v;

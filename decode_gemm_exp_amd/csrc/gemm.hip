@@ -718,11 +718,25 @@ hipError_t launch_gemv_group(const GemvGroup& g, int fmt, const uint16_t* x, int
 }  // namespace
 
 // Variant numbering seen through uw_kernel_cfg.variant: 1 = VALU GEMV (any
-// batch, eight rows per launch), 2.. = the MFMA tiles of gemm_mfma.hip, then
-// the register-fed MFMA kernels of gemm_rf.hip (stored [N][K] only).
-int rf_first_variant() { return 2 + mfma2_tile_count(); }
+// batch, eight rows per launch), 2.. = the MFMA tiles of gemm_mfma.hip with
+// 64-wide K steps, then the register-fed MFMA kernels of gemm_rf.hip, then
+// the tiles with 128-wide K steps (these two families: stored [N][K] only).
+int rf_first_variant() { return 2 + mfma2_wide_first(); }
+static int wide_first_variant() { return rf_first_variant() + mfma_rf_kinds(); }
 int gemm_variant_count() { return 1 + mfma2_tile_count() + mfma_rf_kinds(); }
 bool gemm_variant_supported(int v, int layout) { return v < rf_first_variant() || layout == 0; }
+bool gemm_variant_is_rf(int v) { return v >= rf_first_variant() && v < wide_first_variant(); }
+int gemm_variant_tile(int v) {
+  if (v >= 2 && v < rf_first_variant()) return v - 2;
+  if (v >= wide_first_variant() && v <= gemm_variant_count()) return mfma2_wide_first() + (v - wide_first_variant());
+  return -1;
+}
+static int tile_variant(int tile) {
+  return tile < mfma2_wide_first() ? 2 + tile : wide_first_variant() + (tile - mfma2_wide_first());
+}
+// the wide-step versions of the 128x128 and 32x128 tiles
+static int wide_tile_128x128() { return mfma2_wide_first() + 1; }
+static int wide_tile_32x128() { return mfma2_wide_first() + 2; }
 
 // Default kernel by batch, from sweeps over the 8B and 70B MLP shapes (every
 // variant, both layouts, palette-direct and BF16 weights):
@@ -766,7 +780,8 @@ static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_c
     if (batch <= 64 && mfma_rf_supported(w, 3) && (int64_t)((w.n + 127) / 128) * 8 >= (int64_t)device_cus() * 7)
       return rf_first_variant() + 3;
     if (batch <= 64) return 2 + 0;
-    if (batch <= 128) return 2 + 1;
+    // 65 to 128 rows: 128x128 tiles, with 128-wide K steps where those pay
+    if (batch <= 128) return mfma2_wide_pays(w, batch, wide_tile_128x128()) ? tile_variant(wide_tile_128x128()) : 2 + 1;
     if (batch <= 512) return 2 + 7;
     const int64_t tiles = (int64_t)((w.n + 255) / 256) * ((batch + 255) / 256);
     return tiles * 8 >= (int64_t)device_cus() * 7 ? big : 2 + 1;
@@ -807,7 +822,7 @@ void describe_gemm(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg,
     }
     return;
   }
-  if (v >= rf_first_variant()) {
+  if (gemm_variant_is_rf(v)) {
     const int kind = v - rf_first_variant();
     const int tiles = kind == 0 ? 2 : kind == 1 ? 4 : kind == 2 ? 1 : 2;   // row tiles per wave
     out->tile_n = 16 * tiles;                                               // rows of W per wave
@@ -818,20 +833,17 @@ void describe_gemm(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg,
                   tiles);
     return;
   }
-  const int tile = v - 2;
-  int bm = 0, bn = 0;
+  const int tile = gemm_variant_tile(v);
+  int bm = 0, bn = 0, waves = 0, wgm = 0, kw = 0;
+  bool xreg = false;
   mfma2_tile_dims(tile, &bm, &bn);
+  mfma2_tile_shape(tile, &waves, &wgm, &xreg, &kw);
   out->tile_m = bm;
   out->tile_n = bn;
-  out->waves = tile >= 7 ? 8 : 4;
-  const int wgm = tile == 5 || tile == 6 ? 1 : tile == 8 ? 8 : 2;
+  out->waves = waves;
   out->k_slices = mfma2_slices(w, batch, tile, cfg ? cfg->split_k : 0);
-  if (tile == 8)
-    std::snprintf(out->kernel, sizeof(out->kernel), "k_mfma2<%d, %d, %d, %d, %d, %d, true>", w.layout, w.fmt, bm,
-                  bn, wgm, out->waves);
-  else
-    std::snprintf(out->kernel, sizeof(out->kernel), "k_mfma2<%d, %d, %d, %d, %d, %d, false>", w.layout, w.fmt, bm,
-                  bn, wgm, out->waves);
+  std::snprintf(out->kernel, sizeof(out->kernel), "k_mfma2<%d, %d, %d, %d, %d, %d, %s, %d>", w.layout, w.fmt, bm, bn,
+                wgm, waves, xreg ? "true" : "false", kw);
 }
 
 // From 8 to 32 rows a group of stored [N][K] matrices of at most 128 M
@@ -911,11 +923,11 @@ size_t gemm_partial_elems(const WeightView& w, int64_t batch, const uw_kernel_cf
     const int64_t rows = batch < kGemvMaxBatch ? batch : kGemvMaxBatch;
     return (size_t)kn_slices(w, (int)rows, cfg) * (size_t)rows * (size_t)w.n;
   }
-  if (v >= rf_first_variant())
+  if (gemm_variant_is_rf(v))
     return w.layout == 0 ? mfma_rf_partial_elems(w, batch, v - rf_first_variant(), cfg ? cfg->split_k : 0,
                                                  device_cus())
                          : 0;
-  return mfma2_partial_elems(w, batch, v - 2, cfg ? cfg->split_k : 0);
+  return mfma2_partial_elems(w, batch, gemm_variant_tile(v), cfg ? cfg->split_k : 0);
 }
 
 // The most any variant needs at this batch (split hint as given).
@@ -965,9 +977,10 @@ static int tile_group_plan(const WeightView* ws, int count, int64_t batch, const
     ntot += ws[i].n;
   }
   wide.n = ntot;
-  if (group_takes_tile32(ws, count, batch, cfg)) return 5;   // the 32x128 tile
+  if (group_takes_tile32(ws, count, batch, cfg))   // the 32x128 tile, with 128-wide K steps where those pay
+    return mfma2_wide_pays(wide, batch, wide_tile_32x128()) ? wide_tile_32x128() : 5;
   const int v = resolve_variant(wide, batch, cfg);
-  if (v >= 2 && v < rf_first_variant()) return v - 2;
+  if (gemm_variant_tile(v) >= 0) return gemm_variant_tile(v);
   // The group as one matrix would take a register-fed kernel, which the
   // default picks by width.  From 33 to 64 rows the group is one launch of
   // 64x128 tiles instead (70B gate+up at 64 rows: 219.7 us against 228.9 us
@@ -975,11 +988,11 @@ static int tile_group_plan(const WeightView* ws, int count, int64_t batch, const
   // matrices alone each take the tile: 63 us against 2 x 38 us).  Up to 32
   // rows it is one launch of the tile a matrix alone would take, if any;
   // matrices that each take the register-fed kernel run one by one.
-  if (v >= rf_first_variant() && !(cfg && cfg->variant > 0)) {
+  if (gemm_variant_is_rf(v) && !(cfg && cfg->variant > 0)) {
     if (batch > 32) return 0;
     for (int i = 0; i < count; ++i) {
-      const int vi = resolve_variant(ws[i], batch, cfg);
-      if (vi >= 2 && vi < rf_first_variant()) return vi - 2;
+      const int ti = gemm_variant_tile(resolve_variant(ws[i], batch, cfg));
+      if (ti >= 0) return ti;
     }
   }
   return -1;
@@ -1050,10 +1063,12 @@ hipError_t launch_gemm(const WeightView& w, const uint16_t* x, int64_t batch, fl
     }
     return hipSuccess;
   }
-  if (v >= rf_first_variant())
+  if (!gemm_variant_supported(v, (int)w.layout)) return hipErrorNotSupported;
+  if (gemm_variant_is_rf(v))
     return launch_mfma_rf(w, x, batch, y, ldy, col0, v - rf_first_variant(), cfg ? cfg->split_k : 0, device_cus(),
                           partial, partial_elems, s);
-  return launch_mfma2(w, x, batch, y, ldy, col0, v - 2, cfg ? cfg->split_k : 0, partial, partial_elems, s);
+  return launch_mfma2(w, x, batch, y, ldy, col0, gemm_variant_tile(v), cfg ? cfg->split_k : 0, partial, partial_elems,
+                      s);
 }
 
 }  // namespace uw

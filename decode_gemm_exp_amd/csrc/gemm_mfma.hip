@@ -37,7 +37,6 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int kBK = 64;
-constexpr int kLDK = kBK + 8;   // bf16 per LDS row: 144 bytes keeps 16-byte alignment, spreads banks
 
 // Raw compressed data of one 16-weight chunk, as loaded from HBM.
 struct Raw {
@@ -132,10 +131,13 @@ __device__ __forceinline__ void block_tile(int b, int ntiles, int mtiles, int& n
   }
 }
 
-template <int LAYOUT, int BN>
-constexpr int w_ld() { return LAYOUT == 0 ? kLDK : BN + 16; }   // KN rows: BN + 16 keeps transposing reads conflict-light
-template <int LAYOUT, int BN>
-constexpr int w_tile_elems() { return LAYOUT == 0 ? BN * kLDK : kBK * (BN + 16); }
+// bf16 per LDS row of an x tile or an [N][K] weight tile for a K step of
+// 64 KW: 144 or 272 bytes keeps 16-byte alignment and spreads banks
+constexpr int ld_k(int kw) { return kBK * kw + 8; }
+template <int LAYOUT, int BN, int KW>
+constexpr int w_ld() { return LAYOUT == 0 ? ld_k(KW) : BN + 16; }   // KN rows: BN + 16 keeps transposing reads conflict-light
+template <int LAYOUT, int BN, int KW>
+constexpr int w_tile_elems() { return LAYOUT == 0 ? BN * ld_k(KW) : kBK * (BN + 16); }
 
 // x [B][K] -> the A fragments of v_mfma_f32_32x32x16_bf16 in the lanes'
 // read order, for the tiles that keep x in registers: fragment (R, S) (rows
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(256) void k_pack_xa(const uint16_t* __restrict__ x,
 // rebuilt weight tile is shared through LDS.  With BM = 512 every weight is
 // rebuilt once per 512 batch rows (the 256-row tiles rebuild it once per 256),
 // LDS carries a third less per MFMA, and the LDS tile is small.
-template <int LAYOUT, int FMT, int BM, int BN, int WGM, int NW = 4, bool XREG = false>
+template <int LAYOUT, int FMT, int BM, int BN, int WGM, int NW = 4, bool XREG = false, int KW = 1>
 __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_t* __restrict__ x, int B,
                                                    float* __restrict__ y, int64_t ldy, int64_t kslice,
                                                    float* __restrict__ part, int64_t pld, int mtiles) {
@@ -179,10 +181,14 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
   constexpr int WGN = NW / WGM;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int XC = XREG ? 0 : BM * 8 / NT;   // 16-byte x chunks per thread per step (LDS-staged x)
-  constexpr int WC = BN * 4 / NT;              // 16-weight chunks per thread per step
-  constexpr int LDW = w_ld<LAYOUT, BN>();
-  constexpr int XS = XREG ? 0 : BM * kLDK, WS = w_tile_elems<LAYOUT, BN>();
+  constexpr int BK = kBK * KW;                   // k per step
+  constexpr int LDK = ld_k(KW);
+  constexpr int XPR = BK / 8, WPR = BK / 16;     // x chunks per x row, weight chunks per [N][K] row
+  constexpr int XC = XREG ? 0 : BM * XPR / NT;   // 16-byte x chunks per thread per step (LDS-staged x)
+  constexpr int WC = BN * 4 * KW / NT;           // 16-weight chunks per thread per step
+  constexpr int LDW = w_ld<LAYOUT, BN, KW>();
+  constexpr int XS = XREG ? 0 : BM * LDK, WS = w_tile_elems<LAYOUT, BN, KW>();
+  static_assert(KW == 1 || (LAYOUT == 0 && !XREG), "wide K steps: [N][K] tiles with x in LDS");
   constexpr int kValuPerMfma = FMT == kFmtBf16 ? 1 : 4;
   static_assert(TM >= 1 && TN >= 1 && (XREG || XC >= 1) && WC >= 1, "tile too small");
   static_assert(!XREG || WGN == 1, "x in registers: a wave owns its rows across the tile width");
@@ -200,7 +206,7 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
   const int64_t n0 = (int64_t)nt * BN, m0 = (int64_t)mt * BM;
   const int64_t kb = (int64_t)blockIdx.z * kslice;
   const int64_t ke = kb + kslice < K ? kb + kslice : K;
-  const int steps = (int)((ke - kb + kBK - 1) / kBK);
+  const int steps = (int)((ke - kb + BK - 1) / BK);
 
   // Resources over what the block reads; offsets are 32-bit and advance by a
   // constant per step.  [N][K]: rows [n0, min(n0 + BN, N)) from column kb
@@ -235,35 +241,35 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
   const __amdgpu_buffer_rsrc_t rx =
       XREG ? rsrc(x, (uint64_t)mtiles * (BM / 32) * (uint64_t)SK * 1024u) : rsrc(x, (uint64_t)B * (uint64_t)K * 2);
   constexpr int QN = BN / 16;
-  // per step: a stored [N][K] chunk moves 64 columns on, a [K][N] chunk 64 rows
-  const uint32_t wadv = LAYOUT == 0 ? (uint32_t)kBK : (uint32_t)kBK * (uint32_t)N;
+  // per step: a stored [N][K] chunk moves BK columns on, a [K][N] chunk 64 rows
+  const uint32_t wadv = LAYOUT == 0 ? (uint32_t)BK : (uint32_t)kBK * (uint32_t)N;
 
-  // chunk i of this thread (c = tid + i NT): [N][K] -> row c / 4, columns
-  // 16 (c % 4) of the step; [K][N] -> k row c / QN, columns 16 (c % QN).  The
-  // chunks of one thread differ only in their row, by NT / 4 (or NT / QN)
-  // rows, so one offset register serves all of them: wo = element offset of
+  // chunk i of this thread (c = tid + i NT): [N][K] -> row c / WPR, columns
+  // 16 (c % WPR) of the step; [K][N] -> k row c / QN, columns 16 (c % QN).
+  // The chunks of one thread differ only in their row, by NT / WPR (or
+  // NT / QN) rows, so one offset register serves all of them: wo = element offset of
   // chunk 0 in the step whose data loads next, chunk i at wo + i wstride.
   // The column within the row is the same for every chunk and every step
   // (steps move by multiples of 64 elements): whi = the chunk's 8 index bytes
   // are the upper half of their aligned 16, wsub = its offset in its group.
-  static_assert(NT % 16 == 0 && NT % QN == 0, "chunk columns must repeat across a thread's chunks");
-  const uint32_t wstride = LAYOUT == 0 ? (uint32_t)(NT / 4) * (uint32_t)K : (uint32_t)(NT / QN) * (uint32_t)N;
+  static_assert(NT % WPR == 0 && NT % XPR == 0 && NT % QN == 0, "chunk columns must repeat across a thread's chunks");
+  const uint32_t wstride = LAYOUT == 0 ? (uint32_t)(NT / WPR) * (uint32_t)K : (uint32_t)(NT / QN) * (uint32_t)N;
   uint32_t wo;
   int wkr;
   if constexpr (LAYOUT == 0) {
-    wo = (uint32_t)(tid >> 2) * (uint32_t)K + 16u * (uint32_t)(tid & 3);
-    wkr = 0;
+    wo = ((uint32_t)tid / WPR) * (uint32_t)K + 16u * ((uint32_t)tid % WPR);
+    wkr = 16 * (int)((uint32_t)tid % WPR);   // the chunks' column in the step
   } else {
     wo = (uint32_t)(tid / QN) * (uint32_t)N + 16u * (uint32_t)(tid % QN);
     wkr = tid / QN;
   }
   const uint32_t wsub = (wb32 + wo) & 48u;
   const bool whi = (wsub & 16u) != 0;
-  // x chunk i: row m0 + c / 8, columns 8 (c % 8) of the step, at xo + i
+  // x chunk i: row m0 + c / XPR, columns 8 (c % XPR) of the step, at xo + i
   // xstride bytes; rows past the batch read zero (never stored), columns past
   // K read the next row's values (finite; a K tail meets zeroed weight rows)
-  const uint32_t xstride = (uint32_t)(NT / 8) * (uint32_t)K * 2u;
-  uint32_t xo = (uint32_t)((uint64_t)(m0 + (tid >> 3)) * (uint64_t)K + (uint64_t)kb + 8u * (uint32_t)(tid & 7)) * 2u;
+  const uint32_t xstride = (uint32_t)(NT / XPR) * (uint32_t)K * 2u;
+  uint32_t xo = (uint32_t)((uint64_t)(m0 + (unsigned)tid / XPR) * (uint64_t)K + (uint64_t)kb + 8u * ((uint32_t)tid % XPR)) * 2u;
   int kstep = 0;   // k of the step whose data loads next, from kb
   const int klen = (int)(ke - kb);
   // XREG: this lane's piece of the packed A fragment (row fragment 0, k slice
@@ -327,18 +333,20 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
         wr[i].v = bload16w<LAYOUT == 1>(rvx, verb ? rank * 64u + wsub : kPastEnd);
         wverb[i] = verb;
       }
-      // zeroed when rebuilt: only [K][N] rows past the slice.  Chunks past N
-      // only feed output columns that are never stored.
+      // zeroed when rebuilt: [K][N] rows past the slice, and with wide steps
+      // [N][K] columns past the slice (a slice of an odd number of 64-wide
+      // steps ends half way through its last step).  Chunks past N only feed
+      // output columns that are never stored.
       if constexpr (LAYOUT == 0) {
-        wval[i] = true;
+        wval[i] = KW == 1 || kstep + wkr < klen;
       } else {
         wval[i] = kstep + wkr + i * (NT / QN) < klen;
       }
     }
     if (part == 3) {   // the step's last part: every chunk of the step has loaded
-      xo += 2u * kBK;
+      xo += 2u * BK;
       wo += wadv;
-      kstep += kBK;
+      kstep += BK;
     }
   };
   // registers of a step -> LDS buffer (x as is, weights rebuilt)
@@ -347,7 +355,7 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
     for (int i = 0; i < XC; ++i) {
       if (!in_part(i, XC, part)) continue;
       const int c = tid + i * NT;
-      *reinterpret_cast<uint4*>(&xs[(c >> 3) * kLDK + (c & 7) * 8]) = xr[i];
+      *reinterpret_cast<uint4*>(&xs[((uint32_t)c / XPR) * LDK + ((uint32_t)c % XPR) * 8]) = xr[i];
     }
 #pragma unroll
     for (int i = 0; i < WC; ++i) {
@@ -357,7 +365,7 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
       const int c = tid + i * NT;
       uint4* d;
       if constexpr (LAYOUT == 0) {
-        d = reinterpret_cast<uint4*>(&ws[(c >> 2) * kLDK + (c & 3) * 16]);
+        d = reinterpret_cast<uint4*>(&ws[((uint32_t)c / WPR) * LDK + ((uint32_t)c % WPR) * 16]);
       } else {
         d = reinterpret_cast<uint4*>(&ws[(c / QN) * LDW + (c % QN) * 16]);
       }
@@ -383,14 +391,14 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int row = wm * WM + i * 32 + (lane & 31);
-        a[i] = *reinterpret_cast<const bf16x8*>(&xs[row * kLDK + kk + 8 * (lane >> 5)]);
+        a[i] = *reinterpret_cast<const bf16x8*>(&xs[row * LDK + kk + 8 * (lane >> 5)]);
       }
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       if constexpr (LAYOUT == 0) {
         const int col = wn * WN + j * 32 + (lane & 31);
-        b[j] = *reinterpret_cast<const bf16x8*>(&ws[col * kLDK + kk + 8 * (lane >> 5)]);
+        b[j] = *reinterpret_cast<const bf16x8*>(&ws[col * LDK + kk + 8 * (lane >> 5)]);
       } else {
         b[j] = b_frag_kmajor(ws, LDW, kk, wn * WN + j * 32, lane);
       }
@@ -402,8 +410,13 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(XREG ? xa[sl][i] : a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (XREG) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[sl][i], b[j], acc[i][j], 0, 0, 0);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+      }
     if constexpr (XREG) {
       load_xa(sl);
       if (sl == 3) xao += 4u * 1024u;
@@ -451,24 +464,32 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
       // ask the scheduler to alternate one MFMA with a few VALU operations of
       // the rebuild, so the vector ALU works while the matrix core runs
 #pragma unroll
-      for (int q = 0; q < TM * TN; ++q) {
+      for (int q = 0; q < KW * TM * TN; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // VALU
       }
       __builtin_amdgcn_sched_barrier(0);
     };
+    // k slice sl runs from fragment set sl % 2, which then reads slice
+    // sl + 2; part p follows slice KW (p + 1) - 1
     read_frags(xs_c, ws_c, 0, fa0, fb0);
     read_frags(xs_c, ws_c, 16, fa1, fb1);
-    mfma_set(0, fa0, fb0);
-    rest(0);
-    read_frags(xs_c, ws_c, 32, fa0, fb0);
-    mfma_set(1, fa1, fb1);
-    rest(1);
-    read_frags(xs_c, ws_c, 48, fa1, fb1);
-    mfma_set(2, fa0, fb0);
-    rest(2);
-    mfma_set(3, fa1, fb1);
-    rest(3);
+#pragma unroll
+    for (int sl = 0; sl < 4 * KW; ++sl) {
+      if (sl % 2 == 0) {
+        mfma_set(sl, fa0, fb0);
+      } else {
+        mfma_set(sl, fa1, fb1);
+      }
+      if (sl % KW == KW - 1) rest(sl / KW);
+      if (sl + 2 < 4 * KW) {
+        if (sl % 2 == 0) {
+          read_frags(xs_c, ws_c, 16 * (sl + 2), fa0, fb0);
+        } else {
+          read_frags(xs_c, ws_c, 16 * (sl + 2), fa1, fb1);
+        }
+      }
+    }
   };
   // XREG: drain the prologue's loads here, once.  Otherwise the compiler's
   // wait-count merge of the loop entry (where the last loads issued are the
@@ -498,38 +519,72 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
 
 typedef void (*Mfma2Fn)(Mfma2Group, const uint16_t*, int, float*, int64_t, int64_t, float*, int64_t, int);
 
+// Tiles of the big-tile kernel: BM x BN, waves in a WGM x (waves / WGM) grid.
+struct Tile2 {
+  int bm, bn, waves, wgm;
+  bool xreg;   // x in registers, only the weight tile in LDS (single rebuild per 512 rows)
+  int nk_kw;   // K step of 64 nk_kw; 2 only for stored [N][K] weights
+};
+// 32-row tiles (one MFMA row tile, four waves side by side) are for small
+// batches; then 256x256 with eight waves (two per SIMD); then the
+// single-rebuild tile, 512 rows x 128 columns, eight waves of 64 rows.  The
+// last four are the 64x128, 128x128, 32x128 and 32x256 tiles with 128-wide K
+// steps for stored [N][K] weights: each step reads whole 128-byte lines of
+// sign+mantissa bytes per row (a 64-wide step reads half a line per row and
+// the other half a step later), for twice the LDS, so one block per CU.
+constexpr Tile2 kTiles2[] = {
+    {64, 128, 4, 2, false, 1},  {128, 128, 4, 2, false, 1}, {128, 256, 4, 2, false, 1}, {256, 128, 4, 2, false, 1},
+    {256, 256, 4, 2, false, 1}, {32, 128, 4, 1, false, 1},  {32, 256, 4, 1, false, 1},  {256, 256, 8, 2, false, 1},
+    {512, 128, 8, 8, true, 1},  {64, 128, 4, 2, false, 2},  {128, 128, 4, 2, false, 2}, {32, 128, 4, 1, false, 2},
+    {32, 256, 4, 1, false, 2}};
+constexpr int kTileCount = (int)(sizeof(kTiles2) / sizeof(kTiles2[0]));
+constexpr int kWideFirst = 9;   // the first tile with 128-wide K steps
+constexpr int tile_kw(int tile) { return kTiles2[tile].nk_kw; }
+
+// the kernel of tile T for layout L (none: a wide-step tile for [K][N])
+template <int L, int F, int T>
+Mfma2Fn inst() {
+  constexpr Tile2 t = kTiles2[T];
+  if constexpr (L == 1 && t.nk_kw > 1) {
+    return nullptr;
+  } else {
+    return k_mfma2<L, F, t.bm, t.bn, t.wgm, t.waves, t.xreg, t.nk_kw>;
+  }
+}
+
 template <int L, int F>
 Mfma2Fn pick(int tile) {
+  static_assert(kTileCount == 13, "one case per tile");
   switch (tile) {
-    case 0: return k_mfma2<L, F, 64, 128, 2>;
-    case 1: return k_mfma2<L, F, 128, 128, 2>;
-    case 2: return k_mfma2<L, F, 128, 256, 2>;
-    case 3: return k_mfma2<L, F, 256, 128, 2>;
-    case 4: return k_mfma2<L, F, 256, 256, 2>;
-    case 5: return k_mfma2<L, F, 32, 128, 1>;
-    case 6: return k_mfma2<L, F, 32, 256, 1>;
-    case 7: return k_mfma2<L, F, 256, 256, 2, 8>;
-    default: return k_mfma2<L, F, 512, 128, 8, 8, true>;
+    case 0: return inst<L, F, 0>();
+    case 1: return inst<L, F, 1>();
+    case 2: return inst<L, F, 2>();
+    case 3: return inst<L, F, 3>();
+    case 4: return inst<L, F, 4>();
+    case 5: return inst<L, F, 5>();
+    case 6: return inst<L, F, 6>();
+    case 7: return inst<L, F, 7>();
+    case 8: return inst<L, F, 8>();
+    case 9: return inst<L, F, 9>();
+    case 10: return inst<L, F, 10>();
+    case 11: return inst<L, F, 11>();
+    case 12: return inst<L, F, 12>();
+    default: return nullptr;
   }
 }
 
 }  // namespace
-
-// Tiles of the big-tile kernel: {BM, BN}.
-struct Tile2 {
-  int bm, bn, waves;
-  bool xreg;   // x in registers, only the weight tile in LDS (single rebuild per 512 rows)
-};
-// 32-row tiles (one MFMA row tile, four waves side by side) are for small
-// batches; then 256x256 with eight waves (two per SIMD); the last is the
-// single-rebuild tile, 512 rows x 128 columns, eight waves of 64 rows
-static const Tile2 kTiles2[] = {{64, 128, 4, false},  {128, 128, 4, false}, {128, 256, 4, false},
-                                {256, 128, 4, false}, {256, 256, 4, false}, {32, 128, 4, false},
-                                {32, 256, 4, false},  {256, 256, 8, false}, {512, 128, 8, true}};
-int mfma2_tile_count() { return (int)(sizeof(kTiles2) / sizeof(kTiles2[0])); }
+int mfma2_tile_count() { return kTileCount; }
+int mfma2_wide_first() { return kWideFirst; }
 void mfma2_tile_dims(int tile, int* bm, int* bn) {
   *bm = kTiles2[tile].bm;
   *bn = kTiles2[tile].bn;
+}
+void mfma2_tile_shape(int tile, int* waves, int* wgm, bool* xreg, int* kw) {
+  *waves = kTiles2[tile].waves;
+  *wgm = kTiles2[tile].wgm;
+  *xreg = kTiles2[tile].xreg;
+  *kw = kTiles2[tile].nk_kw;
 }
 
 // K slices (powers of two, each slice >= 8 steps): until the grid covers the
@@ -544,8 +599,9 @@ void mfma2_tile_dims(int tile, int* bm, int* bn) {
 // slices, 187 us with none).
 // LDS of one block: x and weight tiles, double buffered
 size_t mfma2_lds_bytes(int layout, const Tile2& t) {
-  const size_t wtile = layout == 0 ? (size_t)t.bn * kLDK : (size_t)kBK * (size_t)(t.bn + 16);
-  return 2 * ((t.xreg ? 0 : (size_t)t.bm * kLDK) + wtile) * sizeof(uint16_t);
+  const size_t ldk = (size_t)ld_k(t.nk_kw);
+  const size_t wtile = layout == 0 ? (size_t)t.bn * ldk : (size_t)kBK * (size_t)(t.bn + 16);
+  return 2 * ((t.xreg ? 0 : (size_t)t.bm * ldk) + wtile) * sizeof(uint16_t);
 }
 // blocks a CU holds at once: by LDS, and one for the eight-wave tiles (their
 // registers fill the SIMDs at two waves each)
@@ -569,7 +625,8 @@ int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint) {
   // 8B q+k+v 96 tiles: 4 slices 91 us, 2 slices 71 us; 70B q+k+v 160 tiles:
   // 2 slices 239 us, none 198 us)
   const int64_t per_cu = mfma2_blocks_per_cu((int)w.layout, t);
-  const bool one_round = batch <= 64 || t.bm >= 256;
+  // the wide-step tiles (one block per CU) never queue a second round
+  const bool one_round = batch <= 64 || t.bm >= 256 || t.nk_kw > 1;
   const int64_t hold = one_round ? cus * (per_cu > 0 ? per_cu : 1) : INT64_MAX;
   int s = split_hint > 0 ? split_hint : 1;
   if (split_hint <= 0)
@@ -594,6 +651,21 @@ int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint) {
   const int64_t steps = ((int64_t)w.k + 63) / 64;
   if (s > steps) s = (int)steps;
   return s;
+}
+
+// Whether a tile with 128-wide K steps is the default in place of its
+// 64-wide version: its grid at one block per CU, K split as above, still
+// covers seven eighths of the CUs, and every block's K range is at least
+// 2048 (16 steps), so its two-step prologue stays small against the loop.
+// Where either fails the 64-wide tile, two or three blocks per CU, is faster.
+bool mfma2_wide_pays(const WeightView& w, int64_t batch, int tile) {
+  const Tile2 t = kTiles2[tile];
+  if (w.layout != 0 || t.nk_kw < 2) return false;
+  const int64_t blocks = ((int64_t)w.n + t.bn - 1) / t.bn * ((batch + t.bm - 1) / t.bm);
+  const int s = mfma2_slices(w, batch, tile, 0);
+  const int64_t bk = 64 * (int64_t)t.nk_kw;
+  const int64_t kslice = (((int64_t)w.k + bk - 1) / bk + s - 1) / s * bk;
+  return blocks * s * 8 >= (int64_t)device_cus() * 7 && kslice >= 2048;
 }
 
 // bytes of x packed into A fragments for a tile that keeps x in registers
@@ -634,8 +706,9 @@ static hipError_t launch_group(Mfma2Group grp, const uint16_t* x, int64_t batch,
   wide.n = ntot;
   wide.fmt = fmt;
   const int slices = mfma2_slices(wide, batch, tile, split_hint);
-  const int64_t steps = ((int64_t)w0.k + 63) / 64;
-  const int64_t kslice = ((steps + slices - 1) / slices) * 64;
+  const int64_t bk = 64 * (int64_t)t.nk_kw;   // k per step
+  const int64_t steps = ((int64_t)w0.k + bk - 1) / bk;
+  const int64_t kslice = ((steps + slices - 1) / slices) * bk;
   // every buffer resource the kernel builds spans at most kRecMax bytes:
   // x, a [N][K] block's rows, a [K][N] slice's rows, the verbatim section
   if ((uint64_t)batch * w0.k * 2 > kRecMax) return hipErrorNotSupported;
@@ -661,6 +734,7 @@ static hipError_t launch_group(Mfma2Group grp, const uint16_t* x, int64_t batch,
     xk = reinterpret_cast<const uint16_t*>(packed);
   }
   Mfma2Fn f;
+  if (t.nk_kw > 1 && w0.layout != 0) return hipErrorNotSupported;
   if (w0.layout == 0) {
     f = fmt == kFmtBf16 ? pick<0, kFmtBf16>(tile) : fmt == kFmtExp ? pick<0, kFmtExp>(tile)
         : fmt == kFmtPal ? pick<0, kFmtPal>(tile) : pick<0, kFmtPalRun>(tile);
@@ -668,6 +742,7 @@ static hipError_t launch_group(Mfma2Group grp, const uint16_t* x, int64_t batch,
     f = fmt == kFmtBf16 ? pick<1, kFmtBf16>(tile) : fmt == kFmtExp ? pick<1, kFmtExp>(tile)
         : fmt == kFmtPal ? pick<1, kFmtPal>(tile) : pick<1, kFmtPalRun>(tile);
   }
+  if (f == nullptr) return hipErrorNotSupported;
   const size_t lds = mfma2_lds_bytes((int)w0.layout, t);
   {
     hipError_t e = allow_dynamic_lds((const void*)f, (int)lds);

@@ -213,10 +213,27 @@ def rf_variants(uw):
             if uw.uw_plan_gemm(m, 0, 16, {"variant": v})["kernel"].startswith("k_mfma_rf")]
 
 
+def wide_variants(uw):
+    """The LDS tiles with 128-wide K steps (stored [N][K]): the last template
+    argument of the kernel each variant plans is the K step in units of 64."""
+    w = torch.zeros(64, 128, dtype=torch.bfloat16, device=DEV)
+    m = uw.uw_compress(w, 64, 128, 0)
+    out = []
+    for v in range(1, uw.variant_count() + 1):
+        kern = uw.uw_plan_gemm(m, 0, 16, {"variant": v})["kernel"]
+        if kern.startswith("k_mfma2<") and kern.endswith(", 2>"):
+            out.append(v)
+    assert len(out) == 4, out
+    return out
+
+
 # the small tiles (64x128, 32x128, 32x256) over K slices of 1, 2, 5 and an
 # odd or even number of steps, forced K splits that leave uneven slices,
 # both layouts, a ragged batch (and a ragged N where the layout allows it:
-# stored [K][N] keeps N a multiple of 64)
+# stored [K][N] keeps N a multiple of 64); for stored [N][K] also the tiles
+# with 128-wide K steps, where K = 64, 320 and 2112 end half way through a
+# step and the forced splits of 2112 (17 steps) leave a half-step slice end
+# and, at 7 slices, an empty last slice
 @pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("k", [64, 128, 320, 2112])
 def test_gemm_small_tiles_step_counts(uw, synth, oracle, layout, k):
@@ -229,7 +246,7 @@ def test_gemm_small_tiles_step_counts(uw, synth, oracle, layout, k):
     uw.uw_transcode_palette(m, None)
     w_np, x_np = bits(w), bits(x)
     splits = (1, 3, 7) if k == 2112 else (1,)
-    for v in (2 + 0, 2 + 5, 2 + 6):
+    for v in (2 + 0, 2 + 5, 2 + 6) + (tuple(wide_variants(uw)) if layout == 0 else ()):
         for sk in splits:
             for p in (0, 1, 3):
                 y = run_pipeline(uw, m, p, x, cfg={"variant": v, "split_k": sk})
@@ -253,8 +270,12 @@ def test_gemm_mid_batch_split(uw, synth, oracle, layout, batch):
     for p in range(4):
         y = run_pipeline(uw, m, p, x)
         check_gemm(oracle, y, x_np, w_np, layout, what=f"pipeline {p}")
-    # ... and the single-rebuild 512x128 tile (x in registers), split and not
-    for v, sk in ((2 + 7, 3), (2 + 4, 5), (2 + 8, 3), (2 + 8, 1)):
+    # ... and the single-rebuild 512x128 tile (x in registers), split and not,
+    # and ([N][K]) the 128x128 tile with 128-wide K steps
+    cases = ((2 + 7, 3), (2 + 4, 5), (2 + 8, 3), (2 + 8, 1))
+    if layout == 0:
+        cases += tuple((v, sk) for v in wide_variants(uw)[1:2] for sk in (1, 3))
+    for v, sk in cases:
         for p in (0, 3):
             y = run_pipeline(uw, m, p, x, cfg={"variant": v, "split_k": sk})
             check_gemm(oracle, y, x_np, w_np, layout, what=f"pipeline {p} variant {v} split {sk}")
