@@ -734,9 +734,10 @@ int gemm_variant_tile(int v) {
 static int tile_variant(int tile) {
   return tile < mfma2_wide_first() ? 2 + tile : wide_first_variant() + (tile - mfma2_wide_first());
 }
-// the wide-step versions of the 128x128 and 32x128 tiles
+// the wide-step versions of the 128x128, 32x128 and single-rebuild tiles
 static int wide_tile_128x128() { return mfma2_wide_first() + 1; }
 static int wide_tile_32x128() { return mfma2_wide_first() + 2; }
+static int wide_tile_xreg() { return mfma2_wide_first() + 4; }
 
 // Default kernel by batch, from sweeps over the 8B and 70B MLP shapes (every
 // variant, both layouts, palette-direct and BF16 weights):
@@ -766,7 +767,12 @@ static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_c
   // pads no more rows than 256-row tiles (an even number of 256-row tiles):
   // 70B at 1024 rows, palette-direct gate 507 -> 477 us, down 502 -> 457 us,
   // exponent gate 471 -> 435 us; at 512 rows palette-direct 267 -> 244 us
-  if (batch > 256 && ((batch + 255) / 256) % 2 == 0) return 2 + 8;
+  // With stored [N][K] byte-format weights its 128-wide K steps read whole
+  // lines per row (70B gate, palette-direct: 512 rows 240.5 -> 225.2 us,
+  // 768 rows 430.4 -> 415.6, 1024 rows 449.3 -> 434.7, 2048 rows 879.9 ->
+  // 851.4; exponent weights 1 % faster), identical results.
+  if (batch > 256 && ((batch + 255) / 256) % 2 == 0)
+    return w.layout == 0 && w.fmt != kFmtBf16 ? tile_variant(wide_tile_xreg()) : 2 + 8;
   if (w.layout == 0) {
     if (batch <= 4) return 1;
     if (batch <= 32 && mfma_rf_supported(w, 2) && (int64_t)((w.n + 63) / 64) * 8 >= (int64_t)device_cus() * 7)

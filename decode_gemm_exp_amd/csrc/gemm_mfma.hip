@@ -188,7 +188,7 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
   constexpr int WC = BN * 4 * KW / NT;           // 16-weight chunks per thread per step
   constexpr int LDW = w_ld<LAYOUT, BN, KW>();
   constexpr int XS = XREG ? 0 : BM * LDK, WS = w_tile_elems<LAYOUT, BN, KW>();
-  static_assert(KW == 1 || (LAYOUT == 0 && !XREG), "wide K steps: [N][K] tiles with x in LDS");
+  static_assert(KW == 1 || LAYOUT == 0, "wide K steps: [N][K] tiles only");
   constexpr int kValuPerMfma = FMT == kFmtBf16 ? 1 : 4;
   static_assert(TM >= 1 && TN >= 1 && (XREG || XC >= 1) && WC >= 1, "tile too small");
   static_assert(!XREG || WGN == 1, "x in registers: a wave owns its rows across the tile width");
@@ -272,9 +272,10 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
   uint32_t xo = (uint32_t)((uint64_t)(m0 + (unsigned)tid / XPR) * (uint64_t)K + (uint64_t)kb + 8u * ((uint32_t)tid % XPR)) * 2u;
   int kstep = 0;   // k of the step whose data loads next, from kb
   const int klen = (int)(ke - kb);
-  // XREG: this lane's piece of the packed A fragment (row fragment 0, k slice
-  // 0) of the step whose x loads next; row fragment i is SK fragments on,
-  // slice s one fragment (1 KB), a step four
+  // XREG: this lane's piece of the packed A fragment (row fragment 0) of the
+  // next four k slices to load; row fragment i is SK fragments on, slice s
+  // one fragment (1 KB).  The registers hold four slices, a ring: slice s
+  // runs from xa[s % 4], which then loads slice s + 4.
   uint32_t xao = 0;
   if constexpr (XREG)
     xao = (uint32_t)((((uint64_t)(m0 + wm * WM) / 32) * (uint64_t)SK + (uint64_t)kb / 16) * 1024u) +
@@ -405,21 +406,21 @@ __global__ __launch_bounds__(64 * NW) void k_mfma2(Mfma2Group grp, const uint16_
     }
   };
   // the MFMAs of k slice sl; XREG takes A from the slice's registers, which
-  // then load the next step's slice
+  // then load the slice four on
   auto mfma_set = [&](int sl, const bf16x8 (&a)[TM], const bf16x8 (&b)[TN]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         if constexpr (XREG) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[sl][i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[sl % 4][i], b[j], acc[i][j], 0, 0, 0);
         } else {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
       }
     if constexpr (XREG) {
-      load_xa(sl);
-      if (sl == 3) xao += 4u * 1024u;
+      load_xa(sl % 4);
+      if (sl % 4 == 3) xao += 4u * 1024u;
     }
   };
 
@@ -528,15 +529,16 @@ struct Tile2 {
 // 32-row tiles (one MFMA row tile, four waves side by side) are for small
 // batches; then 256x256 with eight waves (two per SIMD); then the
 // single-rebuild tile, 512 rows x 128 columns, eight waves of 64 rows.  The
-// last four are the 64x128, 128x128, 32x128 and 32x256 tiles with 128-wide K
-// steps for stored [N][K] weights: each step reads whole 128-byte lines of
-// sign+mantissa bytes per row (a 64-wide step reads half a line per row and
-// the other half a step later), for twice the LDS, so one block per CU.
+// last five are the 64x128, 128x128, 32x128, 32x256 and single-rebuild
+// tiles with 128-wide K steps for stored [N][K] weights: each step reads
+// whole 128-byte lines of sign+mantissa bytes per row (a 64-wide step reads
+// half a line per row and the other half a step later), for twice the LDS
+// (one block per CU for the four-wave tiles).
 constexpr Tile2 kTiles2[] = {
     {64, 128, 4, 2, false, 1},  {128, 128, 4, 2, false, 1}, {128, 256, 4, 2, false, 1}, {256, 128, 4, 2, false, 1},
     {256, 256, 4, 2, false, 1}, {32, 128, 4, 1, false, 1},  {32, 256, 4, 1, false, 1},  {256, 256, 8, 2, false, 1},
     {512, 128, 8, 8, true, 1},  {64, 128, 4, 2, false, 2},  {128, 128, 4, 2, false, 2}, {32, 128, 4, 1, false, 2},
-    {32, 256, 4, 1, false, 2}};
+    {32, 256, 4, 1, false, 2},  {512, 128, 8, 8, true, 2}};
 constexpr int kTileCount = (int)(sizeof(kTiles2) / sizeof(kTiles2[0]));
 constexpr int kWideFirst = 9;   // the first tile with 128-wide K steps
 constexpr int tile_kw(int tile) { return kTiles2[tile].nk_kw; }
@@ -554,7 +556,7 @@ Mfma2Fn inst() {
 
 template <int L, int F>
 Mfma2Fn pick(int tile) {
-  static_assert(kTileCount == 13, "one case per tile");
+  static_assert(kTileCount == 14, "one case per tile");
   switch (tile) {
     case 0: return inst<L, F, 0>();
     case 1: return inst<L, F, 1>();
@@ -569,6 +571,7 @@ Mfma2Fn pick(int tile) {
     case 10: return inst<L, F, 10>();
     case 11: return inst<L, F, 11>();
     case 12: return inst<L, F, 12>();
+    case 13: return inst<L, F, 13>();
     default: return nullptr;
   }
 }
@@ -658,9 +661,10 @@ int mfma2_slices(const WeightView& w, int64_t batch, int tile, int split_hint) {
 // covers seven eighths of the CUs, and every block's K range is at least
 // 2048 (16 steps), so its two-step prologue stays small against the loop.
 // Where either fails the 64-wide tile, two or three blocks per CU, is faster.
+// BF16 weights (two bytes each) already read whole lines with 64-wide steps.
 bool mfma2_wide_pays(const WeightView& w, int64_t batch, int tile) {
   const Tile2 t = kTiles2[tile];
-  if (w.layout != 0 || t.nk_kw < 2) return false;
+  if (w.layout != 0 || t.nk_kw < 2 || w.fmt == kFmtBf16) return false;
   const int64_t blocks = ((int64_t)w.n + t.bn - 1) / t.bn * ((batch + t.bm - 1) / t.bm);
   const int s = mfma2_slices(w, batch, tile, 0);
   const int64_t bk = 64 * (int64_t)t.nk_kw;
