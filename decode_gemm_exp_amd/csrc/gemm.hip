@@ -738,6 +738,7 @@ static int tile_variant(int tile) {
 static int wide_tile_128x128() { return mfma2_wide_first() + 1; }
 static int wide_tile_32x128() { return mfma2_wide_first() + 2; }
 static int wide_tile_xreg() { return mfma2_wide_first() + 4; }
+static int wide_tile_xreg256() { return mfma2_wide_first() + 5; }
 
 // Default kernel by batch, from sweeps over the 8B and 70B MLP shapes (every
 // variant, both layouts, palette-direct and BF16 weights):
@@ -788,6 +789,11 @@ static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_c
     if (batch <= 64) return 2 + 0;
     // 65 to 128 rows: 128x128 tiles, with 128-wide K steps where those pay
     if (batch <= 128) return mfma2_wide_pays(w, batch, wide_tile_128x128()) ? tile_variant(wide_tile_128x128()) : 2 + 1;
+    // 129 to 256 rows: 256-row tiles; for byte-format weights the 256x128
+    // single-rebuild tile with 128-wide K steps where those pay (70B gate,
+    // palette-direct: 192 rows 159.2 -> 146.5 us, 256 rows 159.6 -> 152.5;
+    // exponent weights at 256 rows 167.0 -> 152.4)
+    if (batch <= 256 && mfma2_wide_pays(w, batch, wide_tile_xreg256())) return tile_variant(wide_tile_xreg256());
     if (batch <= 512) return 2 + 7;
     const int64_t tiles = (int64_t)((w.n + 255) / 256) * ((batch + 255) / 256);
     return tiles * 8 >= (int64_t)device_cus() * 7 ? big : 2 + 1;

@@ -343,7 +343,7 @@ uw_status uw_plan_gemm(const uw_matrix* m, uw_pipeline p, int64_t batch, const u
                        uw_gemm_plan* out);
 
 /* Number of GEMM variants selectable through uw_kernel_cfg.variant, numbered
- * 1..count (count = 19): 1 = VALU GEMV (v_dot2; any batch, eight rows per
+ * 1..count (count = 20): 1 = VALU GEMV (v_dot2; any batch, eight rows per
  * launch); 2..10 = MFMA tiles 64x128, 128x128, 128x256, 256x128, 256x256,
  * 32x128, 32x256, 256x256 with eight waves, and 512x128 with x in registers
  * (batch rows x columns; weights rebuilt into LDS once per block, so the
@@ -352,10 +352,11 @@ uw_status uw_plan_gemm(const uw_matrix* m, uw_pipeline p, int64_t batch, const u
  * each wave loading its own x; 13, 14 = register-fed MFMA with one or two
  * tiles per wave, the four waves of a block sharing each window of x through
  * LDS (register-fed: weights rebuilt in registers; 64 batch rows per launch);
- * 15..19 = the MFMA tiles 64x128, 128x128, 32x128, 32x256 and 512x128 with
- * x in registers, with K steps of 128, which read whole 128-byte lines of
- * each stored row per step for twice the LDS (one block per CU).  11..19
- * take stored [N][K] only:
+ * 15..20 = the MFMA tiles 64x128, 128x128, 32x128, 32x256, 512x128 with x in
+ * registers and 256x128 with x in registers (eight waves of 32 rows), with
+ * K steps of 128, which read whole 128-byte lines of each stored row per
+ * step for twice the LDS (one block per CU).  11..20 take stored [N][K]
+ * only:
  * UW_ERR_UNSUPPORTED for [K][N].  split_k applies to the KN GEMV, the
  * LDS-tiled and the register-fed MFMA kernels. */
 int32_t uw_variant_count(void);

@@ -223,7 +223,7 @@ def wide_variants(uw):
         kern = uw.uw_plan_gemm(m, 0, 16, {"variant": v})["kernel"]
         if kern.startswith("k_mfma2<") and kern.endswith(", 2>"):
             out.append(v)
-    assert len(out) == 5, out
+    assert len(out) == 6, out
     return out
 
 
@@ -271,11 +271,12 @@ def test_gemm_mid_batch_split(uw, synth, oracle, layout, batch):
         y = run_pipeline(uw, m, p, x)
         check_gemm(oracle, y, x_np, w_np, layout, what=f"pipeline {p}")
     # ... and the single-rebuild 512x128 tile (x in registers), split and not,
-    # and ([N][K]) the 128x128 and single-rebuild tiles with 128-wide K steps
+    # and ([N][K]) the 128x128 and both single-rebuild tiles with 128-wide K
+    # steps
     cases = ((2 + 7, 3), (2 + 4, 5), (2 + 8, 3), (2 + 8, 1))
     if layout == 0:
         wide = wide_variants(uw)
-        cases += tuple((v, sk) for v in (wide[1], wide[4]) for sk in (1, 3))
+        cases += tuple((v, sk) for v in (wide[1], wide[4], wide[5]) for sk in (1, 3))
     for v, sk in cases:
         for p in (0, 3):
             y = run_pipeline(uw, m, p, x, cfg={"variant": v, "split_k": sk})
