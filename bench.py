@@ -591,21 +591,30 @@ def cpu_baseline_c5(synth, wl, batches, min_rows: int = 128):
     for b in batches:
         for K in {s[2] for s in subs}:
             xs[(b, K)] = synth.bits_numpy(synth.activations(b, K, seed=wl.seed + 901 + b))
+    t0 = time.perf_counter()
     comp = [oracle.compress(w, seg_groups=4, layout=layout) for w, layout, _ in subs]
+    t_compress = time.perf_counter() - t0
     M = sum(w.size for w, _, _ in subs)
 
-    def work(i: int, b: int) -> None:
+    split = [0.0, 0.0]   # single-thread sweep: seconds in decode_full, in the fp64 GEMM
+
+    def work(i: int, b: int, tally: bool = False) -> None:
         w, layout, K = subs[i]
+        t0 = time.perf_counter()
         st, full = comp[i].decode_full()
         assert st == 0
+        t1 = time.perf_counter()
         oracle.gemm_ref(xs[(b, K)], full.reshape(w.shape), layout, threads=1)
+        if tally:
+            split[0] += t1 - t0
+            split[1] += time.perf_counter() - t1
 
     def sweep(nthreads: int) -> float:
         t0 = time.perf_counter()
         if nthreads == 1:
             for b in batches:
                 for i in range(len(subs)):
-                    work(i, b)
+                    work(i, b, True)
         else:
             with cf.ThreadPoolExecutor(max_workers=nthreads) as ex:
                 list(ex.map(lambda a: work(*a), [(i, b) for b in batches for i in range(len(subs))]))
@@ -614,6 +623,32 @@ def cpu_baseline_c5(synth, wl, batches, min_rows: int = 128):
     t_multi = sweep(threads)
     t_one = sweep(1)
     rate = lambda t: len(batches) * 2 * M / t / 1e9  # noqa: E731
+
+    # single-thread time of each phase over the whole sample: compress (timed
+    # above), one pass of each decode mode, and the fp64 GEMM at every batch
+    # (its share of the single-thread sweep)
+    def timed(fn) -> float:
+        t0 = time.perf_counter()
+        for c in comp:
+            st, _ = fn(c)
+            assert st == 0
+        return time.perf_counter() - t0
+
+    t_full = timed(lambda c: c.decode_full())
+    t_exp = timed(lambda c: c.decode_exponent())
+    t_tc = timed(lambda c: c.transcode())
+    t_gemm = split[1]
+    layer = sum(n * k for _, n, k, _ in wl.mats)   # weights of one full layer
+    scale = layer / M
+    phases = {"compress_s": round(t_compress, 3), "decode_full_s": round(t_full, 3),
+              "decode_exponent_s": round(t_exp, 3), "transcode_s": round(t_tc, 3),
+              "gemm_fp64_all_batches_s": round(t_gemm, 3),
+              "weights_per_s": {k: round(M / t, 1) for k, t in (("compress", t_compress), ("decode_full", t_full),
+                                                               ("decode_exponent", t_exp), ("transcode", t_tc))},
+              "extrapolated": (f"x{scale:.1f} per full layer, x80 layers (extrapolated, not run): "
+                               f"compress {t_compress * scale * 80 / 3600:.2f} h, one sweep (decode_full + fp64 GEMM "
+                               f"per batch) {t_one * scale * 80 / 3600:.2f} h on 1 thread, "
+                               f"{t_multi * scale * 80 / 3600:.2f} h on {threads}")}
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -622,6 +657,7 @@ def cpu_baseline_c5(synth, wl, batches, min_rows: int = 128):
         pass
     return {"value": round(rate(t_multi), 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "single_thread_value": round(rate(t_one), 4), "cpu_model": model, "nproc": os.cpu_count(),
+            "phases_single_thread": phases,
             "sample": (f"{M} weights of one 70B MLP layer ({min_rows} output features of each of gate, up, down, "
                        f"N(0,0.02), in {len(subs)} oracle-compressed sub-matrices); per batch of the sweep "
                        f"{list(batches)}: decode_full of each + fp64 reference GEMM; {t_one:.1f} s on 1 thread, "
