@@ -99,6 +99,20 @@ def load_traffic(stage: str, workload: str = "gate8b"):
     return k.get("hbm_bytes_per_launch")
 
 
+def load_valu_floor(stage: str):
+    """The decoder's VALU floor (its VALU instruction count from committed
+    rocprofv3 counters at one 64-lane instruction per SIMD every 4 cycles on
+    1024 SIMDs at 2.4 GHz), if the counters were taken on the current source."""
+    path = os.path.join(ROOT, "profiles", "decode_counters_gate8b.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        k = json.load(f).get("kernels", {}).get(stage)
+    if not k or k.get("source_sha") != source_sha(stage):
+        return None
+    return k
+
+
 def cpu_baseline_gate8b(w_np, x_np, min_seconds: float = 10.0):
     """The oracle, as it stands, on the same matrix: 3 decodes + 4 fp64 GEMVs
     per step, repeated whole steps until min_seconds have passed."""
@@ -893,6 +907,10 @@ def gate8b_section(uw, synth, torch, dev, args, with_cpu: bool):
         kernels[st] = {"kernel": STAGE_KERNELS[st], "us": round(stage_us[st], 2), "alg_bytes": int(ab),
                        "gbs": round(ab / t / 1e9, 1), "hbm_frac": round(ab / t / 1e9 / HBM_PEAK_GBS, 4),
                        "traffic": load_traffic(st)}
+        vf = load_valu_floor(st) if st.startswith(("decode", "transcode")) else None
+        if vf:   # the decoders against the vector ALU as well as HBM
+            kernels[st]["alu"] = {"valu_instr": int(vf["valu_instr"]), "floor_us": vf["valu_floor_us"],
+                                  "frac": round(vf["valu_floor_us"] / stage_us[st], 4)}
     pipes = {}
     for p, (pre, gem) in zip(PIPE_NAMES, [("decode_full", "gemv_full"), ("decode_exponent", "gemv_exponent"),
                                           ("transcode", "gemv_transcode"), (None, "gemv_direct")]):
