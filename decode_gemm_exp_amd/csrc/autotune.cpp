@@ -235,7 +235,7 @@ extern "C" uw_status uw_autotune(const uw_matrix* const* ms, const int32_t* proj
             if (bm > 32 && batch < 8) continue;                 // 64- to 256-row tiles from batch 8 on
             if (bm == 32 && (batch < 2 || batch > 128)) continue;   // 32-row tiles for batches 2..128
             if (bm == 512 && batch < 256) continue;                 // the 512-row tile from batch 256
-            if (tile >= uw::mfma2_wide_first() && bm == 256 && batch < 128) continue;   // its 256-row version from 128
+            if (tile >= uw::mfma2_late_first() && bm == 256 && batch < 128) continue;   // its 256-row version from 128
             if (uw::gemm_variant_is_rf(v) && batch > 2 * uw::mfma_rf_max_batch()) continue;   // <= 128 rows
             Choice c;
             c.pipeline = pl;
@@ -483,7 +483,7 @@ extern "C" uw_status uw_autotune_grouped(const uw_matrix* const* ms, int group, 
         if (bm > 32 && batch < 8) continue;
         if (bm == 32 && (batch < 2 || batch > 128)) continue;
         if (bm == 512 && batch < 256) continue;
-        if (tile >= uw::mfma2_wide_first() && bm == 256 && batch < 128) continue;
+        if (tile >= uw::mfma2_late_first() && bm == 256 && batch < 128) continue;
         if (uw::gemm_variant_is_rf(v) && batch > 2 * uw::mfma_rf_max_batch()) continue;
         Choice c;
         c.pipeline = pl;

@@ -718,27 +718,39 @@ hipError_t launch_gemv_group(const GemvGroup& g, int fmt, const uint16_t* x, int
 }  // namespace
 
 // Variant numbering seen through uw_kernel_cfg.variant: 1 = VALU GEMV (any
-// batch, eight rows per launch), 2.. = the MFMA tiles of gemm_mfma.hip with
-// 64-wide K steps, then the register-fed MFMA kernels of gemm_rf.hip, then
-// the tiles with 128-wide K steps (these two families: stored [N][K] only).
-int rf_first_variant() { return 2 + mfma2_wide_first(); }
-static int wide_first_variant() { return rf_first_variant() + mfma_rf_kinds(); }
+// batch, eight rows per launch), 2.. = the first nine MFMA tiles of
+// gemm_mfma.hip (64-wide K steps), then the register-fed MFMA kernels of
+// gemm_rf.hip, then the later tiles: those with 128-wide K steps (like the
+// register-fed kernels, stored [N][K] only) and the eight-wave 128x128,
+// 128x256 and 64x128 tiles.
+int rf_first_variant() { return 2 + mfma2_late_first(); }
+static int late_first_variant() { return rf_first_variant() + mfma_rf_kinds(); }
 int gemm_variant_count() { return 1 + mfma2_tile_count() + mfma_rf_kinds(); }
-bool gemm_variant_supported(int v, int layout) { return v < rf_first_variant() || layout == 0; }
-bool gemm_variant_is_rf(int v) { return v >= rf_first_variant() && v < wide_first_variant(); }
+bool gemm_variant_supported(int v, int layout) {
+  if (layout == 0 || v < rf_first_variant()) return true;
+  const int tile = gemm_variant_tile(v);   // none for the register-fed kernels
+  if (tile < 0) return false;
+  int waves = 0, wgm = 0, kw = 0;
+  bool xreg = false;
+  mfma2_tile_shape(tile, &waves, &wgm, &xreg, &kw);
+  return kw == 1;
+}
+bool gemm_variant_is_rf(int v) { return v >= rf_first_variant() && v < late_first_variant(); }
 int gemm_variant_tile(int v) {
   if (v >= 2 && v < rf_first_variant()) return v - 2;
-  if (v >= wide_first_variant() && v <= gemm_variant_count()) return mfma2_wide_first() + (v - wide_first_variant());
+  if (v >= late_first_variant() && v <= gemm_variant_count()) return mfma2_late_first() + (v - late_first_variant());
   return -1;
 }
 static int tile_variant(int tile) {
-  return tile < mfma2_wide_first() ? 2 + tile : wide_first_variant() + (tile - mfma2_wide_first());
+  return tile < mfma2_late_first() ? 2 + tile : late_first_variant() + (tile - mfma2_late_first());
 }
 // the wide-step versions of the 128x128, 32x128 and single-rebuild tiles
-static int wide_tile_128x128() { return mfma2_wide_first() + 1; }
-static int wide_tile_32x128() { return mfma2_wide_first() + 2; }
-static int wide_tile_xreg() { return mfma2_wide_first() + 4; }
-static int wide_tile_xreg256() { return mfma2_wide_first() + 5; }
+static int wide_tile_128x128() { return mfma2_late_first() + 1; }
+static int wide_tile_32x128() { return mfma2_late_first() + 2; }
+static int wide_tile_xreg() { return mfma2_late_first() + 4; }
+static int wide_tile_xreg256() { return mfma2_late_first() + 5; }
+// the eight-wave 128x256 tile (64-wide K steps, either layout)
+static int eight_wave_128x256() { return mfma2_late_first() + 7; }
 
 // Default kernel by batch, from sweeps over the 8B and 70B MLP shapes (every
 // variant, both layouts, palette-direct and BF16 weights):
@@ -755,8 +767,12 @@ static int wide_tile_xreg256() { return mfma2_wide_first() + 5; }
 //     rows, 224 tiles: palette-direct 252 -> 164 us), else 128x128 (8B q at
 //     1024 rows, 64 tiles: 80 vs 81 us palette-direct, 46 vs 64 us BF16);
 //   stored [K][N]: VALU GEMV for one row, then LDS tiles 32x256 up to 32,
-//     64x128 up to 64, 128x256 up to 128, 256x256 beyond (70B down at 192
-//     rows, palette-direct: 292 -> 186 us).
+//     the eight-wave 128x256 up to 128 (70B down, palette-direct, against
+//     the four-wave 64x128 at 48 / 64 rows and 128x256 at 96 / 128 rows:
+//     93.5 / 98.1 / 99.9 / 102.6 -> 84.8 / 89.2 / 91.7 / 101.1 us; on
+//     another box 64 / 128 rows against 128x256 105.8 / 124.8 -> 99.4 /
+//     102.7 us), 256x256 beyond (70B down at 192 rows, palette-direct: 292
+//     -> 186 us).
 // The 256x256 tile runs with eight waves (two per SIMD) for palette weights,
 // whose rebuild then issues beside the other wave's MFMAs (70B gate,
 // palette-direct, 1024 rows: 737 -> 602 us); BF16 and exponent weights gain
@@ -800,8 +816,7 @@ static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_c
   }
   if (batch == 1) return 1;
   if (batch <= 32) return 2 + 6;
-  if (batch <= 64) return 2 + 0;
-  if (batch <= 128) return 2 + 2;
+  if (batch <= 128) return tile_variant(eight_wave_128x256());
   return big;
 }
 

@@ -529,19 +529,24 @@ struct Tile2 {
 // 32-row tiles (one MFMA row tile, four waves side by side) are for small
 // batches; then 256x256 with eight waves (two per SIMD); then the
 // single-rebuild tile, 512 rows x 128 columns, eight waves of 64 rows.  The
-// last six are the 64x128, 128x128, 32x128, 32x256 and single-rebuild tiles
+// next six are the 64x128, 128x128, 32x128, 32x256 and single-rebuild tiles
 // with 128-wide K steps for stored [N][K] weights, and a 256-row
 // single-rebuild tile (eight waves of 32 rows) with them: each step reads
 // whole 128-byte lines of sign+mantissa bytes per row (a 64-wide step reads
 // half a line per row and the other half a step later), for twice the LDS
-// (one block per CU for the four-wave tiles).
+// (one block per CU for the four-wave tiles).  The last four run eight
+// waves of 32 x 32 to 64 x 64 on the 128x128, 128x256 and 64x128 tiles:
+// the same LDS as their four-wave versions, which it limits to one block
+// per CU, holds twice the waves, so twice the loads are in flight and one
+// wave's rebuild issues beside the other's MFMAs on each SIMD.
 constexpr Tile2 kTiles2[] = {
     {64, 128, 4, 2, false, 1},  {128, 128, 4, 2, false, 1}, {128, 256, 4, 2, false, 1}, {256, 128, 4, 2, false, 1},
     {256, 256, 4, 2, false, 1}, {32, 128, 4, 1, false, 1},  {32, 256, 4, 1, false, 1},  {256, 256, 8, 2, false, 1},
     {512, 128, 8, 8, true, 1},  {64, 128, 4, 2, false, 2},  {128, 128, 4, 2, false, 2}, {32, 128, 4, 1, false, 2},
-    {32, 256, 4, 1, false, 2},  {512, 128, 8, 8, true, 2},  {256, 128, 8, 8, true, 2}};
+    {32, 256, 4, 1, false, 2},  {512, 128, 8, 8, true, 2},  {256, 128, 8, 8, true, 2}, {128, 128, 8, 2, false, 2},
+    {128, 256, 8, 2, false, 1}, {64, 128, 8, 2, false, 1},  {64, 128, 8, 2, false, 2}};
 constexpr int kTileCount = (int)(sizeof(kTiles2) / sizeof(kTiles2[0]));
-constexpr int kWideFirst = 9;   // the first tile with 128-wide K steps
+constexpr int kLateFirst = 9;   // the first tile numbered after the register-fed kernels
 constexpr int tile_kw(int tile) { return kTiles2[tile].nk_kw; }
 
 // the kernel of tile T for layout L (none: a wide-step tile for [K][N])
@@ -557,7 +562,7 @@ Mfma2Fn inst() {
 
 template <int L, int F>
 Mfma2Fn pick(int tile) {
-  static_assert(kTileCount == 15, "one case per tile");
+  static_assert(kTileCount == 19, "one case per tile");
   switch (tile) {
     case 0: return inst<L, F, 0>();
     case 1: return inst<L, F, 1>();
@@ -574,13 +579,17 @@ Mfma2Fn pick(int tile) {
     case 12: return inst<L, F, 12>();
     case 13: return inst<L, F, 13>();
     case 14: return inst<L, F, 14>();
+    case 15: return inst<L, F, 15>();
+    case 16: return inst<L, F, 16>();
+    case 17: return inst<L, F, 17>();
+    case 18: return inst<L, F, 18>();
     default: return nullptr;
   }
 }
 
 }  // namespace
 int mfma2_tile_count() { return kTileCount; }
-int mfma2_wide_first() { return kWideFirst; }
+int mfma2_late_first() { return kLateFirst; }
 void mfma2_tile_dims(int tile, int* bm, int* bn) {
   *bm = kTiles2[tile].bm;
   *bn = kTiles2[tile].bn;

@@ -197,7 +197,7 @@ hipError_t launch_sum_slices(const float* part, int slices, uint64_t n, int64_t 
 int mfma2_tile_count();
 void mfma2_tile_dims(int tile, int* bm, int* bn);
 void mfma2_tile_shape(int tile, int* waves, int* wgm, bool* xreg, int* kw);   // kw: K step in units of 64
-int mfma2_wide_first();                                 // first tile with 128-wide K steps ([N][K] only)
+int mfma2_late_first();   // first tile numbered after the register-fed kernels (128-wide K steps, eight-wave 128x256 and 64x128)
 bool mfma2_wide_pays(const WeightView& w, int64_t batch, int tile);
 bool gemm_variant_is_rf(int v);                         // a register-fed MFMA variant
 int gemm_variant_tile(int v);                           // the MFMA tile of variant v, or -1

@@ -37,7 +37,7 @@ def test_status_strings_and_version(uw):
     for st in range(-7, 1):
         assert uw._lib.uw_status_str(st)
     assert uw.version() >> 16 == 1
-    assert uw.variant_count() == 20   # GEMV, nine LDS tiles, four register-fed kinds, six wide-step tiles
+    assert uw.variant_count() == 24   # GEMV, nine LDS tiles, four register-fed kinds, six wide-step tiles, four eight-wave tiles
 
 
 def test_invalid_arguments_rejected_without_device(uw):

@@ -190,8 +190,9 @@ def test_gemm_ragged_all_pipelines(uw, synth, oracle, layout, batch):
         y = run_pipeline(uw, m, p, x)
         check_gemm(oracle, y, x_np, w_np, layout, what=f"pipeline {p}")
     # every variant, forced (the register-fed ones, last, take stored [N][K] only)
+    nk_only = set(rf_variants(uw)) | set(wide_variants(uw))
     for v in range(1, uw.variant_count() + 1):
-        if layout == 1 and v >= RF_FIRST(uw):
+        if layout == 1 and v in nk_only:
             with pytest.raises(uw.UwError) as ei:
                 run_pipeline(uw, m, 3, x, cfg={"variant": v})
             assert ei.value.status == uw.UW_ERR_UNSUPPORTED
@@ -223,11 +224,24 @@ def wide_variants(uw):
         kern = uw.uw_plan_gemm(m, 0, 16, {"variant": v})["kernel"]
         if kern.startswith("k_mfma2<") and kern.endswith(", 2>"):
             out.append(v)
-    assert len(out) == 6, out
+    assert len(out) == 8, out
     return out
 
 
-# the small tiles (64x128, 32x128, 32x256) over K slices of 1, 2, 5 and an
+def eight_wave_variants(uw):
+    """The eight-wave 128x256 and 64x128 tiles with 64-wide K steps (either
+    layout), found from the kernel each variant plans."""
+    w = torch.zeros(64, 128, dtype=torch.bfloat16, device=DEV)
+    m = uw.uw_compress(w, 64, 128, 0)
+    out = [v for v in range(1, uw.variant_count() + 1)
+           if any(uw.uw_plan_gemm(m, 0, 16, {"variant": v})["kernel"].endswith(t)
+                  for t in (", 128, 256, 2, 8, false, 1>", ", 64, 128, 2, 8, false, 1>"))]
+    assert len(out) == 2, out
+    return out
+
+
+# the small tiles (64x128, 32x128, 32x256, and the eight-wave 128x256 and
+# 64x128) over K slices of 1, 2, 5 and an
 # odd or even number of steps, forced K splits that leave uneven slices,
 # both layouts, a ragged batch (and a ragged N where the layout allows it:
 # stored [K][N] keeps N a multiple of 64); for stored [N][K] also the tiles
@@ -246,7 +260,7 @@ def test_gemm_small_tiles_step_counts(uw, synth, oracle, layout, k):
     uw.uw_transcode_palette(m, None)
     w_np, x_np = bits(w), bits(x)
     splits = (1, 3, 7) if k == 2112 else (1,)
-    for v in (2 + 0, 2 + 5, 2 + 6) + (tuple(wide_variants(uw)) if layout == 0 else ()):
+    for v in (2 + 0, 2 + 5, 2 + 6) + tuple(eight_wave_variants(uw)) + (tuple(wide_variants(uw)) if layout == 0 else ()):
         for sk in splits:
             for p in (0, 1, 3):
                 y = run_pipeline(uw, m, p, x, cfg={"variant": v, "split_k": sk})
