@@ -744,13 +744,15 @@ int gemm_variant_tile(int v) {
 static int tile_variant(int tile) {
   return tile < mfma2_late_first() ? 2 + tile : late_first_variant() + (tile - mfma2_late_first());
 }
-// the wide-step versions of the 128x128, 32x128 and single-rebuild tiles
-static int wide_tile_128x128() { return mfma2_late_first() + 1; }
+// the wide-step versions of the 32x128 and single-rebuild tiles
 static int wide_tile_32x128() { return mfma2_late_first() + 2; }
 static int wide_tile_xreg() { return mfma2_late_first() + 4; }
 static int wide_tile_xreg256() { return mfma2_late_first() + 5; }
-// the eight-wave 128x256 tile (64-wide K steps, either layout)
+// the eight-wave tiles: 128x128 and 64x128 with 128-wide K steps, 128x256
+// with 64-wide ones (either layout)
+static int eight_wave_128x128_wide() { return mfma2_late_first() + 6; }
 static int eight_wave_128x256() { return mfma2_late_first() + 7; }
+static int eight_wave_64x128_wide() { return mfma2_late_first() + 9; }
 
 // Default kernel by batch, from sweeps over the 8B and 70B MLP shapes (every
 // variant, both layouts, palette-direct and BF16 weights):
@@ -760,8 +762,9 @@ static int eight_wave_128x256() { return mfma2_late_first() + 7; }
 //     99.8 / 95.0 / 108.4 -> 84.6 / 83.5 / 96.7 us, 8B gate 8 / 16 rows 34.2
 //     / 36.1 -> 31.6 / 32.1 us; on narrower matrices it loses, 8B q with 64
 //     blocks at 8 rows 20.5 vs 13.2 us, and x per wave with two row tiles
-//     per wave stays), then LDS tiles 64x128 up to 64, 128x128 up to 128,
-//     the eight-wave 256x256 up to 512 (K split to fill the CUs: 70B gate at
+//     per wave stays), then LDS tiles 64x128 up to 64, 128x128 up to 128
+//     (both with eight waves and 128-wide K steps where those pay), the
+//     eight-wave 256x256 up to 512 (K split to fill the CUs: 70B gate at
 //     512 rows, palette-direct 466 -> 319 us, BF16 295 -> 234 us), and beyond
 //     256x256 when its tiles cover seven eighths of the CUs (8B gate at 1024
 //     rows, 224 tiles: palette-direct 252 -> 164 us), else 128x128 (8B q at
@@ -776,7 +779,8 @@ static int eight_wave_128x256() { return mfma2_late_first() + 7; }
 // The 256x256 tile runs with eight waves (two per SIMD) for palette weights,
 // whose rebuild then issues beside the other wave's MFMAs (70B gate,
 // palette-direct, 1024 rows: 737 -> 602 us); BF16 and exponent weights gain
-// nothing from it.  Tile indices are those of gemm_mfma.hip (variant = 2 + index).
+// nothing from it.  Tile indices are those of gemm_mfma.hip; tile_variant
+// gives the variant number of a tile.
 static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_cfg* cfg) {
   if (cfg && cfg->variant > 0 && cfg->variant <= gemm_variant_count()) return cfg->variant;
   const int big = fmt_is_pal(w.fmt) ? 2 + 7 : 2 + 4;
@@ -795,16 +799,25 @@ static int resolve_variant(const WeightView& w, int64_t batch, const uw_kernel_c
     if (batch <= 32 && mfma_rf_supported(w, 2) && (int64_t)((w.n + 63) / 64) * 8 >= (int64_t)device_cus() * 7)
       return rf_first_variant() + 2;
     if (batch <= 32 && mfma_rf_supported(w, 0)) return rf_first_variant();
-    // 33 to 64 rows: x shared, two row tiles per wave, when its 128-row
+    // 33 to 64 rows: the eight-wave 64x128 tile with 128-wide K steps where
+    // those pay (70B gate, palette-direct, 48 / 64 rows: 110.0 / 103.5 us
+    // against 114.1 / 111.7 for the register-fed kernel below and 117.1 /
+    // 120.0 for the four-wave 64x128 tile); else x shared, two row tiles
+    // per wave, when its 128-row
     // blocks cover seven eighths of the CUs (70B gate, palette, 40 / 48 / 64
     // rows: 115.4 / 110.9 / 113.5 us against 119.0 / 119.8 / 123.9 for the
     // 64x128 tile); narrower matrices keep the tile (8B gate 42.5 vs 38.1 us
     // at 64 rows)
+    if (batch <= 64 && mfma2_wide_pays(w, batch, eight_wave_64x128_wide())) return tile_variant(eight_wave_64x128_wide());
     if (batch <= 64 && mfma_rf_supported(w, 3) && (int64_t)((w.n + 127) / 128) * 8 >= (int64_t)device_cus() * 7)
       return rf_first_variant() + 3;
     if (batch <= 64) return 2 + 0;
-    // 65 to 128 rows: 128x128 tiles, with 128-wide K steps where those pay
-    if (batch <= 128) return mfma2_wide_pays(w, batch, wide_tile_128x128()) ? tile_variant(wide_tile_128x128()) : 2 + 1;
+    // 65 to 128 rows: 128x128 tiles, eight waves with 128-wide K steps where
+    // those pay (70B gate, palette-direct, against four waves: 96 / 128 rows
+    // 110.6 / 108.7 -> 110.1 / 109.4 us on one box, 128 rows 127.9 -> 119.3
+    // on another)
+    if (batch <= 128)
+      return mfma2_wide_pays(w, batch, eight_wave_128x128_wide()) ? tile_variant(eight_wave_128x128_wide()) : 2 + 1;
     // 129 to 256 rows: 256-row tiles; for byte-format weights the 256x128
     // single-rebuild tile with 128-wide K steps where those pay (70B gate,
     // palette-direct: 192 rows 159.2 -> 146.5 us, 256 rows 159.6 -> 152.5;
