@@ -150,9 +150,12 @@ def test_tuning_table_rejects_malformed_entries(uw):
             uw.uw_set_tuning([bad[0], b])
         assert ei.value.status == -1
         assert uw.uw_lookup_tuning(28672, 8192, 0, 3, 1) is None   # none of the call's entries was added
-    # register-fed variants are [N][K] only
-    with pytest.raises(uw.UwError):
-        uw.uw_set_tuning([_entry(uw, 8, 3, variant=uw.variant_count(), layout=1)])
+    # register-fed variants (the first follows the GEMV and the nine LDS
+    # tiles with 64-wide K steps) and 128-wide K steps (variant 21, the
+    # eight-wave 128x128) are [N][K] only
+    for v in (11, 21):
+        with pytest.raises(uw.UwError):
+            uw.uw_set_tuning([_entry(uw, 8, 3, variant=v, layout=1)])
     assert uw._lib.uw_lookup_tuning(1, 1, 0, 3, 0, None) == -1
 
 
