@@ -358,14 +358,41 @@ __global__ __launch_bounds__(staged_max_threads<CH>()) void k_decode_staged(Deco
       (uint8_t*)a.out + ob0, (short)0, (int)(oleft < kRecordsMax ? oleft : kRecordsMax), 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
       (void*)a.vexp, (short)0, (int)(a.vexp_bytes < kRecordsMax ? a.vexp_bytes : kRecordsMax), 0x00020000);
-  // stream range of this wave -> LDS (16 bytes per lane per step)
+  // stream range of this wave -> LDS (16 bytes per lane per load) and the
+  // block's share of the table: every load of a batch is issued before the
+  // first LDS write waits on them, so the copy costs one memory latency per
+  // batch rather than one per 16-byte piece.  Pieces past the range load
+  // from past the resource's end (zero) and are not written.
   const uint32_t nwords = we1 - ws0;
-  for (uint32_t i = (uint32_t)lane * 4u; i < nwords; i += 256u) {
-    const uint4 v = load_chunk<MODE == kDecodeNibble>(rs, ws0 + i);
-    *reinterpret_cast<uint4*>(&sbuf[i]) = v;
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc((void*)a.lut, (short)0, (int)kLutBytes, 0x00020000);
+  constexpr uint32_t kCopyBatch = 8;   // 2048 stream words per wave per batch
+  constexpr uint32_t kLutBatch = 4;    // table pieces per thread per batch
+  constexpr uint32_t kLutPieces = kLutBytes / 16u;
+  const uint32_t nthreads = blockDim.x;
+  for (uint32_t base = 0, lbase = 0; base < nwords || lbase < kLutPieces;
+       base += 256u * kCopyBatch, lbase += kLutBatch * nthreads) {
+    uint4 v[kCopyBatch], t[kLutBatch];
+#pragma unroll
+    for (uint32_t j = 0; j < kCopyBatch; ++j) {
+      const uint32_t i = base + j * 256u + (uint32_t)lane * 4u;
+      v[j] = load_chunk<MODE == kDecodeNibble>(rs, i < nwords ? ws0 + i : kPastEnd / 4u);
+    }
+#pragma unroll
+    for (uint32_t j = 0; j < kLutBatch; ++j) {
+      const uint32_t i = lbase + j * nthreads + threadIdx.x;
+      t[j] = buf_load16(rl, i < kLutPieces ? i * 16u : kPastEnd);
+    }
+#pragma unroll
+    for (uint32_t j = 0; j < kLutBatch; ++j) {
+      const uint32_t i = lbase + j * nthreads + threadIdx.x;
+      if (i < kLutPieces) reinterpret_cast<uint4*>(lut)[i] = t[j];
+    }
+#pragma unroll
+    for (uint32_t j = 0; j < kCopyBatch; ++j) {
+      const uint32_t i = base + j * 256u + (uint32_t)lane * 4u;
+      if (i < nwords) *reinterpret_cast<uint4*>(&sbuf[i]) = v[j];
+    }
   }
-  for (int i = threadIdx.x; i < (int)(kLutBytes / 16u); i += (int)blockDim.x)
-    reinterpret_cast<uint4*>(lut)[i] = reinterpret_cast<const uint4*>(a.lut)[i];
   __syncthreads();
   if (!wval) return;
 
